@@ -1,0 +1,226 @@
+"""Benchmark of one MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one colibri_moe_layer_forward (quantise, route, union dispatch,
+gate/up + SiLU + requant, down, combine) over one batch of synthetic tokens
+already resident in HBM.  The default workload is the S = 1 decode layer
+(H = 6144, 256 experts of I = 2048, top-8, packed int4, plus a shared
+expert).  To keep the 256 MB last-level cache from serving weights that a
+real model would have evicted, consecutive steps rotate over several copies
+of the layer at distinct addresses and over distinct token batches.
+
+Prints one JSON line with the throughput (routed tokens/s per layer), a
+roofline object for the dominant kernel (timed with HIP events recorded by
+the library between its stages on the benchmark's stream), a CPU baseline
+(the oracle, single-threaded, on a bounded sample), and the S = 512 prefill
+figure of the same layer.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published (TOPS)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0: per-workload default)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--copies", type=int, default=8, help="layer copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    return ap.parse_args()
+
+
+def expert_bytes(w):
+    """Packed weights plus row scales of one expert (gate, up, down)."""
+    H, I, b = w.hidden, w.inter, w.bits
+    return 3 * H * I * b // 8 + (2 * I + H) * 4
+
+
+def stage_bytes(w, n_units_touched, S):
+    """Algorithmic HBM bytes of each stage for one step (n_units_touched =
+    distinct routed experts + the shared expert)."""
+    H, I, E, k, b = w.hidden, w.inter, w.n_experts, w.top_k, w.bits
+    gu = n_units_touched * (2 * I * H * b // 8 + 2 * I * 4)
+    dn = n_units_touched * (H * I * b // 8 + H * 4)
+    return {
+        "route": E * H * 4 + E * 4 + S * H * 4,
+        "gate_up": gu,
+        "down": dn,
+        "combine": S * H * 4,
+    }
+
+
+def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True):
+    import numpy as np
+    dev_layers = []
+    base = synth.make_layer(w, device="cuda")
+
+    def qb(b):
+        return qre.QBank(b.storage, b.scale_storage, b.bits)
+
+    def mk(L):
+        sh = [qb(L.sh_gate), qb(L.sh_up), qb(L.sh_down)] if w.has_shared else None
+        return qre.MoELayer(w.hidden, w.inter, w.n_experts, w.top_k, w.rsf, L.router_w, L.bias,
+                            qb(L.gate), qb(L.up), qb(L.down), sh)
+    dev_layers.append((mk(base), base))
+    for c in range(1, copies):
+        clone = synth.Layer(w, base.router_w.clone(), base.bias.clone(),
+                            *[None if b is None else synth.Bank(b.n_mat, b.rows, b.K, b.bits, [], [],
+                                                                b.storage.clone(), b.scale_storage.clone())
+                              for b in (base.gate, base.up, base.down, base.sh_gate, base.sh_up, base.sh_down)])
+        dev_layers.append((mk(clone), clone))
+    n_batches = max(copies, 16) if w.S <= 8 else 2
+    xs = [synth.activations(w, tag=f"/bench{i}").cuda() for i in range(n_batches)]
+    out = torch.empty_like(xs[0])
+    ws = dev_layers[0][0].workspace(w.S)
+    torch.cuda.synchronize()
+
+    def step(i):
+        qre.moe_layer_forward(dev_layers[i % copies][0], xs[i % n_batches], out, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+
+    res = {"steps": steps, "gpu_ms": gpu_ms, "wall_s": wall}
+    if timed_stages:
+        # same steps again through the staged entry point: per-stage durations
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(qre.COLI_N_STAGE_EVENTS)]
+               for _ in range(steps)]
+        for row in evs:  # materialise the events
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            qre.moe_layer_forward_staged(dev_layers[i % copies][0], xs[i % n_batches], out, ws,
+                                         [e.cuda_event for e in evs[i]])
+        torch.cuda.synchronize()
+        per = {s: 0.0 for s in qre.STAGES}
+        for row in evs:
+            for j, s in enumerate(qre.STAGES):
+                per[s] += row[j].elapsed_time(row[j + 1])
+        res["stage_ms"] = {s: v / steps for s, v in per.items()}
+    # union size of each batch (for algorithmic bytes)
+    uniq = []
+    for x in xs:
+        ids, _ = qre.route(dev_layers[0][0], x)
+        uniq.append(len(set(ids.cpu().numpy().reshape(-1).tolist())))
+    res["mean_unique_experts"] = float(np.mean([uniq[i % n_batches] for i in range(steps)]))
+    del dev_layers, base, xs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(synth, w, n_tokens):
+    """The oracle, as it stands, on n_tokens tokens of the same workload."""
+    import oracle
+    import numpy as np
+    x = synth.activations(w, S=n_tokens, tag="/cpu").numpy()
+    router_w, bias = synth.router_weights(w), synth.router_bias(w)
+    t0 = time.perf_counter()
+    ids, _, _ = oracle.route(x, router_w, bias, w.top_k, w.rsf)
+    t_route = time.perf_counter() - t0
+    needed = sorted(set(ids.reshape(-1).tolist()))
+    L = synth.make_layer(w, experts=needed, device="cpu")
+    t0 = time.perf_counter()
+    oracle.layer_forward(L, x)
+    t = time.perf_counter() - t0
+    return {"value": n_tokens / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the {w.name} workload through the single-threaded C oracle "
+                      f"(full layer per token; {t:.1f} s, router-only pass {t_route:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on one MI355X and this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_routed_expert_sigmoid_amd as qre
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qre.lib()
+    w = synth.WORKLOADS[args.workload]
+    steps = args.steps or (2000 if w.S <= 8 else 50)
+    res = run_workload(qre, synth, torch, w, steps, args.warmup, args.copies)
+    ms = res["gpu_ms"] / steps
+    value = w.S * steps / (res["gpu_ms"] / 1000.0)
+    U = res["mean_unique_experts"] + (1 if w.has_shared else 0)
+    sb = stage_bytes(w, U, w.S)
+    stage_ms = res["stage_ms"]
+    dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    achieved = sb[dom] / (stage_ms[dom] / 1000.0) / 1e9
+    layer_bytes = U * expert_bytes(w) + sb["route"] + sb["combine"]
+    line = {
+        "metric": "routed tokens/sec per MoE layer (S=1 decode, S=512 prefill); % HBM BW / % int8 MFMA",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded SplitMix64 weights and activations; no checkpoint)",
+        "config": {"workload": f"{w.name}: MoE layer H={w.hidden} I={w.inter} E={w.n_experts} "
+                               f"top-{w.top_k} int{w.bits} weights + shared expert, S={w.S}",
+                   "S": w.S, "weights": f"int{w.bits}", "layer_copies_rotated": args.copies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": f"ffn_{dom}_gemv<{w.bits}>", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None},
+        "layer": {"algorithmic_bytes": layer_bytes, "unique_routed_experts": res["mean_unique_experts"],
+                  "hbm_GBps_whole_layer": layer_bytes / (ms / 1000.0) / 1e9,
+                  "hbm_frac_whole_layer": layer_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
+                  "stage_ms": stage_ms},
+    }
+    if not args.no_prefill and args.workload == "decode":
+        wp = synth.WORKLOADS["prefill"]
+        rp = run_workload(qre, synth, torch, wp, 20, 3, 2)
+        msp = rp["gpu_ms"] / 20
+        Up = rp["mean_unique_experts"] + 1
+        ops = 2 * wp.S * (wp.top_k + 1) * 3 * wp.hidden * wp.inter
+        bytes_p = Up * expert_bytes(wp) + stage_bytes(wp, Up, wp.S)["route"]
+        line["prefill"] = {"workload": f"prefill: same layer, S={wp.S}", "value": wp.S / (msp / 1000.0),
+                           "unit": "tokens/s", "ms_per_step": msp,
+                           "hbm_frac": bytes_p / (msp / 1000.0) / 1e9 / HBM_PEAK_GBS,
+                           "int8_mfma_frac": ops / (msp / 1000.0) / 1e12 / INT8_PEAK_TOPS,
+                           "stage_ms": rp["stage_ms"]}
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or (4 if w.S <= 8 else 2)
+        line["cpu_baseline"] = cpu_baseline(synth, w, n)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+/*
+ * dispatch.hip -- batched-union dispatch and the routing-weighted combine.
+ *
+ * Union dispatch ("Show HN: 如何在我的低配置电脑上运行 GLM-5.2", implemented
+ * features, batched-union MoE item: every expert present in the batch is read
+ * once and applied to all positions routed to it).  The (token, slot) pairs
+ * p = t*k + j are grouped by expert with a histogram, an exclusive prefix sum
+ * and a stable counting sort, all inside one 1024-thread workgroup, with no
+ * atomics on positions: ranks come from wave ballots and per-wave counts, so
+ * the result is the unique stable order.
+ *
+ * Combine ("colibrì 深度拆解", section 4.3: shared-expert output plus the
+ * routing-weighted sum of the selected experts' outputs).
+ */
+#include "device_common.h"
+#include "kernels.h"
+
+namespace coli {
+
+constexpr int kDispThreads = 1024;
+constexpr int kDispWaves = kDispThreads / 64;
+constexpr int kMaxE = 1024;
+
+/* Workgroup exclusive scan of one value per thread (1024 threads).  Returns
+ * the exclusive prefix; *total receives the sum.  `tmp` holds kDispWaves ints. */
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tmp, int32_t* total)
+{
+    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int32_t inc = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        int32_t o = __shfl_up(inc, off, 64);
+        if (lane >= off)
+            inc += o;
+    }
+    if (lane == 63)
+        tmp[wv] = inc;
+    __syncthreads();
+    if (wv == 0) {
+        int32_t w = lane < kDispWaves ? tmp[lane] : 0;
+        int32_t winc = w;
+        for (int off = 1; off < kDispWaves; off <<= 1) {
+            int32_t o = __shfl_up(winc, off, 64);
+            if (lane >= off)
+                winc += o;
+        }
+        if (lane < kDispWaves)
+            tmp[lane] = winc - w; /* exclusive wave base */
+        if (lane == kDispWaves - 1)
+            tmp[kDispWaves] = winc;
+    }
+    __syncthreads();
+    int32_t res = tmp[wv] + inc - v;
+    *total = tmp[kDispWaves];
+    __syncthreads();
+    return res;
+}
+
+/* Writes the work units of expert e (count n, first sorted position off). */
+__device__ __forceinline__ void emit_units(Unit* units, int32_t ubase, int32_t e, int32_t off,
+                                           int32_t n, int32_t max_units)
+{
+    for (int32_t u = 0; u * kUnitTokens < n && ubase + u < max_units; ++u) {
+        Unit U;
+        U.e = e;
+        U.pos0 = off + u * kUnitTokens;
+        U.ntok = (n - u * kUnitTokens) < kUnitTokens ? (n - u * kUnitTokens) : kUnitTokens;
+        U.pad = 0;
+        units[ubase + u] = U;
+    }
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
+    const int32_t* __restrict__ ids, int32_t S, int32_t k, int32_t E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
+    int32_t* __restrict__ n_active, Unit* __restrict__ units, int32_t* __restrict__ n_units)
+{
+    __shared__ int32_t cnt[kMaxE];
+    __shared__ int32_t base[kMaxE];
+    __shared__ uint8_t wcnt[kDispWaves][kMaxE];
+    __shared__ int32_t tmp[kDispWaves + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int32_t P = S * k;
+
+    for (int e = tid; e < kMaxE; e += kDispThreads) {
+        cnt[e] = 0;
+        for (int w = 0; w < kDispWaves; ++w)
+            wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    /* ids outside [0, E) violate the documented precondition; they are
+     * clamped so that no access leaves its buffer. */
+    for (int32_t p = tid; p < P; p += kDispThreads)
+        atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
+    __syncthreads();
+
+    /* offsets, active list and unit list: one expert per thread */
+    const int32_t e = tid;
+    const int32_t c = e < E ? cnt[e] : 0;
+    int32_t tot;
+    const int32_t off = block_exclusive_scan(c, tmp, &tot);
+    const int32_t aidx = block_exclusive_scan(c > 0 ? 1 : 0, tmp, &tot);
+    const int32_t nact = tot;
+    const int32_t nu = (c + kUnitTokens - 1) / kUnitTokens;
+    const int32_t ubase = block_exclusive_scan(nu, tmp, &tot);
+    const int32_t nunits = tot;
+    if (e < E) {
+        base[e] = off;
+        offsets[e] = off;
+        if (c > 0)
+            active[aidx] = e;
+        if (units)
+            emit_units(units, ubase, e, off, c, 0x7fffffff);
+    }
+    if (tid == 0) {
+        offsets[E] = P;
+        *n_active = nact;
+        if (n_units)
+            *n_units = nunits;
+    }
+    __syncthreads();
+
+    /* stable placement, 1024 pairs per round */
+    int nbits = 1;
+    while ((1 << nbits) < E)
+        ++nbits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int32_t r0 = 0; r0 < P; r0 += kDispThreads) {
+        const int32_t p = r0 + tid;
+        const bool valid = p < P;
+        const int32_t ex = valid ? min(max(ids[p], 0), E - 1) : 0;
+        uint64_t m = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            uint64_t bal = __ballot(valid && ((ex >> b) & 1));
+            m &= ((ex >> b) & 1) ? bal : ~bal;
+        }
+        const int32_t rank = __popcll(m & lt_mask);
+        if (valid && rank == 0)
+            wcnt[wv][ex] = (uint8_t)__popcll(m);
+        __syncthreads();
+        if (valid) {
+            int32_t pos = base[ex] + rank;
+            for (int w = 0; w < wv; ++w)
+                pos += wcnt[w][ex];
+            sorted[pos] = p;
+            if (inv)
+                inv[p] = pos;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kDispThreads) {
+            int32_t add = 0;
+            for (int w = 0; w < kDispWaves; ++w) {
+                add += wcnt[w][ee];
+                wcnt[w][ee] = 0;
+            }
+            base[ee] += add;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, int32_t* offsets,
+                           int32_t* sorted, int32_t* inv, int32_t* active, int32_t* n_active,
+                           Unit* units, int32_t* n_units, hipStream_t st)
+{
+    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, st, ids, S, k, E, offsets,
+                       sorted, inv, active, n_active, units, n_units);
+    return hipGetLastError();
+}
+
+/* Unit list from offsets produced elsewhere.  Offsets that break the
+ * documented contract (non-decreasing, last == S*k) cannot make it write past
+ * max_units units; the FFN kernels bound positions separately. */
+__global__ __launch_bounds__(kDispThreads) void schedule_kernel(const int32_t* __restrict__ offsets,
+                                                                int32_t n_mat, int32_t max_units,
+                                                                Unit* __restrict__ units,
+                                                                int32_t* __restrict__ n_units)
+{
+    __shared__ int32_t tmp[kDispWaves + 1];
+    const int e = threadIdx.x;
+    const int32_t off = e < n_mat ? offsets[e] : 0;
+    const int32_t c = e < n_mat ? max(0, offsets[e + 1] - off) : 0;
+    const int32_t nu = (c + kUnitTokens - 1) / kUnitTokens;
+    int32_t tot;
+    const int32_t ubase = block_exclusive_scan(nu, tmp, &tot);
+    if (e < n_mat)
+        emit_units(units, ubase, e, off, c, max_units);
+    if (e == 0)
+        *n_units = min(tot, max_units);
+}
+
+hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, int32_t max_units, Unit* units,
+                           int32_t* n_units, hipStream_t st)
+{
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kDispThreads), 0, st, offsets, n_mat,
+                       max_units, units, n_units);
+    return hipGetLastError();
+}
+
+/* ---- combine: out[t] = y_shared[t] + sum_j w[t][j] * y[inv[t*k+j]] -------- */
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ w, int32_t S,
+                                                      int32_t k, int32_t H, int32_t shared_row0,
+                                                      float* __restrict__ out)
+{
+    const int64_t n4 = H / 4;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)S * n4)
+        return;
+    const int32_t t = (int32_t)(gid / n4);
+    const int64_t c = gid - (int64_t)t * n4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (shared_row0 >= 0)
+        acc = reinterpret_cast<const float4*>(y + (int64_t)(shared_row0 + t) * H)[c];
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = t * k + j;
+        const float wj = w[p];
+        const float4 v = reinterpret_cast<const float4*>(y + (int64_t)inv[p] * H)[c];
+        acc.x = __builtin_fmaf(wj, v.x, acc.x);
+        acc.y = __builtin_fmaf(wj, v.y, acc.y);
+        acc.z = __builtin_fmaf(wj, v.z, acc.z);
+        acc.w = __builtin_fmaf(wj, v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(out + (int64_t)t * H)[c] = acc;
+}
+
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int32_t S, int32_t k,
+                          int32_t H, int32_t shared_row0, float* out, hipStream_t st)
+{
+    if (S == 0)
+        return hipSuccess;
+    int64_t threads = (int64_t)S * (H / 4);
+    hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, y,
+                       inv, w, S, k, H, shared_row0, out);
+    return hipGetLastError();
+}
+
+} // namespace coli

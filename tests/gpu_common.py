@@ -1,0 +1,64 @@
+"""Shared helpers of the GPU parity tests: moving generated layers to the
+device, gap-checked activations, and the output tolerance."""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+# Routing-score gap below which a token's draw is replaced (the oracle's k-th
+# minus (k+1)-th selection score must exceed it; GPU and oracle logits differ
+# by fp32 summation order only, orders of magnitude less).
+GAP = 1e-5
+# Final outputs: max |gpu - oracle| <= REL_TOL * RMS(oracle output).
+REL_TOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(L: synth.Layer):
+    import quantized_routed_expert_sigmoid_amd as qre
+
+    def qb(b):
+        return qre.QBank(b.storage.cuda().contiguous(), b.scale_storage.cuda().contiguous(), b.bits)
+    w = L.w
+    shared = [qb(L.sh_gate), qb(L.sh_up), qb(L.sh_down)] if w.has_shared else None
+    return qre.MoELayer(w.hidden, w.inter, w.n_experts, w.top_k, w.rsf,
+                        L.router_w.cuda().contiguous(), L.bias.cuda().contiguous(),
+                        qb(L.gate), qb(L.up), qb(L.down), shared)
+
+
+def gapped_activations(w: synth.Workload, router_w, bias, S=None, tag=""):
+    """Activations whose oracle routing gaps all exceed GAP (redrawing a
+    token's row with the next attempt number until they do)."""
+    S = w.S if S is None else S
+    attempts = {}
+    x = synth.activations(w, S, tag=tag).numpy()
+    W, b = router_w.cpu().numpy(), bias.cpu().numpy()
+    for t in range(S):
+        a = 0
+        while True:
+            r = oracle.route_token(x[t], W, b, w.top_k, w.rsf)
+            if r["gap"] > GAP:
+                break
+            a += 1
+            x[t] = synth.token_activation(w, t, a, tag).numpy()
+        if a:
+            attempts[t] = a
+    return torch.from_numpy(x), attempts
+
+
+def assert_close_rms(gpu_out, ref_out, what=""):
+    ref = np.asarray(ref_out, dtype=np.float64)
+    got = np.asarray(gpu_out, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert err <= REL_TOL * rms, f"{what}: max|diff| {err:.3e} > {REL_TOL} * rms {rms:.3e}"
+    return err / rms if rms > 0 else 0.0

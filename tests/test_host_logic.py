@@ -1,0 +1,168 @@
+"""Host-side checks of the GPU library that need no GPU: the container
+unpacking logic of its kernels (compiled for the CPU against emulated
+instructions) versus the oracle, and the C ABI's exports and argument
+validation (every error path returns before any HIP call)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HARNESS_SRC = os.path.join(ROOT, "tests", "qdot_harness.cpp")
+
+
+@pytest.fixture(scope="module")
+def harness(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("harness") / "libqdot_harness.so")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-o", out, HARNESS_SRC], check=True)
+    lib = ctypes.CDLL(out)
+    lib.harness_block_partial.restype = ctypes.c_int32
+    lib.harness_block_partial.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+@pytest.mark.parametrize("bits,lo,hi", [(8, -127, 127), (4, -8, 7), (2, -2, 1)])
+def test_kernel_unpack_matches_oracle_partials(harness, bits, lo, hi):
+    rng = np.random.default_rng(7 + bits)
+    K = 32 * 64
+    for trial in range(8):
+        codes = rng.integers(lo, hi + 1, size=K).astype(np.int8)
+        if trial == 0:
+            codes[:] = lo  # extreme values
+        if trial == 1:
+            codes[:] = hi
+        row = oracle.pack_row(codes, bits)
+        q = rng.integers(-127, 128, size=K).astype(np.int8)
+        if trial == 2:
+            q[:] = -127
+        bb = 4 * bits  # bytes per 32-element block
+        for b in range(K // 32):
+            wblk = np.ascontiguousarray(row[b * bb:(b + 1) * bb])
+            qb = np.ascontiguousarray(q[32 * b:32 * (b + 1)])
+            got = harness.harness_block_partial(bits, wblk.ctypes.data, qb.ctypes.data)
+            assert got == oracle.block_partial(row, bits, q, b), (trial, b)
+
+
+# ---------------------------------------------------------------------------
+# C ABI: exports and validation (no kernel is launched by any call below)
+# ---------------------------------------------------------------------------
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "colibri.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(colibri_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def capi():
+    import quantized_routed_expert_sigmoid_amd as qre
+    return qre
+
+
+def test_library_exports_every_declared_symbol(capi):
+    lib = capi.lib()
+    syms = _declared_symbols()
+    assert len(syms) == 9
+    for name in syms:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(capi):
+    for code in range(5):
+        assert capi.status_string(code)
+    assert capi.status_string(99) == "unknown status"
+
+
+def _fake_layer(capi, **over):
+    """A descriptor with plausible (fake, never dereferenced) device pointers."""
+    H, I, E, k = 256, 128, 16, 2
+    fake = 0x10000000
+
+    def bank(n, rows, K, q=8):
+        return capi.QBankDesc(fake, fake, n, rows, K, q)
+    d = dict(hidden=H, inter=I, n_experts=E, top_k=k, rsf=1.0, router_w=fake, router_bias=fake,
+             gate=bank(E, I, H), up=bank(E, I, H), down=bank(E, H, I), has_shared=1,
+             sh_gate=bank(1, I, H), sh_up=bank(1, I, H), sh_down=bank(1, H, I))
+    d.update(over)
+    return capi.LayerDesc(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["rsf"],
+                          d["router_w"], d["router_bias"], d["gate"], d["up"], d["down"],
+                          d["has_shared"], d["sh_gate"], d["sh_up"], d["sh_down"])
+
+
+def test_workspace_size_and_invalid_layers(capi):
+    lib = capi.lib()
+    L = _fake_layer(capi)
+    n8 = lib.colibri_workspace_bytes(ctypes.byref(L), 8)
+    n1 = lib.colibri_workspace_bytes(ctypes.byref(L), 1)
+    assert n8 > n1 > 0 and n8 % 256 == 0
+    for bad in (dict(hidden=250), dict(inter=0), dict(top_k=17), dict(top_k=0), dict(n_experts=0),
+                dict(router_w=0), dict(gate=capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 255, 8)),
+                dict(gate=capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 256, 3)),
+                dict(gate=capi.QBankDesc(0x10000008, 0x10000000, 16, 128, 256, 8)),
+                dict(down=capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 128, 4)),
+                dict(sh_down=capi.QBankDesc(0x10000000, 0x10000000, 2, 256, 128, 8))):
+        Lb = _fake_layer(capi, **bad)
+        assert lib.colibri_workspace_bytes(ctypes.byref(Lb), 8) == 0, bad
+    assert lib.colibri_workspace_bytes(None, 8) == 0
+    assert lib.colibri_workspace_bytes(ctypes.byref(L), -1) == 0
+
+
+def test_layer_forward_error_paths(capi):
+    lib = capi.lib()
+    L = _fake_layer(capi)
+    fake = 0x20000000
+    need = lib.colibri_workspace_bytes(ctypes.byref(L), 8)
+    f = lib.colibri_moe_layer_forward
+    assert f(None, fake, 8, fake, fake, need, None) == capi.COLI_E_INVAL
+    assert f(ctypes.byref(L), fake, -1, fake, fake, need, None) == capi.COLI_E_INVAL
+    assert f(ctypes.byref(L), fake, 0, fake, fake, need, None) == capi.COLI_OK  # empty batch: no-op
+    assert f(ctypes.byref(L), None, 8, fake, fake, need, None) == capi.COLI_E_INVAL
+    assert f(ctypes.byref(L), fake, 8, None, fake, need, None) == capi.COLI_E_INVAL
+    assert f(ctypes.byref(L), fake, 8, fake, None, need, None) == capi.COLI_E_INVAL
+    assert f(ctypes.byref(L), fake + 4, 8, fake, fake, need, None) == capi.COLI_E_UNSUPPORTED
+    assert f(ctypes.byref(L), fake, 8, fake, fake + 16, need, None) == capi.COLI_E_UNSUPPORTED
+    assert f(ctypes.byref(L), fake, 8, fake, fake, need - 1, None) == capi.COLI_E_WORKSPACE
+    assert f(ctypes.byref(L), fake, 70000, fake, fake, 1 << 40, None) == capi.COLI_E_UNSUPPORTED
+    Lq = _fake_layer(capi, up=capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 256, 4))
+    assert f(ctypes.byref(Lq), fake, 8, fake, fake, need, None) == capi.COLI_E_UNSUPPORTED
+    Lk = _fake_layer(capi, top_k=65, n_experts=100,
+                     gate=capi.QBankDesc(0x10000000, 0x10000000, 100, 128, 256, 8))
+    assert f(ctypes.byref(Lk), fake, 8, fake, fake, need, None) == capi.COLI_E_UNSUPPORTED
+
+
+def test_stage_calls_error_paths(capi):
+    lib = capi.lib()
+    L = _fake_layer(capi)
+    fake = 0x20000000
+    need = lib.colibri_workspace_bytes(ctypes.byref(L), 4)
+    assert lib.colibri_quantize_q8_0(fake, 4, 250, fake, fake, None) == capi.COLI_E_INVAL
+    assert lib.colibri_quantize_q8_0(fake, -1, 256, fake, fake, None) == capi.COLI_E_INVAL
+    assert lib.colibri_quantize_q8_0(fake, 0, 256, fake, fake, None) == capi.COLI_OK
+    assert lib.colibri_quantize_q8_0(None, 4, 256, fake, fake, None) == capi.COLI_E_INVAL
+    assert lib.colibri_quantize_q8_0(fake + 8, 4, 256, fake, fake, None) == capi.COLI_E_UNSUPPORTED
+    assert lib.colibri_route(ctypes.byref(L), fake, 4, None, fake, fake, need, None) == capi.COLI_E_INVAL
+    assert lib.colibri_route(ctypes.byref(L), fake, 4, fake, fake, fake, need - 256, None) == capi.COLI_E_WORKSPACE
+    assert lib.colibri_route(ctypes.byref(L), fake, 0, fake, fake, fake, 0, None) == capi.COLI_OK
+    d = lib.colibri_moe_dispatch
+    assert d(fake, 4, 3, 2, fake, fake, fake, fake, None, 0, None) == capi.COLI_E_INVAL  # k > E
+    assert d(fake, 4, 2, 2000, fake, fake, fake, fake, None, 0, None) == capi.COLI_E_UNSUPPORTED
+    assert d(fake, 4, 2, 16, None, fake, fake, fake, None, 0, None) == capi.COLI_E_INVAL
+    assert d(fake, -2, 2, 16, fake, fake, fake, fake, None, 0, None) == capi.COLI_E_INVAL
+    g = capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 256, 8)
+    dn = capi.QBankDesc(0x10000000, 0x10000000, 16, 256, 128, 8)
+    wsz = lib.colibri_expert_ffn_workspace_bytes(ctypes.byref(g), ctypes.byref(dn), 4, 2)
+    assert wsz > 0
+    ffn = lib.colibri_expert_ffn_q
+    args = [ctypes.byref(g), ctypes.byref(g), ctypes.byref(dn), fake, fake, 4, fake, fake, 2, fake, fake]
+    assert ffn(*args, wsz - 1, None) == capi.COLI_E_WORKSPACE
+    bad_up = capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 256, 2)
+    assert ffn(ctypes.byref(g), ctypes.byref(bad_up), ctypes.byref(dn), *args[3:], wsz, None) == capi.COLI_E_UNSUPPORTED
+    bad_dn = capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 128, 8)
+    assert ffn(ctypes.byref(g), ctypes.byref(g), ctypes.byref(bad_dn), *args[3:], wsz, None) == capi.COLI_E_INVAL
+    assert ffn(*args[:9], None, fake, wsz, None) == capi.COLI_E_INVAL
