@@ -69,12 +69,11 @@ def test_route_parity(qre, case):
     say(f"route case={case} S={w.S} E={w.n_experts} k={w.top_k}")
     x, _ = gapped_activations(w, L.router_w, L.bias)
     ids_ref, w_ref, _ = oracle.route(x.numpy(), L.router_w, L.bias, w.top_k, w.rsf)
-    # a descriptor needs banks; reuse tiny fake-free ones only for the router fields
+    # a layer descriptor needs expert banks: give the full-size router small ones
     if L.gate is None:
-        dummy = synth.scaled(synth.WORKLOADS["tiny"], name="dummy", hidden=w.hidden, inter=32,
-                             n_experts=w.n_experts, top_k=w.top_k, layer="dummy")
-        D = synth.make_layer(synth.scaled(dummy, n_experts=w.n_experts))
-        L = synth.Layer(w, L.router_w, L.bias, D.gate, D.up, D.down, None, None, None)
+        wd = synth.scaled(w, name="router_dummy", layer="router_dummy", inter=32, has_shared=False, bits=2)
+        D = synth.make_layer(wd)
+        L = synth.Layer(wd, L.router_w, L.bias, D.gate, D.up, D.down, None, None, None)
     dev = to_device(L)
     ids, wts = qre.route(dev, x.cuda())
     torch.cuda.synchronize()
