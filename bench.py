@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one elementwise fp32 copy of this many MiB (a known-size kernel "
+                         "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -168,6 +171,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     qre.lib()
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     steps = args.steps or (2000 if w.S <= 8 else 50)
     res = run_workload(qre, synth, torch, w, steps, args.warmup, args.copies)

@@ -72,6 +72,7 @@ enum { COLI_Q8 = 8, COLI_Q4 = 4, COLI_Q2 = 2 };
 #define COLI_MAX_TOPK 64
 #define COLI_MAX_TOKENS 65536
 #define COLI_MAX_PAIRS (1 << 20) /* S * top_k */
+#define COLI_MAX_DIM 8192        /* hidden and inter */
 
 /*
  * A bank of n_mat quantised matrices, each [rows][K] row-major, one fp32 scale
@@ -166,8 +167,12 @@ int colibri_moe_dispatch(const int32_t* topk_ids, int32_t S, int32_t k, int32_t 
  *   u[r] likewise with up;  h[r] = silu(g[r]) * u[r];  h -> Q8_0 (hq, hd)
  *   y[i][n] = down.row_scale[e][n] * F(down row (e, n), hq, hd)       (n < H)
  * where F folds the exact int32 block partials S_b = sum over 32 elements of
- * weight code * activation code, acc = fmaf(d_b, (float)S_b, acc) in ascending
- * block order from +0.  silu(g) = g / (1 + exp(-g)) with exp by Cody-Waite
+ * weight code * activation code: the nb = K/32 blocks form four consecutive
+ * groups (group g: blocks floor(g*nb/4) .. floor((g+1)*nb/4)-1), each folded
+ * acc = fmaf(d_b, (float)S_b, acc) in ascending block order from +0, and the
+ * four group sums are added left to right (the pages leave the order of the
+ * fp32 accumulation open; this one is fixed so that results are bit-exact
+ * across batch sizes and kernels).  silu(g) = g / (1 + exp(-g)) with exp by Cody-Waite
  * reduction and a degree-7 Taylor polynomial (+inf above 88, +0 below -87).
  * xq int8 [S][hidden] and xd fp32 [S][hidden/32] come from
  * colibri_quantize_q8_0; offsets / pairs from colibri_moe_dispatch (or, for a

@@ -85,9 +85,11 @@ void ref_pack_row(const int8_t* codes, int32_t K, int32_t bits, uint8_t* out);
 /* ---- integer dot path ---- */
 /* Exact int32 partial of block b: sum over 32 elements of weight * code. */
 int32_t ref_block_partial(const uint8_t* row, int32_t bits, const int8_t* q, int32_t b);
-/* Canonical quantised row dot: fold the K/32 block partials in ascending
- * block order, acc = fmaf(d_b, (float)S_b, acc) starting from +0, then one
- * multiply by the row scale. */
+/* Canonical quantised row dot: the nb = K/32 block partials are folded in
+ * four consecutive groups (group g: blocks floor(g*nb/4) .. floor((g+1)*nb/4)-1),
+ * each acc = fmaf(d_b, (float)S_b, acc) from +0 in ascending block order; the
+ * four group sums are added left to right; then one multiply by the row
+ * scale. */
 float ref_qdot(const uint8_t* row, int32_t bits, float row_scale,
                const int8_t* q, const float* d, int32_t K);
 /* The same quantity, unblocked, in fp64 (used to bound the fp32 fold). */

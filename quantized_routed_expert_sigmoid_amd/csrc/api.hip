@@ -42,7 +42,7 @@ int check_dims(int32_t H, int32_t I)
 {
     if (H <= 0 || I <= 0 || H % 32 != 0 || I % 32 != 0)
         return COLI_E_INVAL;
-    if (H > (1 << 20) || I > (1 << 20))
+    if (H > COLI_MAX_DIM || I > COLI_MAX_DIM)
         return COLI_E_UNSUPPORTED;
     return COLI_OK;
 }
@@ -322,6 +322,7 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
     a.seg[0] = routed_seg(gate, up, down, sorted_pairs, units, n_units, k, S, rows, maxu, 0);
     a.seg[1] = a.seg[0];
     a.nseg = 1;
+    a.unit_tokens = kUnitTokens; /* caller offsets: units may hold several tokens */
     a.H = H;
     a.I = I;
     a.xq = xq;
@@ -384,20 +385,27 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     };
     hipError_t e = mark(0, hipSuccess);
     if (e == hipSuccess)
-        e = launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
-    if (e == hipSuccess)
+        e = S <= kSmallS
+                ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
+                : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
+    if (e == hipSuccess && S > kSmallS)
         e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && S > kSmallS)
         e = launch_router_select(logits, L->router_bias, S, E, k, L->routed_scaling_factor, ids, w, s);
     e = mark(1, e);
     if (e == hipSuccess)
-        e = launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, s);
+        e = S <= kSmallS
+                ? launch_select_dispatch_small(logits, L->router_bias, S, E, k, L->routed_scaling_factor,
+                                               ids, w, offsets, sorted, inv, active, n_active, units,
+                                               n_units, s)
+                : launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, s);
     e = mark(2, e);
 
     FfnArgs a;
     a.seg[0] = routed_seg(&L->gate, &L->up, &L->down, sorted, units, n_units, k, S, P,
                           max_routed_units(P, E), 0);
     a.nseg = 1;
+    a.unit_tokens = S == 1 ? 1 : kUnitTokens; /* distinct experts per token */
     a.H = H;
     a.I = I;
     a.xq = xq;

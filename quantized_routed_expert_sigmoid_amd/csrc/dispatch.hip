@@ -14,6 +14,7 @@
  */
 #include "device_common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace coli {
 
@@ -69,15 +70,24 @@ __device__ __forceinline__ void emit_units(Unit* units, int32_t ubase, int32_t e
     }
 }
 
-__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
-    const int32_t* __restrict__ ids, int32_t S, int32_t k, int32_t E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
-    int32_t* __restrict__ n_active, Unit* __restrict__ units, int32_t* __restrict__ n_units)
+struct DispatchShared {
+    int32_t cnt[kMaxE];
+    int32_t base[kMaxE];
+    uint8_t wcnt[kDispWaves][kMaxE];
+    int32_t tmp[kDispWaves + 1];
+};
+
+/* The dispatch, run by all 1024 threads of a workgroup.  `ids` may point to
+ * global memory or to LDS. */
+__device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int32_t k, int32_t E,
+                                              int32_t* offsets, int32_t* sorted, int32_t* inv,
+                                              int32_t* active, int32_t* n_active, Unit* units,
+                                              int32_t* n_units, DispatchShared& sh)
 {
-    __shared__ int32_t cnt[kMaxE];
-    __shared__ int32_t base[kMaxE];
-    __shared__ uint8_t wcnt[kDispWaves][kMaxE];
-    __shared__ int32_t tmp[kDispWaves + 1];
+    int32_t* cnt = sh.cnt;
+    int32_t* base = sh.base;
+    auto& wcnt = sh.wcnt;
+    int32_t* tmp = sh.tmp;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int32_t P = S * k;
 
@@ -158,12 +168,51 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     }
 }
 
+__global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
+    const int32_t* __restrict__ ids, int32_t S, int32_t k, int32_t E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
+    int32_t* __restrict__ n_active, Unit* __restrict__ units, int32_t* __restrict__ n_units)
+{
+    __shared__ DispatchShared sh;
+    dispatch_body(ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, sh);
+}
+
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, int32_t* offsets,
                            int32_t* sorted, int32_t* inv, int32_t* active, int32_t* n_active,
                            Unit* units, int32_t* n_units, hipStream_t st)
 {
     hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, st, ids, S, k, E, offsets,
                        sorted, inv, active, n_active, units, n_units);
+    return hipGetLastError();
+}
+
+/* Small batches (S <= kSmallS): wave t selects token t's experts (select.h),
+ * then the whole workgroup dispatches the S*k pairs from LDS. */
+__global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
+    const float* __restrict__ logits, const float* __restrict__ bias, int32_t S, int32_t E, int32_t k,
+    float rsf, int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
+    int32_t* __restrict__ n_active, Unit* __restrict__ units, int32_t* __restrict__ n_units)
+{
+    __shared__ DispatchShared sh;
+    __shared__ float sel_s[kSmallS][64];
+    __shared__ int32_t sel_ids[kSmallS * 64];
+    const int wv = threadIdx.x >> 6;
+    if (wv < S)
+        select_token(logits + (int64_t)wv * E, bias, E, k, rsf, ids + (int64_t)wv * k,
+                     weights + (int64_t)wv * k, sel_s[wv], sel_ids + wv * k);
+    __syncthreads();
+    dispatch_body(sel_ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, sh);
+}
+
+hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
+                                        int32_t k, float rsf, int32_t* ids, float* weights,
+                                        int32_t* offsets, int32_t* sorted, int32_t* inv,
+                                        int32_t* active, int32_t* n_active, Unit* units,
+                                        int32_t* n_units, hipStream_t st)
+{
+    hipLaunchKernelGGL(select_dispatch_small, dim3(1), dim3(kDispThreads), 0, st, logits, bias, S, E, k,
+                       rsf, ids, weights, offsets, sorted, inv, active, n_active, units, n_units);
     return hipGetLastError();
 }
 

@@ -106,21 +106,36 @@ __device__ __forceinline__ int token_of(const FfnSeg& sg, int pos)
     return min(max(tok, 0), sg.S - 1);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+/* Weight loads are streamed once per call: nontemporal loads keep them from
+ * displacing reused data in the caches (measured +5-10% read bandwidth). */
 template <int BITS>
 __device__ __forceinline__ void load_block(const uint8_t* p, uint32_t (&w)[BITS])
 {
     if constexpr (BITS == 8) {
-        const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-        const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
         w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     } else if constexpr (BITS == 4) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     } else {
-        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
         w[0] = a.x; w[1] = a.y;
     }
+}
+
+/* Orders one wave's LDS writes before its following LDS reads by other lanes
+ * of the same wave.  A wave's LDS instructions execute in issue order, so only
+ * the compiler has to be kept from moving accesses across this point. */
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ void load_codes(const int8_t* p, uint32_t (&x)[8])
@@ -138,70 +153,169 @@ __device__ __forceinline__ int part_index(int t, int o, int rho, int writer)
     return t * 512 + o * 64 + 8 * ((rho + o) & 7) + ((writer + o) & 7);
 }
 
-/* The K loop shared by both kernels: rows of this lane's octet start at
- * row0 (8 consecutive rows, rowbytes apart); act(t) gives token t's codes,
- * scl(t) its block scales; `rows_ok` masks rows past the matrix end.
- * Returns the folded accumulators of row (8o + lane-in-octet). */
+/* Waves per job: wave g computes fold group g (see block_group). */
+constexpr int kGroups = 4;
+
+/* First block of fold group g out of nb blocks: the canonical fold adds four
+ * consecutive groups of blocks, each folded from +0 in ascending order. */
+__device__ __forceinline__ int block_group(int g, int nb)
+{
+    return (g * nb) / kGroups;
+}
+
+/* Blocks of one fold group that a wave stages in LDS (K <= 8192). */
+constexpr int kMaxGroupBlocks = 64;
+
 template <int BITS>
-__device__ __forceinline__ void k_loop(const uint8_t* row0, int64_t rowbytes, int nb, int ntok,
-                                       const int8_t* const (&act)[kUnitTokens],
-                                       const float* const (&scl)[kUnitTokens], int rows_ok,
-                                       int32_t* part, float (&acc)[kUnitTokens])
+struct StepWeights {
+    uint32_t w[8][BITS];
+};
+
+/* LDS owned by one wave of a job: the partial transpose area, and the wave's
+ * fold group of activation codes (already in block_partial operand order) and
+ * block scales for each token of the unit. */
+template <int TMAX>
+struct WaveLds {
+    int32_t part[TMAX * 512];
+    uint32_t xa[TMAX][kMaxGroupBlocks][8];
+    float d[TMAX][kMaxGroupBlocks];
+};
+
+/* Loads this lane's block of each of its octet's 8 rows for one K step. */
+template <int BITS>
+__device__ __forceinline__ void load_step(StepWeights<BITS>& W, const uint8_t* row0, int64_t rowbytes,
+                                          int b, bool valid, int rows_ok)
+{
+#pragma unroll
+    for (int rho = 0; rho < 8; ++rho) {
+        if (valid && rho < rows_ok) {
+            load_block<BITS>(row0 + rho * rowbytes + (int64_t)b * (4 * BITS), W.w[rho]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < BITS; ++i)
+                W.w[rho][i] = 0;
+        }
+    }
+}
+
+/* Stages the codes and scales of blocks [b_begin, b_end) of every token into
+ * the wave's LDS (one block per lane), once per job. */
+template <int BITS, int TMAX>
+__device__ __forceinline__ void stage_activations(WaveLds<TMAX>& L, int b_begin, int b_end, int ntok,
+                                                  const int8_t* const (&act)[TMAX],
+                                                  const float* const (&scl)[TMAX])
+{
+    const int lane = threadIdx.x & 63;
+    const int b = b_begin + lane;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < ntok && b < b_end) {
+            uint32_t x[8], xa[8];
+            load_codes(act[t] + (int64_t)b * 32, x);
+            prep_activation<BITS>(x, xa);
+            uint4* dst = reinterpret_cast<uint4*>(L.xa[t][lane]);
+            dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+            dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+            L.d[t][lane] = scl[t][b];
+        }
+    }
+    wave_lds_sync();
+}
+
+/* Block partials of K step st of the wave's group (nblk blocks), transposed
+ * through the wave's LDS, folded into acc (lane = row 8o + j of the octet). */
+template <int BITS, int TMAX>
+__device__ __forceinline__ void fold_step(const StepWeights<BITS>& W, int st, int nblk, int ntok,
+                                          WaveLds<TMAX>& L, float (&acc)[TMAX])
 {
     const int lane = threadIdx.x & 63;
     const int o = lane >> 3, j8 = lane & 7;
-    for (int s = 0; s < nb; s += 8) {
-        const int b = s + j8;
-        const bool valid = b < nb;
-        uint32_t w[8][BITS];
+    const int lb = 8 * st + j8;
+    const bool valid = lb < nblk;
 #pragma unroll
-        for (int rho = 0; rho < 8; ++rho) {
-            if (valid && rho < rows_ok) {
-                load_block<BITS>(row0 + rho * rowbytes + (int64_t)b * (4 * BITS), w[rho]);
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < ntok) {
+            uint32_t xa[8];
+            if (valid) {
+                const uint4* src = reinterpret_cast<const uint4*>(L.xa[t][lb]);
+                const uint4 u0 = src[0], u1 = src[1];
+                xa[0] = u0.x; xa[1] = u0.y; xa[2] = u0.z; xa[3] = u0.w;
+                xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
             } else {
 #pragma unroll
-                for (int i = 0; i < BITS; ++i)
-                    w[rho][i] = 0;
+                for (int i = 0; i < 8; ++i)
+                    xa[i] = 0;
             }
+#pragma unroll
+            for (int rho = 0; rho < 8; ++rho)
+                L.part[part_index(t, o, rho, j8)] = block_partial<BITS>(W.w[rho], xa);
         }
+    }
+    wave_lds_sync();
+    const int nbs = max(0, min(8, nblk - 8 * st));
 #pragma unroll
-        for (int t = 0; t < kUnitTokens; ++t) {
-            if (t < ntok) {
-                uint32_t x[8], xa[8];
-                if (valid) {
-                    load_codes(act[t] + (int64_t)b * 32, x);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        x[i] = 0;
-                }
-                prep_activation<BITS>(x, xa);
-#pragma unroll
-                for (int rho = 0; rho < 8; ++rho)
-                    part[part_index(t, o, rho, j8)] = block_partial<BITS>(w[rho], xa);
-            }
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < ntok) {
+            for (int jj = 0; jj < nbs; ++jj)
+                acc[t] = __builtin_fmaf(L.d[t][8 * st + jj], (float)L.part[part_index(t, o, j8, jj)], acc[t]);
         }
-        __syncthreads();
-        const int nbs = min(8, nb - s);
-#pragma unroll
-        for (int t = 0; t < kUnitTokens; ++t) {
-            if (t < ntok) {
-                const float* d = scl[t] + s;
-                for (int jj = 0; jj < nbs; ++jj)
-                    acc[t] = __builtin_fmaf(d[jj], (float)part[part_index(t, o, j8, jj)], acc[t]);
-            }
+    }
+    wave_lds_sync();
+}
+
+/* The K loop of one wave over its fold group, blocks [b_begin, b_end), in
+ * steps of 8 blocks, the next step's weight loads issued before the current
+ * step is computed.  Waves of a workgroup run their loops independently. */
+template <int BITS, int TMAX>
+__device__ __forceinline__ void k_loop(const uint8_t* row0, int64_t rowbytes, int b_begin, int b_end,
+                                       int ntok, int rows_ok, WaveLds<TMAX>& L, float (&acc)[TMAX])
+{
+    const int j8 = threadIdx.x & 7;
+    const int nblk = b_end - b_begin;
+    const int nsteps = (nblk + 7) / 8;
+    StepWeights<BITS> A, B;
+    if (nsteps > 0)
+        load_step<BITS>(A, row0, rowbytes, b_begin + j8, j8 < nblk, rows_ok);
+    for (int st = 0; st < nsteps; st += 2) {
+        const int l1 = 8 * (st + 1) + j8, l2 = 8 * (st + 2) + j8;
+        if (st + 1 < nsteps)
+            load_step<BITS>(B, row0, rowbytes, b_begin + l1, l1 < nblk, rows_ok);
+        fold_step<BITS, TMAX>(A, st, nblk, ntok, L, acc);
+        if (st + 1 < nsteps) {
+            if (st + 2 < nsteps)
+                load_step<BITS>(A, row0, rowbytes, b_begin + l2, l2 < nblk, rows_ok);
+            fold_step<BITS, TMAX>(B, st + 1, nblk, ntok, L, acc);
         }
-        __syncthreads();
+    }
+}
+
+/* Adds the four group sums of each row in order; valid on wave 0 only. */
+template <int TMAX>
+__device__ __forceinline__ void sum_groups(float (*gsum)[TMAX][64], float (&acc)[TMAX])
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+        gsum[wv][t][lane] = acc[t];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        float v = gsum[0][t][lane];
+        v = v + gsum[1][t][lane];
+        v = v + gsum[2][t][lane];
+        v = v + gsum[3][t][lane];
+        acc[t] = v;
     }
 }
 
 } // namespace
 
-template <int BITS>
-__global__ __launch_bounds__(64) void ffn_gate_up_gemv(FfnArgs a)
+template <int BITS, int TMAX>
+__global__ __launch_bounds__(256) void ffn_gate_up_gemv(FfnArgs a)
 {
-    __shared__ int32_t part[kUnitTokens * 512];
-    const int lane = threadIdx.x;
+    __shared__ WaveLds<TMAX> lds[kGroups];
+    __shared__ float gsum[kGroups][TMAX][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int o = lane >> 3;
     const int RB = a.I / 32;
     JobLoc L;
@@ -211,30 +325,36 @@ __global__ __launch_bounds__(64) void ffn_gate_up_gemv(FfnArgs a)
     int e, pos0, ntok;
     if (!unit_info(sg, L.unit, e, pos0, ntok))
         return;
+    ntok = min(ntok, TMAX);
     const int nb = a.H / 32;
     const int64_t rowbytes = (int64_t)a.H * BITS / 8;
-    const int8_t* act[kUnitTokens];
-    const float* scl[kUnitTokens];
+    const int8_t* act[TMAX];
+    const float* scl[TMAX];
 #pragma unroll
-    for (int t = 0; t < kUnitTokens; ++t) {
+    for (int t = 0; t < TMAX; ++t) {
         const int tok = token_of(sg, pos0 + (t < ntok ? t : 0));
         act[t] = a.xq + (int64_t)tok * a.H;
         scl[t] = a.xd + (int64_t)tok * nb;
     }
+    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
+    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
     /* octets 0..3: gate rows rb*32 + 8o ..; octets 4..7: the same up rows */
     const uint8_t* row0 = (o < 4 ? sg.gate_w : sg.up_w) +
                           ((int64_t)e * a.I + L.rb * 32 + 8 * (o & 3)) * rowbytes;
-    float acc[kUnitTokens];
+    float acc[TMAX];
 #pragma unroll
-    for (int t = 0; t < kUnitTokens; ++t)
+    for (int t = 0; t < TMAX; ++t)
         acc[t] = 0.0f;
-    k_loop<BITS>(row0, rowbytes, nb, ntok, act, scl, 8, part, acc);
+    k_loop<BITS, TMAX>(row0, rowbytes, b0, b1, ntok, 8, lds[wv], acc);
+    sum_groups<TMAX>(gsum, acc);
+    if (wv != 0)
+        return;
 
     const int r = L.rb * 32 + (lane & 31);
     const float sc = (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
     const int nbi = a.I / 32;
 #pragma unroll
-    for (int t = 0; t < kUnitTokens; ++t) {
+    for (int t = 0; t < TMAX; ++t) {
         if (t < ntok) {
             const float v = sc * acc[t];
             const float u = shfl_xor(v, 32);
@@ -253,11 +373,12 @@ __global__ __launch_bounds__(64) void ffn_gate_up_gemv(FfnArgs a)
     }
 }
 
-template <int BITS>
-__global__ __launch_bounds__(64) void ffn_down_gemv(FfnArgs a)
+template <int BITS, int TMAX>
+__global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
 {
-    __shared__ int32_t part[kUnitTokens * 512];
-    const int lane = threadIdx.x;
+    __shared__ WaveLds<TMAX> lds[kGroups];
+    __shared__ float gsum[kGroups][TMAX][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int o = lane >> 3;
     const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
     JobLoc L;
@@ -267,30 +388,36 @@ __global__ __launch_bounds__(64) void ffn_down_gemv(FfnArgs a)
     int e, pos0, ntok;
     if (!unit_info(sg, L.unit, e, pos0, ntok))
         return;
+    ntok = min(ntok, TMAX);
     const int nb = a.I / 32;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
-    const int8_t* act[kUnitTokens];
-    const float* scl[kUnitTokens];
+    const int8_t* act[TMAX];
+    const float* scl[TMAX];
 #pragma unroll
-    for (int t = 0; t < kUnitTokens; ++t) {
+    for (int t = 0; t < TMAX; ++t) {
         const int64_t row_in = sg.out_base + pos0 + (t < ntok ? t : 0);
         act[t] = a.hq + row_in * a.I;
         scl[t] = a.hd + row_in * nb;
     }
+    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
+    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
     const int first = L.rb * kRowsPerJob + 8 * o;
     const int rows_ok = min(8, max(0, a.H - first));
     const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + first) * rowbytes;
-    float acc[kUnitTokens];
+    float acc[TMAX];
 #pragma unroll
-    for (int t = 0; t < kUnitTokens; ++t)
+    for (int t = 0; t < TMAX; ++t)
         acc[t] = 0.0f;
-    k_loop<BITS>(row0, rowbytes, nb, ntok, act, scl, rows_ok, part, acc);
+    k_loop<BITS, TMAX>(row0, rowbytes, b0, b1, ntok, rows_ok, lds[wv], acc);
+    sum_groups<TMAX>(gsum, acc);
+    if (wv != 0)
+        return;
 
     const int n = L.rb * kRowsPerJob + lane;
     if (n < a.H) {
         const float sc = sg.down_s[(int64_t)e * a.H + n];
 #pragma unroll
-        for (int t = 0; t < kUnitTokens; ++t)
+        for (int t = 0; t < TMAX; ++t)
             if (t < ntok)
                 a.y[(int64_t)(sg.out_base + pos0 + t) * a.H + n] = sc * acc[t];
     }
@@ -304,17 +431,37 @@ static int64_t total_jobs(const FfnArgs& a, int RB)
     return n;
 }
 
+template <int TMAX>
+static void launch_gate_up_t(const FfnArgs& a, int32_t bits, dim3 grid, hipStream_t st)
+{
+    const dim3 block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL((ffn_gate_up_gemv<8, TMAX>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((ffn_gate_up_gemv<4, TMAX>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((ffn_gate_up_gemv<2, TMAX>), grid, block, 0, st, a); break;
+    }
+}
+
+template <int TMAX>
+static void launch_down_t(const FfnArgs& a, int32_t bits, dim3 grid, hipStream_t st)
+{
+    const dim3 block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL((ffn_down_gemv<8, TMAX>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((ffn_down_gemv<4, TMAX>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((ffn_down_gemv<2, TMAX>), grid, block, 0, st, a); break;
+    }
+}
+
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int32_t bits, hipStream_t st)
 {
     const int64_t jobs = total_jobs(a, a.I / 32);
     if (jobs == 0)
         return hipSuccess;
-    const dim3 grid((uint32_t)jobs), block(64);
-    switch (bits) {
-    case 8: hipLaunchKernelGGL(ffn_gate_up_gemv<8>, grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL(ffn_gate_up_gemv<4>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(ffn_gate_up_gemv<2>, grid, block, 0, st, a); break;
-    }
+    if (a.unit_tokens == 1)
+        launch_gate_up_t<1>(a, bits, dim3((uint32_t)jobs), st);
+    else
+        launch_gate_up_t<kUnitTokens>(a, bits, dim3((uint32_t)jobs), st);
     return hipGetLastError();
 }
 
@@ -323,12 +470,10 @@ hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st)
     const int64_t jobs = total_jobs(a, (a.H + kRowsPerJob - 1) / kRowsPerJob);
     if (jobs == 0)
         return hipSuccess;
-    const dim3 grid((uint32_t)jobs), block(64);
-    switch (bits) {
-    case 8: hipLaunchKernelGGL(ffn_down_gemv<8>, grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL(ffn_down_gemv<4>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(ffn_down_gemv<2>, grid, block, 0, st, a); break;
-    }
+    if (a.unit_tokens == 1)
+        launch_down_t<1>(a, bits, dim3((uint32_t)jobs), st);
+    else
+        launch_down_t<kUnitTokens>(a, bits, dim3((uint32_t)jobs), st);
     return hipGetLastError();
 }
 

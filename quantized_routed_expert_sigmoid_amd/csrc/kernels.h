@@ -15,6 +15,10 @@ namespace coli {
  * more tokens are split into several units. */
 constexpr int kUnitTokens = 4;
 
+/* Batches of at most this many tokens use the small-batch router kernels
+ * (a workgroup per router row; selection and dispatch in one workgroup). */
+constexpr int kSmallS = 8;
+
 /* A work unit: expert e applied to sorted positions [pos0, pos0 + ntok). */
 struct Unit {
     int32_t e, pos0, ntok, pad;
@@ -42,6 +46,7 @@ struct FfnSeg {
 struct FfnArgs {
     FfnSeg seg[2];
     int32_t nseg;
+    int32_t unit_tokens; /* most tokens any unit holds: 1 or kUnitTokens */
     int32_t H, I;
     const int8_t* xq; /* [S][H]   */
     const float* xd;  /* [S][H/32] */
@@ -72,6 +77,17 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
 hipError_t launch_router_select(const float* logits, const float* bias, int32_t S, int32_t E,
                                 int32_t k, float rsf, int32_t* ids, float* weights,
                                 hipStream_t st);
+
+/* S <= kSmallS: router logits and Q8_0 quantisation of x in one launch. */
+hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
+                                   float* logits, int8_t* xq, float* xd, hipStream_t st);
+
+/* S <= kSmallS: selection, union dispatch and unit list in one workgroup. */
+hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
+                                        int32_t k, float rsf, int32_t* ids, float* weights,
+                                        int32_t* offsets, int32_t* sorted, int32_t* inv,
+                                        int32_t* active, int32_t* n_active, Unit* units,
+                                        int32_t* n_units, hipStream_t st);
 
 /* Union dispatch; `units` / `n_units` may be null (then no unit list). */
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E,

@@ -12,6 +12,7 @@
  */
 #include "device_common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace coli {
 
@@ -54,48 +55,84 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t n_blocks, int8_t* q, flo
 }
 
 /* ---- router logits --------------------------------------------------------
- * Few tokens: one wave per expert streams its router row once (float4,
- * coalesced) and keeps one partial sum per token; wave reduction at the end.
- * Many tokens: 32 x 32 output tiles through LDS. Both sum in fp32. */
+ * Few tokens: one 256-thread workgroup per expert streams its router row once
+ * (float4, coalesced, each wave a quarter of the row), keeps one partial sum
+ * per token and reduces across lanes and waves.  Many tokens: 32 x 32 output
+ * tiles through LDS.  Both sum in fp32 (the order is free: only the
+ * selection decision depends on it, and inputs keep a score gap).
+ *
+ * With xq != nullptr the small-batch kernel also quantises x: workgroups
+ * past the E router rows each quantise 32 blocks. */
 
-constexpr int kSmallS = 8;
+__device__ __forceinline__ void quantize_blocks(const float* x, int64_t n_blocks, int8_t* q, float* d,
+                                                int64_t gid)
+{
+    const int64_t blk = gid >> 3;
+    const bool live = blk < n_blocks;
+    const float4 v = live ? reinterpret_cast<const float4*>(x)[gid] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, shfl_xor(a, 1));
+    a = fmaxf(a, shfl_xor(a, 2));
+    a = fmaxf(a, shfl_xor(a, 4));
+    if (!live)
+        return;
+    const float scale = a / 127.0f;
+    const float inv = (a == 0.0f) ? 0.0f : 1.0f / scale;
+    const uint32_t packed = (uint32_t)(q8_code(v.x, inv) & 0xFF) |
+                            ((uint32_t)(q8_code(v.y, inv) & 0xFF) << 8) |
+                            ((uint32_t)(q8_code(v.z, inv) & 0xFF) << 16) |
+                            ((uint32_t)(q8_code(v.w, inv) & 0xFF) << 24);
+    reinterpret_cast<uint32_t*>(q)[gid] = packed;
+    if ((gid & 7) == 0)
+        d[blk] = scale;
+}
 
 __global__ __launch_bounds__(256) void router_logits_small(const float* __restrict__ x, int32_t S,
                                                            int32_t H, int32_t E,
                                                            const float* __restrict__ w,
-                                                           float* __restrict__ logits)
+                                                           float* __restrict__ logits,
+                                                           int8_t* __restrict__ xq,
+                                                           float* __restrict__ xd)
 {
-    int lane = threadIdx.x & 63;
-    int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E)
+    __shared__ float part[4][kSmallS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int e = blockIdx.x;
+    if (e >= E) {
+        /* quantiser workgroups */
+        const int64_t n_blocks = (int64_t)S * (H / 32);
+        quantize_blocks(x, n_blocks, xq, xd, (int64_t)(e - E) * 256 + threadIdx.x);
         return;
+    }
     const float4* wr = reinterpret_cast<const float4*>(w + (int64_t)e * H);
     float acc[kSmallS];
 #pragma unroll
     for (int t = 0; t < kSmallS; ++t)
         acc[t] = 0.0f;
-    int n4 = H / 4;
-    for (int i = lane; i < n4; i += 64) {
-        float4 wv = wr[i];
+    const int n4 = H / 4;
+    const int q0 = (wv * n4) / 4, q1 = ((wv + 1) * n4) / 4;
+    for (int i = q0 + lane; i < q1; i += 64) {
+        const float4 wv4 = wr[i];
 #pragma unroll
         for (int t = 0; t < kSmallS; ++t) {
             if (t < S) {
-                float4 xv = reinterpret_cast<const float4*>(x + (int64_t)t * H)[i];
-                acc[t] = __builtin_fmaf(wv.x, xv.x, acc[t]);
-                acc[t] = __builtin_fmaf(wv.y, xv.y, acc[t]);
-                acc[t] = __builtin_fmaf(wv.z, xv.z, acc[t]);
-                acc[t] = __builtin_fmaf(wv.w, xv.w, acc[t]);
+                const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)t * H)[i];
+                acc[t] = __builtin_fmaf(wv4.x, xv.x, acc[t]);
+                acc[t] = __builtin_fmaf(wv4.y, xv.y, acc[t]);
+                acc[t] = __builtin_fmaf(wv4.z, xv.z, acc[t]);
+                acc[t] = __builtin_fmaf(wv4.w, xv.w, acc[t]);
             }
         }
     }
 #pragma unroll
     for (int t = 0; t < kSmallS; ++t) {
-        if (t < S) {
-            float s = wave_sum(acc[t]);
-            if (lane == 0)
-                logits[(int64_t)t * E + e] = s;
-        }
+        const float s = wave_sum(acc[t]);
+        if (lane == 0)
+            part[wv][t] = s;
     }
+    __syncthreads();
+    if (threadIdx.x < S)
+        logits[(int64_t)threadIdx.x * E + e] =
+            ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
 }
 
 constexpr int kTile = 32;
@@ -156,8 +193,8 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
     if (S == 0)
         return hipSuccess;
     if (S <= kSmallS) {
-        hipLaunchKernelGGL(router_logits_small, dim3((E + 3) / 4), dim3(256), 0, st, x, S, H, E, w,
-                           logits);
+        hipLaunchKernelGGL(router_logits_small, dim3(E), dim3(256), 0, st, x, S, H, E, w, logits,
+                           (int8_t*)nullptr, (float*)nullptr);
     } else {
         dim3 grid((S + kTile - 1) / kTile, (E + kTile - 1) / kTile);
         hipLaunchKernelGGL(router_logits_tiled, grid, dim3(256), 0, st, x, S, H, E, w, logits);
@@ -165,18 +202,19 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
     return hipGetLastError();
 }
 
-/* ---- router selection: one wave per token ---------------------------------
- * Each lane holds the scores of experts lane, lane+64, ...; the top-k is k
- * rounds of a wave-wide maximum over 64-bit keys (order-preserving score bits
- * above the complemented expert id, so equal scores resolve to the lower id). */
-
-constexpr int kMaxPerLane = 16; /* E <= 1024 */
-
-__device__ __forceinline__ uint32_t order_bits(float c)
+hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
+                                   float* logits, int8_t* xq, float* xd, hipStream_t st)
 {
-    uint32_t u = __float_as_uint(c);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    if (S == 0)
+        return hipSuccess;
+    const int64_t qthreads = (int64_t)S * (H / 32) * 8;
+    const int64_t qgroups = (qthreads + 255) / 256;
+    hipLaunchKernelGGL(router_logits_small, dim3((uint32_t)(E + qgroups)), dim3(256), 0, st, x, S, H, E,
+                       w, logits, xq, xd);
+    return hipGetLastError();
 }
+
+/* ---- router selection: one wave per token (select.h) ------------------- */
 
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ logits,
                                                             const float* __restrict__ bias,
@@ -185,56 +223,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
                                                             float* __restrict__ weights)
 {
     __shared__ float sel_s[4][64];
-    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int t = blockIdx.x * 4 + wv;
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
     if (t >= S)
         return;
-    const float* lt = logits + (int64_t)t * E;
-    float s[kMaxPerLane];
-    uint64_t key[kMaxPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        int e = lane + 64 * i;
-        if (e < E) {
-            float sg = 1.0f / (1.0f + expf(-lt[e]));
-            s[i] = sg;
-            key[i] = ((uint64_t)order_bits(sg + bias[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-        } else {
-            s[i] = 0.0f;
-            key[i] = 0;
-        }
-    }
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            best = key[i] > best ? key[i] : best;
-        for (int m = 32; m >= 1; m >>= 1) {
-            uint64_t o = __shfl_xor(best, m, 64);
-            best = o > best ? o : best;
-        }
-        int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-        float cand = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            if (key[i] == best) {
-                cand = s[i];
-                key[i] = 0; /* taken */
-            }
-        }
-        float sj = __shfl(cand, e & 63, 64);
-        if (lane == 0) {
-            sel_s[wv][j] = sj;
-            ids[(int64_t)t * k + j] = e;
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    float denom = 0.0f;
-    for (int j = 0; j < k; ++j)
-        denom += sel_s[wv][j];
-    if (lane < k)
-        weights[(int64_t)t * k + lane] = rsf * (sel_s[wv][lane] / denom);
+    select_token(logits + (int64_t)t * E, bias, E, k, rsf, ids + (int64_t)t * k,
+                 weights + (int64_t)t * k, sel_s[wv], nullptr);
 }
 
 hipError_t launch_router_select(const float* logits, const float* bias, int32_t S, int32_t E,

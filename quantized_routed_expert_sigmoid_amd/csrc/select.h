@@ -1,0 +1,86 @@
+/*
+ * select.h -- top-k selection of the sigmoid router for one token, run by
+ * one wavefront ("Show HN: 如何在我的低配置电脑上运行 GLM-5.2", implemented-
+ * features section, sigmoid-router item: DeepSeek-V3 style sigmoid scores,
+ * noaux_tc selection bias, routed_scaling_factor).
+ *
+ * Each lane holds the scores of experts lane, lane+64, ...; the top-k is k
+ * rounds of a wave-wide maximum over 64-bit keys (order-preserving score bits
+ * above the complemented expert id, so equal scores resolve to the lower id).
+ * Weights: rsf * s_j / sum of the selected unbiased scores (slot order).
+ */
+#ifndef COLI_SELECT_H
+#define COLI_SELECT_H
+
+#include "device_common.h"
+
+namespace coli {
+
+constexpr int kMaxPerLane = 16; /* E <= 1024 */
+
+__device__ __forceinline__ uint32_t order_bits(float c)
+{
+    uint32_t u = __float_as_uint(c);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+/* lt: the token's E logits; writes ids_out[0..k), w_out[0..k) and, when
+ * ids_lds is not null, ids_lds[0..k).  sel_s: 64 floats of LDS owned by the
+ * calling wave. */
+__device__ __forceinline__ void select_token(const float* lt, const float* bias, int32_t E, int32_t k,
+                                             float rsf, int32_t* ids_out, float* w_out, float* sel_s,
+                                             int32_t* ids_lds)
+{
+    const int lane = threadIdx.x & 63;
+    float s[kMaxPerLane];
+    uint64_t key[kMaxPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            const float sg = 1.0f / (1.0f + expf(-lt[e]));
+            s[i] = sg;
+            key[i] = ((uint64_t)order_bits(sg + bias[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+        } else {
+            s[i] = 0.0f;
+            key[i] = 0;
+        }
+    }
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i)
+            best = key[i] > best ? key[i] : best;
+        for (int m = 32; m >= 1; m >>= 1) {
+            const uint64_t o = __shfl_xor(best, m, 64);
+            best = o > best ? o : best;
+        }
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+        float cand = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) {
+            if (key[i] == best) {
+                cand = s[i];
+                key[i] = 0; /* taken */
+            }
+        }
+        const float sj = __shfl(cand, e & 63, 64);
+        if (lane == 0) {
+            sel_s[j] = sj;
+            ids_out[j] = e;
+            if (ids_lds)
+                ids_lds[j] = e;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    float denom = 0.0f;
+    for (int j = 0; j < k; ++j)
+        denom += sel_s[j];
+    if (lane < k)
+        w_out[lane] = rsf * (sel_s[lane] / denom);
+}
+
+} // namespace coli
+
+#endif
