@@ -101,6 +101,25 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+/* Wave-wide max / min of unsigned values with DPP lane moves (no LDS
+ * crossbar): row shifts 1, 2, 4, 8 scan each 16-lane row, row broadcasts 15
+ * and 31 carry the row results into the last row; lane 63 holds the result,
+ * which is read back as a uniform value.  Lanes a move does not reach keep
+ * the operation's identity. */
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
+{
+    const int id = MAX ? 0 : (int)0xFFFFFFFFu;
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false)); /* row_shr:1 */
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false)); /* row_shr:2 */
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false)); /* row_shr:4 */
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false)); /* row_shr:8 */
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false)); /* row_bcast:15 */
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false)); /* row_bcast:31 */
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 } // namespace coli
 
 #endif

@@ -23,13 +23,15 @@ constexpr int kDispWaves = kDispThreads / 64;
 constexpr int kMaxE = 1024;
 
 /* Workgroup exclusive scan of one value per thread (1024 threads).  Returns
- * the exclusive prefix; *total receives the sum.  `tmp` holds kDispWaves ints. */
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tmp, int32_t* total)
+ * the exclusive prefix; *total receives the sum.  `tmp` holds kDispWaves + 1
+ * values. */
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* tmp, T* total)
 {
-    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int32_t inc = v;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    T inc = v;
     for (int off = 1; off < 64; off <<= 1) {
-        int32_t o = __shfl_up(inc, off, 64);
+        const T o = __shfl_up(inc, off, 64);
         if (lane >= off)
             inc += o;
     }
@@ -37,10 +39,10 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tmp,
         tmp[wv] = inc;
     __syncthreads();
     if (wv == 0) {
-        int32_t w = lane < kDispWaves ? tmp[lane] : 0;
-        int32_t winc = w;
+        const T w = lane < kDispWaves ? tmp[lane] : T(0);
+        T winc = w;
         for (int off = 1; off < kDispWaves; off <<= 1) {
-            int32_t o = __shfl_up(winc, off, 64);
+            const T o = __shfl_up(winc, off, 64);
             if (lane >= off)
                 winc += o;
         }
@@ -50,7 +52,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* tmp,
             tmp[kDispWaves] = winc;
     }
     __syncthreads();
-    int32_t res = tmp[wv] + inc - v;
+    const T res = tmp[wv] + inc - v;
     *total = tmp[kDispWaves];
     __syncthreads();
     return res;
@@ -74,7 +76,7 @@ struct DispatchShared {
     int32_t cnt[kMaxE];
     int32_t base[kMaxE];
     uint8_t wcnt[kDispWaves][kMaxE];
-    int32_t tmp[kDispWaves + 1];
+    uint64_t tmp[kDispWaves + 1];
 };
 
 /* The dispatch, run by all 1024 threads of a workgroup.  `ids` may point to
@@ -87,7 +89,6 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
     int32_t* cnt = sh.cnt;
     int32_t* base = sh.base;
     auto& wcnt = sh.wcnt;
-    int32_t* tmp = sh.tmp;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int32_t P = S * k;
 
@@ -103,16 +104,20 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
         atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
     __syncthreads();
 
-    /* offsets, active list and unit list: one expert per thread */
+    /* offsets, active list and unit list: one expert per thread, one scan of
+     * the three counts packed in 64 bits (count: bits 0..21, active flag:
+     * 22..32, units: 33..54; no field can carry into the next) */
     const int32_t e = tid;
     const int32_t c = e < E ? cnt[e] : 0;
-    int32_t tot;
-    const int32_t off = block_exclusive_scan(c, tmp, &tot);
-    const int32_t aidx = block_exclusive_scan(c > 0 ? 1 : 0, tmp, &tot);
-    const int32_t nact = tot;
     const int32_t nu = (c + kUnitTokens - 1) / kUnitTokens;
-    const int32_t ubase = block_exclusive_scan(nu, tmp, &tot);
-    const int32_t nunits = tot;
+    const uint64_t packed = (uint64_t)c | ((uint64_t)(c > 0 ? 1 : 0) << 22) | ((uint64_t)nu << 33);
+    uint64_t tot;
+    const uint64_t pre = block_exclusive_scan<uint64_t>(packed, sh.tmp, &tot);
+    const int32_t off = (int32_t)(pre & 0x3FFFFF);
+    const int32_t aidx = (int32_t)((pre >> 22) & 0x7FF);
+    const int32_t ubase = (int32_t)(pre >> 33);
+    const int32_t nact = (int32_t)((tot >> 22) & 0x7FF);
+    const int32_t nunits = (int32_t)(tot >> 33);
     if (e < E) {
         base[e] = off;
         offsets[e] = off;

@@ -32,39 +32,46 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
                                              int32_t* ids_lds)
 {
     const int lane = threadIdx.x & 63;
+    const int per_lane = (E + 63) / 64; /* uniform */
     float s[kMaxPerLane];
-    uint64_t key[kMaxPerLane];
+    uint32_t key[kMaxPerLane]; /* order-preserving bits of the biased score; 0 = unavailable */
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = lane + 64 * i;
-        if (e < E) {
+        if (i < per_lane && e < E) {
             const float sg = 1.0f / (1.0f + expf(-lt[e]));
             s[i] = sg;
-            key[i] = ((uint64_t)order_bits(sg + bias[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+            key[i] = order_bits(sg + bias[e]);
         } else {
             s[i] = 0.0f;
             key[i] = 0;
         }
     }
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
+        /* best score, then the lowest expert id holding it */
+        uint32_t best = 0;
 #pragma unroll
         for (int i = 0; i < kMaxPerLane; ++i)
-            best = key[i] > best ? key[i] : best;
-        for (int m = 32; m >= 1; m >>= 1) {
-            const uint64_t o = __shfl_xor(best, m, 64);
-            best = o > best ? o : best;
-        }
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+            if (i < per_lane)
+                best = key[i] > best ? key[i] : best;
+        best = wave_reduce_u32<true>(best);
+        uint32_t mine = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i)
+            if (i < per_lane && key[i] == best && mine == 0xFFFFFFFFu)
+                mine = (uint32_t)(lane + 64 * i);
+        const int e = (int)wave_reduce_u32<false>(mine);
+        const int ie = e >> 6; /* uniform */
         float cand = 0.0f;
 #pragma unroll
         for (int i = 0; i < kMaxPerLane; ++i) {
-            if (key[i] == best) {
+            if (i == ie) {
                 cand = s[i];
-                key[i] = 0; /* taken */
+                if (lane == (e & 63))
+                    key[i] = 0; /* taken */
             }
         }
-        const float sj = __shfl(cand, e & 63, 64);
+        const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cand), e & 63));
         if (lane == 0) {
             sel_s[j] = sj;
             ids_out[j] = e;
