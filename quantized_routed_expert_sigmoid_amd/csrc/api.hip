@@ -89,7 +89,8 @@ int check_tokens(int32_t S, int32_t k)
 
 /* Byte offsets of the workspace regions. */
 struct Layout {
-    size_t logits, units, n_units, hq, hd, xq, xd, ids, w, offsets, sorted, inv, active, n_active, y;
+    size_t logits, units, n_units, munits, n_munits, hq, hd, xq, xd, ids, w, offsets, sorted, inv,
+        active, n_active, y;
     size_t total;
 };
 
@@ -103,11 +104,6 @@ struct Bump {
     }
 };
 
-int32_t layer_max_units(int32_t S, int32_t k, int32_t E, bool shared)
-{
-    return max_routed_units((int64_t)S * k, E) + (shared ? identity_units(S) : 0);
-}
-
 Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S, bool shared)
 {
     const int64_t P = (int64_t)S * k;
@@ -115,8 +111,10 @@ Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S, bool 
     Bump b;
     Layout L;
     L.logits = b.take((size_t)S * E * 4);
-    L.units = b.take((size_t)layer_max_units(S, k, E, shared) * sizeof(Unit));
+    L.units = b.take((size_t)max_gemv_units(P, E) * sizeof(Unit));
     L.n_units = b.take(16);
+    L.munits = b.take((size_t)max_mfma_units(P, E, S) * sizeof(Unit));
+    L.n_munits = b.take(16);
     L.hq = b.take((size_t)rows * I);
     L.hd = b.take((size_t)rows * (I / 32) * 4);
     L.xq = b.take((size_t)S * H);
@@ -134,8 +132,15 @@ Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S, bool 
 }
 
 struct FfnLayout {
-    size_t units, n_units, hq, hd, total;
+    size_t units, n_units, munits, n_munits, hq, hd, total;
 };
+
+/* Caller offsets may give one expert several pairs of the same token, so
+ * every expert may reach the MFMA threshold: bound with the largest S. */
+int32_t ffn_max_munits(int64_t rows, int32_t n_mat)
+{
+    return max_mfma_units(rows, n_mat, kMfmaMinTokens);
+}
 
 FfnLayout ffn_layout(int32_t H, int32_t I, int32_t n_mat, int32_t S, int32_t k)
 {
@@ -143,8 +148,10 @@ FfnLayout ffn_layout(int32_t H, int32_t I, int32_t n_mat, int32_t S, int32_t k)
     const int64_t rows = (int64_t)S * k;
     Bump b;
     FfnLayout L;
-    L.units = b.take((size_t)max_routed_units(rows, n_mat) * sizeof(Unit));
+    L.units = b.take((size_t)max_gemv_units(rows, n_mat) * sizeof(Unit));
     L.n_units = b.take(16);
+    L.munits = b.take((size_t)ffn_max_munits(rows, n_mat) * sizeof(Unit));
+    L.n_munits = b.take(16);
     L.hq = b.take((size_t)rows * I);
     L.hd = b.take((size_t)rows * (I / 32) * 4);
     L.total = b.at;
@@ -162,9 +169,10 @@ int hip_status(hipError_t e)
     return e == hipSuccess ? COLI_OK : COLI_E_HIP;
 }
 
-FfnSeg routed_seg(const coli_qbank* g, const coli_qbank* u, const coli_qbank* d, const int32_t* sorted,
-                  const Unit* units, const int32_t* n_units, int32_t k, int32_t S, int32_t rows,
-                  int32_t max_units, int32_t out_base)
+/* A routed group (ul != nullptr: unit lists from the dispatch or schedule
+ * kernel) or the identity group of the shared expert (ul == nullptr). */
+FfnSeg make_seg(const coli_qbank* g, const coli_qbank* u, const coli_qbank* d, const int32_t* sorted,
+                const UnitLists* ul, int32_t k, int32_t S, int32_t rows, int32_t out_base)
 {
     FfnSeg s;
     s.gate_w = static_cast<const uint8_t*>(g->data);
@@ -174,15 +182,32 @@ FfnSeg routed_seg(const coli_qbank* g, const coli_qbank* u, const coli_qbank* d,
     s.down_w = static_cast<const uint8_t*>(d->data);
     s.down_s = d->row_scale;
     s.sorted = sorted;
-    s.units = units;
-    s.n_units = n_units;
+    s.units = ul ? ul->units : nullptr;
+    s.n_units = ul ? ul->n_units : nullptr;
+    s.munits = ul ? ul->munits : nullptr;
+    s.n_munits = ul ? ul->n_munits : nullptr;
+    s.max_units = ul ? ul->max_units : identity_gemv_units(S);
+    s.max_munits = ul ? ul->max_munits : identity_mfma_units(S);
     s.k = k;
     s.out_base = out_base;
-    s.max_units = max_units;
     s.S = S;
     s.rows = rows;
     s.n_mat = g->n_mat;
     return s;
+}
+
+/* gate/up then down, each with both kernel families (a family with no
+ * possible unit launches nothing). */
+hipError_t run_ffn(const FfnArgs& a, int32_t bits_gu, int32_t bits_d, hipStream_t s)
+{
+    hipError_t e = launch_ffn_gate_up(a, bits_gu, s);
+    if (e == hipSuccess)
+        e = launch_ffn_gate_up_mfma(a, bits_gu, s);
+    if (e == hipSuccess)
+        e = launch_ffn_down(a, bits_d, s);
+    if (e == hipSuccess)
+        e = launch_ffn_down_mfma(a, bits_d, s);
+    return e;
 }
 
 } // namespace
@@ -275,8 +300,7 @@ int colibri_moe_dispatch(const int32_t* topk_ids, int32_t S, int32_t k, int32_t 
     if (!expert_offsets || !active_experts || !n_active || (S > 0 && (!topk_ids || !sorted_pairs)))
         return COLI_E_INVAL;
     return hip_status(launch_dispatch(topk_ids, S, k, E, expert_offsets, sorted_pairs, nullptr,
-                                      active_experts, n_active, nullptr, nullptr,
-                                      (hipStream_t)stream));
+                                      active_experts, n_active, nullptr, (hipStream_t)stream));
 }
 
 int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const coli_qbank* down,
@@ -314,12 +338,16 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
         return COLI_E_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const int32_t rows = S * k;
-    const int32_t maxu = max_routed_units(rows, n_mat);
-    Unit* units = at<Unit>(ws, Lo.units);
-    int32_t* n_units = at<int32_t>(ws, Lo.n_units);
-    hipError_t e = launch_schedule(expert_offsets, n_mat, maxu, units, n_units, s);
+    UnitLists ul;
+    ul.units = at<Unit>(ws, Lo.units);
+    ul.n_units = at<int32_t>(ws, Lo.n_units);
+    ul.max_units = max_gemv_units(rows, n_mat);
+    ul.munits = at<Unit>(ws, Lo.munits);
+    ul.n_munits = at<int32_t>(ws, Lo.n_munits);
+    ul.max_munits = ffn_max_munits(rows, n_mat);
+    hipError_t e = launch_schedule(expert_offsets, n_mat, ul, s);
     FfnArgs a;
-    a.seg[0] = routed_seg(gate, up, down, sorted_pairs, units, n_units, k, S, rows, maxu, 0);
+    a.seg[0] = make_seg(gate, up, down, sorted_pairs, &ul, k, S, rows, 0);
     a.seg[1] = a.seg[0];
     a.nseg = 1;
     a.unit_tokens = kUnitTokens; /* caller offsets: units may hold several tokens */
@@ -331,9 +359,7 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
     a.hd = at<float>(ws, Lo.hd);
     a.y = y;
     if (e == hipSuccess)
-        e = launch_ffn_gate_up(a, gate->qtype, s);
-    if (e == hipSuccess)
-        e = launch_ffn_down(a, down->qtype, s);
+        e = run_ffn(a, gate->qtype, down->qtype, s);
     return hip_status(e);
 }
 
@@ -374,8 +400,13 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     int32_t* inv = at<int32_t>(ws, Lo.inv);
     int32_t* active = at<int32_t>(ws, Lo.active);
     int32_t* n_active = at<int32_t>(ws, Lo.n_active);
-    Unit* units = at<Unit>(ws, Lo.units);
-    int32_t* n_units = at<int32_t>(ws, Lo.n_units);
+    UnitLists ul;
+    ul.units = at<Unit>(ws, Lo.units);
+    ul.n_units = at<int32_t>(ws, Lo.n_units);
+    ul.max_units = max_gemv_units(P, E);
+    ul.munits = at<Unit>(ws, Lo.munits);
+    ul.n_munits = at<int32_t>(ws, Lo.n_munits);
+    ul.max_munits = max_mfma_units(P, E, S);
     float* y = at<float>(ws, Lo.y);
 
     auto mark = [&](int i, hipError_t prev) -> hipError_t {
@@ -396,14 +427,12 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     if (e == hipSuccess)
         e = S <= kSmallS
                 ? launch_select_dispatch_small(logits, L->router_bias, S, E, k, L->routed_scaling_factor,
-                                               ids, w, offsets, sorted, inv, active, n_active, units,
-                                               n_units, s)
-                : launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, s);
+                                               ids, w, offsets, sorted, inv, active, n_active, ul, s)
+                : launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, s);
     e = mark(2, e);
 
     FfnArgs a;
-    a.seg[0] = routed_seg(&L->gate, &L->up, &L->down, sorted, units, n_units, k, S, P,
-                          max_routed_units(P, E), 0);
+    a.seg[0] = make_seg(&L->gate, &L->up, &L->down, sorted, &ul, k, S, P, 0);
     a.nseg = 1;
     a.unit_tokens = S == 1 ? 1 : kUnitTokens; /* distinct experts per token */
     a.H = H;
@@ -415,8 +444,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     a.y = y;
     FfnArgs b = a; /* shared expert, when it cannot share the routed launch */
     if (shared) {
-        FfnSeg sh = routed_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, nullptr, 1, S, S,
-                               identity_units(S), P);
+        FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P);
         if (L->sh_gate.qtype == L->gate.qtype && L->sh_down.qtype == L->down.qtype) {
             a.seg[1] = sh;
             a.nseg = 2;
@@ -430,13 +458,21 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     }
     if (e == hipSuccess)
         e = launch_ffn_gate_up(a, L->gate.qtype, s);
+    if (e == hipSuccess)
+        e = launch_ffn_gate_up_mfma(a, L->gate.qtype, s);
     if (e == hipSuccess && b.nseg)
         e = launch_ffn_gate_up(b, L->sh_gate.qtype, s);
+    if (e == hipSuccess && b.nseg)
+        e = launch_ffn_gate_up_mfma(b, L->sh_gate.qtype, s);
     e = mark(3, e);
     if (e == hipSuccess)
         e = launch_ffn_down(a, L->down.qtype, s);
+    if (e == hipSuccess)
+        e = launch_ffn_down_mfma(a, L->down.qtype, s);
     if (e == hipSuccess && b.nseg)
         e = launch_ffn_down(b, L->sh_down.qtype, s);
+    if (e == hipSuccess && b.nseg)
+        e = launch_ffn_down_mfma(b, L->sh_down.qtype, s);
     e = mark(4, e);
     if (e == hipSuccess)
         e = launch_combine(y, inv, w, S, k, H, shared ? P : -1, out, s);

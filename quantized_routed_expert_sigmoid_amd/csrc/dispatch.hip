@@ -58,18 +58,36 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* tmp, T* total)
     return res;
 }
 
-/* Writes the work units of expert e (count n, first sorted position off). */
+/* Writes the work units of expert e (count n, first sorted position off) in
+ * chunks of `chunk` positions, never past max_units units in all. */
 __device__ __forceinline__ void emit_units(Unit* units, int32_t ubase, int32_t e, int32_t off,
-                                           int32_t n, int32_t max_units)
+                                           int32_t n, int32_t chunk, int32_t max_units)
 {
-    for (int32_t u = 0; u * kUnitTokens < n && ubase + u < max_units; ++u) {
+    for (int32_t u = 0; u * chunk < n && ubase + u < max_units; ++u) {
         Unit U;
         U.e = e;
-        U.pos0 = off + u * kUnitTokens;
-        U.ntok = (n - u * kUnitTokens) < kUnitTokens ? (n - u * kUnitTokens) : kUnitTokens;
+        U.pos0 = off + u * chunk;
+        U.ntok = (n - u * chunk) < chunk ? (n - u * chunk) : chunk;
         U.pad = 0;
         units[ubase + u] = U;
     }
+}
+
+/* Unit counts of an expert with c positions: (GEMV units, MFMA units). */
+__device__ __forceinline__ void unit_counts(int32_t c, int32_t& nu_g, int32_t& nu_m)
+{
+    const bool big = c >= kMfmaMinTokens;
+    nu_g = big ? 0 : (c + kUnitTokens - 1) / kUnitTokens;
+    nu_m = big ? (c + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
+}
+
+/* Packed per-expert counts for one workgroup scan: positions (bits 0..20),
+ * active flag (21..31), GEMV units (32..43), MFMA units (44..58).  With at
+ * most 2^20 pairs and 1024 experts no field can carry into the next. */
+__device__ __forceinline__ uint64_t pack_counts(int32_t c, int32_t nu_g, int32_t nu_m)
+{
+    return (uint64_t)c | ((uint64_t)(c > 0 ? 1 : 0) << 21) | ((uint64_t)nu_g << 32) |
+           ((uint64_t)nu_m << 44);
 }
 
 struct DispatchShared {
@@ -83,8 +101,8 @@ struct DispatchShared {
  * global memory or to LDS. */
 __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int32_t k, int32_t E,
                                               int32_t* offsets, int32_t* sorted, int32_t* inv,
-                                              int32_t* active, int32_t* n_active, Unit* units,
-                                              int32_t* n_units, DispatchShared& sh)
+                                              int32_t* active, int32_t* n_active, const UnitLists* ul,
+                                              DispatchShared& sh)
 {
     int32_t* cnt = sh.cnt;
     int32_t* base = sh.base;
@@ -104,33 +122,35 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
         atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
     __syncthreads();
 
-    /* offsets, active list and unit list: one expert per thread, one scan of
-     * the three counts packed in 64 bits (count: bits 0..21, active flag:
-     * 22..32, units: 33..54; no field can carry into the next) */
+    /* offsets, active list and unit lists: one expert per thread, one scan of
+     * the packed counts */
     const int32_t e = tid;
     const int32_t c = e < E ? cnt[e] : 0;
-    const int32_t nu = (c + kUnitTokens - 1) / kUnitTokens;
-    const uint64_t packed = (uint64_t)c | ((uint64_t)(c > 0 ? 1 : 0) << 22) | ((uint64_t)nu << 33);
+    int32_t nu_g, nu_m;
+    unit_counts(c, nu_g, nu_m);
     uint64_t tot;
-    const uint64_t pre = block_exclusive_scan<uint64_t>(packed, sh.tmp, &tot);
-    const int32_t off = (int32_t)(pre & 0x3FFFFF);
-    const int32_t aidx = (int32_t)((pre >> 22) & 0x7FF);
-    const int32_t ubase = (int32_t)(pre >> 33);
-    const int32_t nact = (int32_t)((tot >> 22) & 0x7FF);
-    const int32_t nunits = (int32_t)(tot >> 33);
+    const uint64_t pre = block_exclusive_scan<uint64_t>(pack_counts(c, nu_g, nu_m), sh.tmp, &tot);
+    const int32_t off = (int32_t)(pre & 0x1FFFFF);
+    const int32_t aidx = (int32_t)((pre >> 21) & 0x7FF);
+    const int32_t gbase = (int32_t)((pre >> 32) & 0xFFF);
+    const int32_t mbase = (int32_t)(pre >> 44);
     if (e < E) {
         base[e] = off;
         offsets[e] = off;
         if (c > 0)
             active[aidx] = e;
-        if (units)
-            emit_units(units, ubase, e, off, c, 0x7fffffff);
+        if (ul) {
+            emit_units(ul->units, gbase, e, off, nu_g ? c : 0, kUnitTokens, ul->max_units);
+            emit_units(ul->munits, mbase, e, off, nu_m ? c : 0, kMfmaUnitTokens, ul->max_munits);
+        }
     }
     if (tid == 0) {
         offsets[E] = P;
-        *n_active = nact;
-        if (n_units)
-            *n_units = nunits;
+        *n_active = (int32_t)((tot >> 21) & 0x7FF);
+        if (ul) {
+            *ul->n_units = min((int32_t)((tot >> 32) & 0xFFF), ul->max_units);
+            *ul->n_munits = min((int32_t)(tot >> 44), ul->max_munits);
+        }
     }
     __syncthreads();
 
@@ -176,18 +196,19 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
 __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     const int32_t* __restrict__ ids, int32_t S, int32_t k, int32_t E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
-    int32_t* __restrict__ n_active, Unit* __restrict__ units, int32_t* __restrict__ n_units)
+    int32_t* __restrict__ n_active, UnitLists ul, int32_t has_units)
 {
     __shared__ DispatchShared sh;
-    dispatch_body(ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, sh);
+    dispatch_body(ids, S, k, E, offsets, sorted, inv, active, n_active, has_units ? &ul : nullptr, sh);
 }
 
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, int32_t* offsets,
                            int32_t* sorted, int32_t* inv, int32_t* active, int32_t* n_active,
-                           Unit* units, int32_t* n_units, hipStream_t st)
+                           const UnitLists* ul, hipStream_t st)
 {
+    UnitLists none = {};
     hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, st, ids, S, k, E, offsets,
-                       sorted, inv, active, n_active, units, n_units);
+                       sorted, inv, active, n_active, ul ? *ul : none, ul ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -197,7 +218,7 @@ __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
     const float* __restrict__ logits, const float* __restrict__ bias, int32_t S, int32_t E, int32_t k,
     float rsf, int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
-    int32_t* __restrict__ n_active, Unit* __restrict__ units, int32_t* __restrict__ n_units)
+    int32_t* __restrict__ n_active, UnitLists ul)
 {
     __shared__ DispatchShared sh;
     __shared__ float sel_s[kSmallS][64];
@@ -207,46 +228,48 @@ __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
         select_token(logits + (int64_t)wv * E, bias, E, k, rsf, ids + (int64_t)wv * k,
                      weights + (int64_t)wv * k, sel_s[wv], sel_ids + wv * k);
     __syncthreads();
-    dispatch_body(sel_ids, S, k, E, offsets, sorted, inv, active, n_active, units, n_units, sh);
+    dispatch_body(sel_ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, sh);
 }
 
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
                                         int32_t k, float rsf, int32_t* ids, float* weights,
                                         int32_t* offsets, int32_t* sorted, int32_t* inv,
-                                        int32_t* active, int32_t* n_active, Unit* units,
-                                        int32_t* n_units, hipStream_t st)
+                                        int32_t* active, int32_t* n_active, const UnitLists& ul,
+                                        hipStream_t st)
 {
     hipLaunchKernelGGL(select_dispatch_small, dim3(1), dim3(kDispThreads), 0, st, logits, bias, S, E, k,
-                       rsf, ids, weights, offsets, sorted, inv, active, n_active, units, n_units);
+                       rsf, ids, weights, offsets, sorted, inv, active, n_active, ul);
     return hipGetLastError();
 }
 
-/* Unit list from offsets produced elsewhere.  Offsets that break the
+/* Unit lists from offsets produced elsewhere.  Offsets that break the
  * documented contract (non-decreasing, last == S*k) cannot make it write past
- * max_units units; the FFN kernels bound positions separately. */
+ * the lists' bounds; the FFN kernels bound positions separately. */
 __global__ __launch_bounds__(kDispThreads) void schedule_kernel(const int32_t* __restrict__ offsets,
-                                                                int32_t n_mat, int32_t max_units,
-                                                                Unit* __restrict__ units,
-                                                                int32_t* __restrict__ n_units)
+                                                                int32_t n_mat, UnitLists ul)
 {
-    __shared__ int32_t tmp[kDispWaves + 1];
+    __shared__ uint64_t tmp[kDispWaves + 1];
     const int e = threadIdx.x;
     const int32_t off = e < n_mat ? offsets[e] : 0;
-    const int32_t c = e < n_mat ? max(0, offsets[e + 1] - off) : 0;
-    const int32_t nu = (c + kUnitTokens - 1) / kUnitTokens;
-    int32_t tot;
-    const int32_t ubase = block_exclusive_scan(nu, tmp, &tot);
-    if (e < n_mat)
-        emit_units(units, ubase, e, off, c, max_units);
-    if (e == 0)
-        *n_units = min(tot, max_units);
+    const int32_t c = e < n_mat ? min(max(0, offsets[e + 1] - off), kPairLimit) : 0;
+    int32_t nu_g, nu_m;
+    unit_counts(c, nu_g, nu_m);
+    uint64_t tot;
+    const uint64_t pre = block_exclusive_scan<uint64_t>(pack_counts(c, nu_g, nu_m), tmp, &tot);
+    if (e < n_mat) {
+        emit_units(ul.units, (int32_t)((pre >> 32) & 0xFFF), e, off, nu_g ? c : 0, kUnitTokens,
+                   ul.max_units);
+        emit_units(ul.munits, (int32_t)(pre >> 44), e, off, nu_m ? c : 0, kMfmaUnitTokens, ul.max_munits);
+    }
+    if (e == 0) {
+        *ul.n_units = min((int32_t)((tot >> 32) & 0xFFF), ul.max_units);
+        *ul.n_munits = min((int32_t)(tot >> 44), ul.max_munits);
+    }
 }
 
-hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, int32_t max_units, Unit* units,
-                           int32_t* n_units, hipStream_t st)
+hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, const UnitLists& ul, hipStream_t st)
 {
-    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kDispThreads), 0, st, offsets, n_mat,
-                       max_units, units, n_units);
+    hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kDispThreads), 0, st, offsets, n_mat, ul);
     return hipGetLastError();
 }
 

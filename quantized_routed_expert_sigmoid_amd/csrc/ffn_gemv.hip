@@ -51,6 +51,9 @@ __device__ __forceinline__ FfnSeg pick(const FfnArgs& a, int s)
     r.sorted = one ? a.seg[1].sorted : a.seg[0].sorted;
     r.units = one ? a.seg[1].units : a.seg[0].units;
     r.n_units = one ? a.seg[1].n_units : a.seg[0].n_units;
+    r.munits = one ? a.seg[1].munits : a.seg[0].munits;
+    r.n_munits = one ? a.seg[1].n_munits : a.seg[0].n_munits;
+    r.max_munits = one ? a.seg[1].max_munits : a.seg[0].max_munits;
     r.k = one ? a.seg[1].k : a.seg[0].k;
     r.out_base = one ? a.seg[1].out_base : a.seg[0].out_base;
     r.max_units = one ? a.seg[1].max_units : a.seg[0].max_units;

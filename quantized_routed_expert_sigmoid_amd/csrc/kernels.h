@@ -15,6 +15,15 @@ namespace coli {
  * more tokens are split into several units. */
 constexpr int kUnitTokens = 4;
 
+/* Experts holding at least this many tokens of a batch run on the int8
+ * matrix cores (ffn_mfma.hip) in units of up to kMfmaUnitTokens tokens;
+ * experts with fewer run on the GEMV kernels (ffn_gemv.hip). */
+constexpr int kMfmaMinTokens = 8;
+constexpr int kMfmaUnitTokens = 64;
+
+/* Most (token, slot) pairs of one call (the ABI's limit). */
+constexpr int32_t kPairLimit = 1 << 20;
+
 /* Batches of at most this many tokens use the small-batch router kernels
  * (a workgroup per router row; selection and dispatch in one workgroup). */
 constexpr int kSmallS = 8;
@@ -24,7 +33,19 @@ struct Unit {
     int32_t e, pos0, ntok, pad;
 };
 
-/* One group of experts run by the FFN kernels. */
+/* Device unit lists written by the dispatch (or schedule) kernel. */
+struct UnitLists {
+    Unit* units;       /* GEMV units (experts with < kMfmaMinTokens tokens) */
+    int32_t* n_units;
+    int32_t max_units;
+    Unit* munits;      /* MFMA units */
+    int32_t* n_munits;
+    int32_t max_munits;
+};
+
+/* One group of experts run by the FFN kernels.  A group with units ==
+ * munits == nullptr is one expert applied to positions [0, S) in order (the
+ * shared expert); its max_units / max_munits select which kernels take it. */
 struct FfnSeg {
     const uint8_t* gate_w;
     const float* gate_s;
@@ -32,21 +53,24 @@ struct FfnSeg {
     const float* up_s;
     const uint8_t* down_w;
     const float* down_s;
-    const int32_t* sorted; /* pair index per sorted position; nullptr: identity */
-    const Unit* units;     /* device unit list; nullptr: one expert, units of kUnitTokens tokens over positions [0, S) */
-    const int32_t* n_units; /* device count of `units` */
-    int32_t k;              /* token of pair p is p / k */
-    int32_t out_base;       /* first row of this group in hq / hd / y */
-    int32_t max_units;      /* upper bound on the unit count (grid sizing) */
-    int32_t S;              /* tokens of the batch */
-    int32_t rows;           /* sorted positions of this group (S*k, or S for identity) */
-    int32_t n_mat;          /* matrices in the group's banks */
+    const int32_t* sorted;   /* pair index per sorted position; nullptr: identity */
+    const Unit* units;       /* GEMV unit list (device) */
+    const int32_t* n_units;
+    const Unit* munits;      /* MFMA unit list (device) */
+    const int32_t* n_munits;
+    int32_t k;               /* token of pair p is p / k */
+    int32_t out_base;        /* first row of this group in hq / hd / y */
+    int32_t max_units;       /* grid bounds of the two kernel families */
+    int32_t max_munits;
+    int32_t S;               /* tokens of the batch */
+    int32_t rows;            /* sorted positions of this group (S*k, or S for identity) */
+    int32_t n_mat;           /* matrices in the group's banks */
 };
 
 struct FfnArgs {
     FfnSeg seg[2];
     int32_t nseg;
-    int32_t unit_tokens; /* most tokens any unit holds: 1 or kUnitTokens */
+    int32_t unit_tokens; /* most tokens any GEMV unit holds: 1 or kUnitTokens */
     int32_t H, I;
     const int8_t* xq; /* [S][H]   */
     const float* xd;  /* [S][H/32] */
@@ -55,17 +79,35 @@ struct FfnArgs {
     float* y;         /* [rows][H] */
 };
 
-/* Upper bound on the number of units of a routed group with P pairs over E
- * experts: sum_e ceil(n_e / U) <= (P + (U - 1) * min(E, P)) / U. */
-inline int32_t max_routed_units(int64_t P, int32_t E)
+/* Bounds on the unit counts of a routed group with P pairs of S tokens over
+ * E experts (n_e pairs each, sum P, n_e <= S).  GEMV: experts with n_e <
+ * kMfmaMinTokens give ceil(n_e / 4) <= 2 units each.  MFMA: experts with
+ * n_e >= kMfmaMinTokens give ceil(n_e / 64) <= n_e / 64 + 1 units each. */
+inline int32_t max_gemv_units(int64_t P, int32_t E)
 {
-    int64_t active = P < E ? P : E;
-    return (int32_t)((P + (kUnitTokens - 1) * active) / kUnitTokens);
+    const int64_t active = P < E ? P : E;
+    const int64_t a = (P + (kUnitTokens - 1) * active) / kUnitTokens;
+    const int64_t b = 2 * active;
+    return (int32_t)(a < b ? a : b);
 }
 
-inline int32_t identity_units(int32_t S)
+inline int32_t max_mfma_units(int64_t P, int32_t E, int32_t S)
 {
-    return (S + kUnitTokens - 1) / kUnitTokens;
+    if (S < kMfmaMinTokens)
+        return 0;
+    const int64_t big = P / kMfmaMinTokens < E ? P / kMfmaMinTokens : E;
+    return (int32_t)(P / kMfmaUnitTokens + big + 1);
+}
+
+/* Units of a one-expert identity group over S tokens. */
+inline int32_t identity_gemv_units(int32_t S)
+{
+    return S >= kMfmaMinTokens ? 0 : (S + kUnitTokens - 1) / kUnitTokens;
+}
+
+inline int32_t identity_mfma_units(int32_t S)
+{
+    return S >= kMfmaMinTokens ? (S + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
 }
 
 hipError_t launch_quantize_q8_0(const float* x, int64_t n_blocks, int8_t* q, float* d,
@@ -82,25 +124,29 @@ hipError_t launch_router_select(const float* logits, const float* bias, int32_t 
 hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
                                    float* logits, int8_t* xq, float* xd, hipStream_t st);
 
-/* S <= kSmallS: selection, union dispatch and unit list in one workgroup. */
+/* S <= kSmallS: selection, union dispatch and unit lists in one workgroup. */
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
                                         int32_t k, float rsf, int32_t* ids, float* weights,
                                         int32_t* offsets, int32_t* sorted, int32_t* inv,
-                                        int32_t* active, int32_t* n_active, Unit* units,
-                                        int32_t* n_units, hipStream_t st);
+                                        int32_t* active, int32_t* n_active, const UnitLists& ul,
+                                        hipStream_t st);
 
-/* Union dispatch; `units` / `n_units` may be null (then no unit list). */
+/* Union dispatch; `ul` may be null (then no unit lists). */
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E,
                            int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* active,
-                           int32_t* n_active, Unit* units, int32_t* n_units, hipStream_t st);
+                           int32_t* n_active, const UnitLists* ul, hipStream_t st);
 
-/* Unit list from expert offsets (for a caller-provided dispatch), at most
- * max_units units. */
-hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, int32_t max_units, Unit* units,
-                           int32_t* n_units, hipStream_t st);
+/* Unit lists from expert offsets (for a caller-provided dispatch), bounded
+ * by ul.max_units / ul.max_munits. */
+hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, const UnitLists& ul,
+                           hipStream_t st);
 
+/* GEMV and MFMA kernel families; each launches nothing when its units are
+ * impossible for the batch. */
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st);
+hipError_t launch_ffn_gate_up_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
+hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int32_t S,
                           int32_t k, int32_t H, int32_t shared_row0, float* out, hipStream_t st);

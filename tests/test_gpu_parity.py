@@ -116,10 +116,18 @@ def _ffn_case(bits, H, I, E, S, k, seed):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 2])
-@pytest.mark.parametrize("H,I,E,S,k", [(256, 128, 16, 13, 3), (96, 64, 4, 9, 2), (512, 256, 3, 11, 3)])
-def test_expert_ffn_bit_exact(qre, bits, H, I, E, S, k):
-    say(f"ffn bits={bits} H={H} I={I} E={E} S={S} k={k}")
+@pytest.mark.parametrize("H,I,E,S,k,scale", [
+    (256, 128, 16, 13, 3, 1.0),   # GEMV units (experts with few tokens)
+    (96, 64, 4, 9, 2, 1.0),       # ragged 64-row tail of the down projection
+    (512, 256, 3, 11, 3, 1.0),    # experts with >= 8 tokens: int8 matrix cores
+    (256, 160, 2, 100, 2, 1.0),   # two 64-token MFMA units per expert, ragged N tile
+    (96, 96, 5, 40, 3, 1.0),      # MFMA with ragged rows and K tails
+    (256, 128, 3, 24, 2, 1e-36),  # tiny activations: block scale * 2^-(8-b) subnormal
+])
+def test_expert_ffn_bit_exact(qre, bits, H, I, E, S, k, scale):
+    say(f"ffn bits={bits} H={H} I={I} E={E} S={S} k={k} scale={scale}")
     g, u, d, x, ids = _ffn_case(bits, H, I, E, S, k, seed=bits * 100 + H + S)
+    x = (x * np.float32(scale)).astype(np.float32)
     xq, xd = oracle.quantize_q8_0(x)
     disp = oracle.dispatch(ids, E)
     y_ref = np.empty((S * k, H), np.float32)
@@ -160,6 +168,13 @@ SMALL_LAYERS = {
                      top_k=4, S=24, has_shared=True, rsf=2.5, var_router=1.0 / 1024, var_bias=1e-4),
     "one_expert": dict(name="one", layer="one", n_experts=4, top_k=1, S=5),
     "all_experts": dict(name="all", layer="all", n_experts=8, top_k=8, S=6, has_shared=True),
+    # experts with >= 8 tokens and a shared expert over S >= 8 run on the matrix cores
+    "mfma_int4": dict(name="mf4", layer="mf4", bits=4, hidden=512, inter=256, n_experts=8, top_k=2,
+                      S=64, has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
+    "mfma_int8_mixed": dict(name="mf8", layer="mf8", bits=8, hidden=256, inter=128, n_experts=32,
+                            top_k=4, S=40, has_shared=True),
+    "mfma_int2_long": dict(name="mf2", layer="mf2", bits=2, hidden=256, inter=192, n_experts=4,
+                           top_k=2, S=150, has_shared=True),
 }
 
 
