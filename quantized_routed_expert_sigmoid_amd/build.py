@@ -25,9 +25,14 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
 
 
+# The matrix-core kernels keep MFMA results in ordinary VGPRs (no
+# accumulation-register copies between the MFMA and the fp32 fold).
+EXTRA = {"ffn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is expected
     noise = "'-packed-fp32-ops' is not a recognized feature"

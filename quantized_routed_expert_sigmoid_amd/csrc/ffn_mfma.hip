@@ -7,7 +7,7 @@
  * gate and up in one dispatch).
  *
  * Work unit: one expert and up to kMfmaUnitTokens of its sorted positions
- * (up to four N-tiles of 16 tokens).  A 256-thread workgroup covers 64 row
+ * (up to two N-tiles of 16 tokens).  A 256-thread workgroup covers 64 row
  * dots (gate/up kernel: 32 gate rows and the same 32 up rows, one 32-block of
  * h; down kernel: 64 output rows); wave w owns the 16-row M-tile w.
  *
@@ -16,14 +16,18 @@
  * enter as their packed fields shifted to the top of each byte (2^(8-b) * v,
  * see qdot.h) and activations in the matching operand order; the 2^(8-b)
  * factor is taken out of the block scale (exact whenever d * 2^-(8-b) is a
- * normal number; otherwise the wave shifts the partials back instead).  The
- * fp32 fold is the canonical one: four consecutive block groups, each from +0
- * in ascending block order, group sums added in order, then the row scale.
+ * normal number; a K step holding any other scale shifts the partials back
+ * instead).  The fp32 fold is the canonical one: four consecutive block
+ * groups, each from +0 in ascending block order, group sums added in order,
+ * then the row scale.
  *
- * Per K step of four blocks the workgroup stages the weight tile (64 rows x 4
- * blocks) and the activation tile (64 tokens x 4 blocks, operand order, with
- * scales) in LDS, double-buffered: the next step's global loads are in flight
- * while the current step's MFMAs and folds run.
+ * Memory pipeline.  A K step is 128 bytes of every weight row (8 blocks of
+ * int4 / int2 half that, 4 blocks of int8) and the matching activation
+ * blocks of the unit's tokens.  Each thread holds two steps of global loads
+ * in registers while the workgroup multiplies a third out of LDS, so every
+ * workgroup keeps two steps (16 KB of int4 weights) in flight; one barrier
+ * per step.  LDS row strides are padded so that the MFMA operand reads of a
+ * wave hit distinct banks.
  */
 #include "device_common.h"
 #include "kernels.h"
@@ -32,23 +36,34 @@ namespace coli {
 
 namespace {
 
-constexpr int kStep = 4;   /* K blocks per step */
-constexpr int kTokPad = 9; /* operand words per (token, block) in LDS (8 + 1 pad) */
+constexpr int kTok = kMfmaUnitTokens; /* tokens of a unit (N) */
 
 template <int BITS>
-struct MfmaLds {
-    uint32_t a[2][64][kStep][BITS + 1];  /* weight tile, natural packed words (+1 pad) */
-    uint32_t b[2][64][kStep][kTokPad];   /* activation operands */
-    float d[2][64][kStep];               /* activation block scales */
+struct Cfg {
+    static constexpr int kStep = BITS == 8 ? 4 : 8;                   /* K blocks per step */
+    static constexpr int kRowWords = kStep * BITS;                    /* packed words per row and step */
+    static constexpr int kRowStride = kRowWords + (BITS == 2 ? 1 : 2); /* LDS words per row */
+    static constexpr int kBpt = kStep / 4;                            /* weight blocks per loading thread */
+    static constexpr int kXpt = kStep == 8 ? 8 : 4;                   /* activation words per loading thread */
+};
+
+/* LDS of the K loop, double-buffered. */
+template <int BITS>
+struct KLds {
+    uint32_t a[2][64 * Cfg<BITS>::kRowStride];              /* weight rows, packed words */
+    uint32_t b[2][Cfg<BITS>::kStep][4][kTok][2];           /* operand words 2g, 2g+1 per (block, g, token) */
+    float ds[2][Cfg<BITS>::kStep][kTok];                    /* block scale * 2^-(8-b) */
+    float dr[2][Cfg<BITS>::kStep][kTok];                    /* block scale */
+    int flag[2];                                            /* step whose scales need the exact-shift fold */
 };
 
 struct EpiLds {
-    float v[64][65];                     /* [row dot][token] */
+    float v[64][kTok + 1]; /* [row dot][token] */
 };
 
 template <int BITS>
 union MfmaShared {
-    MfmaLds<BITS> k;
+    KLds<BITS> k;
     EpiLds e;
 };
 
@@ -90,12 +105,12 @@ __device__ __forceinline__ bool munit_info(const FfnSeg& sg, int u, int& e, int&
         ntok = U.ntok;
     } else {
         e = 0;
-        pos0 = u * kMfmaUnitTokens;
-        ntok = kMfmaUnitTokens;
+        pos0 = u * kTok;
+        ntok = kTok;
     }
     if (e < 0 || e >= sg.n_mat || pos0 < 0 || pos0 >= sg.rows || ntok <= 0)
         return false;
-    ntok = min(min(ntok, kMfmaUnitTokens), sg.rows - pos0);
+    ntok = min(min(ntok, kTok), sg.rows - pos0);
     return true;
 }
 
@@ -109,80 +124,112 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-/* Registers holding one thread's share of the next step's global loads. */
+/* One thread's share of a K step's global loads. */
 template <int BITS>
-struct Prefetch {
-    uint32_t w[BITS];
-    uint32_t x[8];
+struct Stage {
+    uint32_t w[Cfg<BITS>::kBpt * BITS];
+    uint32_t x[Cfg<BITS>::kXpt];
     float d;
 };
 
-/* Thread l of the workgroup loads block (b0 + (l & 3)) of row dot (l >> 2)
- * and of token (l >> 2). */
+/* Where a thread loads from.  Weights: row dot (l >> 2), blocks kBpt*(l & 3)
+ * .. of the step.  Activations: token (l & 31), block (l >> 5) of the step
+ * (int8: block (l >> 6), half ((l >> 5) & 1)).  Block indices past the row
+ * are clamped to its last block: those loads stay in bounds and their data
+ * is never multiplied. */
+struct LoadLane {
+    const uint8_t* wrow;
+    const int8_t* xrow;
+    const float* xdrow;
+    int nb;
+};
+
 template <int BITS>
-__device__ __forceinline__ void fetch(Prefetch<BITS>& P, const uint8_t* wrow, int64_t rowbytes,
-                                      bool row_ok, const int8_t* xrow, const float* xdrow, bool tok_ok,
-                                      int b, int nb)
+__device__ __forceinline__ void fetch(Stage<BITS>& P, const LoadLane& L, int st)
 {
-    (void)rowbytes;
-    const bool blk_ok = b < nb;
-    if (row_ok && blk_ok) {
-        const uint8_t* p = wrow + (int64_t)b * (4 * BITS);
+    using C = Cfg<BITS>;
+    const int l = threadIdx.x;
+    const int wb0 = st * C::kStep + C::kBpt * (l & 3);
+#pragma unroll
+    for (int i = 0; i < C::kBpt; ++i) {
+        const int b = min(wb0 + i, L.nb - 1);
+        const uint8_t* p = L.wrow + (int64_t)b * (4 * BITS);
         if constexpr (BITS == 8) {
-            const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+            const u32x4 u = reinterpret_cast<const u32x4*>(p)[0];
+            const u32x4 v = reinterpret_cast<const u32x4*>(p)[1];
             P.w[0] = u.x; P.w[1] = u.y; P.w[2] = u.z; P.w[3] = u.w;
             P.w[4] = v.x; P.w[5] = v.y; P.w[6] = v.z; P.w[7] = v.w;
         } else if constexpr (BITS == 4) {
-            const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-            P.w[0] = u.x; P.w[1] = u.y; P.w[2] = u.z; P.w[3] = u.w;
+            const u32x4 u = reinterpret_cast<const u32x4*>(p)[0];
+            P.w[4 * i + 0] = u.x; P.w[4 * i + 1] = u.y; P.w[4 * i + 2] = u.z; P.w[4 * i + 3] = u.w;
         } else {
-            const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-            P.w[0] = u.x; P.w[1] = u.y;
+            const u32x2 u = reinterpret_cast<const u32x2*>(p)[0];
+            P.w[2 * i + 0] = u.x; P.w[2 * i + 1] = u.y;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < BITS; ++i)
-            P.w[i] = 0;
     }
-    if (tok_ok && blk_ok) {
-        const uint4* q = reinterpret_cast<const uint4*>(xrow + (int64_t)b * 32);
-        const uint4 u = q[0], v = q[1];
+    if constexpr (C::kStep == 8) {
+        const int b = min(st * C::kStep + (l >> 5), L.nb - 1);
+        const u32x4* q = reinterpret_cast<const u32x4*>(L.xrow + (int64_t)b * 32);
+        const u32x4 u = q[0], v = q[1];
         P.x[0] = u.x; P.x[1] = u.y; P.x[2] = u.z; P.x[3] = u.w;
         P.x[4] = v.x; P.x[5] = v.y; P.x[6] = v.z; P.x[7] = v.w;
-        P.d = xdrow[b];
+        P.d = L.xdrow[b];
     } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            P.x[i] = 0;
-        P.d = 0.0f;
+        const int b = min(st * C::kStep + (l >> 6), L.nb - 1);
+        const u32x4 u = reinterpret_cast<const u32x4*>(L.xrow + (int64_t)b * 32)[(l >> 5) & 1];
+        P.x[0] = u.x; P.x[1] = u.y; P.x[2] = u.z; P.x[3] = u.w;
+        P.d = L.xdrow[b];
     }
 }
 
 template <int BITS>
-__device__ __forceinline__ void commit(const Prefetch<BITS>& P, MfmaLds<BITS>& S, int buf)
+__device__ __forceinline__ void commit(const Stage<BITS>& P, KLds<BITS>& S, int buf, int st)
 {
-    const int l = threadIdx.x, r = l >> 2, j = l & 3;
+    using C = Cfg<BITS>;
+    constexpr int SHIFT = 8 - BITS;
+    const int l = threadIdx.x;
+    uint32_t* ad = &S.a[buf][(l >> 2) * C::kRowStride + C::kBpt * BITS * (l & 3)];
 #pragma unroll
-    for (int i = 0; i < BITS; ++i)
-        S.a[buf][r][j][i] = P.w[i];
-    uint32_t xa[8];
-    prep_activation<BITS>(P.x, xa);
+    for (int i = 0; i < C::kBpt * BITS; ++i)
+        ad[i] = P.w[i];
+    const int t = l & 31;
+    int j;
+    if constexpr (C::kStep == 8) {
+        j = l >> 5;
+        uint32_t xa[8];
+        prep_activation<BITS>(P.x, xa);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        S.b[buf][r][j][i] = xa[i];
-    S.d[buf][r][j] = P.d;
+        for (int g = 0; g < 4; ++g) {
+            S.b[buf][j][g][t][0] = xa[2 * g];
+            S.b[buf][j][g][t][1] = xa[2 * g + 1];
+        }
+    } else {
+        /* int8: natural operand order, half h holds operand groups 2h, 2h+1 */
+        j = l >> 6;
+        const int h = (l >> 5) & 1;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+            S.b[buf][j][2 * h + gg][t][0] = P.x[2 * gg];
+            S.b[buf][j][2 * h + gg][t][1] = P.x[2 * gg + 1];
+        }
+    }
+    const float ds = P.d * (1.0f / (float)(1 << SHIFT));
+    S.ds[buf][j][t] = ds;
+    S.dr[buf][j][t] = P.d;
+    if (SHIFT != 0 && P.d != 0.0f && !(ds >= 1.17549435e-38f))
+        S.flag[buf] = st;
 }
 
 /* A operand of lane group g (elements 8g .. 8g+7 of the block, in the order
- * prep_activation gives the activation codes) from the row's packed words. */
+ * prep_activation gives the activation codes) from the block's packed words. */
 template <int BITS>
 __device__ __forceinline__ long a_operand(const uint32_t* w, int g)
 {
     uint32_t lo, hi;
     if constexpr (BITS == 8) {
-        lo = w[2 * g];
-        hi = w[2 * g + 1];
+        const uint2 v = *reinterpret_cast<const uint2*>(w + 2 * g);
+        lo = v.x;
+        hi = v.y;
     } else if constexpr (BITS == 4) {
         lo = w[g] & 0xF0F0F0F0u;
         hi = (w[g] << 4) & 0xF0F0F0F0u;
@@ -195,91 +242,144 @@ __device__ __forceinline__ long a_operand(const uint32_t* w, int g)
     return (long)(((uint64_t)hi << 32) | lo);
 }
 
-/* B operand of lane group g: activation operand words 2g, 2g+1. */
-__device__ __forceinline__ long b_operand(const uint32_t* xa, int g)
-{
-    return (long)(((uint64_t)xa[2 * g + 1] << 32) | xa[2 * g]);
-}
-
-/* The K loop shared by both kernels.  Returns tot[n][v]: the folded sums of
- * rows 16w + 4(lane/16) + v for token 16n + lane%16. */
-template <int BITS>
-__device__ __forceinline__ void mfma_k_loop(MfmaLds<BITS>& S, const uint8_t* wrow, int64_t rowbytes,
-                                            bool row_ok, const int8_t* xrow, const float* xdrow,
-                                            bool tok_ok, int nb, int ntiles, float (&tot)[4][4])
+/* One block of a K step: the MFMA of each N-tile and its fold into acc. */
+template <int BITS, int NT, bool EXACT_SHIFT>
+__device__ __forceinline__ void block_mfma(const KLds<BITS>& S, int buf, int j, const uint32_t* arow,
+                                           int r, int g, float (&acc)[2][4])
 {
     constexpr int SHIFT = 8 - BITS;
-    const float unscale = 1.0f / (float)(1 << SHIFT);
+    const long A = a_operand<BITS>(arow + j * BITS, g);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int t = 16 * n + r;
+        const uint2 bw = *reinterpret_cast<const uint2*>(&S.b[buf][j][g][t][0]);
+        const long B = (long)(((uint64_t)bw.y << 32) | bw.x);
+        const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        if constexpr (!EXACT_SHIFT) {
+            const float d = S.ds[buf][j][t];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[n][v] = __builtin_fmaf(d, (float)c[v], acc[n][v]);
+        } else {
+            const float d = S.dr[buf][j][t];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[n][v] = __builtin_fmaf(d, (float)(c[v] >> SHIFT), acc[n][v]);
+        }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void flush(float (&acc)[2][4], float (&tot)[2][4])
+{
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            tot[n][v] = tot[n][v] + acc[n][v];
+            acc[n][v] = 0.0f;
+        }
+}
+
+/* Multiplies one K step out of LDS buffer `buf` into acc / tot (NT N-tiles).
+ *
+ * The common step -- all kStep blocks inside the row, no canonical group
+ * boundary strictly inside it, every scale exact after the 2^-(8-b) factor --
+ * runs as straight-line code (a boundary at its first block is flushed
+ * before it).  Any other step checks each block: the row end, the group
+ * boundaries (a repeated boundary adds +0) and the shift-back fold. */
+template <int BITS, int NT>
+__device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int nb, int bnd1, int bnd2,
+                                     int bnd3, float (&acc)[2][4], float (&tot)[2][4])
+{
+    using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int j_ld = threadIdx.x & 3;
-    const int bnd1 = nb / 4, bnd2 = (2 * nb) / 4, bnd3 = (3 * nb) / 4;
-    float acc[4][4];
+    const uint32_t* arow = &S.a[buf][(16 * wv + r) * C::kRowStride];
+    const int b0 = st * C::kStep, b1 = b0 + C::kStep;
+    if (b0 >= nb)
+        return;
+    const bool exact_shift = BITS != 8 && __builtin_amdgcn_readfirstlane(S.flag[buf]) == st;
+    const bool inner = (bnd1 > b0 && bnd1 < b1) || (bnd2 > b0 && bnd2 < b1) || (bnd3 > b0 && bnd3 < b1);
+    if (b1 <= nb && !inner && !exact_shift) {
+        if (b0 == bnd1 || b0 == bnd2 || b0 == bnd3)
+            flush<NT>(acc, tot);
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+        for (int j = 0; j < C::kStep; ++j)
+            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc);
+        return;
+    }
+    for (int j = 0; j < C::kStep; ++j) {
+        const int b = b0 + j;
+        if (b >= nb)
+            break;
+        if (b == bnd1 || b == bnd2 || b == bnd3)
+            flush<NT>(acc, tot);
+        if (exact_shift)
+            block_mfma<BITS, NT, true>(S, buf, j, arow, r, g, acc);
+        else
+            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc);
+    }
+}
+
+/* The K loop shared by both kernels, for NT N-tiles.  Leaves in tot[n][v]
+ * the folded sums of row dot 16w + 4(lane/16) + v for token 16n + lane%16.
+ *
+ * Step st is multiplied out of LDS buffer st & 1.  While an even step is
+ * multiplied, P1 holds the loads of st + 1 and P0 those of st + 2 (the roles
+ * swap for odd steps).  Every fetch and commit is unconditional -- loads past
+ * the last step are clamped in bounds and their LDS copies never multiplied --
+ * so the two register sets stay put across iterations and each commit waits
+ * only for its own loads. */
+template <int BITS, int NT>
+__device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, float (&tot)[2][4])
+{
+    using C = Cfg<BITS>;
+    const int nb = L.nb;
+    const int bnd1 = nb / 4, bnd2 = (2 * nb) / 4, bnd3 = (3 * nb) / 4;
+    float acc[2][4];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             acc[n][v] = 0.0f;
             tot[n][v] = 0.0f;
         }
-    const int nsteps = (nb + kStep - 1) / kStep;
-    Prefetch<BITS> P;
-    fetch<BITS>(P, wrow, rowbytes, row_ok, xrow, xdrow, tok_ok, j_ld, nb);
-    commit<BITS>(P, S, 0);
+    const int nsteps = (nb + C::kStep - 1) / C::kStep;
+    Stage<BITS> P0, P1;
+    fetch<BITS>(P0, L, 0);
+    fetch<BITS>(P1, L, 1);
+    if (threadIdx.x < 2)
+        S.flag[threadIdx.x] = -1;
     __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nsteps)
-            fetch<BITS>(P, wrow, rowbytes, row_ok, xrow, xdrow, tok_ok, (st + 1) * kStep + j_ld, nb);
-#pragma unroll
-        for (int j = 0; j < kStep; ++j) {
-            const int b = st * kStep + j;
-            if (b >= nb)
-                break;
-            /* canonical group boundaries (a repeated boundary adds +0) */
-            const int flushes = (b == bnd1) + (b == bnd2) + (b == bnd3);
-            if (flushes) {
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        tot[n][v] = tot[n][v] + acc[n][v];
-                        acc[n][v] = 0.0f;
-                    }
-            }
-            const long A = a_operand<BITS>(S.a[buf][16 * wv + r][j], g);
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                if (n < ntiles) {
-                    const int t = 16 * n + r;
-                    const long B = b_operand(S.b[buf][t][j], g);
-                    i32x4 c = {0, 0, 0, 0};
-                    c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, c, 0, 0, 0);
-                    const float d = S.d[buf][t][j];
-                    const float ds = d * unscale;
-                    const bool exact = (d == 0.0f) || (ds >= 1.17549435e-38f);
-                    if (SHIFT == 0 || __ballot(!exact) == 0) {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[n][v] = __builtin_fmaf(SHIFT ? ds : d, (float)c[v], acc[n][v]);
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            acc[n][v] = __builtin_fmaf(d, (float)(c[v] >> SHIFT), acc[n][v]);
-                    }
-                }
-            }
-        }
+    commit<BITS>(P0, S, 0, 0);
+    fetch<BITS>(P0, L, 2);
+    __syncthreads();
+    for (int st = 0; st < nsteps; st += 2) {
+        step<BITS, NT>(S, 0, st, nb, bnd1, bnd2, bnd3, acc, tot);
+        commit<BITS>(P1, S, 1, st + 1);
+        fetch<BITS>(P1, L, st + 3);
         __syncthreads();
-        if (st + 1 < nsteps)
-            commit<BITS>(P, S, buf ^ 1);
+        step<BITS, NT>(S, 1, st + 1, nb, bnd1, bnd2, bnd3, acc, tot);
+        commit<BITS>(P0, S, 0, st + 2);
+        fetch<BITS>(P0, L, st + 4);
         __syncthreads();
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             tot[n][v] = tot[n][v] + acc[n][v];
+}
+
+template <int BITS>
+__device__ __forceinline__ void mfma_k_loop(KLds<BITS>& S, const LoadLane& L, int ntiles,
+                                            float (&tot)[2][4])
+{
+    if (ntiles > 1)
+        k_loop_nt<BITS, 2>(S, L, tot);
+    else
+        k_loop_nt<BITS, 1>(S, L, tot);
 }
 
 } // namespace
@@ -290,26 +390,27 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     __shared__ MfmaShared<BITS> sm;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = a.I / 32;
-    MLoc L;
-    if (!locate_m(a, blockIdx.x, RB, L))
+    MLoc M;
+    if (!locate_m(a, blockIdx.x, RB, M))
         return;
-    const FfnSeg sg = pick_m(a, L.seg);
+    const FfnSeg sg = pick_m(a, M.seg);
     int e, pos0, ntok;
-    if (!munit_info(sg, L.unit, e, pos0, ntok))
+    if (!munit_info(sg, M.unit, e, pos0, ntok))
         return;
     const int nb = a.H / 32;
     const int64_t rowbytes = (int64_t)a.H * BITS / 8;
-    /* this thread's load lane: row dot l>>2 (gate rows 0..31, then up) and token l>>2 */
-    const int rd = threadIdx.x >> 2;
-    const uint8_t* wrow = (rd < 32 ? sg.gate_w : sg.up_w) +
-                          ((int64_t)e * a.I + L.rb * 32 + (rd & 31)) * rowbytes;
-    const bool tok_ok = rd < ntok;
-    const int tok = token_of_m(sg, pos0 + (tok_ok ? rd : 0));
-    const int8_t* xrow = a.xq + (int64_t)tok * a.H;
-    const float* xdrow = a.xd + (int64_t)tok * nb;
+    /* load lanes: row dot l >> 2 (gate rows 0..31, then the same up rows) and
+     * token l & 31 (tokens past the unit load its first token) */
+    const int rd = threadIdx.x >> 2, tl = threadIdx.x & 31;
+    LoadLane L;
+    L.wrow = (rd < 32 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + M.rb * 32 + (rd & 31)) * rowbytes;
+    const int tok = token_of_m(sg, pos0 + (tl < ntok ? tl : 0));
+    L.xrow = a.xq + (int64_t)tok * a.H;
+    L.xdrow = a.xd + (int64_t)tok * nb;
+    L.nb = nb;
     const int ntiles = (ntok + 15) / 16;
-    float tot[4][4];
-    mfma_k_loop<BITS>(sm.k, wrow, rowbytes, true, xrow, xdrow, tok_ok, nb, ntiles, tot);
+    float tot[2][4];
+    mfma_k_loop<BITS>(sm.k, L, ntiles, tot);
 
     /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
      * h = silu(g) * u and one Q8_0 block of h per token */
@@ -317,38 +418,38 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int rdot = 16 * wv + 4 * g + v;
-        const float sc = (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + L.rb * 32 + (rdot & 31)];
+        const float sc = (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < 2; ++n)
             if (n < ntiles)
                 sm.e.v[rdot][16 * n + r] = sc * tot[n][v];
     }
     __syncthreads();
-    const int t = threadIdx.x >> 2, q = threadIdx.x & 3;
-    float h[8];
+    /* thread: token t, elements 4q .. 4q+3 of the h block */
+    const int t = threadIdx.x >> 3, q = threadIdx.x & 7;
+    float h[4];
     float am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float gv = sm.e.v[8 * q + i][t];
-        const float uv = sm.e.v[32 + 8 * q + i][t];
+    for (int i = 0; i < 4; ++i) {
+        const float gv = sm.e.v[4 * q + i][t];
+        const float uv = sm.e.v[32 + 4 * q + i][t];
         h[i] = canon_silu(gv) * uv;
         am = fmaxf(am, __builtin_fabsf(h[i]));
     }
     am = fmaxf(am, shfl_xor(am, 1));
     am = fmaxf(am, shfl_xor(am, 2));
+    am = fmaxf(am, shfl_xor(am, 4));
     if (t < ntok) {
         const float dsc = am / 127.0f;
         const float inv = (am == 0.0f) ? 0.0f : 1.0f / dsc;
-        uint32_t lo = 0, hi = 0;
+        uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lo |= (uint32_t)(q8_code(h[i], inv) & 0xFF) << (8 * i);
-            hi |= (uint32_t)(q8_code(h[4 + i], inv) & 0xFF) << (8 * i);
-        }
+        for (int i = 0; i < 4; ++i)
+            word |= (uint32_t)(q8_code(h[i], inv) & 0xFF) << (8 * i);
         const int64_t row_out = sg.out_base + pos0 + t;
-        *reinterpret_cast<uint2*>(a.hq + row_out * a.I + L.rb * 32 + 8 * q) = make_uint2(lo, hi);
+        *reinterpret_cast<uint32_t*>(a.hq + row_out * a.I + M.rb * 32 + 4 * q) = word;
         if (q == 0)
-            a.hd[row_out * (a.I / 32) + L.rb] = dsc;
+            a.hd[row_out * (a.I / 32) + M.rb] = dsc;
     }
 }
 
@@ -358,50 +459,48 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     __shared__ MfmaShared<BITS> sm;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = (a.H + 63) / 64;
-    MLoc L;
-    if (!locate_m(a, blockIdx.x, RB, L))
+    MLoc M;
+    if (!locate_m(a, blockIdx.x, RB, M))
         return;
-    const FfnSeg sg = pick_m(a, L.seg);
+    const FfnSeg sg = pick_m(a, M.seg);
     int e, pos0, ntok;
-    if (!munit_info(sg, L.unit, e, pos0, ntok))
+    if (!munit_info(sg, M.unit, e, pos0, ntok))
         return;
     const int nb = a.I / 32;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
-    const int rd = threadIdx.x >> 2;
-    const int row = L.rb * 64 + rd;
-    const bool row_ok = row < a.H;
-    const uint8_t* wrow = sg.down_w + ((int64_t)e * a.H + (row_ok ? row : 0)) * rowbytes;
-    const bool tok_ok = rd < ntok;
-    const int64_t row_in = sg.out_base + pos0 + (tok_ok ? rd : 0);
-    const int8_t* xrow = a.hq + row_in * a.I;
-    const float* xdrow = a.hd + row_in * nb;
+    const int rd = threadIdx.x >> 2, tl = threadIdx.x & 31;
+    const int row = M.rb * 64 + rd;
+    LoadLane L;
+    L.wrow = sg.down_w + ((int64_t)e * a.H + (row < a.H ? row : 0)) * rowbytes;
+    const int64_t row_in = sg.out_base + pos0 + (tl < ntok ? tl : 0);
+    L.xrow = a.hq + row_in * a.I;
+    L.xdrow = a.hd + row_in * nb;
+    L.nb = nb;
     const int ntiles = (ntok + 15) / 16;
-    float tot[4][4];
-    mfma_k_loop<BITS>(sm.k, wrow, rowbytes, row_ok, xrow, xdrow, tok_ok, nb, ntiles, tot);
+    float tot[2][4];
+    mfma_k_loop<BITS>(sm.k, L, ntiles, tot);
 
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int rr = 16 * wv + 4 * g + v;
-        const int n_out = L.rb * 64 + rr;
+        const int n_out = M.rb * 64 + rr;
         const float sc = n_out < a.H ? sg.down_s[(int64_t)e * a.H + n_out] : 0.0f;
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < 2; ++n)
             if (n < ntiles)
                 sm.e.v[rr][16 * n + r] = sc * tot[n][v];
     }
     __syncthreads();
-    /* thread: token t, rows 16q .. 16q+15 of the block */
-    const int t = threadIdx.x >> 2, q = threadIdx.x & 3;
-    if (t < ntok) {
-        float* yr = a.y + (int64_t)(sg.out_base + pos0 + t) * a.H + L.rb * 64 + 16 * q;
+    /* thread: token t, rows 8q .. 8q+7 of the block */
+    const int t = threadIdx.x >> 3, q = threadIdx.x & 7;
+    if (t < ntok && M.rb * 64 + 8 * q < a.H) {
+        float* yr = a.y + (int64_t)(sg.out_base + pos0 + t) * a.H + M.rb * 64 + 8 * q;
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            if (L.rb * 64 + 16 * q + i < a.H) {
-                const float4 o = make_float4(sm.e.v[16 * q + i][t], sm.e.v[16 * q + i + 1][t],
-                                             sm.e.v[16 * q + i + 2][t], sm.e.v[16 * q + i + 3][t]);
-                *reinterpret_cast<float4*>(yr + i) = o;
-            }
+        for (int i = 0; i < 8; i += 4) {
+            const float4 o = make_float4(sm.e.v[8 * q + i][t], sm.e.v[8 * q + i + 1][t],
+                                         sm.e.v[8 * q + i + 2][t], sm.e.v[8 * q + i + 3][t]);
+            *reinterpret_cast<float4*>(yr + i) = o;
         }
     }
 }

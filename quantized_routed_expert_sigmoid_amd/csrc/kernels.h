@@ -19,7 +19,7 @@ constexpr int kUnitTokens = 4;
  * matrix cores (ffn_mfma.hip) in units of up to kMfmaUnitTokens tokens;
  * experts with fewer run on the GEMV kernels (ffn_gemv.hip). */
 constexpr int kMfmaMinTokens = 8;
-constexpr int kMfmaUnitTokens = 64;
+constexpr int kMfmaUnitTokens = 32;
 
 /* Most (token, slot) pairs of one call (the ABI's limit). */
 constexpr int32_t kPairLimit = 1 << 20;
@@ -82,7 +82,7 @@ struct FfnArgs {
 /* Bounds on the unit counts of a routed group with P pairs of S tokens over
  * E experts (n_e pairs each, sum P, n_e <= S).  GEMV: experts with n_e <
  * kMfmaMinTokens give ceil(n_e / 4) <= 2 units each.  MFMA: experts with
- * n_e >= kMfmaMinTokens give ceil(n_e / 64) <= n_e / 64 + 1 units each. */
+ * n_e >= kMfmaMinTokens give ceil(n_e / 32) <= n_e / 32 + 1 units each. */
 inline int32_t max_gemv_units(int64_t P, int32_t E)
 {
     const int64_t active = P < E ? P : E;

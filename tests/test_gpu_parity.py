@@ -120,7 +120,7 @@ def _ffn_case(bits, H, I, E, S, k, seed):
     (256, 128, 16, 13, 3, 1.0),   # GEMV units (experts with few tokens)
     (96, 64, 4, 9, 2, 1.0),       # ragged 64-row tail of the down projection
     (512, 256, 3, 11, 3, 1.0),    # experts with >= 8 tokens: int8 matrix cores
-    (256, 160, 2, 100, 2, 1.0),   # two 64-token MFMA units per expert, ragged N tile
+    (256, 160, 2, 100, 2, 1.0),   # several 32-token MFMA units per expert, ragged N tile
     (96, 96, 5, 40, 3, 1.0),      # MFMA with ragged rows and K tails
     (256, 128, 3, 24, 2, 1e-36),  # tiny activations: block scale * 2^-(8-b) subnormal
 ])
