@@ -110,7 +110,7 @@ Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S, bool 
     const int64_t rows = P + (shared ? S : 0);
     Bump b;
     Layout L;
-    L.logits = b.take((size_t)S * E * 4);
+    L.logits = b.take((size_t)router_parts(S, E, H) * S * E * 4);
     L.units = b.take((size_t)max_gemv_units(P, E) * sizeof(Unit));
     L.n_units = b.take(16);
     L.munits = b.take((size_t)max_mfma_units(P, E, S) * sizeof(Unit));
@@ -279,8 +279,8 @@ int colibri_route(const coli_moe_layer* L, const float* x, int32_t S, int32_t* t
     float* logits = at<float>(ws, Lo.logits);
     hipError_t e = launch_router_logits(x, S, L->hidden, L->n_experts, L->router_w, logits, s);
     if (e == hipSuccess)
-        e = launch_router_select(logits, L->router_bias, S, L->n_experts, L->top_k,
-                                 L->routed_scaling_factor, topk_ids, topk_w, s);
+        e = launch_router_select(logits, router_parts(S, L->n_experts, L->hidden), L->router_bias, S,
+                                 L->n_experts, L->top_k, L->routed_scaling_factor, topk_ids, topk_w, s);
     return hip_status(e);
 }
 
@@ -422,7 +422,8 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     if (e == hipSuccess && S > kSmallS)
         e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
     if (e == hipSuccess && S > kSmallS)
-        e = launch_router_select(logits, L->router_bias, S, E, k, L->routed_scaling_factor, ids, w, s);
+        e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
+                                 L->routed_scaling_factor, ids, w, s);
     e = mark(1, e);
     if (e == hipSuccess)
         e = S <= kSmallS

@@ -110,14 +110,33 @@ inline int32_t identity_mfma_units(int32_t S)
     return S >= kMfmaMinTokens ? (S + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
 }
 
+/* K slices of the many-token router logits (S > kSmallS): enough 64 x 64
+ * tiles times slices for about 512 workgroups, at most 16 slices and one
+ * 16-wide k chunk per slice; 1 for small batches.  The logits buffer holds
+ * router_parts * S * E floats. */
+inline int32_t router_parts(int32_t S, int32_t E, int32_t H)
+{
+    if (S <= kSmallS)
+        return 1;
+    const int64_t tiles = (int64_t)((S + 63) / 64) * ((E + 63) / 64);
+    int64_t p = (512 + tiles - 1) / tiles;
+    if (p > 16)
+        p = 16;
+    if (p > H / 16)
+        p = H / 16;
+    return (int32_t)(p < 1 ? 1 : p);
+}
+
 hipError_t launch_quantize_q8_0(const float* x, int64_t n_blocks, int8_t* q, float* d,
                                 hipStream_t st);
 
+/* Writes router_parts(S, E, H) partial logit slices [part][S][E]. */
 hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
                                 const float* w, float* logits, hipStream_t st);
 
-hipError_t launch_router_select(const float* logits, const float* bias, int32_t S, int32_t E,
-                                int32_t k, float rsf, int32_t* ids, float* weights,
+/* Selection from n_parts partial logit slices (added in slice order). */
+hipError_t launch_router_select(const float* logits, int32_t n_parts, const float* bias, int32_t S,
+                                int32_t E, int32_t k, float rsf, int32_t* ids, float* weights,
                                 hipStream_t st);
 
 /* S <= kSmallS: router logits and Q8_0 quantisation of x in one launch. */

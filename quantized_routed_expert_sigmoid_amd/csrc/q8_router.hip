@@ -57,8 +57,8 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t n_blocks, int8_t* q, flo
 /* ---- router logits --------------------------------------------------------
  * Few tokens: one 256-thread workgroup per expert streams its router row once
  * (float4, coalesced, each wave a quarter of the row), keeps one partial sum
- * per token and reduces across lanes and waves.  Many tokens: 32 x 32 output
- * tiles through LDS.  Both sum in fp32 (the order is free: only the
+ * per token and reduces across lanes and waves.  Many tokens: fp32 matrix
+ * cores over 64 x 64 output tiles and K slices.  Both sum in fp32 (the order is free: only the
  * selection decision depends on it, and inputs keep a score gap).
  *
  * With xq != nullptr the small-batch kernel also quantises x: workgroups
@@ -135,56 +135,86 @@ __global__ __launch_bounds__(256) void router_logits_small(const float* __restri
             ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
 }
 
-constexpr int kTile = 32;
-constexpr int kTileK = 32;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void router_logits_tiled(const float* __restrict__ x, int32_t S,
-                                                           int32_t H, int32_t E,
-                                                           const float* __restrict__ w,
-                                                           float* __restrict__ logits)
+/* Many tokens: fp32 matrix cores (v_mfma_f32_16x16x4f32).  A workgroup
+ * computes a 64-token x 64-expert tile of one K slice; the launch splits K
+ * into n_parts slices so that it fills the chip, and the selection kernel
+ * adds the slices in order.  Wave (wm, wn) owns 32 tokens x 32 experts, 2 x 2
+ * MFMA tiles.  Operands come straight from global memory: lane (r, kg) loads
+ * four consecutive k of each of its token rows and expert rows, and MFMA i of
+ * a 16-k chunk takes element i -- any assignment of k to MFMA slots is exact
+ * as long as both operands use the same one.  Rows past S or E load the last
+ * row; their results are not stored. */
+__global__ __launch_bounds__(256) void router_logits_mfma(const float* __restrict__ x, int32_t S,
+                                                          int32_t H, int32_t E,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ part, int32_t n_parts)
 {
-    __shared__ float xs[kTileK][kTile + 1];
-    __shared__ float ws[kTileK][kTile + 1];
-    int t0 = blockIdx.x * kTile, e0 = blockIdx.y * kTile;
-    int tid = threadIdx.x;
-    int tr = (tid / 16) * 2, tc = (tid % 16) * 2; /* 2 x 2 outputs per thread */
-    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    int lr = tid / 8, lk = (tid % 8) * 4; /* loader: row lr, 4 consecutive k */
-    for (int k0 = 0; k0 < H; k0 += kTileK) {
-        {
-            int t = t0 + lr;
-            float4 v = (t < S) ? *reinterpret_cast<const float4*>(x + (int64_t)t * H + k0 + lk)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            xs[lk + 0][lr] = v.x;
-            xs[lk + 1][lr] = v.y;
-            xs[lk + 2][lr] = v.z;
-            xs[lk + 3][lr] = v.w;
-            int e = e0 + lr;
-            float4 u = (e < E) ? *reinterpret_cast<const float4*>(w + (int64_t)e * H + k0 + lk)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            ws[lk + 0][lr] = u.x;
-            ws[lk + 1][lr] = u.y;
-            ws[lk + 2][lr] = u.z;
-            ws[lk + 3][lr] = u.w;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < kTileK; ++kk) {
-            float a0 = xs[kk][tr], a1 = xs[kk][tr + 1];
-            float b0 = ws[kk][tc], b1 = ws[kk][tc + 1];
-            acc[0][0] = __builtin_fmaf(a0, b0, acc[0][0]);
-            acc[0][1] = __builtin_fmaf(a0, b1, acc[0][1]);
-            acc[1][0] = __builtin_fmaf(a1, b0, acc[1][0]);
-            acc[1][1] = __builtin_fmaf(a1, b1, acc[1][1]);
-        }
-        __syncthreads();
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int r = lane & 15, kg = lane >> 4;
+    const int p = blockIdx.x % n_parts;
+    const int tile = blockIdx.x / n_parts;
+    const int tiles_e = (E + 63) / 64;
+    const int t0 = (tile / tiles_e) * 64 + (wv >> 1) * 32;
+    const int e0 = (tile % tiles_e) * 64 + (wv & 1) * 32;
+    const float* xr[2];
+    const float* wr[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        xr[m] = x + (int64_t)min(t0 + 16 * m + r, S - 1) * H + 4 * kg;
+        wr[m] = w + (int64_t)min(e0 + 16 * m + r, E - 1) * H + 4 * kg;
     }
-    for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j) {
-            int t = t0 + tr + i, e = e0 + tc + j;
-            if (t < S && e < E)
-                logits[(int64_t)t * E + e] = acc[i][j];
+    const int nchunk = H / 16;
+    const int c0 = (int)((int64_t)p * nchunk / n_parts);
+    const int c1 = (int)((int64_t)(p + 1) * nchunk / n_parts);
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+            acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float4 a[2], b[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        a[m] = *reinterpret_cast<const float4*>(xr[m] + (int64_t)c0 * 16);
+        b[m] = *reinterpret_cast<const float4*>(wr[m] + (int64_t)c0 * 16);
+    }
+    for (int c = c0; c < c1; ++c) {
+        const int cn = min(c + 1, c1 - 1);
+        float4 an[2], bn[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            an[m] = *reinterpret_cast<const float4*>(xr[m] + (int64_t)cn * 16);
+            bn[m] = *reinterpret_cast<const float4*>(wr[m] + (int64_t)cn * 16);
         }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].x, b[n].x, acc[m][n], 0, 0, 0);
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].y, b[n].y, acc[m][n], 0, 0, 0);
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].z, b[n].z, acc[m][n], 0, 0, 0);
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].w, b[n].w, acc[m][n], 0, 0, 0);
+            }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            a[m] = an[m];
+            b[m] = bn[m];
+        }
+    }
+    /* lane holds D[4 kg + v][r]: token t0 + 16m + 4kg + v, expert e0 + 16n + r */
+    float* out = part + (int64_t)p * S * E;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + 16 * m + 4 * kg + v, e = e0 + 16 * n + r;
+                if (t < S && e < E)
+                    out[(int64_t)t * E + e] = acc[m][n][v];
+            }
 }
 
 hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
@@ -196,8 +226,10 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
         hipLaunchKernelGGL(router_logits_small, dim3(E), dim3(256), 0, st, x, S, H, E, w, logits,
                            (int8_t*)nullptr, (float*)nullptr);
     } else {
-        dim3 grid((S + kTile - 1) / kTile, (E + kTile - 1) / kTile);
-        hipLaunchKernelGGL(router_logits_tiled, grid, dim3(256), 0, st, x, S, H, E, w, logits);
+        const int32_t parts = router_parts(S, E, H);
+        const int64_t tiles = (int64_t)((S + 63) / 64) * ((E + 63) / 64);
+        hipLaunchKernelGGL(router_logits_mfma, dim3((uint32_t)(tiles * parts)), dim3(256), 0, st, x, S, H,
+                           E, w, logits, parts);
     }
     return hipGetLastError();
 }
@@ -217,6 +249,7 @@ hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t
 /* ---- router selection: one wave per token (select.h) ------------------- */
 
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ logits,
+                                                            int32_t n_parts,
                                                             const float* __restrict__ bias,
                                                             int32_t S, int32_t E, int32_t k,
                                                             float rsf, int32_t* __restrict__ ids,
@@ -228,16 +261,17 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
     if (t >= S)
         return;
     select_token(logits + (int64_t)t * E, bias, E, k, rsf, ids + (int64_t)t * k,
-                 weights + (int64_t)t * k, sel_s[wv], nullptr);
+                 weights + (int64_t)t * k, sel_s[wv], nullptr, n_parts, (int64_t)S * E);
 }
 
-hipError_t launch_router_select(const float* logits, const float* bias, int32_t S, int32_t E,
-                                int32_t k, float rsf, int32_t* ids, float* weights, hipStream_t st)
+hipError_t launch_router_select(const float* logits, int32_t n_parts, const float* bias, int32_t S,
+                                int32_t E, int32_t k, float rsf, int32_t* ids, float* weights,
+                                hipStream_t st)
 {
     if (S == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(router_select_kernel, dim3((S + 3) / 4), dim3(256), 0, st, logits, bias, S, E,
-                       k, rsf, ids, weights);
+    hipLaunchKernelGGL(router_select_kernel, dim3((S + 3) / 4), dim3(256), 0, st, logits, n_parts, bias,
+                       S, E, k, rsf, ids, weights);
     return hipGetLastError();
 }
 

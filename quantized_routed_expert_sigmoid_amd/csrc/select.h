@@ -5,8 +5,9 @@
  * noaux_tc selection bias, routed_scaling_factor).
  *
  * Each lane holds the scores of experts lane, lane+64, ...; the top-k is k
- * rounds of a wave-wide maximum over 64-bit keys (order-preserving score bits
- * above the complemented expert id, so equal scores resolve to the lower id).
+ * rounds of a wave-wide maximum of the order-preserving bits of the biased
+ * score followed by a wave-wide minimum of the expert ids holding it (equal
+ * scores resolve to the lower id).
  * Weights: rsf * s_j / sum of the selected unbiased scores (slot order).
  */
 #ifndef COLI_SELECT_H
@@ -24,12 +25,14 @@ __device__ __forceinline__ uint32_t order_bits(float c)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-/* lt: the token's E logits; writes ids_out[0..k), w_out[0..k) and, when
+/* lt: the token's E logits, or with n_parts > 1 the first of n_parts partial
+ * sums part_stride floats apart (added in slice order); writes ids_out[0..k), w_out[0..k) and, when
  * ids_lds is not null, ids_lds[0..k).  sel_s: 64 floats of LDS owned by the
  * calling wave. */
 __device__ __forceinline__ void select_token(const float* lt, const float* bias, int32_t E, int32_t k,
                                              float rsf, int32_t* ids_out, float* w_out, float* sel_s,
-                                             int32_t* ids_lds)
+                                             int32_t* ids_lds, int32_t n_parts = 1,
+                                             int64_t part_stride = 0)
 {
     const int lane = threadIdx.x & 63;
     const int per_lane = (E + 63) / 64; /* uniform */
@@ -39,7 +42,10 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
     for (int i = 0; i < kMaxPerLane; ++i) {
         const int e = lane + 64 * i;
         if (i < per_lane && e < E) {
-            const float sg = 1.0f / (1.0f + expf(-lt[e]));
+            float l = lt[e];
+            for (int p = 1; p < n_parts; ++p) /* K slices, added in order */
+                l = l + lt[p * part_stride + e];
+            const float sg = 1.0f / (1.0f + expf(-l));
             s[i] = sg;
             key[i] = order_bits(sg + bias[e]);
         } else {

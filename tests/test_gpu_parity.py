@@ -56,12 +56,21 @@ def _small_layer(name, **kw):
     return w, synth.make_layer(w)
 
 
-@pytest.mark.parametrize("case", ["tiny", "wide_k", "decode_router"])
+@pytest.mark.parametrize("case", ["tiny", "wide_k", "ragged_tiles", "decode_router", "glm_router_s70"])
 def test_route_parity(qre, case):
+    """Small batches take the one-workgroup-per-expert router; larger ones the
+    matrix-core router with K slices (ragged 64 x 64 tiles included)."""
     if case == "tiny":
         w, L = _small_layer("tiny_r")
     elif case == "wide_k":
         w, L = _small_layer("wide_k", layer="wide_k", n_experts=64, top_k=6, S=37, rsf=2.5)
+    elif case == "ragged_tiles":
+        w, L = _small_layer("ragged_r", layer="ragged_r", hidden=512, n_experts=100, top_k=6, S=300,
+                            rsf=2.5, var_router=1.0 / 512)
+    elif case == "glm_router_s70":
+        base = synth.WORKLOADS["prefill"]
+        w = synth.scaled(base, name="router_s70", S=70)
+        L = synth.Layer(w, synth.router_weights(w), synth.router_bias(w), None, None, None, None, None, None)
     else:
         base = synth.WORKLOADS["decode"]
         w = synth.scaled(base, name="router_only", S=16)
