@@ -66,6 +66,16 @@ def stage_bytes(w, n_units_touched, S):
     }
 
 
+def stage_kernel(w, stage):
+    """The kernel(s) one FFN stage launches for this workload."""
+    if w.S == 1:
+        return {"gate_up": f"ffn_gate_up_decode<{w.bits}> (top-k selection + gate/up GEMV)",
+                "down": f"ffn_down_decode<{w.bits}>"}[stage]
+    if w.S < 8:
+        return f"ffn_{stage}_gemv<{w.bits},4>"
+    return f"ffn_{stage}_gemv<{w.bits},4> + ffn_{stage}_mfma<{w.bits}>"
+
+
 def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True):
     import numpy as np
     dev_layers = []
@@ -206,7 +216,7 @@ def main():
                                f"top-{w.top_k} int{w.bits} weights + shared expert, S={w.S}",
                    "S": w.S, "weights": f"int{w.bits}", "layer_copies_rotated": args.copies,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": f"ffn_{dom}_gemv<{w.bits}>", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": stage_kernel(w, dom), "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None},
         "layer": {"algorithmic_bytes": layer_bytes, "unique_routed_experts": res["mean_unique_experts"],

@@ -414,24 +414,6 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
             return prev;
         return hipEventRecord((hipEvent_t)stage_events[i], s);
     };
-    hipError_t e = mark(0, hipSuccess);
-    if (e == hipSuccess)
-        e = S <= kSmallS
-                ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
-                : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
-    if (e == hipSuccess && S > kSmallS)
-        e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
-    if (e == hipSuccess && S > kSmallS)
-        e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
-                                 L->routed_scaling_factor, ids, w, s);
-    e = mark(1, e);
-    if (e == hipSuccess)
-        e = S <= kSmallS
-                ? launch_select_dispatch_small(logits, L->router_bias, S, E, k, L->routed_scaling_factor,
-                                               ids, w, offsets, sorted, inv, active, n_active, ul, s)
-                : launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, s);
-    e = mark(2, e);
-
     FfnArgs a;
     a.seg[0] = make_seg(&L->gate, &L->up, &L->down, sorted, &ul, k, S, P, 0);
     a.nseg = 1;
@@ -457,6 +439,51 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     } else {
         b.nseg = 0;
     }
+
+    /* One token whose shared expert (if any) runs in the routed launches:
+     * router logits with quantisation, selection with gate/up, down, combine. */
+    const bool one_token = S == 1 && b.nseg == 0;
+
+    hipError_t e = mark(0, hipSuccess);
+    if (e == hipSuccess)
+        e = S <= kSmallS
+                ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
+                : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
+    if (e == hipSuccess && S > kSmallS)
+        e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
+    if (e == hipSuccess && S > kSmallS)
+        e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
+                                 L->routed_scaling_factor, ids, w, s);
+    e = mark(1, e);
+    if (one_token) {
+        DecodeArgs dd;
+        dd.f = a;
+        dd.logits = logits;
+        dd.bias = L->router_bias;
+        dd.E = E;
+        dd.k = k;
+        dd.rsf = L->routed_scaling_factor;
+        dd.ids = ids;
+        dd.w = w;
+        e = mark(2, e);
+        if (e == hipSuccess)
+            e = launch_ffn_gate_up_decode(dd, L->gate.qtype, s);
+        e = mark(3, e);
+        if (e == hipSuccess)
+            e = launch_ffn_down_decode(dd, L->down.qtype, s);
+        e = mark(4, e);
+        if (e == hipSuccess)
+            e = launch_combine(y, nullptr, w, 1, k, H, shared ? k : -1, out, s);
+        e = mark(5, e);
+        return hip_status(e);
+    }
+    if (e == hipSuccess)
+        e = S <= kSmallS
+                ? launch_select_dispatch_small(logits, L->router_bias, S, E, k, L->routed_scaling_factor,
+                                               ids, w, offsets, sorted, inv, active, n_active, ul, s)
+                : launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, s);
+    e = mark(2, e);
+
     if (e == hipSuccess)
         e = launch_ffn_gate_up(a, L->gate.qtype, s);
     if (e == hipSuccess)

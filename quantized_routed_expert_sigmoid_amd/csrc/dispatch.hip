@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int j = 0; j < k; ++j) {
         const int32_t p = t * k + j;
         const float wj = w[p];
-        const float4 v = reinterpret_cast<const float4*>(y + (int64_t)inv[p] * H)[c];
+        const float4 v = reinterpret_cast<const float4*>(y + (int64_t)(inv ? inv[p] : p) * H)[c];
         acc.x = __builtin_fmaf(wj, v.x, acc.x);
         acc.y = __builtin_fmaf(wj, v.y, acc.y);
         acc.z = __builtin_fmaf(wj, v.z, acc.z);

@@ -26,6 +26,7 @@
  */
 #include "device_common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace coli {
 
@@ -225,6 +226,37 @@ __device__ __forceinline__ void stage_activations(WaveLds<TMAX>& L, int b_begin,
     wave_lds_sync();
 }
 
+/* One token's block of the wave's group, held in registers between its load
+ * and its LDS commit (so other loads can be issued in between). */
+struct TokenBlock {
+    uint32_t x[8];
+    float d;
+};
+
+__device__ __forceinline__ void load_token_block(TokenBlock& T, const int8_t* act, const float* scl,
+                                                 int b_begin, int b_end)
+{
+    const int b = min(b_begin + (int)(threadIdx.x & 63), b_end - 1);
+    load_codes(act + (int64_t)b * 32, T.x);
+    T.d = scl[b];
+}
+
+template <int BITS>
+__device__ __forceinline__ void commit_token_block(const TokenBlock& T, WaveLds<1>& L, int b_begin,
+                                                   int b_end)
+{
+    const int lane = threadIdx.x & 63;
+    if (b_begin + lane < b_end) {
+        uint32_t xa[8];
+        prep_activation<BITS>(T.x, xa);
+        uint4* dst = reinterpret_cast<uint4*>(L.xa[0][lane]);
+        dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+        dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+        L.d[0][lane] = T.d;
+    }
+    wave_lds_sync();
+}
+
 /* Block partials of K step st of the wave's group (nblk blocks), transposed
  * through the wave's LDS, folded into acc (lane = row 8o + j of the octet). */
 template <int BITS, int TMAX>
@@ -266,19 +298,28 @@ __device__ __forceinline__ void fold_step(const StepWeights<BITS>& W, int st, in
     wave_lds_sync();
 }
 
+/* Issues the weight loads of the first K step of a wave's fold group. */
+template <int BITS>
+__device__ __forceinline__ void first_step(StepWeights<BITS>& A, const uint8_t* row0, int64_t rowbytes,
+                                           int b_begin, int b_end, int rows_ok)
+{
+    const int j8 = threadIdx.x & 7;
+    load_step<BITS>(A, row0, rowbytes, b_begin + j8, j8 < b_end - b_begin, rows_ok);
+}
+
 /* The K loop of one wave over its fold group, blocks [b_begin, b_end), in
  * steps of 8 blocks, the next step's weight loads issued before the current
- * step is computed.  Waves of a workgroup run their loops independently. */
+ * step is computed; A holds the first step (first_step).  Waves of a
+ * workgroup run their loops independently. */
 template <int BITS, int TMAX>
-__device__ __forceinline__ void k_loop(const uint8_t* row0, int64_t rowbytes, int b_begin, int b_end,
-                                       int ntok, int rows_ok, WaveLds<TMAX>& L, float (&acc)[TMAX])
+__device__ __forceinline__ void k_loop(StepWeights<BITS>& A, const uint8_t* row0, int64_t rowbytes,
+                                       int b_begin, int b_end, int ntok, int rows_ok, WaveLds<TMAX>& L,
+                                       float (&acc)[TMAX])
 {
     const int j8 = threadIdx.x & 7;
     const int nblk = b_end - b_begin;
     const int nsteps = (nblk + 7) / 8;
-    StepWeights<BITS> A, B;
-    if (nsteps > 0)
-        load_step<BITS>(A, row0, rowbytes, b_begin + j8, j8 < nblk, rows_ok);
+    StepWeights<BITS> B;
     for (int st = 0; st < nsteps; st += 2) {
         const int l1 = 8 * (st + 1) + j8, l2 = 8 * (st + 2) + j8;
         if (st + 1 < nsteps)
@@ -340,15 +381,17 @@ __global__ __launch_bounds__(256) void ffn_gate_up_gemv(FfnArgs a)
         scl[t] = a.xd + (int64_t)tok * nb;
     }
     const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
-    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
     /* octets 0..3: gate rows rb*32 + 8o ..; octets 4..7: the same up rows */
     const uint8_t* row0 = (o < 4 ? sg.gate_w : sg.up_w) +
                           ((int64_t)e * a.I + L.rb * 32 + 8 * (o & 3)) * rowbytes;
+    StepWeights<BITS> A;
+    first_step<BITS>(A, row0, rowbytes, b0, b1, 8);
+    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
     float acc[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
         acc[t] = 0.0f;
-    k_loop<BITS, TMAX>(row0, rowbytes, b0, b1, ntok, 8, lds[wv], acc);
+    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, 8, lds[wv], acc);
     sum_groups<TMAX>(gsum, acc);
     if (wv != 0)
         return;
@@ -403,15 +446,17 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
         scl[t] = a.hd + row_in * nb;
     }
     const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
-    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
     const int first = L.rb * kRowsPerJob + 8 * o;
     const int rows_ok = min(8, max(0, a.H - first));
     const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + first) * rowbytes;
+    StepWeights<BITS> A;
+    first_step<BITS>(A, row0, rowbytes, b0, b1, rows_ok);
+    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
     float acc[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
         acc[t] = 0.0f;
-    k_loop<BITS, TMAX>(row0, rowbytes, b0, b1, ntok, rows_ok, lds[wv], acc);
+    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, rows_ok, lds[wv], acc);
     sum_groups<TMAX>(gsum, acc);
     if (wv != 0)
         return;
@@ -424,6 +469,114 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
             if (t < ntok)
                 a.y[(int64_t)(sg.out_base + pos0 + t) * a.H + n] = sc * acc[t];
     }
+}
+
+/* ---- one-token batches ---------------------------------------------------
+ * Unit u < k is the expert of selection slot u, unit k the shared expert;
+ * hq / hd / y row u belongs to unit u, so the combine reads y in slot order.
+ * The gate/up kernel selects the experts itself: every wave runs the top-k
+ * over the token's logits (the same selection as router_select_kernel), so
+ * no workgroup waits for another, and workgroup 0 stores ids and weights.
+ *
+ * (A combine inside the down kernel -- the last unit to finish a row block
+ * adding the others' rows -- needs a device-scope release per workgroup,
+ * which on this chip writes back the XCD's L2; measured 3x slower than the
+ * separate combine launch.) */
+
+template <int BITS>
+__global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
+{
+    __shared__ WaveLds<1> lds[kGroups];
+    __shared__ float gsum[kGroups][1][64];
+    __shared__ float sel_s[kGroups][64];
+    __shared__ float sel_w[kGroups][64];
+    __shared__ int32_t sel_ids[kGroups][64];
+    const FfnArgs& a = d.f;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int o = lane >> 3;
+    const int RB = a.I / 32;
+    const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
+    const int u = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
+    if (u >= nunits)
+        return;
+    const bool routed = u < d.k;
+    const FfnSeg sg = pick(a, routed ? 0 : 1);
+    const int nb = a.H / 32;
+    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
+    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
+    TokenBlock T;
+    if (b1 > b0)
+        load_token_block(T, a.xq, a.xd, b0, b1);
+    int e = 0;
+    if (routed) {
+        const bool store = blockIdx.x == 0 && wv == 0;
+        select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids[wv], store ? d.w : sel_w[wv],
+                     sel_s[wv], sel_ids[wv]);
+        wave_lds_sync();
+        e = min(max(sel_ids[wv][u], 0), sg.n_mat - 1);
+    }
+    const uint8_t* row0 = (o < 4 ? sg.gate_w : sg.up_w) +
+                          ((int64_t)e * a.I + rb * 32 + 8 * (o & 3)) * rowbytes;
+    StepWeights<BITS> A;
+    first_step<BITS>(A, row0, rowbytes, b0, b1, 8);
+    if (b1 > b0)
+        commit_token_block<BITS>(T, lds[wv], b0, b1);
+    float acc[1] = {0.0f};
+    k_loop<BITS, 1>(A, row0, rowbytes, b0, b1, 1, 8, lds[wv], acc);
+    sum_groups<1>(gsum, acc);
+    if (wv != 0)
+        return;
+    const int r = rb * 32 + (lane & 31);
+    const float sc = (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
+    const float v = sc * acc[0];
+    const float up = shfl_xor(v, 32);
+    const float h = canon_silu(v) * up;
+    float am = lane < 32 ? __builtin_fabsf(h) : 0.0f;
+    for (int m = 16; m >= 1; m >>= 1)
+        am = fmaxf(am, shfl_xor(am, m));
+    const float dsc = am / 127.0f;
+    const float inv = (am == 0.0f) ? 0.0f : 1.0f / dsc;
+    if (lane < 32)
+        a.hq[(int64_t)u * a.I + r] = (int8_t)q8_code(h, inv);
+    if (lane == 0)
+        a.hd[(int64_t)u * (a.I / 32) + rb] = dsc;
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
+{
+    __shared__ WaveLds<1> lds[kGroups];
+    __shared__ float gsum[kGroups][1][64];
+    const FfnArgs& a = d.f;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int o = lane >> 3;
+    const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
+    const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
+    const int u = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
+    if (u >= nunits)
+        return;
+    const bool routed = u < d.k;
+    const FfnSeg sg = pick(a, routed ? 0 : 1);
+    const int e = routed ? min(max(d.ids[u], 0), sg.n_mat - 1) : 0;
+    const int nb = a.I / 32;
+    const int64_t rowbytes = (int64_t)a.I * BITS / 8;
+    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
+    const int first = rb * kRowsPerJob + 8 * o;
+    const int rows_ok = min(8, max(0, a.H - first));
+    const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + first) * rowbytes;
+    StepWeights<BITS> A;
+    first_step<BITS>(A, row0, rowbytes, b0, b1, rows_ok);
+    const int8_t* act[1] = {a.hq + (int64_t)u * a.I};
+    const float* scl[1] = {a.hd + (int64_t)u * nb};
+    stage_activations<BITS, 1>(lds[wv], b0, b1, 1, act, scl);
+    float acc[1] = {0.0f};
+    k_loop<BITS, 1>(A, row0, rowbytes, b0, b1, 1, rows_ok, lds[wv], acc);
+    sum_groups<1>(gsum, acc);
+    if (wv != 0)
+        return;
+    const int n = rb * kRowsPerJob + lane;
+    if (n < a.H)
+        a.y[(int64_t)u * a.H + n] = sg.down_s[(int64_t)e * a.H + n] * acc[0];
 }
 
 static int64_t total_jobs(const FfnArgs& a, int RB)
@@ -477,6 +630,30 @@ hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st)
         launch_down_t<1>(a, bits, dim3((uint32_t)jobs), st);
     else
         launch_down_t<kUnitTokens>(a, bits, dim3((uint32_t)jobs), st);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
+{
+    const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 ? 1 : 0)) * (d.f.I / 32);
+    const dim3 grid((uint32_t)jobs), block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL(ffn_gate_up_decode<8>, grid, block, 0, st, d); break;
+    case 4: hipLaunchKernelGGL(ffn_gate_up_decode<4>, grid, block, 0, st, d); break;
+    default: hipLaunchKernelGGL(ffn_gate_up_decode<2>, grid, block, 0, st, d); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
+{
+    const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 ? 1 : 0)) * ((d.f.H + kRowsPerJob - 1) / kRowsPerJob);
+    const dim3 grid((uint32_t)jobs), block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL(ffn_down_decode<8>, grid, block, 0, st, d); break;
+    case 4: hipLaunchKernelGGL(ffn_down_decode<4>, grid, block, 0, st, d); break;
+    default: hipLaunchKernelGGL(ffn_down_decode<2>, grid, block, 0, st, d); break;
+    }
     return hipGetLastError();
 }
 

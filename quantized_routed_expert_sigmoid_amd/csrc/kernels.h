@@ -79,6 +79,19 @@ struct FfnArgs {
     float* y;         /* [rows][H] */
 };
 
+/* One-token batch (decode): selection inside the gate/up kernel.  f.seg[0]
+ * is the routed bank (n_mat = E), f.seg[1] the shared expert when
+ * f.nseg == 2; hq / hd / y hold one row per unit (slot order, shared last). */
+struct DecodeArgs {
+    FfnArgs f;
+    const float* logits; /* [E] */
+    const float* bias;   /* [E] */
+    int32_t E, k;
+    float rsf;
+    int32_t* ids;        /* [k] selected experts, slot order */
+    float* w;            /* [k] routing weights */
+};
+
 /* Bounds on the unit counts of a routed group with P pairs of S tokens over
  * E experts (n_e pairs each, sum P, n_e <= S).  GEMV: experts with n_e <
  * kMfmaMinTokens give ceil(n_e / 4) <= 2 units each.  MFMA: experts with
@@ -167,6 +180,11 @@ hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_gate_up_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 
+hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
+hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
+
+/* out[t] = y[shared_row0 + t] (if shared_row0 >= 0) + sum_j w[t*k+j] * y[row(t*k+j)],
+ * row(p) = inv[p], or p when inv is null. */
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int32_t S,
                           int32_t k, int32_t H, int32_t shared_row0, float* out, hipStream_t st);
 

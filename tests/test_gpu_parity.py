@@ -184,6 +184,12 @@ SMALL_LAYERS = {
                             top_k=4, S=40, has_shared=True),
     "mfma_int2_long": dict(name="mf2", layer="mf2", bits=2, hidden=256, inter=192, n_experts=4,
                            top_k=2, S=150, has_shared=True),
+    # one token: selection inside the gate/up kernel, combine inside the down kernel
+    "decode_int4": dict(name="dec4", layer="dec4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
+                        S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
+    "decode_int8_noshared": dict(name="dec8", layer="dec8", bits=8, n_experts=32, top_k=4, S=1),
+    "decode_int2_ragged": dict(name="dec2", layer="dec2", bits=2, hidden=352, inter=96, n_experts=16,
+                               top_k=3, S=1, has_shared=True, var_router=1.0 / 352),
 }
 
 
@@ -202,6 +208,23 @@ def test_layer_parity_small(qre, case):
     assert_close_rms(out.cpu().numpy(), ref["out"], case)
 
 
+@pytest.mark.parametrize("S", [1, 3, 20])
+def test_layer_parity_shared_other_bits(qre, S):
+    """A shared expert stored at another width runs in launches of its own
+    (for one token too, where the fused decode kernels do not apply)."""
+    w4 = synth.scaled(synth.WORKLOADS["tiny"], name="mix4", layer="mix4", bits=4, hidden=512, inter=256,
+                      n_experts=32, top_k=4, S=S, has_shared=True, var_router=1.0 / 512)
+    w8 = synth.scaled(w4, layer="mix8", bits=8)
+    L4, L8 = synth.make_layer(w4), synth.make_layer(w8)
+    L = synth.Layer(w4, L4.router_w, L4.bias, L4.gate, L4.up, L4.down, L8.sh_gate, L8.sh_up, L8.sh_down)
+    say(f"layer shared int8 / routed int4 S={S}")
+    x, _ = gapped_activations(w4, L.router_w, L.bias)
+    ref = oracle.layer_forward(L, x.numpy())
+    out = qre.moe_layer_forward(to_device(L), x.cuda())
+    torch.cuda.synchronize()
+    assert_close_rms(out.cpu().numpy(), ref["out"], f"mixed S={S}")
+
+
 def test_layer_empty_batch_is_noop(qre):
     w, L = _small_layer("tiny_e")
     dev = to_device(L)
@@ -211,9 +234,10 @@ def test_layer_empty_batch_is_noop(qre):
     assert out.shape == (0, w.hidden)
 
 
-def test_layer_repeatable_bitwise(qre):
+@pytest.mark.parametrize("case", ["tiny_int4_long", "decode_int4"])
+def test_layer_repeatable_bitwise(qre, case):
     """Two runs on the same inputs give identical bits (no atomics on data)."""
-    w = synth.scaled(synth.WORKLOADS["tiny"], **SMALL_LAYERS["tiny_int4_long"])
+    w = synth.scaled(synth.WORKLOADS["tiny"], **SMALL_LAYERS[case])
     L = synth.make_layer(w)
     dev = to_device(L)
     x = synth.activations(w).cuda()
