@@ -185,21 +185,19 @@ struct WaveLds {
     float d[TMAX][kMaxGroupBlocks];
 };
 
-/* Loads this lane's block of each of its octet's 8 rows for one K step. */
+/* Loads this lane's block of each of its octet's 8 rows for one K step.
+ * The loads are unconditional: rows past rows_ok read the octet's first row
+ * and a block past the group reads b_last (both in bounds; their partials
+ * are never folded or stored), so no load sits under a branch and each use
+ * waits only for its own step. */
 template <int BITS>
 __device__ __forceinline__ void load_step(StepWeights<BITS>& W, const uint8_t* row0, int64_t rowbytes,
-                                          int b, bool valid, int rows_ok)
+                                          int b, int b_last, int rows_ok)
 {
+    const int bb = min(b, b_last);
 #pragma unroll
-    for (int rho = 0; rho < 8; ++rho) {
-        if (valid && rho < rows_ok) {
-            load_block<BITS>(row0 + rho * rowbytes + (int64_t)b * (4 * BITS), W.w[rho]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < BITS; ++i)
-                W.w[rho][i] = 0;
-        }
-    }
+    for (int rho = 0; rho < 8; ++rho)
+        load_block<BITS>(row0 + (rho < rows_ok ? rho : 0) * rowbytes + (int64_t)bb * (4 * BITS), W.w[rho]);
 }
 
 /* Stages the codes and scales of blocks [b_begin, b_end) of every token into
@@ -304,7 +302,7 @@ __device__ __forceinline__ void first_step(StepWeights<BITS>& A, const uint8_t* 
                                            int b_begin, int b_end, int rows_ok)
 {
     const int j8 = threadIdx.x & 7;
-    load_step<BITS>(A, row0, rowbytes, b_begin + j8, j8 < b_end - b_begin, rows_ok);
+    load_step<BITS>(A, row0, rowbytes, b_begin + j8, max(b_end, b_begin + 1) - 1, rows_ok);
 }
 
 /* The K loop of one wave over its fold group, blocks [b_begin, b_end), in
@@ -319,17 +317,15 @@ __device__ __forceinline__ void k_loop(StepWeights<BITS>& A, const uint8_t* row0
     const int j8 = threadIdx.x & 7;
     const int nblk = b_end - b_begin;
     const int nsteps = (nblk + 7) / 8;
+    const int b_last = max(b_end, b_begin + 1) - 1;
     StepWeights<BITS> B;
+    /* loads and steps are unconditional (a step past the group folds
+     * nothing), so A and B keep their registers across iterations */
     for (int st = 0; st < nsteps; st += 2) {
-        const int l1 = 8 * (st + 1) + j8, l2 = 8 * (st + 2) + j8;
-        if (st + 1 < nsteps)
-            load_step<BITS>(B, row0, rowbytes, b_begin + l1, l1 < nblk, rows_ok);
+        load_step<BITS>(B, row0, rowbytes, b_begin + 8 * (st + 1) + j8, b_last, rows_ok);
         fold_step<BITS, TMAX>(A, st, nblk, ntok, L, acc);
-        if (st + 1 < nsteps) {
-            if (st + 2 < nsteps)
-                load_step<BITS>(A, row0, rowbytes, b_begin + l2, l2 < nblk, rows_ok);
-            fold_step<BITS, TMAX>(B, st + 1, nblk, ntok, L, acc);
-        }
+        load_step<BITS>(A, row0, rowbytes, b_begin + 8 * (st + 2) + j8, b_last, rows_ok);
+        fold_step<BITS, TMAX>(B, st + 1, nblk, ntok, L, acc);
     }
 }
 
@@ -448,7 +444,7 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
     const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
     const int first = L.rb * kRowsPerJob + 8 * o;
     const int rows_ok = min(8, max(0, a.H - first));
-    const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + first) * rowbytes;
+    const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + min(first, a.H - 1)) * rowbytes;
     StepWeights<BITS> A;
     first_step<BITS>(A, row0, rowbytes, b0, b1, rows_ok);
     stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
@@ -478,22 +474,161 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
  * over the token's logits (the same selection as router_select_kernel), so
  * no workgroup waits for another, and workgroup 0 stores ids and weights.
  *
+ * Whole-row loads.  A job is 64 rows; wave w owns rows 16w .. 16w+15 and
+ * reads them whole, two rows per load instruction: lane l takes row
+ * 2p + (l >> 5) of pair p and blocks (l & 31) + 32 i, i < NI, so each half
+ * wave reads 32 consecutive blocks of one row (512 bytes at int4).  Reading
+ * each row in one sweep streams markedly faster than splitting K across the
+ * waves (measured 6.5 vs 5.5 TB/s on 113 MB).  A lane's activation blocks are
+ * the same for every row, so they stay in registers.  The exact partials of
+ * the 16 rows go to LDS; lane (r, g) then folds row r's group g in ascending
+ * block order and the four group sums are added in order.
+ *
  * (A combine inside the down kernel -- the last unit to finish a row block
  * adding the others' rows -- needs a device-scope release per workgroup,
  * which on this chip writes back the XCD's L2; measured 3x slower than the
  * separate combine launch.) */
 
-template <int BITS>
+constexpr int kDecRows = 16; /* rows of a job per wave */
+
+/* Load instructions per row pair for nb blocks, rounded up to an
+ * instantiated count. */
+inline int dec_ni(int nb)
+{
+    const int n = (nb + 31) / 32;
+    return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 6 ? 6 : 8;
+}
+
+/* Dynamic LDS, in words: per wave the partials [16][nb | 1] (before the K
+ * loop the selection's scratch), then the token's block scales [nb] and the
+ * job's row sums [64]. */
+__host__ __device__ inline int dec_region(int nb)
+{
+    const int p = kDecRows * (nb | 1);
+    return p > 192 ? p : 192;
+}
+
+__host__ __device__ inline size_t dec_lds_bytes(int nb)
+{
+    return (size_t)(kGroups * dec_region(nb) + nb + 64) * 4;
+}
+
+template <int BITS, int NI>
+struct PairLoad {
+    uint32_t w[NI][BITS];
+};
+
+/* Loads are unconditional: a lane past the job's rows or the row's blocks
+ * reads the last row / block instead (in bounds; its partial is never used),
+ * so no load sits under a branch and each use waits only for its own loads. */
+template <int BITS, int NI>
+__device__ __forceinline__ void pair_load(PairLoad<BITS, NI>& L, const uint8_t* rows0, int64_t rowbytes,
+                                          int p, int rows_ok, int nb)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = min(2 * p + (lane >> 5), max(rows_ok, 1) - 1), c = lane & 31;
+    const uint8_t* rp = rows0 + (int64_t)row * rowbytes;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        load_block<BITS>(rp + (int64_t)min(c + 32 * i, nb - 1) * (4 * BITS), L.w[i]);
+}
+
+template <int BITS, int NI>
+__device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const uint32_t (&xa)[NI][8], int p,
+                                              int nb, int32_t* P, int sp)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = 2 * p + (lane >> 5), c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int b = c + 32 * i;
+        if (row < kDecRows && b < nb)
+            P[row * sp + b] = block_partial<BITS>(L.w[i], xa[i]);
+    }
+}
+
+/* The wave's 16 rows (rows0: its first row; rows_ok of them exist): returns
+ * on every lane the folded sum of row (lane & 15) before the row scale.
+ * The caller has issued pair 0 into A (so the weight stream starts before
+ * the activations are prepared); two pairs are in flight while one is
+ * multiplied. */
+template <int BITS, int NI>
+__device__ __forceinline__ float dec_k_loop(PairLoad<BITS, NI>& A, const uint8_t* rows0, int64_t rowbytes,
+                                            int rows_ok, int nb, const uint32_t (&xa)[NI][8], int32_t* P,
+                                            int sp, const float* dl)
+{
+    PairLoad<BITS, NI> B;
+#pragma unroll
+    for (int p = 0; p < kDecRows / 2; p += 2) {
+        pair_load<BITS, NI>(B, rows0, rowbytes, p + 1, rows_ok, nb);
+        pair_partials<BITS, NI>(A, xa, p, nb, P, sp);
+        if (p + 2 < kDecRows / 2) /* resolved at compile time */
+            pair_load<BITS, NI>(A, rows0, rowbytes, p + 2, rows_ok, nb);
+        pair_partials<BITS, NI>(B, xa, p + 1, nb, P, sp);
+    }
+    wave_lds_sync();
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
+    const int32_t* pr = P + r * sp;
+    float acc = 0.0f;
+    int b = b0;
+    /* eight partials and scales read ahead of their (in-order) fmas */
+    for (; b + 8 <= b1; b += 8) {
+        int32_t q[8];
+        float dd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            q[i] = pr[b + i];
+            dd[i] = dl[b + i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+    }
+    for (; b < b1; ++b)
+        acc = __builtin_fmaf(dl[b], (float)pr[b], acc);
+    float v = __shfl(acc, r, kWave);
+    v = v + __shfl(acc, 16 + r, kWave);
+    v = v + __shfl(acc, 32 + r, kWave);
+    v = v + __shfl(acc, 48 + r, kWave);
+    return v;
+}
+
+/* The token's activation blocks (l & 31) + 32 i, loaded raw ... */
+template <int NI>
+__device__ __forceinline__ void dec_act_load(const int8_t* act, int nb, uint32_t (&x)[NI][8])
+{
+    const int c = threadIdx.x & 31;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        load_codes(act + (int64_t)min(c + 32 * i, nb - 1) * 32, x[i]);
+}
+
+/* ... then put in operand order; every wave also writes the block scales
+ * (the same values) so that its own reads follow its own writes. */
+template <int BITS, int NI>
+__device__ __forceinline__ void dec_act_prep(uint32_t (&x)[NI][8], const float* scl, int nb, float* dl)
+{
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        uint32_t xa[8];
+        prep_activation<BITS>(x[i], xa);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            x[i][q] = xa[q];
+    }
+    for (int b = threadIdx.x & 63; b < nb; b += 64)
+        dl[b] = scl[b];
+    wave_lds_sync();
+}
+
+template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
 {
-    __shared__ WaveLds<1> lds[kGroups];
-    __shared__ float gsum[kGroups][1][64];
-    __shared__ float sel_s[kGroups][64];
-    __shared__ float sel_w[kGroups][64];
-    __shared__ int32_t sel_ids[kGroups][64];
+    extern __shared__ int32_t dec_lds[];
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int o = lane >> 3;
     const int RB = a.I / 32;
     const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
     const int u = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
@@ -501,34 +636,42 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         return;
     const bool routed = u < d.k;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
-    const int nb = a.H / 32;
-    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
-    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
-    TokenBlock T;
-    if (b1 > b0)
-        load_token_block(T, a.xq, a.xd, b0, b1);
+    const int nb = a.H / 32, sp = nb | 1, region = dec_region(nb);
+    int32_t* P = dec_lds + wv * region;
+    float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
+    float* rsum = dl + nb;
+    uint32_t xa[NI][8];
+    dec_act_load<NI>(a.xq, nb, xa);
     int e = 0;
     if (routed) {
+        /* selection scratch in the wave's (not yet used) partial buffer */
+        float* sel_s = reinterpret_cast<float*>(P);
+        float* sel_w = sel_s + 64;
+        int32_t* sel_ids = P + 128;
         const bool store = blockIdx.x == 0 && wv == 0;
-        select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids[wv], store ? d.w : sel_w[wv],
-                     sel_s[wv], sel_ids[wv]);
+        select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids, store ? d.w : sel_w, sel_s,
+                     sel_ids);
         wave_lds_sync();
-        e = min(max(sel_ids[wv][u], 0), sg.n_mat - 1);
+        e = min(max(sel_ids[u], 0), sg.n_mat - 1);
+        wave_lds_sync();
     }
-    const uint8_t* row0 = (o < 4 ? sg.gate_w : sg.up_w) +
-                          ((int64_t)e * a.I + rb * 32 + 8 * (o & 3)) * rowbytes;
-    StepWeights<BITS> A;
-    first_step<BITS>(A, row0, rowbytes, b0, b1, 8);
-    if (b1 > b0)
-        commit_token_block<BITS>(T, lds[wv], b0, b1);
-    float acc[1] = {0.0f};
-    k_loop<BITS, 1>(A, row0, rowbytes, b0, b1, 1, 8, lds[wv], acc);
-    sum_groups<1>(gsum, acc);
+    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
+    /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
+    const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) +
+                           ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * rowbytes;
+    PairLoad<BITS, NI> A;
+    pair_load<BITS, NI>(A, rows0, rowbytes, 0, kDecRows, nb);
+    dec_act_prep<BITS, NI>(xa, a.xd, nb, dl);
+    const float v16 = dec_k_loop<BITS, NI>(A, rows0, rowbytes, kDecRows, nb, xa, P, sp, dl);
+    if (lane < 16)
+        rsum[16 * wv + lane] = v16;
+    __syncthreads();
     if (wv != 0)
         return;
+    const float acc = rsum[lane];
     const int r = rb * 32 + (lane & 31);
     const float sc = (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
-    const float v = sc * acc[0];
+    const float v = sc * acc;
     const float up = shfl_xor(v, 32);
     const float h = canon_silu(v) * up;
     float am = lane < 32 ? __builtin_fabsf(h) : 0.0f;
@@ -542,14 +685,12 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         a.hd[(int64_t)u * (a.I / 32) + rb] = dsc;
 }
 
-template <int BITS>
+template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
 {
-    __shared__ WaveLds<1> lds[kGroups];
-    __shared__ float gsum[kGroups][1][64];
+    extern __shared__ int32_t dec_lds[];
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int o = lane >> 3;
     const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
     const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
     const int u = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
@@ -558,25 +699,22 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     const bool routed = u < d.k;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
     const int e = routed ? min(max(d.ids[u], 0), sg.n_mat - 1) : 0;
-    const int nb = a.I / 32;
+    const int nb = a.I / 32, sp = nb | 1, region = dec_region(nb);
+    int32_t* P = dec_lds + wv * region;
+    float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
+    uint32_t xa[NI][8];
+    dec_act_load<NI>(a.hq + (int64_t)u * a.I, nb, xa);
+    const int row0 = rb * kRowsPerJob + kDecRows * wv;
+    const int rows_ok = min(kDecRows, max(0, a.H - row0));
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
-    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
-    const int first = rb * kRowsPerJob + 8 * o;
-    const int rows_ok = min(8, max(0, a.H - first));
-    const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + first) * rowbytes;
-    StepWeights<BITS> A;
-    first_step<BITS>(A, row0, rowbytes, b0, b1, rows_ok);
-    const int8_t* act[1] = {a.hq + (int64_t)u * a.I};
-    const float* scl[1] = {a.hd + (int64_t)u * nb};
-    stage_activations<BITS, 1>(lds[wv], b0, b1, 1, act, scl);
-    float acc[1] = {0.0f};
-    k_loop<BITS, 1>(A, row0, rowbytes, b0, b1, 1, rows_ok, lds[wv], acc);
-    sum_groups<1>(gsum, acc);
-    if (wv != 0)
-        return;
-    const int n = rb * kRowsPerJob + lane;
-    if (n < a.H)
-        a.y[(int64_t)u * a.H + n] = sg.down_s[(int64_t)e * a.H + n] * acc[0];
+    const uint8_t* rows0 = sg.down_w + ((int64_t)e * a.H + min(row0, a.H - 1)) * rowbytes;
+    PairLoad<BITS, NI> A;
+    pair_load<BITS, NI>(A, rows0, rowbytes, 0, rows_ok, nb);
+    dec_act_prep<BITS, NI>(xa, a.hd + (int64_t)u * nb, nb, dl);
+    const float v = dec_k_loop<BITS, NI>(A, rows0, rowbytes, rows_ok, nb, xa, P, sp, dl);
+    const int n = row0 + lane;
+    if (lane < rows_ok)
+        a.y[(int64_t)u * a.H + n] = sg.down_s[(int64_t)e * a.H + n] * v;
 }
 
 static int64_t total_jobs(const FfnArgs& a, int RB)
@@ -633,14 +771,40 @@ hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st)
     return hipGetLastError();
 }
 
+template <int NI>
+static void gate_up_decode_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, hipStream_t st)
+{
+    const dim3 block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL((ffn_gate_up_decode<8, NI>), grid, block, lds, st, d); break;
+    case 4: hipLaunchKernelGGL((ffn_gate_up_decode<4, NI>), grid, block, lds, st, d); break;
+    default: hipLaunchKernelGGL((ffn_gate_up_decode<2, NI>), grid, block, lds, st, d); break;
+    }
+}
+
+template <int NI>
+static void down_decode_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, hipStream_t st)
+{
+    const dim3 block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL((ffn_down_decode<8, NI>), grid, block, lds, st, d); break;
+    case 4: hipLaunchKernelGGL((ffn_down_decode<4, NI>), grid, block, lds, st, d); break;
+    default: hipLaunchKernelGGL((ffn_down_decode<2, NI>), grid, block, lds, st, d); break;
+    }
+}
+
 hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
 {
     const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 ? 1 : 0)) * (d.f.I / 32);
-    const dim3 grid((uint32_t)jobs), block(64 * kGroups);
-    switch (bits) {
-    case 8: hipLaunchKernelGGL(ffn_gate_up_decode<8>, grid, block, 0, st, d); break;
-    case 4: hipLaunchKernelGGL(ffn_gate_up_decode<4>, grid, block, 0, st, d); break;
-    default: hipLaunchKernelGGL(ffn_gate_up_decode<2>, grid, block, 0, st, d); break;
+    const int nb = d.f.H / 32;
+    const dim3 grid((uint32_t)jobs);
+    const size_t lds = dec_lds_bytes(nb);
+    switch (dec_ni(nb)) {
+    case 1: gate_up_decode_ni<1>(d, bits, grid, lds, st); break;
+    case 2: gate_up_decode_ni<2>(d, bits, grid, lds, st); break;
+    case 4: gate_up_decode_ni<4>(d, bits, grid, lds, st); break;
+    case 6: gate_up_decode_ni<6>(d, bits, grid, lds, st); break;
+    default: gate_up_decode_ni<8>(d, bits, grid, lds, st); break;
     }
     return hipGetLastError();
 }
@@ -648,11 +812,15 @@ hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStrea
 hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
 {
     const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 ? 1 : 0)) * ((d.f.H + kRowsPerJob - 1) / kRowsPerJob);
-    const dim3 grid((uint32_t)jobs), block(64 * kGroups);
-    switch (bits) {
-    case 8: hipLaunchKernelGGL(ffn_down_decode<8>, grid, block, 0, st, d); break;
-    case 4: hipLaunchKernelGGL(ffn_down_decode<4>, grid, block, 0, st, d); break;
-    default: hipLaunchKernelGGL(ffn_down_decode<2>, grid, block, 0, st, d); break;
+    const int nb = d.f.I / 32;
+    const dim3 grid((uint32_t)jobs);
+    const size_t lds = dec_lds_bytes(nb);
+    switch (dec_ni(nb)) {
+    case 1: down_decode_ni<1>(d, bits, grid, lds, st); break;
+    case 2: down_decode_ni<2>(d, bits, grid, lds, st); break;
+    case 4: down_decode_ni<4>(d, bits, grid, lds, st); break;
+    case 6: down_decode_ni<6>(d, bits, grid, lds, st); break;
+    default: down_decode_ni<8>(d, bits, grid, lds, st); break;
     }
     return hipGetLastError();
 }

@@ -190,6 +190,10 @@ SMALL_LAYERS = {
     "decode_int8_noshared": dict(name="dec8", layer="dec8", bits=8, n_experts=32, top_k=4, S=1),
     "decode_int2_ragged": dict(name="dec2", layer="dec2", bits=2, hidden=352, inter=96, n_experts=16,
                                top_k=3, S=1, has_shared=True, var_router=1.0 / 352),
+    "decode_int4_k2080": dict(name="dec4b", layer="dec4b", bits=4, hidden=2080, inter=160, n_experts=16,
+                              top_k=4, S=1, has_shared=True, var_router=1.0 / 2080),
+    "decode_int8_k8192": dict(name="dec8b", layer="dec8b", bits=8, hidden=8192, inter=128, n_experts=8,
+                              top_k=2, S=1, has_shared=False, var_router=1.0 / 8192),
 }
 
 
