@@ -66,6 +66,76 @@ def stage_bytes(w, n_units_touched, S):
     }
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _hip_runtime():
+    """The HIP runtime this process already uses (torch's)."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    lib = ctypes.CDLL(path or "libamdhip64.so")
+    lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class TimingEvents:
+    """HIP events for stage timing only, created without the system-scope
+    fence on record (a fenced event writes back and invalidates the caches,
+    which adds microseconds to every stage it brackets)."""
+
+    def __init__(self, n):
+        import ctypes
+        self._ct = ctypes
+        self.lib = _hip_runtime()
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.lib.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e.value)
+
+    def elapsed_ms(self, i, j):
+        t = self._ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self._ct.byref(t), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return t.value
+
+    def close(self):
+        for e in self.ev:
+            self.lib.hipEventDestroy(e)
+        self.ev = []
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_gate_up_traffic.json")
+
+
+def measured_traffic(w, stage):
+    """HBM bytes per launch of the stage's kernel from the committed counter
+    runs, or None when no record matches (other workload or stage, or the
+    kernel sources changed since the counters were taken)."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    with open(TRAFFIC_RECORD) as f:
+        rec = json.load(f)
+    if rec.get("workload") != w.name or stage != "gate_up":
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def stage_kernel(w, stage):
     """The kernel(s) one FFN stage launches for this workload."""
     if w.S == 1:
@@ -123,20 +193,18 @@ def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True)
     res = {"steps": steps, "gpu_ms": gpu_ms, "wall_s": wall}
     if timed_stages:
         # same steps again through the staged entry point: per-stage durations
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(qre.COLI_N_STAGE_EVENTS)]
-               for _ in range(steps)]
-        for row in evs:  # materialise the events
-            for e in row:
-                e.record(stream)
+        n_ev = qre.COLI_N_STAGE_EVENTS
+        tev = TimingEvents(steps * n_ev)
         torch.cuda.synchronize()
         for i in range(steps):
             qre.moe_layer_forward_staged(dev_layers[i % copies][0], xs[i % n_batches], out, ws,
-                                         [e.cuda_event for e in evs[i]])
+                                         tev.ev[i * n_ev:(i + 1) * n_ev])
         torch.cuda.synchronize()
         per = {s: 0.0 for s in qre.STAGES}
-        for row in evs:
+        for i in range(steps):
             for j, s in enumerate(qre.STAGES):
-                per[s] += row[j].elapsed_time(row[j + 1])
+                per[s] += tev.elapsed_ms(i * n_ev + j, i * n_ev + j + 1)
+        tev.close()
         res["stage_ms"] = {s: v / steps for s, v in per.items()}
     # union size of each batch (for algorithmic bytes)
     uniq = []
@@ -218,7 +286,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": stage_kernel(w, dom), "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": measured_traffic(w, dom), "algorithmic_bytes": sb[dom]},
         "layer": {"algorithmic_bytes": layer_bytes, "unique_routed_experts": res["mean_unique_experts"],
                   "hbm_GBps_whole_layer": layer_bytes / (ms / 1000.0) / 1e9,
                   "hbm_frac_whole_layer": layer_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
@@ -237,7 +305,7 @@ def main():
                            "int8_mfma_frac": ops / (msp / 1000.0) / 1e12 / INT8_PEAK_TOPS,
                            "stage_ms": rp["stage_ms"]}
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or (4 if w.S <= 8 else 2)
+        n = args.cpu_sample_tokens or (40 if w.S <= 8 else 4)
         line["cpu_baseline"] = cpu_baseline(synth, w, n)
     print(json.dumps(line), flush=True)
 
