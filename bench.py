@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=0, help="timed steps (0: per-workload default)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode")
-    ap.add_argument("--copies", type=int, default=8, help="layer copies rotated across steps")
+    ap.add_argument("--copies", type=int, default=16, help="layer copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
@@ -82,6 +82,7 @@ def _hip_runtime():
     lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -101,6 +102,11 @@ class TimingEvents:
             if rc != 0:
                 raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             self.ev.append(e.value)
+
+    def record(self, i, stream):
+        rc = self.lib.hipEventRecord(self.ev[i], self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, i, j):
         t = self._ct.c_float()
@@ -191,6 +197,18 @@ def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True)
     gpu_ms = t_start.elapsed_time(t_end)
 
     res = {"steps": steps, "gpu_ms": gpu_ms, "wall_s": wall}
+    # per-step distribution: a start / end event around every step
+    pev = TimingEvents(2 * steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        pev.record(2 * i, stream)
+        step(i)
+        pev.record(2 * i + 1, stream)
+    torch.cuda.synchronize()
+    per_step = sorted(pev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps))
+    pev.close()
+    res["step_ms_quantiles"] = {q: per_step[min(steps - 1, int(f * steps))]
+                                for q, f in (("p10", 0.1), ("median", 0.5), ("p90", 0.9))}
     if timed_stages:
         # same steps again through the staged entry point: per-stage durations
         n_ev = qre.COLI_N_STAGE_EVENTS
@@ -275,6 +293,7 @@ def main():
         "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_ms_quantiles": res["step_ms_quantiles"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

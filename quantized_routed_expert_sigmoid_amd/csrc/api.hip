@@ -465,15 +465,23 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         dd.rsf = L->routed_scaling_factor;
         dd.ids = ids;
         dd.w = w;
+        dd.out = out;
         e = mark(2, e);
         if (e == hipSuccess)
             e = launch_ffn_gate_up_decode(dd, L->gate.qtype, s);
         e = mark(3, e);
-        if (e == hipSuccess)
-            e = launch_ffn_down_decode(dd, L->down.qtype, s);
-        e = mark(4, e);
-        if (e == hipSuccess)
-            e = launch_combine(y, nullptr, w, 1, k, H, shared ? k : -1, out, s);
+        if (down_combine_decode_fits(dd)) {
+            /* down and combine in one launch: the combine stage is empty */
+            if (e == hipSuccess)
+                e = launch_ffn_down_combine_decode(dd, L->down.qtype, s);
+            e = mark(4, e);
+        } else {
+            if (e == hipSuccess)
+                e = launch_ffn_down_decode(dd, L->down.qtype, s);
+            e = mark(4, e);
+            if (e == hipSuccess)
+                e = launch_combine(y, nullptr, w, 1, k, H, shared ? k : -1, out, s);
+        }
         e = mark(5, e);
         return hip_status(e);
     }

@@ -717,6 +717,148 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
         a.y[(int64_t)u * a.H + n] = sg.down_s[(int64_t)e * a.H + n] * v;
 }
 
+/* ---- one token: down projection with the combine --------------------------
+ * A workgroup owns 8 output rows for all U = k (+1 shared) units; wave w
+ * streams rows 2w, 2w+1 of every unit's down matrix as whole-row pairs
+ * (pair j = unit j), two units in flight.  All units' h codes are staged in
+ * LDS in operand order once per workgroup (measured faster than each lane
+ * loading its own h blocks per unit, and than four units in flight).  After
+ * the canonical fold of each (unit, row), the wave forms
+ * out = y_shared + sum_j w_j * y_j for its rows with the same fma order as
+ * combine_kernel, so the result is bit-identical to down + combine without
+ * the y round trip or the extra launch.  (8 rows per workgroup give H / 8 =
+ * 768 workgroups at H = 6144: three per CU.) */
+
+constexpr int kDcRows = 8; /* output rows per workgroup; wave w owns rows 2w, 2w+1 */
+
+/* LDS words: h codes [U][nb][8], h scales [U][nb], per wave the partials
+ * [2U][nb | 1] and the row values [2U]. */
+__host__ __device__ inline size_t dc_lds_words(int U, int nb)
+{
+    return (size_t)U * nb * 9 + (size_t)kGroups * 2 * U * ((nb | 1) + 1);
+}
+
+inline bool dc_fits(int U, int nb)
+{
+    return dc_lds_words(U, nb) * 4 <= 64 * 1024;
+}
+
+/* First of this wave's two rows of unit j's down matrix. */
+__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int j, int row0, int64_t rowbytes)
+{
+    const FfnArgs& a = d.f;
+    const bool routed = j < d.k;
+    const uint8_t* w = routed ? a.seg[0].down_w : a.seg[1].down_w;
+    const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
+    const int e = routed ? min(max(d.ids[j], 0), n_mat - 1) : 0;
+    return w + ((int64_t)e * a.H + row0) * rowbytes;
+}
+
+template <int NI>
+__device__ __forceinline__ void dc_act(const uint32_t* xal, int j, int nb, uint32_t (&xa)[NI][8])
+{
+    const int c = threadIdx.x & 31;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)j * nb + min(c + 32 * i, nb - 1)) * 8);
+        const uint4 u0 = src[0], u1 = src[1];
+        xa[i][0] = u0.x; xa[i][1] = u0.y; xa[i][2] = u0.z; xa[i][3] = u0.w;
+        xa[i][4] = u1.x; xa[i][5] = u1.y; xa[i][6] = u1.z; xa[i][7] = u1.w;
+    }
+}
+
+template <int BITS, int NI>
+__global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
+{
+    extern __shared__ int32_t dc_lds[];
+    const FfnArgs& a = d.f;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const bool shared = a.nseg > 1;
+    const int U = d.k + (shared ? 1 : 0);
+    const int nb = a.I / 32, sp = nb | 1;
+    uint32_t* xal = reinterpret_cast<uint32_t*>(dc_lds);        /* [U][nb][8] */
+    float* dls = reinterpret_cast<float*>(xal + U * nb * 8);    /* [U][nb] */
+    int32_t* P = reinterpret_cast<int32_t*>(dls + U * nb) + wv * (2 * U * sp);
+    float* ys = reinterpret_cast<float*>(dc_lds) + U * nb * 9 + kGroups * 2 * U * sp + wv * 2 * U;
+    const int row0 = blockIdx.x * kDcRows + 2 * wv;
+    const int64_t rowbytes = (int64_t)a.I * BITS / 8;
+
+    /* unit 0's pair is issued before h is staged */
+    PairLoad<BITS, NI> A, B;
+    pair_load<BITS, NI>(A, dc_rows(d, 0, row0, rowbytes), rowbytes, 0, 2, nb);
+    for (int i = threadIdx.x; i < U * nb; i += 64 * kGroups) {
+        const int j = i / nb, b = i - j * nb;
+        uint32_t x[8], xa[8];
+        load_codes(a.hq + (int64_t)j * a.I + (int64_t)b * 32, x);
+        prep_activation<BITS>(x, xa);
+        uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
+        dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+        dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+        dls[i] = a.hd[(int64_t)j * nb + b];
+    }
+    __syncthreads();
+
+    /* unit j's pair is in A for even j and in B for odd j; loads are
+     * unconditional (past the last unit they reload it: in bounds, unused) */
+    for (int j = 0; j < U; j += 2) {
+        uint32_t xa[NI][8];
+        pair_load<BITS, NI>(B, dc_rows(d, min(j + 1, U - 1), row0, rowbytes), rowbytes, 0, 2, nb);
+        dc_act<NI>(xal, j, nb, xa);
+        pair_partials<BITS, NI>(A, xa, 0, nb, P + 2 * j * sp, sp);
+        pair_load<BITS, NI>(A, dc_rows(d, min(j + 2, U - 1), row0, rowbytes), rowbytes, 0, 2, nb);
+        if (j + 1 < U) {
+            dc_act<NI>(xal, j + 1, nb, xa);
+            pair_partials<BITS, NI>(B, xa, 0, nb, P + 2 * (j + 1) * sp, sp);
+        }
+    }
+    wave_lds_sync();
+
+    /* fold: chain (rd, g) = (unit rd / 2, row rd % 2; group g) */
+    for (int c0 = 0; c0 < 8 * U; c0 += 64) {
+        const int ci = c0 + lane;
+        const int rd = min(ci >> 2, 2 * U - 1), g = ci & 3;
+        const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
+        const int32_t* pr = P + rd * sp;
+        const float* dj = dls + (rd >> 1) * nb;
+        float acc = 0.0f;
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
+            int32_t q[8];
+            float dd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                q[i] = pr[b + i];
+                dd[i] = dj[b + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+        }
+        for (; b < b1; ++b)
+            acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
+        const int base = lane & ~3;
+        float v = __shfl(acc, base, kWave);
+        v = v + __shfl(acc, base + 1, kWave);
+        v = v + __shfl(acc, base + 2, kWave);
+        v = v + __shfl(acc, base + 3, kWave);
+        if (g == 0 && ci < 8 * U) {
+            const int j = rd >> 1, n = row0 + (rd & 1);
+            const bool routed = j < d.k;
+            const float* ds = routed ? a.seg[0].down_s : a.seg[1].down_s;
+            const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
+            const int e = routed ? min(max(d.ids[j], 0), n_mat - 1) : 0;
+            ys[rd] = ds[(int64_t)e * a.H + n] * v;
+        }
+    }
+    wave_lds_sync();
+    if (lane < 2) {
+        float outv = shared ? ys[2 * d.k + lane] : 0.0f;
+        for (int j = 0; j < d.k; ++j)
+            outv = __builtin_fmaf(d.w[j], ys[2 * j + lane], outv);
+        d.out[row0 + lane] = outv;
+    }
+}
+
 static int64_t total_jobs(const FfnArgs& a, int RB)
 {
     int64_t n = (int64_t)a.seg[0].max_units * RB;
@@ -821,6 +963,38 @@ hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t
     case 4: down_decode_ni<4>(d, bits, grid, lds, st); break;
     case 6: down_decode_ni<6>(d, bits, grid, lds, st); break;
     default: down_decode_ni<8>(d, bits, grid, lds, st); break;
+    }
+    return hipGetLastError();
+}
+
+template <int NI>
+static void down_combine_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, hipStream_t st)
+{
+    const dim3 block(64 * kGroups);
+    switch (bits) {
+    case 8: hipLaunchKernelGGL((ffn_down_combine_decode<8, NI>), grid, block, lds, st, d); break;
+    case 4: hipLaunchKernelGGL((ffn_down_combine_decode<4, NI>), grid, block, lds, st, d); break;
+    default: hipLaunchKernelGGL((ffn_down_combine_decode<2, NI>), grid, block, lds, st, d); break;
+    }
+}
+
+bool down_combine_decode_fits(const DecodeArgs& d)
+{
+    return d.f.H % kDcRows == 0 && dc_fits(d.k + (d.f.nseg > 1 ? 1 : 0), d.f.I / 32);
+}
+
+hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
+{
+    const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
+    const int nb = d.f.I / 32;
+    const dim3 grid((uint32_t)(d.f.H / kDcRows));
+    const size_t lds = dc_lds_words(U, nb) * 4;
+    switch (dec_ni(nb)) {
+    case 1: down_combine_ni<1>(d, bits, grid, lds, st); break;
+    case 2: down_combine_ni<2>(d, bits, grid, lds, st); break;
+    case 4: down_combine_ni<4>(d, bits, grid, lds, st); break;
+    case 6: down_combine_ni<6>(d, bits, grid, lds, st); break;
+    default: down_combine_ni<8>(d, bits, grid, lds, st); break;
     }
     return hipGetLastError();
 }

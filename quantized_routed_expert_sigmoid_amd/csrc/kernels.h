@@ -90,6 +90,7 @@ struct DecodeArgs {
     float rsf;
     int32_t* ids;        /* [k] selected experts, slot order */
     float* w;            /* [k] routing weights */
+    float* out;          /* [H] layer output (down + combine launch) */
 };
 
 /* Bounds on the unit counts of a routed group with P pairs of S tokens over
@@ -182,6 +183,11 @@ hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 
 hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
+
+/* Down projection and combine in one launch (writes out, not y); usable
+ * when H is a multiple of 16 and all units' h fit the workgroup's LDS. */
+bool down_combine_decode_fits(const DecodeArgs& d);
+hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 
 /* out[t] = y[shared_row0 + t] (if shared_row0 >= 0) + sum_j w[t*k+j] * y[row(t*k+j)],
  * row(p) = inv[p], or p when inv is null. */

@@ -194,6 +194,9 @@ SMALL_LAYERS = {
                               top_k=4, S=1, has_shared=True, var_router=1.0 / 2080),
     "decode_int8_k8192": dict(name="dec8b", layer="dec8b", bits=8, hidden=8192, inter=128, n_experts=8,
                               top_k=2, S=1, has_shared=False, var_router=1.0 / 8192),
+    # 33 units of I = 2048 do not fit the fused down + combine: separate launches
+    "decode_many_slots": dict(name="decm", layer="decm", bits=4, hidden=256, inter=2048, n_experts=64,
+                              top_k=32, S=1, has_shared=True, var_router=1.0 / 256),
 }
 
 
