@@ -99,6 +99,23 @@ typedef struct coli_qbank {
  * The shared expert (has_shared != 0) has the same shapes with n_mat = 1.
  * router_w is fp32 [n_experts][hidden]; router_bias fp32 [n_experts] enters
  * expert selection only.  hidden % 32 == 0 and inter % 32 == 0.
+ *
+ * Router variants (zero-initialised fields, or n_group = topk_group = 1 and
+ * top_p = 1, give the plain top-k of the sigmoid-router item):
+ *   n_group > 1: group-limited selection, the group stage of DeepSeek-V3's
+ *     noaux_tc routing.  Experts form n_group equal contiguous groups; a
+ *     group's score is the sum of its two largest biased scores (fp32); the
+ *     topk_group best groups are kept (ties to the lower group); the top-k
+ *     runs over the kept groups' experts.  Requires n_experts % n_group == 0,
+ *     n_experts / n_group >= 2, 1 <= topk_group <= n_group and
+ *     top_k <= topk_group * n_experts / n_group.
+ *   0 < top_p < 1: adaptive expert top-p ([README] practical-flags list:
+ *     fewer expert reads per token).  The k selected slots are ordered by
+ *     unbiased score (descending, ties in slot order); their shares s / sum s
+ *     are accumulated in fp32 and the shortest prefix whose cumulative share
+ *     reaches top_p is kept (at least one slot).  Kept slots keep their
+ *     positions and weights rsf * s_j / sum over kept s; dropped slots get id
+ *     -1 and weight 0 and are not computed.
  */
 typedef struct coli_moe_layer {
     int32_t hidden, inter, n_experts, top_k;
@@ -108,6 +125,9 @@ typedef struct coli_moe_layer {
     coli_qbank gate, up, down;
     int32_t has_shared;
     coli_qbank sh_gate, sh_up, sh_down;
+    int32_t n_group;    /* 0 or 1: no group stage */
+    int32_t topk_group; /* groups kept when n_group > 1 */
+    float top_p;        /* 0 or >= 1: no top-p */
 } coli_moe_layer;
 
 /* Workspace bytes that every call below needs for layer L and up to S tokens
@@ -134,17 +154,19 @@ int colibri_quantize_q8_0(const float* x, int32_t rows, int32_t K, int8_t* q, fl
  * Router ([README] sigmoid-router item).  x: fp32 [S][hidden].  For each token:
  * logits l_e = x . router_w[e] (fp32), s_e = 1 / (1 + exp(-l_e)),
  * c_e = s_e + router_bias[e]; the top_k experts by c (ties to the lower id;
- * one expert group) fill slots in that order; topk_w[t][j] =
- * routed_scaling_factor * s_(j) / sum_j' s_(j') from the unbiased scores.
- * Writes topk_ids int32 [S][top_k] and topk_w fp32 [S][top_k].  S == 0 is a
- * no-op.
+ * with n_group > 1 among the kept groups' experts) fill slots in that order;
+ * topk_w[t][j] = routed_scaling_factor * s_(j) / sum_j' s_(j') from the
+ * unbiased scores (with top_p, over the kept slots; dropped slots: id -1,
+ * weight 0).  Writes topk_ids int32 [S][top_k] and topk_w fp32 [S][top_k].
+ * S == 0 is a no-op.
  */
 int colibri_route(const coli_moe_layer* L, const float* x, int32_t S, int32_t* topk_ids,
                   float* topk_w, void* ws, size_t ws_bytes, coli_stream_t stream);
 
 /*
  * Batched-union dispatch ([README] batched-union MoE item).  Pairs p = t*k + j
- * of topk_ids [S][k] are stably grouped by expert id in [0, E):
+ * of topk_ids [S][k] are stably grouped by expert id in [0, E); a negative id
+ * (a slot dropped by top-p) is no pair and is left out of every output:
  *   expert_offsets int32 [E+1]: exclusive prefix of the per-expert counts;
  *   sorted_pairs   int32 [S*k]: pair indices ordered by (expert, p);
  *   active_experts int32 [E]  : experts with count > 0, ascending (entries
@@ -177,8 +199,9 @@ int colibri_moe_dispatch(const int32_t* topk_ids, int32_t S, int32_t k, int32_t 
  * xq int8 [S][hidden] and xd fp32 [S][hidden/32] come from
  * colibri_quantize_q8_0; offsets / pairs from colibri_moe_dispatch (or, for a
  * one-matrix bank, {0, S} and the identity with k = 1).  Writes y fp32
- * [S*k][hidden] in sorted order (16-byte aligned).  expert_offsets[n_mat] must
- * equal S*k.
+ * [S*k][hidden] in sorted order (16-byte aligned); rows from
+ * expert_offsets[n_mat] <= S*k on (fewer when slots were dropped) are left
+ * untouched.
  */
 int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const coli_qbank* down,
                          const int8_t* xq, const float* xd, int32_t S,
@@ -187,7 +210,8 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
 
 /*
  * Whole layer ([DIVE] 4.3): out[t] = y_shared[t] + sum_j topk_w[t][j] *
- * y_routed[t][j] (fp32, slot order), with the steps above.  x and out are fp32
+ * y_routed[t][j] (fp32, slot order, dropped slots skipped), with the steps
+ * above.  x and out are fp32
  * [S][hidden], 16-byte aligned.  S == 0 is a no-op.
  */
 int colibri_moe_layer_forward(const coli_moe_layer* L, const float* x, int32_t S, float* out,

@@ -43,13 +43,18 @@ class RefBank(ctypes.Structure):
                 ("n_mat", _i32), ("rows", _i32), ("K", _i32), ("bits", _i32)]
 
 
+class RefRouteOpts(ctypes.Structure):
+    _fields_ = [("n_group", _i32), ("topk_group", _i32), ("top_p", _f32)]
+
+
 class RefLayer(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("inter", _i32), ("n_experts", _i32), ("top_k", _i32),
                 ("routed_scaling_factor", _f32),
                 ("router_w", _p), ("router_bias", _p),
                 ("gate", RefBank), ("up", RefBank), ("down", RefBank),
                 ("has_shared", _i32),
-                ("sh_gate", RefBank), ("sh_up", RefBank), ("sh_down", RefBank)]
+                ("sh_gate", RefBank), ("sh_up", RefBank), ("sh_down", RefBank),
+                ("route", RefRouteOpts)]
 
 
 def lib():
@@ -82,6 +87,9 @@ def lib():
         L.ref_expert_ffn.argtypes = [ctypes.POINTER(RefBank)] * 3 + [_i32, _p, _p] + [_p] * 6
         L.ref_route_token.restype = ctypes.c_int
         L.ref_route_token.argtypes = [_p, _i32, _i32, _i32, _p, _p, _f32, _p, _p, _p, _p, _p]
+        L.ref_route_token_opt.restype = ctypes.c_int
+        L.ref_route_token_opt.argtypes = [_p, _i32, _i32, _i32, _p, _p, _f32, ctypes.POINTER(RefRouteOpts),
+                                          _p, _p, _p, _p, _p]
         L.ref_dispatch.argtypes = [_p, _i32, _i32, _i32, _p, _p, _p, _p, _p]
         L.ref_moe_layer_forward.restype = ctypes.c_int
         L.ref_moe_layer_forward.argtypes = [ctypes.POINTER(RefLayer), _p, _i32, _p,
@@ -209,8 +217,13 @@ def expert_ffn(gate, up, down, e: int, xq, xd):
     return out
 
 
-def route_token(x, router_w, bias, k: int, rsf: float):
-    """One token.  Returns dict ids, w (fp64), s, c, gap."""
+def route_opts(n_group: int = 1, topk_group: int = 1, top_p: float = 1.0) -> RefRouteOpts:
+    return RefRouteOpts(n_group, topk_group, top_p)
+
+
+def route_token(x, router_w, bias, k: int, rsf: float, opts: Optional[RefRouteOpts] = None):
+    """One token.  Returns dict ids (-1: slot dropped by top-p), w (fp64), s, c,
+    gap (smallest decision margin)."""
     x, W, b = _c(_as_np(x), np.float32), _c(_as_np(router_w), np.float32), _c(_as_np(bias), np.float32)
     E, H = W.shape
     ids = np.empty(k, np.int32)
@@ -218,17 +231,21 @@ def route_token(x, router_w, bias, k: int, rsf: float):
     s = np.empty(E, np.float32)
     c = np.empty(E, np.float32)
     gap = np.empty(1, np.float32)
-    st = lib().ref_route_token(_ptr(x), H, E, k, _ptr(W), _ptr(b), rsf,
-                               _ptr(ids), _ptr(w), _ptr(s), _ptr(c), _ptr(gap))
+    if opts is None:
+        st = lib().ref_route_token(_ptr(x), H, E, k, _ptr(W), _ptr(b), rsf,
+                                   _ptr(ids), _ptr(w), _ptr(s), _ptr(c), _ptr(gap))
+    else:
+        st = lib().ref_route_token_opt(_ptr(x), H, E, k, _ptr(W), _ptr(b), rsf, ctypes.byref(opts),
+                                       _ptr(ids), _ptr(w), _ptr(s), _ptr(c), _ptr(gap))
     if st != 0:
         raise RuntimeError(f"ref_route_token status {st}")
     return dict(ids=ids, w=w, s=s, c=c, gap=float(gap[0]))
 
 
-def route(x, router_w, bias, k: int, rsf: float):
+def route(x, router_w, bias, k: int, rsf: float, opts: Optional[RefRouteOpts] = None):
     """All tokens of x [S][H]: ids [S][k], w [S][k] fp64, gaps [S]."""
     x = _c(_as_np(x), np.float32)
-    res = [route_token(x[t], router_w, bias, k, rsf) for t in range(x.shape[0])]
+    res = [route_token(x[t], router_w, bias, k, rsf, opts) for t in range(x.shape[0])]
     S = x.shape[0]
     ids = np.array([r["ids"] for r in res], np.int32).reshape(S, k)
     w = np.array([r["w"] for r in res], np.float64).reshape(S, k)
@@ -267,7 +284,8 @@ class LayerHandle:
                           self.router_w.ctypes.data, self.bias.ctypes.data,
                           self.banks[0].c, self.banks[1].c, self.banks[2].c,
                           1 if w.has_shared else 0,
-                          self.sh[0].c, self.sh[1].c, self.sh[2].c)
+                          self.sh[0].c, self.sh[1].c, self.sh[2].c,
+                          route_opts(w.n_group, w.topk_group, w.top_p))
 
 
 def layer_forward(layer, x):

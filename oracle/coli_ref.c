@@ -247,15 +247,73 @@ int ref_expert_ffn(const ref_bank* gate, const ref_bank* up, const ref_bank* dow
 /* give no group parameters), bias used for selection only.                  */
 /* ------------------------------------------------------------------------ */
 
+/* Group stage of group-limited selection (DeepSeek-V3's noaux_tc routing,
+ * restated): marks eligible[e] for the experts of the topk_group groups with
+ * the largest top-2 sums of c; returns the kept/dropped group-score margin
+ * (+inf when every group is kept). */
+static float group_stage(const float* c, int32_t E, int32_t n_group, int32_t topk_group, char* eligible)
+{
+    const int32_t gsz = E / n_group;
+    float* score = (float*)malloc(sizeof(float) * (size_t)n_group);
+    char* kept = (char*)calloc((size_t)n_group, 1);
+    for (int32_t g = 0; g < n_group; ++g) {
+        /* the two largest c of the group (a repeated maximum counts twice) */
+        float first = -INFINITY, second = -INFINITY;
+        for (int32_t e = g * gsz; e < (g + 1) * gsz; ++e) {
+            if (c[e] > first) {
+                second = first;
+                first = c[e];
+            } else if (c[e] > second) {
+                second = c[e];
+            }
+        }
+        score[g] = first + second;
+    }
+    for (int32_t r = 0; r < topk_group; ++r) {
+        int32_t best = -1;
+        for (int32_t g = 0; g < n_group; ++g)
+            if (!kept[g] && (best < 0 || score[g] > score[best]))
+                best = g; /* strict '>' keeps the lower group on ties */
+        kept[best] = 1;
+    }
+    float worst_kept = INFINITY, best_dropped = -INFINITY;
+    for (int32_t g = 0; g < n_group; ++g) {
+        if (kept[g] && score[g] < worst_kept)
+            worst_kept = score[g];
+        if (!kept[g] && score[g] > best_dropped)
+            best_dropped = score[g];
+    }
+    for (int32_t e = 0; e < E; ++e)
+        eligible[e] = kept[e / gsz];
+    free(score);
+    free(kept);
+    return topk_group == n_group ? INFINITY : worst_kept - best_dropped;
+}
+
 int ref_route_token(const float* x, int32_t H, int32_t E, int32_t k,
                     const float* router_w, const float* bias, float rsf,
                     int32_t* ids, double* w, float* s_out, float* c_out, float* gap)
 {
+    return ref_route_token_opt(x, H, E, k, router_w, bias, rsf, NULL, ids, w, s_out, c_out, gap);
+}
+
+int ref_route_token_opt(const float* x, int32_t H, int32_t E, int32_t k,
+                        const float* router_w, const float* bias, float rsf,
+                        const ref_route_opts* opt, int32_t* ids, double* w, float* s_out,
+                        float* c_out, float* gap)
+{
+    const int32_t n_group = (opt && opt->n_group > 1) ? opt->n_group : 1;
+    const int32_t topk_group = n_group > 1 ? opt->topk_group : 1;
+    const float top_p = (opt && opt->top_p > 0.0f && opt->top_p < 1.0f) ? opt->top_p : 1.0f;
     if (k < 1 || k > E)
+        return REF_E_INVAL;
+    if (n_group > 1 && (E % n_group || E / n_group < 2 || topk_group < 1 || topk_group > n_group ||
+                        k > topk_group * (E / n_group)))
         return REF_E_INVAL;
     float* s = (float*)malloc(sizeof(float) * (size_t)E);
     float* c = (float*)malloc(sizeof(float) * (size_t)E);
     char* taken = (char*)calloc((size_t)E, 1);
+    char* eligible = (char*)malloc((size_t)E);
     for (int32_t e = 0; e < E; ++e) {
         double acc = 0.0;
         for (int32_t i = 0; i < H; ++i)
@@ -263,11 +321,15 @@ int ref_route_token(const float* x, int32_t H, int32_t E, int32_t k,
         float logit = (float)acc;
         s[e] = 1.0f / (1.0f + expf(-logit));
         c[e] = s[e] + bias[e];
+        eligible[e] = 1;
     }
+    float margin = INFINITY;
+    if (n_group > 1)
+        margin = group_stage(c, E, n_group, topk_group, eligible);
     for (int32_t j = 0; j < k; ++j) {
         int32_t best = -1;
         for (int32_t e = 0; e < E; ++e) {
-            if (taken[e])
+            if (taken[e] || !eligible[e])
                 continue;
             if (best < 0 || c[e] > c[best])
                 best = e; /* strict '>' keeps the lower id on ties */
@@ -275,22 +337,70 @@ int ref_route_token(const float* x, int32_t H, int32_t E, int32_t k,
         taken[best] = 1;
         ids[j] = best;
     }
-    if (gap) {
-        if (k == E) {
-            *gap = INFINITY;
-        } else {
-            float best_rest = -INFINITY;
-            for (int32_t e = 0; e < E; ++e)
-                if (!taken[e] && c[e] > best_rest)
-                    best_rest = c[e];
-            *gap = c[ids[k - 1]] - best_rest;
-        }
+    {
+        float best_rest = -INFINITY;
+        for (int32_t e = 0; e < E; ++e)
+            if (eligible[e] && !taken[e] && c[e] > best_rest)
+                best_rest = c[e];
+        const float g = c[ids[k - 1]] - best_rest; /* +inf when nothing is left */
+        if (g < margin)
+            margin = g;
     }
+    /* adaptive top-p: decisions in fp32 */
+    char* kept = (char*)malloc((size_t)k);
+    for (int32_t j = 0; j < k; ++j)
+        kept[j] = 1;
+    if (top_p < 1.0f) {
+        float den = 0.0f;
+        for (int32_t j = 0; j < k; ++j)
+            den = den + s[ids[j]];
+        int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+        for (int32_t j = 0; j < k; ++j) {
+            /* insertion by s descending; equal s keep slot order */
+            int32_t i = j;
+            while (i > 0 && s[ids[order[i - 1]]] < s[ids[j]]) {
+                order[i] = order[i - 1];
+                --i;
+            }
+            order[i] = j;
+        }
+        float cum = 0.0f, prev = 0.0f;
+        int32_t m = 0;
+        while (m < k) {
+            prev = cum;
+            cum = cum + s[ids[order[m]]] / den;
+            ++m;
+            if (cum >= top_p)
+                break;
+        }
+        for (int32_t j = 0; j < k; ++j)
+            kept[j] = 0;
+        for (int32_t i = 0; i < m; ++i)
+            kept[order[i]] = 1;
+        /* margins: one slot fewer stays below top_p; the cut slot reaches it */
+        float mp = top_p - prev;
+        if (cum >= top_p && cum - top_p < mp)
+            mp = cum - top_p;
+        if (mp < margin)
+            margin = mp;
+        free(order);
+    }
+    if (gap)
+        *gap = margin;
     double denom = 0.0;
     for (int32_t j = 0; j < k; ++j)
-        denom += (double)s[ids[j]];
-    for (int32_t j = 0; j < k; ++j)
-        w[j] = (double)rsf * ((double)s[ids[j]] / denom);
+        if (kept[j])
+            denom += (double)s[ids[j]];
+    for (int32_t j = 0; j < k; ++j) {
+        if (kept[j]) {
+            w[j] = (double)rsf * ((double)s[ids[j]] / denom);
+        } else {
+            w[j] = 0.0;
+            ids[j] = -1;
+        }
+    }
+    free(kept);
+    free(eligible);
     if (s_out)
         memcpy(s_out, s, sizeof(float) * (size_t)E);
     if (c_out)
@@ -315,11 +425,17 @@ void ref_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E,
     for (int32_t e = 0; e <= E; ++e)
         offsets[e] = 0;
     for (int32_t p = 0; p < P; ++p)
-        offsets[ids[p] + 1] += 1;
+        if (ids[p] >= 0)
+            offsets[ids[p] + 1] += 1;
     for (int32_t e = 0; e < E; ++e)
         offsets[e + 1] += offsets[e];
     for (int32_t p = 0; p < P; ++p) {
         int32_t e = ids[p];
+        if (e < 0) {
+            if (inv)
+                inv[p] = -1;
+            continue;
+        }
         int32_t pos = offsets[e] + fill[e];
         fill[e] += 1;
         sorted[pos] = p;
@@ -356,8 +472,8 @@ int ref_moe_layer_forward(const ref_layer* L, const float* x, int32_t S, double*
         const float* xt = x + (int64_t)t * H;
         double* ot = out + (int64_t)t * H;
         ref_quantize_q8_0(xt, H, xq, xd);
-        status = ref_route_token(xt, H, E, k, L->router_w, L->router_bias,
-                                 L->routed_scaling_factor, ids, w, NULL, NULL, NULL);
+        status = ref_route_token_opt(xt, H, E, k, L->router_w, L->router_bias,
+                                     L->routed_scaling_factor, &L->route, ids, w, NULL, NULL, NULL);
         if (status != REF_OK)
             break;
         for (int32_t n = 0; n < H; ++n)
@@ -373,6 +489,11 @@ int ref_moe_layer_forward(const ref_layer* L, const float* x, int32_t S, double*
                 memcpy(y_shared + (int64_t)t * H, y, sizeof(float) * (size_t)H);
         }
         for (int32_t j = 0; j < k && status == REF_OK; ++j) {
+            if (ids[j] < 0) { /* slot dropped by top-p */
+                if (y_routed)
+                    memset(y_routed + ((int64_t)t * k + j) * H, 0, sizeof(float) * (size_t)H);
+                continue;
+            }
             status = ref_expert_ffn(&L->gate, &L->up, &L->down, ids[j], xq, xd,
                                     NULL, NULL, NULL, NULL, NULL, y);
             if (status != REF_OK)

@@ -60,6 +60,20 @@ typedef struct ref_bank {
     int32_t n_mat, rows, K, bits;
 } ref_bank;
 
+/* Router variants.  n_group > 1: group-limited selection (experts in n_group
+ * equal contiguous groups; a group's score is the sum of its two largest
+ * biased scores; the topk_group best groups are kept, ties to the lower
+ * group; top-k runs over the kept groups' experts).  0 < top_p < 1: adaptive
+ * expert top-p (the k slots ordered by unbiased score, descending, ties in
+ * slot order; shares s / sum s accumulated in fp32; the shortest prefix whose
+ * cumulative share reaches top_p is kept, at least one slot; dropped slots get
+ * id -1 and weight 0, kept weights are renormalised over the kept slots). */
+typedef struct ref_route_opts {
+    int32_t n_group;
+    int32_t topk_group;
+    float top_p;
+} ref_route_opts;
+
 typedef struct ref_layer {
     int32_t hidden, inter, n_experts, top_k;
     float routed_scaling_factor;
@@ -68,6 +82,7 @@ typedef struct ref_layer {
     ref_bank gate, up, down;   /* routed: gate/up [I][H], down [H][I] per expert */
     int32_t has_shared;
     ref_bank sh_gate, sh_up, sh_down; /* one matrix each */
+    ref_route_opts route;      /* n_group 0 or 1 and top_p 0 or >= 1: plain top-k */
 } ref_layer;
 
 /* ---- activation quantisation (Q8_0 style, blocks of 32, fp32 scale) ---- */
@@ -121,11 +136,21 @@ int ref_expert_ffn(const ref_bank* gate, const ref_bank* up, const ref_bank* dow
 int ref_route_token(const float* x, int32_t H, int32_t E, int32_t k,
                     const float* router_w, const float* bias, float rsf,
                     int32_t* ids, double* w, float* s, float* c, float* gap);
+/* The same with the router variants of ref_route_opts (NULL: none).  gap is
+ * the smallest decision margin: the expert gap above among the eligible
+ * experts, with n_group > 1 also the topk_group-th kept group score minus the
+ * best dropped one, with top-p also the distances of top_p from the
+ * cumulative shares just before and at the cut. */
+int ref_route_token_opt(const float* x, int32_t H, int32_t E, int32_t k,
+                        const float* router_w, const float* bias, float rsf,
+                        const ref_route_opts* opt, int32_t* ids, double* w, float* s, float* c,
+                        float* gap);
 
 /* ---- union dispatch ----
  * pairs p = t*k + j.  counts -> exclusive offsets[E+1]; sorted[] = pairs
  * stably ordered by expert; inv[p] = position of p in sorted[]; active[] =
- * experts with count > 0 ascending, *n_active their number. */
+ * experts with count > 0 ascending, *n_active their number.  A negative id
+ * (a slot dropped by top-p) is no pair: it is not counted and inv[p] = -1. */
 void ref_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E,
                   int32_t* offsets, int32_t* sorted, int32_t* inv,
                   int32_t* active, int32_t* n_active);

@@ -40,7 +40,8 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("inter", _i32), ("n_experts", _i32), ("top_k", _i32),
                 ("routed_scaling_factor", ctypes.c_float), ("router_w", _vp), ("router_bias", _vp),
                 ("gate", QBankDesc), ("up", QBankDesc), ("down", QBankDesc), ("has_shared", _i32),
-                ("sh_gate", QBankDesc), ("sh_up", QBankDesc), ("sh_down", QBankDesc)]
+                ("sh_gate", QBankDesc), ("sh_up", QBankDesc), ("sh_down", QBankDesc),
+                ("n_group", _i32), ("topk_group", _i32), ("top_p", ctypes.c_float)]
 
 
 class ColibriError(RuntimeError):
@@ -129,7 +130,8 @@ class MoELayer:
 
     def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, rsf: float,
                  router_w: torch.Tensor, router_bias: torch.Tensor, gate: QBank, up: QBank,
-                 down: QBank, shared: Optional[Sequence[QBank]] = None):
+                 down: QBank, shared: Optional[Sequence[QBank]] = None,
+                 n_group: int = 1, topk_group: int = 1, top_p: float = 1.0):
         self.hidden, self.inter, self.n_experts, self.top_k, self.rsf = hidden, inter, n_experts, top_k, rsf
         self.router_w, self.router_bias = router_w, router_bias
         self.gate, self.up, self.down = gate, up, down
@@ -137,7 +139,7 @@ class MoELayer:
         sh = self.shared or (gate, up, down)
         self.desc = LayerDesc(hidden, inter, n_experts, top_k, rsf, _ptr(router_w), _ptr(router_bias),
                               gate.desc(), up.desc(), down.desc(), 1 if self.shared else 0,
-                              sh[0].desc(), sh[1].desc(), sh[2].desc())
+                              sh[0].desc(), sh[1].desc(), sh[2].desc(), n_group, topk_group, top_p)
 
     def workspace_bytes(self, S: int) -> int:
         n = lib().colibri_workspace_bytes(ctypes.byref(self.desc), S)

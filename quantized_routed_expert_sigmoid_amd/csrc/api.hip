@@ -68,6 +68,14 @@ int check_layer(const coli_moe_layer* L)
         return st;
     if (L->gate.qtype != L->up.qtype)
         return COLI_E_UNSUPPORTED;
+    if (L->n_group < 0 || !(L->top_p >= 0.0f)) /* also rejects a NaN top_p */
+        return COLI_E_INVAL;
+    if (L->n_group > 1) {
+        const int32_t G = L->n_group;
+        if (G > kMaxGroups || E % G || E / G < 2 || L->topk_group < 1 || L->topk_group > G ||
+            L->top_k > L->topk_group * (E / G))
+            return COLI_E_INVAL;
+    }
     if (L->has_shared) {
         if ((st = check_bank(&L->sh_gate, 1, I, H)) || (st = check_bank(&L->sh_up, 1, I, H)) ||
             (st = check_bank(&L->sh_down, 1, H, I)))
@@ -85,6 +93,15 @@ int check_tokens(int32_t S, int32_t k)
     if (S > COLI_MAX_TOKENS || (int64_t)S * k > COLI_MAX_PAIRS)
         return COLI_E_UNSUPPORTED;
     return COLI_OK;
+}
+
+RouteOpts route_opts(const coli_moe_layer* L)
+{
+    RouteOpts o;
+    o.n_group = L->n_group > 1 ? L->n_group : 1;
+    o.topk_group = L->n_group > 1 ? L->topk_group : 1;
+    o.top_p = L->top_p;
+    return o;
 }
 
 /* Byte offsets of the workspace regions. */
@@ -280,7 +297,8 @@ int colibri_route(const coli_moe_layer* L, const float* x, int32_t S, int32_t* t
     hipError_t e = launch_router_logits(x, S, L->hidden, L->n_experts, L->router_w, logits, s);
     if (e == hipSuccess)
         e = launch_router_select(logits, router_parts(S, L->n_experts, L->hidden), L->router_bias, S,
-                                 L->n_experts, L->top_k, L->routed_scaling_factor, topk_ids, topk_w, s);
+                                 L->n_experts, L->top_k, L->routed_scaling_factor, route_opts(L), topk_ids,
+                                 topk_w, s);
     return hip_status(e);
 }
 
@@ -453,7 +471,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
     if (e == hipSuccess && S > kSmallS)
         e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
-                                 L->routed_scaling_factor, ids, w, s);
+                                 L->routed_scaling_factor, route_opts(L), ids, w, s);
     e = mark(1, e);
     if (one_token) {
         DecodeArgs dd;
@@ -463,6 +481,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         dd.E = E;
         dd.k = k;
         dd.rsf = L->routed_scaling_factor;
+        dd.opt = route_opts(L);
         dd.ids = ids;
         dd.w = w;
         dd.out = out;
@@ -480,7 +499,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
                 e = launch_ffn_down_decode(dd, L->down.qtype, s);
             e = mark(4, e);
             if (e == hipSuccess)
-                e = launch_combine(y, nullptr, w, 1, k, H, shared ? k : -1, out, s);
+                e = launch_combine(y, nullptr, ids, w, 1, k, H, shared ? k : -1, out, s);
         }
         e = mark(5, e);
         return hip_status(e);
@@ -488,7 +507,8 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     if (e == hipSuccess)
         e = S <= kSmallS
                 ? launch_select_dispatch_small(logits, L->router_bias, S, E, k, L->routed_scaling_factor,
-                                               ids, w, offsets, sorted, inv, active, n_active, ul, s)
+                                               route_opts(L), ids, w, offsets, sorted, inv, active,
+                                               n_active, ul, s)
                 : launch_dispatch(ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, s);
     e = mark(2, e);
 
@@ -511,7 +531,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         e = launch_ffn_down_mfma(b, L->sh_down.qtype, s);
     e = mark(4, e);
     if (e == hipSuccess)
-        e = launch_combine(y, inv, w, S, k, H, shared ? P : -1, out, s);
+        e = launch_combine(y, inv, ids, w, S, k, H, shared ? P : -1, out, s);
     e = mark(5, e);
     return hip_status(e);
 }

@@ -116,10 +116,12 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
             wcnt[w][e] = 0;
     }
     __syncthreads();
-    /* ids outside [0, E) violate the documented precondition; they are
-     * clamped so that no access leaves its buffer. */
+    /* a negative id is a dropped slot (no pair); ids past E - 1 violate the
+     * documented precondition and are clamped so that no access leaves its
+     * buffer */
     for (int32_t p = tid; p < P; p += kDispThreads)
-        atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);
+        if (ids[p] >= 0)
+            atomicAdd(&cnt[min(ids[p], E - 1)], 1);
     __syncthreads();
 
     /* offsets, active list and unit lists: one expert per thread, one scan of
@@ -145,7 +147,7 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
         }
     }
     if (tid == 0) {
-        offsets[E] = P;
+        offsets[E] = (int32_t)(tot & 0x1FFFFF); /* pairs kept */
         *n_active = (int32_t)((tot >> 21) & 0x7FF);
         if (ul) {
             *ul->n_units = min((int32_t)((tot >> 32) & 0xFFF), ul->max_units);
@@ -161,8 +163,11 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int32_t r0 = 0; r0 < P; r0 += kDispThreads) {
         const int32_t p = r0 + tid;
-        const bool valid = p < P;
-        const int32_t ex = valid ? min(max(ids[p], 0), E - 1) : 0;
+        const int32_t id = p < P ? ids[p] : -1;
+        const bool valid = id >= 0;
+        const int32_t ex = valid ? min(id, E - 1) : 0;
+        if (p < P && !valid && inv)
+            inv[p] = -1;
         uint64_t m = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             uint64_t bal = __ballot(valid && ((ex >> b) & 1));
@@ -216,29 +221,29 @@ hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, 
  * then the whole workgroup dispatches the S*k pairs from LDS. */
 __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
     const float* __restrict__ logits, const float* __restrict__ bias, int32_t S, int32_t E, int32_t k,
-    float rsf, int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ active,
-    int32_t* __restrict__ n_active, UnitLists ul)
+    float rsf, RouteOpts opt, int32_t* __restrict__ ids, float* __restrict__ weights,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, UnitLists ul)
 {
     __shared__ DispatchShared sh;
-    __shared__ float sel_s[kSmallS][64];
+    __shared__ float sel_s[kSmallS][128];
     __shared__ int32_t sel_ids[kSmallS * 64];
     const int wv = threadIdx.x >> 6;
     if (wv < S)
         select_token(logits + (int64_t)wv * E, bias, E, k, rsf, ids + (int64_t)wv * k,
-                     weights + (int64_t)wv * k, sel_s[wv], sel_ids + wv * k);
+                     weights + (int64_t)wv * k, sel_s[wv], sel_ids + wv * k, 1, 0, opt);
     __syncthreads();
     dispatch_body(sel_ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, sh);
 }
 
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
-                                        int32_t k, float rsf, int32_t* ids, float* weights,
-                                        int32_t* offsets, int32_t* sorted, int32_t* inv,
+                                        int32_t k, float rsf, const RouteOpts& opt, int32_t* ids,
+                                        float* weights, int32_t* offsets, int32_t* sorted, int32_t* inv,
                                         int32_t* active, int32_t* n_active, const UnitLists& ul,
                                         hipStream_t st)
 {
     hipLaunchKernelGGL(select_dispatch_small, dim3(1), dim3(kDispThreads), 0, st, logits, bias, S, E, k,
-                       rsf, ids, weights, offsets, sorted, inv, active, n_active, ul);
+                       rsf, opt, ids, weights, offsets, sorted, inv, active, n_active, ul);
     return hipGetLastError();
 }
 
@@ -273,10 +278,12 @@ hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, const UnitList
     return hipGetLastError();
 }
 
-/* ---- combine: out[t] = y_shared[t] + sum_j w[t][j] * y[inv[t*k+j]] -------- */
+/* ---- combine: out[t] = y_shared[t] + sum_j w[t][j] * y[inv[t*k+j]] --------
+ * (dropped slots, inv < 0 or with inv null ids < 0, are skipped) */
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
+                                                      const int32_t* __restrict__ ids,
                                                       const float* __restrict__ w, int32_t S,
                                                       int32_t k, int32_t H, int32_t shared_row0,
                                                       float* __restrict__ out)
@@ -292,8 +299,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         acc = reinterpret_cast<const float4*>(y + (int64_t)(shared_row0 + t) * H)[c];
     for (int j = 0; j < k; ++j) {
         const int32_t p = t * k + j;
+        const int32_t row = inv ? inv[p] : (ids[p] >= 0 ? p : -1);
+        if (row < 0) /* slot dropped by top-p */
+            continue;
         const float wj = w[p];
-        const float4 v = reinterpret_cast<const float4*>(y + (int64_t)(inv ? inv[p] : p) * H)[c];
+        const float4 v = reinterpret_cast<const float4*>(y + (int64_t)row * H)[c];
         acc.x = __builtin_fmaf(wj, v.x, acc.x);
         acc.y = __builtin_fmaf(wj, v.y, acc.y);
         acc.z = __builtin_fmaf(wj, v.z, acc.z);
@@ -302,14 +312,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     reinterpret_cast<float4*>(out + (int64_t)t * H)[c] = acc;
 }
 
-hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int32_t S, int32_t k,
-                          int32_t H, int32_t shared_row0, float* out, hipStream_t st)
+hipError_t launch_combine(const float* y, const int32_t* inv, const int32_t* ids, const float* w,
+                          int32_t S, int32_t k, int32_t H, int32_t shared_row0, float* out, hipStream_t st)
 {
     if (S == 0)
         return hipSuccess;
     int64_t threads = (int64_t)S * (H / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, y,
-                       inv, w, S, k, H, shared_row0, out);
+                       inv, ids, w, S, k, H, shared_row0, out);
     return hipGetLastError();
 }
 

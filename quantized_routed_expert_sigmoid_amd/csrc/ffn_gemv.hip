@@ -505,7 +505,7 @@ inline int dec_ni(int nb)
 __host__ __device__ inline int dec_region(int nb)
 {
     const int p = kDecRows * (nb | 1);
-    return p > 192 ? p : 192;
+    return p > 256 ? p : 256;
 }
 
 __host__ __device__ inline size_t dec_lds_bytes(int nb)
@@ -646,14 +646,17 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     if (routed) {
         /* selection scratch in the wave's (not yet used) partial buffer */
         float* sel_s = reinterpret_cast<float*>(P);
-        float* sel_w = sel_s + 64;
-        int32_t* sel_ids = P + 128;
+        float* sel_w = sel_s + 128;
+        int32_t* sel_ids = P + 192;
         const bool store = blockIdx.x == 0 && wv == 0;
         select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids, store ? d.w : sel_w, sel_s,
-                     sel_ids);
+                     sel_ids, 1, 0, d.opt);
         wave_lds_sync();
-        e = min(max(sel_ids[u], 0), sg.n_mat - 1);
+        const int sel = sel_ids[u];
         wave_lds_sync();
+        if (sel < 0) /* slot dropped by top-p: every wave sees the same selection */
+            return;
+        e = min(sel, sg.n_mat - 1);
     }
     const int64_t rowbytes = (int64_t)a.H * BITS / 8;
     /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
@@ -697,8 +700,10 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     if (u >= nunits)
         return;
     const bool routed = u < d.k;
+    if (routed && d.ids[u] < 0) /* slot dropped by top-p */
+        return;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
-    const int e = routed ? min(max(d.ids[u], 0), sg.n_mat - 1) : 0;
+    const int e = routed ? min(d.ids[u], sg.n_mat - 1) : 0;
     const int nb = a.I / 32, sp = nb | 1, region = dec_region(nb);
     int32_t* P = dec_lds + wv * region;
     float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
@@ -743,14 +748,15 @@ inline bool dc_fits(int U, int nb)
     return dc_lds_words(U, nb) * 4 <= 64 * 1024;
 }
 
-/* First of this wave's two rows of unit j's down matrix. */
-__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int j, int row0, int64_t rowbytes)
+/* First of this wave's two rows of unit u's down matrix (u = slot, or k for
+ * the shared expert). */
+__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int u, int row0, int64_t rowbytes)
 {
     const FfnArgs& a = d.f;
-    const bool routed = j < d.k;
+    const bool routed = u < d.k;
     const uint8_t* w = routed ? a.seg[0].down_w : a.seg[1].down_w;
     const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
-    const int e = routed ? min(max(d.ids[j], 0), n_mat - 1) : 0;
+    const int e = routed ? min(max(d.ids[u], 0), n_mat - 1) : 0;
     return w + ((int64_t)e * a.H + row0) * rowbytes;
 }
 
@@ -767,6 +773,20 @@ __device__ __forceinline__ void dc_act(const uint32_t* xal, int j, int nb, uint3
     }
 }
 
+/* Unit of compacted index n: the n-th kept routed slot (bit set in `kept`),
+ * then the shared expert (index k).  Without top-p every slot is kept and
+ * the index is the slot. */
+__device__ __forceinline__ int dc_unit(uint64_t kept, int n_kept, int k, int n, bool all_kept)
+{
+    if (n >= n_kept)
+        return k;
+    if (all_kept)
+        return n;
+    for (int i = 0; i < n; ++i)
+        kept &= kept - 1;
+    return __builtin_ctzll(kept);
+}
+
 template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
 {
@@ -774,7 +794,12 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const bool shared = a.nseg > 1;
-    const int U = d.k + (shared ? 1 : 0);
+    /* slots dropped by top-p are neither streamed nor combined: the units are
+     * the kept routed slots in slot order, then the shared expert */
+    const bool all_kept = !(d.opt.top_p > 0.0f && d.opt.top_p < 1.0f);
+    const uint64_t kept = all_kept ? 0 : __ballot(lane < d.k && d.ids[lane] >= 0);
+    const int n_kept = all_kept ? d.k : __popcll(kept);
+    const int U = n_kept + (shared ? 1 : 0);
     const int nb = a.I / 32, sp = nb | 1;
     uint32_t* xal = reinterpret_cast<uint32_t*>(dc_lds);        /* [U][nb][8] */
     float* dls = reinterpret_cast<float*>(xal + U * nb * 8);    /* [U][nb] */
@@ -783,29 +808,34 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     const int row0 = blockIdx.x * kDcRows + 2 * wv;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
 
-    /* unit 0's pair is issued before h is staged */
+    if (U == 0)
+        return;
+    /* compacted unit 0's pair is issued before h is staged */
     PairLoad<BITS, NI> A, B;
-    pair_load<BITS, NI>(A, dc_rows(d, 0, row0, rowbytes), rowbytes, 0, 2, nb);
+    pair_load<BITS, NI>(A, dc_rows(d, dc_unit(kept, n_kept, d.k, 0, all_kept), row0, rowbytes), rowbytes, 0, 2, nb);
     for (int i = threadIdx.x; i < U * nb; i += 64 * kGroups) {
         const int j = i / nb, b = i - j * nb;
+        const int u = dc_unit(kept, n_kept, d.k, j, all_kept);
         uint32_t x[8], xa[8];
-        load_codes(a.hq + (int64_t)j * a.I + (int64_t)b * 32, x);
+        load_codes(a.hq + (int64_t)u * a.I + (int64_t)b * 32, x);
         prep_activation<BITS>(x, xa);
         uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
         dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
         dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
-        dls[i] = a.hd[(int64_t)j * nb + b];
+        dls[i] = a.hd[(int64_t)u * nb + b];
     }
     __syncthreads();
 
-    /* unit j's pair is in A for even j and in B for odd j; loads are
+    /* compacted unit j's pair is in A for even j and in B for odd j; loads are
      * unconditional (past the last unit they reload it: in bounds, unused) */
     for (int j = 0; j < U; j += 2) {
         uint32_t xa[NI][8];
-        pair_load<BITS, NI>(B, dc_rows(d, min(j + 1, U - 1), row0, rowbytes), rowbytes, 0, 2, nb);
+        pair_load<BITS, NI>(B, dc_rows(d, dc_unit(kept, n_kept, d.k, min(j + 1, U - 1), all_kept), row0, rowbytes),
+                            rowbytes, 0, 2, nb);
         dc_act<NI>(xal, j, nb, xa);
         pair_partials<BITS, NI>(A, xa, 0, nb, P + 2 * j * sp, sp);
-        pair_load<BITS, NI>(A, dc_rows(d, min(j + 2, U - 1), row0, rowbytes), rowbytes, 0, 2, nb);
+        pair_load<BITS, NI>(A, dc_rows(d, dc_unit(kept, n_kept, d.k, min(j + 2, U - 1), all_kept), row0, rowbytes),
+                            rowbytes, 0, 2, nb);
         if (j + 1 < U) {
             dc_act<NI>(xal, j + 1, nb, xa);
             pair_partials<BITS, NI>(B, xa, 0, nb, P + 2 * (j + 1) * sp, sp);
@@ -842,19 +872,20 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
         v = v + __shfl(acc, base + 2, kWave);
         v = v + __shfl(acc, base + 3, kWave);
         if (g == 0 && ci < 8 * U) {
-            const int j = rd >> 1, n = row0 + (rd & 1);
-            const bool routed = j < d.k;
+            const int u = dc_unit(kept, n_kept, d.k, rd >> 1, all_kept), n = row0 + (rd & 1);
+            const bool routed = u < d.k;
             const float* ds = routed ? a.seg[0].down_s : a.seg[1].down_s;
             const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
-            const int e = routed ? min(max(d.ids[j], 0), n_mat - 1) : 0;
+            const int e = routed ? min(max(d.ids[u], 0), n_mat - 1) : 0;
             ys[rd] = ds[(int64_t)e * a.H + n] * v;
         }
     }
     wave_lds_sync();
     if (lane < 2) {
-        float outv = shared ? ys[2 * d.k + lane] : 0.0f;
-        for (int j = 0; j < d.k; ++j)
-            outv = __builtin_fmaf(d.w[j], ys[2 * j + lane], outv);
+        /* compacted order is slot order: the combine's fma order is kept */
+        float outv = shared ? ys[2 * n_kept + lane] : 0.0f;
+        for (int j = 0; j < n_kept; ++j)
+            outv = __builtin_fmaf(d.w[dc_unit(kept, n_kept, d.k, j, all_kept)], ys[2 * j + lane], outv);
         d.out[row0 + lane] = outv;
     }
 }

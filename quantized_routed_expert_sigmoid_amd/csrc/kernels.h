@@ -28,6 +28,15 @@ constexpr int32_t kPairLimit = 1 << 20;
  * (a workgroup per router row; selection and dispatch in one workgroup). */
 constexpr int kSmallS = 8;
 
+/* Most expert groups of group-limited selection. */
+constexpr int kMaxGroups = 64;
+
+/* Router variants (n_group <= 1 and top_p outside (0, 1): plain top-k). */
+struct RouteOpts {
+    int32_t n_group, topk_group;
+    float top_p;
+};
+
 /* A work unit: expert e applied to sorted positions [pos0, pos0 + ntok). */
 struct Unit {
     int32_t e, pos0, ntok, pad;
@@ -88,7 +97,8 @@ struct DecodeArgs {
     const float* bias;   /* [E] */
     int32_t E, k;
     float rsf;
-    int32_t* ids;        /* [k] selected experts, slot order */
+    RouteOpts opt;
+    int32_t* ids;        /* [k] selected experts, slot order (-1: dropped) */
     float* w;            /* [k] routing weights */
     float* out;          /* [H] layer output (down + combine launch) */
 };
@@ -150,8 +160,8 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
 
 /* Selection from n_parts partial logit slices (added in slice order). */
 hipError_t launch_router_select(const float* logits, int32_t n_parts, const float* bias, int32_t S,
-                                int32_t E, int32_t k, float rsf, int32_t* ids, float* weights,
-                                hipStream_t st);
+                                int32_t E, int32_t k, float rsf, const RouteOpts& opt, int32_t* ids,
+                                float* weights, hipStream_t st);
 
 /* S <= kSmallS: router logits and Q8_0 quantisation of x in one launch. */
 hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
@@ -159,8 +169,8 @@ hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t
 
 /* S <= kSmallS: selection, union dispatch and unit lists in one workgroup. */
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
-                                        int32_t k, float rsf, int32_t* ids, float* weights,
-                                        int32_t* offsets, int32_t* sorted, int32_t* inv,
+                                        int32_t k, float rsf, const RouteOpts& opt, int32_t* ids,
+                                        float* weights, int32_t* offsets, int32_t* sorted, int32_t* inv,
                                         int32_t* active, int32_t* n_active, const UnitLists& ul,
                                         hipStream_t st);
 
@@ -190,9 +200,11 @@ bool down_combine_decode_fits(const DecodeArgs& d);
 hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 
 /* out[t] = y[shared_row0 + t] (if shared_row0 >= 0) + sum_j w[t*k+j] * y[row(t*k+j)],
- * row(p) = inv[p], or p when inv is null. */
-hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, int32_t S,
-                          int32_t k, int32_t H, int32_t shared_row0, float* out, hipStream_t st);
+ * row(p) = inv[p], or p when inv is null; slots with inv[p] < 0 (inv null:
+ * ids[p] < 0) were dropped and are skipped. */
+hipError_t launch_combine(const float* y, const int32_t* inv, const int32_t* ids, const float* w,
+                          int32_t S, int32_t k, int32_t H, int32_t shared_row0, float* out,
+                          hipStream_t st);
 
 } // namespace coli
 

@@ -252,26 +252,27 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
                                                             int32_t n_parts,
                                                             const float* __restrict__ bias,
                                                             int32_t S, int32_t E, int32_t k,
-                                                            float rsf, int32_t* __restrict__ ids,
+                                                            float rsf, RouteOpts opt,
+                                                            int32_t* __restrict__ ids,
                                                             float* __restrict__ weights)
 {
-    __shared__ float sel_s[4][64];
+    __shared__ float sel_s[4][128];
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= S)
         return;
     select_token(logits + (int64_t)t * E, bias, E, k, rsf, ids + (int64_t)t * k,
-                 weights + (int64_t)t * k, sel_s[wv], nullptr, n_parts, (int64_t)S * E);
+                 weights + (int64_t)t * k, sel_s[wv], nullptr, n_parts, (int64_t)S * E, opt);
 }
 
 hipError_t launch_router_select(const float* logits, int32_t n_parts, const float* bias, int32_t S,
-                                int32_t E, int32_t k, float rsf, int32_t* ids, float* weights,
-                                hipStream_t st)
+                                int32_t E, int32_t k, float rsf, const RouteOpts& opt, int32_t* ids,
+                                float* weights, hipStream_t st)
 {
     if (S == 0)
         return hipSuccess;
     hipLaunchKernelGGL(router_select_kernel, dim3((S + 3) / 4), dim3(256), 0, st, logits, n_parts, bias,
-                       S, E, k, rsf, ids, weights);
+                       S, E, k, rsf, opt, ids, weights);
     return hipGetLastError();
 }
 

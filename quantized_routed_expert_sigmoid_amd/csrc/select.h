@@ -14,6 +14,7 @@
 #define COLI_SELECT_H
 
 #include "device_common.h"
+#include "kernels.h"
 
 namespace coli {
 
@@ -25,14 +26,61 @@ __device__ __forceinline__ uint32_t order_bits(float c)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+/* The float an order_bits key came from. */
+__device__ __forceinline__ float key_value(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+/* Wave maximum of key over the lane's experts e with group(e) == g (all
+ * experts when g < 0), then the lowest such expert holding it; returns the
+ * key and writes the expert to *e_out (-1 when the set is empty). */
+__device__ __forceinline__ uint32_t argmax_key(const uint32_t (&key)[kMaxPerLane], int per_lane, int E, int gsz,
+                                               int g, int skip_e, int* e_out)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + 64 * i;
+        if (i < per_lane && e < E && (g < 0 || e / gsz == g) && e != skip_e)
+            best = key[i] > best ? key[i] : best;
+    }
+    best = wave_reduce_u32<true>(best);
+    uint32_t mine = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + 64 * i;
+        if (i < per_lane && e < E && (g < 0 || e / gsz == g) && e != skip_e && key[i] == best &&
+            mine == 0xFFFFFFFFu)
+            mine = (uint32_t)e;
+    }
+    const uint32_t e = wave_reduce_u32<false>(mine);
+    *e_out = best == 0 ? -1 : (int)e;
+    return best;
+}
+
 /* lt: the token's E logits, or with n_parts > 1 the first of n_parts partial
- * sums part_stride floats apart (added in slice order); writes ids_out[0..k), w_out[0..k) and, when
- * ids_lds is not null, ids_lds[0..k).  sel_s: 64 floats of LDS owned by the
- * calling wave. */
+ * sums part_stride floats apart (added in slice order).  Writes ids_out[0..k),
+ * w_out[0..k) and, when ids_lds is not null, ids_lds[0..k).  sel_s: 128 floats
+ * of LDS owned by the calling wave.  Called by a whole wave.
+ *
+ * Group stage (opt.n_group > 1): per group the largest biased score, the
+ * lowest expert holding it, then the largest score among the group's other
+ * experts; their fp32 sum is the group score.  topk_group rounds of a wave
+ * maximum pick the groups (ties to the lower group); experts of the other
+ * groups become unavailable.
+ *
+ * Top-p (0 < opt.top_p < 1): each slot's rank by unbiased score (descending,
+ * ties in slot order) is computed in parallel; lane 0 then accumulates the
+ * fp32 shares s / sum s in rank order, in the order and precision of the
+ * oracle, up to the first cumulative share >= top_p.  Slots past the cut get
+ * id -1 and weight 0; the kept weights are renormalised over the kept slots
+ * (denominator in slot order). */
 __device__ __forceinline__ void select_token(const float* lt, const float* bias, int32_t E, int32_t k,
                                              float rsf, int32_t* ids_out, float* w_out, float* sel_s,
                                              int32_t* ids_lds, int32_t n_parts = 1,
-                                             int64_t part_stride = 0)
+                                             int64_t part_stride = 0, RouteOpts opt = RouteOpts{1, 1, 1.0f})
 {
     const int lane = threadIdx.x & 63;
     const int per_lane = (E + 63) / 64; /* uniform */
@@ -51,6 +99,32 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
         } else {
             s[i] = 0.0f;
             key[i] = 0;
+        }
+    }
+    if (opt.n_group > 1) {
+        const int G = min(opt.n_group, kMaxGroups), gsz = E / G;
+        float gscore = 0.0f;
+        for (int g = 0; g < G; ++g) {
+            int e1, e2;
+            const uint32_t k1 = argmax_key(key, per_lane, E, gsz, g, -1, &e1);
+            const uint32_t k2 = argmax_key(key, per_lane, E, gsz, g, e1, &e2);
+            if (lane == g)
+                gscore = key_value(k1) + key_value(k2);
+        }
+        uint32_t gkey = lane < G ? order_bits(gscore) : 0;
+        uint64_t kept = 0;
+        for (int r = 0; r < opt.topk_group; ++r) {
+            const uint32_t best = wave_reduce_u32<true>(gkey);
+            const uint32_t gsel = wave_reduce_u32<false>(gkey == best && lane < G ? (uint32_t)lane : 0xFFFFFFFFu);
+            kept |= 1ull << gsel;
+            if (lane == (int)gsel)
+                gkey = 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) {
+            const int e = lane + 64 * i;
+            if (i < per_lane && e < E && !((kept >> (e / gsz)) & 1))
+                key[i] = 0;
         }
     }
     for (int j = 0; j < k; ++j) {
@@ -87,6 +161,57 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (opt.top_p > 0.0f && opt.top_p < 1.0f) {
+        int32_t* slot_of_rank = reinterpret_cast<int32_t*>(sel_s + 64);
+        if (lane < k) {
+            const float mine = sel_s[lane];
+            int rank = 0;
+            for (int i = 0; i < k; ++i)
+                rank += (sel_s[i] > mine || (sel_s[i] == mine && i < lane)) ? 1 : 0;
+            slot_of_rank[rank] = lane;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        int m = k;
+        if (lane == 0) {
+            float den = 0.0f;
+            for (int j = 0; j < k; ++j)
+                den = den + sel_s[j];
+            float cum = 0.0f;
+            for (int r = 0; r < k; ++r) {
+                cum = cum + sel_s[slot_of_rank[r]] / den;
+                if (cum >= opt.top_p) {
+                    m = r + 1;
+                    break;
+                }
+            }
+        }
+        m = __builtin_amdgcn_readfirstlane(m);
+        /* slot j is kept iff its rank is below m */
+        bool keep = false;
+        if (lane < k) {
+            const float mine = sel_s[lane];
+            int rank = 0;
+            for (int i = 0; i < k; ++i)
+                rank += (sel_s[i] > mine || (sel_s[i] == mine && i < lane)) ? 1 : 0;
+            keep = rank < m;
+        }
+        const uint64_t kept_slots = __ballot(keep);
+        float denom = 0.0f;
+        for (int j = 0; j < k; ++j)
+            if ((kept_slots >> j) & 1)
+                denom += sel_s[j];
+        if (lane < k)
+            w_out[lane] = keep ? rsf * (sel_s[lane] / denom) : 0.0f;
+        if (lane == 0) /* the lane that stored the ids rewrites them, in order */
+            for (int j = 0; j < k; ++j)
+                if (!((kept_slots >> j) & 1)) {
+                    ids_out[j] = -1;
+                    if (ids_lds)
+                        ids_lds[j] = -1;
+                }
+        return;
+    }
     float denom = 0.0f;
     for (int j = 0; j < k; ++j)
         denom += sel_s[j];

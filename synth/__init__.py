@@ -153,6 +153,10 @@ class Workload:
     zipf_beta: float = 0.1
     scale_mult: float = 0.02
     seed: int = 0
+    # router variants (1, 1, 1.0: plain top-k)
+    n_group: int = 1
+    topk_group: int = 1
+    top_p: float = 1.0
 
     def row_bytes(self, K: int) -> int:
         return K * self.bits // 8

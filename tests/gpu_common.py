@@ -32,7 +32,8 @@ def to_device(L: synth.Layer):
     shared = [qb(L.sh_gate), qb(L.sh_up), qb(L.sh_down)] if w.has_shared else None
     return qre.MoELayer(w.hidden, w.inter, w.n_experts, w.top_k, w.rsf,
                         L.router_w.cuda().contiguous(), L.bias.cuda().contiguous(),
-                        qb(L.gate), qb(L.up), qb(L.down), shared)
+                        qb(L.gate), qb(L.up), qb(L.down), shared,
+                        w.n_group, w.topk_group, w.top_p)
 
 
 def gapped_activations(w: synth.Workload, router_w, bias, S=None, tag=""):
@@ -42,10 +43,11 @@ def gapped_activations(w: synth.Workload, router_w, bias, S=None, tag=""):
     attempts = {}
     x = synth.activations(w, S, tag=tag).numpy()
     W, b = router_w.cpu().numpy(), bias.cpu().numpy()
+    opts = oracle.route_opts(w.n_group, w.topk_group, w.top_p)
     for t in range(S):
         a = 0
         while True:
-            r = oracle.route_token(x[t], W, b, w.top_k, w.rsf)
+            r = oracle.route_token(x[t], W, b, w.top_k, w.rsf, opts)
             if r["gap"] > GAP:
                 break
             a += 1

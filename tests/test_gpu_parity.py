@@ -56,6 +56,49 @@ def _small_layer(name, **kw):
     return w, synth.make_layer(w)
 
 
+ROUTE_VARIANTS = {
+    "group_limited": dict(name="rv_g", layer="rv_g", n_experts=64, top_k=6, S=37, rsf=2.5, n_group=8,
+                          topk_group=3),
+    "top_p": dict(name="rv_p", layer="rv_p", n_experts=64, top_k=8, S=37, rsf=2.5, top_p=0.6),
+    "group_top_p_small_batch": dict(name="rv_gp", layer="rv_gp", n_experts=64, top_k=8, S=6, rsf=2.5,
+                                    n_group=8, topk_group=4, top_p=0.7),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROUTE_VARIANTS))
+def test_route_variant_parity(qre, case):
+    """Group-limited selection and adaptive top-p: ids (-1 for dropped slots)
+    exact, weights within rtol 2e-6 and exactly 0 for dropped slots."""
+    w, L = _small_layer(**ROUTE_VARIANTS[case])
+    say(f"route variant {case} S={w.S} E={w.n_experts} k={w.top_k}")
+    x, _ = gapped_activations(w, L.router_w, L.bias)
+    opts = oracle.route_opts(w.n_group, w.topk_group, w.top_p)
+    ids_ref, w_ref, _ = oracle.route(x.numpy(), L.router_w, L.bias, w.top_k, w.rsf, opts)
+    ids, wts = qre.route(to_device(L), x.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    got = wts.cpu().numpy()
+    assert np.all(got[ids_ref < 0] == 0.0)
+    np.testing.assert_allclose(got, w_ref, rtol=2e-6, atol=1e-7)
+    if w.top_p < 1.0:
+        assert np.any(ids_ref < 0)
+
+
+def test_dispatch_skips_dropped_slots_bit_exact(qre):
+    rng = np.random.default_rng(77)
+    S, k, E = 300, 8, 256
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(S)]).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.35] = -1
+    off, srt, act, na = qre.moe_dispatch(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(ids, E)
+    n_pairs = int(ref["offsets"][E])
+    assert np.array_equal(off.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(srt.cpu().numpy()[:n_pairs], ref["sorted"][:n_pairs])
+    n = int(na.cpu()[0])
+    assert n == ref["n_active"] and np.array_equal(act.cpu().numpy()[:n], ref["active"])
+
+
 @pytest.mark.parametrize("case", ["tiny", "wide_k", "ragged_tiles", "decode_router", "glm_router_s70"])
 def test_route_parity(qre, case):
     """Small batches take the one-workgroup-per-expert router; larger ones the
@@ -197,6 +240,16 @@ SMALL_LAYERS = {
     # 33 units of I = 2048 do not fit the fused down + combine: separate launches
     "decode_many_slots": dict(name="decm", layer="decm", bits=4, hidden=256, inter=2048, n_experts=64,
                               top_k=32, S=1, has_shared=True, var_router=1.0 / 256),
+    # router variants: group-limited selection and adaptive top-p on each path
+    "rv_decode_int4": dict(name="rvd", layer="rvd", bits=4, hidden=512, inter=256, n_experts=64, top_k=8,
+                           S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, n_group=8, topk_group=4,
+                           top_p=0.6),
+    "rv_decode_many_slots": dict(name="rvm", layer="decm", bits=4, hidden=256, inter=2048, n_experts=64,
+                                 top_k=32, S=1, has_shared=True, var_router=1.0 / 256, top_p=0.5),
+    "rv_small_batch": dict(name="rvs", layer="rvs", bits=8, n_experts=32, top_k=4, S=6, has_shared=True,
+                           n_group=4, topk_group=2, top_p=0.8),
+    "rv_mfma": dict(name="rvf", layer="rvf", bits=4, hidden=512, inter=256, n_experts=16, top_k=4, S=80,
+                    has_shared=True, rsf=2.5, var_router=1.0 / 512, n_group=4, topk_group=2, top_p=0.75),
 }
 
 

@@ -89,10 +89,12 @@ def _fake_layer(capi, **over):
     d = dict(hidden=H, inter=I, n_experts=E, top_k=k, rsf=1.0, router_w=fake, router_bias=fake,
              gate=bank(E, I, H), up=bank(E, I, H), down=bank(E, H, I), has_shared=1,
              sh_gate=bank(1, I, H), sh_up=bank(1, I, H), sh_down=bank(1, H, I))
+    d.update(n_group=1, topk_group=1, top_p=1.0)
     d.update(over)
     return capi.LayerDesc(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["rsf"],
                           d["router_w"], d["router_bias"], d["gate"], d["up"], d["down"],
-                          d["has_shared"], d["sh_gate"], d["sh_up"], d["sh_down"])
+                          d["has_shared"], d["sh_gate"], d["sh_up"], d["sh_down"],
+                          d["n_group"], d["topk_group"], d["top_p"])
 
 
 def test_workspace_size_and_invalid_layers(capi):
@@ -111,6 +113,21 @@ def test_workspace_size_and_invalid_layers(capi):
         assert lib.colibri_workspace_bytes(ctypes.byref(Lb), 8) == 0, bad
     assert lib.colibri_workspace_bytes(None, 8) == 0
     assert lib.colibri_workspace_bytes(ctypes.byref(L), -1) == 0
+
+
+def test_router_variant_validation(capi):
+    lib = capi.lib()
+    ok = [dict(n_group=0), dict(n_group=4, topk_group=2), dict(n_group=8, topk_group=1, top_k=2),
+          dict(top_p=0.0), dict(top_p=0.5), dict(top_p=1.0), dict(top_p=3.0),
+          dict(n_group=4, topk_group=4, top_p=0.7)]
+    for good in ok:
+        assert lib.colibri_workspace_bytes(ctypes.byref(_fake_layer(capi, **good)), 8) > 0, good
+    # E = 16: groups must divide it, hold >= 2 experts each, and keep >= top_k experts
+    bad = [dict(n_group=3, topk_group=1), dict(n_group=16, topk_group=4), dict(n_group=4, topk_group=0),
+           dict(n_group=4, topk_group=5), dict(n_group=8, topk_group=1, top_k=3), dict(n_group=-1),
+           dict(top_p=-0.5), dict(top_p=float("nan"))]
+    for b in bad:
+        assert lib.colibri_workspace_bytes(ctypes.byref(_fake_layer(capi, **b)), 8) == 0, b
 
 
 def test_layer_forward_error_paths(capi):

@@ -280,6 +280,138 @@ def test_router_k_equals_E_is_full_normalisation():
 
 
 # ---------------------------------------------------------------------------
+# Router variants: group-limited selection and adaptive expert top-p
+# ---------------------------------------------------------------------------
+
+def _flat_router(bias):
+    """W = 0: every logit is 0 and every s is exactly 1/2, so c = 1/2 + bias."""
+    E = bias.shape[0]
+    return np.zeros(8, np.float32), np.zeros((E, 8), np.float32), bias.astype(np.float32)
+
+
+def test_router_group_stage_off_is_plain_top_k():
+    for trial in range(20):
+        x, W, b = _router_case(E=32)
+        k = int(RNG.integers(1, 9))
+        plain = oracle.route_token(x, W, b, k, 2.5)
+        for opts in (oracle.route_opts(1, 1, 1.0), oracle.route_opts(4, 4, 1.0), oracle.route_opts(8, 8, 1.0)):
+            r = oracle.route_token(x, W, b, k, 2.5, opts)
+            assert np.array_equal(r["ids"], plain["ids"])
+            assert np.array_equal(r["w"], plain["w"])
+
+
+def test_router_group_stage_hand_example():
+    # groups {0,1} {2,3} {4,5} {6,7}; c = 0.5 + bias
+    b = np.array([0.9, -0.4, 0.5, 0.45, 0.4, 0.4, -0.1, 0.0])
+    x, W, b = _flat_router(b)
+    # group scores (top-2 sums): 1.5, 1.95, 1.8, 0.9 -> groups 1 and 2 kept;
+    # expert 0 has the best single score but its group is dropped
+    r = oracle.route_token(x, W, b, 2, 2.0, oracle.route_opts(4, 2, 1.0))
+    assert r["ids"].tolist() == [2, 3]
+    assert r["w"].tolist() == [1.0, 1.0]
+    plain = oracle.route_token(x, W, b, 2, 2.0)
+    assert plain["ids"].tolist() == [0, 2]
+    # a tie between group scores keeps the lower group
+    b2 = np.array([0.3, 0.2, 0.0, 0.0, 0.3, 0.2, 0.0, 0.0])
+    x, W, b2 = _flat_router(b2)
+    r = oracle.route_token(x, W, b2, 2, 1.0, oracle.route_opts(4, 1, 1.0))
+    assert r["ids"].tolist() == [0, 1]
+
+
+def test_router_group_stage_invariants():
+    for trial in range(60):
+        E = 32
+        n_group = int(RNG.choice([2, 4, 8]))
+        gsz = E // n_group
+        topk_group = int(RNG.integers(1, n_group + 1))
+        k = int(RNG.integers(1, min(8, topk_group * gsz) + 1))
+        x, W, b = _router_case(E=E)
+        r = oracle.route_token(x, W, b, k, 2.5, oracle.route_opts(n_group, topk_group, 1.0))
+        c = r["c"]
+        # group scores from a sort (independent of the oracle's running top-2)
+        score = np.array([np.float32(np.sort(c[g * gsz:(g + 1) * gsz])[-1]) +
+                          np.float32(np.sort(c[g * gsz:(g + 1) * gsz])[-2]) for g in range(n_group)], np.float32)
+        kept = sorted(range(n_group), key=lambda g: (-float(score[g]), g))[:topk_group]
+        eligible = [e for e in range(E) if e // gsz in kept]
+        assert all(int(e) // gsz in kept for e in r["ids"])
+        # brute force over the eligible experts: e is chosen iff fewer than k precede it
+        chosen = [e for e in eligible
+                  if sum(1 for f in eligible if c[f] > c[e] or (c[f] == c[e] and f < e)) < k]
+        assert r["ids"].tolist() == sorted(chosen, key=lambda e: (-float(c[e]), e))
+        assert abs(r["w"].sum() - 2.5) <= 1e-12
+        assert r["gap"] > 0
+
+
+def test_router_top_p_limits():
+    for trial in range(20):
+        x, W, b = _router_case(E=32)
+        k = int(RNG.integers(2, 9))
+        plain = oracle.route_token(x, W, b, k, 2.5)
+        full = oracle.route_token(x, W, b, k, 2.5, oracle.route_opts(1, 1, 1.0))
+        assert np.array_equal(full["ids"], plain["ids"]) and np.array_equal(full["w"], plain["w"])
+        one = oracle.route_token(x, W, b, k, 2.5, oracle.route_opts(1, 1, 1e-6))
+        s = plain["s"][plain["ids"]]
+        top = int(np.argmax(s))  # first slot with the largest s
+        assert [j for j in range(k) if one["ids"][j] >= 0] == [top]
+        assert one["ids"][top] == plain["ids"][top] and one["w"][top] == 2.5
+        assert all(one["w"][j] == 0.0 for j in range(k) if j != top)
+
+
+def test_router_top_p_invariants():
+    for trial in range(80):
+        x, W, b = _router_case(E=32)
+        k = int(RNG.integers(2, 9))
+        p = float(RNG.uniform(0.05, 0.99))
+        plain = oracle.route_token(x, W, b, k, 2.5)
+        r = oracle.route_token(x, W, b, k, 2.5, oracle.route_opts(1, 1, p))
+        s = plain["s"][plain["ids"]].astype(np.float64)
+        kept = [j for j in range(k) if r["ids"][j] >= 0]
+        dropped = [j for j in range(k) if r["ids"][j] < 0]
+        assert kept  # at least one slot
+        # kept slots keep their experts and positions; they hold the largest s
+        assert all(r["ids"][j] == plain["ids"][j] for j in kept)
+        if dropped:
+            assert min(s[kept]) >= max(s[dropped])
+        # weights renormalised over the kept slots
+        assert abs(r["w"].sum() - 2.5) <= 1e-12
+        assert all(r["w"][j] == 0.0 for j in dropped)
+        assert np.allclose(r["w"][kept], 2.5 * s[kept] / s[kept].sum(), rtol=1e-15)
+        # the cut is the shortest prefix reaching p (fp64 shares, fp32 slack)
+        share = np.sort(s)[::-1] / s.sum()
+        m = len(kept)
+        assert share[:m].sum() >= p - 1e-6
+        if m > 1:
+            assert share[:m - 1].sum() < p + 1e-6
+
+
+def test_router_top_p_monotone_in_p():
+    x, W, b = _router_case(E=32)
+    counts = []
+    for p in np.linspace(0.01, 0.99, 40):
+        r = oracle.route_token(x, W, b, 8, 1.0, oracle.route_opts(1, 1, float(p)))
+        counts.append(int(np.sum(r["ids"] >= 0)))
+    assert counts == sorted(counts) and counts[0] == 1
+
+
+def test_dispatch_skips_dropped_slots():
+    for trial in range(20):
+        S, k, E = int(RNG.integers(1, 30)), int(RNG.integers(2, 5)), int(RNG.integers(4, 20))
+        ids = np.stack([RNG.choice(E, size=k, replace=False) for _ in range(S)]).astype(np.int32)
+        drop = RNG.random(ids.shape) < 0.3
+        ids[drop] = -1
+        r = oracle.dispatch(ids, E)
+        flat = ids.reshape(-1)
+        valid = [p for p in range(S * k) if flat[p] >= 0]
+        assert r["offsets"][E] == len(valid)
+        assert sorted(r["sorted"][:len(valid)].tolist()) == valid
+        for p in range(S * k):
+            if flat[p] < 0:
+                assert r["inv"][p] == -1
+            else:
+                assert r["sorted"][r["inv"][p]] == p
+
+
+# ---------------------------------------------------------------------------
 # Union dispatch (README batched-union item)
 # ---------------------------------------------------------------------------
 
@@ -510,6 +642,35 @@ def test_layer_traces_agree_with_expert_function():
         for j in range(w.top_k):
             f = oracle.expert_ffn(L.gate, L.up, L.down, int(r["ids"][t, j]), r["xq"][t], r["xd"][t])
             assert f["y"].tobytes() == r["y_routed"][t * w.top_k + j].tobytes()
+
+
+@pytest.mark.parametrize("n_group,topk_group,top_p", [(4, 2, 1.0), (1, 1, 0.6), (4, 3, 0.5)])
+def test_layer_with_router_variants_composes(n_group, topk_group, top_p):
+    """The layer with group-limited selection / top-p equals the shared output
+    plus the router's kept slots weighted over the expert function (fp64)."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], name="tiny_rv", has_shared=True, rsf=2.5, top_k=4,
+                     n_group=n_group, topk_group=topk_group, top_p=top_p)
+    L = synth.make_layer(w)
+    x = synth.activations(w).numpy()
+    r = oracle.layer_forward(L, x)
+    opts = oracle.route_opts(n_group, topk_group, top_p)
+    G, U, D = oracle.bank(L.gate), oracle.bank(L.up), oracle.bank(L.down)
+    SG, SU, SD = oracle.bank(L.sh_gate), oracle.bank(L.sh_up), oracle.bank(L.sh_down)
+    n_dropped = 0
+    for t in range(w.S):
+        rt = oracle.route_token(x[t], L.router_w, L.bias, w.top_k, w.rsf, opts)
+        assert np.array_equal(rt["ids"], r["ids"][t])
+        q, dq = oracle.quantize_q8_0(x[t][None, :])
+        want = oracle.expert_ffn(SG, SU, SD, 0, q[0], dq[0])["y"].astype(np.float64)
+        for j in range(w.top_k):
+            if rt["ids"][j] < 0:
+                n_dropped += 1
+                continue
+            y = oracle.expert_ffn(G, U, D, int(rt["ids"][j]), q[0], dq[0])["y"].astype(np.float64)
+            want = want + rt["w"][j] * y
+        assert np.array_equal(r["out"][t], want)
+    if top_p < 1.0:
+        assert n_dropped > 0
 
 
 # ---------------------------------------------------------------------------
