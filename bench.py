@@ -15,6 +15,13 @@ roofline object for the dominant kernel (timed with HIP events recorded by
 the library between its stages on the benchmark's stream), a CPU baseline
 (the oracle, single-threaded, on a bounded sample), and the S = 512 prefill
 figure of the same layer.
+
+    python bench.py --tier [--tier-fractions 1,0.5,0.25]
+
+instead runs the layer with its routed experts in pinned host memory behind
+an HBM slot bank (colibri_tier_forward) and prints decode tokens/s, expert
+hit rate and host-to-device traffic per resident fraction, for uniform and
+for Zipf-skewed routing.
 """
 
 import argparse
@@ -40,6 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--tier", action="store_true",
+                    help="tiered-residency sweep instead of the resident layer: routed experts in "
+                         "pinned host memory behind an HBM slot bank (prints its own JSON line)")
+    ap.add_argument("--tier-fractions", default="1,0.75,0.5,0.25,0.125",
+                    help="resident fractions n_slots / n_experts of the sweep")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one elementwise fp32 copy of this many MiB (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -235,6 +247,87 @@ def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True)
     return res
 
 
+PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction after 128b/130b encoding
+
+
+def h2d_probe(torch, nbytes, reps=3):
+    """Copy-engine rate of pinned host -> HBM transfers of nbytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    rate = reps * nbytes / (time.perf_counter() - t0) / 1e9
+    del src, dst
+    return rate
+
+
+def run_tier(qre, synth, torch, w, fractions, steps):
+    """Decode through colibri_tier_forward at several resident fractions, for
+    uniform routing (the workload's normal bias) and for Zipf-skewed expert
+    popularity (the skewed workload's bias recipe on the same weights)."""
+    import numpy as np
+    base = synth.make_layer(w, device="cuda")
+    E = w.n_experts
+
+    def pinned(t):
+        p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        p.copy_(t)
+        return p
+
+    def host_bank(b):
+        return qre.QBank(pinned(b.storage), pinned(b.scale_storage), b.bits)
+
+    def dev_bank(b):
+        return qre.QBank(b.storage, b.scale_storage, b.bits)
+    routed = [host_bank(b) for b in (base.gate, base.up, base.down)]
+    shared = [dev_bank(b) for b in (base.sh_gate, base.sh_up, base.sh_down)] if w.has_shared else None
+    biases = {"uniform": base.bias,
+              "zipf": synth.router_bias(synth.scaled(w, bias_kind="zipf")).to("cuda")}
+    for b in (base.gate, base.up, base.down):
+        b.storage = b.scale_storage = None
+        b.data, b.scale = [], []
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    probe = h2d_probe(torch, 16 * expert_bytes(w))
+    xs = [synth.activations(w, tag=f"/tier{i}").cuda() for i in range(512)]
+    out = torch.empty_like(xs[0])
+    sweep = []
+    for kind, bias in biases.items():
+        layer = qre.MoELayer(w.hidden, w.inter, E, w.top_k, w.rsf, base.router_w, bias, *routed, shared)
+        for f in fractions:
+            n_slots = max(1, min(E, int(round(f * E))))
+            tier = qre.TieredLayer(layer, n_slots)
+            ws = tier.workspace(w.S)
+            if n_slots == E:
+                tier.pin(list(range(E)))  # everything resident: no misses at all
+            warm = max(64, 4 * n_slots // max(1, w.top_k))
+            for i in range(warm):
+                tier.forward(xs[i % len(xs)], out, ws)
+            torch.cuda.synchronize()
+            s0 = tier.stats()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                tier.forward(xs[(warm + i) % len(xs)], out, ws)
+            torch.cuda.synchronize()
+            t = time.perf_counter() - t0
+            s1 = tier.stats()
+            hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+            moved = misses * expert_bytes(w)
+            sweep.append({"routing": kind, "resident_fraction": n_slots / E, "n_slots": n_slots,
+                          "tokens_per_s": steps * w.S / t, "ms_per_step": 1000.0 * t / steps,
+                          "expert_hit_rate": hits / max(1, hits + misses),
+                          "expert_loads_per_step": misses / steps,
+                          "passes_per_step": (s1["passes"] - s0["passes"]) / steps,
+                          "h2d_GBps": moved / t / 1e9})
+            tier.close()
+            del ws
+    return {"h2d_probe_GBps": probe, "sweep": sweep}
+
+
 def cpu_baseline(synth, w, n_tokens):
     """The oracle, as it stands, on n_tokens tokens of the same workload."""
     import oracle
@@ -275,6 +368,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.workload]
+    if args.tier:
+        fr = [float(v) for v in args.tier_fractions.split(",")]
+        steps = args.steps or 300
+        r = run_tier(qre, synth, torch, w, fr, steps)
+        print(json.dumps({
+            "metric": "tiered decode tokens/sec per MoE layer vs HBM-resident expert fraction",
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "higher_is_better": True, "dtype": "int8",
+            "data": "synthetic (seeded SplitMix64 weights and activations; no checkpoint)",
+            "config": {"workload": f"{w.name}: MoE layer H={w.hidden} I={w.inter} E={w.n_experts} "
+                                   f"top-{w.top_k} int{w.bits}, routed experts in pinned host memory, "
+                                   f"S={w.S}", "expert_bytes": expert_bytes(w)},
+            "roofline": {"bound": "pcie", "unit": "GB/s", "peak": PCIE_PEAK_GBS,
+                         "copy_engine_probe": r["h2d_probe_GBps"]},
+            "sweep": r["sweep"]}), flush=True)
+        return
     steps = args.steps or (2000 if w.S <= 8 else 50)
     res = run_workload(qre, synth, torch, w, steps, args.warmup, args.copies)
     ms = res["gpu_ms"] / steps

@@ -28,9 +28,12 @@
  *   - Every pointer argument except the descriptor structs is DEVICE memory
  *     owned by the caller.  The library allocates nothing, frees nothing and
  *     keeps no pointer after a call returns.  Descriptor structs are host
- *     memory read during the call only.
+ *     memory read during the call only.  (The tiered-residency objects at the
+ *     end of this header are the exception; their section says what they
+ *     own, keep and wait for.)
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
- *     default stream).  No call synchronises the host or copies to the host.
+ *     default stream).  No call outside the tiered-residency section
+ *     synchronises the host or copies to the host.
  *   - Scratch memory is the caller's workspace `ws` of `ws_bytes` bytes,
  *     256-byte aligned, sized by colibri_workspace_bytes().  Concurrent calls
  *     need distinct workspaces; workspace contents need no initialisation.
@@ -229,6 +232,149 @@ int colibri_moe_layer_forward(const coli_moe_layer* L, const float* x, int32_t S
 int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, int32_t S, float* out,
                                      void* ws, size_t ws_bytes, coli_stream_t stream,
                                      void* const* stage_events);
+
+/* ===========================================================================
+ * Tiered expert residency ([README] section "思路" (idea): the routed experts
+ * live in a slow tier and stream in on demand through a per-layer LRU cache
+ * with an optional pinned hot store; its learned-cache paragraph: the experts
+ * routed most often are pinned; its deferred cold-expert pipeline paragraph:
+ * resident experts compute while the missing ones load in the background and
+ * their results join before the layer ends).  On one MI355X the fast tier is
+ * a bank of n_slots expert slots in HBM and the slow tier is pinned host
+ * memory, read over PCIe by the copy engines.
+ *
+ * Two objects:
+ *   coli_expert_cache  the host-side slot cache and planner.  No GPU calls:
+ *                      it runs without a GPU and plans every tier forward.
+ *   coli_tier          one layer whose routed experts live in the slow tier,
+ *                      with its own cache, slot bank, copy stream and events.
+ * Unlike the calls above, these objects own host memory and (coli_tier) HIP
+ * objects, and colibri_tier_forward waits for its stream once per call to
+ * read the routed ids on the host.
+ * ========================================================================= */
+
+typedef struct coli_expert_cache coli_expert_cache;
+
+/* Pair codes written by colibri_cache_plan: pass << COLI_PLAN_SLOT_BITS | slot. */
+#define COLI_PLAN_SLOT_BITS 11
+
+/* One expert load: `expert` into `slot`, needed by pass `pass`.  When
+ * after >= 0 the load may start only once pass `after` of the same plan has
+ * finished (that pass still reads the slot's previous occupant). */
+typedef struct coli_cache_load {
+    int32_t expert, slot, pass, after;
+} coli_cache_load;
+
+typedef struct coli_cache_plan {
+    int32_t n_pass; /* passes; pass 0 computes the experts found resident */
+    int32_t n_load; /* loads written (one per miss) */
+    int32_t n_hit;  /* distinct routed experts found resident */
+    int32_t n_miss; /* distinct routed experts that have to be loaded */
+} coli_cache_plan;
+
+typedef struct coli_cache_stats {
+    uint64_t plans;     /* successful colibri_cache_plan calls */
+    uint64_t pairs;     /* routed pairs planned (dropped slots excluded) */
+    uint64_t hits;      /* per plan: distinct experts found resident, summed */
+    uint64_t misses;    /* per plan: distinct experts loaded, summed */
+    uint64_t pin_loads; /* loads made by colibri_cache_pin */
+    uint64_t passes;    /* summed over plans */
+    int32_t resident;   /* slots holding an expert now */
+    int32_t pinned;     /* slots pinned now */
+} coli_cache_stats;
+
+/* A cache of n_slots empty slots for n_experts experts (1 <= n_slots <=
+ * n_experts <= COLI_MAX_EXPERTS). */
+int colibri_cache_create(int32_t n_experts, int32_t n_slots, coli_expert_cache** out);
+void colibri_cache_destroy(coli_expert_cache* c);
+
+/*
+ * Pins n distinct experts in [0, n_experts) for good (the hot store): a
+ * resident one keeps its slot; any other takes a victim slot (empty first,
+ * then least recently used, ties to the lower slot) and is listed in loads
+ * (host, n entries; pass 0, after -1), *n_load of them.  The pinned set may
+ * hold at most n_slots - 1 experts unless it holds all of them (n_slots ==
+ * n_experts), so that a miss always finds a slot: COLI_E_UNSUPPORTED
+ * otherwise.  Invalid or refused calls change nothing.
+ */
+int colibri_cache_pin(coli_expert_cache* c, const int32_t* experts, int32_t n,
+                      coli_cache_load* loads, int32_t* n_load);
+
+/* Unpins every expert; they stay resident. */
+void colibri_cache_unpin(coli_expert_cache* c);
+
+/*
+ * Plans one batch.  ids [P] (host) are routed expert ids, -1 for a dropped
+ * slot.  The distinct experts are taken in order of first appearance; those
+ * resident (hits) run in pass 0 from their slots.  Misses take slots from a
+ * ring: first the slots neither pinned nor holding a hit (empty first, then
+ * least recently used, ties to the lower slot), then the unpinned hit slots
+ * (reusable after pass 0).  With R ring slots, misses that fit (n_miss <= R)
+ * all run in pass 1; otherwise they run in chunks of c = max(1, R/2) per
+ * pass, miss i taking ring slot i mod R, so that (for R >= 2) one chunk's
+ * loads overlap the previous chunk's compute.  Every expert
+ * of the batch becomes most recently used; usage counts grow by its pairs.
+ * Host outputs: pair_code [P] (pass << COLI_PLAN_SLOT_BITS | slot, -1 for a
+ * dropped slot), loads [min(P, n_experts)] in pass order, pass_pairs
+ * [min(P, n_experts) + 1] (pairs per pass), *plan.  An id >= n_experts is
+ * COLI_E_INVAL and changes nothing.
+ */
+int colibri_cache_plan(coli_expert_cache* c, const int32_t* ids, int32_t P, int32_t* pair_code,
+                       coli_cache_load* loads, int32_t* pass_pairs, coli_cache_plan* plan);
+
+int colibri_cache_stats(const coli_expert_cache* c, coli_cache_stats* st);
+
+/* Host copies of the state: slot_of [n_experts] (slot or -1) and usage
+ * [n_experts] (routed pairs so far); either may be NULL. */
+int colibri_cache_state(const coli_expert_cache* c, int32_t* slot_of, uint64_t* usage);
+
+typedef struct coli_tier coli_tier;
+
+/* Device bytes of a slot bank of n_slots experts of layer L: gate, up and
+ * down codes and scales, each region 256-byte aligned (0 if L is invalid or
+ * n_slots is outside [1, n_experts]). */
+size_t colibri_tier_slot_bytes(const coli_moe_layer* L, int32_t n_slots);
+
+/*
+ * A tiered layer on the current device.  L is a complete layer descriptor
+ * whose routed banks (gate, up, down with n_mat = n_experts) are the slow
+ * tier: pinned host memory (hipHostMalloc) or device memory; pageable host
+ * memory is COLI_E_UNSUPPORTED.  Router and shared expert are device memory
+ * as for colibri_moe_layer_forward.  slot_mem is device memory of slot_bytes
+ * >= colibri_tier_slot_bytes(L, n_slots) bytes, 256-byte aligned.  The tier
+ * keeps L's pointers and slot_mem until colibri_tier_destroy, and creates a
+ * non-blocking copy stream (default priority) and events.
+ */
+int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem, size_t slot_bytes,
+                        coli_tier** out);
+
+/* Waits for the tier's copy stream, then frees its host state and HIP objects. */
+void colibri_tier_destroy(coli_tier* t);
+
+/* The tier's cache, for colibri_cache_stats / colibri_cache_state only. */
+const coli_expert_cache* colibri_tier_cache(const coli_tier* t);
+
+/* Pins experts (colibri_cache_pin) and enqueues their loads on `stream`. */
+int colibri_tier_pin(coli_tier* t, const int32_t* experts, int32_t n, coli_stream_t stream);
+
+/* Workspace bytes of colibri_tier_forward for up to S tokens (0 if invalid). */
+size_t colibri_tier_workspace_bytes(const coli_tier* t, int32_t S);
+
+/*
+ * colibri_moe_layer_forward with the routed experts taken from the slot
+ * bank.  Routes on `stream`, copies the ids to the host and waits for
+ * `stream`; plans the batch (colibri_cache_plan); computes pass 0 (the
+ * resident experts and the shared expert) on `stream` while the copy stream
+ * loads the misses; every later pass waits for its own loads; one combine
+ * ends the call.  The output is bit-identical to colibri_moe_layer_forward
+ * on the same weights.  Calls on one tier must be ordered on one stream and
+ * made with the tier's device current; pinned host staging is allocated
+ * the first time a call has more pairs than every call before it.  After a
+ * HIP error the cache forgets every slot (pins included) and the call
+ * returns COLI_E_HIP.
+ */
+int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, void* ws,
+                         size_t ws_bytes, coli_stream_t stream);
 
 /* Static text for a status code. */
 const char* colibri_status_string(int status);

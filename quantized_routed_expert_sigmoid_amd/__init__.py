@@ -82,6 +82,26 @@ def lib():
         L.colibri_moe_layer_forward_staged.restype = ctypes.c_int
         L.colibri_moe_layer_forward_staged.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp,
                                                        _vp]
+        for name, res, args in [
+                ("colibri_cache_create", ctypes.c_int, [_i32, _i32, ctypes.POINTER(_vp)]),
+                ("colibri_cache_destroy", None, [_vp]),
+                ("colibri_cache_pin", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
+                ("colibri_cache_unpin", None, [_vp]),
+                ("colibri_cache_plan", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+                ("colibri_cache_stats", ctypes.c_int, [_vp, _vp]),
+                ("colibri_cache_state", ctypes.c_int, [_vp, _vp, _vp]),
+                ("colibri_tier_slot_bytes", ctypes.c_size_t, [_vp, _i32]),
+                ("colibri_tier_create", ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t,
+                                                       ctypes.POINTER(_vp)]),
+                ("colibri_tier_destroy", None, [_vp]),
+                ("colibri_tier_cache", _vp, [_vp]),
+                ("colibri_tier_pin", ctypes.c_int, [_vp, _vp, _i32, _vp]),
+                ("colibri_tier_workspace_bytes", ctypes.c_size_t, [_vp, _i32]),
+                ("colibri_tier_forward", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t,
+                                                        _vp])]:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
         _lib = L
     return _lib
 
@@ -105,6 +125,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+def _bank_ptr(t: torch.Tensor):
+    """Device memory, or pinned host memory (the slow tier of a tiered layer)."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("device or pinned host tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -121,8 +150,8 @@ class QBank:
 
     def desc(self) -> QBankDesc:
         n_mat, rows, rb = self.data.shape
-        return QBankDesc(_ptr(self.data), _ptr(self.scale), n_mat, rows, rb * 8 // self.qtype,
-                         self.qtype)
+        return QBankDesc(_bank_ptr(self.data), _bank_ptr(self.scale), n_mat, rows,
+                         rb * 8 // self.qtype, self.qtype)
 
 
 class MoELayer:
@@ -220,3 +249,159 @@ def moe_layer_forward_staged(layer: MoELayer, x: torch.Tensor, out: torch.Tensor
                                                   _ptr(out), _ptr(ws), ws.numel(), _stream(), arr),
            "colibri_moe_layer_forward_staged")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Tiered expert residency: host-side slot cache and the tiered layer.
+
+_u64 = ctypes.c_uint64
+PLAN_SLOT_BITS = 11
+
+
+class CacheLoad(ctypes.Structure):
+    """coli_cache_load"""
+    _fields_ = [("expert", _i32), ("slot", _i32), ("pass_", _i32), ("after", _i32)]
+
+
+class CachePlan(ctypes.Structure):
+    """coli_cache_plan"""
+    _fields_ = [("n_pass", _i32), ("n_load", _i32), ("n_hit", _i32), ("n_miss", _i32)]
+
+
+class CacheStats(ctypes.Structure):
+    """coli_cache_stats"""
+    _fields_ = [("plans", _u64), ("pairs", _u64), ("hits", _u64), ("misses", _u64),
+                ("pin_loads", _u64), ("passes", _u64), ("resident", _i32), ("pinned", _i32)]
+
+
+def _i32_array(values):
+    a = (_i32 * max(len(values), 1))()
+    for i, v in enumerate(values):
+        a[i] = int(v)
+    return a
+
+
+def _cache_stats(handle) -> dict:
+    st = CacheStats()
+    _check(lib().colibri_cache_stats(handle, ctypes.byref(st)), "colibri_cache_stats")
+    return {f: getattr(st, f) for f, _ in CacheStats._fields_}
+
+
+def _cache_state(handle, n_experts: int):
+    slot_of = (_i32 * n_experts)()
+    usage = (_u64 * n_experts)()
+    _check(lib().colibri_cache_state(handle, slot_of, usage), "colibri_cache_state")
+    return list(slot_of), list(usage)
+
+
+class ExpertCache:
+    """The host-side slot cache and planner (colibri_cache_*); needs no GPU."""
+
+    def __init__(self, n_experts: int, n_slots: int):
+        h = _vp()
+        _check(lib().colibri_cache_create(n_experts, n_slots, ctypes.byref(h)), "colibri_cache_create")
+        self._h, self.n_experts, self.n_slots = h, n_experts, n_slots
+
+    def close(self):
+        if self._h:
+            lib().colibri_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pin(self, experts: Sequence[int]):
+        """-> [(expert, slot)] loads the pins need."""
+        arr = _i32_array(experts)
+        loads = (CacheLoad * max(len(experts), 1))()
+        n = _i32(0)
+        _check(lib().colibri_cache_pin(self._h, arr, len(experts), loads, ctypes.byref(n)),
+               "colibri_cache_pin")
+        return [(loads[i].expert, loads[i].slot) for i in range(n.value)]
+
+    def unpin(self):
+        lib().colibri_cache_unpin(self._h)
+
+    def plan(self, ids: Sequence[int]) -> dict:
+        """ids: routed expert ids (-1: dropped slot) -> codes, loads (expert,
+        slot, pass, after), pass_pairs and the counts."""
+        P = len(ids)
+        m = min(P, self.n_experts)
+        arr = _i32_array(ids)
+        codes = (_i32 * max(P, 1))()
+        loads = (CacheLoad * max(m, 1))()
+        pp = (_i32 * (m + 1))()
+        plan = CachePlan()
+        _check(lib().colibri_cache_plan(self._h, arr, P, codes, loads, pp, ctypes.byref(plan)),
+               "colibri_cache_plan")
+        return {"codes": list(codes)[:P],
+                "loads": [(loads[i].expert, loads[i].slot, loads[i].pass_, loads[i].after)
+                          for i in range(plan.n_load)],
+                "pass_pairs": list(pp)[:plan.n_pass], "n_pass": plan.n_pass, "n_hit": plan.n_hit,
+                "n_miss": plan.n_miss}
+
+    def stats(self) -> dict:
+        return _cache_stats(self._h)
+
+    def state(self):
+        """-> (slot_of [E], usage [E])."""
+        return _cache_state(self._h, self.n_experts)
+
+
+class TieredLayer:
+    """A layer whose routed experts live in pinned host memory (layer's
+    gate/up/down QBanks on pinned CPU tensors) behind an HBM slot bank of
+    n_slots experts (colibri_tier_*)."""
+
+    def __init__(self, layer: MoELayer, n_slots: int):
+        self.layer, self.n_slots = layer, n_slots
+        nb = lib().colibri_tier_slot_bytes(ctypes.byref(layer.desc), n_slots)
+        if nb == 0:
+            raise ColibriError(COLI_E_INVAL, "colibri_tier_slot_bytes")
+        self.slot_mem = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        h = _vp()
+        _check(lib().colibri_tier_create(ctypes.byref(layer.desc), n_slots, _ptr(self.slot_mem), nb,
+                                         ctypes.byref(h)), "colibri_tier_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().colibri_tier_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pin(self, experts: Sequence[int]):
+        arr = _i32_array(experts)
+        _check(lib().colibri_tier_pin(self._h, arr, len(experts), _stream()), "colibri_tier_pin")
+
+    def workspace_bytes(self, S: int) -> int:
+        n = lib().colibri_tier_workspace_bytes(self._h, S)
+        if n == 0:
+            raise ColibriError(COLI_E_INVAL, "colibri_tier_workspace_bytes")
+        return n
+
+    def workspace(self, S: int) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(S), dtype=torch.uint8, device="cuda")
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+        S = x.shape[0]
+        out = torch.empty_like(x) if out is None else out
+        ws = self.workspace(S) if ws is None else ws
+        _check(lib().colibri_tier_forward(self._h, _ptr(x), S, _ptr(out), _ptr(ws), ws.numel(),
+                                          _stream()), "colibri_tier_forward")
+        return out
+
+    def stats(self) -> dict:
+        return _cache_stats(lib().colibri_tier_cache(self._h))
+
+    def state(self):
+        return _cache_state(lib().colibri_tier_cache(self._h), self.layer.n_experts)

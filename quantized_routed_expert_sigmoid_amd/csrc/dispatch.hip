@@ -97,12 +97,33 @@ struct DispatchShared {
     uint64_t tmp[kDispWaves + 1];
 };
 
-/* The dispatch, run by all 1024 threads of a workgroup.  `ids` may point to
- * global memory or to LDS. */
-__device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int32_t k, int32_t E,
+/* Routed ids of the pairs, read from global memory or LDS. */
+struct PlainIds {
+    const int32_t* ids;
+    __device__ __forceinline__ int32_t operator()(int32_t p) const { return ids[p]; }
+};
+
+/* The pairs of one pass of a tiered forward: codes hold pass << kPassSlotBits
+ * | slot, or -1; pairs of other passes read as dropped. */
+struct PassIds {
+    const int32_t* codes;
+    int32_t pass;
+    __device__ __forceinline__ int32_t operator()(int32_t p) const
+    {
+        const int32_t v = codes[p];
+        return (v >= 0 && (v >> kPassSlotBits) == pass) ? (v & ((1 << kPassSlotBits) - 1)) : -1;
+    }
+};
+
+/* The dispatch, run by all 1024 threads of a workgroup.  Kept pairs get
+ * inv = inv_base + sorted position; dropped pairs get inv = -1 when
+ * mark_dropped is set and are left untouched otherwise. */
+template <typename Ids>
+__device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t k, int32_t E,
                                               int32_t* offsets, int32_t* sorted, int32_t* inv,
                                               int32_t* active, int32_t* n_active, const UnitLists* ul,
-                                              DispatchShared& sh)
+                                              DispatchShared& sh, int32_t inv_base = 0,
+                                              bool mark_dropped = true)
 {
     int32_t* cnt = sh.cnt;
     int32_t* base = sh.base;
@@ -119,9 +140,11 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
     /* a negative id is a dropped slot (no pair); ids past E - 1 violate the
      * documented precondition and are clamped so that no access leaves its
      * buffer */
-    for (int32_t p = tid; p < P; p += kDispThreads)
-        if (ids[p] >= 0)
-            atomicAdd(&cnt[min(ids[p], E - 1)], 1);
+    for (int32_t p = tid; p < P; p += kDispThreads) {
+        const int32_t id = ids(p);
+        if (id >= 0)
+            atomicAdd(&cnt[min(id, E - 1)], 1);
+    }
     __syncthreads();
 
     /* offsets, active list and unit lists: one expert per thread, one scan of
@@ -163,10 +186,10 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int32_t r0 = 0; r0 < P; r0 += kDispThreads) {
         const int32_t p = r0 + tid;
-        const int32_t id = p < P ? ids[p] : -1;
+        const int32_t id = p < P ? ids(p) : -1;
         const bool valid = id >= 0;
         const int32_t ex = valid ? min(id, E - 1) : 0;
-        if (p < P && !valid && inv)
+        if (p < P && !valid && inv && mark_dropped)
             inv[p] = -1;
         uint64_t m = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
@@ -183,7 +206,7 @@ __device__ __forceinline__ void dispatch_body(const int32_t* ids, int32_t S, int
                 pos += wcnt[w][ex];
             sorted[pos] = p;
             if (inv)
-                inv[p] = pos;
+                inv[p] = inv_base + pos;
         }
         __syncthreads();
         for (int ee = tid; ee < E; ee += kDispThreads) {
@@ -204,7 +227,8 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     int32_t* __restrict__ n_active, UnitLists ul, int32_t has_units)
 {
     __shared__ DispatchShared sh;
-    dispatch_body(ids, S, k, E, offsets, sorted, inv, active, n_active, has_units ? &ul : nullptr, sh);
+    dispatch_body(PlainIds{ids}, S, k, E, offsets, sorted, inv, active, n_active,
+                  has_units ? &ul : nullptr, sh);
 }
 
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, int32_t* offsets,
@@ -214,6 +238,27 @@ hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, 
     UnitLists none = {};
     hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kDispThreads), 0, st, ids, S, k, E, offsets,
                        sorted, inv, active, n_active, ul ? *ul : none, ul ? 1 : 0);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kDispThreads) void dispatch_pass_kernel(
+    const int32_t* __restrict__ codes, int32_t pass, int32_t inv_base, int32_t S, int32_t k,
+    int32_t n_slots, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ inv, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    UnitLists ul)
+{
+    __shared__ DispatchShared sh;
+    dispatch_body(PassIds{codes, pass}, S, k, n_slots, offsets, sorted, inv, active, n_active, &ul, sh,
+                  inv_base, pass == 0);
+}
+
+hipError_t launch_dispatch_pass(const int32_t* codes, int32_t pass, int32_t inv_base, int32_t S,
+                                int32_t k, int32_t n_slots, int32_t* offsets, int32_t* sorted,
+                                int32_t* inv, int32_t* active, int32_t* n_active, const UnitLists& ul,
+                                hipStream_t st)
+{
+    hipLaunchKernelGGL(dispatch_pass_kernel, dim3(1), dim3(kDispThreads), 0, st, codes, pass, inv_base,
+                       S, k, n_slots, offsets, sorted, inv, active, n_active, ul);
     return hipGetLastError();
 }
 
@@ -233,7 +278,7 @@ __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
         select_token(logits + (int64_t)wv * E, bias, E, k, rsf, ids + (int64_t)wv * k,
                      weights + (int64_t)wv * k, sel_s[wv], sel_ids + wv * k, 1, 0, opt);
     __syncthreads();
-    dispatch_body(sel_ids, S, k, E, offsets, sorted, inv, active, n_active, &ul, sh);
+    dispatch_body(PlainIds{sel_ids}, S, k, E, offsets, sorted, inv, active, n_active, &ul, sh);
 }
 
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,

@@ -28,6 +28,11 @@ constexpr int32_t kPairLimit = 1 << 20;
  * (a workgroup per router row; selection and dispatch in one workgroup). */
 constexpr int kSmallS = 8;
 
+/* Pair codes of a tiered forward: pass << kPassSlotBits | slot (slots below
+ * 2^kPassSlotBits, which the expert limit of 1024 keeps); the same width as
+ * COLI_PLAN_SLOT_BITS of the C ABI. */
+constexpr int kPassSlotBits = 11;
+
 /* Most expert groups of group-limited selection. */
 constexpr int kMaxGroups = 64;
 
@@ -178,6 +183,15 @@ hipError_t launch_select_dispatch_small(const float* logits, const float* bias, 
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E,
                            int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* active,
                            int32_t* n_active, const UnitLists* ul, hipStream_t st);
+
+/* Union dispatch of one pass of a tiered forward over n_slots slot matrices:
+ * the pairs whose code names `pass` (see kPassSlotBits); they get inv =
+ * inv_base + sorted position.  Pass 0 also sets inv = -1 for every other
+ * pair; later passes leave those entries alone. */
+hipError_t launch_dispatch_pass(const int32_t* codes, int32_t pass, int32_t inv_base, int32_t S,
+                                int32_t k, int32_t n_slots, int32_t* offsets, int32_t* sorted,
+                                int32_t* inv, int32_t* active, int32_t* n_active, const UnitLists& ul,
+                                hipStream_t st);
 
 /* Unit lists from expert offsets (for a caller-provided dispatch), bounded
  * by ul.max_units / ul.max_munits. */

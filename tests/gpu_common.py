@@ -64,3 +64,26 @@ def assert_close_rms(gpu_out, ref_out, what=""):
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     assert err <= REL_TOL * rms, f"{what}: max|diff| {err:.3e} > {REL_TOL} * rms {rms:.3e}"
     return err / rms if rms > 0 else 0.0
+
+
+def pinned_copy(t: torch.Tensor) -> torch.Tensor:
+    """A copy of t in newly allocated pinned host memory."""
+    p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    p.copy_(t)
+    return p
+
+
+def to_slow_tier(L: synth.Layer, dev, where="host"):
+    """The layer with its routed banks in pinned host memory (where="host")
+    or in device memory (where="device"); router and shared expert are dev's
+    device tensors."""
+    import quantized_routed_expert_sigmoid_amd as qre
+
+    def qb(b):
+        if where == "device":
+            return qre.QBank(b.storage.cuda().contiguous(), b.scale_storage.cuda().contiguous(), b.bits)
+        return qre.QBank(pinned_copy(b.storage.contiguous()), pinned_copy(b.scale_storage.contiguous()),
+                         b.bits)
+    w = L.w
+    return qre.MoELayer(w.hidden, w.inter, w.n_experts, w.top_k, w.rsf, dev.router_w, dev.router_bias,
+                        qb(L.gate), qb(L.up), qb(L.down), dev.shared, w.n_group, w.topk_group, w.top_p)

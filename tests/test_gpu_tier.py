@@ -1,0 +1,162 @@
+"""Tiered expert residency on the GPU (colibri_tier_* through the C ABI):
+the routed experts live in pinned host memory behind a slot bank of a few
+experts in HBM.  Every tiered forward must equal the resident forward on the
+same weights bit for bit -- over sequences of batches that hit, miss, evict
+and reload slots, with chunked passes when a batch needs more experts than
+there are slots, with pinned experts, top-p-dropped slots and a shared
+expert at another width -- and one case is checked against the oracle
+directly."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_common import assert_close_rms, gapped_activations, say, to_device, to_slow_tier
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qre():
+    import quantized_routed_expert_sigmoid_amd as m
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    m.lib()
+    return m
+
+
+TIER_CASES = {
+    # one token: the resident forward runs the fused decode kernels
+    "decode_int4": dict(name="tdec4", layer="dec4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
+                        S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
+    "long_int4_shared": dict(name="tl4", layer="tiny_int4", bits=4, S=37, has_shared=True),
+    "mfma_int4": dict(name="tmf4", layer="mf4", bits=4, hidden=512, inter=256, n_experts=8, top_k=2, S=64,
+                      has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
+    "small_topp_groups": dict(name="trvs", layer="rvs", bits=8, n_experts=32, top_k=4, S=6,
+                              has_shared=True, n_group=4, topk_group=2, top_p=0.8),
+    "many_slots_int2": dict(name="tm2", layer="tm2", bits=2, hidden=256, inter=96, n_experts=64, top_k=16,
+                            S=3, has_shared=False, var_router=1.0 / 256),
+}
+SLOTS = {"decode_int4": [1, 8, 64], "long_int4_shared": [1, 3, 16], "mfma_int4": [1, 3, 8],
+         "small_topp_groups": [2, 9], "many_slots_int2": [2, 17, 40]}
+# batch order with repeats, so that later batches hit what earlier ones loaded
+ORDER = [0, 1, 0, 2, 1, 0, 3]
+
+
+def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+
+
+def _run_sequence(qre, w, dev, tier, order=ORDER, S=None):
+    S = w.S if S is None else S
+    xs = {}
+    misses = 0
+    for b in order:
+        if b not in xs:
+            xs[b] = synth.activations(w, S, tag=f"tier{b}").cuda()
+        before = tier.stats()["misses"]
+        ref = qre.moe_layer_forward(dev, xs[b])
+        got = tier.forward(xs[b])
+        torch.cuda.synchronize()
+        assert bits_equal(got, ref), f"batch {b}: tiered output differs from the resident forward"
+        misses += tier.stats()["misses"] - before
+    return misses
+
+
+@pytest.mark.parametrize("case,n_slots", [(c, n) for c in sorted(TIER_CASES) for n in SLOTS[c]])
+def test_tier_matches_resident_bitwise(qre, case, n_slots):
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES[case])
+    say(f"tier case={case} slots={n_slots} E={w.n_experts} k={w.top_k} S={w.S} bits={w.bits}")
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    tier = qre.TieredLayer(to_slow_tier(L, dev), n_slots)
+    misses = _run_sequence(qre, w, dev, tier)
+    st = tier.stats()
+    say(f"  plans={st['plans']} hits={st['hits']} misses={st['misses']} passes={st['passes']}")
+    assert st["plans"] == len(ORDER) and misses == st["misses"] > 0
+    assert st["resident"] == min(n_slots, st["misses"])
+    if n_slots == 1 and w.S * w.top_k > 1:
+        assert st["passes"] > 2 * st["plans"]  # chunked: one miss per pass
+    slot_of, usage = tier.state()
+    assert sum(usage) == st["pairs"]
+    tier.close()
+
+
+def test_tier_against_oracle(qre):
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["long_int4_shared"])
+    L = synth.make_layer(w)
+    x, _ = gapped_activations(w, L.router_w, L.bias)
+    ref = oracle.layer_forward(L, x.numpy())
+    dev = to_device(L)
+    tier = qre.TieredLayer(to_slow_tier(L, dev), 3)
+    out = tier.forward(x.cuda())
+    torch.cuda.synchronize()
+    assert_close_rms(out.cpu().numpy(), ref["out"], "tier vs oracle")
+
+
+def test_tier_pinned_hot_set(qre):
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["decode_int4"])
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    tier = qre.TieredLayer(to_slow_tier(L, dev), 10)
+    hot = [3, 17, 40, 63, 5, 22]
+    tier.pin(hot)
+    assert tier.stats()["pinned"] == len(hot) and tier.stats()["pin_loads"] == len(hot)
+    _run_sequence(qre, w, dev, tier, order=[0, 1, 2, 3, 4, 0, 5, 1])
+    slot_of, _ = tier.state()
+    assert all(slot_of[e] >= 0 for e in hot)
+    with pytest.raises(qre.ColibriError):
+        tier.pin([0, 1, 2, 4])  # 10 pins would leave no slot for misses
+    tier.close()
+
+
+def test_tier_device_slow_tier_and_other_width_shared(qre):
+    """The slow tier may be device memory; a shared expert at another width
+    runs in launches of its own in pass 0."""
+    w4 = synth.scaled(synth.WORKLOADS["tiny"], name="tmix4", layer="mix4", bits=4, hidden=512, inter=256,
+                      n_experts=32, top_k=4, S=3, has_shared=True, var_router=1.0 / 512)
+    w8 = synth.scaled(w4, layer="mix8", bits=8)
+    L4, L8 = synth.make_layer(w4), synth.make_layer(w8)
+    L = synth.Layer(w4, L4.router_w, L4.bias, L4.gate, L4.up, L4.down, L8.sh_gate, L8.sh_up, L8.sh_down)
+    dev = to_device(L)
+    for where, n in [("device", 5), ("host", 2)]:
+        tier = qre.TieredLayer(to_slow_tier(L, dev, where), n)
+        _run_sequence(qre, w4, dev, tier, order=[0, 1, 0, 2])
+        for S in (1, 20):
+            _run_sequence(qre, w4, dev, tier, order=[5, 6], S=S)
+        tier.close()
+
+
+def test_tier_argument_errors(qre):
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["long_int4_shared"])
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    slow = to_slow_tier(L, dev)
+    lib = qre.lib()
+    assert lib.colibri_tier_slot_bytes(ctypes.byref(slow.desc), 0) == 0
+    assert lib.colibri_tier_slot_bytes(ctypes.byref(slow.desc), w.n_experts + 1) == 0
+    nb = lib.colibri_tier_slot_bytes(ctypes.byref(slow.desc), 4)
+    mem = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    h = ctypes.c_void_p()
+    assert lib.colibri_tier_create(ctypes.byref(slow.desc), 4, mem.data_ptr(), nb - 1,
+                                   ctypes.byref(h)) == qre.COLI_E_WORKSPACE
+    # a routed bank in pageable host memory cannot feed the copy engines
+    pageable = np.zeros(L.gate.storage.numel(), dtype=np.uint8)
+    desc = qre.LayerDesc.from_buffer_copy(slow.desc)
+    desc.gate.data = pageable.ctypes.data
+    assert lib.colibri_tier_create(ctypes.byref(desc), 4, mem.data_ptr(), nb,
+                                   ctypes.byref(h)) == qre.COLI_E_UNSUPPORTED
+    tier = qre.TieredLayer(slow, 4)
+    x = synth.activations(w).cuda()
+    ws = tier.workspace(w.S)
+    with pytest.raises(qre.ColibriError) as ei:
+        tier.forward(x, ws=ws[:-256])
+    assert ei.value.status == qre.COLI_E_WORKSPACE
+    assert tier.stats()["plans"] == 0  # refused before anything ran
+    empty = tier.forward(torch.zeros(0, w.hidden, device="cuda"))
+    assert empty.shape == (0, w.hidden)
+    tier.close()

@@ -68,7 +68,7 @@ def capi():
 def test_library_exports_every_declared_symbol(capi):
     lib = capi.lib()
     syms = _declared_symbols()
-    assert len(syms) == 9
+    assert len(syms) == 23
     for name in syms:
         assert hasattr(lib, name), name
 
@@ -95,6 +95,38 @@ def _fake_layer(capi, **over):
                           d["router_w"], d["router_bias"], d["gate"], d["up"], d["down"],
                           d["has_shared"], d["sh_gate"], d["sh_up"], d["sh_down"],
                           d["n_group"], d["topk_group"], d["top_p"])
+
+
+def test_tier_sizes_and_validation_before_any_hip_call(capi):
+    """Slot-bank sizes and the tier calls' argument checks (none of them
+    reaches the HIP runtime)."""
+    lib = capi.lib()
+    L = _fake_layer(capi, gate=capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 256, 4),
+                    up=capi.QBankDesc(0x10000000, 0x10000000, 16, 128, 256, 4),
+                    down=capi.QBankDesc(0x10000000, 0x10000000, 16, 256, 128, 2))
+    n3 = lib.colibri_tier_slot_bytes(ctypes.byref(L), 3)
+    # gate + up: 3 * 128 rows * 128 B, scales 3 * 128 * 4; down: 3 * 256 * 32 B, scales 3 * 256 * 4
+    expect = 2 * (3 * 128 * 128 + 3 * 128 * 4) + 3 * 256 * 32 + 3 * 256 * 4
+    assert n3 == expect  # every region is a multiple of 256 here
+    assert lib.colibri_tier_slot_bytes(ctypes.byref(L), 0) == 0
+    assert lib.colibri_tier_slot_bytes(ctypes.byref(L), 17) == 0
+    h = ctypes.c_void_p()
+    assert lib.colibri_tier_create(ctypes.byref(L), 3, 0x10000000, n3, None) == capi.COLI_E_INVAL
+    assert lib.colibri_tier_create(ctypes.byref(L), 0, 0x10000000, n3, ctypes.byref(h)) == capi.COLI_E_INVAL
+    assert lib.colibri_tier_create(ctypes.byref(L), 3, None, n3, ctypes.byref(h)) == capi.COLI_E_INVAL
+    assert lib.colibri_tier_create(ctypes.byref(L), 3, 0x10000010, n3,
+                                   ctypes.byref(h)) == capi.COLI_E_UNSUPPORTED
+    assert lib.colibri_tier_create(ctypes.byref(L), 3, 0x10000000, n3 - 1,
+                                   ctypes.byref(h)) == capi.COLI_E_WORKSPACE
+    Lb = _fake_layer(capi, top_k=0)
+    assert lib.colibri_tier_create(ctypes.byref(Lb), 3, 0x10000000, n3, ctypes.byref(h)) == capi.COLI_E_INVAL
+    assert not h.value
+    assert lib.colibri_tier_forward(None, 0x10000000, 1, 0x10000000, 0x10000000, 1 << 20,
+                                    None) == capi.COLI_E_INVAL
+    assert lib.colibri_tier_pin(None, None, 0, None) == capi.COLI_E_INVAL
+    assert lib.colibri_tier_workspace_bytes(None, 4) == 0
+    assert lib.colibri_tier_cache(None) is None
+    lib.colibri_tier_destroy(None)
 
 
 def test_workspace_size_and_invalid_layers(capi):
