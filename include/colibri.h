@@ -241,16 +241,17 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
  * resident experts compute while the missing ones load in the background and
  * their results join before the layer ends).  On one MI355X the fast tier is
  * a bank of n_slots expert slots in HBM and the slow tier is pinned host
- * memory, read over PCIe by the copy engines.
+ * memory, which kernels read over PCIe.
  *
  * Two objects:
- *   coli_expert_cache  the host-side slot cache and planner.  No GPU calls:
- *                      it runs without a GPU and plans every tier forward.
+ *   coli_expert_cache  the slot-cache policy as a host object (no GPU
+ *                      calls): the reference that the tier's device planner
+ *                      follows step for step, usable on its own.
  *   coli_tier          one layer whose routed experts live in the slow tier,
- *                      with its own cache, slot bank, copy stream and events.
+ *                      with its cache state in HBM, its slot bank, a copy
+ *                      stream and events.
  * Unlike the calls above, these objects own host memory and (coli_tier) HIP
- * objects, and colibri_tier_forward waits for its stream once per call to
- * read the routed ids on the host.
+ * objects; which calls wait for the host is stated with each.
  * ========================================================================= */
 
 typedef struct coli_expert_cache coli_expert_cache;
@@ -273,11 +274,11 @@ typedef struct coli_cache_plan {
 } coli_cache_plan;
 
 typedef struct coli_cache_stats {
-    uint64_t plans;     /* successful colibri_cache_plan calls */
+    uint64_t plans;     /* successful plans */
     uint64_t pairs;     /* routed pairs planned (dropped slots excluded) */
     uint64_t hits;      /* per plan: distinct experts found resident, summed */
     uint64_t misses;    /* per plan: distinct experts loaded, summed */
-    uint64_t pin_loads; /* loads made by colibri_cache_pin */
+    uint64_t pin_loads; /* loads made by pinning */
     uint64_t passes;    /* summed over plans */
     int32_t resident;   /* slots holding an expert now */
     int32_t pinned;     /* slots pinned now */
@@ -292,7 +293,7 @@ void colibri_cache_destroy(coli_expert_cache* c);
  * Pins n distinct experts in [0, n_experts) for good (the hot store): a
  * resident one keeps its slot; any other takes a victim slot (empty first,
  * then least recently used, ties to the lower slot) and is listed in loads
- * (host, n entries; pass 0, after -1), *n_load of them.  The pinned set may
+ * (host, n entries; pass 1, after -1), *n_load of them.  The pinned set may
  * hold at most n_slots - 1 experts unless it holds all of them (n_slots ==
  * n_experts), so that a miss always finds a slot: COLI_E_UNSUPPORTED
  * otherwise.  Invalid or refused calls change nothing.
@@ -312,9 +313,10 @@ void colibri_cache_unpin(coli_expert_cache* c);
  * (reusable after pass 0).  With R ring slots, misses that fit (n_miss <= R)
  * all run in pass 1; otherwise they run in chunks of c = max(1, R/2) per
  * pass, miss i taking ring slot i mod R, so that (for R >= 2) one chunk's
- * loads overlap the previous chunk's compute.  Every expert
- * of the batch becomes most recently used; usage counts grow by its pairs.
- * Host outputs: pair_code [P] (pass << COLI_PLAN_SLOT_BITS | slot, -1 for a
+ * loads overlap the previous chunk's compute.  Each ring slot ends up with
+ * its last miss; what it held before is evicted.  Every expert of the batch
+ * becomes most recently used; usage counts grow by its pairs.  Host
+ * outputs: pair_code [P] (pass << COLI_PLAN_SLOT_BITS | slot, -1 for a
  * dropped slot), loads [min(P, n_experts)] in pass order, pass_pairs
  * [min(P, n_experts) + 1] (pairs per pass), *plan.  An id >= n_experts is
  * COLI_E_INVAL and changes nothing.
@@ -330,20 +332,23 @@ int colibri_cache_state(const coli_expert_cache* c, int32_t* slot_of, uint64_t* 
 
 typedef struct coli_tier coli_tier;
 
-/* Device bytes of a slot bank of n_slots experts of layer L: gate, up and
- * down codes and scales, each region 256-byte aligned (0 if L is invalid or
- * n_slots is outside [1, n_experts]). */
+/* Device bytes that colibri_tier_create needs for n_slots experts of layer
+ * L: the slot bank (gate, up and down codes and scales) and the cache state,
+ * each region 256-byte aligned (0 if L is invalid or n_slots is outside
+ * [1, n_experts]). */
 size_t colibri_tier_slot_bytes(const coli_moe_layer* L, int32_t n_slots);
 
 /*
  * A tiered layer on the current device.  L is a complete layer descriptor
  * whose routed banks (gate, up, down with n_mat = n_experts) are the slow
- * tier: pinned host memory (hipHostMalloc) or device memory; pageable host
- * memory is COLI_E_UNSUPPORTED.  Router and shared expert are device memory
- * as for colibri_moe_layer_forward.  slot_mem is device memory of slot_bytes
- * >= colibri_tier_slot_bytes(L, n_slots) bytes, 256-byte aligned.  The tier
- * keeps L's pointers and slot_mem until colibri_tier_destroy, and creates a
- * non-blocking copy stream (default priority) and events.
+ * tier: pinned host memory (hipHostMalloc) or device memory, row scales
+ * 16-byte aligned; pageable host memory is COLI_E_UNSUPPORTED.  Router and
+ * shared expert are device memory as for colibri_moe_layer_forward.
+ * slot_mem is device memory of slot_bytes >= colibri_tier_slot_bytes(L,
+ * n_slots) bytes, 256-byte aligned, that the tier owns until
+ * colibri_tier_destroy, as it keeps L's pointers.  Creates a non-blocking
+ * copy stream (default priority) and events, and waits for the state's
+ * initialisation: all slots empty, nothing pinned.
  */
 int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem, size_t slot_bytes,
                         coli_tier** out);
@@ -351,10 +356,10 @@ int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem
 /* Waits for the tier's copy stream, then frees its host state and HIP objects. */
 void colibri_tier_destroy(coli_tier* t);
 
-/* The tier's cache, for colibri_cache_stats / colibri_cache_state only. */
-const coli_expert_cache* colibri_tier_cache(const coli_tier* t);
-
-/* Pins experts (colibri_cache_pin) and enqueues their loads on `stream`. */
+/*
+ * Pins experts (the policy of colibri_cache_pin, same limit): the pin
+ * kernel and the loads run on `stream`, and the call waits for them.
+ */
 int colibri_tier_pin(coli_tier* t, const int32_t* experts, int32_t n, coli_stream_t stream);
 
 /* Workspace bytes of colibri_tier_forward for up to S tokens (0 if invalid). */
@@ -362,19 +367,30 @@ size_t colibri_tier_workspace_bytes(const coli_tier* t, int32_t S);
 
 /*
  * colibri_moe_layer_forward with the routed experts taken from the slot
- * bank.  Routes on `stream`, copies the ids to the host and waits for
- * `stream`; plans the batch (colibri_cache_plan); computes pass 0 (the
- * resident experts and the shared expert) on `stream` while the copy stream
- * loads the misses; every later pass waits for its own loads; one combine
- * ends the call.  The output is bit-identical to colibri_moe_layer_forward
- * on the same weights.  Calls on one tier must be ordered on one stream and
- * made with the tier's device current; pinned host staging is allocated
- * the first time a call has more pairs than every call before it.  After a
- * HIP error the cache forgets every slot (pins included) and the call
- * returns COLI_E_HIP.
+ * bank.  On `stream`: route, then the plan kernel (the policy of
+ * colibri_cache_plan on the routed ids, on the state in device memory),
+ * then pass 0 (the resident experts and the shared expert) while the fetch
+ * kernel on the tier's copy stream reads the misses from the slow tier into
+ * their slots; pass 1 waits for that fetch; one combine ends the call.
+ * When n_slots minus the pinned experts is at least min(S * top_k,
+ * n_experts), every plan has at most these two passes and the call returns
+ * without waiting for the device; with every expert pinned, pass 0 alone.  Otherwise a plan may need more passes:
+ * the call then waits once for the plan to reach the host (pass 0 is
+ * already running) and enqueues each later pass after its own fetch.  The
+ * output is bit-identical to colibri_moe_layer_forward on the same weights.
+ * Calls on one tier must be ordered on one stream and made with the tier's
+ * device current; pinned host staging is allocated the first time a
+ * many-pass call needs more than any call before it.  After a HIP error the
+ * tier's state is unspecified: destroy it.
  */
 int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, void* ws,
                          size_t ws_bytes, coli_stream_t stream);
+
+/* Statistics of the tier's cache (as colibri_cache_stats); waits for `stream`. */
+int colibri_tier_stats(const coli_tier* t, coli_cache_stats* st, coli_stream_t stream);
+
+/* Host copies of the tier's state (as colibri_cache_state); waits for `stream`. */
+int colibri_tier_state(const coli_tier* t, int32_t* slot_of, uint64_t* usage, coli_stream_t stream);
 
 /* Static text for a status code. */
 const char* colibri_status_string(int status);

@@ -94,7 +94,8 @@ def lib():
                 ("colibri_tier_create", ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t,
                                                        ctypes.POINTER(_vp)]),
                 ("colibri_tier_destroy", None, [_vp]),
-                ("colibri_tier_cache", _vp, [_vp]),
+                ("colibri_tier_stats", ctypes.c_int, [_vp, _vp, _vp]),
+                ("colibri_tier_state", ctypes.c_int, [_vp, _vp, _vp, _vp]),
                 ("colibri_tier_pin", ctypes.c_int, [_vp, _vp, _i32, _vp]),
                 ("colibri_tier_workspace_bytes", ctypes.c_size_t, [_vp, _i32]),
                 ("colibri_tier_forward", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t,
@@ -401,7 +402,14 @@ class TieredLayer:
         return out
 
     def stats(self) -> dict:
-        return _cache_stats(lib().colibri_tier_cache(self._h))
+        st = CacheStats()
+        _check(lib().colibri_tier_stats(self._h, ctypes.byref(st), _stream()), "colibri_tier_stats")
+        return {f: getattr(st, f) for f, _ in CacheStats._fields_}
 
     def state(self):
-        return _cache_state(lib().colibri_tier_cache(self._h), self.layer.n_experts)
+        """-> (slot_of [E], usage [E])."""
+        E = self.layer.n_experts
+        slot_of = (_i32 * E)()
+        usage = (_u64 * E)()
+        _check(lib().colibri_tier_state(self._h, slot_of, usage, _stream()), "colibri_tier_state")
+        return list(slot_of), list(usage)

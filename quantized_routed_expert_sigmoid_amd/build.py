@@ -15,7 +15,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcolibri.so")
 
 SOURCES = ["api.hip", "q8_router.hip", "dispatch.hip", "ffn_gemv.hip", "ffn_mfma.hip", "tier.hip",
-           "expert_cache.cpp"]
+           "tier_kernels.hip", "expert_cache.cpp"]
 
 ARCH = "gfx950"
 # -ffp-contract=off: every fused multiply-add in the kernels is an explicit

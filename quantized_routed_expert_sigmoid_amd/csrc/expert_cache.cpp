@@ -79,7 +79,7 @@ int ExpertCache::pin(const int32_t* experts, int32_t n, coli_cache_load* loads, 
             victims(excl_, ring_);
             s = ring_[0];
             place(e, s);
-            loads[(*n_load)++] = coli_cache_load{e, s, 0, -1};
+            loads[(*n_load)++] = coli_cache_load{e, s, 1, -1};
             ++st_.pin_loads;
         }
         if (!pinned_[s]) {

@@ -205,6 +205,59 @@ hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_gate_up_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 
+/* ---- tiered expert store (tier_kernels.hip) ------------------------------
+ * The slot cache's state lives in device memory next to the slot bank; the
+ * plan kernel follows the policy of the host planner (expert_cache.cpp)
+ * step for step. */
+constexpr int kTierMaxE = 1024; /* experts and slots */
+
+struct TierHdr {
+    uint32_t tick; /* plans and pins so far (the LRU clock) */
+    int32_t pad;
+    unsigned long long plans, pairs, hits, misses, pin_loads, passes;
+};
+
+struct TierState {
+    TierHdr* hdr;
+    int32_t* slot_of;          /* [E]: slot or -1 */
+    int32_t* expert_in;        /* [n]: expert or -1 */
+    uint32_t* last_use;        /* [n]: tick of the last use */
+    int32_t* pinned;           /* [n] */
+    unsigned long long* usage; /* [E]: routed pairs */
+    int32_t E, n;
+};
+
+/* info[] fields written by the plan and pin kernels. */
+enum { kInfoPass = 0, kInfoLoad, kInfoHit, kInfoMiss, kInfoChunk, kInfoRing, kInfoError, kInfoN = 8 };
+
+/* Per-expert regions of the slow tier and the slot bank, in 16-byte units:
+ * gate codes, gate scales, up codes, up scales, down codes, down scales.
+ * Expert e's region r starts at src[r] + e * len[r]; slot s's at dst[r] +
+ * s * len[r]. */
+struct TierBanks {
+    const uint4* src[6];
+    uint4* dst[6];
+    int64_t len[6];
+};
+
+hipError_t launch_tier_init(const TierState& st, hipStream_t s);
+
+/* Plans P routed ids (ids >= E or < 0 count as dropped): codes [P], loads
+ * [min(P, E)] {expert, slot, pass, after}, info [kInfoN], pass_pairs
+ * [min(P, E) + 1]; updates the state. */
+hipError_t launch_tier_plan(const int32_t* ids, int32_t P, const TierState& st, int32_t* codes,
+                            int4* loads, int32_t* info, int32_t* pass_pairs, hipStream_t s);
+
+/* Pins n experts (validated by the host): loads [n] and info as for a plan
+ * whose single miss pass is pass 1. */
+hipError_t launch_tier_pin(const int32_t* experts, int32_t n, const TierState& st, int4* loads,
+                           int32_t* info, hipStream_t s);
+
+/* Copies the loads of `pass` (from info's chunk and load count) from the slow
+ * tier into their slots. */
+hipError_t launch_tier_fetch(const int4* loads, const int32_t* info, int32_t pass, const TierBanks& b,
+                             hipStream_t s);
+
 hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 

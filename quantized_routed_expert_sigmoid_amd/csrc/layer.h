@@ -120,10 +120,13 @@ struct Bump {
     }
 };
 
-inline Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S, bool shared)
+/* extra_rows: rows of hq / hd / y beyond the P routed rows, before the S
+ * shared-expert rows. */
+inline Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S, bool shared,
+                           int64_t extra_rows = 0)
 {
     const int64_t P = (int64_t)S * k;
-    const int64_t rows = P + (shared ? S : 0);
+    const int64_t rows = P + extra_rows + (shared ? S : 0);
     Bump b;
     Layout L;
     L.logits = b.take((size_t)router_parts(S, E, H) * S * E * 4);

@@ -1,7 +1,7 @@
 /*
  * tier.hip -- tiered expert residency (colibri_tier_* of the C ABI): the
  * routed experts of one layer live in pinned host memory, a slot bank in HBM
- * caches some of them, and the layer forward streams the misses in over PCIe
+ * caches some of them, and the layer forward pulls the misses in over PCIe
  * while the resident experts compute.
  *
  * The placement follows "Show HN: 如何在我的低配置电脑上运行 GLM-5.2",
@@ -9,25 +9,25 @@
  * optional pinned hot set) and its paragraph on the deferred cold-expert
  * pipeline (resident experts run while the missing ones load in the
  * background; the late results join before the layer completes).  There the
- * tiers are RAM over disk; here they are HBM over pinned host memory, and the
- * loads are copy-engine transfers on a stream of their own.
+ * tiers are RAM over disk and the planner runs on the CPU; here they are HBM
+ * over pinned host memory, the cache state lives in HBM, and both the plan
+ * and the loads are kernels, so a forward needs nothing from the host.
  *
  * One forward:
- *   1. quantise + router + selection on the caller's stream (the kernels of
- *      the resident forward); the routed ids go to pinned host staging and
- *      the host waits for the stream;
- *   2. the slot cache plans the batch (expert_cache.cpp): pair codes (pass,
- *      slot), loads and passes; the codes go back to the device;
+ *   1. quantise + router + selection (the kernels of the resident forward);
+ *   2. the plan kernel (tier_kernels.hip) gives every pair a pass and a
+ *      slot, lists the loads and updates the cache state;
  *   3. pass 0 -- dispatch of the resident experts' pairs over the slot bank,
  *      FFN over those pairs and the shared expert -- runs on the caller's
- *      stream at once; the copy stream loads the misses, each load waiting
- *      only for the pass that still reads its slot's previous occupant;
- *   4. pass j >= 1 waits for its loads, dispatches its pairs (inv continues
- *      where the previous passes stopped) and runs the FFN;
+ *      stream while the fetch kernel, on the tier's copy stream, pulls the
+ *      misses from pinned host memory into their slots;
+ *   4. pass 1 waits for the fetch.  When the unpinned slots cannot hold
+ *      every expert a batch may route to, a plan may need more passes: the
+ *      plan is then read back to the host once, and each later pass waits
+ *      for its own fetch, which waits for the pass that last read its slots;
  *   5. one combine over every pass's rows, in slot order as in the resident
  *      forward, so the output is the resident forward's bit for bit.
  */
-#include "expert_cache.h"
 #include "layer.h"
 
 #include <new>
@@ -36,6 +36,7 @@
 using namespace coli;
 
 static_assert(kPassSlotBits == COLI_PLAN_SLOT_BITS, "pair code layouts differ");
+static_assert(kTierMaxE == COLI_MAX_EXPERTS, "planner sized for the expert limit");
 
 namespace {
 
@@ -45,50 +46,86 @@ size_t row_bytes(int32_t K, int32_t qtype)
     return (size_t)K * qtype / 8;
 }
 
+/* slot_mem: the six slot-bank regions, then the cache state and the pin
+ * scratch. */
 struct SlotLayout {
-    size_t gate, gate_s, up, up_s, down, down_s, total;
+    size_t reg[6];
+    size_t hdr, slot_of, expert_in, last_use, pinned, usage, pin_experts, pin_loads, pin_info, total;
 };
 
-SlotLayout slot_layout(const coli_moe_layer* L, int32_t n_slots)
+SlotLayout slot_layout(const coli_moe_layer* L, int32_t n)
 {
-    const int32_t H = L->hidden, I = L->inter;
+    const int32_t H = L->hidden, I = L->inter, E = L->n_experts;
     Bump b;
     SlotLayout s;
-    s.gate = b.take((size_t)n_slots * I * row_bytes(H, L->gate.qtype));
-    s.gate_s = b.take((size_t)n_slots * I * 4);
-    s.up = b.take((size_t)n_slots * I * row_bytes(H, L->up.qtype));
-    s.up_s = b.take((size_t)n_slots * I * 4);
-    s.down = b.take((size_t)n_slots * H * row_bytes(I, L->down.qtype));
-    s.down_s = b.take((size_t)n_slots * H * 4);
+    s.reg[0] = b.take((size_t)n * I * row_bytes(H, L->gate.qtype));
+    s.reg[1] = b.take((size_t)n * I * 4);
+    s.reg[2] = b.take((size_t)n * I * row_bytes(H, L->up.qtype));
+    s.reg[3] = b.take((size_t)n * I * 4);
+    s.reg[4] = b.take((size_t)n * H * row_bytes(I, L->down.qtype));
+    s.reg[5] = b.take((size_t)n * H * 4);
+    s.hdr = b.take(sizeof(TierHdr));
+    s.slot_of = b.take((size_t)E * 4);
+    s.expert_in = b.take((size_t)n * 4);
+    s.last_use = b.take((size_t)n * 4);
+    s.pinned = b.take((size_t)n * 4);
+    s.usage = b.take((size_t)E * 8);
+    s.pin_experts = b.take((size_t)kTierMaxE * 4);
+    s.pin_loads = b.take((size_t)kTierMaxE * 16);
+    s.pin_info = b.take((size_t)kInfoN * 4);
     s.total = b.at;
     return s;
 }
 
-/* Pinned host memory or device memory: what a copy engine reads
- * asynchronously. */
-bool transferable(const void* p)
+/* Per-expert bytes of the six regions (gate, gate scales, up, up scales,
+ * down, down scales). */
+void region_bytes(const coli_moe_layer* L, size_t out[6])
+{
+    const int32_t H = L->hidden, I = L->inter;
+    out[0] = (size_t)I * row_bytes(H, L->gate.qtype);
+    out[1] = (size_t)I * 4;
+    out[2] = (size_t)I * row_bytes(H, L->up.qtype);
+    out[3] = (size_t)I * 4;
+    out[4] = (size_t)H * row_bytes(I, L->down.qtype);
+    out[5] = (size_t)H * 4;
+}
+
+/* The device address of slow-tier memory: pinned host memory (mapped into
+ * the device's address space) or device memory; nullptr otherwise. */
+const void* device_view(const void* p)
 {
     hipPointerAttribute_t a;
     if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-        (void)hipGetLastError(); /* clear the sticky error of a pageable pointer */
-        return false;
+        (void)hipGetLastError(); /* clear the error a pageable pointer leaves */
+        return nullptr;
     }
-    return a.type == hipMemoryTypeHost || a.type == hipMemoryTypeDevice ||
-           a.type == hipMemoryTypeManaged;
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged)
+        return p;
+    if (a.type == hipMemoryTypeHost)
+        return a.devicePointer ? a.devicePointer : p;
+    return nullptr;
 }
 
+/* Workspace of a tiered forward: the resident layout with P more rows of
+ * hq / hd / y (pass 1 writes rows P .. 2P-1, the shared expert 2P ..), then
+ * the plan. */
 struct TierLayout {
     Layout l;
-    size_t codes, total;
+    size_t codes, loads, info, pass_pairs, total;
 };
 
 TierLayout tier_layout(const coli_moe_layer* L, int32_t S)
 {
+    const int64_t P = (int64_t)S * L->top_k;
+    const int64_t m = P < L->n_experts ? P : L->n_experts;
     TierLayout t;
-    t.l = layer_layout(L->hidden, L->inter, L->n_experts, L->top_k, S, L->has_shared != 0);
+    t.l = layer_layout(L->hidden, L->inter, L->n_experts, L->top_k, S, L->has_shared != 0, P);
     Bump b;
     b.at = t.l.total;
-    t.codes = b.take((size_t)S * L->top_k * 4);
+    t.codes = b.take((size_t)P * 4);
+    t.loads = b.take((size_t)m * 16);
+    t.info = b.take((size_t)kInfoN * 4);
+    t.pass_pairs = b.take((size_t)(m + 1) * 4);
     t.total = b.at;
     return t;
 }
@@ -96,84 +133,73 @@ TierLayout tier_layout(const coli_moe_layer* L, int32_t S)
 } // namespace
 
 struct coli_tier {
-    coli_moe_layer L;          /* slow-tier routed banks, device router and shared expert */
-    coli_qbank slot[3];        /* gate, up, down slot banks (n_mat = n_slots) */
-    coli_expert_cache cache;
+    coli_moe_layer L;        /* slow-tier routed banks, device router and shared expert */
+    coli_qbank slot[3];      /* gate, up, down slot banks (n_mat = n_slots) */
+    TierState st;
+    TierBanks banks;
+    size_t expert_bytes = 0;
+    int32_t n_slots = 0;
     int device = -1;
     hipStream_t copy = nullptr;
-    std::vector<hipEvent_t> ev_pass, ev_load;
-    int32_t* h_ids = nullptr;  /* pinned staging, h_cap pairs */
-    int32_t* h_codes = nullptr;
-    int64_t h_cap = 0;
-    std::vector<coli_cache_load> loads;
-    std::vector<int32_t> pass_pairs;
+    hipEvent_t ev_plan = nullptr, ev_d2h = nullptr;
+    std::vector<hipEvent_t> ev_pass, ev_fetch;
+    std::vector<uint8_t> pinned_e; /* host mirror of the pinned set */
+    int32_t n_pinned = 0;
+    int32_t* pin_experts = nullptr; /* device */
+    int4* pin_loads = nullptr;
+    int32_t* pin_info = nullptr;
+    int32_t* h_buf = nullptr;       /* pinned host staging */
+    size_t h_cap = 0;               /* int32 entries */
 
-    coli_tier(const coli_moe_layer& l, int32_t n_slots) : L(l), cache(l.n_experts, n_slots) {}
-
-    /* Grows staging, plan arrays and event pools for P pairs. */
-    hipError_t reserve(int64_t P, hipStream_t s)
+    ~coli_tier()
     {
-        const int64_t m = P < L.n_experts ? P : L.n_experts;
-        if ((int64_t)loads.size() < m)
-            loads.resize(m);
-        if ((int64_t)pass_pairs.size() < m + 1)
-            pass_pairs.resize(m + 1);
-        while ((int64_t)ev_pass.size() < m + 1) {
+        if (copy) {
+            (void)hipStreamSynchronize(copy);
+            (void)hipStreamDestroy(copy);
+        }
+        for (hipEvent_t e : ev_pass)
+            (void)hipEventDestroy(e);
+        for (hipEvent_t e : ev_fetch)
+            (void)hipEventDestroy(e);
+        if (ev_plan)
+            (void)hipEventDestroy(ev_plan);
+        if (ev_d2h)
+            (void)hipEventDestroy(ev_d2h);
+        if (h_buf)
+            (void)hipHostFree(h_buf);
+    }
+
+    hipError_t events(size_t n)
+    {
+        while (ev_pass.size() < n) {
             hipEvent_t a, b;
             hipError_t e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
             if (e != hipSuccess)
                 return e;
-            e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
-            if (e != hipSuccess) {
+            if ((e = hipEventCreateWithFlags(&b, hipEventDisableTiming)) != hipSuccess) {
                 (void)hipEventDestroy(a);
                 return e;
             }
             ev_pass.push_back(a);
-            ev_load.push_back(b);
+            ev_fetch.push_back(b);
         }
-        if (P <= h_cap)
+        return hipSuccess;
+    }
+
+    /* Pinned host staging of at least n int32 entries.  Every earlier use
+     * of the staging has completed when this is called. */
+    hipError_t staging(size_t n)
+    {
+        if (n <= h_cap)
             return hipSuccess;
-        /* the previous call's transfers from the old staging may be pending */
-        hipError_t e = hipStreamSynchronize(s);
-        if (e != hipSuccess)
-            return e;
-        free_staging();
-        if ((e = hipHostMalloc((void**)&h_ids, (size_t)P * 4, hipHostMallocDefault)) != hipSuccess)
-            return e;
-        if ((e = hipHostMalloc((void**)&h_codes, (size_t)P * 4, hipHostMallocDefault)) != hipSuccess)
-            return e;
-        h_cap = P;
-        return hipSuccess;
-    }
-
-    void free_staging()
-    {
-        if (h_ids)
-            (void)hipHostFree(h_ids);
-        if (h_codes)
-            (void)hipHostFree(h_codes);
-        h_ids = h_codes = nullptr;
+        if (h_buf)
+            (void)hipHostFree(h_buf);
+        h_buf = nullptr;
         h_cap = 0;
-    }
-
-    /* Copies expert e's gate, up and down codes and scales into slot s. */
-    hipError_t load(int32_t e, int32_t s, hipStream_t st) const
-    {
-        const coli_qbank* src[3] = {&L.gate, &L.up, &L.down};
-        for (int m = 0; m < 3; ++m) {
-            const coli_qbank& a = *src[m];
-            const coli_qbank& d = slot[m];
-            const size_t rb = row_bytes(a.K, a.qtype) * a.rows;
-            hipError_t r = hipMemcpyAsync((char*)d.data + (size_t)s * rb,
-                                          (const char*)a.data + (size_t)e * rb, rb, hipMemcpyDefault, st);
-            if (r == hipSuccess)
-                r = hipMemcpyAsync((float*)d.row_scale + (size_t)s * a.rows,
-                                   a.row_scale + (size_t)e * a.rows, (size_t)a.rows * 4,
-                                   hipMemcpyDefault, st);
-            if (r != hipSuccess)
-                return r;
-        }
-        return hipSuccess;
+        hipError_t e = hipHostMalloc((void**)&h_buf, n * 4, hipHostMallocDefault);
+        if (e == hipSuccess)
+            h_cap = n;
+        return e;
     }
 };
 
@@ -189,13 +215,11 @@ int check_current_device(const coli_tier* t)
 
 /* The routed and shared FFN of one pass; `shared` only in pass 0. */
 hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const int32_t* codes, int32_t pass,
-                    int32_t base, int32_t S, bool with_routed, bool with_shared, hipStream_t s)
+                    int32_t base, int32_t S, bool with_shared, hipStream_t s)
 {
     const coli_moe_layer* L = &t->L;
     const int32_t H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k;
     const int32_t P = S * k;
-    const int32_t n_slots = t->cache.n_slots();
-    int32_t* offsets = at<int32_t>(ws, Lo.l.offsets);
     int32_t* sorted = at<int32_t>(ws, Lo.l.sorted);
     UnitLists ul;
     ul.units = at<Unit>(ws, Lo.l.units);
@@ -205,12 +229,12 @@ hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const in
     ul.n_munits = at<int32_t>(ws, Lo.l.n_munits);
     ul.max_munits = max_mfma_units(P, E, S);
 
-    hipError_t e = launch_dispatch_pass(codes, pass, base, S, k, n_slots, offsets, sorted,
-                                        at<int32_t>(ws, Lo.l.inv), at<int32_t>(ws, Lo.l.active),
+    hipError_t e = launch_dispatch_pass(codes, pass, base, S, k, t->n_slots, at<int32_t>(ws, Lo.l.offsets),
+                                        sorted, at<int32_t>(ws, Lo.l.inv), at<int32_t>(ws, Lo.l.active),
                                         at<int32_t>(ws, Lo.l.n_active), ul, s);
     FfnArgs a;
     a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], sorted, &ul, k, S, P, base);
-    a.nseg = with_routed ? 1 : 0;
+    a.nseg = 1;
     a.unit_tokens = S == 1 ? 1 : kUnitTokens;
     a.H = H;
     a.I = I;
@@ -222,21 +246,16 @@ hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const in
     FfnArgs b = a;
     b.nseg = 0;
     if (with_shared) {
-        const FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P);
+        const FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, 2 * P);
         if (L->sh_gate.qtype == t->slot[0].qtype && L->sh_down.qtype == t->slot[2].qtype) {
-            if (a.nseg == 1) {
-                a.seg[1] = sh;
-                a.nseg = 2;
-            } else {
-                a.seg[0] = sh;
-                a.nseg = 1;
-            }
+            a.seg[1] = sh;
+            a.nseg = 2;
         } else {
             b.seg[0] = sh;
             b.nseg = 1;
         }
     }
-    if (e == hipSuccess && a.nseg)
+    if (e == hipSuccess)
         e = run_ffn(a, t->slot[0].qtype, t->slot[2].qtype, s);
     if (e == hipSuccess && b.nseg)
         e = run_ffn(b, L->sh_gate.qtype, L->sh_down.qtype, s);
@@ -265,32 +284,67 @@ int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem
         return st;
     if (n_slots < 1 || n_slots > L->n_experts || !slot_mem)
         return COLI_E_INVAL;
-    if (!aligned(slot_mem, kAlign))
+    if (!aligned(slot_mem, kAlign) || !aligned(L->gate.row_scale, 16) || !aligned(L->up.row_scale, 16) ||
+        !aligned(L->down.row_scale, 16))
         return COLI_E_UNSUPPORTED;
     const SlotLayout sl = slot_layout(L, n_slots);
     if (slot_bytes < sl.total)
         return COLI_E_WORKSPACE;
     const void* slow[6] = {L->gate.data, L->gate.row_scale, L->up.data,
                            L->up.row_scale, L->down.data, L->down.row_scale};
-    for (const void* p : slow)
-        if (!transferable(p))
+    const void* view[6];
+    for (int r = 0; r < 6; ++r)
+        if (!(view[r] = device_view(slow[r])))
             return COLI_E_UNSUPPORTED;
 
-    coli_tier* t = new (std::nothrow) coli_tier(*L, n_slots);
+    coli_tier* t = new (std::nothrow) coli_tier();
     if (!t)
         return COLI_E_INVAL;
+    t->L = *L;
+    t->n_slots = n_slots;
+    t->pinned_e.assign(L->n_experts, 0);
+    size_t rb[6];
+    region_bytes(L, rb);
     const coli_qbank* src[3] = {&L->gate, &L->up, &L->down};
-    const size_t off[3][2] = {{sl.gate, sl.gate_s}, {sl.up, sl.up_s}, {sl.down, sl.down_s}};
     for (int m = 0; m < 3; ++m) {
         t->slot[m] = *src[m];
         t->slot[m].n_mat = n_slots;
-        t->slot[m].data = at<uint8_t>(slot_mem, off[m][0]);
-        t->slot[m].row_scale = at<float>(slot_mem, off[m][1]);
+        t->slot[m].data = at<uint8_t>(slot_mem, sl.reg[2 * m]);
+        t->slot[m].row_scale = at<float>(slot_mem, sl.reg[2 * m + 1]);
     }
-    if (hipGetDevice(&t->device) != hipSuccess ||
-        hipStreamCreateWithFlags(&t->copy, hipStreamNonBlocking) != hipSuccess) {
-        t->copy = nullptr;
-        colibri_tier_destroy(t);
+    for (int r = 0; r < 6; ++r) {
+        t->banks.src[r] = static_cast<const uint4*>(view[r]);
+        t->banks.dst[r] = at<uint4>(slot_mem, sl.reg[r]);
+        t->banks.len[r] = (int64_t)(rb[r] / 16);
+        t->expert_bytes += rb[r];
+    }
+    t->st.hdr = at<TierHdr>(slot_mem, sl.hdr);
+    t->st.slot_of = at<int32_t>(slot_mem, sl.slot_of);
+    t->st.expert_in = at<int32_t>(slot_mem, sl.expert_in);
+    t->st.last_use = at<uint32_t>(slot_mem, sl.last_use);
+    t->st.pinned = at<int32_t>(slot_mem, sl.pinned);
+    t->st.usage = at<unsigned long long>(slot_mem, sl.usage);
+    t->st.E = L->n_experts;
+    t->st.n = n_slots;
+    t->pin_experts = at<int32_t>(slot_mem, sl.pin_experts);
+    t->pin_loads = at<int4>(slot_mem, sl.pin_loads);
+    t->pin_info = at<int32_t>(slot_mem, sl.pin_info);
+
+    hipError_t e = hipGetDevice(&t->device);
+    if (e == hipSuccess)
+        e = hipStreamCreateWithFlags(&t->copy, hipStreamNonBlocking);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&t->ev_plan, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&t->ev_d2h, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = t->events(2);
+    if (e == hipSuccess)
+        e = launch_tier_init(t->st, t->copy);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(t->copy);
+    if (e != hipSuccess) {
+        delete t;
         return COLI_E_HIP;
     }
     *out = t;
@@ -299,43 +353,47 @@ int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem
 
 void colibri_tier_destroy(coli_tier* t)
 {
-    if (!t)
-        return;
-    if (t->copy) {
-        (void)hipStreamSynchronize(t->copy);
-        (void)hipStreamDestroy(t->copy);
-    }
-    for (hipEvent_t e : t->ev_pass)
-        (void)hipEventDestroy(e);
-    for (hipEvent_t e : t->ev_load)
-        (void)hipEventDestroy(e);
-    t->free_staging();
     delete t;
-}
-
-const coli_expert_cache* colibri_tier_cache(const coli_tier* t)
-{
-    return t ? &t->cache : nullptr;
 }
 
 int colibri_tier_pin(coli_tier* t, const int32_t* experts, int32_t n, coli_stream_t stream)
 {
-    if (!t)
+    if (!t || n < 0 || (n > 0 && !experts))
         return COLI_E_INVAL;
     int st = check_current_device(t);
-    if (st)
+    if (st || n == 0)
         return st;
-    std::vector<coli_cache_load> loads(n > 0 ? n : 0);
-    int32_t n_load = 0;
-    if ((st = t->cache.pin(experts, n, loads.data(), &n_load)))
-        return st;
-    hipError_t e = hipSuccess;
-    for (int32_t i = 0; i < n_load && e == hipSuccess; ++i)
-        e = t->load(loads[i].expert, loads[i].slot, (hipStream_t)stream);
-    if (e != hipSuccess) {
-        t->cache.reset();
-        return COLI_E_HIP;
+    const int32_t E = t->L.n_experts;
+    std::vector<uint8_t> seen(E, 0);
+    int32_t fresh = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t e = experts[i];
+        if (e < 0 || e >= E || seen[e])
+            return COLI_E_INVAL; /* out of range or repeated */
+        seen[e] = 1;
+        fresh += t->pinned_e[e] ? 0 : 1;
     }
+    const int32_t total = t->n_pinned + fresh;
+    if (!(total <= t->n_slots - 1 || (total == E && t->n_slots == E)))
+        return COLI_E_UNSUPPORTED; /* a slot has to stay free for misses */
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = t->staging((size_t)n);
+    if (e == hipSuccess) {
+        for (int32_t i = 0; i < n; ++i)
+            t->h_buf[i] = experts[i];
+        e = hipMemcpyAsync(t->pin_experts, t->h_buf, (size_t)n * 4, hipMemcpyHostToDevice, s);
+    }
+    if (e == hipSuccess)
+        e = launch_tier_pin(t->pin_experts, n, t->st, t->pin_loads, t->pin_info, s);
+    if (e == hipSuccess)
+        e = launch_tier_fetch(t->pin_loads, t->pin_info, 1, t->banks, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s); /* the staging is free again */
+    if (e != hipSuccess)
+        return COLI_E_HIP;
+    for (int32_t i = 0; i < n; ++i)
+        t->pinned_e[experts[i]] = 1;
+    t->n_pinned = total;
     return COLI_OK;
 }
 
@@ -368,19 +426,28 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
         return COLI_E_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const int32_t H = L->hidden, E = L->n_experts, k = L->top_k;
-    const int32_t P = S * k;
+    const int32_t P = S * k, m = P < E ? P : E;
+    /* with every expert pinned nothing can miss: pass 0 is the whole plan;
+     * otherwise every plan fits two passes when the unpinned slots can take
+     * every expert of the batch */
+    const bool all_pinned = t->n_pinned == E;
+    const bool two_passes = all_pinned || t->n_slots - t->n_pinned >= m;
     int8_t* xq = at<int8_t>(ws, Lo.l.xq);
     float* xd = at<float>(ws, Lo.l.xd);
     float* logits = at<float>(ws, Lo.l.logits);
     int32_t* ids = at<int32_t>(ws, Lo.l.ids);
     float* w = at<float>(ws, Lo.l.w);
     int32_t* codes = at<int32_t>(ws, Lo.codes);
+    int4* loads = at<int4>(ws, Lo.loads);
+    int32_t* info = at<int32_t>(ws, Lo.info);
+    int32_t* pass_pairs = at<int32_t>(ws, Lo.pass_pairs);
+    const size_t n_back = kInfoN + (size_t)(m + 1) + 4 * (size_t)m; /* info, pass_pairs, loads */
 
-    hipError_t e = t->reserve(P, s);
+    hipError_t e = two_passes ? hipSuccess : t->staging(n_back);
     if (e != hipSuccess)
         return COLI_E_HIP;
 
-    /* 1. route */
+    /* 1-2. route and plan */
     e = S <= kSmallS ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
                      : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
     if (e == hipSuccess && S > kSmallS)
@@ -389,57 +456,129 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
         e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
                                  L->routed_scaling_factor, route_opts(L), ids, w, s);
     if (e == hipSuccess)
-        e = hipMemcpyAsync(t->h_ids, ids, (size_t)P * 4, hipMemcpyDeviceToHost, s);
+        e = launch_tier_plan(ids, P, t->st, codes, loads, info, pass_pairs, s);
+    int32_t* h_info = t->h_buf;
+    int32_t* h_pp = two_passes ? nullptr : h_info + kInfoN;
+    int4* h_loads = two_passes ? nullptr : reinterpret_cast<int4*>(h_pp + (m + 1));
+    if (!two_passes) {
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(h_info, info, kInfoN * 4, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(h_pp, pass_pairs, (size_t)(m + 1) * 4, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(h_loads, loads, (size_t)m * 16, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess)
+            e = hipEventRecord(t->ev_d2h, s);
+    }
     if (e == hipSuccess)
-        e = hipStreamSynchronize(s);
-    if (e != hipSuccess)
-        return COLI_E_HIP;
-
-    /* 2. plan */
-    coli_cache_plan plan;
-    if ((st = t->cache.plan(t->h_ids, P, t->h_codes, t->loads.data(), t->pass_pairs.data(), &plan)))
-        return st; /* ids out of range cannot come from the router; nothing was enqueued */
-    e = hipMemcpyAsync(codes, t->h_codes, (size_t)P * 4, hipMemcpyHostToDevice, s);
+        e = hipEventRecord(t->ev_plan, s);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(t->copy, t->ev_plan, 0);
 
     /* 3. pass 0 at once */
     const bool shared = L->has_shared != 0;
     if (e == hipSuccess)
-        e = run_pass(t, Lo, ws, codes, 0, 0, S, t->pass_pairs[0] > 0, shared, s);
+        e = run_pass(t, Lo, ws, codes, 0, 0, S, shared, s);
     if (e == hipSuccess)
         e = hipEventRecord(t->ev_pass[0], s);
 
-    /* 4. later passes, each after its loads */
-    int32_t li = 0, waited = -1, base = t->pass_pairs[0];
-    for (int32_t j = 1; j < plan.n_pass && e == hipSuccess; ++j) {
-        for (; li < plan.n_load && t->loads[li].pass == j && e == hipSuccess; ++li) {
-            const coli_cache_load& ld = t->loads[li];
-            if (ld.after > waited) {
-                e = hipStreamWaitEvent(t->copy, t->ev_pass[ld.after], 0);
-                waited = ld.after;
+    /* 4. the miss passes */
+    if (all_pinned) {
+        /* the copy stream has waited for the plan; nothing to fetch */
+    } else if (two_passes) {
+        if (e == hipSuccess)
+            e = launch_tier_fetch(loads, info, 1, t->banks, t->copy);
+        if (e == hipSuccess)
+            e = hipEventRecord(t->ev_fetch[1], t->copy);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(s, t->ev_fetch[1], 0);
+        if (e == hipSuccess)
+            e = run_pass(t, Lo, ws, codes, 1, P, S, false, s);
+    } else {
+        if (e == hipSuccess)
+            e = hipEventSynchronize(t->ev_d2h);
+        const int32_t n_pass = e == hipSuccess ? h_info[kInfoPass] : 0;
+        if (e == hipSuccess && (h_info[kInfoError] || n_pass < 1 || n_pass > m + 1))
+            e = hipErrorUnknown; /* every slot pinned: excluded by the pin limit */
+        if (e == hipSuccess)
+            e = t->events((size_t)n_pass + 1);
+        int32_t li = 0, waited = -1, base = e == hipSuccess ? h_pp[0] : 0;
+        for (int32_t j = 1; j < n_pass && e == hipSuccess; ++j) {
+            int32_t after = -1;
+            for (; li < h_info[kInfoLoad] && h_loads[li].z == j; ++li)
+                after = h_loads[li].w > after ? h_loads[li].w : after;
+            if (after > waited) {
+                e = hipStreamWaitEvent(t->copy, t->ev_pass[after], 0);
+                waited = after;
             }
             if (e == hipSuccess)
-                e = t->load(ld.expert, ld.slot, t->copy);
+                e = launch_tier_fetch(loads, info, j, t->banks, t->copy);
+            if (e == hipSuccess)
+                e = hipEventRecord(t->ev_fetch[j], t->copy);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(s, t->ev_fetch[j], 0);
+            if (e == hipSuccess)
+                e = run_pass(t, Lo, ws, codes, j, base, S, false, s);
+            if (e == hipSuccess)
+                e = hipEventRecord(t->ev_pass[j], s);
+            base += h_pp[j];
         }
-        if (e == hipSuccess)
-            e = hipEventRecord(t->ev_load[j], t->copy);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(s, t->ev_load[j], 0);
-        if (e == hipSuccess)
-            e = run_pass(t, Lo, ws, codes, j, base, S, true, false, s);
-        if (e == hipSuccess)
-            e = hipEventRecord(t->ev_pass[j], s);
-        base += t->pass_pairs[j];
     }
 
     /* 5. combine over every pass's rows */
     if (e == hipSuccess)
         e = launch_combine(at<float>(ws, Lo.l.y), at<int32_t>(ws, Lo.l.inv), ids, w, S, k, H,
-                           shared ? P : -1, out, s);
-    if (e != hipSuccess) {
-        t->cache.reset();
+                           shared ? 2 * P : -1, out, s);
+    return hip_status(e);
+}
+
+int colibri_tier_stats(const coli_tier* t, coli_cache_stats* out, coli_stream_t stream)
+{
+    if (!t || !out)
+        return COLI_E_INVAL;
+    int st = check_current_device(t);
+    if (st)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    TierHdr h;
+    std::vector<int32_t> ein(t->n_slots);
+    hipError_t e = hipMemcpyAsync(&h, t->st.hdr, sizeof h, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(ein.data(), t->st.expert_in, ein.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
         return COLI_E_HIP;
-    }
+    out->plans = h.plans;
+    out->pairs = h.pairs;
+    out->hits = h.hits;
+    out->misses = h.misses;
+    out->pin_loads = h.pin_loads;
+    out->passes = h.passes;
+    out->resident = 0;
+    for (const int32_t v : ein)
+        out->resident += v >= 0 ? 1 : 0;
+    out->pinned = t->n_pinned;
     return COLI_OK;
+}
+
+int colibri_tier_state(const coli_tier* t, int32_t* slot_of, uint64_t* usage, coli_stream_t stream)
+{
+    if (!t)
+        return COLI_E_INVAL;
+    int st = check_current_device(t);
+    if (st)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t E = (size_t)t->L.n_experts;
+    hipError_t e = hipSuccess;
+    if (slot_of)
+        e = hipMemcpyAsync(slot_of, t->st.slot_of, E * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && usage)
+        e = hipMemcpyAsync(usage, t->st.usage, E * 8, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    return hip_status(e);
 }
 
 } // extern "C"

@@ -5,7 +5,9 @@ same weights bit for bit -- over sequences of batches that hit, miss, evict
 and reload slots, with chunked passes when a batch needs more experts than
 there are slots, with pinned experts, top-p-dropped slots and a shared
 expert at another width -- and one case is checked against the oracle
-directly."""
+directly.  After every forward the device planner's state (slot map, usage,
+counters) must equal that of the host planner (colibri_cache_*, itself
+checked on the CPU against the documented policy) fed the same routed ids."""
 
 import ctypes
 
@@ -51,7 +53,9 @@ def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
     return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
 
 
-def _run_sequence(qre, w, dev, tier, order=ORDER, S=None):
+def _run_sequence(qre, w, dev, tier, order=ORDER, S=None, host=None):
+    """Runs the batches through the tier and the resident layer; `host` (an
+    ExpertCache mirroring the tier) is planned with the same routed ids."""
     S = w.S if S is None else S
     xs = {}
     misses = 0
@@ -64,6 +68,11 @@ def _run_sequence(qre, w, dev, tier, order=ORDER, S=None):
         torch.cuda.synchronize()
         assert bits_equal(got, ref), f"batch {b}: tiered output differs from the resident forward"
         misses += tier.stats()["misses"] - before
+        if host is not None:
+            ids, _ = qre.route(dev, xs[b])
+            host.plan(ids.cpu().reshape(-1).tolist())
+            assert tier.state() == host.state(), f"batch {b}: device and host planners disagree"
+            assert tier.stats() == host.stats()
     return misses
 
 
@@ -74,7 +83,8 @@ def test_tier_matches_resident_bitwise(qre, case, n_slots):
     L = synth.make_layer(w)
     dev = to_device(L)
     tier = qre.TieredLayer(to_slow_tier(L, dev), n_slots)
-    misses = _run_sequence(qre, w, dev, tier)
+    host = qre.ExpertCache(w.n_experts, n_slots)
+    misses = _run_sequence(qre, w, dev, tier, host=host)
     st = tier.stats()
     say(f"  plans={st['plans']} hits={st['hits']} misses={st['misses']} passes={st['passes']}")
     assert st["plans"] == len(ORDER) and misses == st["misses"] > 0
@@ -103,14 +113,34 @@ def test_tier_pinned_hot_set(qre):
     L = synth.make_layer(w)
     dev = to_device(L)
     tier = qre.TieredLayer(to_slow_tier(L, dev), 10)
+    host = qre.ExpertCache(w.n_experts, 10)
     hot = [3, 17, 40, 63, 5, 22]
+    _run_sequence(qre, w, dev, tier, order=[7], host=host)  # something resident before the pins
     tier.pin(hot)
-    assert tier.stats()["pinned"] == len(hot) and tier.stats()["pin_loads"] == len(hot)
-    _run_sequence(qre, w, dev, tier, order=[0, 1, 2, 3, 4, 0, 5, 1])
+    host.pin(hot)
+    assert tier.state() == host.state() and tier.stats() == host.stats()
+    assert tier.stats()["pinned"] == len(hot)
+    _run_sequence(qre, w, dev, tier, order=[0, 1, 2, 3, 4, 0, 5, 1], host=host)
     slot_of, _ = tier.state()
     assert all(slot_of[e] >= 0 for e in hot)
     with pytest.raises(qre.ColibriError):
         tier.pin([0, 1, 2, 4])  # 10 pins would leave no slot for misses
+    tier.close()
+
+
+def test_tier_everything_pinned(qre):
+    """All experts pinned: one pass per call, no loads after the pins."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["long_int4_shared"])
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    E = w.n_experts
+    tier = qre.TieredLayer(to_slow_tier(L, dev), E)
+    host = qre.ExpertCache(E, E)
+    tier.pin(list(range(E))[::-1])
+    host.pin(list(range(E))[::-1])
+    _run_sequence(qre, w, dev, tier, order=[0, 1, 2, 0], host=host)
+    st = tier.stats()
+    assert st["misses"] == 0 and st["passes"] == st["plans"] == 4 and st["pin_loads"] == E
     tier.close()
 
 
@@ -159,4 +189,39 @@ def test_tier_argument_errors(qre):
     assert tier.stats()["plans"] == 0  # refused before anything ran
     empty = tier.forward(torch.zeros(0, w.hidden, device="cuda"))
     assert empty.shape == (0, w.hidden)
+    tier.close()
+
+
+def test_tier_forward_in_a_graph(qre):
+    """With enough unpinned slots the tiered forward never waits for the
+    host, so it can be captured: replays of one captured forward over
+    changing inputs equal the resident forward, and the cache state evolves
+    as for eager calls."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["decode_int4"])
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    tier = qre.TieredLayer(to_slow_tier(L, dev), 12)
+    host = qre.ExpertCache(w.n_experts, 12)
+    x_in = torch.zeros(w.S, w.hidden, device="cuda")
+    out = torch.zeros_like(x_in)
+    ws = tier.workspace(w.S)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            tier.forward(x_in, out, ws)
+    torch.cuda.synchronize()
+    for b in [0, 1, 0, 2, 3, 1]:
+        x = synth.activations(w, tag=f"tier{b}").cuda()
+        x_in.copy_(x)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = qre.moe_layer_forward(dev, x)
+        torch.cuda.synchronize()
+        assert bits_equal(out, ref), f"replay of batch {b}"
+        ids, _ = qre.route(dev, x)
+        host.plan(ids.cpu().reshape(-1).tolist())
+        assert tier.state() == host.state()
     tier.close()
