@@ -52,6 +52,10 @@ def parse():
                          "pinned host memory behind an HBM slot bank (prints its own JSON line)")
     ap.add_argument("--tier-fractions", default="1,0.75,0.5,0.25,0.125",
                     help="resident fractions n_slots / n_experts of the sweep")
+    ap.add_argument("--tier-stack", action="store_true",
+                    help="tiered layer stack with and without router look-ahead prefetch (prints its "
+                         "own JSON line)")
+    ap.add_argument("--stack-layers", type=int, default=4)
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one elementwise fp32 copy of this many MiB (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -328,6 +332,98 @@ def run_tier(qre, synth, torch, w, fractions, steps):
     return {"h2d_probe_GBps": probe, "sweep": sweep}
 
 
+def run_tier_stack(qre, synth, torch, w, n_layers, steps):
+    """A stack of n_layers tiered layers (one shared pinned store of routed
+    experts, a router per layer).  Synthetic residual stream: layer l + 1's
+    input is x_l + sigma * z_l.  With look-ahead, layer l + 1's experts are
+    prefetched from x_l (routed by layer l + 1's router) before layer l runs.
+    Measured per (routing, resident fraction, sigma, look-ahead, S)."""
+    import numpy as np
+    base = synth.make_layer(w, device="cuda")
+    E, H = w.n_experts, w.hidden
+
+    def pinned(t):
+        p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        p.copy_(t)
+        return p
+    routed = [qre.QBank(pinned(b.storage), pinned(b.scale_storage), b.bits) for b in (base.gate, base.up, base.down)]
+    shared = [qre.QBank(b.storage, b.scale_storage, b.bits) for b in (base.sh_gate, base.sh_up, base.sh_down)]
+    for b in (base.gate, base.up, base.down):
+        b.storage = b.scale_storage = None
+        b.data, b.scale = [], []
+    torch.cuda.empty_cache()
+    routers = []
+    for l in range(n_layers):
+        wl = synth.scaled(w, layer=f"{w.layer}/stack{l}")
+        routers.append(synth.router_weights(wl).cuda())
+    biases = {"uniform": [synth.router_bias(synth.scaled(w, layer=f"{w.layer}/stack{l}")).cuda()
+                          for l in range(n_layers)],
+              "zipf": [synth.router_bias(synth.scaled(w, layer=f"{w.layer}/stack{l}", bias_kind="zipf")).cuda()
+                       for l in range(n_layers)]}
+    gen = torch.Generator(device="cuda")
+    out = []
+    for S in (1, 4):
+        for sigma in (0.5, 1.0):
+            gen.manual_seed(1234 + S)
+            n_tok = steps + 64
+            xs = [torch.randn(n_tok, S, H, device="cuda", generator=gen)]
+            for l in range(1, n_layers):
+                xs.append(xs[-1] + sigma * torch.randn(n_tok, S, H, device="cuda", generator=gen))
+            for kind in ("uniform", "zipf"):
+                layers = [qre.MoELayer(H, w.inter, E, w.top_k, w.rsf, routers[l], biases[kind][l], *routed, shared)
+                          for l in range(n_layers)]
+                # recall of the look-ahead prediction over the timed tokens
+                hit = tot = 0
+                for l in range(n_layers - 1):
+                    xa = xs[l][64:].reshape(-1, H)
+                    pred, _ = qre.route(layers[l + 1], xa)
+                    act, _ = qre.route(layers[l + 1], xs[l + 1][64:].reshape(-1, H))
+                    pr, ac = pred.cpu().numpy(), act.cpu().numpy()
+                    for t in range(0, len(ac), S):
+                        a = set(ac[t:t + S].reshape(-1).tolist())
+                        b = set(pr[t:t + S].reshape(-1).tolist())
+                        hit += len(a & b)
+                        tot += len(a)
+                recall = hit / max(1, tot)
+                for f in (0.5, 0.75):
+                    n_slots = int(round(f * E))
+                    for look in (False, True):
+                        tiers = [qre.TieredLayer(layers[l], n_slots) for l in range(n_layers)]
+                        ws = tiers[0].workspace(S)
+                        o = torch.empty(S, H, device="cuda")
+
+                        def token(i):
+                            for l in range(n_layers):
+                                if look and l + 1 < n_layers:
+                                    tiers[l + 1].prefetch(xs[l][i])
+                                tiers[l].forward(xs[l][i], o, ws)
+                        for i in range(64):
+                            token(i)
+                        torch.cuda.synchronize()
+                        s0 = [t.stats() for t in tiers]
+                        t0 = time.perf_counter()
+                        for i in range(64, 64 + steps):
+                            token(i)
+                        torch.cuda.synchronize()
+                        dt = time.perf_counter() - t0
+                        s1 = [t.stats() for t in tiers]
+                        d = {k: sum(b[k] - a[k] for a, b in zip(s0, s1))
+                             for k in ("hits", "misses", "prefetch_loads")}
+                        out.append({"S": S, "sigma": sigma, "routing": kind, "resident_fraction": f,
+                                    "lookahead": look, "recall": recall,
+                                    "tokens_per_s": steps * S / dt,
+                                    "ms_per_layer": 1000.0 * dt / (steps * n_layers),
+                                    "expert_hit_rate": d["hits"] / max(1, d["hits"] + d["misses"]),
+                                    "loads_per_token_layer": (d["misses"] + d["prefetch_loads"]) / (steps * S * n_layers),
+                                    "prefetch_loads_per_token_layer": d["prefetch_loads"] / (steps * S * n_layers)})
+                        print(f"stack S={S} sigma={sigma} {kind} f={f} lookahead={look}: "
+                              f"{out[-1]['tokens_per_s']:.0f} tokens/s", file=sys.stderr, flush=True)
+                        for t in tiers:
+                            t.close()
+                        del tiers, ws
+    return out
+
+
 def cpu_baseline(synth, w, n_tokens):
     """The oracle, as it stands, on n_tokens tokens of the same workload."""
     import oracle
@@ -368,6 +464,18 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.workload]
+    if args.tier_stack:
+        steps = args.steps or 100
+        r = run_tier_stack(qre, synth, torch, w, args.stack_layers, steps)
+        print(json.dumps({
+            "metric": "tiered layer-stack decode tokens/sec with and without router look-ahead prefetch",
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "higher_is_better": True, "dtype": "int8",
+            "data": "synthetic (seeded weights; residual stream x_l+1 = x_l + sigma * z_l; no checkpoint)",
+            "config": {"workload": f"{args.stack_layers} layers of H={w.hidden} I={w.inter} E={w.n_experts} "
+                                   f"top-{w.top_k} int{w.bits}, one shared pinned expert store, a router per "
+                                   "layer", "expert_bytes": expert_bytes(w)},
+            "stack": r}), flush=True)
+        return
     if args.tier:
         fr = [float(v) for v in args.tier_fractions.split(",")]
         steps = args.steps or 300

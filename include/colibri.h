@@ -280,6 +280,8 @@ typedef struct coli_cache_stats {
     uint64_t misses;    /* per plan: distinct experts loaded, summed */
     uint64_t pin_loads; /* loads made by pinning */
     uint64_t passes;    /* summed over plans */
+    uint64_t prefetches;     /* successful look-ahead prefetches */
+    uint64_t prefetch_loads; /* loads made by them */
     int32_t resident;   /* slots holding an expert now */
     int32_t pinned;     /* slots pinned now */
 } coli_cache_stats;
@@ -323,6 +325,19 @@ void colibri_cache_unpin(coli_expert_cache* c);
  */
 int colibri_cache_plan(coli_expert_cache* c, const int32_t* ids, int32_t P, int32_t* pair_code,
                        coli_cache_load* loads, int32_t* pass_pairs, coli_cache_plan* plan);
+
+/*
+ * Look-ahead prefetch ([README] router look-ahead paragraph: the next
+ * layer's experts are predicted from the current layer's state and read
+ * ahead while the current layer computes).  ids [P] (host) are predicted
+ * routed ids.  As colibri_cache_plan, except: the ring is only the slots
+ * neither pinned nor holding a predicted expert, the misses beyond it are
+ * not loaded, and usage is not counted.  Writes loads [min(P, n_experts)]
+ * (pass 1, after -1) and *plan (n_pass 2 if anything is loaded, else 1;
+ * n_miss = n_load = loads made).  Counted in prefetches / prefetch_loads.
+ */
+int colibri_cache_prefetch(coli_expert_cache* c, const int32_t* ids, int32_t P, coli_cache_load* loads,
+                           coli_cache_plan* plan);
 
 int colibri_cache_stats(const coli_expert_cache* c, coli_cache_stats* st);
 
@@ -385,6 +400,19 @@ size_t colibri_tier_workspace_bytes(const coli_tier* t, int32_t S);
  */
 int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, void* ws,
                          size_t ws_bytes, coli_stream_t stream);
+
+/*
+ * Look-ahead prefetch of the tier's experts for activations x fp32
+ * [S][hidden] (S <= 8) that predict this layer's input, for instance the
+ * previous layer's input ([README] router look-ahead paragraph).  Everything
+ * runs on the tier's copy stream after the work enqueued on `stream` so far:
+ * route x with this layer's router (into the tier's own scratch), plan a
+ * prefetch on the state (colibri_cache_prefetch's policy), load the
+ * predicted misses.  Returns without waiting; the caller's stream is not
+ * delayed.  The tier's next forward waits for the prefetch before it plans.
+ * x must not be changed by work on `stream` enqueued before that forward.
+ */
+int colibri_tier_prefetch(coli_tier* t, const float* x, int32_t S, coli_stream_t stream);
 
 /* Statistics of the tier's cache (as colibri_cache_stats); waits for `stream`. */
 int colibri_tier_stats(const coli_tier* t, coli_cache_stats* st, coli_stream_t stream);

@@ -88,6 +88,8 @@ def lib():
                 ("colibri_cache_pin", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
                 ("colibri_cache_unpin", None, [_vp]),
                 ("colibri_cache_plan", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+                ("colibri_cache_prefetch", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
+                ("colibri_tier_prefetch", ctypes.c_int, [_vp, _vp, _i32, _vp]),
                 ("colibri_cache_stats", ctypes.c_int, [_vp, _vp]),
                 ("colibri_cache_state", ctypes.c_int, [_vp, _vp, _vp]),
                 ("colibri_tier_slot_bytes", ctypes.c_size_t, [_vp, _i32]),
@@ -272,7 +274,8 @@ class CachePlan(ctypes.Structure):
 class CacheStats(ctypes.Structure):
     """coli_cache_stats"""
     _fields_ = [("plans", _u64), ("pairs", _u64), ("hits", _u64), ("misses", _u64),
-                ("pin_loads", _u64), ("passes", _u64), ("resident", _i32), ("pinned", _i32)]
+                ("pin_loads", _u64), ("passes", _u64), ("prefetches", _u64), ("prefetch_loads", _u64),
+                ("resident", _i32), ("pinned", _i32)]
 
 
 def _i32_array(values):
@@ -344,6 +347,20 @@ class ExpertCache:
                 "pass_pairs": list(pp)[:plan.n_pass], "n_pass": plan.n_pass, "n_hit": plan.n_hit,
                 "n_miss": plan.n_miss}
 
+    def prefetch(self, ids: Sequence[int]) -> dict:
+        """Look-ahead prefetch of predicted ids -> loads (expert, slot, pass,
+        after) and the counts."""
+        P = len(ids)
+        m = min(P, self.n_experts)
+        arr = _i32_array(ids)
+        loads = (CacheLoad * max(m, 1))()
+        plan = CachePlan()
+        _check(lib().colibri_cache_prefetch(self._h, arr, P, loads, ctypes.byref(plan)),
+               "colibri_cache_prefetch")
+        return {"loads": [(loads[i].expert, loads[i].slot, loads[i].pass_, loads[i].after)
+                          for i in range(plan.n_load)],
+                "n_pass": plan.n_pass, "n_hit": plan.n_hit, "n_miss": plan.n_miss}
+
     def stats(self) -> dict:
         return _cache_stats(self._h)
 
@@ -400,6 +417,11 @@ class TieredLayer:
         _check(lib().colibri_tier_forward(self._h, _ptr(x), S, _ptr(out), _ptr(ws), ws.numel(),
                                           _stream()), "colibri_tier_forward")
         return out
+
+    def prefetch(self, x: torch.Tensor):
+        """Look-ahead prefetch for activations x (S <= 8 tokens) predicting
+        this layer's input; runs on the tier's copy stream."""
+        _check(lib().colibri_tier_prefetch(self._h, _ptr(x), x.shape[0], _stream()), "colibri_tier_prefetch")
 
     def stats(self) -> dict:
         st = CacheStats()

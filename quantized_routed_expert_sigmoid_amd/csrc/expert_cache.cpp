@@ -12,7 +12,8 @@ namespace coli {
 
 ExpertCache::ExpertCache(int32_t n_experts, int32_t n_slots)
     : E_(n_experts), n_slots_(n_slots), slot_of_(n_experts, -1), expert_in_(n_slots, -1),
-      pinned_(n_slots, 0), last_use_(n_slots, 0), usage_(n_experts, 0), ready_(n_slots, -1),
+      pinned_(n_slots, 0), last_use_(n_slots, 0), usage_(n_experts, 0), inflight_(n_slots, 0),
+      ready_(n_slots, -1),
       first_(n_experts, -1), used_(n_experts, 0), excl_(n_slots, 0)
 {
     order_.reserve(n_experts);
@@ -102,6 +103,7 @@ void ExpertCache::reset()
     std::fill(slot_of_.begin(), slot_of_.end(), -1);
     std::fill(expert_in_.begin(), expert_in_.end(), -1);
     std::fill(last_use_.begin(), last_use_.end(), 0);
+    std::fill(inflight_.begin(), inflight_.end(), 0);
     unpin();
 }
 
@@ -126,7 +128,7 @@ int ExpertCache::plan(const int32_t* ids, int32_t P, int32_t* pair_code, coli_ca
     }
 
     /* hits run in pass 0 from the slot they hold */
-    int32_t n_hit = 0, n_miss = 0;
+    int32_t n_hit = 0, n_miss = 0, n_late = 0;
     for (const int32_t e : order_) {
         const int32_t s = slot_of_[e];
         if (s >= 0) {
@@ -142,11 +144,21 @@ int ExpertCache::plan(const int32_t* ids, int32_t P, int32_t* pair_code, coli_ca
     }
 
     /* victim ring: free slots in LRU order, then unpinned hit slots (ready
-     * once pass 0 has finished) */
+     * once pass 0 has finished).  When the misses fit the free slots, a hit
+     * whose slot a prefetch may still be filling (a late hit) runs in pass 1,
+     * which follows every load, and its slot stays out of the ring. */
     victims(excl_, ring_);
     const int32_t n_free = (int32_t)ring_.size();
+    if (n_miss <= n_free) {
+        for (const int32_t e : order_)
+            if (used_[e] == 2 && inflight_[first_[e]]) {
+                excl_[first_[e]] = 2;
+                pass_of_[e] = 1;
+                ++n_late;
+            }
+    }
     for (int32_t s = 0; s < n_slots_; ++s)
-        if (excl_[s] && !pinned_[s])
+        if (excl_[s] == 1 && !pinned_[s])
             ring_.push_back(s);
     const int32_t R = (int32_t)ring_.size();
     for (int32_t i = 0; i < R; ++i)
@@ -179,8 +191,11 @@ int ExpertCache::plan(const int32_t* ids, int32_t P, int32_t* pair_code, coli_ca
         }
         n_pass = 1 + (n_miss + c - 1) / c;
     }
+    if (n_late > 0 && n_pass < 2)
+        n_pass = 2;
 
     if (st == COLI_OK) {
+        std::fill(inflight_.begin(), inflight_.end(), 0);
         std::fill(pass_pairs, pass_pairs + n_pass, 0);
         int64_t kept = 0;
         for (int32_t p = 0; p < P; ++p) {
@@ -209,6 +224,58 @@ int ExpertCache::plan(const int32_t* ids, int32_t P, int32_t* pair_code, coli_ca
         first_[e] = -1;
     }
     return st;
+}
+
+int ExpertCache::prefetch(const int32_t* ids, int32_t P, coli_cache_load* loads, coli_cache_plan* out)
+{
+    if (P < 0 || !out || !loads || (P > 0 && !ids))
+        return COLI_E_INVAL;
+    for (int32_t p = 0; p < P; ++p)
+        if (ids[p] >= E_)
+            return COLI_E_INVAL;
+    ++tick_;
+    order_.clear();
+    for (int32_t p = 0; p < P; ++p) {
+        const int32_t e = ids[p];
+        if (e >= 0 && !used_[e]) {
+            used_[e] = 1;
+            order_.push_back(e);
+        }
+    }
+    int32_t n_hit = 0;
+    for (const int32_t e : order_) {
+        const int32_t s = slot_of_[e];
+        if (s >= 0) {
+            used_[e] = 2;
+            excl_[s] = 1;
+            last_use_[s] = tick_;
+            ++n_hit;
+        }
+    }
+    /* only the free slots: no slot of a predicted expert is given up */
+    victims(excl_, ring_);
+    for (const int32_t e : order_)
+        if (used_[e] == 2)
+            excl_[slot_of_[e]] = 0;
+    const int32_t R = (int32_t)ring_.size();
+    int32_t n_load = 0;
+    for (const int32_t e : order_) {
+        if (used_[e] == 2 || n_load >= R)
+            continue;
+        loads[n_load] = coli_cache_load{e, ring_[n_load], 1, -1};
+        place(e, ring_[n_load]);
+        inflight_[ring_[n_load]] = 1;
+        ++n_load;
+    }
+    for (const int32_t e : order_)
+        used_[e] = 0;
+    out->n_pass = n_load ? 2 : 1;
+    out->n_load = n_load;
+    out->n_hit = n_hit;
+    out->n_miss = n_load;
+    ++st_.prefetches;
+    st_.prefetch_loads += (uint64_t)n_load;
+    return COLI_OK;
 }
 
 void ExpertCache::stats(coli_cache_stats* st) const
@@ -268,6 +335,16 @@ int colibri_cache_plan(coli_expert_cache* c, const int32_t* ids, int32_t P, int3
     if ((int64_t)P > COLI_MAX_PAIRS)
         return COLI_E_UNSUPPORTED;
     return c->plan(ids, P, pair_code, loads, pass_pairs, plan);
+}
+
+int colibri_cache_prefetch(coli_expert_cache* c, const int32_t* ids, int32_t P, coli_cache_load* loads,
+                           coli_cache_plan* plan)
+{
+    if (!c)
+        return COLI_E_INVAL;
+    if ((int64_t)P > COLI_MAX_PAIRS)
+        return COLI_E_UNSUPPORTED;
+    return c->prefetch(ids, P, loads, plan);
 }
 
 int colibri_cache_stats(const coli_expert_cache* c, coli_cache_stats* st)

@@ -36,6 +36,9 @@ public:
     int plan(const int32_t* ids, int32_t P, int32_t* pair_code, coli_cache_load* loads,
              int32_t* pass_pairs, coli_cache_plan* out);
 
+    /* See colibri_cache_prefetch. */
+    int prefetch(const int32_t* ids, int32_t P, coli_cache_load* loads, coli_cache_plan* out);
+
     void stats(coli_cache_stats* st) const;
 
     int32_t n_experts() const { return E_; }
@@ -55,6 +58,7 @@ private:
     std::vector<uint8_t> pinned_;    /* [n_slots] */
     std::vector<uint64_t> last_use_; /* [n_slots]: plan tick of the last use */
     std::vector<uint64_t> usage_;    /* [E]: routed pairs so far */
+    std::vector<uint8_t> inflight_;  /* [n_slots]: loaded by a prefetch no plan has consumed */
     uint64_t tick_ = 0;
     int32_t n_pinned_ = 0;
     coli_cache_stats st_ = {};

@@ -212,9 +212,9 @@ hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
 constexpr int kTierMaxE = 1024; /* experts and slots */
 
 struct TierHdr {
-    uint32_t tick; /* plans and pins so far (the LRU clock) */
+    uint32_t tick; /* plans, prefetches and pins so far (the LRU clock) */
     int32_t pad;
-    unsigned long long plans, pairs, hits, misses, pin_loads, passes;
+    unsigned long long plans, pairs, hits, misses, pin_loads, passes, prefetches, prefetch_loads;
 };
 
 struct TierState {
@@ -223,6 +223,7 @@ struct TierState {
     int32_t* expert_in;        /* [n]: expert or -1 */
     uint32_t* last_use;        /* [n]: tick of the last use */
     int32_t* pinned;           /* [n] */
+    int32_t* inflight;         /* [n]: loaded by a prefetch that no plan has consumed */
     unsigned long long* usage; /* [E]: routed pairs */
     int32_t E, n;
 };
@@ -244,9 +245,13 @@ hipError_t launch_tier_init(const TierState& st, hipStream_t s);
 
 /* Plans P routed ids (ids >= E or < 0 count as dropped): codes [P], loads
  * [min(P, E)] {expert, slot, pass, after}, info [kInfoN], pass_pairs
- * [min(P, E) + 1]; updates the state. */
+ * [min(P, E) + 1]; updates the state.  With `prefetch` set it plans a
+ * look-ahead instead: the misses that fit the free slots are loaded in pass
+ * 1, usage is not counted, and codes / pass_pairs are not written (may be
+ * null). */
 hipError_t launch_tier_plan(const int32_t* ids, int32_t P, const TierState& st, int32_t* codes,
-                            int4* loads, int32_t* info, int32_t* pass_pairs, hipStream_t s);
+                            int4* loads, int32_t* info, int32_t* pass_pairs, bool prefetch,
+                            hipStream_t s);
 
 /* Pins n experts (validated by the host): loads [n] and info as for a plan
  * whose single miss pass is pass 1. */

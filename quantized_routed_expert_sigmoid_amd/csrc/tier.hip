@@ -50,7 +50,8 @@ size_t row_bytes(int32_t K, int32_t qtype)
  * scratch. */
 struct SlotLayout {
     size_t reg[6];
-    size_t hdr, slot_of, expert_in, last_use, pinned, usage, pin_experts, pin_loads, pin_info, total;
+    size_t hdr, slot_of, expert_in, last_use, pinned, inflight, usage, pin_experts, pin_loads, pin_info, pf_loads,
+        pf_info, pf_logits, pf_xq, pf_xd, pf_ids, pf_w, total;
 };
 
 SlotLayout slot_layout(const coli_moe_layer* L, int32_t n)
@@ -69,10 +70,19 @@ SlotLayout slot_layout(const coli_moe_layer* L, int32_t n)
     s.expert_in = b.take((size_t)n * 4);
     s.last_use = b.take((size_t)n * 4);
     s.pinned = b.take((size_t)n * 4);
+    s.inflight = b.take((size_t)n * 4);
     s.usage = b.take((size_t)E * 8);
     s.pin_experts = b.take((size_t)kTierMaxE * 4);
     s.pin_loads = b.take((size_t)kTierMaxE * 16);
     s.pin_info = b.take((size_t)kInfoN * 4);
+    s.pf_loads = b.take((size_t)kTierMaxE * 16);
+    s.pf_info = b.take((size_t)kInfoN * 4);
+    /* the prefetch's own routing scratch, up to kSmallS tokens */
+    s.pf_logits = b.take((size_t)kSmallS * E * 4);
+    s.pf_xq = b.take((size_t)kSmallS * H);
+    s.pf_xd = b.take((size_t)kSmallS * (H / 32) * 4);
+    s.pf_ids = b.take((size_t)kSmallS * L->top_k * 4);
+    s.pf_w = b.take((size_t)kSmallS * L->top_k * 4);
     s.total = b.at;
     return s;
 }
@@ -148,6 +158,17 @@ struct coli_tier {
     int32_t* pin_experts = nullptr; /* device */
     int4* pin_loads = nullptr;
     int32_t* pin_info = nullptr;
+    int4* pf_loads = nullptr;       /* device: the last prefetch's plan */
+    int32_t* pf_info = nullptr;
+    float* pf_logits = nullptr;     /* device: the prefetch's routing scratch */
+    int8_t* pf_xq = nullptr;
+    float* pf_xd = nullptr;
+    int32_t* pf_ids = nullptr;
+    float* pf_w = nullptr;
+    hipEvent_t ev_issue = nullptr;    /* the caller's stream when a prefetch was issued */
+    hipEvent_t ev_pfplan = nullptr;   /* after the last prefetch's plan */
+    hipEvent_t ev_prefetch = nullptr; /* after the last prefetch's fetch */
+    bool prefetch_pending = false;    /* a prefetch fetch no forward has waited for */
     int32_t* h_buf = nullptr;       /* pinned host staging */
     size_t h_cap = 0;               /* int32 entries */
 
@@ -165,6 +186,12 @@ struct coli_tier {
             (void)hipEventDestroy(ev_plan);
         if (ev_d2h)
             (void)hipEventDestroy(ev_d2h);
+        if (ev_prefetch)
+            (void)hipEventDestroy(ev_prefetch);
+        if (ev_issue)
+            (void)hipEventDestroy(ev_issue);
+        if (ev_pfplan)
+            (void)hipEventDestroy(ev_pfplan);
         if (h_buf)
             (void)hipHostFree(h_buf);
     }
@@ -262,6 +289,42 @@ hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const in
     return e;
 }
 
+/* Quantise + router + selection (the resident forward's kernels). */
+hipError_t route_into(const coli_tier* t, const float* x, int32_t S, int8_t* xq, float* xd, float* logits,
+                      int32_t* ids, float* w, hipStream_t s)
+{
+    const coli_moe_layer* L = &t->L;
+    const int32_t H = L->hidden, E = L->n_experts, k = L->top_k;
+    hipError_t e = S <= kSmallS ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
+                                : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
+    if (e == hipSuccess && S > kSmallS)
+        e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
+    if (e == hipSuccess)
+        e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
+                                 L->routed_scaling_factor, route_opts(L), ids, w, s);
+    return e;
+}
+
+/* Argument checks shared by the forward and the prefetch. */
+int check_call(const coli_tier* t, const float* x, int32_t S, const float* out, bool need_out, void* ws,
+               size_t ws_bytes)
+{
+    if (!t)
+        return COLI_E_INVAL;
+    int st = check_tokens(S, t->L.top_k);
+    if (st || S == 0)
+        return st;
+    if (!x || (need_out && !out) || !ws)
+        return COLI_E_INVAL;
+    if (!aligned(x, 16) || (need_out && !aligned(out, 16)) || !aligned(ws, kAlign))
+        return COLI_E_UNSUPPORTED;
+    if ((st = check_current_device(t)))
+        return st;
+    if (ws_bytes < tier_layout(&t->L, S).total)
+        return COLI_E_WORKSPACE;
+    return COLI_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -323,12 +386,20 @@ int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem
     t->st.expert_in = at<int32_t>(slot_mem, sl.expert_in);
     t->st.last_use = at<uint32_t>(slot_mem, sl.last_use);
     t->st.pinned = at<int32_t>(slot_mem, sl.pinned);
+    t->st.inflight = at<int32_t>(slot_mem, sl.inflight);
     t->st.usage = at<unsigned long long>(slot_mem, sl.usage);
     t->st.E = L->n_experts;
     t->st.n = n_slots;
     t->pin_experts = at<int32_t>(slot_mem, sl.pin_experts);
     t->pin_loads = at<int4>(slot_mem, sl.pin_loads);
     t->pin_info = at<int32_t>(slot_mem, sl.pin_info);
+    t->pf_loads = at<int4>(slot_mem, sl.pf_loads);
+    t->pf_info = at<int32_t>(slot_mem, sl.pf_info);
+    t->pf_logits = at<float>(slot_mem, sl.pf_logits);
+    t->pf_xq = at<int8_t>(slot_mem, sl.pf_xq);
+    t->pf_xd = at<float>(slot_mem, sl.pf_xd);
+    t->pf_ids = at<int32_t>(slot_mem, sl.pf_ids);
+    t->pf_w = at<float>(slot_mem, sl.pf_w);
 
     hipError_t e = hipGetDevice(&t->device);
     if (e == hipSuccess)
@@ -337,6 +408,12 @@ int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem
         e = hipEventCreateWithFlags(&t->ev_plan, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&t->ev_d2h, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&t->ev_prefetch, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&t->ev_issue, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&t->ev_pfplan, hipEventDisableTiming);
     if (e == hipSuccess)
         e = t->events(2);
     if (e == hipSuccess)
@@ -377,7 +454,10 @@ int colibri_tier_pin(coli_tier* t, const int32_t* experts, int32_t n, coli_strea
     if (!(total <= t->n_slots - 1 || (total == E && t->n_slots == E)))
         return COLI_E_UNSUPPORTED; /* a slot has to stay free for misses */
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = t->staging((size_t)n);
+    /* a pending prefetch may still be filling slots the pins take */
+    hipError_t e = t->prefetch_pending ? hipStreamWaitEvent(s, t->ev_prefetch, 0) : hipSuccess;
+    if (e == hipSuccess)
+        e = t->staging((size_t)n);
     if (e == hipSuccess) {
         for (int32_t i = 0; i < n; ++i)
             t->h_buf[i] = experts[i];
@@ -404,26 +484,52 @@ size_t colibri_tier_workspace_bytes(const coli_tier* t, int32_t S)
     return tier_layout(&t->L, S).total;
 }
 
+int colibri_tier_prefetch(coli_tier* t, const float* x, int32_t S, coli_stream_t stream)
+{
+    if (!t || S < 0)
+        return COLI_E_INVAL;
+    if (S == 0)
+        return COLI_OK;
+    if (S > kSmallS)
+        return COLI_E_UNSUPPORTED;
+    if (!x)
+        return COLI_E_INVAL;
+    if (!aligned(x, 16))
+        return COLI_E_UNSUPPORTED;
+    int st = check_current_device(t);
+    if (st)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    /* everything runs on the copy stream, after what the caller has
+     * enqueued so far (earlier forwards of this tier included) and after the
+     * previous prefetch (same stream) */
+    hipError_t e = hipEventRecord(t->ev_issue, s);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(t->copy, t->ev_issue, 0);
+    if (e == hipSuccess)
+        e = route_into(t, x, S, t->pf_xq, t->pf_xd, t->pf_logits, t->pf_ids, t->pf_w, t->copy);
+    if (e == hipSuccess)
+        e = launch_tier_plan(t->pf_ids, S * t->L.top_k, t->st, nullptr, t->pf_loads, t->pf_info, nullptr, true,
+                             t->copy);
+    if (e == hipSuccess)
+        e = hipEventRecord(t->ev_pfplan, t->copy);
+    if (e == hipSuccess)
+        e = launch_tier_fetch(t->pf_loads, t->pf_info, 1, t->banks, t->copy);
+    if (e == hipSuccess)
+        e = hipEventRecord(t->ev_prefetch, t->copy);
+    if (e == hipSuccess)
+        t->prefetch_pending = true;
+    return hip_status(e);
+}
+
 int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, void* ws, size_t ws_bytes,
                          coli_stream_t stream)
 {
-    if (!t)
-        return COLI_E_INVAL;
+    int st = check_call(t, x, S, out, true, ws, ws_bytes);
+    if (st || S == 0)
+        return st;
     const coli_moe_layer* L = &t->L;
-    int st = check_tokens(S, L->top_k);
-    if (st)
-        return st;
-    if (S == 0)
-        return COLI_OK;
-    if (!x || !out || !ws)
-        return COLI_E_INVAL;
-    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, kAlign))
-        return COLI_E_UNSUPPORTED;
-    if ((st = check_current_device(t)))
-        return st;
     const TierLayout Lo = tier_layout(L, S);
-    if (ws_bytes < Lo.total)
-        return COLI_E_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const int32_t H = L->hidden, E = L->n_experts, k = L->top_k;
     const int32_t P = S * k, m = P < E ? P : E;
@@ -432,9 +538,6 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
      * every expert of the batch */
     const bool all_pinned = t->n_pinned == E;
     const bool two_passes = all_pinned || t->n_slots - t->n_pinned >= m;
-    int8_t* xq = at<int8_t>(ws, Lo.l.xq);
-    float* xd = at<float>(ws, Lo.l.xd);
-    float* logits = at<float>(ws, Lo.l.logits);
     int32_t* ids = at<int32_t>(ws, Lo.l.ids);
     float* w = at<float>(ws, Lo.l.w);
     int32_t* codes = at<int32_t>(ws, Lo.codes);
@@ -447,16 +550,20 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
     if (e != hipSuccess)
         return COLI_E_HIP;
 
-    /* 1-2. route and plan */
-    e = S <= kSmallS ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
-                     : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
-    if (e == hipSuccess && S > kSmallS)
-        e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
+    /* 1-2. route and plan, the plan after a pending prefetch's plan.  With
+     * two passes the misses always fit the free slots, so the slots the
+     * prefetch is still filling are late hits, read only in pass 1, which
+     * follows the copy stream's loads; otherwise wait for the whole
+     * prefetch */
+    if (t->prefetch_pending) {
+        e = hipStreamWaitEvent(s, two_passes ? t->ev_pfplan : t->ev_prefetch, 0);
+        t->prefetch_pending = false;
+    }
     if (e == hipSuccess)
-        e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
-                                 L->routed_scaling_factor, route_opts(L), ids, w, s);
+        e = route_into(t, x, S, at<int8_t>(ws, Lo.l.xq), at<float>(ws, Lo.l.xd), at<float>(ws, Lo.l.logits),
+                       ids, w, s);
     if (e == hipSuccess)
-        e = launch_tier_plan(ids, P, t->st, codes, loads, info, pass_pairs, s);
+        e = launch_tier_plan(ids, P, t->st, codes, loads, info, pass_pairs, false, s);
     int32_t* h_info = t->h_buf;
     int32_t* h_pp = two_passes ? nullptr : h_info + kInfoN;
     int4* h_loads = two_passes ? nullptr : reinterpret_cast<int4*>(h_pp + (m + 1));
@@ -555,6 +662,8 @@ int colibri_tier_stats(const coli_tier* t, coli_cache_stats* out, coli_stream_t 
     out->misses = h.misses;
     out->pin_loads = h.pin_loads;
     out->passes = h.passes;
+    out->prefetches = h.prefetches;
+    out->prefetch_loads = h.prefetch_loads;
     out->resident = 0;
     for (const int32_t v : ein)
         out->resident += v >= 0 ? 1 : 0;

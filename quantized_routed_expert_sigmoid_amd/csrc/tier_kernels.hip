@@ -19,6 +19,14 @@
  *     when i >= R, for pass 0 when its slot held a hit, else for nothing;
  *   - each ring slot ends up holding its last miss; the occupant it held
  *     before the plan (a hit included) is evicted.
+ * A look-ahead prefetch (the same page's router look-ahead paragraph: the
+ * next layer's experts are predicted from the current state and read ahead)
+ * plans the same way with two differences: the ring is the free slots only
+ * (no slot of an expert the prediction also names is given up), and the
+ * misses beyond it are not loaded; usage is not counted.  The slots a
+ * prefetch loads are marked in flight.  When a plan's misses fit its free
+ * slots, a hit on such a slot (a late hit) runs in pass 1, after every load,
+ * and the slot stays out of the ring; every plan clears the marks.
  * A workgroup of 1024 threads holds one expert and one slot per thread
  * (both at most 1024).  Ranks are counts over LDS arrays, so every result
  * is independent of thread timing.
@@ -44,6 +52,7 @@ __global__ __launch_bounds__(256) void tier_init_kernel(TierState st)
         st.expert_in[i] = -1;
         st.last_use[i] = 0;
         st.pinned[i] = 0;
+        st.inflight[i] = 0;
     }
     if (i == 0) {
         TierHdr h = {};
@@ -70,7 +79,8 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
                                                                  TierState st, int32_t* __restrict__ codes,
                                                                  int4* __restrict__ loads,
                                                                  int32_t* __restrict__ info,
-                                                                 int32_t* __restrict__ pass_pairs)
+                                                                 int32_t* __restrict__ pass_pairs,
+                                                                 int32_t prefetch)
 {
     __shared__ int32_t first[kTierMaxE];  /* first pair of each expert; INT_MAX: absent */
     __shared__ int32_t mfirst[kTierMaxE]; /* the same, misses only */
@@ -80,7 +90,8 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
     __shared__ int32_t miss_e[kTierMaxE]; /* expert of each miss rank */
     __shared__ int32_t ring[kTierMaxE];
     __shared__ unsigned long long key[kTierMaxE];
-    __shared__ uint8_t uh[kTierMaxE];     /* unpinned slot holding a hit */
+    __shared__ uint8_t hs[kTierMaxE];     /* slot holding a hit: 1 unpinned, 3 pinned */
+    __shared__ uint8_t lt[kTierMaxE];     /* slot filled by a prefetch (in flight) */
     __shared__ int32_t pcnt[kTierMaxE + 1];
     __shared__ int32_t kept;
 
@@ -90,7 +101,8 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
     first[tid] = INT_MAX;
     mfirst[tid] = INT_MAX;
     ucnt[tid] = 0;
-    uh[tid] = 0;
+    hs[tid] = 0;
+    lt[tid] = 0;
     pcnt[tid] = 0;
     if (tid == 0) {
         pcnt[kTierMaxE] = 0;
@@ -114,23 +126,31 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
     const bool miss = present && !hit;
     if (miss)
         mfirst[e] = first[e];
-    if (hit && !st.pinned[s_hit])
-        uh[s_hit] = 1;
+    if (hit) {
+        hs[s_hit] = st.pinned[s_hit] ? 3 : 1;
+        lt[s_hit] = (!prefetch && st.inflight[s_hit] != 0) ? 1 : 0;
+    }
     __syncthreads();
-    bool cand = false, is_uh = false;
+    bool cand = false;
     unsigned long long k = ~0ull;
     if (s < n) {
-        is_uh = uh[s] != 0;
-        cand = !st.pinned[s] && !is_uh;
+        cand = hs[s] == 0 && !st.pinned[s];
         if (cand)
             k = victim_key(st.expert_in[s], st.last_use[s], s);
     }
     key[s] = k;
     const int32_t n_free = __syncthreads_count(cand);
-    const int32_t n_uh = __syncthreads_count(is_uh);
     const int32_t n_hit = __syncthreads_count(hit);
-    const int32_t n_miss = __syncthreads_count(miss);
+    const int32_t n_miss_all = __syncthreads_count(miss);
+    /* late hits only when the misses fit the free slots */
+    const bool honor = !prefetch && n_miss_all <= n_free;
+    const bool late = hit && honor && lt[s_hit] != 0;
+    const bool is_uh = !prefetch && s < n && hs[s] == 1 && !(honor && lt[s] != 0);
+    const int32_t n_uh = __syncthreads_count(is_uh);
+    const int32_t n_late = __syncthreads_count(late);
     const int32_t R = n_free + n_uh;
+    /* a prefetch loads only the misses that fit the free slots */
+    const int32_t n_miss = prefetch ? min(n_miss_all, R) : n_miss_all;
     int32_t mrank = 0;
     if (cand) {
         int32_t r = 0;
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
     if (is_uh) {
         int32_t r = 0;
         for (int t = 0; t < s; ++t)
-            r += uh[t];
+            r += (hs[t] == 1 && !(honor && lt[t] != 0)) ? 1 : 0;
         ring[n_free + r] = s;
     }
     if (miss) {
@@ -156,24 +176,27 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
     const bool error = n_miss > 0 && R == 0;
     const int32_t c = error ? 1 : (n_miss <= R ? (n_miss > 0 ? n_miss : 1) : max(1, R / 2));
     if (!error) {
-        if (miss) {
+        if (miss && mrank < n_miss) {
             const int32_t i = mrank, pass = 1 + i / c, r = i % R, slot = ring[r];
             const int32_t after = i < R ? (r < n_free ? -1 : 0) : 1 + (i - R) / c;
             loads[i] = make_int4(e, slot, pass, after);
             pass_of[e] = pass;
             slot_at[e] = slot;
         } else if (hit) {
-            pass_of[e] = 0;
+            pass_of[e] = late ? 1 : 0;
             slot_at[e] = s_hit;
         }
     }
     __syncthreads();
 
     /* state: hits are used now; each ring slot that took misses keeps the
-     * last one and evicts what it held before */
+     * last one and evicts what it held before; a prefetch marks its loads in
+     * flight, a plan consumes every mark */
     if (!error) {
         if (hit)
             st.last_use[s_hit] = tick;
+        if (!prefetch && tid < n)
+            st.inflight[tid] = 0;
         const int r = tid;
         if (r < R && r < n_miss) {
             const int32_t slot = ring[r];
@@ -184,9 +207,11 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
             st.slot_of[en] = slot;
             st.expert_in[slot] = en;
             st.last_use[slot] = tick;
+            if (prefetch)
+                st.inflight[slot] = 1;
         }
     }
-    for (int32_t p = tid; p < P; p += kPlanThreads) {
+    for (int32_t p = tid; p < P && !prefetch; p += kPlanThreads) {
         const int32_t ep = ids[p];
         int32_t code = -1;
         if (!error && ep >= 0 && ep < E) {
@@ -195,13 +220,15 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
         }
         codes[p] = code;
     }
-    if (present && !error) {
+    if (present && !error && !prefetch) {
         st.usage[e] += (unsigned long long)ucnt[e];
         atomicAdd(&kept, ucnt[e]);
     }
     __syncthreads();
-    const int32_t n_pass = (error || n_miss == 0) ? 1 : 1 + (n_miss + c - 1) / c;
-    for (int j = tid; j < n_pass; j += kPlanThreads)
+    int32_t n_pass = (error || n_miss == 0) ? 1 : 1 + (n_miss + c - 1) / c;
+    if (!error && n_late > 0 && n_pass < 2)
+        n_pass = 2;
+    for (int j = tid; j < n_pass && !prefetch; j += kPlanThreads)
         pass_pairs[j] = pcnt[j];
     if (tid == 0) {
         info[kInfoPass] = n_pass;
@@ -214,21 +241,26 @@ __global__ __launch_bounds__(kPlanThreads) void tier_plan_kernel(const int32_t* 
         if (!error) {
             TierHdr h = *st.hdr;
             h.tick = tick;
-            h.plans += 1;
-            h.pairs += (unsigned long long)kept;
-            h.hits += (unsigned long long)n_hit;
-            h.misses += (unsigned long long)n_miss;
-            h.passes += (unsigned long long)n_pass;
+            if (prefetch) {
+                h.prefetches += 1;
+                h.prefetch_loads += (unsigned long long)n_miss;
+            } else {
+                h.plans += 1;
+                h.pairs += (unsigned long long)kept;
+                h.hits += (unsigned long long)n_hit;
+                h.misses += (unsigned long long)n_miss;
+                h.passes += (unsigned long long)n_pass;
+            }
             *st.hdr = h;
         }
     }
 }
 
 hipError_t launch_tier_plan(const int32_t* ids, int32_t P, const TierState& st, int32_t* codes, int4* loads,
-                            int32_t* info, int32_t* pass_pairs, hipStream_t s)
+                            int32_t* info, int32_t* pass_pairs, bool prefetch, hipStream_t s)
 {
     hipLaunchKernelGGL(tier_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, ids, P, st, codes, loads, info,
-                       pass_pairs);
+                       pass_pairs, prefetch ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ class ModelCache:
         self.expert_in = [-1] * n
         self.last = [0] * n
         self.pinned = [False] * n
+        self.inflight = [False] * n
         self.tick = 0
 
     def slot_of(self, e):
@@ -73,10 +74,13 @@ class ModelCache:
                 self.last[s] = self.tick
         misses = [e for e in order if e not in hits]
         free = self.victims(set(hits.values()))
-        ring = free + sorted(s for s in hits.values() if not self.pinned[s])
+        # when the misses fit the free slots, a hit on a slot a prefetch
+        # filled (late) runs in pass 1 and stays out of the ring
+        late = {e for e, s in hits.items() if self.inflight[s]} if len(misses) <= len(free) else set()
+        ring = free + sorted(s for e, s in hits.items() if not self.pinned[s] and e not in late)
         ready = [-1] * len(free) + [0] * (len(ring) - len(free))
         R, m = len(ring), len(misses)
-        where = {e: (0, s) for e, s in hits.items()}
+        where = {e: (1 if e in late else 0, s) for e, s in hits.items()}
         loads = []
         n_pass = 1
         if m:
@@ -88,12 +92,33 @@ class ModelCache:
                 self.place(e, ring[r])
                 where[e] = (p, ring[r])
             n_pass = 1 + (m + c - 1) // c
+        if late:
+            n_pass = max(n_pass, 2)
+        self.inflight = [False] * self.n
         codes = [-1 if e < 0 else (where[e][0] << B) | where[e][1] for e in ids]
         pp = [0] * n_pass
         for e in ids:
             if e >= 0:
                 pp[where[e][0]] += 1
         return codes, loads, pp
+
+    def prefetch(self, ids):
+        self.tick += 1
+        order = list(dict.fromkeys(e for e in ids if e >= 0))
+        hits = {}
+        for e in order:
+            s = self.slot_of(e)
+            if s >= 0:
+                hits[e] = s
+                self.last[s] = self.tick
+        free = self.victims(set(hits.values()))
+        misses = [e for e in order if e not in hits]
+        loads = []
+        for e, s in zip(misses, free):
+            self.place(e, s)
+            self.inflight[s] = True
+            loads.append((e, s, 1, -1))
+        return loads
 
     def slot_map(self):
         m = [-1] * self.E
@@ -303,3 +328,49 @@ def test_stats_accumulate():
         (len(batches), hits, misses, passes, pairs)
     _, usage = c.state()
     assert sum(usage) == pairs
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefetch_matches_model(seed):
+    """Look-ahead prefetches interleaved with plans: same loads and slot map
+    as the model; a prefetch never gives up the slot of a predicted expert or
+    a pinned one, never counts usage, and a plan of the predicted batch right
+    after it finds every prefetched expert resident."""
+    rng = random.Random(500 + seed)
+    E = rng.choice([8, 16, 64, 256])
+    n_slots = rng.randint(2, E)
+    c = q.ExpertCache(E, n_slots)
+    m = ModelCache(E, n_slots)
+    if seed % 2:
+        pins = rng.sample(range(E), rng.randint(1, n_slots - 1))
+        assert c.pin(pins) == m.pin(pins)
+    pinned_slots = {s for s in range(n_slots) if m.pinned[s]}
+    for ids in random_batches(rng, E, 30, 24, hot=rng.sample(range(E), max(1, E // 8))):
+        if rng.random() < 0.5:
+            before, usage_before = c.state()
+            st_before = c.stats()
+            r = c.prefetch(ids)
+            loads = m.prefetch(ids)
+            assert r["loads"] == loads
+            assert all(s not in pinned_slots for _, s, _, _ in loads)
+            predicted = {e for e in ids if e >= 0}
+            for e, s in enumerate(before):
+                if e in predicted and s >= 0:
+                    assert c.state()[0][e] == s, "a predicted resident expert kept its slot"
+            assert c.state()[1] == usage_before
+            st = c.stats()
+            assert st["prefetches"] == st_before["prefetches"] + 1
+            assert st["prefetch_loads"] == st_before["prefetch_loads"] + len(loads)
+            assert st["plans"] == st_before["plans"]
+            if len(predicted) <= n_slots - len(pinned_slots):
+                # a plan of the predicted batch right after the prefetch: no
+                # misses, the prefetched experts as late hits in pass 1
+                r2 = c.plan(ids)
+                codes, _, pp = m.plan(ids)
+                assert r2["n_miss"] == 0 and r2["codes"] == codes and r2["pass_pairs"] == pp
+                assert r2["n_pass"] == (2 if loads else 1)
+        else:
+            res = c.plan(ids)
+            codes, loads, pp = m.plan(ids)
+            assert (res["codes"], res["loads"], res["pass_pairs"]) == (codes, loads, pp)
+        assert c.state()[0] == m.slot_map()

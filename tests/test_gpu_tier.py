@@ -225,3 +225,39 @@ def test_tier_forward_in_a_graph(qre):
         host.plan(ids.cpu().reshape(-1).tolist())
         assert tier.state() == host.state()
     tier.close()
+
+
+@pytest.mark.parametrize("n_slots", [16, 40])
+def test_tier_prefetch_then_forward(qre, n_slots):
+    """Look-ahead prefetches before forwards: outputs stay the resident
+    forward's bit for bit, the device state follows the host planner's
+    prefetch and plan, and a perfectly predicted batch finds everything
+    resident (no misses in its plan)."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["decode_int4"])
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    tier = qre.TieredLayer(to_slow_tier(L, dev), n_slots)
+    host = qre.ExpertCache(w.n_experts, n_slots)
+    xs = [synth.activations(w, tag=f"tier{b}").cuda() for b in range(6)]
+    ws = tier.workspace(w.S)
+    # (predicted batch, actual batch): right, wrong, two prefetches in a row
+    for pred, act in [(0, 0), (1, 2), (3, 3), (4, 1), (5, 5), (2, 2)]:
+        tier.prefetch(xs[pred])
+        ids_p, _ = qre.route(dev, xs[pred])
+        host.prefetch(ids_p.cpu().reshape(-1).tolist())
+        if pred == 4:
+            tier.prefetch(xs[0])
+            ids_p, _ = qre.route(dev, xs[0])
+            host.prefetch(ids_p.cpu().reshape(-1).tolist())
+        before = tier.stats()["misses"]
+        got = tier.forward(xs[act], ws=ws)
+        ref = qre.moe_layer_forward(dev, xs[act])
+        torch.cuda.synchronize()
+        assert bits_equal(got, ref), f"prefetch {pred}, forward {act}"
+        ids, _ = qre.route(dev, xs[act])
+        host.plan(ids.cpu().reshape(-1).tolist())
+        assert tier.state() == host.state() and tier.stats() == host.stats()
+        if pred == act:
+            assert tier.stats()["misses"] == before, "a perfect prediction leaves no miss"
+    assert tier.stats()["prefetches"] == 7
+    tier.close()

@@ -68,7 +68,7 @@ def capi():
 def test_library_exports_every_declared_symbol(capi):
     lib = capi.lib()
     syms = _declared_symbols()
-    assert len(syms) == 24
+    assert len(syms) == 26
     for name in syms:
         assert hasattr(lib, name), name
 
