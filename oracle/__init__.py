@@ -40,7 +40,7 @@ _f32 = ctypes.c_float
 class RefBank(ctypes.Structure):
     _fields_ = [("mat_data", ctypes.POINTER(ctypes.c_void_p)),
                 ("mat_scale", ctypes.POINTER(ctypes.c_void_p)),
-                ("n_mat", _i32), ("rows", _i32), ("K", _i32), ("bits", _i32)]
+                ("n_mat", _i32), ("rows", _i32), ("K", _i32), ("bits", _i32), ("group", _i32)]
 
 
 class RefRouteOpts(ctypes.Structure):
@@ -77,6 +77,10 @@ def lib():
         L.ref_qdot.argtypes = [_p, _i32, _f32, _p, _p, _i32]
         L.ref_qdot_f64.restype = ctypes.c_double
         L.ref_qdot_f64.argtypes = [_p, _i32, _f32, _p, _p, _i32]
+        L.ref_qdot_grouped.restype = _f32
+        L.ref_qdot_grouped.argtypes = [_p, _i32, _p, _i32, _p, _p, _i32]
+        L.ref_qdot_grouped_f64.restype = ctypes.c_double
+        L.ref_qdot_grouped_f64.argtypes = [_p, _i32, _p, _i32, _p, _p, _i32]
         L.ref_cexp.restype = _f32
         L.ref_cexp.argtypes = [_f32]
         L.ref_silu.restype = _f32
@@ -158,6 +162,17 @@ def qdot_f64(row, bits: int, scale: float, q, d) -> float:
     return lib().ref_qdot_f64(_ptr(row), bits, scale, _ptr(q), _ptr(d), q.size)
 
 
+def qdot_grouped(row, bits: int, scales, group: int, q, d) -> float:
+    """Row dot with one scale per `group` columns (scales [K/group])."""
+    row, s, q, d = _c(row, np.uint8), _c(scales, np.float32), _c(q, np.int8), _c(d, np.float32)
+    return lib().ref_qdot_grouped(_ptr(row), bits, _ptr(s), group, _ptr(q), _ptr(d), q.size)
+
+
+def qdot_grouped_f64(row, bits: int, scales, group: int, q, d) -> float:
+    row, s, q, d = _c(row, np.uint8), _c(scales, np.float32), _c(q, np.int8), _c(d, np.float32)
+    return lib().ref_qdot_grouped_f64(_ptr(row), bits, _ptr(s), group, _ptr(q), _ptr(d), q.size)
+
+
 def cexp(z) -> np.ndarray:
     z = _c(z, np.float32)
     out = np.empty_like(z)
@@ -187,19 +202,20 @@ def _as_np(t):
 class _BankHandle:
     """Keeps the numpy arrays alive while the C structure points at them."""
 
-    def __init__(self, n_mat, rows, K, bits, data, scale):
+    def __init__(self, n_mat, rows, K, bits, data, scale, group=0):
         self.data = [None if d is None else _c(_as_np(d), np.uint8) for d in data]
         self.scale = [None if s is None else _c(_as_np(s), np.float32) for s in scale]
         self.dp = (ctypes.c_void_p * n_mat)(*[None if d is None else d.ctypes.data for d in self.data])
         self.sp = (ctypes.c_void_p * n_mat)(*[None if s is None else s.ctypes.data for s in self.scale])
         self.c = RefBank(ctypes.cast(self.dp, ctypes.POINTER(ctypes.c_void_p)),
                          ctypes.cast(self.sp, ctypes.POINTER(ctypes.c_void_p)),
-                         n_mat, rows, K, bits)
+                         n_mat, rows, K, bits, group)
 
 
 def bank(b) -> _BankHandle:
-    """From a synth.Bank (or any object with n_mat/rows/K/bits/data/scale)."""
-    return _BankHandle(b.n_mat, b.rows, b.K, b.bits, b.data, b.scale)
+    """From a synth.Bank (or any object with n_mat/rows/K/bits/data/scale and,
+    for group-wise scales, group)."""
+    return _BankHandle(b.n_mat, b.rows, b.K, b.bits, b.data, b.scale, getattr(b, "group", 0))
 
 
 def expert_ffn(gate, up, down, e: int, xq, xd):

@@ -132,6 +132,42 @@ float ref_qdot(const uint8_t* row, int32_t bits, float row_scale,
     return row_scale * sum;
 }
 
+float ref_qdot_grouped(const uint8_t* row, int32_t bits, const float* s, int32_t group,
+                       const int8_t* q, const float* d, int32_t K)
+{
+    /* Group-wise weight scales, as ref_qdot but with block b's coefficient
+     * s[32b / group] * d_b (one fp32 multiply) and no row scale.  The pages
+     * name group-wise scaling without fixing its layout or where the scale
+     * enters; this reading puts it where the activation block scale already
+     * enters, so that a group of 32 columns is exactly a Q8_0 block. */
+    int32_t nb = K / 32;
+    float group_sum[4];
+    for (int32_t g = 0; g < 4; ++g) {
+        float acc = 0.0f;
+        for (int32_t b = (g * nb) / 4; b < ((g + 1) * nb) / 4; ++b) {
+            int32_t part = ref_block_partial(row, bits, q, b);
+            float t = s[(b * 32) / group] * d[b];
+            acc = fmaf(t, (float)part, acc);
+        }
+        group_sum[g] = acc;
+    }
+    float sum = group_sum[0];
+    sum = sum + group_sum[1];
+    sum = sum + group_sum[2];
+    sum = sum + group_sum[3];
+    return sum;
+}
+
+double ref_qdot_grouped_f64(const uint8_t* row, int32_t bits, const float* s, int32_t group,
+                            const int8_t* q, const float* d, int32_t K)
+{
+    double acc = 0.0;
+    for (int32_t col = 0; col < K; ++col)
+        acc += (double)s[col / group] * (double)ref_weight_code(row, bits, col) * (double)q[col] *
+               (double)d[col / 32];
+    return acc;
+}
+
 double ref_qdot_f64(const uint8_t* row, int32_t bits, float row_scale,
                     const int8_t* q, const float* d, int32_t K)
 {
@@ -203,6 +239,16 @@ static const uint8_t* bank_row(const ref_bank* B, int32_t m, int32_t r)
     return B->mat_data[m] + (int64_t)r * ref_row_bytes(B->K, B->bits);
 }
 
+/* Row r of matrix m dotted with Q8_0 activations, per-row or group-wise
+ * scales as the bank holds them. */
+static float bank_dot(const ref_bank* B, int32_t m, int32_t r, const int8_t* q, const float* d)
+{
+    if (B->group > 0)
+        return ref_qdot_grouped(bank_row(B, m, r), B->bits, B->mat_scale[m] + (int64_t)r * (B->K / B->group),
+                                B->group, q, d, B->K);
+    return ref_qdot(bank_row(B, m, r), B->bits, B->mat_scale[m][r], q, d, B->K);
+}
+
 int ref_expert_ffn(const ref_bank* gate, const ref_bank* up, const ref_bank* down,
                    int32_t e, const int8_t* xq, const float* xd,
                    float* g_out, float* u_out, float* h_out, int8_t* hq_out, float* hd_out,
@@ -213,13 +259,17 @@ int ref_expert_ffn(const ref_bank* gate, const ref_bank* up, const ref_bank* dow
     if (!gate->mat_data[e] || !up->mat_data[e] || !down->mat_data[e] ||
         !gate->mat_scale[e] || !up->mat_scale[e] || !down->mat_scale[e])
         return REF_E_MISSING;
+    const ref_bank* banks[3] = {gate, up, down};
+    for (int32_t j = 0; j < 3; ++j)
+        if (banks[j]->group < 0 || (banks[j]->group > 0 && (banks[j]->group % 32 || banks[j]->K % banks[j]->group)))
+            return REF_E_INVAL;
     int32_t I = gate->rows, H = gate->K;
     float* h = (float*)malloc(sizeof(float) * (size_t)I);
     int8_t* hq = (int8_t*)malloc((size_t)I);
     float* hd = (float*)malloc(sizeof(float) * (size_t)(I / 32));
     for (int32_t i = 0; i < I; ++i) {
-        float g = ref_qdot(bank_row(gate, e, i), gate->bits, gate->mat_scale[e][i], xq, xd, H);
-        float u = ref_qdot(bank_row(up, e, i), up->bits, up->mat_scale[e][i], xq, xd, H);
+        float g = bank_dot(gate, e, i, xq, xd);
+        float u = bank_dot(up, e, i, xq, xd);
         h[i] = ref_silu(g) * u;
         if (g_out)
             g_out[i] = g;
@@ -228,7 +278,7 @@ int ref_expert_ffn(const ref_bank* gate, const ref_bank* up, const ref_bank* dow
     }
     ref_quantize_q8_0(h, I, hq, hd);
     for (int32_t n = 0; n < H; ++n)
-        y[n] = ref_qdot(bank_row(down, e, n), down->bits, down->mat_scale[e][n], hq, hd, I);
+        y[n] = bank_dot(down, e, n, hq, hd);
     if (h_out)
         memcpy(h_out, h, sizeof(float) * (size_t)I);
     if (hq_out)

@@ -44,20 +44,25 @@ extern "C" {
 
 /*
  * A bank of n_mat quantised matrices, each [rows][K], row-major, with one
- * fp32 scale per row ([DIVE] 5.1; [README] quantised-kernel item).
+ * fp32 scale per row ([DIVE] 5.1; [README] quantised-kernel item) or, with
+ * group > 0, one fp32 scale per `group` consecutive columns of a row (the
+ * group-wise scaling that [README]'s quality-benchmark paragraph names as
+ * the likely priority; the pages give no layout, see ref_qdot_grouped).
  *   bits = 8: one two's-complement byte per weight.
  *   bits = 4: byte j of a row holds element 2j in bits 7..4 and element 2j+1
  *             in bits 3..0, each a two's-complement nibble in [-8, 7].
  *   bits = 2: byte j holds elements 4j..4j+3 in bits 7..6, 5..4, 3..2, 1..0,
  *             each a two's-complement 2-bit value in [-2, 1].
- * mat_data[m] / mat_scale[m] point at matrix m's rows / row scales; a NULL
- * entry means "not supplied" (lets a caller hand over only the experts a
- * computation touches).
+ * mat_data[m] / mat_scale[m] point at matrix m's rows / scales (rows floats,
+ * or rows * K/group floats, row r's at r * K/group); a NULL entry means "not
+ * supplied" (lets a caller hand over only the experts a computation
+ * touches).  group: 0, or a multiple of 32 that divides K.
  */
 typedef struct ref_bank {
     const uint8_t* const* mat_data;
     const float* const* mat_scale;
     int32_t n_mat, rows, K, bits;
+    int32_t group;
 } ref_bank;
 
 /* Router variants.  n_group > 1: group-limited selection (experts in n_group
@@ -110,6 +115,17 @@ float ref_qdot(const uint8_t* row, int32_t bits, float row_scale,
 /* The same quantity, unblocked, in fp64 (used to bound the fp32 fold). */
 double ref_qdot_f64(const uint8_t* row, int32_t bits, float row_scale,
                     const int8_t* q, const float* d, int32_t K);
+/* Row dot with group-wise scales s [K/group]: the weight of column c is
+ * s[c / group] times its code, so block b contributes
+ * s[32b / group] * d_b * S_b.  Canonical form: the coefficient
+ * t_b = s[32b / group] * d_b is one fp32 multiply, and t_b takes the place of
+ * d_b in the fold of ref_qdot (same four groups, same order); there is no
+ * row scale. */
+float ref_qdot_grouped(const uint8_t* row, int32_t bits, const float* s, int32_t group,
+                       const int8_t* q, const float* d, int32_t K);
+/* The same quantity, unblocked, in fp64. */
+double ref_qdot_grouped_f64(const uint8_t* row, int32_t bits, const float* s, int32_t group,
+                            const int8_t* q, const float* d, int32_t K);
 
 /* ---- SwiGLU nonlinearity ---- */
 /* exp by Cody-Waite reduction and a degree-7 Taylor polynomial; saturates to

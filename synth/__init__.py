@@ -157,6 +157,8 @@ class Workload:
     n_group: int = 1
     topk_group: int = 1
     top_p: float = 1.0
+    # columns per weight scale in every bank (0: one scale per row)
+    group: int = 0
 
     def row_bytes(self, K: int) -> int:
         return K * self.bits // 8
@@ -202,6 +204,9 @@ class Bank:
     # uint8 tensor and one [n_mat][rows] fp32 tensor that data/scale view.
     storage: Optional[torch.Tensor] = None
     scale_storage: Optional[torch.Tensor] = None
+    # columns per scale (0: scale[m] holds one value per row; else rows * K/group
+    # values, row r's at r * K/group)
+    group: int = 0
 
 
 @dataclasses.dataclass
@@ -257,23 +262,26 @@ def _mat_scale(w: Workload, name: str, m: int, rows: int) -> torch.Tensor:
 
 def make_bank(w: Workload, name: str, n_mat: int, rows: int, K: int,
               experts=None, device="cpu") -> Bank:
-    """Generate a bank; `experts` limits which matrices are materialised."""
+    """Generate a bank; `experts` limits which matrices are materialised.
+    Scales: rows values per matrix, or rows * K/group with group-wise scales
+    (the same |N(0, 1)| * scale_mult recipe per value)."""
     data: List[Optional[torch.Tensor]] = [None] * n_mat
     scale: List[Optional[torch.Tensor]] = [None] * n_mat
     rb = K * w.bits // 8
+    ns = rows * (K // w.group) if w.group else rows
     if experts is None:
         storage = torch.empty(n_mat, rows, rb, dtype=torch.uint8, device=device)
-        scale_storage = torch.empty(n_mat, rows, dtype=torch.float32, device=device)
+        scale_storage = torch.empty(n_mat, ns, dtype=torch.float32, device=device)
         for m in range(n_mat):
             storage[m] = _mat_bytes(w, name, m, rows, K, device)
-            scale_storage[m] = _mat_scale(w, name, m, rows).to(device)
+            scale_storage[m] = _mat_scale(w, name, m, ns).to(device)
             data[m] = storage[m]
             scale[m] = scale_storage[m]
-        return Bank(n_mat, rows, K, w.bits, data, scale, storage, scale_storage)
+        return Bank(n_mat, rows, K, w.bits, data, scale, storage, scale_storage, w.group)
     for m in sorted(set(int(e) for e in experts)):
         data[m] = _mat_bytes(w, name, m, rows, K, device)
-        scale[m] = _mat_scale(w, name, m, rows).to(device)
-    return Bank(n_mat, rows, K, w.bits, data, scale)
+        scale[m] = _mat_scale(w, name, m, ns).to(device)
+    return Bank(n_mat, rows, K, w.bits, data, scale, group=w.group)
 
 
 def make_layer(w: Workload, experts=None, device="cpu") -> Layer:

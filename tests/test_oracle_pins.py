@@ -177,6 +177,73 @@ def test_fold_exact_on_integers():
 
 
 # ---------------------------------------------------------------------------
+# group-wise weight scales (one scale per `group` columns of a row)
+
+GROUP_CASES = [(8, -127, 127, 32), (4, -8, 7, 128), (2, -2, 1, 256), (4, -8, 7, 64)]
+
+
+@pytest.mark.parametrize("bits,lo,hi,group", GROUP_CASES)
+def test_grouped_unit_and_power_of_two_scales(bits, lo, hi, group):
+    """All group scales 1: exactly the per-row fold with row scale 1.  All
+    equal to 2^j: every product and partial sum is scaled exactly, so the
+    result is 2^j times it, bit for bit."""
+    K = 1024
+    for trial in range(10):
+        codes = RNG.integers(lo, hi + 1, size=K).astype(np.int8)
+        row = oracle.pack_row(codes, bits)
+        x = RNG.standard_normal(K).astype(np.float32) * np.float32(10.0 ** RNG.uniform(-2, 2))
+        q, d = oracle.quantize_q8_0(x)
+        base = np.float32(oracle.qdot(row, bits, 1.0, q, d))
+        ones = np.ones(K // group, np.float32)
+        assert np.float32(oracle.qdot_grouped(row, bits, ones, group, q, d)) == base
+        for j in (-3, 5):
+            s = np.full(K // group, 2.0 ** j, np.float32)
+            assert np.float32(oracle.qdot_grouped(row, bits, s, group, q, d)) == np.float32(base * 2.0 ** j)
+
+
+@pytest.mark.parametrize("bits,lo,hi,group", GROUP_CASES)
+def test_grouped_scale_reaches_only_its_columns(bits, lo, hi, group):
+    """Scale 1 on group g0 and 0 elsewhere equals the per-row fold of the row
+    with every code outside columns [g0*group, (g0+1)*group) set to zero (a
+    wrong group index, a scale applied per block instead of per group, or a
+    leftover row scale all break this)."""
+    K = 1024
+    for g0 in range(K // group):
+        codes = RNG.integers(lo, hi + 1, size=K).astype(np.int8)
+        row = oracle.pack_row(codes, bits)
+        x = RNG.standard_normal(K).astype(np.float32)
+        q, d = oracle.quantize_q8_0(x)
+        s = np.zeros(K // group, np.float32)
+        s[g0] = 1.0
+        masked = codes.copy()
+        keep = np.zeros(K, bool)
+        keep[g0 * group:(g0 + 1) * group] = True
+        masked[~keep] = 0
+        want = np.float32(oracle.qdot(oracle.pack_row(masked, bits), bits, 1.0, q, d))
+        assert np.float32(oracle.qdot_grouped(row, bits, s, group, q, d)) == want
+
+
+@pytest.mark.parametrize("bits,lo,hi,group", GROUP_CASES)
+def test_grouped_fold_error_bound(bits, lo, hi, group):
+    """Against the unblocked fp64 sum of s[c / group] * code * q * d: within
+    the fold's bound plus one rounding of each coefficient."""
+    K = 6144
+    for trial in range(10):
+        codes = RNG.integers(lo, hi + 1, size=K).astype(np.int8)
+        row = oracle.pack_row(codes, bits)
+        x = RNG.standard_normal(K).astype(np.float32) * np.float32(10.0 ** RNG.uniform(-3, 3))
+        q, d = oracle.quantize_q8_0(x)
+        s = (np.abs(RNG.standard_normal(K // group)) * 0.02).astype(np.float32)
+        got = float(oracle.qdot_grouped(row, bits, s, group, q, d))
+        exact = oracle.qdot_grouped_f64(row, bits, s, group, q, d)
+        parts = np.array([oracle.block_partial(row, bits, q, b) for b in range(K // 32)], np.float64)
+        coef = np.repeat(s.astype(np.float64), group // 32) * d.astype(np.float64)
+        n = K // 32 + 2
+        bound = (n * U / (1 - n * U)) * float(np.sum(np.abs(coef * parts)))
+        assert abs(got - exact) <= bound + 1e-30, (trial, got, exact, bound)
+
+
+# ---------------------------------------------------------------------------
 # exp and SiLU
 # ---------------------------------------------------------------------------
 
@@ -573,7 +640,10 @@ def _naive_dense_layer(L, x):
 
     def deq(bank_, m):
         rows = np.stack([oracle.unpack_row(r, bank_.bits, bank_.K) for r in np.asarray(bank_.data[m])])
-        return rows.astype(np.float64) * np.asarray(bank_.scale[m], np.float64)[:, None]
+        sc = np.asarray(bank_.scale[m], np.float64)
+        if bank_.group:  # weight of column c = scale of its group * code
+            return rows.astype(np.float64) * np.repeat(sc.reshape(bank_.rows, -1), bank_.group, axis=1)
+        return rows.astype(np.float64) * sc[:, None]
 
     mats = [(deq(L.gate, e), deq(L.up, e), deq(L.down, e)) for e in range(E)]
     sh = (deq(L.sh_gate, 0), deq(L.sh_up, 0), deq(L.sh_down, 0)) if w.has_shared else None
@@ -599,13 +669,19 @@ def _naive_dense_layer(L, x):
     return out
 
 
-@pytest.mark.parametrize("variant", ["tiny", "tiny_shared_rsf", "tiny_int4", "tiny_int2"])
+@pytest.mark.parametrize("variant", ["tiny", "tiny_shared_rsf", "tiny_int4", "tiny_int2", "tiny_group32",
+                                     "tiny_int4_group128", "tiny_int2_group64"])
 def test_layer_against_naive_dense_path(variant):
     base = synth.WORKLOADS["tiny"]
     w = {"tiny": base,
          "tiny_shared_rsf": synth.scaled(base, name="tiny_sh", has_shared=True, rsf=2.5, top_k=3),
          "tiny_int4": synth.scaled(base, name="tiny4", layer="tiny_int4", bits=4, rsf=2.5),
-         "tiny_int2": synth.scaled(base, name="tiny2", layer="tiny_int2", bits=2, has_shared=True)}[variant]
+         "tiny_int2": synth.scaled(base, name="tiny2", layer="tiny_int2", bits=2, has_shared=True),
+         "tiny_group32": synth.scaled(base, name="tiny_g32", layer="tiny_g32", group=32, has_shared=True),
+         "tiny_int4_group128": synth.scaled(base, name="tiny4_g128", layer="tiny4_g128", bits=4, group=128,
+                                            rsf=2.5),
+         "tiny_int2_group64": synth.scaled(base, name="tiny2_g64", layer="tiny2_g64", bits=2, group=64,
+                                           has_shared=True)}[variant]
     L = synth.make_layer(w)
     x = synth.activations(w).numpy()
     r = oracle.layer_forward(L, x)
