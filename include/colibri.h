@@ -79,26 +79,32 @@ enum { COLI_Q8 = 8, COLI_Q4 = 4, COLI_Q2 = 2 };
 
 /*
  * A bank of n_mat quantised matrices, each [rows][K] row-major, one fp32 scale
- * per row ([DIVE] 5.1).  Row r of matrix m starts at byte (m*rows + r) * K *
- * qtype / 8 of `data`; its scale is row_scale[m*rows + r].
+ * per row ([DIVE] 5.1), or with group > 0 one fp32 scale per `group`
+ * consecutive columns of a row (group-wise scales: [README]'s
+ * quality-benchmark paragraph names them as the likely priority).  Row r of
+ * matrix m starts at byte (m*rows + r) * K * qtype / 8 of `data`; its scale is
+ * row_scale[m*rows + r], or with groups its scales are row_scale[(m*rows + r)
+ * * (K/group) + j] for column groups j = 0 .. K/group - 1.
  *   COLI_Q8: one two's-complement byte per weight.
  *   COLI_Q4: byte j of a row holds element 2j in bits 7..4 and element 2j+1 in
  *            bits 3..0, two's-complement nibbles in [-8, 7].
  *   COLI_Q2: byte j holds elements 4j..4j+3 in bits 7..6, 5..4, 3..2, 1..0,
  *            two's-complement values in [-2, 1].
  * Requirements: K % 32 == 0, rows >= 1, n_mat >= 1, `data` 16-byte aligned,
- * `row_scale` 4-byte aligned.
+ * `row_scale` 4-byte aligned; group 0 or a multiple of 32 that divides K.
  */
 typedef struct coli_qbank {
     const void* data;
     const float* row_scale;
     int32_t n_mat, rows, K;
     int32_t qtype; /* COLI_Q8, COLI_Q4 or COLI_Q2 */
+    int32_t group; /* columns per scale; 0: one scale per row */
 } coli_qbank;
 
 /*
  * One layer.  gate/up: n_mat = n_experts, rows = inter, K = hidden; down:
- * n_mat = n_experts, rows = hidden, K = inter.  gate and up share a qtype.
+ * n_mat = n_experts, rows = hidden, K = inter.  gate and up share a qtype and
+ * a group.
  * The shared expert (has_shared != 0) has the same shapes with n_mat = 1.
  * router_w is fp32 [n_experts][hidden]; router_bias fp32 [n_experts] enters
  * expert selection only.  hidden % 32 == 0 and inter % 32 == 0.
@@ -197,7 +203,9 @@ int colibri_moe_dispatch(const int32_t* topk_ids, int32_t S, int32_t k, int32_t 
  * acc = fmaf(d_b, (float)S_b, acc) in ascending block order from +0, and the
  * four group sums are added left to right (the pages leave the order of the
  * fp32 accumulation open; this one is fixed so that results are bit-exact
- * across batch sizes and kernels).  silu(g) = g / (1 + exp(-g)) with exp by Cody-Waite
+ * across batch sizes and kernels).  With group-wise scales s (bank group > 0)
+ * block b's coefficient is the fp32 product s[32b/group] * d_b in place of
+ * d_b, and the row-scale factor is absent.  silu(g) = g / (1 + exp(-g)) with exp by Cody-Waite
  * reduction and a degree-7 Taylor polynomial (+inf above 88, +0 below -87).
  * xq int8 [S][hidden] and xd fp32 [S][hidden/32] come from
  * colibri_quantize_q8_0; offsets / pairs from colibri_moe_dispatch (or, for a

@@ -32,7 +32,7 @@ _i32 = ctypes.c_int32
 class QBankDesc(ctypes.Structure):
     """coli_qbank"""
     _fields_ = [("data", _vp), ("row_scale", _vp), ("n_mat", _i32), ("rows", _i32), ("K", _i32),
-                ("qtype", _i32)]
+                ("qtype", _i32), ("group", _i32)]
 
 
 class LayerDesc(ctypes.Structure):
@@ -146,15 +146,17 @@ def _stream():
 @dataclass
 class QBank:
     """n_mat quantised matrices [rows][K]: data uint8 [n_mat][rows][K*qtype/8],
-    row scales fp32 [n_mat][rows] (device tensors)."""
+    scales fp32 [n_mat][rows] or, with group > 0, [n_mat][rows * K/group]
+    (device tensors)."""
     data: torch.Tensor
     scale: torch.Tensor
     qtype: int
+    group: int = 0
 
     def desc(self) -> QBankDesc:
         n_mat, rows, rb = self.data.shape
         return QBankDesc(_bank_ptr(self.data), _bank_ptr(self.scale), n_mat, rows,
-                         rb * 8 // self.qtype, self.qtype)
+                         rb * 8 // self.qtype, self.qtype, self.group)
 
 
 class MoELayer:

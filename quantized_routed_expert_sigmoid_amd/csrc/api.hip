@@ -125,7 +125,7 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
     if ((st = check_bank(gate, n_mat, I, H)) || (st = check_bank(up, n_mat, I, H)) ||
         (st = check_bank(down, n_mat, H, I)))
         return st;
-    if (gate->qtype != up->qtype)
+    if (gate->qtype != up->qtype || gate->group != up->group)
         return COLI_E_UNSUPPORTED;
     if (S == 0)
         return COLI_OK;

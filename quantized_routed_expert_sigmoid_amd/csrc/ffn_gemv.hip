@@ -38,10 +38,11 @@ struct JobLoc {
     int seg, unit, rb;
 };
 
-/* Field-wise select keeps the segment in scalar registers. */
+/* Field-wise select keeps the segment in scalar registers (every field of
+ * FfnSeg is selected; the zero initialisation only guards additions). */
 __device__ __forceinline__ FfnSeg pick(const FfnArgs& a, int s)
 {
-    FfnSeg r;
+    FfnSeg r = {};
     const bool one = s != 0;
     r.gate_w = one ? a.seg[1].gate_w : a.seg[0].gate_w;
     r.gate_s = one ? a.seg[1].gate_s : a.seg[0].gate_s;
@@ -61,6 +62,8 @@ __device__ __forceinline__ FfnSeg pick(const FfnArgs& a, int s)
     r.S = one ? a.seg[1].S : a.seg[0].S;
     r.rows = one ? a.seg[1].rows : a.seg[0].rows;
     r.n_mat = one ? a.seg[1].n_mat : a.seg[0].n_mat;
+    r.gu_gb = one ? a.seg[1].gu_gb : a.seg[0].gu_gb;
+    r.d_gb = one ? a.seg[1].d_gb : a.seg[0].d_gb;
     return r;
 }
 
@@ -255,11 +258,14 @@ __device__ __forceinline__ void commit_token_block(const TokenBlock& T, WaveLds<
     wave_lds_sync();
 }
 
-/* Block partials of K step st of the wave's group (nblk blocks), transposed
- * through the wave's LDS, folded into acc (lane = row 8o + j of the octet). */
+/* Block partials of K step st of the wave's group (nblk blocks from
+ * b_begin), transposed through the wave's LDS, folded into acc (lane = row
+ * 8o + j of the octet).  ws: the lane's row's group-wise scales (gb blocks
+ * each), or null for per-row scales. */
 template <int BITS, int TMAX>
 __device__ __forceinline__ void fold_step(const StepWeights<BITS>& W, int st, int nblk, int ntok,
-                                          WaveLds<TMAX>& L, float (&acc)[TMAX])
+                                          WaveLds<TMAX>& L, float (&acc)[TMAX], const float* ws, int gb,
+                                          int b_begin)
 {
     const int lane = threadIdx.x & 63;
     const int o = lane >> 3, j8 = lane & 7;
@@ -286,11 +292,22 @@ __device__ __forceinline__ void fold_step(const StepWeights<BITS>& W, int st, in
     }
     wave_lds_sync();
     const int nbs = max(0, min(8, nblk - 8 * st));
+    if (ws) {
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < ntok) {
-            for (int jj = 0; jj < nbs; ++jj)
-                acc[t] = __builtin_fmaf(L.d[t][8 * st + jj], (float)L.part[part_index(t, o, j8, jj)], acc[t]);
+        for (int t = 0; t < TMAX; ++t) {
+            if (t < ntok) {
+                for (int jj = 0; jj < nbs; ++jj)
+                    acc[t] = __builtin_fmaf(group_coef(ws, gb, b_begin + 8 * st + jj, L.d[t][8 * st + jj]),
+                                            (float)L.part[part_index(t, o, j8, jj)], acc[t]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t < ntok) {
+                for (int jj = 0; jj < nbs; ++jj)
+                    acc[t] = __builtin_fmaf(L.d[t][8 * st + jj], (float)L.part[part_index(t, o, j8, jj)], acc[t]);
+            }
         }
     }
     wave_lds_sync();
@@ -312,7 +329,7 @@ __device__ __forceinline__ void first_step(StepWeights<BITS>& A, const uint8_t* 
 template <int BITS, int TMAX>
 __device__ __forceinline__ void k_loop(StepWeights<BITS>& A, const uint8_t* row0, int64_t rowbytes,
                                        int b_begin, int b_end, int ntok, int rows_ok, WaveLds<TMAX>& L,
-                                       float (&acc)[TMAX])
+                                       float (&acc)[TMAX], const float* ws, int gb)
 {
     const int j8 = threadIdx.x & 7;
     const int nblk = b_end - b_begin;
@@ -323,9 +340,9 @@ __device__ __forceinline__ void k_loop(StepWeights<BITS>& A, const uint8_t* row0
      * nothing), so A and B keep their registers across iterations */
     for (int st = 0; st < nsteps; st += 2) {
         load_step<BITS>(B, row0, rowbytes, b_begin + 8 * (st + 1) + j8, b_last, rows_ok);
-        fold_step<BITS, TMAX>(A, st, nblk, ntok, L, acc);
+        fold_step<BITS, TMAX>(A, st, nblk, ntok, L, acc, ws, gb, b_begin);
         load_step<BITS>(A, row0, rowbytes, b_begin + 8 * (st + 2) + j8, b_last, rows_ok);
-        fold_step<BITS, TMAX>(B, st + 1, nblk, ntok, L, acc);
+        fold_step<BITS, TMAX>(B, st + 1, nblk, ntok, L, acc, ws, gb, b_begin);
     }
 }
 
@@ -380,6 +397,11 @@ __global__ __launch_bounds__(256) void ffn_gate_up_gemv(FfnArgs a)
     /* octets 0..3: gate rows rb*32 + 8o ..; octets 4..7: the same up rows */
     const uint8_t* row0 = (o < 4 ? sg.gate_w : sg.up_w) +
                           ((int64_t)e * a.I + L.rb * 32 + 8 * (o & 3)) * rowbytes;
+    /* group-wise scales of this lane's fold row (row 8(o & 3) + j of the job) */
+    const int ng = sg.gu_gb ? nb / sg.gu_gb : 0;
+    const float* ws = sg.gu_gb ? (o < 4 ? sg.gate_s : sg.up_s) +
+                                     ((int64_t)e * a.I + L.rb * 32 + 8 * (o & 3) + (lane & 7)) * ng
+                               : nullptr;
     StepWeights<BITS> A;
     first_step<BITS>(A, row0, rowbytes, b0, b1, 8);
     stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
@@ -387,13 +409,13 @@ __global__ __launch_bounds__(256) void ffn_gate_up_gemv(FfnArgs a)
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
         acc[t] = 0.0f;
-    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, 8, lds[wv], acc);
+    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, 8, lds[wv], acc, ws, sg.gu_gb);
     sum_groups<TMAX>(gsum, acc);
     if (wv != 0)
         return;
 
     const int r = L.rb * 32 + (lane & 31);
-    const float sc = (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
+    const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
     const int nbi = a.I / 32;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
@@ -445,6 +467,8 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
     const int first = L.rb * kRowsPerJob + 8 * o;
     const int rows_ok = min(8, max(0, a.H - first));
     const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + min(first, a.H - 1)) * rowbytes;
+    const int ng = sg.d_gb ? nb / sg.d_gb : 0;
+    const float* ws = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(first + (lane & 7), a.H - 1)) * ng : nullptr;
     StepWeights<BITS> A;
     first_step<BITS>(A, row0, rowbytes, b0, b1, rows_ok);
     stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
@@ -452,14 +476,14 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
         acc[t] = 0.0f;
-    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, rows_ok, lds[wv], acc);
+    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, rows_ok, lds[wv], acc, ws, sg.d_gb);
     sum_groups<TMAX>(gsum, acc);
     if (wv != 0)
         return;
 
     const int n = L.rb * kRowsPerJob + lane;
     if (n < a.H) {
-        const float sc = sg.down_s[(int64_t)e * a.H + n];
+        const float sc = sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n];
 #pragma unroll
         for (int t = 0; t < TMAX; ++t)
             if (t < ntok)
@@ -555,7 +579,7 @@ __device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const
 template <int BITS, int NI>
 __device__ __forceinline__ float dec_k_loop(PairLoad<BITS, NI>& A, const uint8_t* rows0, int64_t rowbytes,
                                             int rows_ok, int nb, const uint32_t (&xa)[NI][8], int32_t* P,
-                                            int sp, const float* dl)
+                                            int sp, const float* dl, const float* ws0, int gb)
 {
     PairLoad<BITS, NI> B;
 #pragma unroll
@@ -573,21 +597,28 @@ __device__ __forceinline__ float dec_k_loop(PairLoad<BITS, NI>& A, const uint8_t
     const int32_t* pr = P + r * sp;
     float acc = 0.0f;
     int b = b0;
-    /* eight partials and scales read ahead of their (in-order) fmas */
-    for (; b + 8 <= b1; b += 8) {
-        int32_t q[8];
-        float dd[8];
+    if (ws0) {
+        /* group-wise scales of row r (rows past rows_ok read the last row's) */
+        const float* ws = ws0 + (int64_t)min(r, max(rows_ok, 1) - 1) * (nb / gb);
+        for (; b < b1; ++b)
+            acc = __builtin_fmaf(group_coef(ws, gb, b, dl[b]), (float)pr[b], acc);
+    } else {
+        /* eight partials and scales read ahead of their (in-order) fmas */
+        for (; b + 8 <= b1; b += 8) {
+            int32_t q[8];
+            float dd[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            q[i] = pr[b + i];
-            dd[i] = dl[b + i];
+            for (int i = 0; i < 8; ++i) {
+                q[i] = pr[b + i];
+                dd[i] = dl[b + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc = __builtin_fmaf(dd[i], (float)q[i], acc);
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+        for (; b < b1; ++b)
+            acc = __builtin_fmaf(dl[b], (float)pr[b], acc);
     }
-    for (; b < b1; ++b)
-        acc = __builtin_fmaf(dl[b], (float)pr[b], acc);
     float v = __shfl(acc, r, kWave);
     v = v + __shfl(acc, 16 + r, kWave);
     v = v + __shfl(acc, 32 + r, kWave);
@@ -665,7 +696,10 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     PairLoad<BITS, NI> A;
     pair_load<BITS, NI>(A, rows0, rowbytes, 0, kDecRows, nb);
     dec_act_prep<BITS, NI>(xa, a.xd, nb, dl);
-    const float v16 = dec_k_loop<BITS, NI>(A, rows0, rowbytes, kDecRows, nb, xa, P, sp, dl);
+    const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) +
+                                      ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * (nb / sg.gu_gb)
+                                : nullptr;
+    const float v16 = dec_k_loop<BITS, NI>(A, rows0, rowbytes, kDecRows, nb, xa, P, sp, dl, ws0, sg.gu_gb);
     if (lane < 16)
         rsum[16 * wv + lane] = v16;
     __syncthreads();
@@ -673,7 +707,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         return;
     const float acc = rsum[lane];
     const int r = rb * 32 + (lane & 31);
-    const float sc = (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
+    const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
     const float v = sc * acc;
     const float up = shfl_xor(v, 32);
     const float h = canon_silu(v) * up;
@@ -716,10 +750,11 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     PairLoad<BITS, NI> A;
     pair_load<BITS, NI>(A, rows0, rowbytes, 0, rows_ok, nb);
     dec_act_prep<BITS, NI>(xa, a.hd + (int64_t)u * nb, nb, dl);
-    const float v = dec_k_loop<BITS, NI>(A, rows0, rowbytes, rows_ok, nb, xa, P, sp, dl);
+    const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(row0, a.H - 1)) * (nb / sg.d_gb) : nullptr;
+    const float v = dec_k_loop<BITS, NI>(A, rows0, rowbytes, rows_ok, nb, xa, P, sp, dl, ws0, sg.d_gb);
     const int n = row0 + lane;
     if (lane < rows_ok)
-        a.y[(int64_t)u * a.H + n] = sg.down_s[(int64_t)e * a.H + n] * v;
+        a.y[(int64_t)u * a.H + n] = (sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n]) * v;
 }
 
 /* ---- one token: down projection with the combine --------------------------
@@ -852,20 +887,33 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
         const float* dj = dls + (rd >> 1) * nb;
         float acc = 0.0f;
         int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int32_t q[8];
-            float dd[8];
+        const int uf = dc_unit(kept, n_kept, d.k, rd >> 1, all_kept);
+        const int gbf = uf < d.k ? a.seg[0].d_gb : a.seg[1].d_gb;
+        if (gbf) {
+            /* group-wise scales of (unit, row) */
+            const bool rt = uf < d.k;
+            const int nm = rt ? a.seg[0].n_mat : a.seg[1].n_mat;
+            const int ef = rt ? min(max(d.ids[uf], 0), nm - 1) : 0;
+            const float* ws = (rt ? a.seg[0].down_s : a.seg[1].down_s) +
+                              ((int64_t)ef * a.H + row0 + (rd & 1)) * (nb / gbf);
+            for (; b < b1; ++b)
+                acc = __builtin_fmaf(group_coef(ws, gbf, b, dj[b]), (float)pr[b], acc);
+        } else {
+            for (; b + 8 <= b1; b += 8) {
+                int32_t q[8];
+                float dd[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                q[i] = pr[b + i];
-                dd[i] = dj[b + i];
+                for (int i = 0; i < 8; ++i) {
+                    q[i] = pr[b + i];
+                    dd[i] = dj[b + i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc = __builtin_fmaf(dd[i], (float)q[i], acc);
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+            for (; b < b1; ++b)
+                acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
         }
-        for (; b < b1; ++b)
-            acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
         const int base = lane & ~3;
         float v = __shfl(acc, base, kWave);
         v = v + __shfl(acc, base + 1, kWave);
@@ -877,7 +925,8 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
             const float* ds = routed ? a.seg[0].down_s : a.seg[1].down_s;
             const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
             const int e = routed ? min(max(d.ids[u], 0), n_mat - 1) : 0;
-            ys[rd] = ds[(int64_t)e * a.H + n] * v;
+            const bool grouped = (routed ? a.seg[0].d_gb : a.seg[1].d_gb) != 0;
+            ys[rd] = (grouped ? 1.0f : ds[(int64_t)e * a.H + n]) * v;
         }
     }
     wave_lds_sync();

@@ -269,6 +269,40 @@ __device__ __forceinline__ void block_mfma(const KLds<BITS>& S, int buf, int j, 
     }
 }
 
+/* Group-wise weight scales of a lane's four row dots (v = 0..3): gb blocks
+ * per scale, ws[v] the row's scales; gb == 0 for per-row scales. */
+struct RowGroups {
+    const float* ws[4];
+    int gb;
+};
+
+/* One block with group-wise scales: coefficient s[v][b / gb] * d (the
+ * canonical fp32 product) for each row dot, on the exact partials (the
+ * 2^(8-b) factor of the packed weights shifted back out). */
+template <int BITS, int NT>
+__device__ __forceinline__ void block_mfma_grouped(const KLds<BITS>& S, int buf, int j, const uint32_t* arow,
+                                                   int r, int g, float (&acc)[2][4], const RowGroups& rg,
+                                                   int gidx)
+{
+    constexpr int SHIFT = 8 - BITS;
+    const long A = a_operand<BITS>(arow + j * BITS, g);
+    float wsv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        wsv[v] = rg.ws[v][gidx];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int t = 16 * n + r;
+        const uint2 bw = *reinterpret_cast<const uint2*>(&S.b[buf][j][g][t][0]);
+        const long B = (long)(((uint64_t)bw.y << 32) | bw.x);
+        const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        const float d = S.dr[buf][j][t];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[n][v] = __builtin_fmaf(wsv[v] * d, (float)(c[v] >> SHIFT), acc[n][v]);
+    }
+}
+
 template <int NT>
 __device__ __forceinline__ void flush(float (&acc)[2][4], float (&tot)[2][4])
 {
@@ -288,9 +322,9 @@ __device__ __forceinline__ void flush(float (&acc)[2][4], float (&tot)[2][4])
  * runs as straight-line code (a boundary at its first block is flushed
  * before it).  Any other step checks each block: the row end, the group
  * boundaries (a repeated boundary adds +0) and the shift-back fold. */
-template <int BITS, int NT>
+template <int BITS, int NT, bool GROUPED>
 __device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int nb, int bnd1, int bnd2,
-                                     int bnd3, float (&acc)[2][4], float (&tot)[2][4])
+                                     int bnd3, float (&acc)[2][4], float (&tot)[2][4], const RowGroups& rg)
 {
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -299,6 +333,19 @@ __device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int n
     const int b0 = st * C::kStep, b1 = b0 + C::kStep;
     if (b0 >= nb)
         return;
+    if constexpr (GROUPED) {
+        if (rg.gb) {
+            for (int j = 0; j < C::kStep; ++j) {
+                const int b = b0 + j;
+                if (b >= nb)
+                    break;
+                if (b == bnd1 || b == bnd2 || b == bnd3)
+                    flush<NT>(acc, tot);
+                block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, rg, b / rg.gb);
+            }
+            return;
+        }
+    }
     const bool exact_shift = BITS != 8 && __builtin_amdgcn_readfirstlane(S.flag[buf]) == st;
     const bool inner = (bnd1 > b0 && bnd1 < b1) || (bnd2 > b0 && bnd2 < b1) || (bnd3 > b0 && bnd3 < b1);
     if (b1 <= nb && !inner && !exact_shift) {
@@ -331,8 +378,9 @@ __device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int n
  * the last step are clamped in bounds and their LDS copies never multiplied --
  * so the two register sets stay put across iterations and each commit waits
  * only for its own loads. */
-template <int BITS, int NT>
-__device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, float (&tot)[2][4])
+template <int BITS, int NT, bool GROUPED>
+__device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, float (&tot)[2][4],
+                                          const RowGroups& rg)
 {
     using C = Cfg<BITS>;
     const int nb = L.nb;
@@ -356,11 +404,11 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, floa
     fetch<BITS>(P0, L, 2);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
-        step<BITS, NT>(S, 0, st, nb, bnd1, bnd2, bnd3, acc, tot);
+        step<BITS, NT, GROUPED>(S, 0, st, nb, bnd1, bnd2, bnd3, acc, tot, rg);
         commit<BITS>(P1, S, 1, st + 1);
         fetch<BITS>(P1, L, st + 3);
         __syncthreads();
-        step<BITS, NT>(S, 1, st + 1, nb, bnd1, bnd2, bnd3, acc, tot);
+        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, bnd1, bnd2, bnd3, acc, tot, rg);
         commit<BITS>(P0, S, 0, st + 2);
         fetch<BITS>(P0, L, st + 4);
         __syncthreads();
@@ -372,19 +420,21 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, floa
             tot[n][v] = tot[n][v] + acc[n][v];
 }
 
-template <int BITS>
+template <int BITS, bool GROUPED>
 __device__ __forceinline__ void mfma_k_loop(KLds<BITS>& S, const LoadLane& L, int ntiles,
-                                            float (&tot)[2][4])
+                                            float (&tot)[2][4], const RowGroups& rg)
 {
     if (ntiles > 1)
-        k_loop_nt<BITS, 2>(S, L, tot);
+        k_loop_nt<BITS, 2, GROUPED>(S, L, tot, rg);
     else
-        k_loop_nt<BITS, 1>(S, L, tot);
+        k_loop_nt<BITS, 1, GROUPED>(S, L, tot, rg);
 }
 
 } // namespace
 
-template <int BITS>
+/* GROUPED: a launch whose segments may hold group-wise scales (a separate
+ * instantiation, so that the per-row kernels keep their registers). */
+template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
 {
     __shared__ MfmaShared<BITS> sm;
@@ -409,16 +459,27 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     L.xdrow = a.xd + (int64_t)tok * nb;
     L.nb = nb;
     const int ntiles = (ntok + 15) / 16;
-    float tot[2][4];
-    mfma_k_loop<BITS>(sm.k, L, ntiles, tot);
-
-    /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
-     * h = silu(g) * u and one Q8_0 block of h per token */
     const int r = lane & 15, g = lane >> 4;
+    /* group-wise scales of the lane's row dots 16w + 4(lane/16) + v */
+    RowGroups rg;
+    rg.gb = GROUPED ? sg.gu_gb : 0;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int rdot = 16 * wv + 4 * g + v;
-        const float sc = (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
+        rg.ws[v] = rg.gb ? (rdot < 32 ? sg.gate_s : sg.up_s) +
+                               ((int64_t)e * a.I + M.rb * 32 + (rdot & 31)) * (nb / rg.gb)
+                         : nullptr;
+    }
+    float tot[2][4];
+    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot, rg);
+
+    /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
+     * h = silu(g) * u and one Q8_0 block of h per token */
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int rdot = 16 * wv + 4 * g + v;
+        const float sc =
+            rg.gb ? 1.0f : (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
@@ -453,7 +514,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     }
 }
 
-template <int BITS>
+template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
 {
     __shared__ MfmaShared<BITS> sm;
@@ -477,15 +538,22 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     L.xdrow = a.hd + row_in * nb;
     L.nb = nb;
     const int ntiles = (ntok + 15) / 16;
-    float tot[2][4];
-    mfma_k_loop<BITS>(sm.k, L, ntiles, tot);
-
     const int r = lane & 15, g = lane >> 4;
+    RowGroups rg;
+    rg.gb = GROUPED ? sg.d_gb : 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int n_out = M.rb * 64 + 16 * wv + 4 * g + v;
+        rg.ws[v] = rg.gb ? sg.down_s + ((int64_t)e * a.H + min(n_out, a.H - 1)) * (nb / rg.gb) : nullptr;
+    }
+    float tot[2][4];
+    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot, rg);
+
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int rr = 16 * wv + 4 * g + v;
         const int n_out = M.rb * 64 + rr;
-        const float sc = n_out < a.H ? sg.down_s[(int64_t)e * a.H + n_out] : 0.0f;
+        const float sc = n_out < a.H ? (rg.gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n_out]) : 0.0f;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
@@ -519,10 +587,14 @@ hipError_t launch_ffn_gate_up_mfma(const FfnArgs& a, int32_t bits, hipStream_t s
     if (jobs == 0)
         return hipSuccess;
     const dim3 grid((uint32_t)jobs), block(256);
-    switch (bits) {
-    case 8: hipLaunchKernelGGL(ffn_gate_up_mfma<8>, grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL(ffn_gate_up_mfma<4>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(ffn_gate_up_mfma<2>, grid, block, 0, st, a); break;
+    const bool grouped = a.seg[0].gu_gb != 0 || (a.nseg > 1 && a.seg[1].gu_gb != 0);
+    switch (bits * 2 + (grouped ? 1 : 0)) {
+    case 16: hipLaunchKernelGGL((ffn_gate_up_mfma<8, false>), grid, block, 0, st, a); break;
+    case 17: hipLaunchKernelGGL((ffn_gate_up_mfma<8, true>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((ffn_gate_up_mfma<4, false>), grid, block, 0, st, a); break;
+    case 9: hipLaunchKernelGGL((ffn_gate_up_mfma<4, true>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((ffn_gate_up_mfma<2, false>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((ffn_gate_up_mfma<2, true>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }
@@ -533,10 +605,14 @@ hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st)
     if (jobs == 0)
         return hipSuccess;
     const dim3 grid((uint32_t)jobs), block(256);
-    switch (bits) {
-    case 8: hipLaunchKernelGGL(ffn_down_mfma<8>, grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL(ffn_down_mfma<4>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(ffn_down_mfma<2>, grid, block, 0, st, a); break;
+    const bool grouped = a.seg[0].d_gb != 0 || (a.nseg > 1 && a.seg[1].d_gb != 0);
+    switch (bits * 2 + (grouped ? 1 : 0)) {
+    case 16: hipLaunchKernelGGL((ffn_down_mfma<8, false>), grid, block, 0, st, a); break;
+    case 17: hipLaunchKernelGGL((ffn_down_mfma<8, true>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((ffn_down_mfma<4, false>), grid, block, 0, st, a); break;
+    case 9: hipLaunchKernelGGL((ffn_down_mfma<4, true>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((ffn_down_mfma<2, false>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((ffn_down_mfma<2, true>), grid, block, 0, st, a); break;
     }
     return hipGetLastError();
 }

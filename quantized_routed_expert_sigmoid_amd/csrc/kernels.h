@@ -79,7 +79,16 @@ struct FfnSeg {
     int32_t S;               /* tokens of the batch */
     int32_t rows;            /* sorted positions of this group (S*k, or S for identity) */
     int32_t n_mat;           /* matrices in the group's banks */
+    int32_t gu_gb, d_gb;     /* Q8_0 blocks per weight scale of gate/up and of down; 0: per-row
+                                scales (row r's K/32/gb scales at scale + (e*rows + r) * K/32/gb) */
 };
+
+/* Coefficient of block b with group-wise weight scales: the row's scale of
+ * b's group times the activation block scale (one fp32 multiply). */
+__device__ __forceinline__ float group_coef(const float* ws, int gb, int b, float d)
+{
+    return ws[b / gb] * d;
+}
 
 struct FfnArgs {
     FfnSeg seg[2];

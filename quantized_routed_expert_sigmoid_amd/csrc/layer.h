@@ -32,6 +32,8 @@ inline int check_bank(const coli_qbank* b, int32_t n_mat, int32_t rows, int32_t 
         return COLI_E_INVAL;
     if (b->qtype != COLI_Q8 && b->qtype != COLI_Q4 && b->qtype != COLI_Q2)
         return COLI_E_UNSUPPORTED;
+    if (b->group < 0 || (b->group > 0 && (b->group % 32 != 0 || K % b->group != 0)))
+        return COLI_E_INVAL;
     if (!aligned(b->data, 16) || !aligned(b->row_scale, 4))
         return COLI_E_UNSUPPORTED;
     return COLI_OK;
@@ -65,7 +67,7 @@ inline int check_layer(const coli_moe_layer* L)
     if ((st = check_bank(&L->gate, E, I, H)) || (st = check_bank(&L->up, E, I, H)) ||
         (st = check_bank(&L->down, E, H, I)))
         return st;
-    if (L->gate.qtype != L->up.qtype)
+    if (L->gate.qtype != L->up.qtype || L->gate.group != L->up.group)
         return COLI_E_UNSUPPORTED;
     if (L->n_group < 0 || !(L->top_p >= 0.0f)) /* also rejects a NaN top_p */
         return COLI_E_INVAL;
@@ -79,7 +81,7 @@ inline int check_layer(const coli_moe_layer* L)
         if ((st = check_bank(&L->sh_gate, 1, I, H)) || (st = check_bank(&L->sh_up, 1, I, H)) ||
             (st = check_bank(&L->sh_down, 1, H, I)))
             return st;
-        if (L->sh_gate.qtype != L->sh_up.qtype)
+        if (L->sh_gate.qtype != L->sh_up.qtype || L->sh_gate.group != L->sh_up.group)
             return COLI_E_UNSUPPORTED;
     }
     return COLI_OK;
@@ -212,6 +214,8 @@ inline FfnSeg make_seg(const coli_qbank* g, const coli_qbank* u, const coli_qban
     s.S = S;
     s.rows = rows;
     s.n_mat = g->n_mat;
+    s.gu_gb = g->group / 32;
+    s.d_gb = d->group / 32;
     return s;
 }
 

@@ -46,6 +46,12 @@ size_t row_bytes(int32_t K, int32_t qtype)
     return (size_t)K * qtype / 8;
 }
 
+/* Scales per row of a bank: one, or one per column group. */
+size_t scales_per_row(const coli_qbank& b)
+{
+    return b.group > 0 ? (size_t)(b.K / b.group) : 1;
+}
+
 /* slot_mem: the six slot-bank regions, then the cache state and the pin
  * scratch. */
 struct SlotLayout {
@@ -60,11 +66,11 @@ SlotLayout slot_layout(const coli_moe_layer* L, int32_t n)
     Bump b;
     SlotLayout s;
     s.reg[0] = b.take((size_t)n * I * row_bytes(H, L->gate.qtype));
-    s.reg[1] = b.take((size_t)n * I * 4);
+    s.reg[1] = b.take((size_t)n * I * scales_per_row(L->gate) * 4);
     s.reg[2] = b.take((size_t)n * I * row_bytes(H, L->up.qtype));
-    s.reg[3] = b.take((size_t)n * I * 4);
+    s.reg[3] = b.take((size_t)n * I * scales_per_row(L->up) * 4);
     s.reg[4] = b.take((size_t)n * H * row_bytes(I, L->down.qtype));
-    s.reg[5] = b.take((size_t)n * H * 4);
+    s.reg[5] = b.take((size_t)n * H * scales_per_row(L->down) * 4);
     s.hdr = b.take(sizeof(TierHdr));
     s.slot_of = b.take((size_t)E * 4);
     s.expert_in = b.take((size_t)n * 4);
@@ -93,11 +99,11 @@ void region_bytes(const coli_moe_layer* L, size_t out[6])
 {
     const int32_t H = L->hidden, I = L->inter;
     out[0] = (size_t)I * row_bytes(H, L->gate.qtype);
-    out[1] = (size_t)I * 4;
+    out[1] = (size_t)I * scales_per_row(L->gate) * 4;
     out[2] = (size_t)I * row_bytes(H, L->up.qtype);
-    out[3] = (size_t)I * 4;
+    out[3] = (size_t)I * scales_per_row(L->up) * 4;
     out[4] = (size_t)H * row_bytes(I, L->down.qtype);
-    out[5] = (size_t)H * 4;
+    out[5] = (size_t)H * scales_per_row(L->down) * 4;
 }
 
 /* The device address of slow-tier memory: pinned host memory (mapped into

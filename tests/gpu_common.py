@@ -27,7 +27,7 @@ def to_device(L: synth.Layer):
     import quantized_routed_expert_sigmoid_amd as qre
 
     def qb(b):
-        return qre.QBank(b.storage.cuda().contiguous(), b.scale_storage.cuda().contiguous(), b.bits)
+        return qre.QBank(b.storage.cuda().contiguous(), b.scale_storage.cuda().contiguous(), b.bits, b.group)
     w = L.w
     shared = [qb(L.sh_gate), qb(L.sh_up), qb(L.sh_down)] if w.has_shared else None
     return qre.MoELayer(w.hidden, w.inter, w.n_experts, w.top_k, w.rsf,
@@ -81,9 +81,10 @@ def to_slow_tier(L: synth.Layer, dev, where="host"):
 
     def qb(b):
         if where == "device":
-            return qre.QBank(b.storage.cuda().contiguous(), b.scale_storage.cuda().contiguous(), b.bits)
+            return qre.QBank(b.storage.cuda().contiguous(), b.scale_storage.cuda().contiguous(), b.bits,
+                             b.group)
         return qre.QBank(pinned_copy(b.storage.contiguous()), pinned_copy(b.scale_storage.contiguous()),
-                         b.bits)
+                         b.bits, b.group)
     w = L.w
     return qre.MoELayer(w.hidden, w.inter, w.n_experts, w.top_k, w.rsf, dev.router_w, dev.router_bias,
                         qb(L.gate), qb(L.up), qb(L.down), dev.shared, w.n_group, w.topk_group, w.top_p)

@@ -151,17 +151,18 @@ def test_dispatch_bit_exact(qre, S, k, E):
     assert np.array_equal(act.cpu().numpy()[:n], ref["active"])
 
 
-def _ffn_case(bits, H, I, E, S, k, seed):
+def _ffn_case(bits, H, I, E, S, k, seed, g_gu=0, g_d=0):
     rng = np.random.default_rng(seed)
     lo, hi = {8: (-127, 127), 4: (-8, 7), 2: (-2, 1)}[bits]
 
-    def bank(rows, K):
+    def bank(rows, K, group):
         data = np.stack([np.stack([oracle.pack_row(rng.integers(lo, hi + 1, size=K).astype(np.int8), bits)
                                    for _ in range(rows)]) for _ in range(E)])
-        scale = (np.abs(rng.standard_normal((E, rows))) * 0.02).astype(np.float32)
+        ns = rows * (K // group) if group else rows
+        scale = (np.abs(rng.standard_normal((E, ns))) * 0.02).astype(np.float32)
         t, s = torch.from_numpy(data), torch.from_numpy(scale)
-        return synth.Bank(E, rows, K, bits, [t[i] for i in range(E)], [s[i] for i in range(E)], t, s)
-    g, u, d = bank(I, H), bank(I, H), bank(H, I)
+        return synth.Bank(E, rows, K, bits, [t[i] for i in range(E)], [s[i] for i in range(E)], t, s, group)
+    g, u, d = bank(I, H, g_gu), bank(I, H, g_gu), bank(H, I, g_d)
     x = rng.standard_normal((S, H)).astype(np.float32)
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(S)]).astype(np.int32)
     return g, u, d, x, ids
@@ -190,6 +191,37 @@ def test_expert_ffn_bit_exact(qre, bits, H, I, E, S, k, scale):
 
     def qb(b):
         return qre.QBank(b.storage.cuda(), b.scale_storage.cuda(), bits)
+    y = qre.expert_ffn_q(qb(g), qb(u), qb(d), torch.from_numpy(xq).cuda(), torch.from_numpy(xd).cuda(),
+                         torch.from_numpy(disp["offsets"]).cuda(), torch.from_numpy(disp["sorted"]).cuda(), k)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert got.tobytes() == y_ref.tobytes(), f"max diff {np.max(np.abs(got - y_ref))}"
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("H,I,E,S,k,g_gu,g_d,scale", [
+    (256, 128, 16, 13, 3, 64, 32, 1.0),    # GEMV units
+    (96, 64, 4, 9, 2, 32, 64, 1.0),        # ragged down tail; one down group per row
+    (512, 256, 3, 11, 3, 128, 256, 1.0),   # matrix cores
+    (256, 160, 2, 100, 2, 256, 32, 1.0),   # several MFMA units, ragged N tile
+    (96, 96, 5, 40, 3, 32, 96, 1.0),       # MFMA with ragged rows and K tails
+    (256, 128, 3, 24, 2, 32, 32, 1e-36),   # tiny activations (subnormal products)
+])
+def test_expert_ffn_grouped_scales_bit_exact(qre, bits, H, I, E, S, k, g_gu, g_d, scale):
+    """Group-wise weight scales on both kernel families, y bit for bit."""
+    say(f"ffn grouped bits={bits} H={H} I={I} E={E} S={S} k={k} groups={g_gu}/{g_d} scale={scale}")
+    g, u, d, x, ids = _ffn_case(bits, H, I, E, S, k, seed=bits * 100 + H + S + 7, g_gu=g_gu, g_d=g_d)
+    x = (x * np.float32(scale)).astype(np.float32)
+    xq, xd = oracle.quantize_q8_0(x)
+    disp = oracle.dispatch(ids, E)
+    y_ref = np.empty((S * k, H), np.float32)
+    G, U, D = oracle.bank(g), oracle.bank(u), oracle.bank(d)
+    flat = ids.reshape(-1)
+    for pos, p in enumerate(disp["sorted"]):
+        y_ref[pos] = oracle.expert_ffn(G, U, D, int(flat[p]), xq[p // k], xd[p // k])["y"]
+
+    def qb(b):
+        return qre.QBank(b.storage.cuda(), b.scale_storage.cuda(), bits, b.group)
     y = qre.expert_ffn_q(qb(g), qb(u), qb(d), torch.from_numpy(xq).cuda(), torch.from_numpy(xd).cuda(),
                          torch.from_numpy(disp["offsets"]).cuda(), torch.from_numpy(disp["sorted"]).cuda(), k)
     torch.cuda.synchronize()
@@ -250,6 +282,17 @@ SMALL_LAYERS = {
                            n_group=4, topk_group=2, top_p=0.8),
     "rv_mfma": dict(name="rvf", layer="rvf", bits=4, hidden=512, inter=256, n_experts=16, top_k=4, S=80,
                     has_shared=True, rsf=2.5, var_router=1.0 / 512, n_group=4, topk_group=2, top_p=0.75),
+    # group-wise weight scales on every path
+    "grp_decode_int4": dict(name="gd4", layer="gd4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
+                            S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, group=128),
+    "grp_decode_many_slots": dict(name="gdm", layer="gdm", bits=4, hidden=256, inter=2048, n_experts=64,
+                                  top_k=32, S=1, has_shared=True, var_router=1.0 / 256, group=256),
+    "grp_small_int8": dict(name="gs8", layer="gs8", bits=8, n_experts=32, top_k=4, S=6, has_shared=True,
+                           group=32),
+    "grp_mfma_int2": dict(name="gm2", layer="gm2", bits=2, hidden=256, inter=192, n_experts=4, top_k=2,
+                          S=150, has_shared=True, group=64),
+    "grp_mfma_int4_topp": dict(name="gmf", layer="gmf", bits=4, hidden=512, inter=256, n_experts=16, top_k=4,
+                               S=80, has_shared=True, rsf=2.5, var_router=1.0 / 512, top_p=0.75, group=128),
 }
 
 

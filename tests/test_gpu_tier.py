@@ -42,9 +42,12 @@ TIER_CASES = {
                               has_shared=True, n_group=4, topk_group=2, top_p=0.8),
     "many_slots_int2": dict(name="tm2", layer="tm2", bits=2, hidden=256, inter=96, n_experts=64, top_k=16,
                             S=3, has_shared=False, var_router=1.0 / 256),
+    # group-wise weight scales: the slot bank carries K/group scales per row
+    "grouped_int4": dict(name="tg4", layer="gd4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
+                         S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, group=128),
 }
 SLOTS = {"decode_int4": [1, 8, 64], "long_int4_shared": [1, 3, 16], "mfma_int4": [1, 3, 8],
-         "small_topp_groups": [2, 9], "many_slots_int2": [2, 17, 40]}
+         "small_topp_groups": [2, 9], "many_slots_int2": [2, 17, 40], "grouped_int4": [2, 12]}
 # batch order with repeats, so that later batches hit what earlier ones loaded
 ORDER = [0, 1, 0, 2, 1, 0, 3]
 

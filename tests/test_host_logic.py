@@ -133,6 +133,25 @@ def test_tier_sizes_and_validation_before_any_hip_call(capi):
     lib.colibri_tier_destroy(None)
 
 
+def test_group_wise_scale_validation(capi):
+    lib = capi.lib()
+    f = 0x10000000
+
+    def qb(n, rows, K, q=4, group=0):
+        return capi.QBankDesc(f, f, n, rows, K, q, group)
+    ok = _fake_layer(capi, gate=qb(16, 128, 256, group=128), up=qb(16, 128, 256, group=128),
+                     down=qb(16, 256, 128, group=32))
+    assert lib.colibri_workspace_bytes(ctypes.byref(ok), 4) > 0
+    for bad in (dict(gate=qb(16, 128, 256, group=48), up=qb(16, 128, 256, group=48)),   # not a multiple of 32
+                dict(gate=qb(16, 128, 256, group=96), up=qb(16, 128, 256, group=96)),   # does not divide K
+                dict(down=qb(16, 256, 128, group=-32)),
+                dict(gate=qb(16, 128, 256, group=512), up=qb(16, 128, 256, group=512))):  # larger than K
+        assert lib.colibri_workspace_bytes(ctypes.byref(_fake_layer(capi, **bad)), 4) == 0
+    # gate and up must share the group size (as they share the width)
+    mixed = _fake_layer(capi, gate=qb(16, 128, 256, group=64), up=qb(16, 128, 256, group=128))
+    assert lib.colibri_workspace_bytes(ctypes.byref(mixed), 4) == 0
+
+
 def test_workspace_size_and_invalid_layers(capi):
     lib = capi.lib()
     L = _fake_layer(capi)
