@@ -56,24 +56,31 @@ def parse():
                     help="tiered layer stack with and without router look-ahead prefetch (prints its "
                          "own JSON line)")
     ap.add_argument("--stack-layers", type=int, default=4)
+    ap.add_argument("--group", type=int, default=0,
+                    help="group-wise weight scales: one fp32 scale per this many columns (0: per row)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one elementwise fp32 copy of this many MiB (a known-size kernel "
                          "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
+def scales_per_row(w, K):
+    """fp32 weight scales per row of a matrix with K columns."""
+    return K // w.group if w.group else 1
+
+
 def expert_bytes(w):
-    """Packed weights plus row scales of one expert (gate, up, down)."""
+    """Packed weights plus scales of one expert (gate, up, down)."""
     H, I, b = w.hidden, w.inter, w.bits
-    return 3 * H * I * b // 8 + (2 * I + H) * 4
+    return 3 * H * I * b // 8 + (2 * I * scales_per_row(w, H) + H * scales_per_row(w, I)) * 4
 
 
 def stage_bytes(w, n_units_touched, S):
     """Algorithmic HBM bytes of each stage for one step (n_units_touched =
     distinct routed experts + the shared expert)."""
     H, I, E, k, b = w.hidden, w.inter, w.n_experts, w.top_k, w.bits
-    gu = n_units_touched * (2 * I * H * b // 8 + 2 * I * 4)
-    dn = n_units_touched * (H * I * b // 8 + H * 4)
+    gu = n_units_touched * (2 * I * H * b // 8 + 2 * I * scales_per_row(w, H) * 4)
+    dn = n_units_touched * (H * I * b // 8 + H * scales_per_row(w, I) * 4)
     return {
         "route": E * H * 4 + E * 4 + S * H * 4,
         "gate_up": gu,
@@ -149,7 +156,7 @@ def measured_traffic(w, stage):
         return None
     with open(TRAFFIC_RECORD) as f:
         rec = json.load(f)
-    if rec.get("workload") != w.name or stage != "gate_up":
+    if rec.get("workload") != w.name or stage != "gate_up" or w.group:
         return None
     h = hashlib.sha256()
     for src in rec["sources"]:
@@ -174,7 +181,7 @@ def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True)
     base = synth.make_layer(w, device="cuda")
 
     def qb(b):
-        return qre.QBank(b.storage, b.scale_storage, b.bits)
+        return qre.QBank(b.storage, b.scale_storage, b.bits, b.group)
 
     def mk(L):
         sh = [qb(L.sh_gate), qb(L.sh_up), qb(L.sh_down)] if w.has_shared else None
@@ -464,6 +471,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = synth.WORKLOADS[args.workload]
+    if args.group:
+        w = synth.scaled(w, group=args.group)
     if args.tier_stack:
         steps = args.steps or 100
         r = run_tier_stack(qre, synth, torch, w, args.stack_layers, steps)
@@ -516,7 +525,9 @@ def main():
         "dtype": "int8",
         "data": "synthetic (seeded SplitMix64 weights and activations; no checkpoint)",
         "config": {"workload": f"{w.name}: MoE layer H={w.hidden} I={w.inter} E={w.n_experts} "
-                               f"top-{w.top_k} int{w.bits} weights + shared expert, S={w.S}",
+                               f"top-{w.top_k} int{w.bits} weights"
+                               + (f" with one scale per {w.group} columns" if w.group else "")
+                               + f" + shared expert, S={w.S}",
                    "S": w.S, "weights": f"int{w.bits}", "layer_copies_rotated": args.copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": stage_kernel(w, dom), "achieved": achieved,
@@ -528,7 +539,7 @@ def main():
                   "stage_ms": stage_ms},
     }
     if not args.no_prefill and args.workload == "decode":
-        wp = synth.WORKLOADS["prefill"]
+        wp = synth.scaled(synth.WORKLOADS["prefill"], group=args.group)
         rp = run_workload(qre, synth, torch, wp, 20, 3, 2)
         msp = rp["gpu_ms"] / 20
         Up = rp["mean_unique_experts"] + 1

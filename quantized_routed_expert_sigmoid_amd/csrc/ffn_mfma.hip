@@ -47,23 +47,26 @@ struct Cfg {
     static constexpr int kXpt = kStep == 8 ? 8 : 4;                   /* activation words per loading thread */
 };
 
-/* LDS of the K loop, double-buffered. */
-template <int BITS>
+/* LDS of the K loop, double-buffered.  GROUPED kernels also stage each
+ * weight row's group-wise scale of every block of the step (one word when
+ * not grouped, so that the per-row kernels keep their LDS size). */
+template <int BITS, bool GROUPED = false>
 struct KLds {
     uint32_t a[2][64 * Cfg<BITS>::kRowStride];              /* weight rows, packed words */
     uint32_t b[2][Cfg<BITS>::kStep][4][kTok][2];           /* operand words 2g, 2g+1 per (block, g, token) */
     float ds[2][Cfg<BITS>::kStep][kTok];                    /* block scale * 2^-(8-b) */
     float dr[2][Cfg<BITS>::kStep][kTok];                    /* block scale */
     int flag[2];                                            /* step whose scales need the exact-shift fold */
+    float ws[2][GROUPED ? 64 * Cfg<BITS>::kStep : 1];       /* [row][block of the step] weight scale */
 };
 
 struct EpiLds {
     float v[64][kTok + 1]; /* [row dot][token] */
 };
 
-template <int BITS>
+template <int BITS, bool GROUPED = false>
 union MfmaShared {
-    KLds<BITS> k;
+    KLds<BITS, GROUPED> k;
     EpiLds e;
 };
 
@@ -124,12 +127,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-/* One thread's share of a K step's global loads. */
-template <int BITS>
+/* One thread's share of a K step's global loads (GROUPED: also the
+ * weight row's scales of its kBpt blocks). */
+template <int BITS, bool GROUPED = false>
 struct Stage {
     uint32_t w[Cfg<BITS>::kBpt * BITS];
     uint32_t x[Cfg<BITS>::kXpt];
     float d;
+    float sc[GROUPED ? Cfg<BITS>::kBpt : 1];
 };
 
 /* Where a thread loads from.  Weights: row dot (l >> 2), blocks kBpt*(l & 3)
@@ -142,14 +147,21 @@ struct LoadLane {
     const int8_t* xrow;
     const float* xdrow;
     int nb;
+    const float* wsrow; /* group-wise scales of the weight row (GROUPED kernels; gb == 0: none) */
+    int gb;             /* blocks per scale */
 };
 
-template <int BITS>
-__device__ __forceinline__ void fetch(Stage<BITS>& P, const LoadLane& L, int st)
+template <int BITS, bool GROUPED>
+__device__ __forceinline__ void fetch(Stage<BITS, GROUPED>& P, const LoadLane& L, int st)
 {
     using C = Cfg<BITS>;
     const int l = threadIdx.x;
     const int wb0 = st * C::kStep + C::kBpt * (l & 3);
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int i = 0; i < C::kBpt; ++i)
+            P.sc[i] = L.gb ? L.wsrow[min(wb0 + i, L.nb - 1) / L.gb] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < C::kBpt; ++i) {
         const int b = min(wb0 + i, L.nb - 1);
@@ -182,12 +194,17 @@ __device__ __forceinline__ void fetch(Stage<BITS>& P, const LoadLane& L, int st)
     }
 }
 
-template <int BITS>
-__device__ __forceinline__ void commit(const Stage<BITS>& P, KLds<BITS>& S, int buf, int st)
+template <int BITS, bool GROUPED>
+__device__ __forceinline__ void commit(const Stage<BITS, GROUPED>& P, KLds<BITS, GROUPED>& S, int buf, int st)
 {
     using C = Cfg<BITS>;
     constexpr int SHIFT = 8 - BITS;
     const int l = threadIdx.x;
+    if constexpr (GROUPED) {
+#pragma unroll
+        for (int i = 0; i < C::kBpt; ++i)
+            S.ws[buf][(l >> 2) * C::kStep + C::kBpt * (l & 3) + i] = P.sc[i];
+    }
     uint32_t* ad = &S.a[buf][(l >> 2) * C::kRowStride + C::kBpt * BITS * (l & 3)];
 #pragma unroll
     for (int i = 0; i < C::kBpt * BITS; ++i)
@@ -243,8 +260,8 @@ __device__ __forceinline__ long a_operand(const uint32_t* w, int g)
 }
 
 /* One block of a K step: the MFMA of each N-tile and its fold into acc. */
-template <int BITS, int NT, bool EXACT_SHIFT>
-__device__ __forceinline__ void block_mfma(const KLds<BITS>& S, int buf, int j, const uint32_t* arow,
+template <int BITS, int NT, bool EXACT_SHIFT, class KL>
+__device__ __forceinline__ void block_mfma(const KL& S, int buf, int j, const uint32_t* arow,
                                            int r, int g, float (&acc)[2][4])
 {
     constexpr int SHIFT = 8 - BITS;
@@ -269,27 +286,22 @@ __device__ __forceinline__ void block_mfma(const KLds<BITS>& S, int buf, int j, 
     }
 }
 
-/* Group-wise weight scales of a lane's four row dots (v = 0..3): gb blocks
- * per scale, ws[v] the row's scales; gb == 0 for per-row scales. */
-struct RowGroups {
-    const float* ws[4];
-    int gb;
-};
-
-/* One block with group-wise scales: coefficient s[v][b / gb] * d (the
- * canonical fp32 product) for each row dot, on the exact partials (the
- * 2^(8-b) factor of the packed weights shifted back out). */
+/* One block with group-wise scales: coefficient s * d (the canonical fp32
+ * product, s the row's scale of the block staged in LDS) for each of the
+ * lane's row dots 16w + 4(lane/16) + v, on the exact partials (the 2^(8-b)
+ * factor of the packed weights shifted back out). */
 template <int BITS, int NT>
-__device__ __forceinline__ void block_mfma_grouped(const KLds<BITS>& S, int buf, int j, const uint32_t* arow,
-                                                   int r, int g, float (&acc)[2][4], const RowGroups& rg,
-                                                   int gidx)
+__device__ __forceinline__ void block_mfma_grouped(const KLds<BITS, true>& S, int buf, int j,
+                                                   const uint32_t* arow, int r, int g, float (&acc)[2][4])
 {
+    using C = Cfg<BITS>;
     constexpr int SHIFT = 8 - BITS;
+    const int wv = threadIdx.x >> 6;
     const long A = a_operand<BITS>(arow + j * BITS, g);
     float wsv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-        wsv[v] = rg.ws[v][gidx];
+        wsv[v] = S.ws[buf][(16 * wv + 4 * g + v) * C::kStep + j];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int t = 16 * n + r;
@@ -323,8 +335,8 @@ __device__ __forceinline__ void flush(float (&acc)[2][4], float (&tot)[2][4])
  * before it).  Any other step checks each block: the row end, the group
  * boundaries (a repeated boundary adds +0) and the shift-back fold. */
 template <int BITS, int NT, bool GROUPED>
-__device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int nb, int bnd1, int bnd2,
-                                     int bnd3, float (&acc)[2][4], float (&tot)[2][4], const RowGroups& rg)
+__device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int st, int nb, int bnd1,
+                                     int bnd2, int bnd3, float (&acc)[2][4], float (&tot)[2][4], int gb)
 {
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -334,14 +346,23 @@ __device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int n
     if (b0 >= nb)
         return;
     if constexpr (GROUPED) {
-        if (rg.gb) {
+        if (gb) {
+            const bool inner_g = (bnd1 > b0 && bnd1 < b1) || (bnd2 > b0 && bnd2 < b1) || (bnd3 > b0 && bnd3 < b1);
+            if (b1 <= nb && !inner_g) {
+                if (b0 == bnd1 || b0 == bnd2 || b0 == bnd3)
+                    flush<NT>(acc, tot);
+#pragma unroll
+                for (int j = 0; j < C::kStep; ++j)
+                    block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc);
+                return;
+            }
             for (int j = 0; j < C::kStep; ++j) {
                 const int b = b0 + j;
                 if (b >= nb)
                     break;
                 if (b == bnd1 || b == bnd2 || b == bnd3)
                     flush<NT>(acc, tot);
-                block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, rg, b / rg.gb);
+                block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc);
             }
             return;
         }
@@ -379,8 +400,7 @@ __device__ __forceinline__ void step(const KLds<BITS>& S, int buf, int st, int n
  * so the two register sets stay put across iterations and each commit waits
  * only for its own loads. */
 template <int BITS, int NT, bool GROUPED>
-__device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, float (&tot)[2][4],
-                                          const RowGroups& rg)
+__device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane& L, float (&tot)[2][4])
 {
     using C = Cfg<BITS>;
     const int nb = L.nb;
@@ -394,23 +414,23 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, floa
             tot[n][v] = 0.0f;
         }
     const int nsteps = (nb + C::kStep - 1) / C::kStep;
-    Stage<BITS> P0, P1;
-    fetch<BITS>(P0, L, 0);
-    fetch<BITS>(P1, L, 1);
+    Stage<BITS, GROUPED> P0, P1;
+    fetch<BITS, GROUPED>(P0, L, 0);
+    fetch<BITS, GROUPED>(P1, L, 1);
     if (threadIdx.x < 2)
         S.flag[threadIdx.x] = -1;
     __syncthreads();
-    commit<BITS>(P0, S, 0, 0);
-    fetch<BITS>(P0, L, 2);
+    commit<BITS, GROUPED>(P0, S, 0, 0);
+    fetch<BITS, GROUPED>(P0, L, 2);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
-        step<BITS, NT, GROUPED>(S, 0, st, nb, bnd1, bnd2, bnd3, acc, tot, rg);
-        commit<BITS>(P1, S, 1, st + 1);
-        fetch<BITS>(P1, L, st + 3);
+        step<BITS, NT, GROUPED>(S, 0, st, nb, bnd1, bnd2, bnd3, acc, tot, L.gb);
+        commit<BITS, GROUPED>(P1, S, 1, st + 1);
+        fetch<BITS, GROUPED>(P1, L, st + 3);
         __syncthreads();
-        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, bnd1, bnd2, bnd3, acc, tot, rg);
-        commit<BITS>(P0, S, 0, st + 2);
-        fetch<BITS>(P0, L, st + 4);
+        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, bnd1, bnd2, bnd3, acc, tot, L.gb);
+        commit<BITS, GROUPED>(P0, S, 0, st + 2);
+        fetch<BITS, GROUPED>(P0, L, st + 4);
         __syncthreads();
     }
 #pragma unroll
@@ -421,13 +441,13 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS>& S, const LoadLane& L, floa
 }
 
 template <int BITS, bool GROUPED>
-__device__ __forceinline__ void mfma_k_loop(KLds<BITS>& S, const LoadLane& L, int ntiles,
-                                            float (&tot)[2][4], const RowGroups& rg)
+__device__ __forceinline__ void mfma_k_loop(KLds<BITS, GROUPED>& S, const LoadLane& L, int ntiles,
+                                            float (&tot)[2][4])
 {
     if (ntiles > 1)
-        k_loop_nt<BITS, 2, GROUPED>(S, L, tot, rg);
+        k_loop_nt<BITS, 2, GROUPED>(S, L, tot);
     else
-        k_loop_nt<BITS, 1, GROUPED>(S, L, tot, rg);
+        k_loop_nt<BITS, 1, GROUPED>(S, L, tot);
 }
 
 } // namespace
@@ -437,7 +457,7 @@ __device__ __forceinline__ void mfma_k_loop(KLds<BITS>& S, const LoadLane& L, in
 template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
 {
-    __shared__ MfmaShared<BITS> sm;
+    __shared__ MfmaShared<BITS, GROUPED> sm;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = a.I / 32;
     MLoc M;
@@ -458,20 +478,14 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     L.xrow = a.xq + (int64_t)tok * a.H;
     L.xdrow = a.xd + (int64_t)tok * nb;
     L.nb = nb;
+    L.gb = GROUPED ? sg.gu_gb : 0;
+    L.wsrow = L.gb ? (rd < 32 ? sg.gate_s : sg.up_s) + ((int64_t)e * a.I + M.rb * 32 + (rd & 31)) * (nb / L.gb)
+                   : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
     /* group-wise scales of the lane's row dots 16w + 4(lane/16) + v */
-    RowGroups rg;
-    rg.gb = GROUPED ? sg.gu_gb : 0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int rdot = 16 * wv + 4 * g + v;
-        rg.ws[v] = rg.gb ? (rdot < 32 ? sg.gate_s : sg.up_s) +
-                               ((int64_t)e * a.I + M.rb * 32 + (rdot & 31)) * (nb / rg.gb)
-                         : nullptr;
-    }
     float tot[2][4];
-    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot, rg);
+    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
 
     /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
      * h = silu(g) * u and one Q8_0 block of h per token */
@@ -479,7 +493,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     for (int v = 0; v < 4; ++v) {
         const int rdot = 16 * wv + 4 * g + v;
         const float sc =
-            rg.gb ? 1.0f : (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
+            L.gb ? 1.0f : (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
@@ -517,7 +531,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
 template <int BITS, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
 {
-    __shared__ MfmaShared<BITS> sm;
+    __shared__ MfmaShared<BITS, GROUPED> sm;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = (a.H + 63) / 64;
     MLoc M;
@@ -537,23 +551,18 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     L.xrow = a.hq + row_in * a.I;
     L.xdrow = a.hd + row_in * nb;
     L.nb = nb;
+    L.gb = GROUPED ? sg.d_gb : 0;
+    L.wsrow = L.gb ? sg.down_s + ((int64_t)e * a.H + (row < a.H ? row : 0)) * (nb / L.gb) : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
-    RowGroups rg;
-    rg.gb = GROUPED ? sg.d_gb : 0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int n_out = M.rb * 64 + 16 * wv + 4 * g + v;
-        rg.ws[v] = rg.gb ? sg.down_s + ((int64_t)e * a.H + min(n_out, a.H - 1)) * (nb / rg.gb) : nullptr;
-    }
     float tot[2][4];
-    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot, rg);
+    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int rr = 16 * wv + 4 * g + v;
         const int n_out = M.rb * 64 + rr;
-        const float sc = n_out < a.H ? (rg.gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n_out]) : 0.0f;
+        const float sc = n_out < a.H ? (L.gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n_out]) : 0.0f;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
