@@ -32,27 +32,27 @@ __device__ __forceinline__ float key_value(uint32_t key)
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-/* Wave maximum of key over the lane's experts e with group(e) == g (all
+/* Wave maximum of key over the lane's PL experts e with group(e) == g (all
  * experts when g < 0), then the lowest such expert holding it; returns the
  * key and writes the expert to *e_out (-1 when the set is empty). */
-__device__ __forceinline__ uint32_t argmax_key(const uint32_t (&key)[kMaxPerLane], int per_lane, int E, int gsz,
-                                               int g, int skip_e, int* e_out)
+template <int PL>
+__device__ __forceinline__ uint32_t argmax_key(const uint32_t (&key)[PL], int E, int gsz, int g, int skip_e,
+                                               int* e_out)
 {
     const int lane = threadIdx.x & 63;
     uint32_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
         const int e = lane + 64 * i;
-        if (i < per_lane && e < E && (g < 0 || e / gsz == g) && e != skip_e)
+        if (e < E && (g < 0 || e / gsz == g) && e != skip_e)
             best = key[i] > best ? key[i] : best;
     }
     best = wave_reduce_u32<true>(best);
     uint32_t mine = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
         const int e = lane + 64 * i;
-        if (i < per_lane && e < E && (g < 0 || e / gsz == g) && e != skip_e && key[i] == best &&
-            mine == 0xFFFFFFFFu)
+        if (e < E && (g < 0 || e / gsz == g) && e != skip_e && key[i] == best && mine == 0xFFFFFFFFu)
             mine = (uint32_t)e;
     }
     const uint32_t e = wave_reduce_u32<false>(mine);
@@ -77,19 +77,19 @@ __device__ __forceinline__ uint32_t argmax_key(const uint32_t (&key)[kMaxPerLane
  * oracle, up to the first cumulative share >= top_p.  Slots past the cut get
  * id -1 and weight 0; the kept weights are renormalised over the kept slots
  * (denominator in slot order). */
-__device__ __forceinline__ void select_token(const float* lt, const float* bias, int32_t E, int32_t k,
-                                             float rsf, int32_t* ids_out, float* w_out, float* sel_s,
-                                             int32_t* ids_lds, int32_t n_parts = 1,
-                                             int64_t part_stride = 0, RouteOpts opt = RouteOpts{1, 1, 1.0f})
+template <int PL>
+__device__ __forceinline__ void select_token_pl(const float* lt, const float* bias, int32_t E, int32_t k,
+                                                float rsf, int32_t* ids_out, float* w_out, float* sel_s,
+                                                int32_t* ids_lds, int32_t n_parts, int64_t part_stride,
+                                                RouteOpts opt)
 {
     const int lane = threadIdx.x & 63;
-    const int per_lane = (E + 63) / 64; /* uniform */
-    float s[kMaxPerLane];
-    uint32_t key[kMaxPerLane]; /* order-preserving bits of the biased score; 0 = unavailable */
+    float s[PL];
+    uint32_t key[PL]; /* order-preserving bits of the biased score; 0 = unavailable */
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
         const int e = lane + 64 * i;
-        if (i < per_lane && e < E) {
+        if (e < E) {
             float l = lt[e];
             for (int p = 1; p < n_parts; ++p) /* K slices, added in order */
                 l = l + lt[p * part_stride + e];
@@ -106,8 +106,8 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
         float gscore = 0.0f;
         for (int g = 0; g < G; ++g) {
             int e1, e2;
-            const uint32_t k1 = argmax_key(key, per_lane, E, gsz, g, -1, &e1);
-            const uint32_t k2 = argmax_key(key, per_lane, E, gsz, g, e1, &e2);
+            const uint32_t k1 = argmax_key<PL>(key, E, gsz, g, -1, &e1);
+            const uint32_t k2 = argmax_key<PL>(key, E, gsz, g, e1, &e2);
             if (lane == g)
                 gscore = key_value(k1) + key_value(k2);
         }
@@ -121,9 +121,9 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
                 gkey = 0;
         }
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
+        for (int i = 0; i < PL; ++i) {
             const int e = lane + 64 * i;
-            if (i < per_lane && e < E && !((kept >> (e / gsz)) & 1))
+            if (e < E && !((kept >> (e / gsz)) & 1))
                 key[i] = 0;
         }
     }
@@ -131,20 +131,19 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
         /* best score, then the lowest expert id holding it */
         uint32_t best = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (i < per_lane)
-                best = key[i] > best ? key[i] : best;
+        for (int i = 0; i < PL; ++i)
+            best = key[i] > best ? key[i] : best;
         best = wave_reduce_u32<true>(best);
         uint32_t mine = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
-            if (i < per_lane && key[i] == best && mine == 0xFFFFFFFFu)
+        for (int i = 0; i < PL; ++i)
+            if (key[i] == best && mine == 0xFFFFFFFFu)
                 mine = (uint32_t)(lane + 64 * i);
         const int e = (int)wave_reduce_u32<false>(mine);
         const int ie = e >> 6; /* uniform */
         float cand = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
+        for (int i = 0; i < PL; ++i) {
             if (i == ie) {
                 cand = s[i];
                 if (lane == (e & 63))
@@ -217,6 +216,27 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
         denom += sel_s[j];
     if (lane < k)
         w_out[lane] = rsf * (sel_s[lane] / denom);
+}
+
+/* Dispatches on the experts per lane (a multiple of 64 up to E), so that the
+ * per-lane loops run exactly as many times as there are experts. */
+__device__ __forceinline__ void select_token(const float* lt, const float* bias, int32_t E, int32_t k,
+                                             float rsf, int32_t* ids_out, float* w_out, float* sel_s,
+                                             int32_t* ids_lds, int32_t n_parts = 1,
+                                             int64_t part_stride = 0, RouteOpts opt = RouteOpts{1, 1, 1.0f})
+{
+    const int per_lane = (E + 63) / 64; /* uniform */
+    if (per_lane <= 1)
+        select_token_pl<1>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+    else if (per_lane <= 2)
+        select_token_pl<2>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+    else if (per_lane <= 4)
+        select_token_pl<4>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+    else if (per_lane <= 8)
+        select_token_pl<8>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+    else
+        select_token_pl<kMaxPerLane>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride,
+                                     opt);
 }
 
 } // namespace coli
