@@ -822,6 +822,8 @@ __device__ __forceinline__ int dc_unit(uint64_t kept, int n_kept, int k, int n, 
     return __builtin_ctzll(kept);
 }
 
+constexpr int kDcStage = 4;
+
 template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
 {
@@ -848,16 +850,34 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     /* compacted unit 0's pair is issued before h is staged */
     PairLoad<BITS, NI> A, B;
     pair_load<BITS, NI>(A, dc_rows(d, dc_unit(kept, n_kept, d.k, 0, all_kept), row0, rowbytes), rowbytes, 0, 2, nb);
-    for (int i = threadIdx.x; i < U * nb; i += 64 * kGroups) {
-        const int j = i / nb, b = i - j * nb;
-        const int u = dc_unit(kept, n_kept, d.k, j, all_kept);
-        uint32_t x[8], xa[8];
-        load_codes(a.hq + (int64_t)u * a.I + (int64_t)b * 32, x);
-        prep_activation<BITS>(x, xa);
-        uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
-        dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
-        dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
-        dls[i] = a.hd[(int64_t)u * nb + b];
+    /* each thread issues the loads of up to kDcStage (unit, block) items
+     * before it converts and stores any: one memory round trip, not one per
+     * item */
+    for (int i0 = threadIdx.x; i0 < U * nb; i0 += 64 * kGroups * kDcStage) {
+        uint32_t x[kDcStage][8];
+        float dv[kDcStage];
+#pragma unroll
+        for (int r = 0; r < kDcStage; ++r) {
+            const int i = i0 + r * 64 * kGroups;
+            if (i < U * nb) {
+                const int j = i / nb, b = i - j * nb;
+                const int u = dc_unit(kept, n_kept, d.k, j, all_kept);
+                load_codes(a.hq + (int64_t)u * a.I + (int64_t)b * 32, x[r]);
+                dv[r] = a.hd[(int64_t)u * nb + b];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kDcStage; ++r) {
+            const int i = i0 + r * 64 * kGroups;
+            if (i < U * nb) {
+                uint32_t xa[8];
+                prep_activation<BITS>(x[r], xa);
+                uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
+                dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+                dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+                dls[i] = dv[r];
+            }
+        }
     }
     __syncthreads();
 

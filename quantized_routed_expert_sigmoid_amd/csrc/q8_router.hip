@@ -56,8 +56,8 @@ hipError_t launch_quantize_q8_0(const float* x, int64_t n_blocks, int8_t* q, flo
 
 /* ---- router logits --------------------------------------------------------
  * Few tokens: one 256-thread workgroup per expert streams its router row once
- * (float4, coalesced, each wave a quarter of the row), keeps one partial sum
- * per token and reduces across lanes and waves.  Many tokens: fp32 matrix
+ * (float4, coalesced, thread t taking float4 t, t + 256, ...), keeps one
+ * partial sum per token and reduces across lanes and waves.  Many tokens: fp32 matrix
  * cores over 64 x 64 output tiles and K slices.  Both sum in fp32 (the order is free: only the
  * selection decision depends on it, and inputs keep a score gap).
  *
@@ -87,6 +87,10 @@ __device__ __forceinline__ void quantize_blocks(const float* x, int64_t n_blocks
         d[blk] = scale;
 }
 
+/* ST: tokens the instantiation carries (S <= ST; tokens past S recompute the
+ * last one and are not stored, so no load sits under a branch); CH: float4
+ * per thread per round. */
+template <int ST, int CH>
 __global__ __launch_bounds__(256) void router_logits_small(const float* __restrict__ x, int32_t S,
                                                            int32_t H, int32_t E,
                                                            const float* __restrict__ w,
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void router_logits_small(const float* __restri
                                                            int8_t* __restrict__ xq,
                                                            float* __restrict__ xd)
 {
-    __shared__ float part[4][kSmallS];
+    __shared__ float part[4][ST];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int e = blockIdx.x;
     if (e >= E) {
@@ -104,27 +108,45 @@ __global__ __launch_bounds__(256) void router_logits_small(const float* __restri
         return;
     }
     const float4* wr = reinterpret_cast<const float4*>(w + (int64_t)e * H);
-    float acc[kSmallS];
+    float acc[ST];
 #pragma unroll
-    for (int t = 0; t < kSmallS; ++t)
+    for (int t = 0; t < ST; ++t)
         acc[t] = 0.0f;
     const int n4 = H / 4;
-    const int q0 = (wv * n4) / 4, q1 = ((wv + 1) * n4) / 4;
-    for (int i = q0 + lane; i < q1; i += 64) {
-        const float4 wv4 = wr[i];
+    /* a round: each thread issues its CH row loads and every token's
+     * matching x loads before any fma -- one memory round trip per round */
+    for (int i0 = threadIdx.x; i0 < n4; i0 += 256 * CH) {
+        float4 wv4[CH];
+        float m[CH];
 #pragma unroll
-        for (int t = 0; t < kSmallS; ++t) {
-            if (t < S) {
-                const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)t * H)[i];
-                acc[t] = __builtin_fmaf(wv4.x, xv.x, acc[t]);
-                acc[t] = __builtin_fmaf(wv4.y, xv.y, acc[t]);
-                acc[t] = __builtin_fmaf(wv4.z, xv.z, acc[t]);
-                acc[t] = __builtin_fmaf(wv4.w, xv.w, acc[t]);
+        for (int u = 0; u < CH; ++u) {
+            /* past the row the last float4 is loaded (in bounds) and its
+             * products are multiplied by 0 (no branch, no early wait) */
+            const int i = i0 + 256 * u;
+            wv4[u] = wr[min(i, n4 - 1)];
+            m[u] = i < n4 ? 1.0f : 0.0f;
+        }
+        float4 xv[ST][CH];
+#pragma unroll
+        for (int t = 0; t < ST; ++t) {
+            const float4* xt = reinterpret_cast<const float4*>(x + (int64_t)min(t, S - 1) * H);
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                xv[t][u] = xt[min(i0 + 256 * u, n4 - 1)];
+        }
+#pragma unroll
+        for (int t = 0; t < ST; ++t) {
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                acc[t] = __builtin_fmaf(wv4[u].x * m[u], xv[t][u].x, acc[t]);
+                acc[t] = __builtin_fmaf(wv4[u].y * m[u], xv[t][u].y, acc[t]);
+                acc[t] = __builtin_fmaf(wv4[u].z * m[u], xv[t][u].z, acc[t]);
+                acc[t] = __builtin_fmaf(wv4[u].w * m[u], xv[t][u].w, acc[t]);
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < kSmallS; ++t) {
+    for (int t = 0; t < ST; ++t) {
         const float s = wave_sum(acc[t]);
         if (lane == 0)
             part[wv][t] = s;
@@ -133,6 +155,20 @@ __global__ __launch_bounds__(256) void router_logits_small(const float* __restri
     if (threadIdx.x < S)
         logits[(int64_t)threadIdx.x * E + e] =
             ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+}
+
+static void launch_logits_small(dim3 grid, int32_t S, hipStream_t st, const float* x, int32_t H, int32_t E,
+                                const float* w, float* logits, int8_t* xq, float* xd)
+{
+    const dim3 block(256);
+    if (S <= 1)
+        hipLaunchKernelGGL((router_logits_small<1, 8>), grid, block, 0, st, x, S, H, E, w, logits, xq, xd);
+    else if (S <= 2)
+        hipLaunchKernelGGL((router_logits_small<2, 8>), grid, block, 0, st, x, S, H, E, w, logits, xq, xd);
+    else if (S <= 4)
+        hipLaunchKernelGGL((router_logits_small<4, 4>), grid, block, 0, st, x, S, H, E, w, logits, xq, xd);
+    else
+        hipLaunchKernelGGL((router_logits_small<kSmallS, 2>), grid, block, 0, st, x, S, H, E, w, logits, xq, xd);
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -223,8 +259,7 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
     if (S == 0)
         return hipSuccess;
     if (S <= kSmallS) {
-        hipLaunchKernelGGL(router_logits_small, dim3(E), dim3(256), 0, st, x, S, H, E, w, logits,
-                           (int8_t*)nullptr, (float*)nullptr);
+        launch_logits_small(dim3(E), S, st, x, H, E, w, logits, (int8_t*)nullptr, (float*)nullptr);
     } else {
         const int32_t parts = router_parts(S, E, H);
         const int64_t tiles = (int64_t)((S + 63) / 64) * ((E + 63) / 64);
@@ -241,8 +276,7 @@ hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t
         return hipSuccess;
     const int64_t qthreads = (int64_t)S * (H / 32) * 8;
     const int64_t qgroups = (qthreads + 255) / 256;
-    hipLaunchKernelGGL(router_logits_small, dim3((uint32_t)(E + qgroups)), dim3(256), 0, st, x, S, H, E,
-                       w, logits, xq, xd);
+    launch_logits_small(dim3((uint32_t)(E + qgroups)), S, st, x, H, E, w, logits, xq, xd);
     return hipGetLastError();
 }
 
