@@ -12,6 +12,7 @@
 #define COLI_QDOT_FN __device__ __forceinline__
 #define COLI_PERM(a, b, s) __builtin_amdgcn_perm((a), (b), (s))
 #define COLI_SDOT4(a, b, c) __builtin_amdgcn_sdot4((int)(a), (int)(b), (c), false)
+#define COLI_SDOT8(a, b, c) __builtin_amdgcn_sdot8((int)(a), (int)(b), (c), false)
 #include "qdot.h"
 
 namespace coli {

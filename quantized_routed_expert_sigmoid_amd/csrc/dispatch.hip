@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
     int32_t* __restrict__ active, int32_t* __restrict__ n_active, UnitLists ul)
 {
     __shared__ DispatchShared sh;
-    __shared__ float sel_s[kSmallS][128];
+    __shared__ __attribute__((aligned(16))) float sel_s[kSmallS][kSelScratch];
     __shared__ int32_t sel_ids[kSmallS * 64];
     const int wv = threadIdx.x >> 6;
     if (wv < S)

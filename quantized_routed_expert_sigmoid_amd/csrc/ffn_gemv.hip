@@ -179,7 +179,7 @@ struct StepWeights {
 };
 
 /* LDS owned by one wave of a job: the partial transpose area, and the wave's
- * fold group of activation codes (already in block_partial operand order) and
+ * fold group of activation codes (already in block_dot operand order) and
  * block scales for each token of the unit. */
 template <int TMAX>
 struct WaveLds {
@@ -217,7 +217,7 @@ __device__ __forceinline__ void stage_activations(WaveLds<TMAX>& L, int b_begin,
         if (t < ntok && b < b_end) {
             uint32_t x[8], xa[8];
             load_codes(act[t] + (int64_t)b * 32, x);
-            prep_activation<BITS>(x, xa);
+            prep_dot<BITS>(x, xa);
             uint4* dst = reinterpret_cast<uint4*>(L.xa[t][lane]);
             dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
             dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
@@ -249,7 +249,7 @@ __device__ __forceinline__ void commit_token_block(const TokenBlock& T, WaveLds<
     const int lane = threadIdx.x & 63;
     if (b_begin + lane < b_end) {
         uint32_t xa[8];
-        prep_activation<BITS>(T.x, xa);
+        prep_dot<BITS>(T.x, xa);
         uint4* dst = reinterpret_cast<uint4*>(L.xa[0][lane]);
         dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
         dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
@@ -287,7 +287,7 @@ __device__ __forceinline__ void fold_step(const StepWeights<BITS>& W, int st, in
             }
 #pragma unroll
             for (int rho = 0; rho < 8; ++rho)
-                L.part[part_index(t, o, rho, j8)] = block_partial<BITS>(W.w[rho], xa);
+                L.part[part_index(t, o, rho, j8)] = block_dot<BITS>(W.w[rho], xa);
         }
     }
     wave_lds_sync();
@@ -525,11 +525,11 @@ inline int dec_ni(int nb)
 
 /* Dynamic LDS, in words: per wave the partials [16][nb | 1] (before the K
  * loop the selection's scratch), then the token's block scales [nb] and the
- * job's row sums [64]. */
+ * job's row sums [64]; at least the selection's scratch and ids (wave 0). */
 __host__ __device__ inline int dec_region(int nb)
 {
     const int p = kDecRows * (nb | 1);
-    return p > 256 ? p : 256;
+    return p > kSelScratch + 64 ? p : kSelScratch + 64;
 }
 
 __host__ __device__ inline size_t dec_lds_bytes(int nb)
@@ -567,7 +567,7 @@ __device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const
     for (int i = 0; i < NI; ++i) {
         const int b = c + 32 * i;
         if (row < kDecRows && b < nb)
-            P[row * sp + b] = block_partial<BITS>(L.w[i], xa[i]);
+            P[row * sp + b] = block_dot<BITS>(L.w[i], xa[i]);
     }
 }
 
@@ -636,20 +636,38 @@ __device__ __forceinline__ void dec_act_load(const int8_t* act, int nb, uint32_t
         load_codes(act + (int64_t)min(c + 32 * i, nb - 1) * 32, x[i]);
 }
 
-/* ... then put in operand order; every wave also writes the block scales
- * (the same values) so that its own reads follow its own writes. */
+/* The block scales b = lane + 64 i, i < kDlPre, loaded with the codes (so
+ * that their latency is spent before the weight stream starts) ... */
+constexpr int kDlPre = 4;
+
+__device__ __forceinline__ void dec_scale_load(const float* scl, int nb, float (&pre)[kDlPre])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kDlPre; ++i)
+        pre[i] = scl[min(lane + 64 * i, nb - 1)];
+}
+
+/* ... then the codes put in operand order; every wave also writes the block
+ * scales (the same values) so that its own reads follow its own writes. */
 template <int BITS, int NI>
-__device__ __forceinline__ void dec_act_prep(uint32_t (&x)[NI][8], const float* scl, int nb, float* dl)
+__device__ __forceinline__ void dec_act_prep(uint32_t (&x)[NI][8], const float (&pre)[kDlPre], const float* scl,
+                                             int nb, float* dl)
 {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         uint32_t xa[8];
-        prep_activation<BITS>(x[i], xa);
+        prep_dot<BITS>(x[i], xa);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             x[i][q] = xa[q];
     }
-    for (int b = threadIdx.x & 63; b < nb; b += 64)
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kDlPre; ++i)
+        if (lane + 64 * i < nb)
+            dl[lane + 64 * i] = pre[i];
+    for (int b = lane + 64 * kDlPre; b < nb; b += 64)
         dl[b] = scl[b];
     wave_lds_sync();
 }
@@ -657,7 +675,7 @@ __device__ __forceinline__ void dec_act_prep(uint32_t (&x)[NI][8], const float* 
 template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
 {
-    extern __shared__ int32_t dec_lds[];
+    extern __shared__ __attribute__((aligned(16))) int32_t dec_lds[];
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = a.I / 32;
@@ -673,19 +691,28 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     float* rsum = dl + nb;
     uint32_t xa[NI][8];
     dec_act_load<NI>(a.xq, nb, xa);
+    float dpre[kDlPre];
+    dec_scale_load(a.xd, nb, dpre);
     int e = 0;
+    bool prepped = false;
     if (routed) {
-        /* selection scratch in the wave's (not yet used) partial buffer */
-        float* sel_s = reinterpret_cast<float*>(P);
-        float* sel_w = sel_s + 128;
-        int32_t* sel_ids = P + 192;
-        const bool store = blockIdx.x == 0 && wv == 0;
-        select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids, store ? d.w : sel_w, sel_s,
-                     sel_ids, 1, 0, d.opt);
-        wave_lds_sync();
+        /* wave 0 alone selects (a chain of wave-wide steps, so it runs best
+         * without the other waves issuing the same work) while waves 1..3
+         * prepare their activations; the scratch is wave 0's (not yet used)
+         * partial buffer */
+        float* sel_s = reinterpret_cast<float*>(dec_lds);
+        int32_t* sel_ids = dec_lds + kSelScratch;
+        if (wv == 0) {
+            const bool store = blockIdx.x == 0; /* the others need the ids only */
+            select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids, store ? d.w : nullptr, sel_s,
+                         sel_ids, 1, 0, d.opt);
+        } else {
+            dec_act_prep<BITS, NI>(xa, dpre, a.xd, nb, dl);
+            prepped = true;
+        }
+        __syncthreads();
         const int sel = sel_ids[u];
-        wave_lds_sync();
-        if (sel < 0) /* slot dropped by top-p: every wave sees the same selection */
+        if (sel < 0) /* slot dropped by top-p: the whole workgroup leaves */
             return;
         e = min(sel, sg.n_mat - 1);
     }
@@ -695,7 +722,12 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
                            ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * rowbytes;
     PairLoad<BITS, NI> A;
     pair_load<BITS, NI>(A, rows0, rowbytes, 0, kDecRows, nb);
-    dec_act_prep<BITS, NI>(xa, a.xd, nb, dl);
+    /* the epilogue's row scale (lane: row rb*32 + lane%32 of gate, then up),
+     * loaded now so that it is in hand after the K loop */
+    const int r = rb * 32 + (lane & 31);
+    const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
+    if (!prepped)
+        dec_act_prep<BITS, NI>(xa, dpre, a.xd, nb, dl);
     const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) +
                                       ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * (nb / sg.gu_gb)
                                 : nullptr;
@@ -706,8 +738,6 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     if (wv != 0)
         return;
     const float acc = rsum[lane];
-    const int r = rb * 32 + (lane & 31);
-    const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
     const float v = sc * acc;
     const float up = shfl_xor(v, 32);
     const float h = canon_silu(v) * up;
@@ -725,7 +755,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
 template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
 {
-    extern __shared__ int32_t dec_lds[];
+    extern __shared__ __attribute__((aligned(16))) int32_t dec_lds[];
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
@@ -743,13 +773,15 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
     uint32_t xa[NI][8];
     dec_act_load<NI>(a.hq + (int64_t)u * a.I, nb, xa);
+    float dpre[kDlPre];
+    dec_scale_load(a.hd + (int64_t)u * nb, nb, dpre);
     const int row0 = rb * kRowsPerJob + kDecRows * wv;
     const int rows_ok = min(kDecRows, max(0, a.H - row0));
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
     const uint8_t* rows0 = sg.down_w + ((int64_t)e * a.H + min(row0, a.H - 1)) * rowbytes;
     PairLoad<BITS, NI> A;
     pair_load<BITS, NI>(A, rows0, rowbytes, 0, rows_ok, nb);
-    dec_act_prep<BITS, NI>(xa, a.hd + (int64_t)u * nb, nb, dl);
+    dec_act_prep<BITS, NI>(xa, dpre, a.hd + (int64_t)u * nb, nb, dl);
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(row0, a.H - 1)) * (nb / sg.d_gb) : nullptr;
     const float v = dec_k_loop<BITS, NI>(A, rows0, rowbytes, rows_ok, nb, xa, P, sp, dl, ws0, sg.d_gb);
     const int n = row0 + lane;
@@ -771,11 +803,11 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
 
 constexpr int kDcRows = 8; /* output rows per workgroup; wave w owns rows 2w, 2w+1 */
 
-/* LDS words: h codes [U][nb][8], h scales [U][nb], per wave the partials
+/* LDS words: h codes [U][nb][8], h scales [U][nb | 1], per wave the partials
  * [2U][nb | 1] and the row values [2U]. */
 __host__ __device__ inline size_t dc_lds_words(int U, int nb)
 {
-    return (size_t)U * nb * 9 + (size_t)kGroups * 2 * U * ((nb | 1) + 1);
+    return (size_t)U * nb * 8 + (size_t)U * (nb | 1) + (size_t)kGroups * 2 * U * ((nb | 1) + 1);
 }
 
 inline bool dc_fits(int U, int nb)
@@ -783,15 +815,12 @@ inline bool dc_fits(int U, int nb)
     return dc_lds_words(U, nb) * 4 <= 64 * 1024;
 }
 
-/* First of this wave's two rows of unit u's down matrix (u = slot, or k for
- * the shared expert). */
-__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int u, int row0, int64_t rowbytes)
+/* First of this wave's two rows of the down matrix of unit u (u = slot, or
+ * k for the shared expert) whose matrix index is e. */
+__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int u, int e, int row0, int64_t rowbytes)
 {
     const FfnArgs& a = d.f;
-    const bool routed = u < d.k;
-    const uint8_t* w = routed ? a.seg[0].down_w : a.seg[1].down_w;
-    const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
-    const int e = routed ? min(max(d.ids[u], 0), n_mat - 1) : 0;
+    const uint8_t* w = u < d.k ? a.seg[0].down_w : a.seg[1].down_w;
     return w + ((int64_t)e * a.H + row0) * rowbytes;
 }
 
@@ -839,17 +868,33 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     const int U = n_kept + (shared ? 1 : 0);
     const int nb = a.I / 32, sp = nb | 1;
     uint32_t* xal = reinterpret_cast<uint32_t*>(dc_lds);        /* [U][nb][8] */
-    float* dls = reinterpret_cast<float*>(xal + U * nb * 8);    /* [U][nb] */
-    int32_t* P = reinterpret_cast<int32_t*>(dls + U * nb) + wv * (2 * U * sp);
-    float* ys = reinterpret_cast<float*>(dc_lds) + U * nb * 9 + kGroups * 2 * U * sp + wv * 2 * U;
+    /* the block scales' rows have the odd stride sp, like the partials', so
+     * that the fold's reads (32 distinct addresses) spread over the banks */
+    float* dls = reinterpret_cast<float*>(xal + U * nb * 8);    /* [U][sp] */
+    int32_t* P0 = reinterpret_cast<int32_t*>(dls + U * sp);      /* [kGroups][2U][sp] */
+    int32_t* P = P0 + wv * (2 * U * sp);
+    float* ys = reinterpret_cast<float*>(P0 + kGroups * 2 * U * sp) + wv * 2 * U;
     const int row0 = blockIdx.x * kDcRows + 2 * wv;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
 
     if (U == 0)
         return;
+    /* per-unit values in lane registers, loaded once (U <= 32): lane j holds
+     * compacted unit j's unit id, matrix index and routing weight, lane
+     * 2j + r the row scale of this wave's row r of unit j */
+    const int u_l = dc_unit(kept, n_kept, d.k, min(lane, U - 1), all_kept);
+    const bool rt_l = u_l < d.k;
+    const int e_l = rt_l ? min(max(d.ids[u_l], 0), a.seg[0].n_mat - 1) : 0;
+    const float w_l = rt_l ? d.w[u_l] : 0.0f;
+    const int u_r = __shfl(u_l, min(lane >> 1, U - 1), kWave);
+    const int e_r = __shfl(e_l, min(lane >> 1, U - 1), kWave);
+    const bool rt_r = u_r < d.k;
+    const float* ds_r = rt_r ? a.seg[0].down_s : a.seg[1].down_s;
+    const float rs_l = (rt_r ? a.seg[0].d_gb : a.seg[1].d_gb) ? 1.0f : ds_r[(int64_t)e_r * a.H + row0 + (lane & 1)];
     /* compacted unit 0's pair is issued before h is staged */
     PairLoad<BITS, NI> A, B;
-    pair_load<BITS, NI>(A, dc_rows(d, dc_unit(kept, n_kept, d.k, 0, all_kept), row0, rowbytes), rowbytes, 0, 2, nb);
+    pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, 0), __builtin_amdgcn_readlane(e_l, 0), row0, rowbytes),
+                        rowbytes, 0, 2, nb);
     /* each thread issues the loads of up to kDcStage (unit, block) items
      * before it converts and stores any: one memory round trip, not one per
      * item */
@@ -871,11 +916,11 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
             const int i = i0 + r * 64 * kGroups;
             if (i < U * nb) {
                 uint32_t xa[8];
-                prep_activation<BITS>(x[r], xa);
+                prep_dot<BITS>(x[r], xa);
                 uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
                 dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
                 dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
-                dls[i] = dv[r];
+                dls[(i / nb) * sp + i % nb] = dv[r];
             }
         }
     }
@@ -885,11 +930,14 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
      * unconditional (past the last unit they reload it: in bounds, unused) */
     for (int j = 0; j < U; j += 2) {
         uint32_t xa[NI][8];
-        pair_load<BITS, NI>(B, dc_rows(d, dc_unit(kept, n_kept, d.k, min(j + 1, U - 1), all_kept), row0, rowbytes),
+        const int j1 = min(j + 1, U - 1), j2 = min(j + 2, U - 1);
+        pair_load<BITS, NI>(B, dc_rows(d, __builtin_amdgcn_readlane(u_l, j1), __builtin_amdgcn_readlane(e_l, j1), row0,
+                                       rowbytes),
                             rowbytes, 0, 2, nb);
         dc_act<NI>(xal, j, nb, xa);
         pair_partials<BITS, NI>(A, xa, 0, nb, P + 2 * j * sp, sp);
-        pair_load<BITS, NI>(A, dc_rows(d, dc_unit(kept, n_kept, d.k, min(j + 2, U - 1), all_kept), row0, rowbytes),
+        pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, j2), __builtin_amdgcn_readlane(e_l, j2), row0,
+                                       rowbytes),
                             rowbytes, 0, 2, nb);
         if (j + 1 < U) {
             dc_act<NI>(xal, j + 1, nb, xa);
@@ -904,17 +952,16 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
         const int rd = min(ci >> 2, 2 * U - 1), g = ci & 3;
         const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
         const int32_t* pr = P + rd * sp;
-        const float* dj = dls + (rd >> 1) * nb;
+        const float* dj = dls + (rd >> 1) * sp;
         float acc = 0.0f;
         int b = b0;
-        const int uf = dc_unit(kept, n_kept, d.k, rd >> 1, all_kept);
+        /* lane values are read before any branch: every lane is active */
+        const int uf = __shfl(u_l, rd >> 1, kWave), ef = __shfl(e_l, rd >> 1, kWave);
+        const float rsv = __shfl(rs_l, rd, kWave);
         const int gbf = uf < d.k ? a.seg[0].d_gb : a.seg[1].d_gb;
         if (gbf) {
             /* group-wise scales of (unit, row) */
-            const bool rt = uf < d.k;
-            const int nm = rt ? a.seg[0].n_mat : a.seg[1].n_mat;
-            const int ef = rt ? min(max(d.ids[uf], 0), nm - 1) : 0;
-            const float* ws = (rt ? a.seg[0].down_s : a.seg[1].down_s) +
+            const float* ws = (uf < d.k ? a.seg[0].down_s : a.seg[1].down_s) +
                               ((int64_t)ef * a.H + row0 + (rd & 1)) * (nb / gbf);
             for (; b < b1; ++b)
                 acc = __builtin_fmaf(group_coef(ws, gbf, b, dj[b]), (float)pr[b], acc);
@@ -939,24 +986,18 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
         v = v + __shfl(acc, base + 1, kWave);
         v = v + __shfl(acc, base + 2, kWave);
         v = v + __shfl(acc, base + 3, kWave);
-        if (g == 0 && ci < 8 * U) {
-            const int u = dc_unit(kept, n_kept, d.k, rd >> 1, all_kept), n = row0 + (rd & 1);
-            const bool routed = u < d.k;
-            const float* ds = routed ? a.seg[0].down_s : a.seg[1].down_s;
-            const int n_mat = routed ? a.seg[0].n_mat : a.seg[1].n_mat;
-            const int e = routed ? min(max(d.ids[u], 0), n_mat - 1) : 0;
-            const bool grouped = (routed ? a.seg[0].d_gb : a.seg[1].d_gb) != 0;
-            ys[rd] = (grouped ? 1.0f : ds[(int64_t)e * a.H + n]) * v;
-        }
+        if (g == 0 && ci < 8 * U)
+            ys[rd] = rsv * v; /* rsv: 1 with group-wise scales */
     }
     wave_lds_sync();
-    if (lane < 2) {
-        /* compacted order is slot order: the combine's fma order is kept */
-        float outv = shared ? ys[2 * n_kept + lane] : 0.0f;
-        for (int j = 0; j < n_kept; ++j)
-            outv = __builtin_fmaf(d.w[dc_unit(kept, n_kept, d.k, j, all_kept)], ys[2 * j + lane], outv);
+    /* compacted order is slot order: the combine's fma order is kept (every
+     * lane runs the chain of row lane & 1; lanes 0 and 1 store) */
+    float outv = shared ? ys[2 * n_kept + (lane & 1)] : 0.0f;
+    for (int j = 0; j < n_kept; ++j)
+        outv = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), j)), ys[2 * j + (lane & 1)],
+                              outv);
+    if (lane < 2)
         d.out[row0 + lane] = outv;
-    }
 }
 
 static int64_t total_jobs(const FfnArgs& a, int RB)
@@ -1080,7 +1121,9 @@ static void down_combine_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t
 
 bool down_combine_decode_fits(const DecodeArgs& d)
 {
-    return d.f.H % kDcRows == 0 && dc_fits(d.k + (d.f.nseg > 1 ? 1 : 0), d.f.I / 32);
+    const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
+    /* per-unit values live in lanes: 2U row scales per wave */
+    return U <= 32 && d.f.H % kDcRows == 0 && dc_fits(U, d.f.I / 32);
 }
 
 hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)

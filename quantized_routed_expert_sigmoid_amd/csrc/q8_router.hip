@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
                                                             int32_t* __restrict__ ids,
                                                             float* __restrict__ weights)
 {
-    __shared__ float sel_s[4][128];
+    __shared__ __attribute__((aligned(16))) float sel_s[4][kSelScratch];
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= S)

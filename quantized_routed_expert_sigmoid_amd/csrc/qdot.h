@@ -15,9 +15,17 @@
  * are permuted once per block so that their byte order matches the order in
  * which the fields come out of the words.
  *
+ * The VALU kernels take int4 another way (prep_dot / block_dot): the
+ * weight nibbles are used in place by v_dot8_i32_i4, against two nibble
+ * planes of the activation codes.  Every int8 code splits exactly as
+ * x = 16 h + l + 8 with h = x >> 4 and l = (x & 15) - 8, both in [-8, 7], so
+ * the block dot is 16 sum(q h) + sum(q l) + 8 sum(q): three dot8 per weight
+ * word and no unpacking.
+ *
  * The file is included by the gfx950 kernels, which define COLI_PERM as
- * __builtin_amdgcn_perm and COLI_SDOT4 as __builtin_amdgcn_sdot4, and by a
- * CPU harness that defines them as emulations to check the layout logic.
+ * __builtin_amdgcn_perm, COLI_SDOT4 as __builtin_amdgcn_sdot4 and COLI_SDOT8
+ * as __builtin_amdgcn_sdot8, and by a CPU harness (tests) that defines them
+ * as emulations to check the layout logic against direct sums.
  * It needs COLI_QDOT_FN (function qualifiers) defined by the includer.
  */
 #ifndef COLI_QDOT_H
@@ -83,6 +91,44 @@ COLI_QDOT_FN int32_t block_partial(const uint32_t* w, const uint32_t (&xa)[8])
             for (int r = 0; r < 4; ++r)
                 s = COLI_SDOT4((w[k] << (2 * r)) & 0xC0C0C0C0u, xa[4 * k + r], s);
         return s >> 6;
+    }
+}
+
+/* Activation operands of block_dot<BITS>: int8 and int2 as prep_activation;
+ * int4 as the two nibble planes, word 2k the h plane and word 2k+1 the l
+ * plane of weight word k (nibble 2j+1 of a weight word is element 2j, nibble
+ * 2j element 2j+1 of its eight). */
+template <int BITS>
+COLI_QDOT_FN void prep_dot(const uint32_t (&x)[8], uint32_t (&xa)[8])
+{
+    if constexpr (BITS != 4) {
+        prep_activation<BITS>(x, xa);
+    } else {
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t ev = COLI_PERM(x[2 * k + 1], x[2 * k], 0x06040200u); /* e0 e2 e4 e6 */
+            const uint32_t od = COLI_PERM(x[2 * k + 1], x[2 * k], 0x07050301u); /* e1 e3 e5 e7 */
+            /* h: the high nibble of each code; l: its low nibble minus 8 */
+            xa[2 * k] = (ev & 0xF0F0F0F0u) | ((od >> 4) & 0x0F0F0F0Fu);
+            xa[2 * k + 1] = (((ev << 4) & 0xF0F0F0F0u) | (od & 0x0F0F0F0Fu)) ^ 0x88888888u;
+        }
+    }
+}
+
+/* Exact block partial of the VALU kernels (the same value as block_partial);
+ * xa: prep_dot. */
+template <int BITS>
+COLI_QDOT_FN int32_t block_dot(const uint32_t* w, const uint32_t (&xa)[8])
+{
+    if constexpr (BITS != 4) {
+        return block_partial<BITS>(w, xa);
+    } else {
+        int32_t sh = 0, sl = 0, sq = 0;
+        for (int k = 0; k < 4; ++k) {
+            sh = COLI_SDOT8(w[k], xa[2 * k], sh);
+            sl = COLI_SDOT8(w[k], xa[2 * k + 1], sl);
+            sq = COLI_SDOT8(w[k], 0x11111111u, sq); /* sum of the word's codes */
+        }
+        return ((2 * sh + sq) << 3) + sl;
     }
 }
 

@@ -4,10 +4,11 @@
  * features section, sigmoid-router item: DeepSeek-V3 style sigmoid scores,
  * noaux_tc selection bias, routed_scaling_factor).
  *
- * Each lane holds the scores of experts lane, lane+64, ...; the top-k is k
- * rounds of a wave-wide maximum of the order-preserving bits of the biased
- * score followed by a wave-wide minimum of the expert ids holding it (equal
- * scores resolve to the lower id).
+ * Each lane holds the scores of experts lane, lane+64, ...; the top-k is taken
+ * on the order-preserving bits of the biased score, equal scores resolving to
+ * the lower id, in slots of descending score.  For k <= 8 the few candidates
+ * above a lower bound of the k-th key are ranked in parallel; otherwise (or
+ * with more than 64 candidates) k rounds of a wave-wide maximum pick them.
  * Weights: rsf * s_j / sum of the selected unbiased scores (slot order).
  */
 #ifndef COLI_SELECT_H
@@ -19,6 +20,7 @@
 namespace coli {
 
 constexpr int kMaxPerLane = 16; /* E <= 1024 */
+constexpr int kSelScratch = 256; /* floats of LDS scratch per selecting wave, 16-byte aligned */
 
 __device__ __forceinline__ uint32_t order_bits(float c)
 {
@@ -62,7 +64,8 @@ __device__ __forceinline__ uint32_t argmax_key(const uint32_t (&key)[PL], int E,
 
 /* lt: the token's E logits, or with n_parts > 1 the first of n_parts partial
  * sums part_stride floats apart (added in slice order).  Writes ids_out[0..k),
- * w_out[0..k) and, when ids_lds is not null, ids_lds[0..k).  sel_s: 128 floats
+ * w_out[0..k) (skipped when w_out is null and top-p is off) and, when ids_lds
+ * is not null, ids_lds[0..k).  sel_s: kSelScratch floats
  * of LDS owned by the calling wave.  Called by a whole wave.
  *
  * Group stage (opt.n_group > 1): per group the largest biased score, the
@@ -127,35 +130,134 @@ __device__ __forceinline__ void select_token_pl(const float* lt, const float* bi
                 key[i] = 0;
         }
     }
-    for (int j = 0; j < k; ++j) {
-        /* best score, then the lowest expert id holding it */
-        uint32_t best = 0;
+    /* Candidates (k <= 8): the maxima of the eight 8-lane groups are eight
+     * distinct keys, so their minimum L is at most the k-th largest key and
+     * every expert of the top-k has a key >= L.  The candidates (few for
+     * scores that are not massively tied) are packed into LDS in ascending id
+     * order and each finds its slot as its rank by (key descending, id
+     * ascending) among them -- no chain of wave-wide steps.  More than 64
+     * candidates: k rounds of a wave-wide maximum instead. */
+    bool done = false;
+    if (k <= 8) {
+        uint32_t g = key[0];
 #pragma unroll
-        for (int i = 0; i < PL; ++i)
-            best = key[i] > best ? key[i] : best;
-        best = wave_reduce_u32<true>(best);
-        uint32_t mine = 0xFFFFFFFFu;
+        for (int i = 1; i < PL; ++i)
+            g = key[i] > g ? key[i] : g;
+        /* row_shr 1, 2, 4: lane 8q + 7 ends with the maximum of lanes 8q .. 8q+7 */
+        uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g, 0x111, 0xF, 0xF, false);
+        g = t > g ? t : g;
+        t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g, 0x112, 0xF, 0xF, false);
+        g = t > g ? t : g;
+        t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)g, 0x114, 0xF, 0xF, false);
+        g = t > g ? t : g;
+        uint32_t L = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < PL; ++i)
-            if (key[i] == best && mine == 0xFFFFFFFFu)
-                mine = (uint32_t)(lane + 64 * i);
-        const int e = (int)wave_reduce_u32<false>(mine);
-        const int ie = e >> 6; /* uniform */
-        float cand = 0.0f;
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)g, 8 * q + 7);
+            L = m < L ? m : L;
+        }
+        uint64_t cm[PL];
+        int n_c = 0;
 #pragma unroll
         for (int i = 0; i < PL; ++i) {
-            if (i == ie) {
-                cand = s[i];
-                if (lane == (e & 63))
-                    key[i] = 0; /* taken */
-            }
+            cm[i] = __ballot(key[i] >= L);
+            n_c += __popcll(cm[i]);
         }
-        const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cand), e & 63));
-        if (lane == 0) {
-            sel_s[j] = sj;
-            ids_out[j] = e;
-            if (ids_lds)
-                ids_lds[j] = e;
+        if (n_c <= 64) {
+            uint32_t* ck = reinterpret_cast<uint32_t*>(sel_s + 64);
+            int32_t* ci = reinterpret_cast<int32_t*>(sel_s + 128);
+            float* cs = sel_s + 192;
+            int base = 0;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) {
+                if ((cm[i] >> lane) & 1) {
+                    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(cm[i] >> 32),
+                                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)cm[i], 0u));
+                    ck[pos] = key[i];
+                    ci[pos] = lane + 64 * i;
+                    cs[pos] = s[i];
+                }
+                base += __popcll(cm[i]);
+            }
+            /* padding to a multiple of 8 never outranks a candidate */
+            const int n_c8 = (n_c + 7) & ~7;
+            if (lane >= n_c && lane < n_c8) {
+                ck[lane] = 0;
+                ci[lane] = 0x7FFFFFFF;
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            if (lane < n_c) {
+                const uint32_t mk = ck[lane];
+                const int mi = ci[lane];
+                int rank = 0;
+                for (int j = 0; j < n_c8; j += 8) {
+                    /* eight candidates per round of (broadcast) reads */
+                    const uint4 k0 = *reinterpret_cast<const uint4*>(ck + j);
+                    const uint4 k1 = *reinterpret_cast<const uint4*>(ck + j + 4);
+                    const int4 i0 = *reinterpret_cast<const int4*>(ci + j);
+                    const int4 i1 = *reinterpret_cast<const int4*>(ci + j + 4);
+                    const uint32_t kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                    const int ii[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        rank += (kk[q] > mk || (kk[q] == mk && ii[q] < mi)) ? 1 : 0;
+                }
+                if (rank < k) {
+                    sel_s[rank] = cs[lane];
+                    ids_out[rank] = mi;
+                    if (ids_lds)
+                        ids_lds[rank] = mi;
+                }
+            }
+            done = true;
+        }
+    }
+    if (!done) {
+        for (int j = 0; j < k; ++j) {
+            /* the lane's best key and the lowest of its indices holding it */
+            uint32_t lbest = key[0];
+            int li = 0;
+#pragma unroll
+            for (int i = 1; i < PL; ++i) {
+                if (key[i] > lbest) {
+                    lbest = key[i];
+                    li = i;
+                }
+            }
+            const uint32_t best = wave_reduce_u32<true>(lbest);
+            const uint64_t holders = __ballot(lbest == best);
+            int e;
+            if (__popcll(holders) == 1) {
+                /* one lane holds it: its lowest index is the lowest expert id */
+                const int wl = __builtin_ctzll(holders);
+                e = wl + 64 * __builtin_amdgcn_readlane(li, wl);
+            } else {
+                /* several lanes: the lowest expert id holding the best key */
+                uint32_t mine = 0xFFFFFFFFu;
+#pragma unroll
+                for (int i = 0; i < PL; ++i)
+                    if (key[i] == best && mine == 0xFFFFFFFFu)
+                        mine = (uint32_t)(lane + 64 * i);
+                e = (int)wave_reduce_u32<false>(mine);
+            }
+            const int ie = e >> 6; /* uniform */
+            float cand = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) {
+                if (i == ie) {
+                    cand = s[i];
+                    if (lane == (e & 63))
+                        key[i] = 0; /* taken */
+                }
+            }
+            const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cand), e & 63));
+            if (lane == 0) {
+                sel_s[j] = sj;
+                ids_out[j] = e;
+                if (ids_lds)
+                    ids_lds[j] = e;
+            }
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -211,6 +313,8 @@ __device__ __forceinline__ void select_token_pl(const float* lt, const float* bi
                 }
         return;
     }
+    if (w_out == nullptr) /* ids only */
+        return;
     float denom = 0.0f;
     for (int j = 0; j < k; ++j)
         denom += sel_s[j];

@@ -1,5 +1,5 @@
 // CPU harness for the GPU library's container unpacking (csrc/qdot.h): the
-// same template code, compiled with g++ against emulations of the two gfx950
+// same template code, compiled with g++ against emulations of the three gfx950
 // instructions it uses, so the layout logic can be checked without a GPU.
 #include <stdint.h>
 #include <string.h>
@@ -25,9 +25,21 @@ static int32_t emu_sdot4(uint32_t a, uint32_t b, int32_t c)
     return c;
 }
 
+// v_dot8_i32_i4: signed nibble dot product plus accumulator (nibble i of
+// each operand is bits 4i+3..4i).
+static int32_t emu_sdot8(uint32_t a, uint32_t b, int32_t c)
+{
+    for (int i = 0; i < 8; ++i) {
+        const int32_t x = (int32_t)((a >> (4 * i)) & 15u), y = (int32_t)((b >> (4 * i)) & 15u);
+        c += (x >= 8 ? x - 16 : x) * (y >= 8 ? y - 16 : y);
+    }
+    return c;
+}
+
 #define COLI_QDOT_FN static inline
 #define COLI_PERM(a, b, s) emu_perm((a), (b), (s))
 #define COLI_SDOT4(a, b, c) emu_sdot4((a), (b), (c))
+#define COLI_SDOT8(a, b, c) emu_sdot8((a), (b), (c))
 #include "../quantized_routed_expert_sigmoid_amd/csrc/qdot.h"
 
 extern "C" int32_t harness_block_partial(int bits, const uint8_t* wblock, const int8_t* codes)
@@ -45,5 +57,24 @@ extern "C" int32_t harness_block_partial(int bits, const uint8_t* wblock, const 
     default:
         coli::prep_activation<2>(x, xa);
         return coli::block_partial<2>(w, xa);
+    }
+}
+
+// The VALU kernels' form (prep_dot / block_dot).
+extern "C" int32_t harness_block_dot(int bits, const uint8_t* wblock, const int8_t* codes)
+{
+    uint32_t x[8], xa[8], w[8];
+    memcpy(x, codes, 32);
+    memcpy(w, wblock, 4 * bits);
+    switch (bits) {
+    case 8:
+        coli::prep_dot<8>(x, xa);
+        return coli::block_dot<8>(w, xa);
+    case 4:
+        coli::prep_dot<4>(x, xa);
+        return coli::block_dot<4>(w, xa);
+    default:
+        coli::prep_dot<2>(x, xa);
+        return coli::block_dot<2>(w, xa);
     }
 }

@@ -22,30 +22,42 @@ def harness(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("harness") / "libqdot_harness.so")
     subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-o", out, HARNESS_SRC], check=True)
     lib = ctypes.CDLL(out)
-    lib.harness_block_partial.restype = ctypes.c_int32
-    lib.harness_block_partial.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for fn in (lib.harness_block_partial, lib.harness_block_dot):
+        fn.restype = ctypes.c_int32
+        fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
+@pytest.mark.parametrize("form", ["block_partial", "block_dot"])
 @pytest.mark.parametrize("bits,lo,hi", [(8, -127, 127), (4, -8, 7), (2, -2, 1)])
-def test_kernel_unpack_matches_oracle_partials(harness, bits, lo, hi):
+def test_kernel_unpack_matches_oracle_partials(harness, bits, lo, hi, form):
+    """Both kernel forms of the exact block partial (the matrix-core operand
+    order and the VALU form, int4 by nibble dot products) against the
+    oracle's, on random codes and the extremes of both ranges: activation
+    codes of +-127 and 120..127 (where a plain two-nibble split of the code
+    would overflow)."""
+    fn = getattr(harness, "harness_" + form)
     rng = np.random.default_rng(7 + bits)
     K = 32 * 64
-    for trial in range(8):
+    for trial in range(10):
         codes = rng.integers(lo, hi + 1, size=K).astype(np.int8)
         if trial == 0:
             codes[:] = lo  # extreme values
-        if trial == 1:
+        if trial in (1, 8):
             codes[:] = hi
         row = oracle.pack_row(codes, bits)
         q = rng.integers(-127, 128, size=K).astype(np.int8)
         if trial == 2:
             q[:] = -127
+        if trial in (3, 8):
+            q[:] = 127
+        if trial == 9:
+            q = rng.integers(120, 128, size=K).astype(np.int8) * rng.choice(np.array([-1, 1], np.int8), size=K)
         bb = 4 * bits  # bytes per 32-element block
         for b in range(K // 32):
             wblk = np.ascontiguousarray(row[b * bb:(b + 1) * bb])
             qb = np.ascontiguousarray(q[32 * b:32 * (b + 1)])
-            got = harness.harness_block_partial(bits, wblk.ctypes.data, qb.ctypes.data)
+            got = fn(bits, wblk.ctypes.data, qb.ctypes.data)
             assert got == oracle.block_partial(row, bits, q, b), (trial, b)
 
 
