@@ -524,17 +524,17 @@ inline int dec_ni(int nb)
 }
 
 /* Dynamic LDS, in words: per wave the partials [16][nb | 1] (before the K
- * loop the selection's scratch), then the token's block scales [nb] and the
- * job's row sums [64]; at least the selection's scratch and ids (wave 0). */
+ * loop wave 0's selection scratch), then the token's block scales [nb], the
+ * job's row sums [64] and the selected ids [64]. */
 __host__ __device__ inline int dec_region(int nb)
 {
     const int p = kDecRows * (nb | 1);
-    return p > kSelScratch + 64 ? p : kSelScratch + 64;
+    return p > kSelScratch ? p : kSelScratch;
 }
 
 __host__ __device__ inline size_t dec_lds_bytes(int nb)
 {
-    return (size_t)(kGroups * dec_region(nb) + nb + 64) * 4;
+    return (size_t)(kGroups * dec_region(nb) + nb + 64 + 64) * 4;
 }
 
 template <int BITS, int NI>
@@ -680,15 +680,20 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = a.I / 32;
     const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
-    const int u = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
-    if (u >= nunits)
+    /* the shared expert's jobs come first: they need no selection, so they
+     * stream while the routed jobs select, and they land first on the CUs
+     * that also receive a third job */
+    const int j = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
+    if (j >= nunits)
         return;
+    const int u = nunits > d.k ? (j == 0 ? d.k : j - 1) : j;
     const bool routed = u < d.k;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
     const int nb = a.H / 32, sp = nb | 1, region = dec_region(nb);
     int32_t* P = dec_lds + wv * region;
     float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
     float* rsum = dl + nb;
+    int32_t* sel_ids = reinterpret_cast<int32_t*>(rsum + 64); /* read by every wave after the barrier */
     uint32_t xa[NI][8];
     dec_act_load<NI>(a.xq, nb, xa);
     float dpre[kDlPre];
@@ -701,9 +706,8 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
          * prepare their activations; the scratch is wave 0's (not yet used)
          * partial buffer */
         float* sel_s = reinterpret_cast<float*>(dec_lds);
-        int32_t* sel_ids = dec_lds + kSelScratch;
         if (wv == 0) {
-            const bool store = blockIdx.x == 0; /* the others need the ids only */
+            const bool store = u == 0 && rb == 0; /* the others need the ids only */
             select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids, store ? d.w : nullptr, sel_s,
                          sel_ids, 1, 0, d.opt);
         } else {
