@@ -883,22 +883,26 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
 
     if (U == 0)
         return;
+    /* stream order: the shared expert first (its rows need no id, so its
+     * first pair is issued before the ids arrive), then the kept routed
+     * slots; partials and the combine stay indexed by compacted unit */
+    auto unit_at = [&](int q) { return shared ? (q == 0 ? U - 1 : q - 1) : q; };
+    PairLoad<BITS, NI> A, B;
+    if (shared)
+        pair_load<BITS, NI>(A, dc_rows(d, d.k, 0, row0, rowbytes), rowbytes, 0, 2, nb);
     /* per-unit values in lane registers, loaded once (U <= 32): lane j holds
-     * compacted unit j's unit id, matrix index and routing weight, lane
-     * 2j + r the row scale of this wave's row r of unit j */
+     * compacted unit j's unit id, matrix index and routing weight (lane
+     * 2j + r gets the row scale of this wave's row r of unit j once h is
+     * staged: its address needs the id, and h's loads need nothing) */
     const int u_l = dc_unit(kept, n_kept, d.k, min(lane, U - 1), all_kept);
     const bool rt_l = u_l < d.k;
     const int e_l = rt_l ? min(max(d.ids[u_l], 0), a.seg[0].n_mat - 1) : 0;
     const float w_l = rt_l ? d.w[u_l] : 0.0f;
-    const int u_r = __shfl(u_l, min(lane >> 1, U - 1), kWave);
-    const int e_r = __shfl(e_l, min(lane >> 1, U - 1), kWave);
-    const bool rt_r = u_r < d.k;
-    const float* ds_r = rt_r ? a.seg[0].down_s : a.seg[1].down_s;
-    const float rs_l = (rt_r ? a.seg[0].d_gb : a.seg[1].d_gb) ? 1.0f : ds_r[(int64_t)e_r * a.H + row0 + (lane & 1)];
-    /* compacted unit 0's pair is issued before h is staged */
-    PairLoad<BITS, NI> A, B;
-    pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, 0), __builtin_amdgcn_readlane(e_l, 0), row0, rowbytes),
-                        rowbytes, 0, 2, nb);
+    /* without a shared expert, compacted unit 0's pair is issued before h is staged */
+    if (!shared)
+        pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, 0), __builtin_amdgcn_readlane(e_l, 0), row0,
+                                       rowbytes),
+                            rowbytes, 0, 2, nb);
     /* each thread issues the loads of up to kDcStage (unit, block) items
      * before it converts and stores any: one memory round trip, not one per
      * item */
@@ -928,24 +932,30 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
             }
         }
     }
+    const int u_r = __shfl(u_l, min(lane >> 1, U - 1), kWave);
+    const int e_r = __shfl(e_l, min(lane >> 1, U - 1), kWave);
+    const bool rt_r = u_r < d.k;
+    const float* ds_r = rt_r ? a.seg[0].down_s : a.seg[1].down_s;
+    const float rs_l = (rt_r ? a.seg[0].d_gb : a.seg[1].d_gb) ? 1.0f : ds_r[(int64_t)e_r * a.H + row0 + (lane & 1)];
     __syncthreads();
 
-    /* compacted unit j's pair is in A for even j and in B for odd j; loads are
-     * unconditional (past the last unit they reload it: in bounds, unused) */
-    for (int j = 0; j < U; j += 2) {
+    /* the pair of stream position q is in A for even q and in B for odd q;
+     * loads are unconditional (past the last unit they reload it: in bounds,
+     * unused) */
+    for (int q = 0; q < U; q += 2) {
         uint32_t xa[NI][8];
-        const int j1 = min(j + 1, U - 1), j2 = min(j + 2, U - 1);
+        const int j0 = unit_at(q), j1 = unit_at(min(q + 1, U - 1)), j2 = unit_at(min(q + 2, U - 1));
         pair_load<BITS, NI>(B, dc_rows(d, __builtin_amdgcn_readlane(u_l, j1), __builtin_amdgcn_readlane(e_l, j1), row0,
                                        rowbytes),
                             rowbytes, 0, 2, nb);
-        dc_act<NI>(xal, j, nb, xa);
-        pair_partials<BITS, NI>(A, xa, 0, nb, P + 2 * j * sp, sp);
+        dc_act<NI>(xal, j0, nb, xa);
+        pair_partials<BITS, NI>(A, xa, 0, nb, P + 2 * j0 * sp, sp);
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, j2), __builtin_amdgcn_readlane(e_l, j2), row0,
                                        rowbytes),
                             rowbytes, 0, 2, nb);
-        if (j + 1 < U) {
-            dc_act<NI>(xal, j + 1, nb, xa);
-            pair_partials<BITS, NI>(B, xa, 0, nb, P + 2 * (j + 1) * sp, sp);
+        if (q + 1 < U) {
+            dc_act<NI>(xal, j1, nb, xa);
+            pair_partials<BITS, NI>(B, xa, 0, nb, P + 2 * j1 * sp, sp);
         }
     }
     wave_lds_sync();
