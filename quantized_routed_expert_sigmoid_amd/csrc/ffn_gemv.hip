@@ -494,9 +494,10 @@ __global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
 /* ---- one-token batches ---------------------------------------------------
  * Unit u < k is the expert of selection slot u, unit k the shared expert;
  * hq / hd / y row u belongs to unit u, so the combine reads y in slot order.
- * The gate/up kernel selects the experts itself: every wave runs the top-k
- * over the token's logits (the same selection as router_select_kernel), so
- * no workgroup waits for another, and workgroup 0 stores ids and weights.
+ * The gate/up kernel selects the experts itself: wave 0 of every routed job
+ * runs the top-k over the token's logits (the same selection as
+ * router_select_kernel), so no workgroup waits for another, and the first
+ * routed job stores ids and weights.
  *
  * Whole-row loads.  A job is 64 rows; wave w owns rows 16w .. 16w+15 and
  * reads them whole, two rows per load instruction: lane l takes row
@@ -793,6 +794,303 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
         a.y[(int64_t)u * a.H + n] = (sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n]) * v;
 }
 
+/* Items a thread stages per round (loads of all issued before any is converted). */
+constexpr int kDcStage = 4;
+
+/* ---- whole rows for units of up to kUnitTokens tokens --------------------
+ *
+ * The job of ffn_gate_up_gemv / ffn_down_gemv (one unit, 64 row dots), with
+ * the whole-row streaming of the one-token kernels: wave w owns 16 whole rows
+ * and reads two rows per load group (lane l: row 2p + l/32, blocks
+ * l mod 32 + 32 i), two pairs in flight.  The unit's activation blocks of
+ * every token are staged once per job in LDS in operand order; after each
+ * pair the wave writes the exact partials of its 2 rows x the unit's tokens
+ * and folds them -- lane (row, token, group) runs the canonical chain of its
+ * group, the four group sums added in order -- while the next two pairs
+ * load.
+ *
+ * Dynamic LDS, in words: codes [TMAX][nb][8], block scales [TMAX][nb | 1],
+ * per wave the partials [2][TMAX][nb | 1], and the job's row values
+ * [64][TMAX]; used while it fits 64 KB. */
+__host__ __device__ inline size_t rows_lds_words(int nb, int tmax)
+{
+    const size_t sp = (size_t)(nb | 1);
+    return (size_t)tmax * nb * 8 + (size_t)tmax * sp + (size_t)kGroups * 2 * tmax * sp + 64 * (size_t)tmax;
+}
+
+inline bool rows_fit(int nb, int tmax)
+{
+    return nb <= 32 * 8 && rows_lds_words(nb, tmax) * 4 <= 64 * 1024;
+}
+
+/* Exact partials of one loaded pair (rows 0, 1) for every token of the
+ * unit, to P[(row * TMAX + t) * sp + b]. */
+template <int BITS, int NI, int TMAX>
+__device__ __forceinline__ void rows_partials(const PairLoad<BITS, NI>& L, const uint32_t* xal, int nb, int ntok,
+                                              int32_t* P, int sp)
+{
+    const int lane = threadIdx.x & 63, c = lane & 31, row = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < ntok) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int b = c + 32 * i;
+                if (b < nb) {
+                    const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)t * nb + b) * 8);
+                    const uint4 u0 = src[0], u1 = src[1];
+                    const uint32_t xa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                    P[(row * TMAX + t) * sp + b] = block_dot<BITS>(L.w[i], xa);
+                }
+            }
+        }
+    }
+}
+
+/* The canonical fold of the pair's 2 rows (rows rbase, rbase + 1 of the
+ * job): lane (r2, t, g) folds group g of row r2 for token t, then the group
+ * sums of (r2, t) are added in order into vs[row][t].  ws0: group-wise scales
+ * of the pair's first row (gb blocks per scale, rows ng apart), or null;
+ * a row past rows_left (not stored) reads the last existing row's. */
+template <int TMAX>
+__device__ __forceinline__ void rows_fold(const int32_t* P, int sp, int nb, int ntok, const float* dls,
+                                          const float* ws0, int gb, int ng, int rows_left, float* vs, int rbase)
+{
+    const int lane = threadIdx.x & 63;
+    const int g = lane & 3, t = (lane >> 2) % TMAX, r4 = (lane >> 2) / TMAX;
+    const int rr = min(r4, 1);
+    const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
+    const int32_t* pr = P + (rr * TMAX + t) * sp;
+    const float* dj = dls + t * sp;
+    float acc = 0.0f;
+    int b = b0;
+    if (ws0) {
+        const float* ws = ws0 + (int64_t)min(rr, max(rows_left, 1) - 1) * ng;
+        for (; b < b1; ++b)
+            acc = __builtin_fmaf(group_coef(ws, gb, b, dj[b]), (float)pr[b], acc);
+    } else {
+        for (; b + 8 <= b1; b += 8) {
+            int32_t q[8];
+            float dd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                q[i] = pr[b + i];
+                dd[i] = dj[b + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+        }
+        for (; b < b1; ++b)
+            acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
+    }
+    const int base = lane & ~3;
+    float v = __shfl(acc, base, kWave);
+    v = v + __shfl(acc, base + 1, kWave);
+    v = v + __shfl(acc, base + 2, kWave);
+    v = v + __shfl(acc, base + 3, kWave);
+    if (g == 0 && r4 < 2 && t < ntok)
+        vs[(rbase + r4) * TMAX + t] = v;
+}
+
+/* Stages the codes (operand order) and block scales of the unit's tokens;
+ * every thread issues up to kDcStage items' loads before converting any. */
+template <int BITS, int TMAX>
+__device__ __forceinline__ void rows_stage(uint32_t* xal, float* dls, int nb, int sp, int ntok,
+                                           const int8_t* const (&act)[TMAX], const float* const (&scl)[TMAX])
+{
+    const int n_items = ntok * nb;
+    for (int i0 = threadIdx.x; i0 < n_items; i0 += 64 * kGroups * kDcStage) {
+        uint32_t x[kDcStage][8];
+        float dv[kDcStage];
+#pragma unroll
+        for (int r = 0; r < kDcStage; ++r) {
+            const int i = i0 + r * 64 * kGroups;
+            if (i < n_items) {
+                const int t = i / nb, b = i - t * nb;
+                const int8_t* ap = act[0];
+                const float* sp0 = scl[0];
+#pragma unroll
+                for (int tt = 1; tt < TMAX; ++tt)
+                    if (t == tt) {
+                        ap = act[tt];
+                        sp0 = scl[tt];
+                    }
+                load_codes(ap + (int64_t)b * 32, x[r]);
+                dv[r] = sp0[b];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kDcStage; ++r) {
+            const int i = i0 + r * 64 * kGroups;
+            if (i < n_items) {
+                const int t = i / nb, b = i - t * nb;
+                uint32_t xa[8];
+                prep_dot<BITS>(x[r], xa);
+                uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
+                dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+                dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+                dls[t * sp + b] = dv[r];
+            }
+        }
+    }
+    __syncthreads();
+}
+
+/* Partials and fold of pair p (in L) into vs[rbase0 + 2p ..]. */
+template <int BITS, int NI, int TMAX>
+__device__ __forceinline__ void rows_pair(const PairLoad<BITS, NI>& L, int p, int rows_ok, int nb, int sp,
+                                          int ntok, const uint32_t* xal, const float* dls, int32_t* P,
+                                          const float* ws0, int gb, int ng, float* vs, int rbase0)
+{
+    rows_partials<BITS, NI, TMAX>(L, xal, nb, ntok, P, sp);
+    wave_lds_sync();
+    const int r_first = min(2 * p, max(rows_ok, 1) - 1);
+    rows_fold<TMAX>(P, sp, nb, ntok, dls, ws0 ? ws0 + (int64_t)r_first * ng : nullptr, gb, ng, rows_ok - 2 * p,
+                    vs, rbase0 + 2 * p);
+    wave_lds_sync(); /* the pair's partials are read before the next overwrites them */
+}
+
+/* The wave's 16 rows (rows0: its first row, rows_ok of them exist), pair 0
+ * already in A; two pairs in flight while one is multiplied and folded. */
+template <int BITS, int NI, int TMAX>
+__device__ __forceinline__ void rows_k_loop(PairLoad<BITS, NI>& A, const uint8_t* rows0, int64_t rowbytes,
+                                            int rows_ok, int nb, int sp, int ntok, const uint32_t* xal,
+                                            const float* dls, int32_t* P, const float* ws0, int gb, int ng,
+                                            float* vs, int rbase0)
+{
+    PairLoad<BITS, NI> B;
+    pair_load<BITS, NI>(B, rows0, rowbytes, 1, rows_ok, nb);
+#pragma unroll
+    for (int p = 0; p < kDecRows / 2; p += 2) {
+        if (p + 2 < kDecRows / 2) { /* resolved at compile time */
+            rows_pair<BITS, NI, TMAX>(A, p, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
+            pair_load<BITS, NI>(A, rows0, rowbytes, p + 2, rows_ok, nb);
+            rows_pair<BITS, NI, TMAX>(B, p + 1, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
+            pair_load<BITS, NI>(B, rows0, rowbytes, p + 3, rows_ok, nb);
+        } else {
+            rows_pair<BITS, NI, TMAX>(A, p, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
+            rows_pair<BITS, NI, TMAX>(B, p + 1, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
+        }
+    }
+}
+
+template <int BITS, int NI, int TMAX>
+__global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) int32_t rw_lds[];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int RB = a.I / 32;
+    JobLoc L;
+    if (!locate(a, blockIdx.x, RB, L))
+        return;
+    const FfnSeg sg = pick(a, L.seg);
+    int e, pos0, ntok;
+    if (!unit_info(sg, L.unit, e, pos0, ntok))
+        return;
+    ntok = min(ntok, TMAX);
+    const int nb = a.H / 32, sp = nb | 1;
+    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
+    uint32_t* xal = reinterpret_cast<uint32_t*>(rw_lds);
+    float* dls = reinterpret_cast<float*>(xal + (int64_t)TMAX * nb * 8);
+    int32_t* P = reinterpret_cast<int32_t*>(dls + TMAX * sp) + wv * (2 * TMAX * sp);
+    float* vs = reinterpret_cast<float*>(reinterpret_cast<int32_t*>(dls + TMAX * sp) + kGroups * 2 * TMAX * sp);
+    /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
+    const int rloc = 16 * (wv & 1);
+    const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + L.rb * 32 + rloc) * rowbytes;
+    PairLoad<BITS, NI> A;
+    pair_load<BITS, NI>(A, rows0, rowbytes, 0, kDecRows, nb);
+    const int r = L.rb * 32 + (lane & 31);
+    const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
+    const int8_t* act[TMAX];
+    const float* scl[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        const int tok = token_of(sg, pos0 + (t < ntok ? t : 0));
+        act[t] = a.xq + (int64_t)tok * a.H;
+        scl[t] = a.xd + (int64_t)tok * nb;
+    }
+    rows_stage<BITS, TMAX>(xal, dls, nb, sp, ntok, act, scl);
+    const int ng = sg.gu_gb ? nb / sg.gu_gb : 0;
+    const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) + ((int64_t)e * a.I + L.rb * 32 + rloc) * ng
+                                : nullptr;
+    /* job row of the wave's first row: gate rows 0..31, up rows 32..63 */
+    rows_k_loop<BITS, NI, TMAX>(A, rows0, rowbytes, kDecRows, nb, sp, ntok, xal, dls, P, ws0, sg.gu_gb, ng, vs,
+                                16 * wv);
+    __syncthreads();
+    if (wv != 0)
+        return;
+    const int nbi = a.I / 32;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < ntok) {
+            const float v = sc * vs[lane * TMAX + t];
+            const float u = shfl_xor(v, 32);
+            const float h = canon_silu(v) * u;
+            float am = lane < 32 ? __builtin_fabsf(h) : 0.0f;
+            for (int m = 16; m >= 1; m >>= 1)
+                am = fmaxf(am, shfl_xor(am, m));
+            const float dsc = am / 127.0f;
+            const float inv = (am == 0.0f) ? 0.0f : 1.0f / dsc;
+            const int64_t row_out = sg.out_base + pos0 + t;
+            if (lane < 32)
+                a.hq[row_out * a.I + r] = (int8_t)q8_code(h, inv);
+            if (lane == 0)
+                a.hd[row_out * nbi + L.rb] = dsc;
+        }
+    }
+}
+
+template <int BITS, int NI, int TMAX>
+__global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) int32_t rw_lds[];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
+    JobLoc L;
+    if (!locate(a, blockIdx.x, RB, L))
+        return;
+    const FfnSeg sg = pick(a, L.seg);
+    int e, pos0, ntok;
+    if (!unit_info(sg, L.unit, e, pos0, ntok))
+        return;
+    ntok = min(ntok, TMAX);
+    const int nb = a.I / 32, sp = nb | 1;
+    const int64_t rowbytes = (int64_t)a.I * BITS / 8;
+    uint32_t* xal = reinterpret_cast<uint32_t*>(rw_lds);
+    float* dls = reinterpret_cast<float*>(xal + (int64_t)TMAX * nb * 8);
+    int32_t* P = reinterpret_cast<int32_t*>(dls + TMAX * sp) + wv * (2 * TMAX * sp);
+    float* vs = reinterpret_cast<float*>(reinterpret_cast<int32_t*>(dls + TMAX * sp) + kGroups * 2 * TMAX * sp);
+    const int first = L.rb * kRowsPerJob + kDecRows * wv;
+    const int rows_ok = min(kDecRows, max(0, a.H - first));
+    const uint8_t* rows0 = sg.down_w + ((int64_t)e * a.H + min(first, a.H - 1)) * rowbytes;
+    PairLoad<BITS, NI> A;
+    pair_load<BITS, NI>(A, rows0, rowbytes, 0, rows_ok, nb);
+    const int n = first + (lane & 15);
+    const float sc = sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + min(n, a.H - 1)];
+    const int8_t* act[TMAX];
+    const float* scl[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        const int64_t row_in = sg.out_base + pos0 + (t < ntok ? t : 0);
+        act[t] = a.hq + row_in * a.I;
+        scl[t] = a.hd + row_in * nb;
+    }
+    rows_stage<BITS, TMAX>(xal, dls, nb, sp, ntok, act, scl);
+    const int ng = sg.d_gb ? nb / sg.d_gb : 0;
+    const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(first, a.H - 1)) * ng : nullptr;
+    rows_k_loop<BITS, NI, TMAX>(A, rows0, rowbytes, rows_ok, nb, sp, ntok, xal, dls, P, ws0, sg.d_gb, ng, vs,
+                                16 * wv);
+    wave_lds_sync();
+    /* lane (row l % 16): its row's value of every token */
+    if (lane < 16 && n < a.H) {
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+            if (t < ntok)
+                a.y[(int64_t)(sg.out_base + pos0 + t) * a.H + n] = sc * vs[(16 * wv + lane) * TMAX + t];
+    }
+}
+
 /* ---- one token: down projection with the combine --------------------------
  * A workgroup owns 8 output rows for all U = k (+1 shared) units; wave w
  * streams rows 2w, 2w+1 of every unit's down matrix as whole-row pairs
@@ -854,8 +1152,6 @@ __device__ __forceinline__ int dc_unit(uint64_t kept, int n_kept, int k, int n, 
         kept &= kept - 1;
     return __builtin_ctzll(kept);
 }
-
-constexpr int kDcStage = 4;
 
 template <int BITS, int NI>
 __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
@@ -1022,10 +1318,42 @@ static int64_t total_jobs(const FfnArgs& a, int RB)
     return n;
 }
 
+template <int NI, int TMAX>
+static void launch_rows_ni(const FfnArgs& a, int32_t bits, bool gate_up, dim3 grid, size_t lds, hipStream_t st)
+{
+    const dim3 block(64 * kGroups);
+    if (gate_up) {
+        switch (bits) {
+        case 8: hipLaunchKernelGGL((ffn_gate_up_rows<8, NI, TMAX>), grid, block, lds, st, a); break;
+        case 4: hipLaunchKernelGGL((ffn_gate_up_rows<4, NI, TMAX>), grid, block, lds, st, a); break;
+        default: hipLaunchKernelGGL((ffn_gate_up_rows<2, NI, TMAX>), grid, block, lds, st, a); break;
+        }
+    } else {
+        switch (bits) {
+        case 8: hipLaunchKernelGGL((ffn_down_rows<8, NI, TMAX>), grid, block, lds, st, a); break;
+        case 4: hipLaunchKernelGGL((ffn_down_rows<4, NI, TMAX>), grid, block, lds, st, a); break;
+        default: hipLaunchKernelGGL((ffn_down_rows<2, NI, TMAX>), grid, block, lds, st, a); break;
+        }
+    }
+}
+
+/* The whole-row kernels when their LDS fits, else the octet kernels. */
 template <int TMAX>
 static void launch_gate_up_t(const FfnArgs& a, int32_t bits, dim3 grid, hipStream_t st)
 {
     const dim3 block(64 * kGroups);
+    const int nb = a.H / 32;
+    if (rows_fit(nb, TMAX)) {
+        const size_t lds = rows_lds_words(nb, TMAX) * 4;
+        switch (dec_ni(nb)) {
+        case 1: launch_rows_ni<1, TMAX>(a, bits, true, grid, lds, st); break;
+        case 2: launch_rows_ni<2, TMAX>(a, bits, true, grid, lds, st); break;
+        case 4: launch_rows_ni<4, TMAX>(a, bits, true, grid, lds, st); break;
+        case 6: launch_rows_ni<6, TMAX>(a, bits, true, grid, lds, st); break;
+        default: launch_rows_ni<8, TMAX>(a, bits, true, grid, lds, st); break;
+        }
+        return;
+    }
     switch (bits) {
     case 8: hipLaunchKernelGGL((ffn_gate_up_gemv<8, TMAX>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((ffn_gate_up_gemv<4, TMAX>), grid, block, 0, st, a); break;
@@ -1037,6 +1365,18 @@ template <int TMAX>
 static void launch_down_t(const FfnArgs& a, int32_t bits, dim3 grid, hipStream_t st)
 {
     const dim3 block(64 * kGroups);
+    const int nb = a.I / 32;
+    if (rows_fit(nb, TMAX)) {
+        const size_t lds = rows_lds_words(nb, TMAX) * 4;
+        switch (dec_ni(nb)) {
+        case 1: launch_rows_ni<1, TMAX>(a, bits, false, grid, lds, st); break;
+        case 2: launch_rows_ni<2, TMAX>(a, bits, false, grid, lds, st); break;
+        case 4: launch_rows_ni<4, TMAX>(a, bits, false, grid, lds, st); break;
+        case 6: launch_rows_ni<6, TMAX>(a, bits, false, grid, lds, st); break;
+        default: launch_rows_ni<8, TMAX>(a, bits, false, grid, lds, st); break;
+        }
+        return;
+    }
     switch (bits) {
     case 8: hipLaunchKernelGGL((ffn_down_gemv<8, TMAX>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((ffn_down_gemv<4, TMAX>), grid, block, 0, st, a); break;
