@@ -276,6 +276,30 @@ def h2d_probe(torch, nbytes, reps=3):
     return rate
 
 
+def tier_graph_rate(torch, tier, xs, out, ws, S, replays=20):
+    """Per-token time of tier.forward replayed from a captured graph."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for x in xs:
+                tier.forward(x, out, ws)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * len(xs))
+    del g
+    return {"graph_ms_per_step": ms, "graph_tokens_per_s": 1000.0 * S / ms}
+
+
 def run_tier(qre, synth, torch, w, fractions, steps):
     """Decode through colibri_tier_forward at several resident fractions, for
     uniform routing (the workload's normal bias) and for Zipf-skewed expert
@@ -328,12 +352,18 @@ def run_tier(qre, synth, torch, w, fractions, steps):
             s1 = tier.stats()
             hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
             moved = misses * expert_bytes(w)
-            sweep.append({"routing": kind, "resident_fraction": n_slots / E, "n_slots": n_slots,
-                          "tokens_per_s": steps * w.S / t, "ms_per_step": 1000.0 * t / steps,
-                          "expert_hit_rate": hits / max(1, hits + misses),
-                          "expert_loads_per_step": misses / steps,
-                          "passes_per_step": (s1["passes"] - s0["passes"]) / steps,
-                          "h2d_GBps": moved / t / 1e9})
+            point = {"routing": kind, "resident_fraction": n_slots / E, "n_slots": n_slots,
+                     "tokens_per_s": steps * w.S / t, "ms_per_step": 1000.0 * t / steps,
+                     "expert_hit_rate": hits / max(1, hits + misses),
+                     "expert_loads_per_step": misses / steps,
+                     "passes_per_step": (s1["passes"] - s0["passes"]) / steps,
+                     "h2d_GBps": moved / t / 1e9}
+            if n_slots == E:
+                # The hit path without the host: 16 forwards over 16 distinct
+                # tokens captured in one graph (nothing misses, so replaying
+                # the same tokens changes no rate), replayed and timed on the GPU.
+                point.update(tier_graph_rate(torch, tier, xs[:16], out, ws, w.S))
+            sweep.append(point)
             tier.close()
             del ws
     return {"h2d_probe_GBps": probe, "sweep": sweep}
