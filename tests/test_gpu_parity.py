@@ -176,6 +176,7 @@ def _ffn_case(bits, H, I, E, S, k, seed, g_gu=0, g_d=0):
     (256, 160, 2, 100, 2, 1.0),   # several 32-token MFMA units per expert, ragged N tile
     (96, 96, 5, 40, 3, 1.0),      # MFMA with ragged rows and K tails
     (256, 128, 3, 24, 2, 1e-36),  # tiny activations: block scale * 2^-(8-b) subnormal
+    (8192, 64, 4, 6, 2, 1.0),     # K = 8192, few tokens per expert: the octet GEMV (whole-row LDS over 64 KB)
 ])
 def test_expert_ffn_bit_exact(qre, bits, H, I, E, S, k, scale):
     say(f"ffn bits={bits} H={H} I={I} E={E} S={S} k={k} scale={scale}")
