@@ -1235,6 +1235,53 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     const float rs_l = (rt_r ? a.seg[0].d_gb : a.seg[1].d_gb) ? 1.0f : ds_r[(int64_t)e_r * a.H + row0 + (lane & 1)];
     __syncthreads();
 
+    /* fold of chains [c_begin, c_end): chain (rd, g) = (compacted unit rd / 2,
+     * row rd % 2; group g), lane ci - c0 of round c0 */
+    auto fold_chains = [&](int c_begin, int c_end) {
+        for (int c0 = c_begin; c0 < c_end; c0 += 64) {
+            const int ci = c0 + lane;
+            const int rd = min(ci >> 2, 2 * U - 1), g = ci & 3;
+            const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
+            const int32_t* pr = P + rd * sp;
+            const float* dj = dls + (rd >> 1) * sp;
+            float acc = 0.0f;
+            int b = b0;
+            /* lane values are read before any branch: every lane is active */
+            const int uf = __shfl(u_l, rd >> 1, kWave), ef = __shfl(e_l, rd >> 1, kWave);
+            const float rsv = __shfl(rs_l, rd, kWave);
+            const int gbf = uf < d.k ? a.seg[0].d_gb : a.seg[1].d_gb;
+            if (gbf) {
+                /* group-wise scales of (unit, row) */
+                const float* ws = (uf < d.k ? a.seg[0].down_s : a.seg[1].down_s) +
+                                  ((int64_t)ef * a.H + row0 + (rd & 1)) * (nb / gbf);
+                for (; b < b1; ++b)
+                    acc = __builtin_fmaf(group_coef(ws, gbf, b, dj[b]), (float)pr[b], acc);
+            } else {
+                for (; b + 8 <= b1; b += 8) {
+                    int32_t q[8];
+                    float dd[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        q[i] = pr[b + i];
+                        dd[i] = dj[b + i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+                }
+                for (; b < b1; ++b)
+                    acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
+            }
+            const int base = lane & ~3;
+            float v = __shfl(acc, base, kWave);
+            v = v + __shfl(acc, base + 1, kWave);
+            v = v + __shfl(acc, base + 2, kWave);
+            v = v + __shfl(acc, base + 3, kWave);
+            if (g == 0 && ci < c_end)
+                ys[rd] = rsv * v; /* rsv: 1 with group-wise scales */
+        }
+    };
+
     /* the pair of stream position q is in A for even q and in B for odd q;
      * loads are unconditional (past the last unit they reload it: in bounds,
      * unused) */
@@ -1253,52 +1300,15 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
             dc_act<NI>(xal, j1, nb, xa);
             pair_partials<BITS, NI>(B, xa, 0, nb, P + 2 * j1 * sp, sp);
         }
+        if (q == 0 && shared) {
+            /* the shared expert (streamed first) is folded while the routed
+             * pairs load, so the final fold is one round for 8 routed units */
+            wave_lds_sync();
+            fold_chains(8 * (U - 1), 8 * U);
+        }
     }
     wave_lds_sync();
-
-    /* fold: chain (rd, g) = (unit rd / 2, row rd % 2; group g) */
-    for (int c0 = 0; c0 < 8 * U; c0 += 64) {
-        const int ci = c0 + lane;
-        const int rd = min(ci >> 2, 2 * U - 1), g = ci & 3;
-        const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
-        const int32_t* pr = P + rd * sp;
-        const float* dj = dls + (rd >> 1) * sp;
-        float acc = 0.0f;
-        int b = b0;
-        /* lane values are read before any branch: every lane is active */
-        const int uf = __shfl(u_l, rd >> 1, kWave), ef = __shfl(e_l, rd >> 1, kWave);
-        const float rsv = __shfl(rs_l, rd, kWave);
-        const int gbf = uf < d.k ? a.seg[0].d_gb : a.seg[1].d_gb;
-        if (gbf) {
-            /* group-wise scales of (unit, row) */
-            const float* ws = (uf < d.k ? a.seg[0].down_s : a.seg[1].down_s) +
-                              ((int64_t)ef * a.H + row0 + (rd & 1)) * (nb / gbf);
-            for (; b < b1; ++b)
-                acc = __builtin_fmaf(group_coef(ws, gbf, b, dj[b]), (float)pr[b], acc);
-        } else {
-            for (; b + 8 <= b1; b += 8) {
-                int32_t q[8];
-                float dd[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    q[i] = pr[b + i];
-                    dd[i] = dj[b + i];
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc = __builtin_fmaf(dd[i], (float)q[i], acc);
-            }
-            for (; b < b1; ++b)
-                acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
-        }
-        const int base = lane & ~3;
-        float v = __shfl(acc, base, kWave);
-        v = v + __shfl(acc, base + 1, kWave);
-        v = v + __shfl(acc, base + 2, kWave);
-        v = v + __shfl(acc, base + 3, kWave);
-        if (g == 0 && ci < 8 * U)
-            ys[rd] = rsv * v; /* rsv: 1 with group-wise scales */
-    }
+    fold_chains(0, shared ? 8 * (U - 1) : 8 * U);
     wave_lds_sync();
     /* compacted order is slot order: the combine's fma order is kept (every
      * lane runs the chain of row lane & 1; lanes 0 and 1 store) */
