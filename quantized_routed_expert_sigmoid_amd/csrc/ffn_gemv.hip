@@ -830,9 +830,10 @@ __device__ __forceinline__ void rows_partials(const PairLoad<BITS, NI>& L, const
                                               int32_t* P, int sp)
 {
     const int lane = threadIdx.x & 63, c = lane & 31, row = lane >> 5;
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < ntok) {
+    /* tokens one at a time (a rolled loop keeps one token's operands live) */
+#pragma unroll 1
+    for (int t = 0; t < ntok; ++t) {
+        {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int b = c + 32 * i;
