@@ -60,6 +60,15 @@ struct KLds {
     float ws[2][GROUPED ? 64 * Cfg<BITS>::kStep : 1];       /* [row][block of the step] weight scale */
 };
 
+/* LDS of the aligned K loop: the two N-tiles' operands of a lane side by
+ * side, so that one read brings both. */
+template <int BITS>
+struct __attribute__((aligned(16))) LeanLds {
+    uint32_t a[2][64 * Cfg<BITS>::kRowStride];             /* weight rows, packed words */
+    __attribute__((aligned(16))) uint32_t b[2][Cfg<BITS>::kStep][4][16][2][2]; /* [block][g][token & 15][tile][word] */
+    __attribute__((aligned(16))) float ds[2][Cfg<BITS>::kStep][16][2];        /* [block][token & 15][tile] */
+};
+
 struct EpiLds {
     float v[64][kTok + 1]; /* [row dot][token] */
 };
@@ -67,6 +76,7 @@ struct EpiLds {
 template <int BITS, bool GROUPED = false>
 union MfmaShared {
     KLds<BITS, GROUPED> k;
+    LeanLds<BITS> l;
     EpiLds e;
 };
 
@@ -411,7 +421,7 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             acc[n][v] = 0.0f;
-            tot[n][v] = 0.0f;
+            tot[n][v] = -0.0f; /* -0 + s == s: the first flush leaves group 0's sum as is */
         }
     const int nsteps = (nb + C::kStep - 1) / C::kStep;
     Stage<BITS, GROUPED> P0, P1;
@@ -450,6 +460,274 @@ __device__ __forceinline__ void mfma_k_loop(KLds<BITS, GROUPED>& S, const LoadLa
         k_loop_nt<BITS, 1, GROUPED>(S, L, tot);
 }
 
+/* ---- the aligned K loop ----------------------------------------------------
+ *
+ * For rows whose four canonical block groups are each a whole, even number
+ * of K steps (nb a multiple of 8 * kStep: H = 6144 and I = 2048 both are),
+ * with per-row weight scales.  Groups become loop boundaries, so a step
+ * never checks for a boundary or the row end.  Every load takes a uniform
+ * base (the wave's weight matrix, the activation arrays, advanced by the
+ * step index) plus a fixed 32-bit per-thread offset, so a step's addressing
+ * costs no vector instructions.  It always folds with the block scale times
+ * 2^-(8-b); a step whose scale would not be exact that way is only noted,
+ * and the caller then recomputes the unit with the general loop above. */
+
+template <int BITS>
+__device__ __forceinline__ bool lean_shape(int nb)
+{
+    return nb > 0 && nb % (8 * Cfg<BITS>::kStep) == 0;
+}
+
+struct LeanLane {
+    const uint8_t* w;  /* wave-uniform: first byte of the wave's weight rows' matrix window */
+    const int8_t* x;   /* uniform: activation codes */
+    const float* xd;   /* uniform: activation block scales */
+    uint32_t wo;       /* thread: byte offset of its first weight block of step 0 */
+    uint32_t xo;       /* thread: element offset of its activation words of step 0 */
+    uint32_t dof;      /* thread: index of its activation block scale of step 0 */
+    int nsteps;
+};
+
+template <int BITS>
+__device__ __forceinline__ void lean_fetch(Stage<BITS, false>& P, const LeanLane& L, int st)
+{
+    using C = Cfg<BITS>;
+    /* steps past the row reload its last step (never multiplied) */
+    const int s = min(st, L.nsteps - 1);
+    const uint8_t* w = L.w + (size_t)s * (C::kStep * 4 * BITS) + L.wo;
+#pragma unroll
+    for (int i = 0; i < C::kBpt; ++i) {
+        const uint8_t* p = w + i * (4 * BITS);
+        if constexpr (BITS == 8) {
+            const u32x4 u = reinterpret_cast<const u32x4*>(p)[0];
+            const u32x4 v = reinterpret_cast<const u32x4*>(p)[1];
+            P.w[0] = u.x; P.w[1] = u.y; P.w[2] = u.z; P.w[3] = u.w;
+            P.w[4] = v.x; P.w[5] = v.y; P.w[6] = v.z; P.w[7] = v.w;
+        } else if constexpr (BITS == 4) {
+            const u32x4 u = reinterpret_cast<const u32x4*>(p)[0];
+            P.w[4 * i + 0] = u.x; P.w[4 * i + 1] = u.y; P.w[4 * i + 2] = u.z; P.w[4 * i + 3] = u.w;
+        } else {
+            const u32x2 u = reinterpret_cast<const u32x2*>(p)[0];
+            P.w[2 * i + 0] = u.x; P.w[2 * i + 1] = u.y;
+        }
+    }
+    const int8_t* x = L.x + (size_t)s * (C::kStep * 32) + L.xo;
+    if constexpr (C::kStep == 8) {
+        const u32x4 u = reinterpret_cast<const u32x4*>(x)[0];
+        const u32x4 v = reinterpret_cast<const u32x4*>(x)[1];
+        P.x[0] = u.x; P.x[1] = u.y; P.x[2] = u.z; P.x[3] = u.w;
+        P.x[4] = v.x; P.x[5] = v.y; P.x[6] = v.z; P.x[7] = v.w;
+    } else {
+        const u32x4 u = reinterpret_cast<const u32x4*>(x)[0];
+        P.x[0] = u.x; P.x[1] = u.y; P.x[2] = u.z; P.x[3] = u.w;
+    }
+    P.d = L.xd[(size_t)s * C::kStep + L.dof];
+}
+
+/* commit() into the aligned loop's layout, without the exact-shift
+ * bookkeeping; true when this thread's block scale times 2^-(8-b) is not
+ * exact. */
+template <int BITS>
+__device__ __forceinline__ bool lean_commit(const Stage<BITS, false>& P, LeanLds<BITS>& S, int buf)
+{
+    using C = Cfg<BITS>;
+    constexpr int SHIFT = 8 - BITS;
+    const int l = threadIdx.x;
+    uint32_t* ad = &S.a[buf][(l >> 2) * C::kRowStride + C::kBpt * BITS * (l & 3)];
+#pragma unroll
+    for (int i = 0; i < C::kBpt * BITS; ++i)
+        ad[i] = P.w[i];
+    const int t = l & 31, tr = t & 15, tn = t >> 4;
+    int j;
+    if constexpr (C::kStep == 8) {
+        j = l >> 5;
+        uint32_t xa[8];
+        prep_activation<BITS>(P.x, xa);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<u32x2*>(&S.b[buf][j][g][tr][tn][0]) = u32x2{xa[2 * g], xa[2 * g + 1]};
+    } else {
+        /* int8: natural operand order, half h holds operand groups 2h, 2h+1 */
+        j = l >> 6;
+        const int h = (l >> 5) & 1;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+            *reinterpret_cast<u32x2*>(&S.b[buf][j][2 * h + gg][tr][tn][0]) = u32x2{P.x[2 * gg], P.x[2 * gg + 1]};
+    }
+    const float ds = P.d * (1.0f / (float)(1 << SHIFT));
+    S.ds[buf][j][tr][tn] = ds;
+    return SHIFT != 0 && P.d != 0.0f && !(ds >= 1.17549435e-38f);
+}
+
+/* One block's LDS operands for a lane: its weight word(s), the B operand of
+ * each N-tile and the tiles' block scales. */
+template <int BITS, int NT>
+struct LeanOps {
+    uint32_t w[BITS == 8 ? 2 : 1];
+    uint32_t b[2 * NT];
+    float d[NT];
+};
+
+template <int BITS, int NT>
+__device__ __forceinline__ void lean_read(const LeanLds<BITS>& S, int buf, int j, const uint32_t* arow, int r,
+                                          int g, LeanOps<BITS, NT>& o)
+{
+    if constexpr (BITS == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(arow + j * BITS + 2 * g);
+        o.w[0] = v.x;
+        o.w[1] = v.y;
+    } else if constexpr (BITS == 4) {
+        o.w[0] = arow[j * BITS + g];
+    } else {
+        o.w[0] = arow[j * BITS + (g >> 1)];
+    }
+    if constexpr (NT == 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&S.b[buf][j][g][r][0][0]);
+        o.b[0] = v.x; o.b[1] = v.y; o.b[2] = v.z; o.b[3] = v.w;
+        const float2 d = *reinterpret_cast<const float2*>(&S.ds[buf][j][r][0]);
+        o.d[0] = d.x;
+        o.d[1] = d.y;
+    } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(&S.b[buf][j][g][r][0][0]);
+        o.b[0] = v.x; o.b[1] = v.y;
+        o.d[0] = S.ds[buf][j][r][0];
+    }
+}
+
+template <int BITS, int NT>
+__device__ __forceinline__ void lean_mfma(const LeanOps<BITS, NT>& o, int g, i32x4 (&c)[NT])
+{
+    /* the A operand of a_operand(), from the one word lane group g needs */
+    uint32_t lo, hi;
+    if constexpr (BITS == 8) {
+        lo = o.w[0];
+        hi = o.w[1];
+    } else if constexpr (BITS == 4) {
+        lo = o.w[0] & 0xF0F0F0F0u;
+        hi = (o.w[0] << 4) & 0xF0F0F0F0u;
+    } else {
+        const int r0 = 2 * (g & 1);
+        lo = (o.w[0] << (2 * r0)) & 0xC0C0C0C0u;
+        hi = (o.w[0] << (2 * r0 + 2)) & 0xC0C0C0C0u;
+    }
+    const long A = (long)(((uint64_t)hi << 32) | lo);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const long B = (long)(((uint64_t)o.b[2 * n + 1] << 32) | o.b[2 * n]);
+        c[n] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+    }
+}
+
+template <int BITS, int NT>
+__device__ __forceinline__ void lean_fold(const LeanOps<BITS, NT>& o, const i32x4 (&c)[NT], float (&acc)[2][4])
+{
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[n][v] = __builtin_fmaf(o.d[n], (float)c[n][v], acc[n][v]);
+}
+
+/* One K step, software-pipelined over its blocks: while block j
+ * multiplies, the operands of block j + 1 are read and block j - 1 is
+ * folded, so neither an LDS read nor an MFMA result is waited for right
+ * before its use. */
+template <int BITS, int NT>
+__device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float (&acc)[2][4])
+{
+    using C = Cfg<BITS>;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const uint32_t* arow = &S.a[buf][(16 * wv + r) * C::kRowStride];
+    LeanOps<BITS, NT> o[3];
+    i32x4 c[2][NT];
+    lean_read<BITS, NT>(S, buf, 0, arow, r, g, o[0]);
+#pragma unroll
+    for (int j = 0; j <= C::kStep; ++j) {
+        if (j + 1 < C::kStep)
+            lean_read<BITS, NT>(S, buf, j + 1, arow, r, g, o[(j + 1) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < C::kStep)
+            lean_mfma<BITS, NT>(o[j % 3], g, c[j & 1]);
+        if (j >= 1)
+            lean_fold<BITS, NT>(o[(j - 1) % 3], c[(j - 1) & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+/* Same pipeline as k_loop_nt (two steps of loads in registers, one in LDS,
+ * one barrier per step).  Returns true (uniformly) when some step's scales
+ * were not exact with the 2^-(8-b) factor taken out; tot is then void. */
+template <int BITS, int NT>
+__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&tot)[2][4])
+{
+    const int spg = L.nsteps / 4; /* even */
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            tot[n][v] = -0.0f; /* -0 + s == s for every s: tot becomes group 0's sum exactly */
+    Stage<BITS, false> P0, P1;
+    lean_fetch<BITS>(P0, L, 0);
+    lean_fetch<BITS>(P1, L, 1);
+    bool bad = lean_commit<BITS>(P0, S, 0);
+    lean_fetch<BITS>(P0, L, 2);
+    __syncthreads();
+    int st = 0;
+#pragma unroll 1
+    for (int grp = 0; grp < 4; ++grp) {
+        float acc[2][4];
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                acc[n][v] = 0.0f;
+#pragma unroll 1
+        for (int s = 0; s < spg; s += 2, st += 2) {
+            lean_step<BITS, NT>(S, 0, acc);
+            bad |= lean_commit<BITS>(P1, S, 1);
+            lean_fetch<BITS>(P1, L, st + 3);
+            __syncthreads();
+            lean_step<BITS, NT>(S, 1, acc);
+            bad |= lean_commit<BITS>(P0, S, 0);
+            lean_fetch<BITS>(P0, L, st + 4);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                tot[n][v] = tot[n][v] + acc[n][v];
+    }
+    return __syncthreads_or(bad) != 0;
+}
+
+template <int BITS>
+__device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, int ntiles,
+                                                 float (&tot)[2][4])
+{
+    if (ntiles > 1)
+        return k_loop_lean<BITS, 2>(S, L, tot);
+    return k_loop_lean<BITS, 1>(S, L, tot);
+}
+
+/* The thread's activation offsets within a step (token row base excluded). */
+template <int BITS>
+__device__ __forceinline__ uint32_t lean_x_in_step()
+{
+    const int l = threadIdx.x;
+    if constexpr (Cfg<BITS>::kStep == 8)
+        return (uint32_t)(l >> 5) * 32u;
+    return (uint32_t)(l >> 6) * 32u + (uint32_t)((l >> 5) & 1) * 16u;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t lean_d_in_step()
+{
+    const int l = threadIdx.x;
+    return (uint32_t)(Cfg<BITS>::kStep == 8 ? (l >> 5) : (l >> 6));
+}
+
 } // namespace
 
 /* GROUPED: a launch whose segments may hold group-wise scales (a separate
@@ -483,9 +761,26 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
                    : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
-    /* group-wise scales of the lane's row dots 16w + 4(lane/16) + v */
     float tot[2][4];
-    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
+    bool general = true;
+    if constexpr (!GROUPED) {
+        /* the aligned loop, while every activation offset fits 31 bits */
+        if (lean_shape<BITS>(nb) && (int64_t)sg.S * a.H < (int64_t(1) << 31)) {
+            const int wvu = __builtin_amdgcn_readfirstlane(wv);
+            LeanLane LL;
+            LL.w = (wvu < 2 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + M.rb * 32) * rowbytes;
+            LL.wo = (uint32_t)(rd & 31) * (uint32_t)rowbytes +
+                    (uint32_t)(Cfg<BITS>::kBpt * 4 * BITS) * (uint32_t)(threadIdx.x & 3);
+            LL.x = a.xq;
+            LL.xo = (uint32_t)tok * (uint32_t)a.H + lean_x_in_step<BITS>();
+            LL.xd = a.xd;
+            LL.dof = (uint32_t)tok * (uint32_t)nb + lean_d_in_step<BITS>();
+            LL.nsteps = nb / Cfg<BITS>::kStep;
+            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, tot);
+        }
+    }
+    if (general)
+        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
 
     /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
      * h = silu(g) * u and one Q8_0 block of h per token */
@@ -556,7 +851,25 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
     float tot[2][4];
-    mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
+    bool general = true;
+    if constexpr (!GROUPED) {
+        /* the aligned loop, while the weight offsets in one matrix fit 31 bits */
+        if (lean_shape<BITS>(nb) && (int64_t)a.H * rowbytes < (int64_t(1) << 31)) {
+            const int64_t r0 = sg.out_base + pos0;
+            LeanLane LL;
+            LL.w = sg.down_w + (int64_t)e * a.H * rowbytes;
+            LL.wo = (uint32_t)(row < a.H ? row : 0) * (uint32_t)rowbytes +
+                    (uint32_t)(Cfg<BITS>::kBpt * 4 * BITS) * (uint32_t)(threadIdx.x & 3);
+            LL.x = a.hq + r0 * a.I;
+            LL.xo = (uint32_t)(tl < ntok ? tl : 0) * (uint32_t)a.I + lean_x_in_step<BITS>();
+            LL.xd = a.hd + r0 * nb;
+            LL.dof = (uint32_t)(tl < ntok ? tl : 0) * (uint32_t)nb + lean_d_in_step<BITS>();
+            LL.nsteps = nb / Cfg<BITS>::kStep;
+            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, tot);
+        }
+    }
+    if (general)
+        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {

@@ -177,6 +177,9 @@ def _ffn_case(bits, H, I, E, S, k, seed, g_gu=0, g_d=0):
     (96, 96, 5, 40, 3, 1.0),      # MFMA with ragged rows and K tails
     (256, 128, 3, 24, 2, 1e-36),  # tiny activations: block scale * 2^-(8-b) subnormal
     (8192, 64, 4, 6, 2, 1.0),     # K = 8192, few tokens per expert: the octet GEMV (whole-row LDS over 64 KB)
+    (2048, 2048, 3, 40, 2, 1.0),  # matrix cores, aligned K loop (whole even step counts per group), two N-tiles
+    (2048, 2048, 6, 40, 2, 1.0),  # aligned K loop, one N-tile
+    (2048, 2048, 3, 24, 2, 1e-36),  # aligned K loop meets subnormal scale products: the general loop redoes the unit
 ])
 def test_expert_ffn_bit_exact(qre, bits, H, I, E, S, k, scale):
     say(f"ffn bits={bits} H={H} I={I} E={E} S={S} k={k} scale={scale}")
