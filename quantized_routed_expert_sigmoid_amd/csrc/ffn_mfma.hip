@@ -60,11 +60,53 @@ struct KLds {
     float ws[2][GROUPED ? 64 * Cfg<BITS>::kStep : 1];       /* [row][block of the step] weight scale */
 };
 
+/* The aligned K loop's weight loads: every instruction reads whole 16-byte
+ * chunks of kCR consecutive chunks per row (a row's whole step), kNL
+ * instructions per thread; its LDS rows are 16-byte aligned, at a stride
+ * whose A-operand reads hit distinct banks. */
+template <int BITS>
+struct LCfg {
+    static constexpr int kCR = Cfg<BITS>::kRowWords / 4; /* 16-byte chunks per row and step */
+    static constexpr int kNL = kCR / 4;                  /* weight loads per thread */
+    static constexpr int kRowsPerLoad = 256 / kCR;
+    static constexpr int kStride = Cfg<BITS>::kRowWords + 4;
+    /* activations: a token's step (kStep blocks) is kXC 16-byte chunks, read
+     * by kXC consecutive lanes; kNXL loads per thread */
+    static constexpr int kXC = 2 * Cfg<BITS>::kStep;
+    static constexpr int kNXL = kXC / 8;
+    static constexpr int kTokPerLoad = 256 / kXC;
+};
+
+/* Token slot of (block j, operand group g) in the aligned loop's B layout:
+ * the 16 tokens of a tile are stored XOR-permuted by (j, g), so that the
+ * stores of one instruction (one token per 16 lanes, every block and half)
+ * spread over the banks while a lane group's reads stay contiguous. */
+__device__ __forceinline__ int lean_slot(int tr, int j, int g)
+{
+    return tr ^ ((2 * j + (g >> 1)) & 15);
+}
+
+/* The block scale a thread loads in each step: consecutive threads take
+ * consecutive blocks of one token, so a wave's load covers whole token
+ * slices (int8: threads 128.. repeat 0..127). */
+template <int BITS>
+__device__ __forceinline__ int lean_d_token()
+{
+    const int l = threadIdx.x;
+    return Cfg<BITS>::kStep == 8 ? (l >> 3) : ((l >> 2) & 31);
+}
+
+template <int BITS>
+__device__ __forceinline__ int lean_d_block()
+{
+    return (int)threadIdx.x & (Cfg<BITS>::kStep - 1);
+}
+
 /* LDS of the aligned K loop: the two N-tiles' operands of a lane side by
  * side, so that one read brings both. */
 template <int BITS>
 struct __attribute__((aligned(16))) LeanLds {
-    uint32_t a[2][64 * Cfg<BITS>::kRowStride];             /* weight rows, packed words */
+    __attribute__((aligned(16))) uint32_t a[2][64 * LCfg<BITS>::kStride]; /* weight rows, packed words */
     __attribute__((aligned(16))) uint32_t b[2][Cfg<BITS>::kStep][4][16][2][2]; /* [block][g][token & 15][tile][word] */
     __attribute__((aligned(16))) float ds[2][Cfg<BITS>::kStep][16][2];        /* [block][token & 15][tile] */
 };
@@ -479,47 +521,32 @@ __device__ __forceinline__ bool lean_shape(int nb)
 }
 
 struct LeanLane {
-    const uint8_t* w;  /* wave-uniform: first byte of the wave's weight rows' matrix window */
-    const int8_t* x;   /* uniform: activation codes */
-    const float* xd;   /* uniform: activation block scales */
-    uint32_t wo;       /* thread: byte offset of its first weight block of step 0 */
-    uint32_t xo;       /* thread: element offset of its activation words of step 0 */
+    const uint8_t* wb[2]; /* wave-uniform: matrix window of weight load i */
+    const int8_t* x;      /* uniform: activation codes */
+    const float* xd;      /* uniform: activation block scales */
+    uint32_t wo[2];       /* thread: byte offset of weight load i's chunk of step 0 */
+    uint32_t xo[2];       /* thread: element offset of activation load i's chunk of step 0 */
     uint32_t dof;      /* thread: index of its activation block scale of step 0 */
     int nsteps;
 };
 
-template <int BITS>
+template <int BITS, int NT>
 __device__ __forceinline__ void lean_fetch(Stage<BITS, false>& P, const LeanLane& L, int st)
 {
     using C = Cfg<BITS>;
     /* steps past the row reload its last step (never multiplied) */
     const int s = min(st, L.nsteps - 1);
-    const uint8_t* w = L.w + (size_t)s * (C::kStep * 4 * BITS) + L.wo;
 #pragma unroll
-    for (int i = 0; i < C::kBpt; ++i) {
-        const uint8_t* p = w + i * (4 * BITS);
-        if constexpr (BITS == 8) {
-            const u32x4 u = reinterpret_cast<const u32x4*>(p)[0];
-            const u32x4 v = reinterpret_cast<const u32x4*>(p)[1];
-            P.w[0] = u.x; P.w[1] = u.y; P.w[2] = u.z; P.w[3] = u.w;
-            P.w[4] = v.x; P.w[5] = v.y; P.w[6] = v.z; P.w[7] = v.w;
-        } else if constexpr (BITS == 4) {
-            const u32x4 u = reinterpret_cast<const u32x4*>(p)[0];
-            P.w[4 * i + 0] = u.x; P.w[4 * i + 1] = u.y; P.w[4 * i + 2] = u.z; P.w[4 * i + 3] = u.w;
-        } else {
-            const u32x2 u = reinterpret_cast<const u32x2*>(p)[0];
-            P.w[2 * i + 0] = u.x; P.w[2 * i + 1] = u.y;
-        }
+    for (int i = 0; i < LCfg<BITS>::kNL; ++i) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(L.wb[i] + (size_t)s * (C::kRowWords * 4) + L.wo[i]);
+        P.w[4 * i + 0] = u.x; P.w[4 * i + 1] = u.y; P.w[4 * i + 2] = u.z; P.w[4 * i + 3] = u.w;
     }
-    const int8_t* x = L.x + (size_t)s * (C::kStep * 32) + L.xo;
-    if constexpr (C::kStep == 8) {
-        const u32x4 u = reinterpret_cast<const u32x4*>(x)[0];
-        const u32x4 v = reinterpret_cast<const u32x4*>(x)[1];
-        P.x[0] = u.x; P.x[1] = u.y; P.x[2] = u.z; P.x[3] = u.w;
-        P.x[4] = v.x; P.x[5] = v.y; P.x[6] = v.z; P.x[7] = v.w;
-    } else {
-        const u32x4 u = reinterpret_cast<const u32x4*>(x)[0];
-        P.x[0] = u.x; P.x[1] = u.y; P.x[2] = u.z; P.x[3] = u.w;
+    /* one tile: the second load (tokens 16..31) is not needed */
+    constexpr int NX = (NT == 1 && LCfg<BITS>::kNXL == 2) ? 1 : LCfg<BITS>::kNXL;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(L.x + (size_t)s * (C::kStep * 32) + L.xo[i]);
+        P.x[4 * i + 0] = u.x; P.x[4 * i + 1] = u.y; P.x[4 * i + 2] = u.z; P.x[4 * i + 3] = u.w;
     }
     P.d = L.xd[(size_t)s * C::kStep + L.dof];
 }
@@ -527,33 +554,58 @@ __device__ __forceinline__ void lean_fetch(Stage<BITS, false>& P, const LeanLane
 /* commit() into the aligned loop's layout, without the exact-shift
  * bookkeeping; true when this thread's block scale times 2^-(8-b) is not
  * exact. */
+/* prep_activation() of one 16-byte half of a block: the operand words of
+ * lane groups 2h and 2h + 1 (h the half). */
 template <int BITS>
+__device__ __forceinline__ void prep_half(const uint32_t* x, uint32_t (&xa)[4])
+{
+    if constexpr (BITS == 8) {
+        xa[0] = x[0]; xa[1] = x[1]; xa[2] = x[2]; xa[3] = x[3];
+    } else if constexpr (BITS == 4) {
+        xa[0] = COLI_PERM(x[1], x[0], 0x06040200u);
+        xa[1] = COLI_PERM(x[1], x[0], 0x07050301u);
+        xa[2] = COLI_PERM(x[3], x[2], 0x06040200u);
+        xa[3] = COLI_PERM(x[3], x[2], 0x07050301u);
+    } else {
+        const uint32_t ab_lo = COLI_PERM(x[1], x[0], 0x05010400u), ab_hi = COLI_PERM(x[1], x[0], 0x07030602u);
+        const uint32_t cd_lo = COLI_PERM(x[3], x[2], 0x05010400u), cd_hi = COLI_PERM(x[3], x[2], 0x07030602u);
+        xa[0] = COLI_PERM(cd_lo, ab_lo, 0x05040100u);
+        xa[1] = COLI_PERM(cd_lo, ab_lo, 0x07060302u);
+        xa[2] = COLI_PERM(cd_hi, ab_hi, 0x05040100u);
+        xa[3] = COLI_PERM(cd_hi, ab_hi, 0x07060302u);
+    }
+}
+
+template <int BITS, int NT>
 __device__ __forceinline__ bool lean_commit(const Stage<BITS, false>& P, LeanLds<BITS>& S, int buf)
 {
     using C = Cfg<BITS>;
     constexpr int SHIFT = 8 - BITS;
+    using LC = LCfg<BITS>;
     const int l = threadIdx.x;
-    uint32_t* ad = &S.a[buf][(l >> 2) * C::kRowStride + C::kBpt * BITS * (l & 3)];
 #pragma unroll
-    for (int i = 0; i < C::kBpt * BITS; ++i)
-        ad[i] = P.w[i];
-    const int t = l & 31, tr = t & 15, tn = t >> 4;
-    int j;
-    if constexpr (C::kStep == 8) {
-        j = l >> 5;
-        uint32_t xa[8];
-        prep_activation<BITS>(P.x, xa);
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<u32x2*>(&S.b[buf][j][g][tr][tn][0]) = u32x2{xa[2 * g], xa[2 * g + 1]};
-    } else {
-        /* int8: natural operand order, half h holds operand groups 2h, 2h+1 */
-        j = l >> 6;
-        const int h = (l >> 5) & 1;
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg)
-            *reinterpret_cast<u32x2*>(&S.b[buf][j][2 * h + gg][tr][tn][0]) = u32x2{P.x[2 * gg], P.x[2 * gg + 1]};
+    for (int i = 0; i < LC::kNL; ++i) {
+        const int row = i * LC::kRowsPerLoad + l / LC::kCR;
+        *reinterpret_cast<u32x4*>(&S.a[buf][row * LC::kStride + 4 * (l % LC::kCR)]) =
+            u32x4{P.w[4 * i], P.w[4 * i + 1], P.w[4 * i + 2], P.w[4 * i + 3]};
     }
+    constexpr int NX = (NT == 1 && LC::kNXL == 2) ? 1 : LC::kNXL;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+        const int tt = i * LC::kTokPerLoad + l / LC::kXC, c = l % LC::kXC;
+        const int jx = c >> 1, h = c & 1;
+        uint32_t xa[4];
+        prep_half<BITS>(&P.x[4 * i], xa);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int g = 2 * h + k;
+            *reinterpret_cast<u32x2*>(&S.b[buf][jx][g][lean_slot(tt & 15, jx, g)][tt >> 4][0]) =
+                u32x2{xa[2 * k], xa[2 * k + 1]};
+        }
+    }
+    /* block scales: token lean_d_token(), block lean_d_block() of the step */
+    const int t = lean_d_token<BITS>(), tr = t & 15, tn = t >> 4;
+    const int j = lean_d_block<BITS>();
     const float ds = P.d * (1.0f / (float)(1 << SHIFT));
     S.ds[buf][j][tr][tn] = ds;
     return SHIFT != 0 && P.d != 0.0f && !(ds >= 1.17549435e-38f);
@@ -581,14 +633,15 @@ __device__ __forceinline__ void lean_read(const LeanLds<BITS>& S, int buf, int j
     } else {
         o.w[0] = arow[j * BITS + (g >> 1)];
     }
+    const int rs = lean_slot(r, j, g);
     if constexpr (NT == 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&S.b[buf][j][g][r][0][0]);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&S.b[buf][j][g][rs][0][0]);
         o.b[0] = v.x; o.b[1] = v.y; o.b[2] = v.z; o.b[3] = v.w;
         const float2 d = *reinterpret_cast<const float2*>(&S.ds[buf][j][r][0]);
         o.d[0] = d.x;
         o.d[1] = d.y;
     } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(&S.b[buf][j][g][r][0][0]);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(&S.b[buf][j][g][rs][0][0]);
         o.b[0] = v.x; o.b[1] = v.y;
         o.d[0] = S.ds[buf][j][r][0];
     }
@@ -638,7 +691,7 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const uint32_t* arow = &S.a[buf][(16 * wv + r) * C::kRowStride];
+    const uint32_t* arow = &S.a[buf][(16 * wv + r) * LCfg<BITS>::kStride];
     LeanOps<BITS, NT> o[3];
     i32x4 c[2][NT];
     lean_read<BITS, NT>(S, buf, 0, arow, r, g, o[0]);
@@ -655,50 +708,62 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
     }
 }
 
-/* Same pipeline as k_loop_nt (two steps of loads in registers, one in LDS,
- * one barrier per step).  Returns true (uniformly) when some step's scales
- * were not exact with the 2^-(8-b) factor taken out; tot is then void. */
-template <int BITS, int NT>
+/* D steps of loads in registers (stage k holds the steps = k mod D), one
+ * in LDS, one barrier per step; the loop body covers U steps so that stage
+ * and LDS buffer indices are compile-time.  Returns true (uniformly) when
+ * some step's scales were not exact with the 2^-(8-b) factor taken out;
+ * tot is then void. */
+#ifndef COLI_LEAN_DEPTH
+#define COLI_LEAN_DEPTH 2
+#endif
+
+template <int BITS, int NT, int D>
 __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&tot)[2][4])
 {
-    const int spg = L.nsteps / 4; /* even */
+    constexpr int U = D == 2 ? 2 : 2 * D;
+    const int spg = L.nsteps / 4;
+    float acc[2][4];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            acc[n][v] = 0.0f;
+            tot[n][v] = -0.0f; /* -0 + s == s for every s: tot becomes group 0's sum exactly */
+        }
+    Stage<BITS, false> P[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+        lean_fetch<BITS, NT>(P[k], L, k);
+    bool bad = lean_commit<BITS, NT>(P[0], S, 0);
+    lean_fetch<BITS, NT>(P[0], L, D);
+    __syncthreads();
+    int next = spg; /* first step of the next canonical group */
+#pragma unroll 1
+    for (int st = 0; st < L.nsteps; st += U) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int s = st + i;
+            if (s == next) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        tot[n][v] = tot[n][v] + acc[n][v];
+                        acc[n][v] = 0.0f;
+                    }
+                next += spg;
+            }
+            lean_step<BITS, NT>(S, i & 1, acc);
+            bad |= lean_commit<BITS, NT>(P[(i + 1) % D], S, (i + 1) & 1);
+            lean_fetch<BITS, NT>(P[(i + 1) % D], L, s + 1 + D);
+            __syncthreads();
+        }
+    }
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            tot[n][v] = -0.0f; /* -0 + s == s for every s: tot becomes group 0's sum exactly */
-    Stage<BITS, false> P0, P1;
-    lean_fetch<BITS>(P0, L, 0);
-    lean_fetch<BITS>(P1, L, 1);
-    bool bad = lean_commit<BITS>(P0, S, 0);
-    lean_fetch<BITS>(P0, L, 2);
-    __syncthreads();
-    int st = 0;
-#pragma unroll 1
-    for (int grp = 0; grp < 4; ++grp) {
-        float acc[2][4];
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                acc[n][v] = 0.0f;
-#pragma unroll 1
-        for (int s = 0; s < spg; s += 2, st += 2) {
-            lean_step<BITS, NT>(S, 0, acc);
-            bad |= lean_commit<BITS>(P1, S, 1);
-            lean_fetch<BITS>(P1, L, st + 3);
-            __syncthreads();
-            lean_step<BITS, NT>(S, 1, acc);
-            bad |= lean_commit<BITS>(P0, S, 0);
-            lean_fetch<BITS>(P0, L, st + 4);
-            __syncthreads();
-        }
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                tot[n][v] = tot[n][v] + acc[n][v];
-    }
+            tot[n][v] = tot[n][v] + acc[n][v];
     return __syncthreads_or(bad) != 0;
 }
 
@@ -706,26 +771,15 @@ template <int BITS>
 __device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, int ntiles,
                                                  float (&tot)[2][4])
 {
+    constexpr int D = COLI_LEAN_DEPTH;
+    if (D != 2 && L.nsteps % (2 * D) == 0) {
+        if (ntiles > 1)
+            return k_loop_lean<BITS, 2, D>(S, L, tot);
+        return k_loop_lean<BITS, 1, D>(S, L, tot);
+    }
     if (ntiles > 1)
-        return k_loop_lean<BITS, 2>(S, L, tot);
-    return k_loop_lean<BITS, 1>(S, L, tot);
-}
-
-/* The thread's activation offsets within a step (token row base excluded). */
-template <int BITS>
-__device__ __forceinline__ uint32_t lean_x_in_step()
-{
-    const int l = threadIdx.x;
-    if constexpr (Cfg<BITS>::kStep == 8)
-        return (uint32_t)(l >> 5) * 32u;
-    return (uint32_t)(l >> 6) * 32u + (uint32_t)((l >> 5) & 1) * 16u;
-}
-
-template <int BITS>
-__device__ __forceinline__ uint32_t lean_d_in_step()
-{
-    const int l = threadIdx.x;
-    return (uint32_t)(Cfg<BITS>::kStep == 8 ? (l >> 5) : (l >> 6));
+        return k_loop_lean<BITS, 2, 2>(S, L, tot);
+    return k_loop_lean<BITS, 1, 2>(S, L, tot);
 }
 
 } // namespace
@@ -766,15 +820,34 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     if constexpr (!GROUPED) {
         /* the aligned loop, while every activation offset fits 31 bits */
         if (lean_shape<BITS>(nb) && (int64_t)sg.S * a.H < (int64_t(1) << 31)) {
-            const int wvu = __builtin_amdgcn_readfirstlane(wv);
+            using LC = LCfg<BITS>;
             LeanLane LL;
-            LL.w = (wvu < 2 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + M.rb * 32) * rowbytes;
-            LL.wo = (uint32_t)(rd & 31) * (uint32_t)rowbytes +
-                    (uint32_t)(Cfg<BITS>::kBpt * 4 * BITS) * (uint32_t)(threadIdx.x & 3);
+#pragma unroll
+            for (int i = 0; i < LC::kNL; ++i) {
+                /* rows 0..31 are gate rows, 32..63 the same up rows; a load's rows
+                 * lie on one side within each wave */
+                const int row = i * LC::kRowsPerLoad + (int)threadIdx.x / LC::kCR;
+                const bool up = __builtin_amdgcn_readfirstlane(row) >= 32;
+                LL.wb[i] = (up ? sg.up_w : sg.gate_w) + ((int64_t)e * a.I + M.rb * 32) * rowbytes;
+                LL.wo[i] = (uint32_t)(row & 31) * (uint32_t)rowbytes + 16u * (uint32_t)(threadIdx.x % LC::kCR);
+            }
+            if constexpr (LC::kNL == 1) {
+                LL.wb[1] = LL.wb[0];
+                LL.wo[1] = LL.wo[0];
+            }
             LL.x = a.xq;
-            LL.xo = (uint32_t)tok * (uint32_t)a.H + lean_x_in_step<BITS>();
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = (i < LC::kNXL ? i : 0) * LC::kTokPerLoad + (int)threadIdx.x / LC::kXC;
+                const int tk = token_of_m(sg, pos0 + (tt < ntok ? tt : 0));
+                LL.xo[i] = (uint32_t)tk * (uint32_t)a.H + 16u * (uint32_t)(threadIdx.x % LC::kXC);
+            }
             LL.xd = a.xd;
-            LL.dof = (uint32_t)tok * (uint32_t)nb + lean_d_in_step<BITS>();
+            {
+                const int td = lean_d_token<BITS>();
+                const int tk = token_of_m(sg, pos0 + (td < ntok ? td : 0));
+                LL.dof = (uint32_t)tk * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
+            }
             LL.nsteps = nb / Cfg<BITS>::kStep;
             general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, tot);
         }
@@ -855,15 +928,26 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     if constexpr (!GROUPED) {
         /* the aligned loop, while the weight offsets in one matrix fit 31 bits */
         if (lean_shape<BITS>(nb) && (int64_t)a.H * rowbytes < (int64_t(1) << 31)) {
+            using LC = LCfg<BITS>;
             const int64_t r0 = sg.out_base + pos0;
             LeanLane LL;
-            LL.w = sg.down_w + (int64_t)e * a.H * rowbytes;
-            LL.wo = (uint32_t)(row < a.H ? row : 0) * (uint32_t)rowbytes +
-                    (uint32_t)(Cfg<BITS>::kBpt * 4 * BITS) * (uint32_t)(threadIdx.x & 3);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rw = M.rb * 64 + (i < LC::kNL ? i : 0) * LC::kRowsPerLoad + (int)threadIdx.x / LC::kCR;
+                LL.wb[i] = sg.down_w + (int64_t)e * a.H * rowbytes;
+                LL.wo[i] = (uint32_t)(rw < a.H ? rw : 0) * (uint32_t)rowbytes + 16u * (uint32_t)(threadIdx.x % LC::kCR);
+            }
             LL.x = a.hq + r0 * a.I;
-            LL.xo = (uint32_t)(tl < ntok ? tl : 0) * (uint32_t)a.I + lean_x_in_step<BITS>();
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tt = (i < LC::kNXL ? i : 0) * LC::kTokPerLoad + (int)threadIdx.x / LC::kXC;
+                LL.xo[i] = (uint32_t)(tt < ntok ? tt : 0) * (uint32_t)a.I + 16u * (uint32_t)(threadIdx.x % LC::kXC);
+            }
             LL.xd = a.hd + r0 * nb;
-            LL.dof = (uint32_t)(tl < ntok ? tl : 0) * (uint32_t)nb + lean_d_in_step<BITS>();
+            {
+                const int td = lean_d_token<BITS>();
+                LL.dof = (uint32_t)(td < ntok ? td : 0) * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
+            }
             LL.nsteps = nb / Cfg<BITS>::kStep;
             general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, tot);
         }
