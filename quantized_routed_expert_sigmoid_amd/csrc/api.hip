@@ -267,11 +267,20 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         dd.ids = ids;
         dd.w = w;
         dd.out = out;
+        dd.hs = nullptr;
+        const bool fused = down_combine_decode_fits(dd);
+        /* With the fused down + combine (which writes no y rows), the shared
+         * expert's gate/up runs as one-wave jobs spread over every CU, its
+         * fp32 h in the y region: the routed jobs then give each CU the same
+         * share.  Per-row scales only. */
+        if (fused && shared && a.nseg > 1 && a.seg[1].gu_gb == 0 && I % 8 == 0 && I <= 2048 &&
+            (int64_t)(k + 1) * H >= I)
+            dd.hs = y;
         e = mark(2, e);
         if (e == hipSuccess)
             e = launch_ffn_gate_up_decode(dd, L->gate.qtype, s);
         e = mark(3, e);
-        if (down_combine_decode_fits(dd)) {
+        if (fused) {
             /* down and combine in one launch: the combine stage is empty */
             if (e == hipSuccess)
                 e = launch_ffn_down_combine_decode(dd, L->down.qtype, s);

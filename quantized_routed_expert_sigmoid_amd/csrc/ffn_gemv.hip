@@ -548,11 +548,12 @@ struct PairLoad {
  * so no load sits under a branch and each use waits only for its own loads. */
 template <int BITS, int NI>
 __device__ __forceinline__ void pair_load(PairLoad<BITS, NI>& L, const uint8_t* rows0, int64_t rowbytes,
-                                          int p, int rows_ok, int nb)
+                                          int p, int rows_ok, int nb, const uint8_t* rows8 = nullptr)
 {
     const int lane = threadIdx.x & 63;
     const int row = min(2 * p + (lane >> 5), max(rows_ok, 1) - 1), c = lane & 31;
-    const uint8_t* rp = rows0 + (int64_t)row * rowbytes;
+    /* rows8: where rows 8.. start, when not right after row 7 */
+    const uint8_t* rp = (rows8 && row >= 8) ? rows8 + (int64_t)(row - 8) * rowbytes : rows0 + (int64_t)row * rowbytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         load_block<BITS>(rp + (int64_t)min(c + 32 * i, nb - 1) * (4 * BITS), L.w[i]);
@@ -580,15 +581,16 @@ __device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const
 template <int BITS, int NI>
 __device__ __forceinline__ float dec_k_loop(PairLoad<BITS, NI>& A, const uint8_t* rows0, int64_t rowbytes,
                                             int rows_ok, int nb, const uint32_t (&xa)[NI][8], int32_t* P,
-                                            int sp, const float* dl, const float* ws0, int gb)
+                                            int sp, const float* dl, const float* ws0, int gb,
+                                            const uint8_t* rows8 = nullptr)
 {
     PairLoad<BITS, NI> B;
 #pragma unroll
     for (int p = 0; p < kDecRows / 2; p += 2) {
-        pair_load<BITS, NI>(B, rows0, rowbytes, p + 1, rows_ok, nb);
+        pair_load<BITS, NI>(B, rows0, rowbytes, p + 1, rows_ok, nb, rows8);
         pair_partials<BITS, NI>(A, xa, p, nb, P, sp);
         if (p + 2 < kDecRows / 2) /* resolved at compile time */
-            pair_load<BITS, NI>(A, rows0, rowbytes, p + 2, rows_ok, nb);
+            pair_load<BITS, NI>(A, rows0, rowbytes, p + 2, rows_ok, nb, rows8);
         pair_partials<BITS, NI>(B, xa, p + 1, nb, P, sp);
     }
     wave_lds_sync();
@@ -680,21 +682,51 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int RB = a.I / 32;
-    const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
-    /* the shared expert's jobs come first: they need no selection, so they
-     * stream while the routed jobs select, and they land first on the CUs
-     * that also receive a third job */
-    const int j = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
-    if (j >= nunits)
-        return;
-    const int u = nunits > d.k ? (j == 0 ? d.k : j - 1) : j;
-    const bool routed = u < d.k;
-    const FfnSeg sg = pick(a, routed ? 0 : 1);
     const int nb = a.H / 32, sp = nb | 1, region = dec_region(nb);
     int32_t* P = dec_lds + wv * region;
     float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
     float* rsum = dl + nb;
     int32_t* sel_ids = reinterpret_cast<int32_t*>(rsum + 64); /* read by every wave after the barrier */
+    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
+    const int n_mini = d.hs ? a.I / 8 : 0;
+    if ((int)blockIdx.x < n_mini) {
+        /* one-wave job of the shared expert (first, so that every CU gets
+         * one before any routed job, and it streams during the selection):
+         * gate rows 8m .. 8m+7 as rows 0..7 and the same up rows as rows
+         * 8..15; h of its 8 rows in fp32 */
+        if (wv != 0)
+            return;
+        const FfnSeg sh = pick(a, 1);
+        const int m = blockIdx.x;
+        const uint8_t* g0 = sh.gate_w + (int64_t)8 * m * rowbytes;
+        const uint8_t* u0 = sh.up_w + (int64_t)8 * m * rowbytes;
+        PairLoad<BITS, NI> A;
+        pair_load<BITS, NI>(A, g0, rowbytes, 0, kDecRows, nb, u0);
+        uint32_t xa[NI][8];
+        dec_act_load<NI>(a.xq, nb, xa);
+        float dpre[kDlPre];
+        dec_scale_load(a.xd, nb, dpre);
+        const int r = lane & 15;
+        const float sc = (r < 8 ? sh.gate_s : sh.up_s)[8 * m + (r & 7)];
+        dec_act_prep<BITS, NI>(xa, dpre, a.xd, nb, dl);
+        const float v16 = dec_k_loop<BITS, NI>(A, g0, rowbytes, kDecRows, nb, xa, P, sp, dl, nullptr, 0, u0);
+        const float v = sc * v16;
+        const float up = __shfl(v, (lane & 7) + 8, kWave);
+        if (lane < 8)
+            d.hs[8 * m + lane] = canon_silu(v) * up;
+        return;
+    }
+    const int nunits = d.k + (a.nseg > 1 && !d.hs ? 1 : 0);
+    /* the shared expert's jobs come first: they need no selection, so they
+     * stream while the routed jobs select, and they land first on the CUs
+     * that also receive a third job */
+    const int jb = blockIdx.x - n_mini;
+    const int j = jb / RB, rb = jb - (jb / RB) * RB;
+    if (j >= nunits)
+        return;
+    const int u = nunits > d.k ? (j == 0 ? d.k : j - 1) : j;
+    const bool routed = u < d.k;
+    const FfnSeg sg = pick(a, routed ? 0 : 1);
     uint32_t xa[NI][8];
     dec_act_load<NI>(a.xq, nb, xa);
     float dpre[kDlPre];
@@ -721,7 +753,6 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
             return;
         e = min(sel, sg.n_mat - 1);
     }
-    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
     /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
     const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) +
                            ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * rowbytes;
@@ -1200,16 +1231,28 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, 0), __builtin_amdgcn_readlane(e_l, 0), row0,
                                        rowbytes),
                             rowbytes, 0, 2, nb);
+    /* the shared expert's h in fp32 (one-wave gate/up jobs; 4 nb <= 256):
+     * thread 4b + q loads elements 8q .. 8q+7 of block b now, and forms the
+     * Q8_0 blocks after the routed items' loads are issued */
+    const bool sh_fp32 = shared && d.hs;
+    const int sb = threadIdx.x >> 2, sq = threadIdx.x & 3;
+    float4 hv0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), hv1 = hv0;
+    if (sh_fp32) {
+        const float4* src = reinterpret_cast<const float4*>(d.hs + (int64_t)min(sb, nb - 1) * 32 + 8 * sq);
+        hv0 = src[0];
+        hv1 = src[1];
+    }
+    const int n_items = (sh_fp32 ? U - 1 : U) * nb;
     /* each thread issues the loads of up to kDcStage (unit, block) items
      * before it converts and stores any: one memory round trip, not one per
      * item */
-    for (int i0 = threadIdx.x; i0 < U * nb; i0 += 64 * kGroups * kDcStage) {
+    for (int i0 = threadIdx.x; i0 < n_items; i0 += 64 * kGroups * kDcStage) {
         uint32_t x[kDcStage][8];
         float dv[kDcStage];
 #pragma unroll
         for (int r = 0; r < kDcStage; ++r) {
             const int i = i0 + r * 64 * kGroups;
-            if (i < U * nb) {
+            if (i < n_items) {
                 const int j = i / nb, b = i - j * nb;
                 const int u = dc_unit(kept, n_kept, d.k, j, all_kept);
                 load_codes(a.hq + (int64_t)u * a.I + (int64_t)b * 32, x[r]);
@@ -1219,7 +1262,7 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
 #pragma unroll
         for (int r = 0; r < kDcStage; ++r) {
             const int i = i0 + r * 64 * kGroups;
-            if (i < U * nb) {
+            if (i < n_items) {
                 uint32_t xa[8];
                 prep_dot<BITS>(x[r], xa);
                 uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
@@ -1227,6 +1270,41 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
                 dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
                 dls[(i / nb) * sp + i % nb] = dv[r];
             }
+        }
+    }
+    if (sh_fp32) {
+        /* the arithmetic of the gate/up epilogue: amax over the block, d =
+         * amax / 127, codes q8_code(h, 1 / d) */
+        const float h[8] = {hv0.x, hv0.y, hv0.z, hv0.w, hv1.x, hv1.y, hv1.z, hv1.w};
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            am = fmaxf(am, __builtin_fabsf(h[i]));
+        am = fmaxf(am, shfl_xor(am, 1));
+        am = fmaxf(am, shfl_xor(am, 2));
+        const float dsc = am / 127.0f;
+        const float inv = (am == 0.0f) ? 0.0f : 1.0f / dsc;
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w0 |= (uint32_t)(q8_code(h[k], inv) & 0xFF) << (8 * k);
+            w1 |= (uint32_t)(q8_code(h[4 + k], inv) & 0xFF) << (8 * k);
+        }
+        /* the block's 8 code words, from its 4 threads */
+        uint32_t x[8];
+        const int base = lane & ~3;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[2 * q] = (uint32_t)__shfl((int)w0, base + q, kWave);
+            x[2 * q + 1] = (uint32_t)__shfl((int)w1, base + q, kWave);
+        }
+        if (sq == 0 && sb < nb) {
+            uint32_t xa[8];
+            prep_dot<BITS>(x, xa);
+            uint4* dst = reinterpret_cast<uint4*>(xal + ((int64_t)(U - 1) * nb + sb) * 8);
+            dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+            dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+            dls[(U - 1) * sp + sb] = dsc;
         }
     }
     const int u_r = __shfl(u_l, min(lane >> 1, U - 1), kWave);
@@ -1443,7 +1521,8 @@ static void down_decode_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t 
 
 hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
 {
-    const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 ? 1 : 0)) * (d.f.I / 32);
+    /* one-wave jobs of the shared expert (d.hs), then whole jobs */
+    const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 && !d.hs ? 1 : 0)) * (d.f.I / 32) + (d.hs ? d.f.I / 8 : 0);
     const int nb = d.f.H / 32;
     const dim3 grid((uint32_t)jobs);
     const size_t lds = dec_lds_bytes(nb);

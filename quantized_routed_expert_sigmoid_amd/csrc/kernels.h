@@ -115,6 +115,12 @@ struct DecodeArgs {
     int32_t* ids;        /* [k] selected experts, slot order (-1: dropped) */
     float* w;            /* [k] routing weights */
     float* out;          /* [H] layer output (down + combine launch) */
+    /* nullptr: the shared expert's gate/up runs as whole jobs into hq / hd.
+     * Otherwise its gate/up runs as I / 8 one-wave jobs of 8 gate and 8 up
+     * rows that write h (fp32, [I]) here, and the fused down + combine
+     * quantises it while staging (per-row scales, I <= 2048 and the fused
+     * launch only). */
+    float* hs;
 };
 
 /* Bounds on the unit counts of a routed group with P pairs of S tokens over
