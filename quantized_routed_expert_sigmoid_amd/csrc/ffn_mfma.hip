@@ -579,7 +579,6 @@ __device__ __forceinline__ void prep_half(const uint32_t* x, uint32_t (&xa)[4])
 template <int BITS, int NT>
 __device__ __forceinline__ bool lean_commit(const Stage<BITS, false>& P, LeanLds<BITS>& S, int buf)
 {
-    using C = Cfg<BITS>;
     constexpr int SHIFT = 8 - BITS;
     using LC = LCfg<BITS>;
     const int l = threadIdx.x;
