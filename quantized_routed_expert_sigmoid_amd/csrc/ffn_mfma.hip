@@ -707,19 +707,16 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
     }
 }
 
-/* D steps of loads in registers (stage k holds the steps = k mod D), one
- * in LDS, one barrier per step; the loop body covers U steps so that stage
- * and LDS buffer indices are compile-time.  Returns true (uniformly) when
- * some step's scales were not exact with the 2^-(8-b) factor taken out;
- * tot is then void. */
-#ifndef COLI_LEAN_DEPTH
-#define COLI_LEAN_DEPTH 2
-#endif
-
-template <int BITS, int NT, int D>
+/* Two steps of loads in registers (stage k holds the steps = k mod 2), one
+ * in LDS, one barrier per step; the loop body covers two steps so that
+ * stage and LDS buffer indices are compile-time.  (Three or four steps in
+ * registers lowered the occupancy and were slower.)  Returns true
+ * (uniformly) when some step's scales were not exact with the 2^-(8-b)
+ * factor taken out; tot is then void. */
+template <int BITS, int NT>
 __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&tot)[2][4])
 {
-    constexpr int U = D == 2 ? 2 : 2 * D;
+    constexpr int D = 2, U = 2;
     const int spg = L.nsteps / 4;
     float acc[2][4];
 #pragma unroll
@@ -770,15 +767,9 @@ template <int BITS>
 __device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, int ntiles,
                                                  float (&tot)[2][4])
 {
-    constexpr int D = COLI_LEAN_DEPTH;
-    if (D != 2 && L.nsteps % (2 * D) == 0) {
-        if (ntiles > 1)
-            return k_loop_lean<BITS, 2, D>(S, L, tot);
-        return k_loop_lean<BITS, 1, D>(S, L, tot);
-    }
     if (ntiles > 1)
-        return k_loop_lean<BITS, 2, 2>(S, L, tot);
-    return k_loop_lean<BITS, 1, 2>(S, L, tot);
+        return k_loop_lean<BITS, 2>(S, L, tot);
+    return k_loop_lean<BITS, 1>(S, L, tot);
 }
 
 } // namespace
