@@ -351,3 +351,22 @@ def test_layer_repeatable_bitwise(qre, case):
     a = qre.moe_layer_forward(dev, x).cpu()
     b = qre.moe_layer_forward(dev, x).cpu()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", ["decode_int4", "decode_int2_ragged", "decode_int4_k2080", "decode_int8_noshared"])
+def test_decode_path_matches_small_batch_bitwise(qre, case):
+    """One token through the fused decode launches (selection inside gate/up,
+    the shared expert as one-wave jobs, combine inside down) gives the same
+    bits as that token twice in a two-token batch (the small-batch kernels):
+    one canonical fold and one Q8_0 of h on every path."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], **SMALL_LAYERS[case])
+    L = synth.make_layer(w)
+    x, _ = gapped_activations(w, L.router_w, L.bias)
+    say(f"decode vs two-token batch case={case}")
+    dev = to_device(L)
+    x1 = x[:1].contiguous()
+    x2 = torch.cat([x1, x1]).contiguous()
+    out1 = qre.moe_layer_forward(dev, x1.cuda()).cpu()
+    out2 = qre.moe_layer_forward(dev, x2.cuda()).cpu()
+    assert torch.equal(out1[0], out2[0]) and torch.equal(out1[0], out2[1]), \
+        f"max diff {(out1[0] - out2[0]).abs().max().item()}"
