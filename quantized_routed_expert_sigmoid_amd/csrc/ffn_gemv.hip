@@ -1135,19 +1135,20 @@ __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
  * the y round trip or the extra launch.  (8 rows per workgroup give H / 8 =
  * 768 workgroups at H = 6144: three per CU.) */
 
-constexpr int kDcRows = 8; /* output rows per workgroup; wave w owns rows 2w, 2w+1 */
+/* A workgroup of DW waves owns 2 DW output rows (wave w: rows 2w, 2w+1).
+ * kDcWide waves (one workgroup per CU at H = 6144) stage every unit's h once
+ * per CU; the vector L1, whose lines bound this kernel, then spends a
+ * twelfth as many lines on h as with three 4-wave workgroups per CU. */
+constexpr int kDcWide = 12;
 
 /* LDS words: h codes [U][nb][8], h scales [U][nb | 1], per wave the partials
  * [2U][nb | 1] and the row values [2U]. */
-__host__ __device__ inline size_t dc_lds_words(int U, int nb)
+__host__ __device__ inline size_t dc_lds_words(int U, int nb, int DW)
 {
-    return (size_t)U * nb * 8 + (size_t)U * (nb | 1) + (size_t)kGroups * 2 * U * ((nb | 1) + 1);
+    return (size_t)U * nb * 8 + (size_t)U * (nb | 1) + (size_t)DW * 2 * U * ((nb | 1) + 1);
 }
 
-inline bool dc_fits(int U, int nb)
-{
-    return dc_lds_words(U, nb) * 4 <= 64 * 1024;
-}
+constexpr size_t kDcLdsMax = 160 * 1024; /* LDS of one CU (gfx950) */
 
 /* First of this wave's two rows of the down matrix of unit u (u = slot, or
  * k for the shared expert) whose matrix index is e. */
@@ -1185,8 +1186,8 @@ __device__ __forceinline__ int dc_unit(uint64_t kept, int n_kept, int k, int n, 
     return __builtin_ctzll(kept);
 }
 
-template <int BITS, int NI>
-__global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
+template <int BITS, int NI, int DW>
+__global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
 {
     extern __shared__ int32_t dc_lds[];
     const FfnArgs& a = d.f;
@@ -1203,10 +1204,10 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     /* the block scales' rows have the odd stride sp, like the partials', so
      * that the fold's reads (32 distinct addresses) spread over the banks */
     float* dls = reinterpret_cast<float*>(xal + U * nb * 8);    /* [U][sp] */
-    int32_t* P0 = reinterpret_cast<int32_t*>(dls + U * sp);      /* [kGroups][2U][sp] */
+    int32_t* P0 = reinterpret_cast<int32_t*>(dls + U * sp);      /* [DW][2U][sp] */
     int32_t* P = P0 + wv * (2 * U * sp);
-    float* ys = reinterpret_cast<float*>(P0 + kGroups * 2 * U * sp) + wv * 2 * U;
-    const int row0 = blockIdx.x * kDcRows + 2 * wv;
+    float* ys = reinterpret_cast<float*>(P0 + DW * 2 * U * sp) + wv * 2 * U;
+    const int row0 = blockIdx.x * (2 * DW) + 2 * wv;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
 
     if (U == 0)
@@ -1246,12 +1247,12 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
     /* each thread issues the loads of up to kDcStage (unit, block) items
      * before it converts and stores any: one memory round trip, not one per
      * item */
-    for (int i0 = threadIdx.x; i0 < n_items; i0 += 64 * kGroups * kDcStage) {
+    for (int i0 = threadIdx.x; i0 < n_items; i0 += 64 * DW * kDcStage) {
         uint32_t x[kDcStage][8];
         float dv[kDcStage];
 #pragma unroll
         for (int r = 0; r < kDcStage; ++r) {
-            const int i = i0 + r * 64 * kGroups;
+            const int i = i0 + r * 64 * DW;
             if (i < n_items) {
                 const int j = i / nb, b = i - j * nb;
                 const int u = dc_unit(kept, n_kept, d.k, j, all_kept);
@@ -1261,7 +1262,7 @@ __global__ __launch_bounds__(256) void ffn_down_combine_decode(DecodeArgs d)
         }
 #pragma unroll
         for (int r = 0; r < kDcStage; ++r) {
-            const int i = i0 + r * 64 * kGroups;
+            const int i = i0 + r * 64 * DW;
             if (i < n_items) {
                 uint32_t xa[8];
                 prep_dot<BITS>(x[r], xa);
@@ -1552,36 +1553,71 @@ hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t
     return hipGetLastError();
 }
 
-template <int NI>
+template <int BITS, int NI, int DW>
+static void down_combine_launch(const DecodeArgs& d, dim3 grid, size_t lds, hipStream_t st)
+{
+    if (lds > 64 * 1024) {
+        static bool raised = false; /* once per instantiation */
+        if (!raised) {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_down_combine_decode<BITS, NI, DW>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDcLdsMax);
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL((ffn_down_combine_decode<BITS, NI, DW>), grid, dim3(64 * DW), lds, st, d);
+}
+
+template <int NI, int DW>
 static void down_combine_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, hipStream_t st)
 {
-    const dim3 block(64 * kGroups);
     switch (bits) {
-    case 8: hipLaunchKernelGGL((ffn_down_combine_decode<8, NI>), grid, block, lds, st, d); break;
-    case 4: hipLaunchKernelGGL((ffn_down_combine_decode<4, NI>), grid, block, lds, st, d); break;
-    default: hipLaunchKernelGGL((ffn_down_combine_decode<2, NI>), grid, block, lds, st, d); break;
+    case 8: down_combine_launch<8, NI, DW>(d, grid, lds, st); break;
+    case 4: down_combine_launch<4, NI, DW>(d, grid, lds, st); break;
+    default: down_combine_launch<2, NI, DW>(d, grid, lds, st); break;
     }
+}
+
+/* Waves per workgroup of the fused down + combine: kDcWide when the rows
+ * divide evenly and its LDS fits a CU, else 4. */
+static int dc_waves(const DecodeArgs& d)
+{
+    const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
+    const int nb = d.f.I / 32;
+    if (d.f.H % (2 * kDcWide) == 0 && dc_lds_words(U, nb, kDcWide) * 4 <= kDcLdsMax)
+        return kDcWide;
+    return kGroups;
 }
 
 bool down_combine_decode_fits(const DecodeArgs& d)
 {
     const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
     /* per-unit values live in lanes: 2U row scales per wave */
-    return U <= 32 && d.f.H % kDcRows == 0 && dc_fits(U, d.f.I / 32);
+    return U <= 32 && d.f.H % (2 * kGroups) == 0 && dc_lds_words(U, d.f.I / 32, kGroups) * 4 <= 64 * 1024;
 }
 
 hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
 {
     const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
     const int nb = d.f.I / 32;
-    const dim3 grid((uint32_t)(d.f.H / kDcRows));
-    const size_t lds = dc_lds_words(U, nb) * 4;
-    switch (dec_ni(nb)) {
-    case 1: down_combine_ni<1>(d, bits, grid, lds, st); break;
-    case 2: down_combine_ni<2>(d, bits, grid, lds, st); break;
-    case 4: down_combine_ni<4>(d, bits, grid, lds, st); break;
-    case 6: down_combine_ni<6>(d, bits, grid, lds, st); break;
-    default: down_combine_ni<8>(d, bits, grid, lds, st); break;
+    const int DW = dc_waves(d);
+    const dim3 grid((uint32_t)(d.f.H / (2 * DW)));
+    const size_t lds = dc_lds_words(U, nb, DW) * 4;
+    if (DW == kDcWide) {
+        switch (dec_ni(nb)) {
+        case 1: down_combine_ni<1, kDcWide>(d, bits, grid, lds, st); break;
+        case 2: down_combine_ni<2, kDcWide>(d, bits, grid, lds, st); break;
+        case 4: down_combine_ni<4, kDcWide>(d, bits, grid, lds, st); break;
+        case 6: down_combine_ni<6, kDcWide>(d, bits, grid, lds, st); break;
+        default: down_combine_ni<8, kDcWide>(d, bits, grid, lds, st); break;
+        }
+    } else {
+        switch (dec_ni(nb)) {
+        case 1: down_combine_ni<1, kGroups>(d, bits, grid, lds, st); break;
+        case 2: down_combine_ni<2, kGroups>(d, bits, grid, lds, st); break;
+        case 4: down_combine_ni<4, kGroups>(d, bits, grid, lds, st); break;
+        case 6: down_combine_ni<6, kGroups>(d, bits, grid, lds, st); break;
+        default: down_combine_ni<8, kGroups>(d, bits, grid, lds, st); break;
+        }
     }
     return hipGetLastError();
 }

@@ -267,6 +267,9 @@ SMALL_LAYERS = {
     "decode_int4": dict(name="dec4", layer="dec4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
                         S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
     "decode_int8_noshared": dict(name="dec8", layer="dec8", bits=8, n_experts=32, top_k=4, S=1),
+    # H a multiple of 24: the 12-wave down + combine (each CU stages h once)
+    "decode_int4_h768": dict(name="dec4w", layer="dec4w", bits=4, hidden=768, inter=256, n_experts=64, top_k=6,
+                             S=1, has_shared=True, rsf=2.5, var_router=1.0 / 768, var_bias=1e-4),
     "decode_int2_ragged": dict(name="dec2", layer="dec2", bits=2, hidden=352, inter=96, n_experts=16,
                                top_k=3, S=1, has_shared=True, var_router=1.0 / 352),
     "decode_int4_k2080": dict(name="dec4b", layer="dec4b", bits=4, hidden=2080, inter=160, n_experts=16,
@@ -353,7 +356,8 @@ def test_layer_repeatable_bitwise(qre, case):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("case", ["decode_int4", "decode_int2_ragged", "decode_int4_k2080", "decode_int8_noshared"])
+@pytest.mark.parametrize("case", ["decode_int4", "decode_int2_ragged", "decode_int4_k2080", "decode_int8_noshared",
+                                  "decode_int4_h768"])
 def test_decode_path_matches_small_batch_bitwise(qre, case):
     """One token through the fused decode launches (selection inside gate/up,
     the shared expert as one-wave jobs, combine inside down) gives the same
