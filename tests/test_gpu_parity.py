@@ -99,12 +99,21 @@ def test_dispatch_skips_dropped_slots_bit_exact(qre):
     assert n == ref["n_active"] and np.array_equal(act.cpu().numpy()[:n], ref["active"])
 
 
-@pytest.mark.parametrize("case", ["tiny", "wide_k", "ragged_tiles", "decode_router", "glm_router_s70"])
+@pytest.mark.parametrize("case", ["tiny", "odd_experts", "decode_router_s1", "decode_router_s8", "wide_k",
+                                  "ragged_tiles", "decode_router", "glm_router_s70"])
 def test_route_parity(qre, case):
-    """Small batches take the one-workgroup-per-expert router; larger ones the
-    matrix-core router with K slices (ragged 64 x 64 tiles included)."""
+    """Small batches (full-size router rows at 1 and 8 tokens included) take
+    the one-workgroup-per-expert router; larger ones the matrix-core router
+    with K slices (ragged 64 x 64 tiles included)."""
     if case == "tiny":
         w, L = _small_layer("tiny_r")
+    elif case == "odd_experts":
+        # 20 experts, rows of 328 float4 (not a multiple of 256 threads)
+        w, L = _small_layer("odd_e", layer="odd_e", hidden=1312, n_experts=20, top_k=4, S=5, rsf=2.5)
+    elif case in ("decode_router_s1", "decode_router_s8"):
+        base = synth.WORKLOADS["decode"]
+        w = synth.scaled(base, name=f"router_{case[-2:]}", S=int(case[-1]))
+        L = synth.Layer(w, synth.router_weights(w), synth.router_bias(w), None, None, None, None, None, None)
     elif case == "wide_k":
         w, L = _small_layer("wide_k", layer="wide_k", n_experts=64, top_k=6, S=37, rsf=2.5)
     elif case == "ragged_tiles":
@@ -289,6 +298,12 @@ SMALL_LAYERS = {
                            n_group=4, topk_group=2, top_p=0.8),
     "rv_mfma": dict(name="rvf", layer="rvf", bits=4, hidden=512, inter=256, n_experts=16, top_k=4, S=80,
                     has_shared=True, rsf=2.5, var_router=1.0 / 512, n_group=4, topk_group=2, top_p=0.75),
+    # 20 experts and a hidden size (1312) that is not a multiple of 24: the
+    # fused down + combine takes its 4-wave workgroups
+    "decode_h1312_e20": dict(name="drr", layer="drr", bits=4, hidden=1312, inter=256, n_experts=20, top_k=4,
+                             S=1, has_shared=True, rsf=2.5),
+    "small_h1312_e20": dict(name="srr", layer="drr", bits=4, hidden=1312, inter=256, n_experts=20, top_k=4,
+                            S=5, has_shared=True, rsf=2.5),
     # group-wise weight scales on every path
     "grp_decode_int4": dict(name="gd4", layer="gd4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
                             S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, group=128),
@@ -357,7 +372,7 @@ def test_layer_repeatable_bitwise(qre, case):
 
 
 @pytest.mark.parametrize("case", ["decode_int4", "decode_int2_ragged", "decode_int4_k2080", "decode_int8_noshared",
-                                  "decode_int4_h768"])
+                                  "decode_int4_h768", "decode_h1312_e20"])
 def test_decode_path_matches_small_batch_bitwise(qre, case):
     """One token through the fused decode launches (selection inside gate/up,
     the shared expert as one-wave jobs, combine inside down) gives the same
