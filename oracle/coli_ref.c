@@ -111,25 +111,15 @@ int32_t ref_block_partial(const uint8_t* row, int32_t bits, const int8_t* q, int
 float ref_qdot(const uint8_t* row, int32_t bits, float row_scale,
                const int8_t* q, const float* d, int32_t K)
 {
-    /* The pages do not fix the order of the fp32 accumulation.  The blocks
-     * are folded in four consecutive groups (group g holds blocks
-     * floor(g*nb/4) .. floor((g+1)*nb/4)-1), each from +0 in ascending block
-     * order, and the group sums are added left to right. */
-    int32_t nb = K / 32;
-    float group[4];
-    for (int32_t g = 0; g < 4; ++g) {
-        float acc = 0.0f;
-        for (int32_t b = (g * nb) / 4; b < ((g + 1) * nb) / 4; ++b) {
-            int32_t part = ref_block_partial(row, bits, q, b);
-            acc = fmaf(d[b], (float)part, acc);
-        }
-        group[g] = acc;
+    /* The pages do not fix the order of the fp32 accumulation; the plain
+     * reading is the sum written out: one fused multiply-add per block, in
+     * ascending block order, starting from +0, then the row scale. */
+    float acc = 0.0f;
+    for (int32_t b = 0; b < K / 32; ++b) {
+        int32_t part = ref_block_partial(row, bits, q, b);
+        acc = fmaf(d[b], (float)part, acc);
     }
-    float sum = group[0];
-    sum = sum + group[1];
-    sum = sum + group[2];
-    sum = sum + group[3];
-    return row_scale * sum;
+    return row_scale * acc;
 }
 
 float ref_qdot_grouped(const uint8_t* row, int32_t bits, const float* s, int32_t group,
@@ -140,22 +130,13 @@ float ref_qdot_grouped(const uint8_t* row, int32_t bits, const float* s, int32_t
      * name group-wise scaling without fixing its layout or where the scale
      * enters; this reading puts it where the activation block scale already
      * enters, so that a group of 32 columns is exactly a Q8_0 block. */
-    int32_t nb = K / 32;
-    float group_sum[4];
-    for (int32_t g = 0; g < 4; ++g) {
-        float acc = 0.0f;
-        for (int32_t b = (g * nb) / 4; b < ((g + 1) * nb) / 4; ++b) {
-            int32_t part = ref_block_partial(row, bits, q, b);
-            float t = s[(b * 32) / group] * d[b];
-            acc = fmaf(t, (float)part, acc);
-        }
-        group_sum[g] = acc;
+    float acc = 0.0f;
+    for (int32_t b = 0; b < K / 32; ++b) {
+        int32_t part = ref_block_partial(row, bits, q, b);
+        float t = s[(b * 32) / group] * d[b];
+        acc = fmaf(t, (float)part, acc);
     }
-    float sum = group_sum[0];
-    sum = sum + group_sum[1];
-    sum = sum + group_sum[2];
-    sum = sum + group_sum[3];
-    return sum;
+    return acc;
 }
 
 double ref_qdot_grouped_f64(const uint8_t* row, int32_t bits, const float* s, int32_t group,

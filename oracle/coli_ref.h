@@ -106,10 +106,8 @@ void ref_pack_row(const int8_t* codes, int32_t K, int32_t bits, uint8_t* out);
 /* Exact int32 partial of block b: sum over 32 elements of weight * code. */
 int32_t ref_block_partial(const uint8_t* row, int32_t bits, const int8_t* q, int32_t b);
 /* Canonical quantised row dot: the nb = K/32 block partials are folded in
- * four consecutive groups (group g: blocks floor(g*nb/4) .. floor((g+1)*nb/4)-1),
- * each acc = fmaf(d_b, (float)S_b, acc) from +0 in ascending block order; the
- * four group sums are added left to right; then one multiply by the row
- * scale. */
+ * one chain, acc = fmaf(d_b, (float)S_b, acc) from acc = +0 for b = 0, 1,
+ * ..., nb-1 in ascending order; then one multiply by the row scale. */
 float ref_qdot(const uint8_t* row, int32_t bits, float row_scale,
                const int8_t* q, const float* d, int32_t K);
 /* The same quantity, unblocked, in fp64 (used to bound the fp32 fold). */
@@ -119,8 +117,8 @@ double ref_qdot_f64(const uint8_t* row, int32_t bits, float row_scale,
  * s[c / group] times its code, so block b contributes
  * s[32b / group] * d_b * S_b.  Canonical form: the coefficient
  * t_b = s[32b / group] * d_b is one fp32 multiply, and t_b takes the place of
- * d_b in the fold of ref_qdot (same four groups, same order); there is no
- * row scale. */
+ * d_b in the fold of ref_qdot (the same ascending chain); there is no row
+ * scale. */
 float ref_qdot_grouped(const uint8_t* row, int32_t bits, const float* s, int32_t group,
                        const int8_t* q, const float* d, int32_t K);
 /* The same quantity, unblocked, in fp64. */

@@ -2,7 +2,9 @@
 the pages' stated layouts and invariants, closed forms, brute force on tiny
 inputs, error bounds and special cases.  CPU only."""
 
+import json
 import math
+import pathlib
 from fractions import Fraction
 
 import numpy as np
@@ -14,6 +16,7 @@ import synth
 from tests import hand_example
 
 RNG = np.random.default_rng(12345)
+GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
 U = 2.0 ** -24  # fp32 unit roundoff
 
 
@@ -174,6 +177,42 @@ def test_fold_exact_on_integers():
     assert oracle.qdot(row, 8, 1.0, q, d2) == oracle.qdot(row, 8, 1.0, q, d) + p3
     # the row scale multiplies the folded sum
     assert oracle.qdot(row, 8, 0.5, q, d) == 0.5 * oracle.qdot(row, 8, 1.0, q, d)
+
+
+def _fold_fixture_case(case, bits):
+    """Row, codes and block scales of a tests/golden/fold_order.json case."""
+    w_cols, q_cols = [], []
+    for blk in case["blocks"]:
+        w_cols += [blk["w"]] * 32
+        c = blk["codes"]
+        q_cols += [int(c.split()[1])] * 32 if isinstance(c, str) else list(c)
+    codes = np.array(w_cols, np.int8)
+    q = np.array(q_cols, np.int8)
+    d = np.array([blk["d"] for blk in case["blocks"]], np.float32)
+    # the fixture's scales are fp32 numbers as written
+    assert [float(v) for v in d] == [blk["d"] for blk in case["blocks"]]
+    return oracle.pack_row(codes, bits), q, d
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_fold_order_hand_worked(bits):
+    """The fold is one ascending chain of fused multiply-adds from +0: two
+    hand-worked rows (tests/golden/fold_order.json) whose exact results
+    differ from a fold in four block groups, from a descending chain and
+    from rounding each product before the add."""
+    fx = json.loads((GOLDEN / "fold_order.json").read_text())
+    for case in fx["cases"]:
+        row, q, d = _fold_fixture_case(case, bits)
+        assert len(q) == case["K"]
+        parts = [oracle.block_partial(row, bits, q, b) for b in range(case["K"] // 32)]
+        assert parts == case["partials"]
+        got = oracle.qdot(row, bits, case["row_scale"], q, d)
+        assert got == case["expected"], (case["name"], got)
+        assert case["expected"] != case["expected_if_grouped_in_fours"]
+        gs = case["group_scales"]
+        s = np.array(gs["scales"], np.float32)
+        got_g = oracle.qdot_grouped(row, bits, s, gs["group"], q, d)
+        assert got_g == gs["expected"], (case["name"], got_g)
 
 
 # ---------------------------------------------------------------------------
