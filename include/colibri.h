@@ -198,12 +198,11 @@ int colibri_moe_dispatch(const int32_t* topk_ids, int32_t S, int32_t k, int32_t 
  *   u[r] likewise with up;  h[r] = silu(g[r]) * u[r];  h -> Q8_0 (hq, hd)
  *   y[i][n] = down.row_scale[e][n] * F(down row (e, n), hq, hd)       (n < H)
  * where F folds the exact int32 block partials S_b = sum over 32 elements of
- * weight code * activation code: the nb = K/32 blocks form four consecutive
- * groups (group g: blocks floor(g*nb/4) .. floor((g+1)*nb/4)-1), each folded
- * acc = fmaf(d_b, (float)S_b, acc) in ascending block order from +0, and the
- * four group sums are added left to right (the pages leave the order of the
- * fp32 accumulation open; this one is fixed so that results are bit-exact
- * across batch sizes and kernels).  With group-wise scales s (bank group > 0)
+ * weight code * activation code in one chain, acc = fmaf(d_b, (float)S_b,
+ * acc) from +0 for b = 0 .. K/32 - 1 in ascending order (the pages leave the
+ * order of the fp32 accumulation open; the sum as written is taken, and it
+ * is the same in every kernel, so results are bit-exact across batch sizes
+ * and kernels).  With group-wise scales s (bank group > 0)
  * block b's coefficient is the fp32 product s[32b/group] * d_b in place of
  * d_b, and the row-scale factor is absent.  silu(g) = g / (1 + exp(-g)) with exp by Cody-Waite
  * reduction and a degree-7 Taylor polynomial (+inf above 88, +0 below -87).

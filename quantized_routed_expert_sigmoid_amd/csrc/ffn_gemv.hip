@@ -1,5 +1,7 @@
 /*
- * ffn_gemv.hip -- gated expert FFN on the integer dot path, GEMV form.
+ * ffn_gemv.hip -- gated expert FFN on the integer dot path, GEMV form, for
+ * experts that hold few tokens of a batch (one-token decode, small verify
+ * batches, the small experts of a prefill).
  *
  * ("Show HN: 如何在我的低配置电脑上运行 GLM-5.2": implemented-features section,
  * integer dot-product item -- Q8_0-style int8 activations -- and quantised-
@@ -7,22 +9,33 @@
  * dequantised on use; Metal section: the routed-expert work is a SwiGLU;
  * resource-policy section: gate and up share one dispatch.)
  *
- * One wavefront is one job: an expert, up to kUnitTokens of its tokens, and
- * 64 weight rows (gate/up kernel: 32 gate rows and the same 32 up rows, i.e.
- * exactly one 32-block of the intermediate h; down kernel: 64 output rows).
+ * A job is one expert, up to kUnitTokens of its tokens and 64 weight rows
+ * (gate/up: 32 gate rows and the same 32 up rows, i.e. exactly one 32-block
+ * of h; down: 64 output rows), run by a workgroup of four waves; wave w owns
+ * 16 whole rows.
  *
- * Lane mapping.  The wave is eight octets of eight lanes; octet o owns rows
- * 8o .. 8o+7 of the job.  For a K step of eight blocks, lane j of an octet
- * loads block (step*8 + j) of each of its octet's eight rows, so each load
- * instruction reads one contiguous run of eight blocks per row (128 bytes at
- * int4).  The exact int32 block partials go through LDS with a skewed 8x8
- * transpose per octet (conflict-free on 64 banks for both the writes and the
- * reads) so that lane j then owns row 8o + j and folds that row's eight
- * partials in ascending block order: acc = fma(d_b, (float)S_b, acc).
+ * Loads.  A wave reads its 16 rows in items of two rows by 32 blocks: lane l
+ * of item (chunk i, pair p) loads block 32 i + (l mod 32) of row 2p + l/32,
+ * so each half wave reads 32 consecutive blocks of one row (512 bytes at
+ * int4: whole cache lines).  Items run chunk by chunk -- the eight pairs of
+ * chunk 0, then those of chunk 1, ... -- with 2 NI items in flight (NI: the
+ * chunks of a row).  Reading whole row spans per instruction streams
+ * markedly faster than splitting K across the waves of a job (measured 6.5
+ * against 5.5 TB/s on 113 MB).
  *
- * Epilogue of the gate/up kernel: g = row scale * acc on lanes 0..31, u on
- * lanes 32..63, h = silu(g) * u, one Q8_0 block of h per token (amax over 32
- * lanes), codes and scale stored for the down kernel.
+ * Fold.  Each exact int32 block partial goes to LDS as an fp32 number (exact:
+ * |S_b| < 2^20).  After the eight items of a chunk, lane (row, token)
+ * continues its row's chain acc = fma(d_b, (float)S_b, acc) over the chunk's
+ * 32 blocks in ascending order -- the canonical fold: one chain from +0 over
+ * all blocks of the row -- while the next chunk's items load; the row scale
+ * multiplies at the end.  Blocks past the row's end hold partial 0 and scale
+ * 0, and fma(0, 0, acc) == acc for every value such a chain can hold (it
+ * starts at +0 and cannot reach -0), so a ragged last chunk needs no branch.
+ *
+ * Epilogue of the gate/up kernels: g = row scale * acc (lanes of the 32
+ * gate rows), u (the same up rows), h = silu(g) * u, one Q8_0 block of h
+ * per token (amax over 32 lanes), codes and scale stored for the down
+ * kernels.
  */
 #include "device_common.h"
 #include "kernels.h"
@@ -33,6 +46,10 @@ namespace coli {
 namespace {
 
 constexpr int kRowsPerJob = 64;
+constexpr int kJobWaves = 4;  /* waves of a GEMV workgroup */
+constexpr int kWaveRows = 16; /* rows of a job per wave */
+constexpr int kChunk = 32;    /* blocks of a row per load item */
+constexpr int kTile = kWaveRows * kChunk; /* words of one token's partial tile */
 
 struct JobLoc {
     int seg, unit, rb;
@@ -153,541 +170,254 @@ __device__ __forceinline__ void load_codes(const int8_t* p, uint32_t (&x)[8])
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-/* LDS word of the partial written by lane `writer` of octet o for row rho of
- * the octet, token t: rows and writers are skewed by the octet index. */
-__device__ __forceinline__ int part_index(int t, int o, int rho, int writer)
+/* Word of partial (row k of the wave's 16, block c of the chunk) in a
+ * token's [16][32] tile.  The quads of a row are XOR-permuted by k / 2, so
+ * an item's writes (rows 2p and 2p + 1: two 32-word runs) and the fold's
+ * quad reads (16 rows, one quad each) both fall on distinct banks. */
+__device__ __forceinline__ int ptile(int k, int c)
 {
-    return t * 512 + o * 64 + 8 * ((rho + o) & 7) + ((writer + o) & 7);
+    return k * kChunk + ((((c >> 2) ^ (k >> 1)) & 7) << 2) + (c & 3);
 }
 
-/* Waves per job: wave g computes fold group g (see block_group). */
-constexpr int kGroups = 4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-/* First block of fold group g out of nb blocks: the canonical fold adds four
- * consecutive groups of blocks, each folded from +0 in ascending order. */
-__device__ __forceinline__ int block_group(int g, int nb)
+/* Continues a row's chain over the 32 blocks of one chunk, in ascending
+ * order: acc = fma(d_c, S_c, acc).  tile: the token's partial tile (row k);
+ * dc: the chunk's 32 block scales (16-byte aligned).  The quad reads run
+ * kFoldAhead quads ahead of the fmas.  An empty asm statement that uses
+ * acc and may touch memory pins each quad's fmas and reads in place:
+ * otherwise the compiler sinks every fma of the loop to its end (the chain
+ * is needed only there) and keeps all the chunks' operands live. */
+constexpr int kFoldAhead = 3;
+
+__device__ __forceinline__ float fold_chunk(const float* tile, int k, const float* dc, float acc)
 {
-    return (g * nb) / kGroups;
-}
-
-/* Blocks of one fold group that a wave stages in LDS (K <= 8192). */
-constexpr int kMaxGroupBlocks = 64;
-
-template <int BITS>
-struct StepWeights {
-    uint32_t w[8][BITS];
-};
-
-/* LDS owned by one wave of a job: the partial transpose area, and the wave's
- * fold group of activation codes (already in block_dot operand order) and
- * block scales for each token of the unit. */
-template <int TMAX>
-struct WaveLds {
-    int32_t part[TMAX * 512];
-    uint32_t xa[TMAX][kMaxGroupBlocks][8];
-    float d[TMAX][kMaxGroupBlocks];
-};
-
-/* Loads this lane's block of each of its octet's 8 rows for one K step.
- * The loads are unconditional: rows past rows_ok read the octet's first row
- * and a block past the group reads b_last (both in bounds; their partials
- * are never folded or stored), so no load sits under a branch and each use
- * waits only for its own step. */
-template <int BITS>
-__device__ __forceinline__ void load_step(StepWeights<BITS>& W, const uint8_t* row0, int64_t rowbytes,
-                                          int b, int b_last, int rows_ok)
-{
-    const int bb = min(b, b_last);
+    const float* row = tile + k * kChunk;
+    const int sw = (k >> 1) & 7;
+    f32x4 s[8], d[8];
 #pragma unroll
-    for (int rho = 0; rho < 8; ++rho)
-        load_block<BITS>(row0 + (rho < rows_ok ? rho : 0) * rowbytes + (int64_t)bb * (4 * BITS), W.w[rho]);
-}
-
-/* Stages the codes and scales of blocks [b_begin, b_end) of every token into
- * the wave's LDS (one block per lane), once per job. */
-template <int BITS, int TMAX>
-__device__ __forceinline__ void stage_activations(WaveLds<TMAX>& L, int b_begin, int b_end, int ntok,
-                                                  const int8_t* const (&act)[TMAX],
-                                                  const float* const (&scl)[TMAX])
-{
-    const int lane = threadIdx.x & 63;
-    const int b = b_begin + lane;
+    for (int q = 0; q < kFoldAhead; ++q) {
+        s[q] = *reinterpret_cast<const f32x4*>(row + ((q ^ sw) << 2));
+        d[q] = *reinterpret_cast<const f32x4*>(dc + 4 * q);
+    }
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < ntok && b < b_end) {
-            uint32_t x[8], xa[8];
-            load_codes(act[t] + (int64_t)b * 32, x);
-            prep_dot<BITS>(x, xa);
-            uint4* dst = reinterpret_cast<uint4*>(L.xa[t][lane]);
-            dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
-            dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
-            L.d[t][lane] = scl[t][b];
+    for (int q = 0; q < 8; ++q) {
+        if (q + kFoldAhead < 8) {
+            s[q + kFoldAhead] = *reinterpret_cast<const f32x4*>(row + (((q + kFoldAhead) ^ sw) << 2));
+            d[q + kFoldAhead] = *reinterpret_cast<const f32x4*>(dc + 4 * (q + kFoldAhead));
         }
+        acc = __builtin_fmaf(d[q].x, s[q].x, acc);
+        acc = __builtin_fmaf(d[q].y, s[q].y, acc);
+        acc = __builtin_fmaf(d[q].z, s[q].z, acc);
+        acc = __builtin_fmaf(d[q].w, s[q].w, acc);
+        asm volatile("" : "+v"(acc) : : "memory");
     }
-    wave_lds_sync();
+    return acc;
 }
 
-/* One token's block of the wave's group, held in registers between its load
- * and its LDS commit (so other loads can be issued in between). */
-struct TokenBlock {
-    uint32_t x[8];
-    float d;
-};
-
-__device__ __forceinline__ void load_token_block(TokenBlock& T, const int8_t* act, const float* scl,
-                                                 int b_begin, int b_end)
+/* The same with group-wise weight scales: block b's coefficient is
+ * ws[b / gb] * d_b (ws: the row's ng scales; b0: the chunk's first block;
+ * blocks past the row read its last scale, their d is 0).  The group index
+ * steps with the block instead of being divided out per block. */
+__device__ __forceinline__ float fold_chunk_grouped(const float* tile, int k, const float* dc, float acc,
+                                                    const float* ws, int gb, int ng, int b0)
 {
-    const int b = min(b_begin + (int)(threadIdx.x & 63), b_end - 1);
-    load_codes(act + (int64_t)b * 32, T.x);
-    T.d = scl[b];
-}
-
-template <int BITS>
-__device__ __forceinline__ void commit_token_block(const TokenBlock& T, WaveLds<1>& L, int b_begin,
-                                                   int b_end)
-{
-    const int lane = threadIdx.x & 63;
-    if (b_begin + lane < b_end) {
-        uint32_t xa[8];
-        prep_dot<BITS>(T.x, xa);
-        uint4* dst = reinterpret_cast<uint4*>(L.xa[0][lane]);
-        dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
-        dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
-        L.d[0][lane] = T.d;
-    }
-    wave_lds_sync();
-}
-
-/* Block partials of K step st of the wave's group (nblk blocks from
- * b_begin), transposed through the wave's LDS, folded into acc (lane = row
- * 8o + j of the octet).  ws: the lane's row's group-wise scales (gb blocks
- * each), or null for per-row scales. */
-template <int BITS, int TMAX>
-__device__ __forceinline__ void fold_step(const StepWeights<BITS>& W, int st, int nblk, int ntok,
-                                          WaveLds<TMAX>& L, float (&acc)[TMAX], const float* ws, int gb,
-                                          int b_begin)
-{
-    const int lane = threadIdx.x & 63;
-    const int o = lane >> 3, j8 = lane & 7;
-    const int lb = 8 * st + j8;
-    const bool valid = lb < nblk;
+    const float* row = tile + k * kChunk;
+    const int sw = (k >> 1) & 7;
+    int g = b0 / gb, rem = b0 - (b0 / gb) * gb;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < ntok) {
-            uint32_t xa[8];
-            if (valid) {
-                const uint4* src = reinterpret_cast<const uint4*>(L.xa[t][lb]);
-                const uint4 u0 = src[0], u1 = src[1];
-                xa[0] = u0.x; xa[1] = u0.y; xa[2] = u0.z; xa[3] = u0.w;
-                xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
-            } else {
+    for (int q = 0; q < 8; ++q) {
+        const f32x4 s = *reinterpret_cast<const f32x4*>(row + ((q ^ sw) << 2));
+        const f32x4 d = *reinterpret_cast<const f32x4*>(dc + 4 * q);
+        const float sv[4] = {s.x, s.y, s.z, s.w}, dv[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    xa[i] = 0;
-            }
-#pragma unroll
-            for (int rho = 0; rho < 8; ++rho)
-                L.part[part_index(t, o, rho, j8)] = block_dot<BITS>(W.w[rho], xa);
-        }
-    }
-    wave_lds_sync();
-    const int nbs = max(0, min(8, nblk - 8 * st));
-    if (ws) {
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < ntok) {
-                for (int jj = 0; jj < nbs; ++jj)
-                    acc[t] = __builtin_fmaf(group_coef(ws, gb, b_begin + 8 * st + jj, L.d[t][8 * st + jj]),
-                                            (float)L.part[part_index(t, o, j8, jj)], acc[t]);
+        for (int j = 0; j < 4; ++j) {
+            acc = __builtin_fmaf(ws[min(g, ng - 1)] * dv[j], sv[j], acc);
+            if (++rem == gb) {
+                rem = 0;
+                ++g;
             }
         }
-    } else {
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < ntok) {
-                for (int jj = 0; jj < nbs; ++jj)
-                    acc[t] = __builtin_fmaf(L.d[t][8 * st + jj], (float)L.part[part_index(t, o, j8, jj)], acc[t]);
-            }
-        }
+        asm volatile("" : "+v"(acc) : : "memory"); /* as in fold_chunk */
     }
-    wave_lds_sync();
+    return acc;
 }
 
-/* Issues the weight loads of the first K step of a wave's fold group. */
+/* Chunks per row for nb blocks, rounded up to an instantiated count. */
+inline int gemv_ni(int nb)
+{
+    const int n = (nb + kChunk - 1) / kChunk;
+    return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 6 ? 6 : 8;
+}
+
+/* One load item of a lane: BITS words of one weight block. */
 template <int BITS>
-__device__ __forceinline__ void first_step(StepWeights<BITS>& A, const uint8_t* row0, int64_t rowbytes,
-                                           int b_begin, int b_end, int rows_ok)
+struct Item {
+    uint32_t w[BITS];
+};
+
+/* Items in flight: 2 NI (two chunks' worth at NI = 4 and below). */
+template <int BITS, int NI>
+struct Ring {
+    Item<BITS> it[2 * NI];
+};
+
+/* Loads item n = (chunk n / 8, pair n % 8) of a wave's 16 rows: rows0 is
+ * row 0 (uniform); rows8, when not null, is where rows 8.. start instead of
+ * right after row 7 (then all 16 rows exist).  A load takes the uniform base
+ * plus a 32-bit lane offset (16 rows of at most 8 KB).  Loads are
+ * unconditional: a lane past the rows or the row's blocks reads the last
+ * existing row / block instead (in bounds; its partial is never folded), so
+ * no load sits under a branch and each use waits only for its own item. */
+template <int BITS>
+__device__ __forceinline__ void item_load(Item<BITS>& W, const uint8_t* rows0, uint32_t rowbytes, int n,
+                                          int rows_ok, int nb, const uint8_t* rows8)
 {
-    const int j8 = threadIdx.x & 7;
-    load_step<BITS>(A, row0, rowbytes, b_begin + j8, max(b_end, b_begin + 1) - 1, rows_ok);
+    const int lane = threadIdx.x & 63;
+    const bool hi = rows8 && (n & 7) >= 4; /* uniform */
+    const int row = min(2 * (n & 7) + (lane >> 5), max(rows_ok, 1) - 1) - (hi ? 8 : 0);
+    const uint32_t off = (uint32_t)row * rowbytes +
+                         (uint32_t)min(kChunk * (n >> 3) + (lane & 31), nb - 1) * (uint32_t)(4 * BITS);
+    load_block<BITS>((hi ? rows8 : rows0) + off, W.w);
 }
 
-/* The K loop of one wave over its fold group, blocks [b_begin, b_end), in
- * steps of 8 blocks, the next step's weight loads issued before the current
- * step is computed; A holds the first step (first_step).  Waves of a
- * workgroup run their loops independently. */
-template <int BITS, int TMAX>
-__device__ __forceinline__ void k_loop(StepWeights<BITS>& A, const uint8_t* row0, int64_t rowbytes,
-                                       int b_begin, int b_end, int ntok, int rows_ok, WaveLds<TMAX>& L,
-                                       float (&acc)[TMAX], const float* ws, int gb)
+/* Issues the first 2 NI items (before the activations are staged, so the
+ * weight stream starts first). */
+template <int BITS, int NI>
+__device__ __forceinline__ void ring_start(Ring<BITS, NI>& R, const uint8_t* rows0, uint32_t rowbytes, int rows_ok,
+                                           int nb, const uint8_t* rows8 = nullptr)
 {
-    const int j8 = threadIdx.x & 7;
-    const int nblk = b_end - b_begin;
-    const int nsteps = (nblk + 7) / 8;
-    const int b_last = max(b_end, b_begin + 1) - 1;
-    StepWeights<BITS> B;
-    /* loads and steps are unconditional (a step past the group folds
-     * nothing), so A and B keep their registers across iterations */
-    for (int st = 0; st < nsteps; st += 2) {
-        load_step<BITS>(B, row0, rowbytes, b_begin + 8 * (st + 1) + j8, b_last, rows_ok);
-        fold_step<BITS, TMAX>(A, st, nblk, ntok, L, acc, ws, gb, b_begin);
-        load_step<BITS>(A, row0, rowbytes, b_begin + 8 * (st + 2) + j8, b_last, rows_ok);
-        fold_step<BITS, TMAX>(B, st + 1, nblk, ntok, L, acc, ws, gb, b_begin);
-    }
+#pragma unroll
+    for (int n = 0; n < 2 * NI; ++n)
+        item_load<BITS>(R.it[n], rows0, rowbytes, n, rows_ok, nb, rows8);
 }
 
-/* Adds the four group sums of each row in order; valid on wave 0 only. */
-template <int TMAX>
-__device__ __forceinline__ void sum_groups(float (*gsum)[TMAX][64], float (&acc)[TMAX])
-{
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t)
-        gsum[wv][t][lane] = acc[t];
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        float v = gsum[0][t][lane];
-        v = v + gsum[1][t][lane];
-        v = v + gsum[2][t][lane];
-        v = v + gsum[3][t][lane];
-        acc[t] = v;
-    }
-}
-
-} // namespace
-
-template <int BITS, int TMAX>
-__global__ __launch_bounds__(256) void ffn_gate_up_gemv(FfnArgs a)
-{
-    __shared__ WaveLds<TMAX> lds[kGroups];
-    __shared__ float gsum[kGroups][TMAX][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int o = lane >> 3;
-    const int RB = a.I / 32;
-    JobLoc L;
-    if (!locate(a, blockIdx.x, RB, L))
-        return;
-    const FfnSeg sg = pick(a, L.seg);
-    int e, pos0, ntok;
-    if (!unit_info(sg, L.unit, e, pos0, ntok))
-        return;
-    ntok = min(ntok, TMAX);
-    const int nb = a.H / 32;
-    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
-    const int8_t* act[TMAX];
-    const float* scl[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        const int tok = token_of(sg, pos0 + (t < ntok ? t : 0));
-        act[t] = a.xq + (int64_t)tok * a.H;
-        scl[t] = a.xd + (int64_t)tok * nb;
-    }
-    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
-    /* octets 0..3: gate rows rb*32 + 8o ..; octets 4..7: the same up rows */
-    const uint8_t* row0 = (o < 4 ? sg.gate_w : sg.up_w) +
-                          ((int64_t)e * a.I + L.rb * 32 + 8 * (o & 3)) * rowbytes;
-    /* group-wise scales of this lane's fold row (row 8(o & 3) + j of the job) */
-    const int ng = sg.gu_gb ? nb / sg.gu_gb : 0;
-    const float* ws = sg.gu_gb ? (o < 4 ? sg.gate_s : sg.up_s) +
-                                     ((int64_t)e * a.I + L.rb * 32 + 8 * (o & 3) + (lane & 7)) * ng
-                               : nullptr;
-    StepWeights<BITS> A;
-    first_step<BITS>(A, row0, rowbytes, b0, b1, 8);
-    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
-    float acc[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t)
-        acc[t] = 0.0f;
-    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, 8, lds[wv], acc, ws, sg.gu_gb);
-    sum_groups<TMAX>(gsum, acc);
-    if (wv != 0)
-        return;
-
-    const int r = L.rb * 32 + (lane & 31);
-    const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
-    const int nbi = a.I / 32;
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < ntok) {
-            const float v = sc * acc[t];
-            const float u = shfl_xor(v, 32);
-            const float h = canon_silu(v) * u;
-            float am = lane < 32 ? __builtin_fabsf(h) : 0.0f;
-            for (int m = 16; m >= 1; m >>= 1)
-                am = fmaxf(am, shfl_xor(am, m));
-            const float dsc = am / 127.0f;
-            const float inv = (am == 0.0f) ? 0.0f : 1.0f / dsc;
-            const int64_t row_out = sg.out_base + pos0 + t;
-            if (lane < 32)
-                a.hq[row_out * a.I + r] = (int8_t)q8_code(h, inv);
-            if (lane == 0)
-                a.hd[row_out * nbi + L.rb] = dsc;
-        }
-    }
-}
-
-template <int BITS, int TMAX>
-__global__ __launch_bounds__(256) void ffn_down_gemv(FfnArgs a)
-{
-    __shared__ WaveLds<TMAX> lds[kGroups];
-    __shared__ float gsum[kGroups][TMAX][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int o = lane >> 3;
-    const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
-    JobLoc L;
-    if (!locate(a, blockIdx.x, RB, L))
-        return;
-    const FfnSeg sg = pick(a, L.seg);
-    int e, pos0, ntok;
-    if (!unit_info(sg, L.unit, e, pos0, ntok))
-        return;
-    ntok = min(ntok, TMAX);
-    const int nb = a.I / 32;
-    const int64_t rowbytes = (int64_t)a.I * BITS / 8;
-    const int8_t* act[TMAX];
-    const float* scl[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        const int64_t row_in = sg.out_base + pos0 + (t < ntok ? t : 0);
-        act[t] = a.hq + row_in * a.I;
-        scl[t] = a.hd + row_in * nb;
-    }
-    const int b0 = block_group(wv, nb), b1 = block_group(wv + 1, nb);
-    const int first = L.rb * kRowsPerJob + 8 * o;
-    const int rows_ok = min(8, max(0, a.H - first));
-    const uint8_t* row0 = sg.down_w + ((int64_t)e * a.H + min(first, a.H - 1)) * rowbytes;
-    const int ng = sg.d_gb ? nb / sg.d_gb : 0;
-    const float* ws = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(first + (lane & 7), a.H - 1)) * ng : nullptr;
-    StepWeights<BITS> A;
-    first_step<BITS>(A, row0, rowbytes, b0, b1, rows_ok);
-    stage_activations<BITS, TMAX>(lds[wv], b0, b1, ntok, act, scl);
-    float acc[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t)
-        acc[t] = 0.0f;
-    k_loop<BITS, TMAX>(A, row0, rowbytes, b0, b1, ntok, rows_ok, lds[wv], acc, ws, sg.d_gb);
-    sum_groups<TMAX>(gsum, acc);
-    if (wv != 0)
-        return;
-
-    const int n = L.rb * kRowsPerJob + lane;
-    if (n < a.H) {
-        const float sc = sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n];
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t)
-            if (t < ntok)
-                a.y[(int64_t)(sg.out_base + pos0 + t) * a.H + n] = sc * acc[t];
-    }
-}
-
-/* ---- one-token batches ---------------------------------------------------
+/* ---- one token ------------------------------------------------------------
  * Unit u < k is the expert of selection slot u, unit k the shared expert;
  * hq / hd / y row u belongs to unit u, so the combine reads y in slot order.
  * The gate/up kernel selects the experts itself: wave 0 of every routed job
  * runs the top-k over the token's logits (the same selection as
  * router_select_kernel), so no workgroup waits for another, and the first
- * routed job stores ids and weights.
- *
- * Whole-row loads.  A job is 64 rows; wave w owns rows 16w .. 16w+15 and
- * reads them whole, two rows per load instruction: lane l takes row
- * 2p + (l >> 5) of pair p and blocks (l & 31) + 32 i, i < NI, so each half
- * wave reads 32 consecutive blocks of one row (512 bytes at int4).  Reading
- * each row in one sweep streams markedly faster than splitting K across the
- * waves (measured 6.5 vs 5.5 TB/s on 113 MB).  A lane's activation blocks are
- * the same for every row, so they stay in registers.  The exact partials of
- * the 16 rows go to LDS; lane (r, g) then folds row r's group g in ascending
- * block order and the four group sums are added in order.
+ * routed job stores ids and weights; meanwhile the other waves stage the
+ * token's activation blocks (operand order) and block scales in LDS.
  *
  * (A combine inside the down kernel -- the last unit to finish a row block
  * adding the others' rows -- needs a device-scope release per workgroup,
  * which on this chip writes back the XCD's L2; measured 3x slower than the
  * separate combine launch.) */
 
-constexpr int kDecRows = 16; /* rows of a job per wave */
-
-/* Load instructions per row pair for nb blocks, rounded up to an
- * instantiated count. */
-inline int dec_ni(int nb)
+/* Dynamic LDS of the one-token kernels, in words: per wave its partial tile
+ * (before the K loop wave 0's selection scratch), then the token's
+ * activation blocks [32 NI][8] and block scales [32 NI] (zero past nb), the
+ * job's row sums [64] and the selected ids [64]. */
+__host__ __device__ inline int dec_region()
 {
-    const int n = (nb + 31) / 32;
-    return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 6 ? 6 : 8;
+    return kTile > kSelScratch ? kTile : kSelScratch;
 }
 
-/* Dynamic LDS, in words: per wave the partials [16][nb | 1] (before the K
- * loop wave 0's selection scratch), then the token's block scales [nb], the
- * job's row sums [64] and the selected ids [64]. */
-__host__ __device__ inline int dec_region(int nb)
+__host__ __device__ inline int dec_dlen(int nb)
 {
-    const int p = kDecRows * (nb | 1);
-    return p > kSelScratch ? p : kSelScratch;
+    const int n = (nb + kChunk - 1) / kChunk;
+    return kChunk * (n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 6 ? 6 : 8);
 }
 
 __host__ __device__ inline size_t dec_lds_bytes(int nb)
 {
-    return (size_t)(kGroups * dec_region(nb) + nb + 64 + 64) * 4;
+    return (size_t)(kJobWaves * dec_region() + 9 * dec_dlen(nb) + 64 + 64) * 4;
 }
 
-template <int BITS, int NI>
-struct PairLoad {
-    uint32_t w[NI][BITS];
-};
-
-/* Loads are unconditional: a lane past the job's rows or the row's blocks
- * reads the last row / block instead (in bounds; its partial is never used),
- * so no load sits under a branch and each use waits only for its own loads. */
-template <int BITS, int NI>
-__device__ __forceinline__ void pair_load(PairLoad<BITS, NI>& L, const uint8_t* rows0, int64_t rowbytes,
-                                          int p, int rows_ok, int nb, const uint8_t* rows8 = nullptr)
+/* The wave's 16 rows against one token (xal, dl: its staged activation
+ * blocks and block scales); R holds items 0 .. 2NI - 1.  Returns on every
+ * lane the chain of row (lane mod 16), before the row scale.  P: the wave's
+ * partial tile.  GROUPED: ws0 holds the group-wise scales of the wave's
+ * row 0 (rows nb / gb apart). */
+template <int BITS, int NI, bool GROUPED>
+__device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* rows0, uint32_t rowbytes, int rows_ok,
+                                            int nb, const uint32_t* xal, float* P, const float* dl,
+                                            const float* ws0, int gb, const uint8_t* rows8 = nullptr)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = min(2 * p + (lane >> 5), max(rows_ok, 1) - 1), c = lane & 31;
-    /* rows8: where rows 8.. start, when not right after row 7 */
-    const uint8_t* rp = (rows8 && row >= 8) ? rows8 + (int64_t)(row - 8) * rowbytes : rows0 + (int64_t)row * rowbytes;
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-        load_block<BITS>(rp + (int64_t)min(c + 32 * i, nb - 1) * (4 * BITS), L.w[i]);
-}
-
-template <int BITS, int NI>
-__device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const uint32_t (&xa)[NI][8], int p,
-                                              int nb, int32_t* P, int sp)
-{
-    const int lane = threadIdx.x & 63;
-    const int row = 2 * p + (lane >> 5), c = lane & 31;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int b = c + 32 * i;
-        if (row < kDecRows && b < nb)
-            P[row * sp + b] = block_dot<BITS>(L.w[i], xa[i]);
-    }
-}
-
-/* The wave's 16 rows (rows0: its first row; rows_ok of them exist): returns
- * on every lane the folded sum of row (lane & 15) before the row scale.
- * The caller has issued pair 0 into A (so the weight stream starts before
- * the activations are prepared); two pairs are in flight while one is
- * multiplied. */
-template <int BITS, int NI>
-__device__ __forceinline__ float dec_k_loop(PairLoad<BITS, NI>& A, const uint8_t* rows0, int64_t rowbytes,
-                                            int rows_ok, int nb, const uint32_t (&xa)[NI][8], int32_t* P,
-                                            int sp, const float* dl, const float* ws0, int gb,
-                                            const uint8_t* rows8 = nullptr)
-{
-    PairLoad<BITS, NI> B;
-#pragma unroll
-    for (int p = 0; p < kDecRows / 2; p += 2) {
-        pair_load<BITS, NI>(B, rows0, rowbytes, p + 1, rows_ok, nb, rows8);
-        pair_partials<BITS, NI>(A, xa, p, nb, P, sp);
-        if (p + 2 < kDecRows / 2) /* resolved at compile time */
-            pair_load<BITS, NI>(A, rows0, rowbytes, p + 2, rows_ok, nb, rows8);
-        pair_partials<BITS, NI>(B, xa, p + 1, nb, P, sp);
-    }
-    wave_lds_sync();
-    const int lane = threadIdx.x & 63;
-    const int r = lane & 15, g = lane >> 4;
-    const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
-    const int32_t* pr = P + r * sp;
+    constexpr int D = 2 * NI, N = 8 * NI;
+    const int lane = threadIdx.x & 63, c = lane & 31, k = lane & 15;
+    const int ng = GROUPED ? nb / gb : 0;
+    const float* ws = GROUPED ? ws0 + (int64_t)min(k, max(rows_ok, 1) - 1) * ng : nullptr;
     float acc = 0.0f;
-    int b = b0;
-    if (ws0) {
-        /* group-wise scales of row r (rows past rows_ok read the last row's) */
-        const float* ws = ws0 + (int64_t)min(r, max(rows_ok, 1) - 1) * (nb / gb);
-        for (; b < b1; ++b)
-            acc = __builtin_fmaf(group_coef(ws, gb, b, dl[b]), (float)pr[b], acc);
-    } else {
-        /* eight partials and scales read ahead of their (in-order) fmas */
-        for (; b + 8 <= b1; b += 8) {
-            int32_t q[8];
-            float dd[8];
+    uint32_t xa[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                q[i] = pr[b + i];
-                dd[i] = dl[b + i];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+    for (int n = 0; n < N; ++n) {
+        const int i = n >> 3, p = n & 7;
+        if (p == 0) {
+            /* the lane's activation block of this chunk */
+            const uint4* src = reinterpret_cast<const uint4*>(xal + (kChunk * i + c) * 8);
+            const uint4 u0 = src[0], u1 = src[1];
+            xa[0] = u0.x; xa[1] = u0.y; xa[2] = u0.z; xa[3] = u0.w;
+            xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
         }
-        for (; b < b1; ++b)
-            acc = __builtin_fmaf(dl[b], (float)pr[b], acc);
+        const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
+        P[ptile(2 * p + (lane >> 5), c)] = kChunk * i + c < nb ? (float)s : 0.0f;
+        if (n + D < N) /* resolved at compile time */
+            item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, rows8);
+        if (p == 7) {
+            wave_lds_sync();
+            if constexpr (GROUPED)
+                acc = fold_chunk_grouped(P, k, dl + kChunk * i, acc, ws, gb, ng, kChunk * i);
+            else
+                acc = fold_chunk(P, k, dl + kChunk * i, acc);
+            wave_lds_sync(); /* the chunk's partials are read before the next chunk's overwrite them */
+        }
     }
-    float v = __shfl(acc, r, kWave);
-    v = v + __shfl(acc, 16 + r, kWave);
-    v = v + __shfl(acc, 32 + r, kWave);
-    v = v + __shfl(acc, 48 + r, kWave);
-    return v;
+    return acc;
 }
 
-/* The token's activation blocks (l & 31) + 32 i, loaded raw ... */
-template <int NI>
-__device__ __forceinline__ void dec_act_load(const int8_t* act, int nb, uint32_t (&x)[NI][8])
+/* Stages the token's activation blocks (operand order) and block scales:
+ * thread `tid` of `nthr` takes blocks tid, tid + nthr, ...; blocks past nb
+ * get scale 0 (their codes are never used).  The caller synchronises. */
+template <int BITS>
+__device__ __forceinline__ void dec_stage(const int8_t* act, const float* scl, int nb, int dlen, int tid, int nthr,
+                                          uint32_t* xal, float* dl)
 {
-    const int c = threadIdx.x & 31;
+    for (int b0 = tid; b0 < dlen; b0 += 2 * nthr) {
+        /* two blocks' loads in flight before either is converted */
+        uint32_t x[2][8];
+        float dv[2];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-        load_codes(act + (int64_t)min(c + 32 * i, nb - 1) * 32, x[i]);
-}
-
-/* The block scales b = lane + 64 i, i < kDlPre, loaded with the codes (so
- * that their latency is spent before the weight stream starts) ... */
-constexpr int kDlPre = 4;
-
-__device__ __forceinline__ void dec_scale_load(const float* scl, int nb, float (&pre)[kDlPre])
-{
-    const int lane = threadIdx.x & 63;
+        for (int r = 0; r < 2; ++r) {
+            const int b = min(b0 + r * nthr, nb - 1);
+            load_codes(act + (int64_t)b * 32, x[r]);
+            dv[r] = scl[b];
+        }
 #pragma unroll
-    for (int i = 0; i < kDlPre; ++i)
-        pre[i] = scl[min(lane + 64 * i, nb - 1)];
-}
-
-/* ... then the codes put in operand order; every wave also writes the block
- * scales (the same values) so that its own reads follow its own writes. */
-template <int BITS, int NI>
-__device__ __forceinline__ void dec_act_prep(uint32_t (&x)[NI][8], const float (&pre)[kDlPre], const float* scl,
-                                             int nb, float* dl)
-{
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        uint32_t xa[8];
-        prep_dot<BITS>(x[i], xa);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            x[i][q] = xa[q];
+        for (int r = 0; r < 2; ++r) {
+            const int b = b0 + r * nthr;
+            if (b < dlen) {
+                uint32_t xa[8];
+                prep_dot<BITS>(x[r], xa);
+                uint4* dst = reinterpret_cast<uint4*>(xal + b * 8);
+                dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
+                dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
+                dl[b] = b < nb ? dv[r] : 0.0f;
+            }
+        }
     }
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < kDlPre; ++i)
-        if (lane + 64 * i < nb)
-            dl[lane + 64 * i] = pre[i];
-    for (int b = lane + 64 * kDlPre; b < nb; b += 64)
-        dl[b] = scl[b];
-    wave_lds_sync();
 }
 
-template <int BITS, int NI>
+} // namespace
+
+/* GROUPED: a launch whose segments may hold group-wise scales (a separate
+ * instantiation, so that the per-row kernels carry no grouped fold). */
+template <int BITS, int NI, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
 {
     extern __shared__ __attribute__((aligned(16))) int32_t dec_lds[];
     const FfnArgs& a = d.f;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int RB = a.I / 32;
-    const int nb = a.H / 32, sp = nb | 1, region = dec_region(nb);
-    int32_t* P = dec_lds + wv * region;
-    float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
-    float* rsum = dl + nb;
+    const int nb = a.H / 32, region = dec_region(), dlen = kChunk * NI;
+    float* P = reinterpret_cast<float*>(dec_lds + wv * region);
+    uint32_t* xal = reinterpret_cast<uint32_t*>(dec_lds + kJobWaves * region);
+    float* dl = reinterpret_cast<float*>(xal + 8 * dlen);
+    float* rsum = dl + dlen;
     int32_t* sel_ids = reinterpret_cast<int32_t*>(rsum + 64); /* read by every wave after the barrier */
-    const int64_t rowbytes = (int64_t)a.H * BITS / 8;
+    const uint32_t rowbytes = (uint32_t)a.H * BITS / 8;
     const int n_mini = d.hs ? a.I / 8 : 0;
     if ((int)blockIdx.x < n_mini) {
         /* one-wave job of the shared expert (first, so that every CU gets
@@ -700,16 +430,13 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         const int m = blockIdx.x;
         const uint8_t* g0 = sh.gate_w + (int64_t)8 * m * rowbytes;
         const uint8_t* u0 = sh.up_w + (int64_t)8 * m * rowbytes;
-        PairLoad<BITS, NI> A;
-        pair_load<BITS, NI>(A, g0, rowbytes, 0, kDecRows, nb, u0);
-        uint32_t xa[NI][8];
-        dec_act_load<NI>(a.xq, nb, xa);
-        float dpre[kDlPre];
-        dec_scale_load(a.xd, nb, dpre);
+        Ring<BITS, NI> R;
+        ring_start<BITS, NI>(R, g0, rowbytes, kWaveRows, nb, u0);
         const int r = lane & 15;
         const float sc = (r < 8 ? sh.gate_s : sh.up_s)[8 * m + (r & 7)];
-        dec_act_prep<BITS, NI>(xa, dpre, a.xd, nb, dl);
-        const float v16 = dec_k_loop<BITS, NI>(A, g0, rowbytes, kDecRows, nb, xa, P, sp, dl, nullptr, 0, u0);
+        dec_stage<BITS>(a.xq, a.xd, nb, dlen, lane, 64, xal, dl);
+        wave_lds_sync();
+        const float v16 = dec_k_loop<BITS, NI, false>(R, g0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0, u0);
         const float v = sc * v16;
         const float up = __shfl(v, (lane & 7) + 8, kWave);
         if (lane < 8)
@@ -727,25 +454,19 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     const int u = nunits > d.k ? (j == 0 ? d.k : j - 1) : j;
     const bool routed = u < d.k;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
-    uint32_t xa[NI][8];
-    dec_act_load<NI>(a.xq, nb, xa);
-    float dpre[kDlPre];
-    dec_scale_load(a.xd, nb, dpre);
     int e = 0;
-    bool prepped = false;
     if (routed) {
         /* wave 0 alone selects (a chain of wave-wide steps, so it runs best
          * without the other waves issuing the same work) while waves 1..3
-         * prepare their activations; the scratch is wave 0's (not yet used)
-         * partial buffer */
+         * stage the activations; the scratch is wave 0's (not yet used)
+         * partial tile */
         float* sel_s = reinterpret_cast<float*>(dec_lds);
         if (wv == 0) {
             const bool store = u == 0 && rb == 0; /* the others need the ids only */
             select_token(d.logits, d.bias, d.E, d.k, d.rsf, store ? d.ids : sel_ids, store ? d.w : nullptr, sel_s,
                          sel_ids, 1, 0, d.opt);
         } else {
-            dec_act_prep<BITS, NI>(xa, dpre, a.xd, nb, dl);
-            prepped = true;
+            dec_stage<BITS>(a.xq, a.xd, nb, dlen, threadIdx.x - 64, 192, xal, dl);
         }
         __syncthreads();
         const int sel = sel_ids[u];
@@ -756,18 +477,22 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
     const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) +
                            ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * rowbytes;
-    PairLoad<BITS, NI> A;
-    pair_load<BITS, NI>(A, rows0, rowbytes, 0, kDecRows, nb);
+    Ring<BITS, NI> R;
+    ring_start<BITS, NI>(R, rows0, rowbytes, kWaveRows, nb);
     /* the epilogue's row scale (lane: row rb*32 + lane%32 of gate, then up),
      * loaded now so that it is in hand after the K loop */
     const int r = rb * 32 + (lane & 31);
     const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
-    if (!prepped)
-        dec_act_prep<BITS, NI>(xa, dpre, a.xd, nb, dl);
+    if (!routed) {
+        dec_stage<BITS>(a.xq, a.xd, nb, dlen, threadIdx.x, 256, xal, dl);
+        __syncthreads();
+    }
     const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) +
                                       ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * (nb / sg.gu_gb)
                                 : nullptr;
-    const float v16 = dec_k_loop<BITS, NI>(A, rows0, rowbytes, kDecRows, nb, xa, P, sp, dl, ws0, sg.gu_gb);
+    const float v16 = GROUPED && sg.gu_gb
+                          ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, ws0, sg.gu_gb)
+                          : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0);
     if (lane < 16)
         rsum[16 * wv + lane] = v16;
     __syncthreads();
@@ -788,12 +513,12 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         a.hd[(int64_t)u * (a.I / 32) + rb] = dsc;
 }
 
-template <int BITS, int NI>
+template <int BITS, int NI, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
 {
     extern __shared__ __attribute__((aligned(16))) int32_t dec_lds[];
     const FfnArgs& a = d.f;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
     const int nunits = d.k + (a.nseg > 1 ? 1 : 0);
     const int u = blockIdx.x / RB, rb = blockIdx.x - (blockIdx.x / RB) * RB;
@@ -804,140 +529,109 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
         return;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
     const int e = routed ? min(d.ids[u], sg.n_mat - 1) : 0;
-    const int nb = a.I / 32, sp = nb | 1, region = dec_region(nb);
-    int32_t* P = dec_lds + wv * region;
-    float* dl = reinterpret_cast<float*>(dec_lds + kGroups * region);
-    uint32_t xa[NI][8];
-    dec_act_load<NI>(a.hq + (int64_t)u * a.I, nb, xa);
-    float dpre[kDlPre];
-    dec_scale_load(a.hd + (int64_t)u * nb, nb, dpre);
-    const int row0 = rb * kRowsPerJob + kDecRows * wv;
-    const int rows_ok = min(kDecRows, max(0, a.H - row0));
-    const int64_t rowbytes = (int64_t)a.I * BITS / 8;
+    const int nb = a.I / 32, region = dec_region(), dlen = kChunk * NI;
+    float* P = reinterpret_cast<float*>(dec_lds + wv * region);
+    uint32_t* xal = reinterpret_cast<uint32_t*>(dec_lds + kJobWaves * region);
+    float* dl = reinterpret_cast<float*>(xal + 8 * dlen);
+    const int row0 = rb * kRowsPerJob + kWaveRows * wv;
+    const int rows_ok = min(kWaveRows, max(0, a.H - row0));
+    const uint32_t rowbytes = (uint32_t)a.I * BITS / 8;
     const uint8_t* rows0 = sg.down_w + ((int64_t)e * a.H + min(row0, a.H - 1)) * rowbytes;
-    PairLoad<BITS, NI> A;
-    pair_load<BITS, NI>(A, rows0, rowbytes, 0, rows_ok, nb);
-    dec_act_prep<BITS, NI>(xa, dpre, a.hd + (int64_t)u * nb, nb, dl);
+    Ring<BITS, NI> R;
+    ring_start<BITS, NI>(R, rows0, rowbytes, rows_ok, nb);
+    dec_stage<BITS>(a.hq + (int64_t)u * a.I, a.hd + (int64_t)u * nb, nb, dlen, threadIdx.x, 256, xal, dl);
+    __syncthreads();
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(row0, a.H - 1)) * (nb / sg.d_gb) : nullptr;
-    const float v = dec_k_loop<BITS, NI>(A, rows0, rowbytes, rows_ok, nb, xa, P, sp, dl, ws0, sg.d_gb);
+    const float v = GROUPED && sg.d_gb
+                        ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, ws0, sg.d_gb)
+                            : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, nullptr, 0);
     const int n = row0 + lane;
     if (lane < rows_ok)
         a.y[(int64_t)u * a.H + n] = (sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n]) * v;
 }
 
+namespace {
+
 /* Items a thread stages per round (loads of all issued before any is converted). */
 constexpr int kDcStage = 4;
 
-/* ---- whole rows for units of up to kUnitTokens tokens --------------------
+/* ---- units of up to TMAX tokens --------------------------------------------
+ * The unit's activation blocks of every token are staged once per job in
+ * LDS in operand order; each item then yields the partials of its two rows
+ * for every token of the unit, and lane (row k, token t) runs the chain of
+ * (k, t).
  *
- * The job of ffn_gate_up_gemv / ffn_down_gemv (one unit, 64 row dots), with
- * the whole-row streaming of the one-token kernels: wave w owns 16 whole rows
- * and reads two rows per load group (lane l: row 2p + l/32, blocks
- * l mod 32 + 32 i), two pairs in flight.  The unit's activation blocks of
- * every token are staged once per job in LDS in operand order; after each
- * pair the wave writes the exact partials of its 2 rows x the unit's tokens
- * and folds them -- lane (row, token, group) runs the canonical chain of its
- * group, the four group sums added in order -- while the next two pairs
- * load.
- *
- * Dynamic LDS, in words: codes [TMAX][nb][8], block scales [TMAX][nb | 1],
- * per wave the partials [2][TMAX][nb | 1], and the job's row values
- * [64][TMAX]; used while it fits 64 KB. */
+ * Dynamic LDS, in words: codes [TMAX][nb][8], block scales [TMAX][32 NI]
+ * (zero past nb), per wave the partial tiles [TMAX][16][32], and the job's
+ * row values [64][TMAX]. */
 __host__ __device__ inline size_t rows_lds_words(int nb, int tmax)
 {
-    const size_t sp = (size_t)(nb | 1);
-    return (size_t)tmax * nb * 8 + (size_t)tmax * sp + (size_t)kGroups * 2 * tmax * sp + 64 * (size_t)tmax;
+    return (size_t)tmax * nb * 8 + (size_t)tmax * dec_dlen(nb) + (size_t)kJobWaves * tmax * kTile +
+           64 * (size_t)tmax;
 }
 
-inline bool rows_fit(int nb, int tmax)
-{
-    return nb <= 32 * 8 && rows_lds_words(nb, tmax) * 4 <= 64 * 1024;
-}
+constexpr size_t kLdsMax = 160 * 1024; /* LDS of one CU (gfx950) */
 
-/* Exact partials of one loaded pair (rows 0, 1) for every token of the
- * unit, to P[(row * TMAX + t) * sp + b]. */
-template <int BITS, int NI, int TMAX>
-__device__ __forceinline__ void rows_partials(const PairLoad<BITS, NI>& L, const uint32_t* xal, int nb, int ntok,
-                                              int32_t* P, int sp)
+/* The wave's 16 rows against the unit's ntok tokens; R holds items
+ * 0 .. 2NI - 1.  Returns on lane (k = l mod 16, t = l / 16) the chain of
+ * row k for token t (lanes of tokens past ntok hold no value).  xal, dls:
+ * the staged codes and scales; P: the wave's TMAX partial tiles. */
+template <int BITS, int NI, int TMAX, bool GROUPED>
+__device__ __forceinline__ float rows_k_loop(Ring<BITS, NI>& R, const uint8_t* rows0, uint32_t rowbytes, int rows_ok,
+                                             int nb, int ntok, const uint32_t* xal, const float* dls, float* P,
+                                             const float* ws0, int gb)
 {
-    const int lane = threadIdx.x & 63, c = lane & 31, row = lane >> 5;
-    /* tokens one at a time (a rolled loop keeps one token's operands live) */
-#pragma unroll 1
-    for (int t = 0; t < ntok; ++t) {
-        {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int b = c + 32 * i;
-                if (b < nb) {
-                    const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)t * nb + b) * 8);
-                    const uint4 u0 = src[0], u1 = src[1];
-                    const uint32_t xa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-                    P[(row * TMAX + t) * sp + b] = block_dot<BITS>(L.w[i], xa);
-                }
-            }
-        }
-    }
-}
-
-/* The canonical fold of the pair's 2 rows (rows rbase, rbase + 1 of the
- * job): lane (r2, t, g) folds group g of row r2 for token t, then the group
- * sums of (r2, t) are added in order into vs[row][t].  ws0: group-wise scales
- * of the pair's first row (gb blocks per scale, rows ng apart), or null;
- * a row past rows_left (not stored) reads the last existing row's. */
-template <int TMAX>
-__device__ __forceinline__ void rows_fold(const int32_t* P, int sp, int nb, int ntok, const float* dls,
-                                          const float* ws0, int gb, int ng, int rows_left, float* vs, int rbase)
-{
-    const int lane = threadIdx.x & 63;
-    const int g = lane & 3, t = (lane >> 2) % TMAX, r4 = (lane >> 2) / TMAX;
-    const int rr = min(r4, 1);
-    const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
-    const int32_t* pr = P + (rr * TMAX + t) * sp;
-    const float* dj = dls + t * sp;
+    constexpr int D = 2 * NI, N = 8 * NI;
+    const int lane = threadIdx.x & 63, c = lane & 31, k = lane & 15;
+    const int tf = min(lane >> 4, TMAX - 1); /* token of the lane's chain */
+    const int sd = kChunk * NI;
+    const int ng = GROUPED ? nb / gb : 0;
+    const float* ws = GROUPED ? ws0 + (int64_t)min(k, max(rows_ok, 1) - 1) * ng : nullptr;
     float acc = 0.0f;
-    int b = b0;
-    if (ws0) {
-        const float* ws = ws0 + (int64_t)min(rr, max(rows_left, 1) - 1) * ng;
-        for (; b < b1; ++b)
-            acc = __builtin_fmaf(group_coef(ws, gb, b, dj[b]), (float)pr[b], acc);
-    } else {
-        for (; b + 8 <= b1; b += 8) {
-            int32_t q[8];
-            float dd[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                q[i] = pr[b + i];
-                dd[i] = dj[b + i];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc = __builtin_fmaf(dd[i], (float)q[i], acc);
+    for (int n = 0; n < N; ++n) {
+        const int i = n >> 3, p = n & 7;
+        const int b = kChunk * i + c;
+        const int bc = min(b, nb - 1);
+        const int w = ptile(2 * p + (lane >> 5), c);
+        /* tokens one at a time (a rolled loop keeps one token's operands live) */
+#pragma unroll 1
+        for (int t = 0; t < ntok; ++t) {
+            const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)t * nb + bc) * 8);
+            const uint4 u0 = src[0], u1 = src[1];
+            const uint32_t xa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
+            P[t * kTile + w] = b < nb ? (float)s : 0.0f;
         }
-        for (; b < b1; ++b)
-            acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
+        if (n + D < N) /* resolved at compile time */
+            item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, nullptr);
+        if (p == 7) {
+            wave_lds_sync();
+            const float* dc = dls + tf * sd + kChunk * i;
+            if constexpr (GROUPED)
+                acc = fold_chunk_grouped(P + tf * kTile, k, dc, acc, ws, gb, ng, kChunk * i);
+            else
+                acc = fold_chunk(P + tf * kTile, k, dc, acc);
+            wave_lds_sync();
+        }
     }
-    const int base = lane & ~3;
-    float v = __shfl(acc, base, kWave);
-    v = v + __shfl(acc, base + 1, kWave);
-    v = v + __shfl(acc, base + 2, kWave);
-    v = v + __shfl(acc, base + 3, kWave);
-    if (g == 0 && r4 < 2 && t < ntok)
-        vs[(rbase + r4) * TMAX + t] = v;
+    return acc;
 }
 
 /* Stages the codes (operand order) and block scales of the unit's tokens;
- * every thread issues up to kDcStage items' loads before converting any. */
+ * every thread issues up to kDcStage items' loads before converting any.
+ * Scales past nb (up to sd per token) are zero. */
 template <int BITS, int TMAX>
-__device__ __forceinline__ void rows_stage(uint32_t* xal, float* dls, int nb, int sp, int ntok,
+__device__ __forceinline__ void rows_stage(uint32_t* xal, float* dls, int nb, int sd, int ntok,
                                            const int8_t* const (&act)[TMAX], const float* const (&scl)[TMAX])
 {
     const int n_items = ntok * nb;
-    for (int i0 = threadIdx.x; i0 < n_items; i0 += 64 * kGroups * kDcStage) {
+    for (int i0 = threadIdx.x; i0 < n_items; i0 += 64 * kJobWaves * kDcStage) {
         uint32_t x[kDcStage][8];
         float dv[kDcStage];
 #pragma unroll
         for (int r = 0; r < kDcStage; ++r) {
-            const int i = i0 + r * 64 * kGroups;
+            const int i = i0 + r * 64 * kJobWaves;
             if (i < n_items) {
                 const int t = i / nb, b = i - t * nb;
                 const int8_t* ap = act[0];
@@ -954,7 +648,7 @@ __device__ __forceinline__ void rows_stage(uint32_t* xal, float* dls, int nb, in
         }
 #pragma unroll
         for (int r = 0; r < kDcStage; ++r) {
-            const int i = i0 + r * 64 * kGroups;
+            const int i = i0 + r * 64 * kJobWaves;
             if (i < n_items) {
                 const int t = i / nb, b = i - t * nb;
                 uint32_t xa[8];
@@ -962,56 +656,22 @@ __device__ __forceinline__ void rows_stage(uint32_t* xal, float* dls, int nb, in
                 uint4* dst = reinterpret_cast<uint4*>(xal + (int64_t)i * 8);
                 dst[0] = make_uint4(xa[0], xa[1], xa[2], xa[3]);
                 dst[1] = make_uint4(xa[4], xa[5], xa[6], xa[7]);
-                dls[t * sp + b] = dv[r];
+                dls[t * sd + b] = dv[r];
             }
         }
     }
+    for (int i = threadIdx.x; i < TMAX * (sd - nb); i += 64 * kJobWaves)
+        dls[(i / (sd - nb)) * sd + nb + i % (sd - nb)] = 0.0f;
     __syncthreads();
 }
 
-/* Partials and fold of pair p (in L) into vs[rbase0 + 2p ..]. */
-template <int BITS, int NI, int TMAX>
-__device__ __forceinline__ void rows_pair(const PairLoad<BITS, NI>& L, int p, int rows_ok, int nb, int sp,
-                                          int ntok, const uint32_t* xal, const float* dls, int32_t* P,
-                                          const float* ws0, int gb, int ng, float* vs, int rbase0)
-{
-    rows_partials<BITS, NI, TMAX>(L, xal, nb, ntok, P, sp);
-    wave_lds_sync();
-    const int r_first = min(2 * p, max(rows_ok, 1) - 1);
-    rows_fold<TMAX>(P, sp, nb, ntok, dls, ws0 ? ws0 + (int64_t)r_first * ng : nullptr, gb, ng, rows_ok - 2 * p,
-                    vs, rbase0 + 2 * p);
-    wave_lds_sync(); /* the pair's partials are read before the next overwrites them */
-}
+} // namespace
 
-/* The wave's 16 rows (rows0: its first row, rows_ok of them exist), pair 0
- * already in A; two pairs in flight while one is multiplied and folded. */
-template <int BITS, int NI, int TMAX>
-__device__ __forceinline__ void rows_k_loop(PairLoad<BITS, NI>& A, const uint8_t* rows0, int64_t rowbytes,
-                                            int rows_ok, int nb, int sp, int ntok, const uint32_t* xal,
-                                            const float* dls, int32_t* P, const float* ws0, int gb, int ng,
-                                            float* vs, int rbase0)
-{
-    PairLoad<BITS, NI> B;
-    pair_load<BITS, NI>(B, rows0, rowbytes, 1, rows_ok, nb);
-#pragma unroll
-    for (int p = 0; p < kDecRows / 2; p += 2) {
-        if (p + 2 < kDecRows / 2) { /* resolved at compile time */
-            rows_pair<BITS, NI, TMAX>(A, p, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
-            pair_load<BITS, NI>(A, rows0, rowbytes, p + 2, rows_ok, nb);
-            rows_pair<BITS, NI, TMAX>(B, p + 1, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
-            pair_load<BITS, NI>(B, rows0, rowbytes, p + 3, rows_ok, nb);
-        } else {
-            rows_pair<BITS, NI, TMAX>(A, p, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
-            rows_pair<BITS, NI, TMAX>(B, p + 1, rows_ok, nb, sp, ntok, xal, dls, P, ws0, gb, ng, vs, rbase0);
-        }
-    }
-}
-
-template <int BITS, int NI, int TMAX>
+template <int BITS, int NI, int TMAX, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) int32_t rw_lds[];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int RB = a.I / 32;
     JobLoc L;
     if (!locate(a, blockIdx.x, RB, L))
@@ -1021,17 +681,17 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
     if (!unit_info(sg, L.unit, e, pos0, ntok))
         return;
     ntok = min(ntok, TMAX);
-    const int nb = a.H / 32, sp = nb | 1;
+    const int nb = a.H / 32, sd = kChunk * NI;
     const int64_t rowbytes = (int64_t)a.H * BITS / 8;
     uint32_t* xal = reinterpret_cast<uint32_t*>(rw_lds);
     float* dls = reinterpret_cast<float*>(xal + (int64_t)TMAX * nb * 8);
-    int32_t* P = reinterpret_cast<int32_t*>(dls + TMAX * sp) + wv * (2 * TMAX * sp);
-    float* vs = reinterpret_cast<float*>(reinterpret_cast<int32_t*>(dls + TMAX * sp) + kGroups * 2 * TMAX * sp);
+    float* P = dls + TMAX * sd + wv * (TMAX * kTile);
+    float* vs = dls + TMAX * sd + kJobWaves * TMAX * kTile;
     /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
     const int rloc = 16 * (wv & 1);
     const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + L.rb * 32 + rloc) * rowbytes;
-    PairLoad<BITS, NI> A;
-    pair_load<BITS, NI>(A, rows0, rowbytes, 0, kDecRows, nb);
+    Ring<BITS, NI> R;
+    ring_start<BITS, NI>(R, rows0, rowbytes, kWaveRows, nb);
     const int r = L.rb * 32 + (lane & 31);
     const float sc = sg.gu_gb ? 1.0f : (lane < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + r];
     const int8_t* act[TMAX];
@@ -1042,13 +702,19 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
         act[t] = a.xq + (int64_t)tok * a.H;
         scl[t] = a.xd + (int64_t)tok * nb;
     }
-    rows_stage<BITS, TMAX>(xal, dls, nb, sp, ntok, act, scl);
+    rows_stage<BITS, TMAX>(xal, dls, nb, sd, ntok, act, scl);
     const int ng = sg.gu_gb ? nb / sg.gu_gb : 0;
     const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) + ((int64_t)e * a.I + L.rb * 32 + rloc) * ng
                                 : nullptr;
-    /* job row of the wave's first row: gate rows 0..31, up rows 32..63 */
-    rows_k_loop<BITS, NI, TMAX>(A, rows0, rowbytes, kDecRows, nb, sp, ntok, xal, dls, P, ws0, sg.gu_gb, ng, vs,
-                                16 * wv);
+    const float v = GROUPED && sg.gu_gb
+                        ? rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P, ws0,
+                                                            sg.gu_gb)
+                        : rows_k_loop<BITS, NI, TMAX, false>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P,
+                                                             nullptr, 0);
+    /* job row of the wave's row k: gate rows 0..31, up rows 32..63 */
+    const int t_l = lane >> 4;
+    if (t_l < ntok)
+        vs[(16 * wv + (lane & 15)) * TMAX + t_l] = v;
     __syncthreads();
     if (wv != 0)
         return;
@@ -1056,9 +722,9 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
         if (t < ntok) {
-            const float v = sc * vs[lane * TMAX + t];
-            const float u = shfl_xor(v, 32);
-            const float h = canon_silu(v) * u;
+            const float gv = sc * vs[lane * TMAX + t];
+            const float u = shfl_xor(gv, 32);
+            const float h = canon_silu(gv) * u;
             float am = lane < 32 ? __builtin_fabsf(h) : 0.0f;
             for (int m = 16; m >= 1; m >>= 1)
                 am = fmaxf(am, shfl_xor(am, m));
@@ -1073,11 +739,11 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
     }
 }
 
-template <int BITS, int NI, int TMAX>
+template <int BITS, int NI, int TMAX, bool GROUPED>
 __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) int32_t rw_lds[];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int RB = (a.H + kRowsPerJob - 1) / kRowsPerJob;
     JobLoc L;
     if (!locate(a, blockIdx.x, RB, L))
@@ -1087,17 +753,16 @@ __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
     if (!unit_info(sg, L.unit, e, pos0, ntok))
         return;
     ntok = min(ntok, TMAX);
-    const int nb = a.I / 32, sp = nb | 1;
+    const int nb = a.I / 32, sd = kChunk * NI;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
     uint32_t* xal = reinterpret_cast<uint32_t*>(rw_lds);
     float* dls = reinterpret_cast<float*>(xal + (int64_t)TMAX * nb * 8);
-    int32_t* P = reinterpret_cast<int32_t*>(dls + TMAX * sp) + wv * (2 * TMAX * sp);
-    float* vs = reinterpret_cast<float*>(reinterpret_cast<int32_t*>(dls + TMAX * sp) + kGroups * 2 * TMAX * sp);
-    const int first = L.rb * kRowsPerJob + kDecRows * wv;
-    const int rows_ok = min(kDecRows, max(0, a.H - first));
+    float* P = dls + TMAX * sd + wv * (TMAX * kTile);
+    const int first = L.rb * kRowsPerJob + kWaveRows * wv;
+    const int rows_ok = min(kWaveRows, max(0, a.H - first));
     const uint8_t* rows0 = sg.down_w + ((int64_t)e * a.H + min(first, a.H - 1)) * rowbytes;
-    PairLoad<BITS, NI> A;
-    pair_load<BITS, NI>(A, rows0, rowbytes, 0, rows_ok, nb);
+    Ring<BITS, NI> R;
+    ring_start<BITS, NI>(R, rows0, rowbytes, rows_ok, nb);
     const int n = first + (lane & 15);
     const float sc = sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + min(n, a.H - 1)];
     const int8_t* act[TMAX];
@@ -1108,55 +773,116 @@ __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
         act[t] = a.hq + row_in * a.I;
         scl[t] = a.hd + row_in * nb;
     }
-    rows_stage<BITS, TMAX>(xal, dls, nb, sp, ntok, act, scl);
+    rows_stage<BITS, TMAX>(xal, dls, nb, sd, ntok, act, scl);
     const int ng = sg.d_gb ? nb / sg.d_gb : 0;
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(first, a.H - 1)) * ng : nullptr;
-    rows_k_loop<BITS, NI, TMAX>(A, rows0, rowbytes, rows_ok, nb, sp, ntok, xal, dls, P, ws0, sg.d_gb, ng, vs,
-                                16 * wv);
-    wave_lds_sync();
-    /* lane (row l % 16): its row's value of every token */
-    if (lane < 16 && n < a.H) {
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t)
-            if (t < ntok)
-                a.y[(int64_t)(sg.out_base + pos0 + t) * a.H + n] = sc * vs[(16 * wv + lane) * TMAX + t];
-    }
+    const float v = GROUPED && sg.d_gb
+                        ? rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P, ws0,
+                                                            sg.d_gb)
+                        : rows_k_loop<BITS, NI, TMAX, false>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P,
+                                                             nullptr, 0);
+    const int t_l = lane >> 4;
+    if (t_l < ntok && (lane & 15) < rows_ok)
+        a.y[(int64_t)(sg.out_base + pos0 + t_l) * a.H + n] = sc * v;
 }
 
+namespace {
+
 /* ---- one token: down projection with the combine --------------------------
- * A workgroup owns 8 output rows for all U = k (+1 shared) units; wave w
+ * A workgroup owns 2 DW output rows for all U = k (+1 shared) units; wave w
  * streams rows 2w, 2w+1 of every unit's down matrix as whole-row pairs
  * (pair j = unit j), two units in flight.  All units' h codes are staged in
  * LDS in operand order once per workgroup (measured faster than each lane
- * loading its own h blocks per unit, and than four units in flight).  After
- * the canonical fold of each (unit, row), the wave forms
+ * loading its own h blocks per unit, and than four units in flight).  Lane
+ * (unit, row) then runs the canonical chain of its row, and the wave forms
  * out = y_shared + sum_j w_j * y_j for its rows with the same fma order as
  * combine_kernel, so the result is bit-identical to down + combine without
- * the y round trip or the extra launch.  (8 rows per workgroup give H / 8 =
- * 768 workgroups at H = 6144: three per CU.) */
-
-/* A workgroup of DW waves owns 2 DW output rows (wave w: rows 2w, 2w+1).
+ * the y round trip or the extra launch.
+ *
  * kDcWide waves (one workgroup per CU at H = 6144) stage every unit's h once
  * per CU; the vector L1, whose lines bound this kernel, then spends a
  * twelfth as many lines on h as with three 4-wave workgroups per CU. */
 constexpr int kDcWide = 12;
 
-/* LDS words: h codes [U][nb][8], h scales [U][nb | 1], per wave the partials
- * [2U][nb | 1] and the row values [2U]. */
-__host__ __device__ inline size_t dc_lds_words(int U, int nb, int DW)
+/* Row stride of the staged scales and of the partials: a multiple of four
+ * words (16-byte quad reads), four words past the row. */
+__host__ __device__ inline int dc_sp(int nb)
 {
-    return (size_t)U * nb * 8 + (size_t)U * (nb | 1) + (size_t)DW * 2 * U * ((nb | 1) + 1);
+    return ((nb + 3) & ~3) + 4;
 }
 
-constexpr size_t kDcLdsMax = 160 * 1024; /* LDS of one CU (gfx950) */
-
-/* First of this wave's two rows of the down matrix of unit u (u = slot, or
- * k for the shared expert) whose matrix index is e. */
-__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int u, int e, int row0, int64_t rowbytes)
+/* LDS words: h codes [U][nb][8], h scales [U][sp], per wave the partials
+ * [2U][sp] and the row values [2U]. */
+__host__ __device__ inline size_t dc_lds_words(int U, int nb, int DW)
 {
-    const FfnArgs& a = d.f;
-    const uint8_t* w = u < d.k ? a.seg[0].down_w : a.seg[1].down_w;
-    return w + ((int64_t)e * a.H + row0) * rowbytes;
+    const size_t sp = (size_t)dc_sp(nb);
+    return (size_t)U * nb * 8 + (size_t)U * sp + (size_t)DW * 2 * U * sp + (size_t)DW * 2 * U;
+}
+
+/* Row pair of one unit: NI loads per lane (blocks (l & 31) + 32 i of row
+ * l / 32 of the pair). */
+template <int BITS, int NI>
+struct PairLoad {
+    uint32_t w[NI][BITS];
+};
+
+template <int BITS, int NI>
+__device__ __forceinline__ void pair_load(PairLoad<BITS, NI>& L, const uint8_t* rows0, int64_t rowbytes, int nb)
+{
+    const int lane = threadIdx.x & 63;
+    const uint8_t* rp = rows0 + (int64_t)(lane >> 5) * rowbytes;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        load_block<BITS>(rp + (int64_t)min((lane & 31) + kChunk * i, nb - 1) * (4 * BITS), L.w[i]);
+}
+
+/* Exact partials of a loaded pair, as fp32, to P[row * sp + b]. */
+template <int BITS, int NI>
+__device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const uint32_t (&xa)[NI][8], int nb,
+                                              float* P, int sp)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int b = c + kChunk * i;
+        if (b < nb)
+            P[row * sp + b] = (float)block_dot<BITS>(L.w[i], xa[i]);
+    }
+}
+
+/* A whole row's chain over nb blocks: pr the partials, dj the block scales
+ * (both 16-byte aligned), in ascending order from acc = +0. */
+__device__ __forceinline__ float fold_row(const float* pr, const float* dj, int nb)
+{
+    float acc = 0.0f;
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(pr + b);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(pr + b + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dj + b);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dj + b + 4);
+        acc = __builtin_fmaf(d0.x, s0.x, acc);
+        acc = __builtin_fmaf(d0.y, s0.y, acc);
+        acc = __builtin_fmaf(d0.z, s0.z, acc);
+        acc = __builtin_fmaf(d0.w, s0.w, acc);
+        acc = __builtin_fmaf(d1.x, s1.x, acc);
+        acc = __builtin_fmaf(d1.y, s1.y, acc);
+        acc = __builtin_fmaf(d1.z, s1.z, acc);
+        acc = __builtin_fmaf(d1.w, s1.w, acc);
+        asm volatile("" : "+v"(acc) : : "memory"); /* as in fold_chunk */
+    }
+    for (; b < nb; ++b)
+        acc = __builtin_fmaf(dj[b], pr[b], acc);
+    return acc;
+}
+
+__device__ __forceinline__ float fold_row_grouped(const float* pr, const float* dj, int nb, const float* ws, int gb)
+{
+    float acc = 0.0f;
+    for (int b = 0; b < nb; ++b)
+        acc = __builtin_fmaf(group_coef(ws, gb, b, dj[b]), pr[b], acc);
+    return acc;
 }
 
 template <int NI>
@@ -1165,11 +891,20 @@ __device__ __forceinline__ void dc_act(const uint32_t* xal, int j, int nb, uint3
     const int c = threadIdx.x & 31;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)j * nb + min(c + 32 * i, nb - 1)) * 8);
+        const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)j * nb + min(c + kChunk * i, nb - 1)) * 8);
         const uint4 u0 = src[0], u1 = src[1];
         xa[i][0] = u0.x; xa[i][1] = u0.y; xa[i][2] = u0.z; xa[i][3] = u0.w;
         xa[i][4] = u1.x; xa[i][5] = u1.y; xa[i][6] = u1.z; xa[i][7] = u1.w;
     }
+}
+
+/* First of this wave's two rows of the down matrix of unit u (u = slot, or
+ * k for the shared expert) whose matrix index is e. */
+__device__ __forceinline__ const uint8_t* dc_rows(const DecodeArgs& d, int u, int e, int row0, int64_t rowbytes)
+{
+    const FfnArgs& a = d.f;
+    const uint8_t* w = u < d.k ? a.seg[0].down_w : a.seg[1].down_w;
+    return w + ((int64_t)e * a.H + row0) * rowbytes;
 }
 
 /* Unit of compacted index n: the n-th kept routed slot (bit set in `kept`),
@@ -1186,10 +921,12 @@ __device__ __forceinline__ int dc_unit(uint64_t kept, int n_kept, int k, int n, 
     return __builtin_ctzll(kept);
 }
 
+} // namespace
+
 template <int BITS, int NI, int DW>
 __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
 {
-    extern __shared__ int32_t dc_lds[];
+    extern __shared__ __attribute__((aligned(16))) int32_t dc_lds[];
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const bool shared = a.nseg > 1;
@@ -1199,14 +936,12 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
     const uint64_t kept = all_kept ? 0 : __ballot(lane < d.k && d.ids[lane] >= 0);
     const int n_kept = all_kept ? d.k : __popcll(kept);
     const int U = n_kept + (shared ? 1 : 0);
-    const int nb = a.I / 32, sp = nb | 1;
-    uint32_t* xal = reinterpret_cast<uint32_t*>(dc_lds);        /* [U][nb][8] */
-    /* the block scales' rows have the odd stride sp, like the partials', so
-     * that the fold's reads (32 distinct addresses) spread over the banks */
-    float* dls = reinterpret_cast<float*>(xal + U * nb * 8);    /* [U][sp] */
-    int32_t* P0 = reinterpret_cast<int32_t*>(dls + U * sp);      /* [DW][2U][sp] */
-    int32_t* P = P0 + wv * (2 * U * sp);
-    float* ys = reinterpret_cast<float*>(P0 + DW * 2 * U * sp) + wv * 2 * U;
+    const int nb = a.I / 32, sp = dc_sp(nb);
+    uint32_t* xal = reinterpret_cast<uint32_t*>(dc_lds);    /* [U][nb][8] */
+    float* dls = reinterpret_cast<float*>(xal + U * nb * 8); /* [U][sp] */
+    float* P0 = dls + U * sp;                                /* [DW][2U][sp] */
+    float* P = P0 + wv * (2 * U * sp);
+    float* ys = P0 + DW * 2 * U * sp + wv * 2 * U;
     const int row0 = blockIdx.x * (2 * DW) + 2 * wv;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
 
@@ -1218,7 +953,7 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
     auto unit_at = [&](int q) { return shared ? (q == 0 ? U - 1 : q - 1) : q; };
     PairLoad<BITS, NI> A, B;
     if (shared)
-        pair_load<BITS, NI>(A, dc_rows(d, d.k, 0, row0, rowbytes), rowbytes, 0, 2, nb);
+        pair_load<BITS, NI>(A, dc_rows(d, d.k, 0, row0, rowbytes), rowbytes, nb);
     /* per-unit values in lane registers, loaded once (U <= 32): lane j holds
      * compacted unit j's unit id, matrix index and routing weight (lane
      * 2j + r gets the row scale of this wave's row r of unit j once h is
@@ -1231,7 +966,7 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
     if (!shared)
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, 0), __builtin_amdgcn_readlane(e_l, 0), row0,
                                        rowbytes),
-                            rowbytes, 0, 2, nb);
+                            rowbytes, nb);
     /* the shared expert's h in fp32 (one-wave gate/up jobs; 4 nb <= 256):
      * thread 4b + q loads elements 8q .. 8q+7 of block b now, and forms the
      * Q8_0 blocks after the routed items' loads are issued */
@@ -1315,51 +1050,28 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
     const float rs_l = (rt_r ? a.seg[0].d_gb : a.seg[1].d_gb) ? 1.0f : ds_r[(int64_t)e_r * a.H + row0 + (lane & 1)];
     __syncthreads();
 
-    /* fold of chains [c_begin, c_end): chain (rd, g) = (compacted unit rd / 2,
-     * row rd % 2; group g), lane ci - c0 of round c0 */
+    /* chains [c_begin, c_end) (at most 64): chain rd = (compacted unit
+     * rd / 2, row rd % 2) on lane rd - c_begin */
     auto fold_chains = [&](int c_begin, int c_end) {
-        for (int c0 = c_begin; c0 < c_end; c0 += 64) {
-            const int ci = c0 + lane;
-            const int rd = min(ci >> 2, 2 * U - 1), g = ci & 3;
-            const int b0 = block_group(g, nb), b1 = block_group(g + 1, nb);
-            const int32_t* pr = P + rd * sp;
-            const float* dj = dls + (rd >> 1) * sp;
-            float acc = 0.0f;
-            int b = b0;
-            /* lane values are read before any branch: every lane is active */
-            const int uf = __shfl(u_l, rd >> 1, kWave), ef = __shfl(e_l, rd >> 1, kWave);
-            const float rsv = __shfl(rs_l, rd, kWave);
-            const int gbf = uf < d.k ? a.seg[0].d_gb : a.seg[1].d_gb;
-            if (gbf) {
-                /* group-wise scales of (unit, row) */
-                const float* ws = (uf < d.k ? a.seg[0].down_s : a.seg[1].down_s) +
-                                  ((int64_t)ef * a.H + row0 + (rd & 1)) * (nb / gbf);
-                for (; b < b1; ++b)
-                    acc = __builtin_fmaf(group_coef(ws, gbf, b, dj[b]), (float)pr[b], acc);
-            } else {
-                for (; b + 8 <= b1; b += 8) {
-                    int32_t q[8];
-                    float dd[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        q[i] = pr[b + i];
-                        dd[i] = dj[b + i];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        acc = __builtin_fmaf(dd[i], (float)q[i], acc);
-                }
-                for (; b < b1; ++b)
-                    acc = __builtin_fmaf(dj[b], (float)pr[b], acc);
-            }
-            const int base = lane & ~3;
-            float v = __shfl(acc, base, kWave);
-            v = v + __shfl(acc, base + 1, kWave);
-            v = v + __shfl(acc, base + 2, kWave);
-            v = v + __shfl(acc, base + 3, kWave);
-            if (g == 0 && ci < c_end)
-                ys[rd] = rsv * v; /* rsv: 1 with group-wise scales */
+        const int ci = c_begin + lane;
+        const int rd = min(ci, 2 * U - 1);
+        /* lane values are read before any branch: every lane is active */
+        const int uf = __shfl(u_l, rd >> 1, kWave), ef = __shfl(e_l, rd >> 1, kWave);
+        const float rsv = __shfl(rs_l, rd, kWave);
+        const int gbf = uf < d.k ? a.seg[0].d_gb : a.seg[1].d_gb;
+        const float* pr = P + rd * sp;
+        const float* dj = dls + (rd >> 1) * sp;
+        float acc;
+        if (gbf) {
+            /* group-wise scales of (unit, row) */
+            const float* ws = (uf < d.k ? a.seg[0].down_s : a.seg[1].down_s) +
+                              ((int64_t)ef * a.H + row0 + (rd & 1)) * (nb / gbf);
+            acc = fold_row_grouped(pr, dj, nb, ws, gbf);
+        } else {
+            acc = fold_row(pr, dj, nb);
         }
+        if (ci < c_end)
+            ys[rd] = rsv * acc; /* rsv: 1 with group-wise scales */
     };
 
     /* the pair of stream position q is in A for even q and in B for odd q;
@@ -1370,25 +1082,25 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
         const int j0 = unit_at(q), j1 = unit_at(min(q + 1, U - 1)), j2 = unit_at(min(q + 2, U - 1));
         pair_load<BITS, NI>(B, dc_rows(d, __builtin_amdgcn_readlane(u_l, j1), __builtin_amdgcn_readlane(e_l, j1), row0,
                                        rowbytes),
-                            rowbytes, 0, 2, nb);
+                            rowbytes, nb);
         dc_act<NI>(xal, j0, nb, xa);
-        pair_partials<BITS, NI>(A, xa, 0, nb, P + 2 * j0 * sp, sp);
+        pair_partials<BITS, NI>(A, xa, nb, P + 2 * j0 * sp, sp);
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, j2), __builtin_amdgcn_readlane(e_l, j2), row0,
                                        rowbytes),
-                            rowbytes, 0, 2, nb);
+                            rowbytes, nb);
         if (q + 1 < U) {
             dc_act<NI>(xal, j1, nb, xa);
-            pair_partials<BITS, NI>(B, xa, 0, nb, P + 2 * j1 * sp, sp);
+            pair_partials<BITS, NI>(B, xa, nb, P + 2 * j1 * sp, sp);
         }
         if (q == 0 && shared) {
             /* the shared expert (streamed first) is folded while the routed
-             * pairs load, so the final fold is one round for 8 routed units */
+             * pairs load */
             wave_lds_sync();
-            fold_chains(8 * (U - 1), 8 * U);
+            fold_chains(2 * (U - 1), 2 * U);
         }
     }
     wave_lds_sync();
-    fold_chains(0, shared ? 8 * (U - 1) : 8 * U);
+    fold_chains(0, shared ? 2 * (U - 1) : 2 * U);
     wave_lds_sync();
     /* compacted order is slot order: the combine's fma order is kept (every
      * lane runs the chain of row lane & 1; lanes 0 and 1 store) */
@@ -1408,70 +1120,66 @@ static int64_t total_jobs(const FfnArgs& a, int RB)
     return n;
 }
 
-template <int NI, int TMAX>
+/* Raises a kernel's dynamic LDS limit once, when it needs more than 64 KB. */
+static void allow_lds(const void* fn, size_t lds)
+{
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+}
+
+template <int BITS, int NI, int TMAX, bool GROUPED>
+static void launch_rows_k(bool gate_up, dim3 grid, size_t lds, const FfnArgs& a, hipStream_t st)
+{
+    const dim3 block(64 * kJobWaves);
+    if (gate_up) {
+        allow_lds(reinterpret_cast<const void*>(&ffn_gate_up_rows<BITS, NI, TMAX, GROUPED>), lds);
+        hipLaunchKernelGGL((ffn_gate_up_rows<BITS, NI, TMAX, GROUPED>), grid, block, lds, st, a);
+    } else {
+        allow_lds(reinterpret_cast<const void*>(&ffn_down_rows<BITS, NI, TMAX, GROUPED>), lds);
+        hipLaunchKernelGGL((ffn_down_rows<BITS, NI, TMAX, GROUPED>), grid, block, lds, st, a);
+    }
+}
+
+template <int NI, int TMAX, bool GROUPED>
 static void launch_rows_ni(const FfnArgs& a, int32_t bits, bool gate_up, dim3 grid, size_t lds, hipStream_t st)
 {
-    const dim3 block(64 * kGroups);
-    if (gate_up) {
-        switch (bits) {
-        case 8: hipLaunchKernelGGL((ffn_gate_up_rows<8, NI, TMAX>), grid, block, lds, st, a); break;
-        case 4: hipLaunchKernelGGL((ffn_gate_up_rows<4, NI, TMAX>), grid, block, lds, st, a); break;
-        default: hipLaunchKernelGGL((ffn_gate_up_rows<2, NI, TMAX>), grid, block, lds, st, a); break;
-        }
-    } else {
-        switch (bits) {
-        case 8: hipLaunchKernelGGL((ffn_down_rows<8, NI, TMAX>), grid, block, lds, st, a); break;
-        case 4: hipLaunchKernelGGL((ffn_down_rows<4, NI, TMAX>), grid, block, lds, st, a); break;
-        default: hipLaunchKernelGGL((ffn_down_rows<2, NI, TMAX>), grid, block, lds, st, a); break;
-        }
+    switch (bits) {
+    case 8: launch_rows_k<8, NI, TMAX, GROUPED>(gate_up, grid, lds, a, st); break;
+    case 4: launch_rows_k<4, NI, TMAX, GROUPED>(gate_up, grid, lds, a, st); break;
+    default: launch_rows_k<2, NI, TMAX, GROUPED>(gate_up, grid, lds, a, st); break;
     }
 }
 
-/* The whole-row kernels when their LDS fits, else the octet kernels. */
-template <int TMAX>
-static void launch_gate_up_t(const FfnArgs& a, int32_t bits, dim3 grid, hipStream_t st)
+template <int TMAX, bool GROUPED>
+static void launch_rows_g(const FfnArgs& a, int32_t bits, bool gate_up, dim3 grid, hipStream_t st)
 {
-    const dim3 block(64 * kGroups);
-    const int nb = a.H / 32;
-    if (rows_fit(nb, TMAX)) {
-        const size_t lds = rows_lds_words(nb, TMAX) * 4;
-        switch (dec_ni(nb)) {
-        case 1: launch_rows_ni<1, TMAX>(a, bits, true, grid, lds, st); break;
-        case 2: launch_rows_ni<2, TMAX>(a, bits, true, grid, lds, st); break;
-        case 4: launch_rows_ni<4, TMAX>(a, bits, true, grid, lds, st); break;
-        case 6: launch_rows_ni<6, TMAX>(a, bits, true, grid, lds, st); break;
-        default: launch_rows_ni<8, TMAX>(a, bits, true, grid, lds, st); break;
-        }
-        return;
-    }
-    switch (bits) {
-    case 8: hipLaunchKernelGGL((ffn_gate_up_gemv<8, TMAX>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((ffn_gate_up_gemv<4, TMAX>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((ffn_gate_up_gemv<2, TMAX>), grid, block, 0, st, a); break;
+    const int nb = gate_up ? a.H / 32 : a.I / 32;
+    const size_t lds = rows_lds_words(nb, TMAX) * 4;
+    switch (gemv_ni(nb)) {
+    case 1: launch_rows_ni<1, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
+    case 2: launch_rows_ni<2, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
+    case 4: launch_rows_ni<4, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
+    case 6: launch_rows_ni<6, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
+    default: launch_rows_ni<8, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
     }
 }
 
-template <int TMAX>
-static void launch_down_t(const FfnArgs& a, int32_t bits, dim3 grid, hipStream_t st)
+/* Whether a launch's segments hold group-wise scales (gate/up or down). */
+static bool any_grouped(const FfnArgs& a, bool gate_up)
 {
-    const dim3 block(64 * kGroups);
-    const int nb = a.I / 32;
-    if (rows_fit(nb, TMAX)) {
-        const size_t lds = rows_lds_words(nb, TMAX) * 4;
-        switch (dec_ni(nb)) {
-        case 1: launch_rows_ni<1, TMAX>(a, bits, false, grid, lds, st); break;
-        case 2: launch_rows_ni<2, TMAX>(a, bits, false, grid, lds, st); break;
-        case 4: launch_rows_ni<4, TMAX>(a, bits, false, grid, lds, st); break;
-        case 6: launch_rows_ni<6, TMAX>(a, bits, false, grid, lds, st); break;
-        default: launch_rows_ni<8, TMAX>(a, bits, false, grid, lds, st); break;
-        }
-        return;
-    }
-    switch (bits) {
-    case 8: hipLaunchKernelGGL((ffn_down_gemv<8, TMAX>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((ffn_down_gemv<4, TMAX>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((ffn_down_gemv<2, TMAX>), grid, block, 0, st, a); break;
-    }
+    bool g = false;
+    for (int i = 0; i < a.nseg && i < 2; ++i)
+        g = g || (gate_up ? a.seg[i].gu_gb : a.seg[i].d_gb) != 0;
+    return g;
+}
+
+template <int TMAX>
+static void launch_rows_t(const FfnArgs& a, int32_t bits, bool gate_up, dim3 grid, hipStream_t st)
+{
+    if (any_grouped(a, gate_up))
+        launch_rows_g<TMAX, true>(a, bits, gate_up, grid, st);
+    else
+        launch_rows_g<TMAX, false>(a, bits, gate_up, grid, st);
 }
 
 hipError_t launch_ffn_gate_up(const FfnArgs& a, int32_t bits, hipStream_t st)
@@ -1480,9 +1188,9 @@ hipError_t launch_ffn_gate_up(const FfnArgs& a, int32_t bits, hipStream_t st)
     if (jobs == 0)
         return hipSuccess;
     if (a.unit_tokens == 1)
-        launch_gate_up_t<1>(a, bits, dim3((uint32_t)jobs), st);
+        launch_rows_t<1>(a, bits, true, dim3((uint32_t)jobs), st);
     else
-        launch_gate_up_t<kUnitTokens>(a, bits, dim3((uint32_t)jobs), st);
+        launch_rows_t<kUnitTokens>(a, bits, true, dim3((uint32_t)jobs), st);
     return hipGetLastError();
 }
 
@@ -1492,31 +1200,55 @@ hipError_t launch_ffn_down(const FfnArgs& a, int32_t bits, hipStream_t st)
     if (jobs == 0)
         return hipSuccess;
     if (a.unit_tokens == 1)
-        launch_down_t<1>(a, bits, dim3((uint32_t)jobs), st);
+        launch_rows_t<1>(a, bits, false, dim3((uint32_t)jobs), st);
     else
-        launch_down_t<kUnitTokens>(a, bits, dim3((uint32_t)jobs), st);
+        launch_rows_t<kUnitTokens>(a, bits, false, dim3((uint32_t)jobs), st);
     return hipGetLastError();
 }
 
-template <int NI>
+template <int NI, bool GROUPED>
 static void gate_up_decode_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, hipStream_t st)
 {
-    const dim3 block(64 * kGroups);
+    const dim3 block(64 * kJobWaves);
     switch (bits) {
-    case 8: hipLaunchKernelGGL((ffn_gate_up_decode<8, NI>), grid, block, lds, st, d); break;
-    case 4: hipLaunchKernelGGL((ffn_gate_up_decode<4, NI>), grid, block, lds, st, d); break;
-    default: hipLaunchKernelGGL((ffn_gate_up_decode<2, NI>), grid, block, lds, st, d); break;
+    case 8: hipLaunchKernelGGL((ffn_gate_up_decode<8, NI, GROUPED>), grid, block, lds, st, d); break;
+    case 4: hipLaunchKernelGGL((ffn_gate_up_decode<4, NI, GROUPED>), grid, block, lds, st, d); break;
+    default: hipLaunchKernelGGL((ffn_gate_up_decode<2, NI, GROUPED>), grid, block, lds, st, d); break;
     }
 }
 
-template <int NI>
+template <int NI, bool GROUPED>
 static void down_decode_ni(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, hipStream_t st)
 {
-    const dim3 block(64 * kGroups);
+    const dim3 block(64 * kJobWaves);
     switch (bits) {
-    case 8: hipLaunchKernelGGL((ffn_down_decode<8, NI>), grid, block, lds, st, d); break;
-    case 4: hipLaunchKernelGGL((ffn_down_decode<4, NI>), grid, block, lds, st, d); break;
-    default: hipLaunchKernelGGL((ffn_down_decode<2, NI>), grid, block, lds, st, d); break;
+    case 8: hipLaunchKernelGGL((ffn_down_decode<8, NI, GROUPED>), grid, block, lds, st, d); break;
+    case 4: hipLaunchKernelGGL((ffn_down_decode<4, NI, GROUPED>), grid, block, lds, st, d); break;
+    default: hipLaunchKernelGGL((ffn_down_decode<2, NI, GROUPED>), grid, block, lds, st, d); break;
+    }
+}
+
+template <bool GROUPED>
+static void gate_up_decode_g(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, int nb, hipStream_t st)
+{
+    switch (gemv_ni(nb)) {
+    case 1: gate_up_decode_ni<1, GROUPED>(d, bits, grid, lds, st); break;
+    case 2: gate_up_decode_ni<2, GROUPED>(d, bits, grid, lds, st); break;
+    case 4: gate_up_decode_ni<4, GROUPED>(d, bits, grid, lds, st); break;
+    case 6: gate_up_decode_ni<6, GROUPED>(d, bits, grid, lds, st); break;
+    default: gate_up_decode_ni<8, GROUPED>(d, bits, grid, lds, st); break;
+    }
+}
+
+template <bool GROUPED>
+static void down_decode_g(const DecodeArgs& d, int32_t bits, dim3 grid, size_t lds, int nb, hipStream_t st)
+{
+    switch (gemv_ni(nb)) {
+    case 1: down_decode_ni<1, GROUPED>(d, bits, grid, lds, st); break;
+    case 2: down_decode_ni<2, GROUPED>(d, bits, grid, lds, st); break;
+    case 4: down_decode_ni<4, GROUPED>(d, bits, grid, lds, st); break;
+    case 6: down_decode_ni<6, GROUPED>(d, bits, grid, lds, st); break;
+    default: down_decode_ni<8, GROUPED>(d, bits, grid, lds, st); break;
     }
 }
 
@@ -1527,13 +1259,10 @@ hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStrea
     const int nb = d.f.H / 32;
     const dim3 grid((uint32_t)jobs);
     const size_t lds = dec_lds_bytes(nb);
-    switch (dec_ni(nb)) {
-    case 1: gate_up_decode_ni<1>(d, bits, grid, lds, st); break;
-    case 2: gate_up_decode_ni<2>(d, bits, grid, lds, st); break;
-    case 4: gate_up_decode_ni<4>(d, bits, grid, lds, st); break;
-    case 6: gate_up_decode_ni<6>(d, bits, grid, lds, st); break;
-    default: gate_up_decode_ni<8>(d, bits, grid, lds, st); break;
-    }
+    if (any_grouped(d.f, true))
+        gate_up_decode_g<true>(d, bits, grid, lds, nb, st);
+    else
+        gate_up_decode_g<false>(d, bits, grid, lds, nb, st);
     return hipGetLastError();
 }
 
@@ -1543,13 +1272,10 @@ hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t
     const int nb = d.f.I / 32;
     const dim3 grid((uint32_t)jobs);
     const size_t lds = dec_lds_bytes(nb);
-    switch (dec_ni(nb)) {
-    case 1: down_decode_ni<1>(d, bits, grid, lds, st); break;
-    case 2: down_decode_ni<2>(d, bits, grid, lds, st); break;
-    case 4: down_decode_ni<4>(d, bits, grid, lds, st); break;
-    case 6: down_decode_ni<6>(d, bits, grid, lds, st); break;
-    default: down_decode_ni<8>(d, bits, grid, lds, st); break;
-    }
+    if (any_grouped(d.f, false))
+        down_decode_g<true>(d, bits, grid, lds, nb, st);
+    else
+        down_decode_g<false>(d, bits, grid, lds, nb, st);
     return hipGetLastError();
 }
 
@@ -1559,8 +1285,7 @@ static void down_combine_launch(const DecodeArgs& d, dim3 grid, size_t lds, hipS
     if (lds > 64 * 1024) {
         static bool raised = false; /* once per instantiation */
         if (!raised) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_down_combine_decode<BITS, NI, DW>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDcLdsMax);
+            allow_lds(reinterpret_cast<const void*>(&ffn_down_combine_decode<BITS, NI, DW>), lds);
             raised = true;
         }
     }
@@ -1583,16 +1308,16 @@ static int dc_waves(const DecodeArgs& d)
 {
     const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
     const int nb = d.f.I / 32;
-    if (d.f.H % (2 * kDcWide) == 0 && dc_lds_words(U, nb, kDcWide) * 4 <= kDcLdsMax)
+    if (d.f.H % (2 * kDcWide) == 0 && dc_lds_words(U, nb, kDcWide) * 4 <= kLdsMax)
         return kDcWide;
-    return kGroups;
+    return kJobWaves;
 }
 
 bool down_combine_decode_fits(const DecodeArgs& d)
 {
     const int U = d.k + (d.f.nseg > 1 ? 1 : 0);
-    /* per-unit values live in lanes: 2U row scales per wave */
-    return U <= 32 && d.f.H % (2 * kGroups) == 0 && dc_lds_words(U, d.f.I / 32, kGroups) * 4 <= 64 * 1024;
+    /* per-unit values live in lanes: 2U row chains per wave */
+    return U <= 32 && d.f.H % (2 * kJobWaves) == 0 && dc_lds_words(U, d.f.I / 32, kJobWaves) * 4 <= 64 * 1024;
 }
 
 hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hipStream_t st)
@@ -1603,7 +1328,7 @@ hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hip
     const dim3 grid((uint32_t)(d.f.H / (2 * DW)));
     const size_t lds = dc_lds_words(U, nb, DW) * 4;
     if (DW == kDcWide) {
-        switch (dec_ni(nb)) {
+        switch (gemv_ni(nb)) {
         case 1: down_combine_ni<1, kDcWide>(d, bits, grid, lds, st); break;
         case 2: down_combine_ni<2, kDcWide>(d, bits, grid, lds, st); break;
         case 4: down_combine_ni<4, kDcWide>(d, bits, grid, lds, st); break;
@@ -1611,12 +1336,12 @@ hipError_t launch_ffn_down_combine_decode(const DecodeArgs& d, int32_t bits, hip
         default: down_combine_ni<8, kDcWide>(d, bits, grid, lds, st); break;
         }
     } else {
-        switch (dec_ni(nb)) {
-        case 1: down_combine_ni<1, kGroups>(d, bits, grid, lds, st); break;
-        case 2: down_combine_ni<2, kGroups>(d, bits, grid, lds, st); break;
-        case 4: down_combine_ni<4, kGroups>(d, bits, grid, lds, st); break;
-        case 6: down_combine_ni<6, kGroups>(d, bits, grid, lds, st); break;
-        default: down_combine_ni<8, kGroups>(d, bits, grid, lds, st); break;
+        switch (gemv_ni(nb)) {
+        case 1: down_combine_ni<1, kJobWaves>(d, bits, grid, lds, st); break;
+        case 2: down_combine_ni<2, kJobWaves>(d, bits, grid, lds, st); break;
+        case 4: down_combine_ni<4, kJobWaves>(d, bits, grid, lds, st); break;
+        case 6: down_combine_ni<6, kJobWaves>(d, bits, grid, lds, st); break;
+        default: down_combine_ni<8, kJobWaves>(d, bits, grid, lds, st); break;
         }
     }
     return hipGetLastError();

@@ -17,9 +17,8 @@
  * see qdot.h) and activations in the matching operand order; the 2^(8-b)
  * factor is taken out of the block scale (exact whenever d * 2^-(8-b) is a
  * normal number; a K step holding any other scale shifts the partials back
- * instead).  The fp32 fold is the canonical one: four consecutive block
- * groups, each from +0 in ascending block order, group sums added in order,
- * then the row scale.
+ * instead).  The fp32 fold is the canonical one: one chain per (row, token)
+ * from +0 over the blocks in ascending order, then the row scale.
  *
  * Memory pipeline.  A K step is 128 bytes of every weight row (8 blocks of
  * int4 / int2 half that, 4 blocks of int8) and the matching activation
@@ -367,28 +366,14 @@ __device__ __forceinline__ void block_mfma_grouped(const KLds<BITS, true>& S, in
     }
 }
 
-template <int NT>
-__device__ __forceinline__ void flush(float (&acc)[2][4], float (&tot)[2][4])
-{
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            tot[n][v] = tot[n][v] + acc[n][v];
-            acc[n][v] = 0.0f;
-        }
-}
-
-/* Multiplies one K step out of LDS buffer `buf` into acc / tot (NT N-tiles).
+/* Multiplies one K step out of LDS buffer `buf` into acc (NT N-tiles).
  *
- * The common step -- all kStep blocks inside the row, no canonical group
- * boundary strictly inside it, every scale exact after the 2^-(8-b) factor --
- * runs as straight-line code (a boundary at its first block is flushed
- * before it).  Any other step checks each block: the row end, the group
- * boundaries (a repeated boundary adds +0) and the shift-back fold. */
+ * The common step -- all kStep blocks inside the row, every scale exact
+ * after the 2^-(8-b) factor -- runs as straight-line code.  Any other step
+ * checks each block: the row end and the shift-back fold. */
 template <int BITS, int NT, bool GROUPED>
-__device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int st, int nb, int bnd1,
-                                     int bnd2, int bnd3, float (&acc)[2][4], float (&tot)[2][4], int gb)
+__device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int st, int nb, float (&acc)[2][4],
+                                     int gb)
 {
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -399,42 +384,25 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
         return;
     if constexpr (GROUPED) {
         if (gb) {
-            const bool inner_g = (bnd1 > b0 && bnd1 < b1) || (bnd2 > b0 && bnd2 < b1) || (bnd3 > b0 && bnd3 < b1);
-            if (b1 <= nb && !inner_g) {
-                if (b0 == bnd1 || b0 == bnd2 || b0 == bnd3)
-                    flush<NT>(acc, tot);
+            if (b1 <= nb) {
 #pragma unroll
                 for (int j = 0; j < C::kStep; ++j)
                     block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc);
                 return;
             }
-            for (int j = 0; j < C::kStep; ++j) {
-                const int b = b0 + j;
-                if (b >= nb)
-                    break;
-                if (b == bnd1 || b == bnd2 || b == bnd3)
-                    flush<NT>(acc, tot);
+            for (int j = 0; j < C::kStep && b0 + j < nb; ++j)
                 block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc);
-            }
             return;
         }
     }
     const bool exact_shift = BITS != 8 && __builtin_amdgcn_readfirstlane(S.flag[buf]) == st;
-    const bool inner = (bnd1 > b0 && bnd1 < b1) || (bnd2 > b0 && bnd2 < b1) || (bnd3 > b0 && bnd3 < b1);
-    if (b1 <= nb && !inner && !exact_shift) {
-        if (b0 == bnd1 || b0 == bnd2 || b0 == bnd3)
-            flush<NT>(acc, tot);
+    if (b1 <= nb && !exact_shift) {
 #pragma unroll
         for (int j = 0; j < C::kStep; ++j)
             block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc);
         return;
     }
-    for (int j = 0; j < C::kStep; ++j) {
-        const int b = b0 + j;
-        if (b >= nb)
-            break;
-        if (b == bnd1 || b == bnd2 || b == bnd3)
-            flush<NT>(acc, tot);
+    for (int j = 0; j < C::kStep && b0 + j < nb; ++j) {
         if (exact_shift)
             block_mfma<BITS, NT, true>(S, buf, j, arow, r, g, acc);
         else
@@ -442,7 +410,7 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
     }
 }
 
-/* The K loop shared by both kernels, for NT N-tiles.  Leaves in tot[n][v]
+/* The K loop shared by both kernels, for NT N-tiles.  Leaves in acc[n][v]
  * the folded sums of row dot 16w + 4(lane/16) + v for token 16n + lane%16.
  *
  * Step st is multiplied out of LDS buffer st & 1.  While an even step is
@@ -452,19 +420,15 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
  * so the two register sets stay put across iterations and each commit waits
  * only for its own loads. */
 template <int BITS, int NT, bool GROUPED>
-__device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane& L, float (&tot)[2][4])
+__device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane& L, float (&acc)[2][4])
 {
     using C = Cfg<BITS>;
     const int nb = L.nb;
-    const int bnd1 = nb / 4, bnd2 = (2 * nb) / 4, bnd3 = (3 * nb) / 4;
-    float acc[2][4];
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < 4; ++v)
             acc[n][v] = 0.0f;
-            tot[n][v] = -0.0f; /* -0 + s == s: the first flush leaves group 0's sum as is */
-        }
     const int nsteps = (nb + C::kStep - 1) / C::kStep;
     Stage<BITS, GROUPED> P0, P1;
     fetch<BITS, GROUPED>(P0, L, 0);
@@ -476,38 +440,32 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane
     fetch<BITS, GROUPED>(P0, L, 2);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
-        step<BITS, NT, GROUPED>(S, 0, st, nb, bnd1, bnd2, bnd3, acc, tot, L.gb);
+        step<BITS, NT, GROUPED>(S, 0, st, nb, acc, L.gb);
         commit<BITS, GROUPED>(P1, S, 1, st + 1);
         fetch<BITS, GROUPED>(P1, L, st + 3);
         __syncthreads();
-        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, bnd1, bnd2, bnd3, acc, tot, L.gb);
+        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, acc, L.gb);
         commit<BITS, GROUPED>(P0, S, 0, st + 2);
         fetch<BITS, GROUPED>(P0, L, st + 4);
         __syncthreads();
     }
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            tot[n][v] = tot[n][v] + acc[n][v];
 }
 
 template <int BITS, bool GROUPED>
 __device__ __forceinline__ void mfma_k_loop(KLds<BITS, GROUPED>& S, const LoadLane& L, int ntiles,
-                                            float (&tot)[2][4])
+                                            float (&acc)[2][4])
 {
     if (ntiles > 1)
-        k_loop_nt<BITS, 2, GROUPED>(S, L, tot);
+        k_loop_nt<BITS, 2, GROUPED>(S, L, acc);
     else
-        k_loop_nt<BITS, 1, GROUPED>(S, L, tot);
+        k_loop_nt<BITS, 1, GROUPED>(S, L, acc);
 }
 
 /* ---- the aligned K loop ----------------------------------------------------
  *
- * For rows whose four canonical block groups are each a whole, even number
- * of K steps (nb a multiple of 8 * kStep: H = 6144 and I = 2048 both are),
- * with per-row weight scales.  Groups become loop boundaries, so a step
- * never checks for a boundary or the row end.  Every load takes a uniform
+ * For rows of a whole, even number of K steps (nb a multiple of 2 kStep:
+ * H = 6144 and I = 2048 both are), with per-row weight scales, so a step
+ * never checks for the row end.  Every load takes a uniform
  * base (the wave's weight matrix, the activation arrays, advanced by the
  * step index) plus a fixed 32-bit per-thread offset, so a step's addressing
  * costs no vector instructions.  It always folds with the block scale times
@@ -517,7 +475,7 @@ __device__ __forceinline__ void mfma_k_loop(KLds<BITS, GROUPED>& S, const LoadLa
 template <int BITS>
 __device__ __forceinline__ bool lean_shape(int nb)
 {
-    return nb > 0 && nb % (8 * Cfg<BITS>::kStep) == 0;
+    return nb > 0 && nb % (2 * Cfg<BITS>::kStep) == 0;
 }
 
 struct LeanLane {
@@ -712,20 +670,16 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
  * stage and LDS buffer indices are compile-time.  (Three or four steps in
  * registers lowered the occupancy and were slower.)  Returns true
  * (uniformly) when some step's scales were not exact with the 2^-(8-b)
- * factor taken out; tot is then void. */
+ * factor taken out; acc is then void. */
 template <int BITS, int NT>
-__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&tot)[2][4])
+__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&acc)[2][4])
 {
     constexpr int D = 2, U = 2;
-    const int spg = L.nsteps / 4;
-    float acc[2][4];
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < 4; ++v)
             acc[n][v] = 0.0f;
-            tot[n][v] = -0.0f; /* -0 + s == s for every s: tot becomes group 0's sum exactly */
-        }
     Stage<BITS, false> P[D];
 #pragma unroll
     for (int k = 0; k < D; ++k)
@@ -733,43 +687,27 @@ __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L,
     bool bad = lean_commit<BITS, NT>(P[0], S, 0);
     lean_fetch<BITS, NT>(P[0], L, D);
     __syncthreads();
-    int next = spg; /* first step of the next canonical group */
 #pragma unroll 1
     for (int st = 0; st < L.nsteps; st += U) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int s = st + i;
-            if (s == next) {
-#pragma unroll
-                for (int n = 0; n < 2; ++n)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        tot[n][v] = tot[n][v] + acc[n][v];
-                        acc[n][v] = 0.0f;
-                    }
-                next += spg;
-            }
             lean_step<BITS, NT>(S, i & 1, acc);
             bad |= lean_commit<BITS, NT>(P[(i + 1) % D], S, (i + 1) & 1);
             lean_fetch<BITS, NT>(P[(i + 1) % D], L, s + 1 + D);
             __syncthreads();
         }
     }
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            tot[n][v] = tot[n][v] + acc[n][v];
     return __syncthreads_or(bad) != 0;
 }
 
 template <int BITS>
 __device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, int ntiles,
-                                                 float (&tot)[2][4])
+                                                 float (&acc)[2][4])
 {
     if (ntiles > 1)
-        return k_loop_lean<BITS, 2>(S, L, tot);
-    return k_loop_lean<BITS, 1>(S, L, tot);
+        return k_loop_lean<BITS, 2>(S, L, acc);
+    return k_loop_lean<BITS, 1>(S, L, acc);
 }
 
 } // namespace
@@ -805,7 +743,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
                    : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
-    float tot[2][4];
+    float acc[2][4];
     bool general = true;
     if constexpr (!GROUPED) {
         /* the aligned loop, while every activation offset fits 31 bits */
@@ -839,11 +777,11 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
                 LL.dof = (uint32_t)tk * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
             }
             LL.nsteps = nb / Cfg<BITS>::kStep;
-            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, tot);
+            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc);
         }
     }
     if (general)
-        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
+        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc);
 
     /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
      * h = silu(g) * u and one Q8_0 block of h per token */
@@ -855,7 +793,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
-                sm.e.v[rdot][16 * n + r] = sc * tot[n][v];
+                sm.e.v[rdot][16 * n + r] = sc * acc[n][v];
     }
     __syncthreads();
     /* thread: token t, elements 4q .. 4q+3 of the h block */
@@ -913,7 +851,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     L.wsrow = L.gb ? sg.down_s + ((int64_t)e * a.H + (row < a.H ? row : 0)) * (nb / L.gb) : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
-    float tot[2][4];
+    float acc[2][4];
     bool general = true;
     if constexpr (!GROUPED) {
         /* the aligned loop, while the weight offsets in one matrix fit 31 bits */
@@ -939,11 +877,11 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
                 LL.dof = (uint32_t)(td < ntok ? td : 0) * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
             }
             LL.nsteps = nb / Cfg<BITS>::kStep;
-            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, tot);
+            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc);
         }
     }
     if (general)
-        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, tot);
+        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc);
 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -953,7 +891,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
-                sm.e.v[rr][16 * n + r] = sc * tot[n][v];
+                sm.e.v[rr][16 * n + r] = sc * acc[n][v];
     }
     __syncthreads();
     /* thread: token t, rows 8q .. 8q+7 of the block */
