@@ -64,7 +64,9 @@ enum {
     COLI_E_INVAL = 1,       /* null pointer, negative size, bad dimension, k > E, ... */
     COLI_E_UNSUPPORTED = 2, /* qtype, misaligned pointer, size beyond a limit below */
     COLI_E_WORKSPACE = 3,   /* ws_bytes smaller than colibri_workspace_bytes() */
-    COLI_E_HIP = 4          /* the HIP runtime reported an error at launch */
+    COLI_E_HIP = 4,         /* the HIP runtime reported an error at launch */
+    COLI_E_SCRATCH = 5      /* colibri_moe_layer_forward_noalloc: the batch's workspace
+                               exceeds COLI_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Weight element width of a bank ([README] quantised-kernel item). */
@@ -239,6 +241,30 @@ int colibri_moe_layer_forward(const coli_moe_layer* L, const float* x, int32_t S
 int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, int32_t S, float* out,
                                      void* ws, size_t ws_bytes, coli_stream_t stream,
                                      void* const* stage_events);
+
+/*
+ * The same layer forward without a caller workspace and without any
+ * allocation, for callers that cannot allocate device memory around the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a static device array of
+ * COLI_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the
+ * process ends; its address on the current device is looked up once, on the
+ * first call on that device.  The call allocates nothing and frees nothing.
+ * x, out and the layer's tensors are as for colibri_moe_layer_forward and
+ * results are identical to it.
+ *   COLI_E_SCRATCH: colibri_workspace_bytes(L, S) > COLI_NOALLOC_SCRATCH_BYTES
+ *                   (a batch that large needs colibri_moe_layer_forward); the
+ *                   check happens before anything is enqueued.
+ *   COLI_E_HIP:     the current device or the array's address could not be
+ *                   obtained.
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents (no call needs it cleared): calls that may overlap on one
+ * GPU -- on different streams, or from different host threads -- race and
+ * must be serialised by the caller.
+ */
+#define COLI_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int colibri_moe_layer_forward_noalloc(const coli_moe_layer* L, const float* x, int32_t S, float* out,
+                                      coli_stream_t stream);
 
 /* ===========================================================================
  * Tiered expert residency ([README] section "思路" (idea): the routed experts

@@ -20,7 +20,8 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcolibri.so")
 
-COLI_OK, COLI_E_INVAL, COLI_E_UNSUPPORTED, COLI_E_WORKSPACE, COLI_E_HIP = 0, 1, 2, 3, 4
+COLI_OK, COLI_E_INVAL, COLI_E_UNSUPPORTED, COLI_E_WORKSPACE, COLI_E_HIP, COLI_E_SCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 16 << 20  # COLI_NOALLOC_SCRATCH_BYTES
 COLI_Q8, COLI_Q4, COLI_Q2 = 8, 4, 2
 COLI_N_STAGE_EVENTS = 6
 STAGES = ("route", "dispatch", "gate_up", "down", "combine")
@@ -79,6 +80,8 @@ def lib():
                                            ctypes.c_size_t, _vp]
         L.colibri_moe_layer_forward.restype = ctypes.c_int
         L.colibri_moe_layer_forward.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
+        L.colibri_moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.colibri_moe_layer_forward_noalloc.argtypes = [_vp, _vp, _i32, _vp, _vp]
         L.colibri_moe_layer_forward_staged.restype = ctypes.c_int
         L.colibri_moe_layer_forward_staged.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp,
                                                        _vp]
@@ -242,6 +245,16 @@ def moe_layer_forward(layer: MoELayer, x: torch.Tensor, out: Optional[torch.Tens
     ws = layer.workspace(S) if ws is None else ws
     _check(lib().colibri_moe_layer_forward(ctypes.byref(layer.desc), _ptr(x), S, _ptr(out), _ptr(ws),
                                            ws.numel(), _stream()), "colibri_moe_layer_forward")
+    return out
+
+
+def moe_layer_forward_noalloc(layer: MoELayer, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """out fp32 [S][hidden] = the layer applied to x, with the library's static
+    per-GPU scratch as workspace (no allocation by the call; out is the
+    caller's).  Batches whose workspace exceeds NOALLOC_SCRATCH_BYTES raise
+    with COLI_E_SCRATCH."""
+    _check(lib().colibri_moe_layer_forward_noalloc(ctypes.byref(layer.desc), _ptr(x), x.shape[0], _ptr(out),
+                                                   _stream()), "colibri_moe_layer_forward_noalloc")
     return out
 
 

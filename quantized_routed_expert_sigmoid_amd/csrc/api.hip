@@ -6,9 +6,41 @@
  */
 #include "layer.h"
 
+#include <mutex>
 #include <stdint.h>
 
 using namespace coli;
+
+namespace {
+
+/* Workspace of colibri_moe_layer_forward_noalloc: one static array per GPU
+ * (each device holds its own copy).  In host code `scratch` names a host-side
+ * stand-in, not device memory: only the address that hipGetSymbolAddress
+ * returns for the current device may reach a kernel or a copy. */
+static __device__ __align__(256) uint8_t scratch[COLI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_at[kMaxDevices]; /* the array's address on each device, once looked up */
+
+/* The array's address on the current device (looked up on the first call
+ * there, with that device current), or null. */
+void* scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_at[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        g_scratch_at[dev] = p;
+    }
+    return g_scratch_at[dev];
+}
+
+} // namespace
 
 
 extern "C" {
@@ -21,6 +53,7 @@ const char* colibri_status_string(int status)
     case COLI_E_UNSUPPORTED: return "unsupported argument (qtype, alignment or size limit)";
     case COLI_E_WORKSPACE: return "workspace too small";
     case COLI_E_HIP: return "HIP launch error";
+    case COLI_E_SCRATCH: return "batch workspace exceeds the static scratch of the allocation-free forward";
     default: return "unknown status";
     }
 }
@@ -325,6 +358,26 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         e = launch_combine(y, inv, ids, w, S, k, H, shared ? P : -1, out, s);
     e = mark(5, e);
     return hip_status(e);
+}
+
+int colibri_moe_layer_forward_noalloc(const coli_moe_layer* L, const float* x, int32_t S, float* out,
+                                      coli_stream_t stream)
+{
+    int st = check_layer(L);
+    if (st || (st = check_tokens(S, L->top_k)))
+        return st;
+    if (S == 0)
+        return COLI_OK;
+    if (!x || !out)
+        return COLI_E_INVAL;
+    const size_t need =
+        layer_layout(L->hidden, L->inter, L->n_experts, L->top_k, S, L->has_shared != 0).total;
+    if (need > COLI_NOALLOC_SCRATCH_BYTES)
+        return COLI_E_SCRATCH;
+    void* ws = scratch_address();
+    if (!ws)
+        return COLI_E_HIP;
+    return colibri_moe_layer_forward(L, x, S, out, ws, COLI_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 } // extern "C"

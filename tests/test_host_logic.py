@@ -80,13 +80,13 @@ def capi():
 def test_library_exports_every_declared_symbol(capi):
     lib = capi.lib()
     syms = _declared_symbols()
-    assert len(syms) == 26
+    assert len(syms) == 27
     for name in syms:
         assert hasattr(lib, name), name
 
 
 def test_status_strings(capi):
-    for code in range(5):
+    for code in range(6):
         assert capi.status_string(code)
     assert capi.status_string(99) == "unknown status"
 
