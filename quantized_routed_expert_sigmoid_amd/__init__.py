@@ -10,6 +10,7 @@ missing -- there is no other implementation to fall back to.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -19,6 +20,9 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcolibri.so")
+# the test-only build (include/colibri_debug.h): the same kernels, which also
+# dump the block partials of one requested slice
+DEBUG_LIB_PATH = os.path.join(PKG, "libcolibri_debug.so")
 
 COLI_OK, COLI_E_INVAL, COLI_E_UNSUPPORTED, COLI_E_WORKSPACE, COLI_E_HIP, COLI_E_SCRATCH = 0, 1, 2, 3, 4, 5
 NOALLOC_SCRATCH_BYTES = 16 << 20  # COLI_NOALLOC_SCRATCH_BYTES
@@ -58,58 +62,87 @@ def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m quantized_routed_expert_sigmoid_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        L.colibri_status_string.restype = ctypes.c_char_p
-        L.colibri_status_string.argtypes = [ctypes.c_int]
-        L.colibri_workspace_bytes.restype = ctypes.c_size_t
-        L.colibri_workspace_bytes.argtypes = [_vp, _i32]
-        L.colibri_expert_ffn_workspace_bytes.restype = ctypes.c_size_t
-        L.colibri_expert_ffn_workspace_bytes.argtypes = [_vp, _vp, _i32, _i32]
-        L.colibri_quantize_q8_0.restype = ctypes.c_int
-        L.colibri_quantize_q8_0.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp]
-        L.colibri_route.restype = ctypes.c_int
-        L.colibri_route.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-        L.colibri_moe_dispatch.restype = ctypes.c_int
-        L.colibri_moe_dispatch.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
-                                           ctypes.c_size_t, _vp]
-        L.colibri_expert_ffn_q.restype = ctypes.c_int
-        L.colibri_expert_ffn_q.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
-                                           ctypes.c_size_t, _vp]
-        L.colibri_moe_layer_forward.restype = ctypes.c_int
-        L.colibri_moe_layer_forward.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
-        L.colibri_moe_layer_forward_noalloc.restype = ctypes.c_int
-        L.colibri_moe_layer_forward_noalloc.argtypes = [_vp, _vp, _i32, _vp, _vp]
-        L.colibri_moe_layer_forward_staged.restype = ctypes.c_int
-        L.colibri_moe_layer_forward_staged.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp,
-                                                       _vp]
-        for name, res, args in [
-                ("colibri_cache_create", ctypes.c_int, [_i32, _i32, ctypes.POINTER(_vp)]),
-                ("colibri_cache_destroy", None, [_vp]),
-                ("colibri_cache_pin", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
-                ("colibri_cache_unpin", None, [_vp]),
-                ("colibri_cache_plan", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
-                ("colibri_cache_prefetch", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
-                ("colibri_tier_prefetch", ctypes.c_int, [_vp, _vp, _i32, _vp]),
-                ("colibri_cache_stats", ctypes.c_int, [_vp, _vp]),
-                ("colibri_cache_state", ctypes.c_int, [_vp, _vp, _vp]),
-                ("colibri_tier_slot_bytes", ctypes.c_size_t, [_vp, _i32]),
-                ("colibri_tier_create", ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t,
-                                                       ctypes.POINTER(_vp)]),
-                ("colibri_tier_destroy", None, [_vp]),
-                ("colibri_tier_stats", ctypes.c_int, [_vp, _vp, _vp]),
-                ("colibri_tier_state", ctypes.c_int, [_vp, _vp, _vp, _vp]),
-                ("colibri_tier_pin", ctypes.c_int, [_vp, _vp, _i32, _vp]),
-                ("colibri_tier_workspace_bytes", ctypes.c_size_t, [_vp, _i32]),
-                ("colibri_tier_forward", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t,
-                                                        _vp])]:
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def _load(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m quantized_routed_expert_sigmoid_amd.build`")
+    L = ctypes.CDLL(path)
+    L.colibri_status_string.restype = ctypes.c_char_p
+    L.colibri_status_string.argtypes = [ctypes.c_int]
+    L.colibri_workspace_bytes.restype = ctypes.c_size_t
+    L.colibri_workspace_bytes.argtypes = [_vp, _i32]
+    L.colibri_expert_ffn_workspace_bytes.restype = ctypes.c_size_t
+    L.colibri_expert_ffn_workspace_bytes.argtypes = [_vp, _vp, _i32, _i32]
+    L.colibri_quantize_q8_0.restype = ctypes.c_int
+    L.colibri_quantize_q8_0.argtypes = [_vp, _i32, _i32, _vp, _vp, _vp]
+    L.colibri_route.restype = ctypes.c_int
+    L.colibri_route.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.colibri_moe_dispatch.restype = ctypes.c_int
+    L.colibri_moe_dispatch.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+    L.colibri_expert_ffn_q.restype = ctypes.c_int
+    L.colibri_expert_ffn_q.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+    L.colibri_moe_layer_forward.restype = ctypes.c_int
+    L.colibri_moe_layer_forward.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
+    L.colibri_moe_layer_forward_noalloc.restype = ctypes.c_int
+    L.colibri_moe_layer_forward_noalloc.argtypes = [_vp, _vp, _i32, _vp, _vp]
+    L.colibri_moe_layer_forward_staged.restype = ctypes.c_int
+    L.colibri_moe_layer_forward_staged.argtypes = [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp,
+                                                   _vp]
+    for name, res, args in [
+            ("colibri_cache_create", ctypes.c_int, [_i32, _i32, ctypes.POINTER(_vp)]),
+            ("colibri_cache_destroy", None, [_vp]),
+            ("colibri_cache_pin", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
+            ("colibri_cache_unpin", None, [_vp]),
+            ("colibri_cache_plan", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+            ("colibri_cache_prefetch", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
+            ("colibri_tier_prefetch", ctypes.c_int, [_vp, _vp, _i32, _vp]),
+            ("colibri_cache_stats", ctypes.c_int, [_vp, _vp]),
+            ("colibri_cache_state", ctypes.c_int, [_vp, _vp, _vp]),
+            ("colibri_tier_slot_bytes", ctypes.c_size_t, [_vp, _i32]),
+            ("colibri_tier_create", ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t,
+                                                   ctypes.POINTER(_vp)]),
+            ("colibri_tier_destroy", None, [_vp]),
+            ("colibri_tier_stats", ctypes.c_int, [_vp, _vp, _vp]),
+            ("colibri_tier_state", ctypes.c_int, [_vp, _vp, _vp, _vp]),
+            ("colibri_tier_pin", ctypes.c_int, [_vp, _vp, _i32, _vp]),
+            ("colibri_tier_workspace_bytes", ctypes.c_size_t, [_vp, _i32]),
+            ("colibri_tier_forward", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t,
+                                                    _vp])]:
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_debug_lib = None
+DBG_GATE, DBG_UP, DBG_DOWN = 0, 1, 2
+
+
+@contextlib.contextmanager
+def debug_partials(out: torch.Tensor, kind: int, o0: int, o1: int, r0: int, r1: int, nb: int):
+    """Runs the calls in the block on the test-only library, which stores the
+    int32 block partials of matrix `kind` (DBG_GATE / DBG_UP / DBG_DOWN),
+    output rows [o0, o1), weight rows [r0, r1), blocks [0, nb) into out
+    (int32, device; see include/colibri_debug.h)."""
+    global _lib, _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+        _debug_lib.colibri_debug_partials.restype = ctypes.c_int
+        _debug_lib.colibri_debug_partials.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32]
+    assert out.dtype == torch.int32 and out.is_cuda and out.numel() >= (o1 - o0) * (r1 - r0) * nb
+    _check(_debug_lib.colibri_debug_partials(_ptr(out), kind, o0, o1, r0, r1, nb), "colibri_debug_partials")
+    saved, _lib = lib(), _debug_lib
+    try:
+        yield
+    finally:
+        _debug_lib.colibri_debug_partials(None, 0, 0, 0, 0, 0, 0)
+        _lib = saved
 
 
 def status_string(status: int) -> str:

@@ -1,4 +1,6 @@
-"""Builds libcolibri.so (the gfx950 HIP library behind include/colibri.h) in-tree.
+"""Builds libcolibri.so (the gfx950 HIP library behind include/colibri.h) in-tree,
+and libcolibri_debug.so, the same sources with COLI_DEBUG_PARTIALS (the
+test-only build of include/colibri_debug.h, which also dumps block partials).
 
     python -m quantized_routed_expert_sigmoid_amd.build
 """
@@ -13,8 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcolibri.so")
+DEBUG_LIB = os.path.join(PKG, "libcolibri_debug.so")
 
-SOURCES = ["api.hip", "q8_router.hip", "dispatch.hip", "ffn_gemv.hip", "ffn_mfma.hip", "tier.hip",
+SOURCES = ["ffn_gemv.hip", "ffn_mfma.hip", "api.hip", "q8_router.hip", "dispatch.hip", "tier.hip",
            "tier_kernels.hip", "expert_cache.cpp"]
 
 ARCH = "gfx950"
@@ -31,9 +34,11 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
 EXTRA = {"ffn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_debug.o" if debug else ".o"))
+    cmd = ["hipcc", *FLAGS, *(["-DCOLI_DEBUG_PARTIALS"] if debug else []), *EXTRA.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is expected
     noise = "'-packed-fp32-ops' is not a recognized feature"
@@ -45,18 +50,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compiles both libraries (the largest sources first, so that the two
+    builds of each run side by side)."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, debug) for src in SOURCES for debug in (False, True)]
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link([o for o, (_, d) in zip(objs, jobs) if not d], LIB)
+    _link([o for o, (_, d) in zip(objs, jobs) if d], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEBUG_LIB}")
     return LIB
 
 

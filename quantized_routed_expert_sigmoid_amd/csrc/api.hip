@@ -42,6 +42,11 @@ void* scratch_address()
 
 } // namespace
 
+#ifdef COLI_DEBUG_PARTIALS
+namespace coli {
+DebugSlice g_debug_slice = {nullptr, 0, 0, 0, 0, 0, 0};
+}
+#endif
 
 extern "C" {
 
@@ -180,6 +185,7 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
     ul.max_munits = ffn_max_munits(rows, n_mat);
     hipError_t e = launch_schedule(expert_offsets, n_mat, ul, s);
     FfnArgs a;
+    debug_attach(a);
     a.seg[0] = make_seg(gate, up, down, sorted_pairs, &ul, k, S, rows, 0);
     a.seg[1] = a.seg[0];
     a.nseg = 1;
@@ -248,6 +254,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         return hipEventRecord((hipEvent_t)stage_events[i], s);
     };
     FfnArgs a;
+    debug_attach(a);
     a.seg[0] = make_seg(&L->gate, &L->up, &L->down, sorted, &ul, k, S, P, 0);
     a.nseg = 1;
     a.unit_tokens = S == 1 ? 1 : kUnitTokens; /* distinct experts per token */
@@ -379,5 +386,15 @@ int colibri_moe_layer_forward_noalloc(const coli_moe_layer* L, const float* x, i
         return COLI_E_HIP;
     return colibri_moe_layer_forward(L, x, S, out, ws, COLI_NOALLOC_SCRATCH_BYTES, stream);
 }
+
+#ifdef COLI_DEBUG_PARTIALS
+int colibri_debug_partials(int32_t* out, int32_t kind, int32_t o0, int32_t o1, int32_t r0, int32_t r1, int32_t nb)
+{
+    if (out && (kind < kDbgGate || kind > kDbgDown || o1 < o0 || r1 < r0 || nb < 0))
+        return COLI_E_INVAL;
+    g_debug_slice = DebugSlice{out, kind, o0, o1, r0, r1, nb};
+    return COLI_OK;
+}
+#endif
 
 } // extern "C"

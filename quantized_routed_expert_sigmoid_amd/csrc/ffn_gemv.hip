@@ -326,6 +326,13 @@ __host__ __device__ inline size_t dec_lds_bytes(int nb)
     return (size_t)(kJobWaves * dec_region() + 9 * dec_dlen(nb) + 64 + 64) * 4;
 }
 
+/* Output row, matrix kind and weight rows of a wave's rows 0..7 and 8..15,
+ * for the test-only partial dump. */
+struct DbgRows {
+    int64_t o;
+    int kind0, row0, kind8, row8;
+};
+
 /* The wave's 16 rows against one token (xal, dl: its staged activation
  * blocks and block scales); R holds items 0 .. 2NI - 1.  Returns on every
  * lane the chain of row (lane mod 16), before the row scale.  P: the wave's
@@ -334,7 +341,8 @@ __host__ __device__ inline size_t dec_lds_bytes(int nb)
 template <int BITS, int NI, bool GROUPED>
 __device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* rows0, uint32_t rowbytes, int rows_ok,
                                             int nb, const uint32_t* xal, float* P, const float* dl,
-                                            const float* ws0, int gb, const uint8_t* rows8 = nullptr)
+                                            const float* ws0, int gb, const FfnArgs& a, const DbgRows& dr,
+                                            const uint8_t* rows8 = nullptr)
 {
     constexpr int D = 2 * NI, N = 8 * NI;
     const int lane = threadIdx.x & 63, c = lane & 31, k = lane & 15;
@@ -353,7 +361,11 @@ __device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* ro
             xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
         }
         const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
-        P[ptile(2 * p + (lane >> 5), c)] = kChunk * i + c < nb ? (float)s : 0.0f;
+        const int row = 2 * p + (lane >> 5);
+        P[ptile(row, c)] = kChunk * i + c < nb ? (float)s : 0.0f;
+        if (row < rows_ok && kChunk * i + c < nb)
+            dbg_partial(a, row < 8 ? dr.kind0 : dr.kind8, dr.o, row < 8 ? dr.row0 + row : dr.row8 + row - 8,
+                        kChunk * i + c, s);
         if (n + D < N) /* resolved at compile time */
             item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, rows8);
         if (p == 7) {
@@ -436,7 +448,9 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         const float sc = (r < 8 ? sh.gate_s : sh.up_s)[8 * m + (r & 7)];
         dec_stage<BITS>(a.xq, a.xd, nb, dlen, lane, 64, xal, dl);
         wave_lds_sync();
-        const float v16 = dec_k_loop<BITS, NI, false>(R, g0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0, u0);
+        const DbgRows dr = {d.k, kDbgGate, 8 * m, kDbgUp, 8 * m};
+        const float v16 =
+            dec_k_loop<BITS, NI, false>(R, g0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0, a, dr, u0);
         const float v = sc * v16;
         const float up = __shfl(v, (lane & 7) + 8, kWave);
         if (lane < 8)
@@ -490,9 +504,12 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) +
                                       ((int64_t)e * a.I + rb * 32 + 16 * (wv & 1)) * (nb / sg.gu_gb)
                                 : nullptr;
-    const float v16 = GROUPED && sg.gu_gb
-                          ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, ws0, sg.gu_gb)
-                          : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0);
+    const int kd = wv < 2 ? kDbgGate : kDbgUp, r16 = rb * 32 + 16 * (wv & 1);
+    const DbgRows dr = {u, kd, r16, kd, r16 + 8};
+    const float v16 =
+        GROUPED && sg.gu_gb
+            ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, ws0, sg.gu_gb, a, dr)
+            : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0, a, dr);
     if (lane < 16)
         rsum[16 * wv + lane] = v16;
     __syncthreads();
@@ -542,9 +559,10 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     dec_stage<BITS>(a.hq + (int64_t)u * a.I, a.hd + (int64_t)u * nb, nb, dlen, threadIdx.x, 256, xal, dl);
     __syncthreads();
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(row0, a.H - 1)) * (nb / sg.d_gb) : nullptr;
+    const DbgRows dr = {u, kDbgDown, row0, kDbgDown, row0 + 8};
     const float v = GROUPED && sg.d_gb
-                        ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, ws0, sg.d_gb)
-                            : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, nullptr, 0);
+                        ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, ws0, sg.d_gb, a, dr)
+                        : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, nullptr, 0, a, dr);
     const int n = row0 + lane;
     if (lane < rows_ok)
         a.y[(int64_t)u * a.H + n] = (sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n]) * v;
@@ -579,7 +597,8 @@ constexpr size_t kLdsMax = 160 * 1024; /* LDS of one CU (gfx950) */
 template <int BITS, int NI, int TMAX, bool GROUPED>
 __device__ __forceinline__ float rows_k_loop(Ring<BITS, NI>& R, const uint8_t* rows0, uint32_t rowbytes, int rows_ok,
                                              int nb, int ntok, const uint32_t* xal, const float* dls, float* P,
-                                             const float* ws0, int gb)
+                                             const float* ws0, int gb, const FfnArgs& a, int64_t o0, int kind,
+                                             int wrow0)
 {
     constexpr int D = 2 * NI, N = 8 * NI;
     const int lane = threadIdx.x & 63, c = lane & 31, k = lane & 15;
@@ -602,6 +621,8 @@ __device__ __forceinline__ float rows_k_loop(Ring<BITS, NI>& R, const uint8_t* r
             const uint32_t xa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
             const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
             P[t * kTile + w] = b < nb ? (float)s : 0.0f;
+            if (b < nb && 2 * p + (lane >> 5) < rows_ok)
+                dbg_partial(a, kind, o0 + t, wrow0 + 2 * p + (lane >> 5), b, s);
         }
         if (n + D < N) /* resolved at compile time */
             item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, nullptr);
@@ -706,11 +727,13 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
     const int ng = sg.gu_gb ? nb / sg.gu_gb : 0;
     const float* ws0 = sg.gu_gb ? (wv < 2 ? sg.gate_s : sg.up_s) + ((int64_t)e * a.I + L.rb * 32 + rloc) * ng
                                 : nullptr;
+    const int64_t o0 = sg.out_base + pos0;
+    const int kd = wv < 2 ? kDbgGate : kDbgUp, wr0 = L.rb * 32 + rloc;
     const float v = GROUPED && sg.gu_gb
                         ? rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P, ws0,
-                                                            sg.gu_gb)
+                                                               sg.gu_gb, a, o0, kd, wr0)
                         : rows_k_loop<BITS, NI, TMAX, false>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P,
-                                                             nullptr, 0);
+                                                             nullptr, 0, a, o0, kd, wr0);
     /* job row of the wave's row k: gate rows 0..31, up rows 32..63 */
     const int t_l = lane >> 4;
     if (t_l < ntok)
@@ -776,11 +799,12 @@ __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
     rows_stage<BITS, TMAX>(xal, dls, nb, sd, ntok, act, scl);
     const int ng = sg.d_gb ? nb / sg.d_gb : 0;
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(first, a.H - 1)) * ng : nullptr;
+    const int64_t o0 = sg.out_base + pos0;
     const float v = GROUPED && sg.d_gb
                         ? rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P, ws0,
-                                                            sg.d_gb)
+                                                               sg.d_gb, a, o0, kDbgDown, first)
                         : rows_k_loop<BITS, NI, TMAX, false>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P,
-                                                             nullptr, 0);
+                                                             nullptr, 0, a, o0, kDbgDown, first);
     const int t_l = lane >> 4;
     if (t_l < ntok && (lane & 15) < rows_ok)
         a.y[(int64_t)(sg.out_base + pos0 + t_l) * a.H + n] = sc * v;
@@ -836,18 +860,22 @@ __device__ __forceinline__ void pair_load(PairLoad<BITS, NI>& L, const uint8_t* 
         load_block<BITS>(rp + (int64_t)min((lane & 31) + kChunk * i, nb - 1) * (4 * BITS), L.w[i]);
 }
 
-/* Exact partials of a loaded pair, as fp32, to P[row * sp + b]. */
+/* Exact partials of a loaded pair, as fp32, to P[row * sp + b] (o, wrow0:
+ * the unit and the pair's first down row, for the test-only dump). */
 template <int BITS, int NI>
 __device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const uint32_t (&xa)[NI][8], int nb,
-                                              float* P, int sp)
+                                              float* P, int sp, const FfnArgs& a, int o, int wrow0)
 {
     const int lane = threadIdx.x & 63;
     const int row = lane >> 5, c = lane & 31;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int b = c + kChunk * i;
-        if (b < nb)
-            P[row * sp + b] = (float)block_dot<BITS>(L.w[i], xa[i]);
+        if (b < nb) {
+            const int32_t s = block_dot<BITS>(L.w[i], xa[i]);
+            P[row * sp + b] = (float)s;
+            dbg_partial(a, kDbgDown, o, wrow0 + row, b, s);
+        }
     }
 }
 
@@ -1084,13 +1112,13 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
                                        rowbytes),
                             rowbytes, nb);
         dc_act<NI>(xal, j0, nb, xa);
-        pair_partials<BITS, NI>(A, xa, nb, P + 2 * j0 * sp, sp);
+        pair_partials<BITS, NI>(A, xa, nb, P + 2 * j0 * sp, sp, a, __builtin_amdgcn_readlane(u_l, j0), row0);
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, j2), __builtin_amdgcn_readlane(e_l, j2), row0,
                                        rowbytes),
                             rowbytes, nb);
         if (q + 1 < U) {
             dc_act<NI>(xal, j1, nb, xa);
-            pair_partials<BITS, NI>(B, xa, nb, P + 2 * j1 * sp, sp);
+            pair_partials<BITS, NI>(B, xa, nb, P + 2 * j1 * sp, sp, a, __builtin_amdgcn_readlane(u_l, j1), row0);
         }
         if (q == 0 && shared) {
             /* the shared expert (streamed first) is folded while the routed

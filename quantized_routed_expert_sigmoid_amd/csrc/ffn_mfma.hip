@@ -178,6 +178,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+/* Where a unit's MFMA results belong, for the test-only partial dump: row
+ * dot rd < split is weight row wlo + rd of kind klo, else whi + rd - split
+ * of kind khi (rows from wmax on do not exist); token t is output row o0 + t
+ * (tokens from ntok on do not exist). */
+struct MDbg {
+    int64_t o0;
+    int ntok, split, klo, khi, wlo, whi, wmax;
+};
+
+/* The exact partials of one MFMA result (N-tile n, block b; the weights
+ * entered as 2^shift times their values). */
+__device__ __forceinline__ void mdbg(const FfnArgs& a, const MDbg& m, const i32x4& c, int n, int b, int shift)
+{
+#ifdef COLI_DEBUG_PARTIALS
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = 16 * n + (lane & 15);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int rd = 16 * wv + 4 * (lane >> 4) + v;
+        const bool lo = rd < m.split;
+        const int wr = lo ? m.wlo + rd : m.whi + rd - m.split;
+        if (t < m.ntok && wr < m.wmax)
+            dbg_partial(a, lo ? m.klo : m.khi, m.o0 + t, wr, b, c[v] >> shift);
+    }
+#else
+    (void)a; (void)m; (void)c; (void)n; (void)b; (void)shift;
+#endif
+}
+
 /* One thread's share of a K step's global loads (GROUPED: also the
  * weight row's scales of its kBpt blocks). */
 template <int BITS, bool GROUPED = false>
@@ -313,7 +342,7 @@ __device__ __forceinline__ long a_operand(const uint32_t* w, int g)
 /* One block of a K step: the MFMA of each N-tile and its fold into acc. */
 template <int BITS, int NT, bool EXACT_SHIFT, class KL>
 __device__ __forceinline__ void block_mfma(const KL& S, int buf, int j, const uint32_t* arow,
-                                           int r, int g, float (&acc)[2][4])
+                                           int r, int g, float (&acc)[2][4], const FfnArgs& a, const MDbg& m, int b)
 {
     constexpr int SHIFT = 8 - BITS;
     const long A = a_operand<BITS>(arow + j * BITS, g);
@@ -323,6 +352,7 @@ __device__ __forceinline__ void block_mfma(const KL& S, int buf, int j, const ui
         const uint2 bw = *reinterpret_cast<const uint2*>(&S.b[buf][j][g][t][0]);
         const long B = (long)(((uint64_t)bw.y << 32) | bw.x);
         const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        mdbg(a, m, c, n, b, SHIFT);
         if constexpr (!EXACT_SHIFT) {
             const float d = S.ds[buf][j][t];
 #pragma unroll
@@ -343,7 +373,8 @@ __device__ __forceinline__ void block_mfma(const KL& S, int buf, int j, const ui
  * factor of the packed weights shifted back out). */
 template <int BITS, int NT>
 __device__ __forceinline__ void block_mfma_grouped(const KLds<BITS, true>& S, int buf, int j,
-                                                   const uint32_t* arow, int r, int g, float (&acc)[2][4])
+                                                   const uint32_t* arow, int r, int g, float (&acc)[2][4],
+                                                   const FfnArgs& a, const MDbg& m, int b)
 {
     using C = Cfg<BITS>;
     constexpr int SHIFT = 8 - BITS;
@@ -359,6 +390,7 @@ __device__ __forceinline__ void block_mfma_grouped(const KLds<BITS, true>& S, in
         const uint2 bw = *reinterpret_cast<const uint2*>(&S.b[buf][j][g][t][0]);
         const long B = (long)(((uint64_t)bw.y << 32) | bw.x);
         const i32x4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, i32x4{0, 0, 0, 0}, 0, 0, 0);
+        mdbg(a, m, c, n, b, SHIFT);
         const float d = S.dr[buf][j][t];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -373,7 +405,7 @@ __device__ __forceinline__ void block_mfma_grouped(const KLds<BITS, true>& S, in
  * checks each block: the row end and the shift-back fold. */
 template <int BITS, int NT, bool GROUPED>
 __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int st, int nb, float (&acc)[2][4],
-                                     int gb)
+                                     int gb, const FfnArgs& a, const MDbg& m)
 {
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -387,11 +419,11 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
             if (b1 <= nb) {
 #pragma unroll
                 for (int j = 0; j < C::kStep; ++j)
-                    block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc);
+                    block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
                 return;
             }
             for (int j = 0; j < C::kStep && b0 + j < nb; ++j)
-                block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc);
+                block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
             return;
         }
     }
@@ -399,14 +431,14 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
     if (b1 <= nb && !exact_shift) {
 #pragma unroll
         for (int j = 0; j < C::kStep; ++j)
-            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc);
+            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
         return;
     }
     for (int j = 0; j < C::kStep && b0 + j < nb; ++j) {
         if (exact_shift)
-            block_mfma<BITS, NT, true>(S, buf, j, arow, r, g, acc);
+            block_mfma<BITS, NT, true>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
         else
-            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc);
+            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
     }
 }
 
@@ -420,7 +452,8 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
  * so the two register sets stay put across iterations and each commit waits
  * only for its own loads. */
 template <int BITS, int NT, bool GROUPED>
-__device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane& L, float (&acc)[2][4])
+__device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane& L, float (&acc)[2][4],
+                                          const FfnArgs& a, const MDbg& m)
 {
     using C = Cfg<BITS>;
     const int nb = L.nb;
@@ -440,11 +473,11 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane
     fetch<BITS, GROUPED>(P0, L, 2);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
-        step<BITS, NT, GROUPED>(S, 0, st, nb, acc, L.gb);
+        step<BITS, NT, GROUPED>(S, 0, st, nb, acc, L.gb, a, m);
         commit<BITS, GROUPED>(P1, S, 1, st + 1);
         fetch<BITS, GROUPED>(P1, L, st + 3);
         __syncthreads();
-        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, acc, L.gb);
+        step<BITS, NT, GROUPED>(S, 1, st + 1, nb, acc, L.gb, a, m);
         commit<BITS, GROUPED>(P0, S, 0, st + 2);
         fetch<BITS, GROUPED>(P0, L, st + 4);
         __syncthreads();
@@ -453,12 +486,12 @@ __device__ __forceinline__ void k_loop_nt(KLds<BITS, GROUPED>& S, const LoadLane
 
 template <int BITS, bool GROUPED>
 __device__ __forceinline__ void mfma_k_loop(KLds<BITS, GROUPED>& S, const LoadLane& L, int ntiles,
-                                            float (&acc)[2][4])
+                                            float (&acc)[2][4], const FfnArgs& a, const MDbg& m)
 {
     if (ntiles > 1)
-        k_loop_nt<BITS, 2, GROUPED>(S, L, acc);
+        k_loop_nt<BITS, 2, GROUPED>(S, L, acc, a, m);
     else
-        k_loop_nt<BITS, 1, GROUPED>(S, L, acc);
+        k_loop_nt<BITS, 1, GROUPED>(S, L, acc, a, m);
 }
 
 /* ---- the aligned K loop ----------------------------------------------------
@@ -643,7 +676,8 @@ __device__ __forceinline__ void lean_fold(const LeanOps<BITS, NT>& o, const i32x
  * folded, so neither an LDS read nor an MFMA result is waited for right
  * before its use. */
 template <int BITS, int NT>
-__device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float (&acc)[2][4])
+__device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float (&acc)[2][4], const FfnArgs& a,
+                                          const MDbg& m, int st)
 {
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -657,8 +691,12 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
         if (j + 1 < C::kStep)
             lean_read<BITS, NT>(S, buf, j + 1, arow, r, g, o[(j + 1) % 3]);
         __builtin_amdgcn_sched_barrier(0);
-        if (j < C::kStep)
+        if (j < C::kStep) {
             lean_mfma<BITS, NT>(o[j % 3], g, c[j & 1]);
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                mdbg(a, m, c[j & 1][n], n, st * C::kStep + j, 8 - BITS);
+        }
         if (j >= 1)
             lean_fold<BITS, NT>(o[(j - 1) % 3], c[(j - 1) & 1], acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -672,7 +710,8 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
  * (uniformly) when some step's scales were not exact with the 2^-(8-b)
  * factor taken out; acc is then void. */
 template <int BITS, int NT>
-__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&acc)[2][4])
+__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&acc)[2][4],
+                                            const FfnArgs& a, const MDbg& m)
 {
     constexpr int D = 2, U = 2;
 #pragma unroll
@@ -692,7 +731,7 @@ __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L,
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int s = st + i;
-            lean_step<BITS, NT>(S, i & 1, acc);
+            lean_step<BITS, NT>(S, i & 1, acc, a, m, s);
             bad |= lean_commit<BITS, NT>(P[(i + 1) % D], S, (i + 1) & 1);
             lean_fetch<BITS, NT>(P[(i + 1) % D], L, s + 1 + D);
             __syncthreads();
@@ -703,11 +742,11 @@ __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L,
 
 template <int BITS>
 __device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, int ntiles,
-                                                 float (&acc)[2][4])
+                                                 float (&acc)[2][4], const FfnArgs& a, const MDbg& m)
 {
     if (ntiles > 1)
-        return k_loop_lean<BITS, 2>(S, L, acc);
-    return k_loop_lean<BITS, 1>(S, L, acc);
+        return k_loop_lean<BITS, 2>(S, L, acc, a, m);
+    return k_loop_lean<BITS, 1>(S, L, acc, a, m);
 }
 
 } // namespace
@@ -743,6 +782,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
                    : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
+    const MDbg md = {sg.out_base + pos0, ntok, 32, kDbgGate, kDbgUp, M.rb * 32, M.rb * 32, a.I};
     float acc[2][4];
     bool general = true;
     if constexpr (!GROUPED) {
@@ -777,11 +817,11 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
                 LL.dof = (uint32_t)tk * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
             }
             LL.nsteps = nb / Cfg<BITS>::kStep;
-            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc);
+            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc, a, md);
         }
     }
     if (general)
-        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc);
+        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc, a, md);
 
     /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
      * h = silu(g) * u and one Q8_0 block of h per token */
@@ -851,6 +891,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     L.wsrow = L.gb ? sg.down_s + ((int64_t)e * a.H + (row < a.H ? row : 0)) * (nb / L.gb) : nullptr;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
+    const MDbg md = {sg.out_base + pos0, ntok, 64, kDbgDown, kDbgDown, M.rb * 64, M.rb * 64, a.H};
     float acc[2][4];
     bool general = true;
     if constexpr (!GROUPED) {
@@ -877,11 +918,11 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
                 LL.dof = (uint32_t)(td < ntok ? td : 0) * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
             }
             LL.nsteps = nb / Cfg<BITS>::kStep;
-            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc);
+            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc, a, md);
         }
     }
     if (general)
-        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc);
+        mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc, a, md);
 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {

@@ -90,7 +90,23 @@ __device__ __forceinline__ float group_coef(const float* ws, int gb, int b, floa
     return ws[b / gb] * d;
 }
 
+/* Test-only build (COLI_DEBUG_PARTIALS): the FFN kernels also store the
+ * exact int32 block partials they compute for one slice -- matrix kind
+ * (kDbgGate, kDbgUp, kDbgDown), output rows [o0, o1) of hq / y (sorted
+ * positions, or units of a one-token batch), weight rows [r0, r1), blocks
+ * below nb -- at out[((o - o0) * (r1 - r0) + (r - r0)) * nb + b].  In the
+ * product build FfnArgs carries no slice and the hook is empty. */
+enum { kDbgGate = 0, kDbgUp = 1, kDbgDown = 2 };
+
+struct DebugSlice {
+    int32_t* out; /* device; null: off */
+    int32_t kind, o0, o1, r0, r1, nb;
+};
+
 struct FfnArgs {
+#ifdef COLI_DEBUG_PARTIALS
+    DebugSlice dbg;
+#endif
     FfnSeg seg[2];
     int32_t nseg;
     int32_t unit_tokens; /* most tokens any GEMV unit holds: 1 or kUnitTokens */
@@ -101,6 +117,19 @@ struct FfnArgs {
     float* hd;        /* [rows][I/32] */
     float* y;         /* [rows][H] */
 };
+
+/* Stores partial s of (kind, output row o, weight row r, block b) when the
+ * slice holds it (test-only build). */
+__device__ __forceinline__ void dbg_partial(const FfnArgs& a, int kind, int64_t o, int r, int b, int32_t s)
+{
+#ifdef COLI_DEBUG_PARTIALS
+    const DebugSlice& d = a.dbg;
+    if (d.out && kind == d.kind && o >= d.o0 && o < d.o1 && r >= d.r0 && r < d.r1 && b >= 0 && b < d.nb)
+        d.out[((o - d.o0) * (int64_t)(d.r1 - d.r0) + (r - d.r0)) * d.nb + b] = s;
+#else
+    (void)a; (void)kind; (void)o; (void)r; (void)b; (void)s;
+#endif
+}
 
 /* One-token batch (decode): selection inside the gate/up kernel.  f.seg[0]
  * is the routed bank (n_mat = E), f.seg[1] the shared expert when

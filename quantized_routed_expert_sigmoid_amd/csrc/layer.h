@@ -185,6 +185,22 @@ inline T* at(void* ws, size_t off)
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+#ifdef COLI_DEBUG_PARTIALS
+/* The slice of block partials the FFN kernels store (test-only build; set by
+ * colibri_debug_partials). */
+extern DebugSlice g_debug_slice;
+#endif
+
+/* Hands the test-only build's partial slice to a launch (nothing otherwise). */
+inline void debug_attach(FfnArgs& a)
+{
+#ifdef COLI_DEBUG_PARTIALS
+    a.dbg = g_debug_slice;
+#else
+    (void)a;
+#endif
+}
+
 inline int hip_status(hipError_t e)
 {
     return e == hipSuccess ? COLI_OK : COLI_E_HIP;

@@ -266,6 +266,7 @@ hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const in
                                         sorted, at<int32_t>(ws, Lo.l.inv), at<int32_t>(ws, Lo.l.active),
                                         at<int32_t>(ws, Lo.l.n_active), ul, s);
     FfnArgs a;
+    debug_attach(a);
     a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], sorted, &ul, k, S, P, base);
     a.nseg = 1;
     a.unit_tokens = S == 1 ? 1 : kUnitTokens;
