@@ -1,20 +1,25 @@
 """Benchmark of one MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--only]
 
 A step is one colibri_moe_layer_forward (quantise, route, union dispatch,
 gate/up + SiLU + requant, down, combine) over one batch of synthetic tokens
-already resident in HBM.  The default workload is the S = 1 decode layer
-(H = 6144, 256 experts of I = 2048, top-8, packed int4, plus a shared
-expert).  To keep the 256 MB last-level cache from serving weights that a
-real model would have evicted, consecutive steps rotate over several copies
-of the layer at distinct addresses and over distinct token batches.
+already resident in HBM.  The headline workload (--workload, default the
+S = 1 decode layer: H = 6144, 256 experts of I = 2048, top-8, packed int4,
+plus a shared expert) is timed for K steps; unless --only is given, the other
+four workloads (tiny S = 8 int8, verify S = 4 int8, prefill S = 512 int4,
+skewed S = 2048 int2) follow with their own step counts.  To keep the 256 MB
+last-level cache from serving weights that a real model would have evicted,
+consecutive steps rotate over several copies of the layer at distinct
+addresses and over distinct token batches.
 
-Prints one JSON line with the throughput (routed tokens/s per layer), a
-roofline object for the dominant kernel (timed with HIP events recorded by
-the library between its stages on the benchmark's stream), a CPU baseline
-(the oracle, single-threaded, on a bounded sample), and the S = 512 prefill
-figure of the same layer.
+Prints one JSON line: the headline throughput (routed tokens/s per layer)
+with a roofline object for its dominant kernel (timed with HIP events
+recorded by the library between its stages on the benchmark's stream); per
+workload, tokens/s with its HBM, int8 matrix-core and VALU-fold rooflines and
+the binding one; the device's measured read-stream and int8 MFMA rates
+beside the published peaks; and per workload a CPU baseline (the oracle,
+single-threaded, pinned to one CPU, on a bounded sample of the batch).
 
     python bench.py --tier [--tier-fractions 1,0.5,0.25]
 
@@ -45,8 +50,7 @@ def parse():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--copies", type=int, default=16, help="layer copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--only", action="store_true", help="time only --workload (default: all five configs)")
     ap.add_argument("--tier", action="store_true",
                     help="tiered-residency sweep instead of the resident layer: routed experts in "
                          "pinned host memory behind an HBM slot bank (prints its own JSON line)")
@@ -175,7 +179,7 @@ def stage_kernel(w, stage):
     return f"ffn_{stage}_gemv<{w.bits},4> + ffn_{stage}_mfma<{w.bits}>"
 
 
-def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True):
+def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True, cpu_tokens=0):
     import numpy as np
     dev_layers = []
     base = synth.make_layer(w, device="cuda")
@@ -253,7 +257,12 @@ def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True)
         ids, _ = qre.route(dev_layers[0][0], x)
         uniq.append(len(set(ids.cpu().numpy().reshape(-1).tolist())))
     res["mean_unique_experts"] = float(np.mean([uniq[i % n_batches] for i in range(steps)]))
-    del dev_layers, base, xs, ws
+    del dev_layers, ws
+    torch.cuda.empty_cache()
+    if cpu_tokens:
+        xall = torch.cat(xs)  # the rotated batches: S = 1 decode draws its sample from several
+        res["cpu_baseline"] = cpu_baseline(synth, w, base, xall, min(cpu_tokens, xall.shape[0]))
+    del base, xs
     torch.cuda.empty_cache()
     return res
 
@@ -461,23 +470,143 @@ def run_tier_stack(qre, synth, torch, w, n_layers, steps):
     return out
 
 
-def cpu_baseline(synth, w, n_tokens):
-    """The oracle, as it stands, on n_tokens tokens of the same workload."""
+def cpu_info():
+    """Host CPU model, logical CPUs and physical cores (from /proc/cpuinfo)."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "nproc_allowed": len(os.sched_getaffinity(0)),
+            "physical_cores": len(cores) or None}
+
+
+def cpu_baseline(synth, w, Lg, x, n_tokens):
+    """The oracle, as it stands, on n_tokens tokens of the workload's batch x,
+    single-threaded, with this thread pinned to one CPU (the experts it needs
+    are copied from the device layer Lg; their generation is not timed)."""
     import oracle
     import numpy as np
-    x = synth.activations(w, S=n_tokens, tag="/cpu").numpy()
-    router_w, bias = synth.router_weights(w), synth.router_bias(w)
-    t0 = time.perf_counter()
-    ids, _, _ = oracle.route(x, router_w, bias, w.top_k, w.rsf)
-    t_route = time.perf_counter() - t0
-    needed = sorted(set(ids.reshape(-1).tolist()))
-    L = synth.make_layer(w, experts=needed, device="cpu")
-    t0 = time.perf_counter()
-    oracle.layer_forward(L, x)
-    t = time.perf_counter() - t0
+    xs = x[:n_tokens].cpu().numpy()
+    router_w, bias = Lg.router_w.cpu(), Lg.bias.cpu()
+    ids, _, _ = oracle.route(xs, router_w, bias, w.top_k, w.rsf)
+    needed = set(ids.reshape(-1).tolist())
+
+    def sub(b):
+        return synth.Bank(b.n_mat, b.rows, b.K, b.bits,
+                          [b.storage[m].cpu() if m in needed else None for m in range(b.n_mat)],
+                          [b.scale_storage[m].cpu() if m in needed else None for m in range(b.n_mat)],
+                          group=b.group)
+
+    def full(b):
+        return None if b is None else synth.Bank(1, b.rows, b.K, b.bits, [b.storage[0].cpu()],
+                                                 [b.scale_storage[0].cpu()], group=b.group)
+    L = synth.Layer(w, router_w, bias, sub(Lg.gate), sub(Lg.up), sub(Lg.down),
+                    full(Lg.sh_gate), full(Lg.sh_up), full(Lg.sh_down))
+    Lh = oracle.LayerHandle(L)
+    old = os.sched_getaffinity(0)
+    cpu = max(old)
+    os.sched_setaffinity(0, {cpu})
+    try:
+        t0 = time.perf_counter()
+        oracle.layer_forward(Lh, xs)
+        t = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, old)
+    ops = n_tokens * layer_ops(w)
+    info = cpu_info()
     return {"value": n_tokens / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tokens} tokens of the {w.name} workload through the single-threaded C oracle "
-                      f"(full layer per token; {t:.1f} s, router-only pass {t_route:.1f} s)"}
+            "GOPs": ops / t / 1e9, "pinned_cpu": cpu, **info,
+            "sample": f"{n_tokens} tokens of the {w.name} batches through the single-threaded C "
+                      f"oracle (full layer per token: router, {w.top_k} routed experts"
+                      + (" + shared expert" if w.has_shared else "") + f", combine), {t:.2f} s on one CPU"}
+
+
+def layer_ops(w):
+    """int8 multiply-add operations of one token's routed and shared experts (2 per MAC)."""
+    return 2 * (w.top_k + (1 if w.has_shared else 0)) * 3 * w.hidden * w.inter
+
+
+def fold_triples(w):
+    """(token, row, block) fp32 folds of one token: one fma per triple."""
+    n = w.top_k + (1 if w.has_shared else 0)
+    return n * (2 * w.inter * w.hidden // 32 + w.hidden * w.inter // 32)
+
+
+VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9  # lane operations per second (non-packed fp32)
+
+
+def device_peaks(torch, qre_probes):
+    """Achievable rates of this device: a 1 GiB nontemporal read stream and
+    int8 matrix-core loops (K = 32, the form the layer uses, and K = 64)."""
+    import ctypes
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
+    nbytes = buf.numel() * 4
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    read = {}
+    for blocked in (0, 1):
+        for blocks in (512, 1024, 2048, 4096, 8192):
+            args = (ctypes.c_void_p(buf.data_ptr()), nbytes, blocks, blocked, ctypes.c_void_p(sink.data_ptr()),
+                    ctypes.c_void_p(st))
+            assert qre_probes.colibri_probe_read(*args) == 0
+            e0.record()
+            reps = 5
+            for _ in range(reps):
+                qre_probes.colibri_probe_read(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            read[("blocked" if blocked else "grid_stride", blocks)] = \
+                reps * nbytes / (e0.elapsed_time(e1) / 1000.0) / 1e9
+    best = max(read, key=read.get)
+    del buf
+    mfma = {}
+    for k in (32, 64):
+        blocks, iters = 1024, 4096
+        qre_probes.colibri_probe_mfma_i8(k, 64, blocks, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st))
+        e0.record()
+        assert qre_probes.colibri_probe_mfma_i8(k, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                                ctypes.c_void_p(st)) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ops = blocks * 4 * iters * 8 * 16 * 16 * k * 2
+        mfma[k] = ops / (e0.elapsed_time(e1) / 1000.0) / 1e12
+    return {"hbm_read_stream_GBps": read[best], "read_stream_best": f"{best[0]}, {best[1]} workgroups",
+            "int8_mfma_k32_TOPS": mfma[32], "int8_mfma_k64_TOPS": mfma[64],
+            "spec": {"hbm_GBps": HBM_PEAK_GBS, "int8_mfma_TOPS": INT8_PEAK_TOPS,
+                     "valu_lane_ops_per_s": VALU_PEAK_LANE_OPS},
+            "how": "read stream: 1 GiB read once per launch with 16-byte nontemporal loads, best of grid-stride and "
+                   "blocked layouts over 512..8192 workgroups; matrix cores: 1024 workgroups of 4 waves, 8 "
+                   "independent int8 MFMA chains per wave"}
+
+
+def load_probes():
+    import ctypes
+    path = os.path.join(ROOT, "quantized_routed_expert_sigmoid_amd", "libcolibri_probes.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m quantized_routed_expert_sigmoid_amd.build`")
+    L = ctypes.CDLL(path)
+    L.colibri_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    L.colibri_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    return L
 
 
 def main():
@@ -530,60 +659,123 @@ def main():
                          "copy_engine_probe": r["h2d_probe_GBps"]},
             "sweep": r["sweep"]}), flush=True)
         return
-    steps = args.steps or (2000 if w.S <= 8 else 50)
-    res = run_workload(qre, synth, torch, w, steps, args.warmup, args.copies)
-    ms = res["gpu_ms"] / steps
-    value = w.S * steps / (res["gpu_ms"] / 1000.0)
-    U = res["mean_unique_experts"] + (1 if w.has_shared else 0)
+    configs = [args.workload] if args.only else ["decode", "tiny", "verify", "prefill", "skewed"]
+    if args.workload not in configs:
+        configs.insert(0, args.workload)
+    per = {}
+    probes = load_probes()
+    peaks = device_peaks(torch, probes)
+    for name in configs:
+        wc = synth.WORKLOADS[name]
+        if args.group:
+            wc = synth.scaled(wc, group=args.group)
+        steps, warmup, copies = (args.steps, args.warmup, args.copies) if name == args.workload else \
+            DEFAULTS[name]
+        steps = steps or DEFAULTS[name][0]
+        print(f"bench: {name} S={wc.S} int{wc.bits}: {steps} steps over {copies} layer copies",
+              file=sys.stderr, flush=True)
+        cpu_n = 0 if args.no_cpu_baseline else CPU_TOKENS[name]
+        res = run_workload(qre, synth, torch, wc, steps, warmup, copies, cpu_tokens=cpu_n)
+        per[name] = config_summary(wc, res, peaks, copies)
+    w = synth.WORKLOADS[args.workload] if not args.group else synth.scaled(synth.WORKLOADS[args.workload],
+                                                                              group=args.group)
+    head = per[args.workload]
+    res_h = head.pop("_res")
+    stage_ms = res_h["stage_ms"]
+    U = res_h["mean_unique_experts"] + (1 if w.has_shared else 0)
     sb = stage_bytes(w, U, w.S)
-    stage_ms = res["stage_ms"]
-    dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    dom = max(("gate_up", "down"), key=lambda st: stage_ms[st])
     achieved = sb[dom] / (stage_ms[dom] / 1000.0) / 1e9
-    layer_bytes = U * expert_bytes(w) + sb["route"] + sb["combine"]
     line = {
         "metric": "routed tokens/sec per MoE layer (S=1 decode, S=512 prefill); % HBM BW / % int8 MFMA",
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": ms,
-        "step_ms_quantiles": res["step_ms_quantiles"],
+        "ms_per_step": head["ms_per_step"],
+        "step_ms_quantiles": head["step_ms_quantiles"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded SplitMix64 weights and activations; no checkpoint)",
-        "config": {"workload": f"{w.name}: MoE layer H={w.hidden} I={w.inter} E={w.n_experts} "
-                               f"top-{w.top_k} int{w.bits} weights"
-                               + (f" with one scale per {w.group} columns" if w.group else "")
-                               + f" + shared expert, S={w.S}",
-                   "S": w.S, "weights": f"int{w.bits}", "layer_copies_rotated": args.copies,
-                   "parallelism": "single GPU"},
+        "config": {"workload": head["workload"], "S": w.S, "weights": f"int{w.bits}",
+                   "layer_copies_rotated": head["layer_copies_rotated"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": stage_kernel(w, dom), "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w, dom), "algorithmic_bytes": sb[dom]},
-        "layer": {"algorithmic_bytes": layer_bytes, "unique_routed_experts": res["mean_unique_experts"],
-                  "hbm_GBps_whole_layer": layer_bytes / (ms / 1000.0) / 1e9,
-                  "hbm_frac_whole_layer": layer_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
-                  "stage_ms": stage_ms},
+                     "traffic": measured_traffic(w, dom), "algorithmic_bytes": sb[dom],
+                     "frac_of_measured_read_stream": achieved / peaks["hbm_read_stream_GBps"]},
+        "layer": head["rooflines"],
+        "stage_ms": head["stage_ms"],
+        "device_peaks": peaks,
+        "configs": {CONFIG_IDS[n]: {k: v for k, v in per[n].items() if k != "_res"} for n in configs},
     }
-    if not args.no_prefill and args.workload == "decode":
-        wp = synth.scaled(synth.WORKLOADS["prefill"], group=args.group)
-        rp = run_workload(qre, synth, torch, wp, 20, 3, 2)
-        msp = rp["gpu_ms"] / 20
-        Up = rp["mean_unique_experts"] + 1
-        ops = 2 * wp.S * (wp.top_k + 1) * 3 * wp.hidden * wp.inter
-        bytes_p = Up * expert_bytes(wp) + stage_bytes(wp, Up, wp.S)["route"]
-        line["prefill"] = {"workload": f"prefill: same layer, S={wp.S}", "value": wp.S / (msp / 1000.0),
-                           "unit": "tokens/s", "ms_per_step": msp,
-                           "hbm_frac": bytes_p / (msp / 1000.0) / 1e9 / HBM_PEAK_GBS,
-                           "int8_mfma_frac": ops / (msp / 1000.0) / 1e12 / INT8_PEAK_TOPS,
-                           "stage_ms": rp["stage_ms"]}
-    if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or (40 if w.S <= 8 else 4)
-        line["cpu_baseline"] = cpu_baseline(synth, w, n)
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(line), flush=True)
+
+
+CONFIG_IDS = {"tiny": "C1_tiny", "decode": "C2_decode", "prefill": "C3_prefill", "verify": "C4_verify",
+              "skewed": "C5_skewed"}
+# steps, warmup, layer copies rotated per workload (batches whose weights fit
+# the 256 MB last-level cache rotate enough copies that the cache cannot
+# serve them)
+DEFAULTS = {"tiny": (2000, 50, 16), "decode": (2000, 20, 16), "verify": (500, 20, 4), "prefill": (30, 3, 2),
+            "skewed": (20, 3, 2)}
+CPU_TOKENS = {"tiny": 128, "decode": 8, "verify": 4, "prefill": 8, "skewed": 8}
+
+
+def config_summary(w, res, peaks, copies):
+    """Throughput of one workload and its rooflines: HBM (algorithmic bytes:
+    the touched experts, router, x and out), int8 matrix cores (2 per MAC of
+    every routed and shared expert row), VALU (one fp32 fold per token, row
+    and block); `binding` names the bound the workload meets first."""
+    steps = res["steps"]
+    ms = res["gpu_ms"] / steps
+    t = ms / 1000.0
+    U = res["mean_unique_experts"] + (1 if w.has_shared else 0)
+    sb = stage_bytes(w, U, w.S)
+    layer_bytes = U * expert_bytes(w) + sb["route"] + sb["combine"]
+    ops = w.S * layer_ops(w)
+    triples = w.S * fold_triples(w)
+    bounds = {"hbm": layer_bytes / (HBM_PEAK_GBS * 1e9), "int8_mfma": ops / (INT8_PEAK_TOPS * 1e12),
+              "valu_fold": triples / VALU_PEAK_LANE_OPS}
+    binding = max(bounds, key=bounds.get)
+    if bounds[binding] < 10e-6:
+        binding = "latency"  # every bound below 10 us: launches and round trips dominate
+    stage_ms = dict(res["stage_ms"])
+    extra = {}
+    if w.S == 1:
+        # one token: the selection runs inside gate/up and the combine inside
+        # down, so those two stages are empty; what they show is the cost of
+        # the event pair
+        extra["event_pair_overhead_ms"] = 0.5 * (stage_ms.pop("dispatch") + stage_ms.pop("combine"))
+        stage_ms["gate_up_with_selection"] = stage_ms.pop("gate_up")
+        stage_ms["down_with_combine"] = stage_ms.pop("down")
+    return {
+        "workload": f"{w.name}: MoE layer H={w.hidden} I={w.inter} E={w.n_experts} top-{w.top_k} int{w.bits} "
+                    "weights" + (f" with one scale per {w.group} columns" if w.group else "")
+                    + (" + shared expert" if w.has_shared else "") + f", S={w.S}",
+        "value": w.S / t, "unit": "tokens/s", "ms_per_step": ms, "us_per_step": 1000.0 * ms, "steps": steps,
+        "layer_copies_rotated": copies, "step_ms_quantiles": res["step_ms_quantiles"],
+        "unique_routed_experts": res["mean_unique_experts"],
+        "rooflines": {
+            "hbm": {"algorithmic_bytes": layer_bytes, "achieved_GBps": layer_bytes / t / 1e9,
+                    "frac": layer_bytes / t / 1e9 / HBM_PEAK_GBS,
+                    "frac_of_measured_read_stream": layer_bytes / t / 1e9 / peaks["hbm_read_stream_GBps"],
+                    "time_at_peak_ms": 1000.0 * bounds["hbm"]},
+            "int8_mfma": {"ops": ops, "achieved_TOPS": ops / t / 1e12, "frac": ops / t / 1e12 / INT8_PEAK_TOPS,
+                          "frac_of_measured_k32": ops / t / 1e12 / peaks["int8_mfma_k32_TOPS"],
+                          "time_at_peak_ms": 1000.0 * bounds["int8_mfma"]},
+            "valu_fold": {"fold_triples": triples, "frac": triples / t / VALU_PEAK_LANE_OPS,
+                          "time_at_peak_ms": 1000.0 * bounds["valu_fold"],
+                          "note": "one lane operation per (token, row, block) fold at 256 CUs x 64 lanes x 2.4 GHz"},
+            "binding": binding},
+        "stage_ms": stage_ms, **extra,
+        **({"cpu_baseline": res["cpu_baseline"]} if "cpu_baseline" in res else {}),
+        "_res": res,
+    }
 
 
 if __name__ == "__main__":

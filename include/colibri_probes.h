@@ -1,0 +1,36 @@
+/*
+ * colibri_probes.h -- measurement kernels (libcolibri_probes.so) used by the
+ * benchmark to report achievable device rates beside the published MI355X
+ * peaks: an HBM read stream and an int8 matrix-core loop.  They compute
+ * nothing of the layer.  Pointers are device memory owned by the caller;
+ * work is enqueued on `stream` (a hipStream_t); returns 0, 1 for a bad
+ * argument (nothing enqueued), 4 for a launch error.
+ */
+#ifndef COLIBRI_PROBES_H
+#define COLIBRI_PROBES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads every byte of buf (bytes a multiple of 16, buf 16-byte aligned) once
+ * with 16-byte nontemporal loads from n_blocks workgroups of 256 threads:
+ * blocked != 0, workgroup b streams the b-th contiguous span; otherwise the
+ * grid strides over the buffer.  sink holds n_blocks words (written only in
+ * an unlikely case: it keeps the loads from being removed). */
+int colibri_probe_read(const void* buf, size_t bytes, int32_t n_blocks, int32_t blocked, uint32_t* sink,
+                       void* stream);
+
+/* n_blocks workgroups of four waves; each wave issues iters rounds of 8
+ * independent v_mfma_i32_16x16x{k}_i8 (k = 32 or 64), i.e. 8 * iters *
+ * 16 * 16 * k * 2 integer operations per wave.  sink: n_blocks words. */
+int colibri_probe_mfma_i8(int32_t k, int32_t iters, int32_t n_blocks, int32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcolibri.so")
 DEBUG_LIB = os.path.join(PKG, "libcolibri_debug.so")
+# measurement kernels of the benchmark (include/colibri_probes.h)
+PROBES_LIB = os.path.join(PKG, "libcolibri_probes.so")
+PROBES_SRC = "probes.hip"
 
 SOURCES = ["ffn_gemv.hip", "ffn_mfma.hip", "api.hip", "q8_router.hip", "dispatch.hip", "tier.hip",
            "tier_kernels.hip", "expert_cache.cpp"]
@@ -63,13 +66,14 @@ def build(verbose: bool = True) -> str:
     """Compiles both libraries (the largest sources first, so that the two
     builds of each run side by side)."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = [(src, debug) for src in SOURCES for debug in (False, True)]
+    jobs = [(src, debug) for src in SOURCES for debug in (False, True)] + [(PROBES_SRC, False)]
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, jobs))
-    _link([o for o, (_, d) in zip(objs, jobs) if not d], LIB)
+    _link([o for o, (src, d) in zip(objs, jobs) if not d and src != PROBES_SRC], LIB)
     _link([o for o, (_, d) in zip(objs, jobs) if d], DEBUG_LIB)
+    _link([o for o, (src, _) in zip(objs, jobs) if src == PROBES_SRC], PROBES_LIB)
     if verbose:
-        print(f"built {LIB} and {DEBUG_LIB}")
+        print(f"built {LIB}, {DEBUG_LIB} and {PROBES_LIB}")
     return LIB
 
 

@@ -1,0 +1,134 @@
+/*
+ * probes.hip -- measurement kernels behind include/colibri_probes.h: the
+ * achievable HBM read rate and int8 matrix-core rate of the device, measured
+ * beside the published peaks that the layer's roofline fractions use.  They
+ * compute nothing of the layer.
+ */
+#include "../../include/colibri_probes.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kReadUnroll = 8;
+
+/* Every 16-byte chunk of the buffer read once (nontemporal, as the layer's
+ * weight streams), kReadUnroll loads of a thread in flight at a time; the
+ * xor of all words keeps the loads alive and is stored only when it equals
+ * an unlikely value.  BLOCKED: workgroup b streams the b-th contiguous span
+ * of the buffer (kReadUnroll consecutive 4 KB pieces per round); otherwise
+ * the whole grid strides over the buffer. */
+template <bool BLOCKED>
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                         uint32_t* sink)
+{
+    uint32_t acc = 0;
+    size_t i, end, stride;
+    if constexpr (BLOCKED) {
+        const size_t span = (n16 + gridDim.x - 1) / gridDim.x;
+        i = (size_t)blockIdx.x * span + threadIdx.x;
+        end = min(n16, (size_t)(blockIdx.x + 1) * span);
+        stride = 256;
+    } else {
+        i = (size_t)blockIdx.x * 256 + threadIdx.x;
+        end = n16;
+        stride = (size_t)gridDim.x * 256;
+    }
+    for (; i + (kReadUnroll - 1) * stride < end; i += kReadUnroll * stride) {
+        u32x4 v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < end; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u)
+        sink[blockIdx.x] = acc;
+}
+
+constexpr int kChains = 8; /* independent accumulators per wave (covers the MFMA latency) */
+
+/* iters rounds of kChains independent int8 MFMAs per wave: K = 32 (one
+ * 32-element block per instruction, the form the layer's kernels use) or
+ * K = 64.  Each chain has operands and a start value of its own, so that
+ * the compiler cannot merge the chains into one dependent sequence. */
+template <int K>
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int32_t* sink)
+{
+    const int lane = threadIdx.x & 63;
+    i32x4 c[kChains];
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+        c[j] = i32x4{lane + j, 3 * j, lane ^ j, 7 + j};
+    if constexpr (K == 32) {
+        long a[kChains], b[kChains];
+#pragma unroll
+        for (int j = 0; j < kChains; ++j) {
+            a[j] = (long)(0x0102030401020304ull * (uint64_t)(lane + 1 + j));
+            b[j] = (long)(0x0403020104030201ull * (uint64_t)(lane + 3 + 2 * j));
+        }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kChains; ++j)
+                c[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[j], b[j], c[j], 0, 0, 0);
+        }
+    } else {
+        i32x4 a[kChains], b[kChains];
+#pragma unroll
+        for (int j = 0; j < kChains; ++j) {
+            a[j] = i32x4{lane + 1 + j, 0x01020304 + j, lane * 3, 7 ^ j};
+            b[j] = i32x4{0x04030201 ^ j, lane + 5, 11 + j, lane};
+        }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kChains; ++j)
+                c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], b[j], c[j], 0, 0, 0);
+        }
+    }
+    int32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+        s += c[j][0] ^ c[j][1] ^ c[j][2] ^ c[j][3];
+    if (s == 0x1F2E3D4C)
+        sink[blockIdx.x] = s;
+}
+
+} // namespace
+
+extern "C" {
+
+int colibri_probe_read(const void* buf, size_t bytes, int32_t n_blocks, int32_t blocked, uint32_t* sink,
+                       void* stream)
+{
+    if (!buf || !sink || n_blocks <= 0 || bytes % 16 != 0 || ((uintptr_t)buf % 16) != 0)
+        return 1;
+    if (blocked)
+        hipLaunchKernelGGL(probe_read_kernel<true>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream,
+                           static_cast<const u32x4*>(buf), bytes / 16, sink);
+    else
+        hipLaunchKernelGGL(probe_read_kernel<false>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream,
+                           static_cast<const u32x4*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int colibri_probe_mfma_i8(int32_t k, int32_t iters, int32_t n_blocks, int32_t* sink, void* stream)
+{
+    if (!sink || n_blocks <= 0 || iters <= 0 || (k != 32 && k != 64))
+        return 1;
+    if (k == 32)
+        hipLaunchKernelGGL(probe_mfma_kernel<32>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    else
+        hipLaunchKernelGGL(probe_mfma_kernel<64>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+} // extern "C"
