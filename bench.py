@@ -173,10 +173,10 @@ def stage_kernel(w, stage):
     """The kernel(s) one FFN stage launches for this workload."""
     if w.S == 1:
         return {"gate_up": f"ffn_gate_up_decode<{w.bits}> (top-k selection + gate/up GEMV)",
-                "down": f"ffn_down_decode<{w.bits}>"}[stage]
+                "down": f"ffn_down_combine_decode<{w.bits}> (down GEMV + weighted combine)"}[stage]
     if w.S < 8:
-        return f"ffn_{stage}_gemv<{w.bits},4>"
-    return f"ffn_{stage}_gemv<{w.bits},4> + ffn_{stage}_mfma<{w.bits}>"
+        return f"ffn_{stage}_rows<{w.bits}>"
+    return f"ffn_{stage}_rows<{w.bits}> + ffn_{stage}_mfma<{w.bits}>"
 
 
 def run_workload(qre, synth, torch, w, steps, warmup, copies, timed_stages=True, cpu_tokens=0):
@@ -379,11 +379,14 @@ def run_tier(qre, synth, torch, w, fractions, steps):
 
 
 def run_tier_stack(qre, synth, torch, w, n_layers, steps):
-    """A stack of n_layers tiered layers (one shared pinned store of routed
-    experts, a router per layer).  Synthetic residual stream: layer l + 1's
-    input is x_l + sigma * z_l.  With look-ahead, layer l + 1's experts are
-    prefetched from x_l (routed by layer l + 1's router) before layer l runs.
-    Measured per (routing, resident fraction, sigma, look-ahead, S)."""
+    """Verify steps through a stack of n_layers tiered layers (one shared
+    pinned store of routed experts, a router per layer), one
+    colibri_tier_verify_step per step.  Synthetic residual stream: layer
+    l + 1's input is x_l + sigma * z_l.  With look-ahead, layer l + 1's
+    experts are predicted from x_l inside the step.  Measured per (S,
+    routing, resident fraction, sigma, look-ahead): positions/s, expert hit
+    rate, loads, and the draft-union statistics (distinct experts per layer
+    and step, and the share of them the previous step also used)."""
     import numpy as np
     base = synth.make_layer(w, device="cuda")
     E, H = w.n_experts, w.hidden
@@ -407,6 +410,7 @@ def run_tier_stack(qre, synth, torch, w, n_layers, steps):
               "zipf": [synth.router_bias(synth.scaled(w, layer=f"{w.layer}/stack{l}", bias_kind="zipf")).cuda()
                        for l in range(n_layers)]}
     gen = torch.Generator(device="cuda")
+    nw = (E + 31) // 32
     out = []
     for S in (1, 4):
         for sigma in (0.5, 1.0):
@@ -415,15 +419,16 @@ def run_tier_stack(qre, synth, torch, w, n_layers, steps):
             xs = [torch.randn(n_tok, S, H, device="cuda", generator=gen)]
             for l in range(1, n_layers):
                 xs.append(xs[-1] + sigma * torch.randn(n_tok, S, H, device="cuda", generator=gen))
+            X = torch.stack(xs, dim=1).contiguous()  # [n_tok][n_layers][S][H]
+            del xs
             for kind in ("uniform", "zipf"):
                 layers = [qre.MoELayer(H, w.inter, E, w.top_k, w.rsf, routers[l], biases[kind][l], *routed, shared)
                           for l in range(n_layers)]
-                # recall of the look-ahead prediction over the timed tokens
+                # recall of the look-ahead prediction over the timed steps
                 hit = tot = 0
                 for l in range(n_layers - 1):
-                    xa = xs[l][64:].reshape(-1, H)
-                    pred, _ = qre.route(layers[l + 1], xa)
-                    act, _ = qre.route(layers[l + 1], xs[l + 1][64:].reshape(-1, H))
+                    pred, _ = qre.route(layers[l + 1], X[64:, l].reshape(-1, H).contiguous())
+                    act, _ = qre.route(layers[l + 1], X[64:, l + 1].reshape(-1, H).contiguous())
                     pr, ac = pred.cpu().numpy(), act.cpu().numpy()
                     for t in range(0, len(ac), S):
                         a = set(ac[t:t + S].reshape(-1).tolist())
@@ -433,40 +438,46 @@ def run_tier_stack(qre, synth, torch, w, n_layers, steps):
                 recall = hit / max(1, tot)
                 for f in (0.5, 0.75):
                     n_slots = int(round(f * E))
+                    rate = {}
                     for look in (False, True):
                         tiers = [qre.TieredLayer(layers[l], n_slots) for l in range(n_layers)]
                         ws = tiers[0].workspace(S)
-                        o = torch.empty(S, H, device="cuda")
-
-                        def token(i):
-                            for l in range(n_layers):
-                                if look and l + 1 < n_layers:
-                                    tiers[l + 1].prefetch(xs[l][i])
-                                tiers[l].forward(xs[l][i], o, ws)
+                        o = torch.empty(n_layers, S, H, device="cuda")
+                        mask = torch.zeros(n_layers, nw, dtype=torch.int32, device="cuda")
+                        st = torch.zeros(n_tok, n_layers, 2, dtype=torch.int32, device="cuda")
                         for i in range(64):
-                            token(i)
+                            qre.tier_verify_step(tiers, X[i], o, ws, mask, st[i], lookahead=look)
                         torch.cuda.synchronize()
                         s0 = [t.stats() for t in tiers]
                         t0 = time.perf_counter()
                         for i in range(64, 64 + steps):
-                            token(i)
+                            qre.tier_verify_step(tiers, X[i], o, ws, mask, st[i], lookahead=look)
                         torch.cuda.synchronize()
                         dt = time.perf_counter() - t0
                         s1 = [t.stats() for t in tiers]
                         d = {k: sum(b[k] - a[k] for a, b in zip(s0, s1))
                              for k in ("hits", "misses", "prefetch_loads")}
+                        u = st[64:64 + steps].cpu().numpy().astype(np.float64)
+                        union, reuse = u[..., 0], u[..., 1]
+                        rate[look] = steps * S / dt
                         out.append({"S": S, "sigma": sigma, "routing": kind, "resident_fraction": f,
                                     "lookahead": look, "recall": recall,
-                                    "tokens_per_s": steps * S / dt,
+                                    "tokens_per_s": rate[look],
                                     "ms_per_layer": 1000.0 * dt / (steps * n_layers),
                                     "expert_hit_rate": d["hits"] / max(1, d["hits"] + d["misses"]),
                                     "loads_per_token_layer": (d["misses"] + d["prefetch_loads"]) / (steps * S * n_layers),
-                                    "prefetch_loads_per_token_layer": d["prefetch_loads"] / (steps * S * n_layers)})
+                                    "prefetch_loads_per_token_layer": d["prefetch_loads"] / (steps * S * n_layers),
+                                    "union_per_layer_step": float(union.mean()),
+                                    "union_per_position": float(union.mean() / S),
+                                    "reuse_of_previous_step": float(reuse.sum() / max(1.0, union.sum())),
+                                    **({"speedup_vs_no_lookahead": rate[True] / rate[False]} if look else {})})
                         print(f"stack S={S} sigma={sigma} {kind} f={f} lookahead={look}: "
-                              f"{out[-1]['tokens_per_s']:.0f} tokens/s", file=sys.stderr, flush=True)
+                              f"{out[-1]['tokens_per_s']:.0f} positions/s, union {out[-1]['union_per_layer_step']:.1f}",
+                              file=sys.stderr, flush=True)
                         for t in tiers:
                             t.close()
                         del tiers, ws
+            del X
     return out
 
 
@@ -555,6 +566,7 @@ def device_peaks(torch, qre_probes):
     """Achievable rates of this device: a 1 GiB nontemporal read stream and
     int8 matrix-core loops (K = 32, the form the layer uses, and K = 64)."""
     import ctypes
+    import synth
     st = torch.cuda.current_stream().cuda_stream
     sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
     buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
@@ -576,6 +588,31 @@ def device_peaks(torch, qre_probes):
                 reps * nbytes / (e0.elapsed_time(e1) / 1000.0) / 1e9
     best = max(read, key=read.get)
     del buf
+    # the one-token kernels' weight read pattern alone, at the decode layer's
+    # sizes: gate+up and down of top_k + 1 experts, 16 rows per wave, 16
+    # copies rotated past the caches
+    wd = synth.WORKLOADS["decode"]
+    u = wd.top_k + (1 if wd.has_shared else 0)
+    pattern = {}
+    for name, rows, rowbytes in (("gate_up", 2 * wd.inter * u, wd.hidden * wd.bits // 8),
+                                 ("down", wd.hidden * u, wd.inter * wd.bits // 8)):
+        ni, waves = rowbytes // 512, rows // 16
+        nbytes = waves * 16 * rowbytes
+        copies = torch.ones(16 * nbytes // 4, dtype=torch.int32, device="cuda")
+        bases = [copies.data_ptr() + c * nbytes for c in range(16)]
+        for c in range(16):
+            assert qre_probes.colibri_probe_rows(ctypes.c_void_p(bases[c]), ni, waves, 1,
+                                                 ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)) == 0
+        reps = 64
+        e0.record()
+        for r in range(reps):
+            qre_probes.colibri_probe_rows(ctypes.c_void_p(bases[r % 16]), ni, waves, 1,
+                                          ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st))
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        pattern[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / us / 1e3}
+        del copies
     mfma = {}
     for k in (32, 64):
         blocks, iters = 1024, 4096
@@ -589,11 +626,14 @@ def device_peaks(torch, qre_probes):
         mfma[k] = ops / (e0.elapsed_time(e1) / 1000.0) / 1e12
     return {"hbm_read_stream_GBps": read[best], "read_stream_best": f"{best[0]}, {best[1]} workgroups",
             "int8_mfma_k32_TOPS": mfma[32], "int8_mfma_k64_TOPS": mfma[64],
+            "decode_read_pattern": pattern,
             "spec": {"hbm_GBps": HBM_PEAK_GBS, "int8_mfma_TOPS": INT8_PEAK_TOPS,
                      "valu_lane_ops_per_s": VALU_PEAK_LANE_OPS},
             "how": "read stream: 1 GiB read once per launch with 16-byte nontemporal loads, best of grid-stride and "
                    "blocked layouts over 512..8192 workgroups; matrix cores: 1024 workgroups of 4 waves, 8 "
-                   "independent int8 MFMA chains per wave"}
+                   "independent int8 MFMA chains per wave; decode read pattern: the one-token kernels' weight "
+                   "loads (items of 2 rows x 512 B, chunk-major, 16 rows per wave) with no arithmetic, at the "
+                   "decode layer's gate+up and down sizes, one launch each, 16 copies rotated"}
 
 
 def load_probes():
@@ -602,6 +642,8 @@ def load_probes():
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m quantized_routed_expert_sigmoid_amd.build`")
     L = ctypes.CDLL(path)
+    L.colibri_probe_rows.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
     L.colibri_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_void_p]
     L.colibri_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -636,7 +678,8 @@ def main():
         steps = args.steps or 100
         r = run_tier_stack(qre, synth, torch, w, args.stack_layers, steps)
         print(json.dumps({
-            "metric": "tiered layer-stack decode tokens/sec with and without router look-ahead prefetch",
+            "metric": "tiered layer-stack verify positions/sec with and without router look-ahead prefetch "
+                      "(one colibri_tier_verify_step per step), with draft-union statistics",
             "unit": "tokens/s", "n_gpus": 1, "steps": steps, "higher_is_better": True, "dtype": "int8",
             "data": "synthetic (seeded weights; residual stream x_l+1 = x_l + sigma * z_l; no checkpoint)",
             "config": {"workload": f"{args.stack_layers} layers of H={w.hidden} I={w.inter} E={w.n_experts} "
@@ -753,6 +796,14 @@ def config_summary(w, res, peaks, copies):
         extra["event_pair_overhead_ms"] = 0.5 * (stage_ms.pop("dispatch") + stage_ms.pop("combine"))
         stage_ms["gate_up_with_selection"] = stage_ms.pop("gate_up")
         stage_ms["down_with_combine"] = stage_ms.pop("down")
+        pat = peaks.get("decode_read_pattern", {})
+        if w.name == "decode" and pat:
+            # the same weight bytes read in the same pattern by a kernel that
+            # does nothing else: the launch-inclusive floor of each stage
+            extra["read_pattern_floor_ms"] = {k: v["us"] / 1000.0 for k, v in pat.items()}
+            extra["stage_frac_of_read_pattern"] = {
+                "gate_up": pat["gate_up"]["us"] / 1000.0 / stage_ms["gate_up_with_selection"],
+                "down": pat["down"]["us"] / 1000.0 / stage_ms["down_with_combine"]}
     return {
         "workload": f"{w.name}: MoE layer H={w.hidden} I={w.inter} E={w.n_experts} top-{w.top_k} int{w.bits} "
                     "weights" + (f" with one scale per {w.group} columns" if w.group else "")

@@ -447,6 +447,49 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
  */
 int colibri_tier_prefetch(coli_tier* t, const float* x, int32_t S, coli_stream_t stream);
 
+/*
+ * One step of batched verification through a stack of tiered layers: the
+ * S positions of one step (for speculative decoding, the last accepted
+ * token and its drafts, checked in one batched forward: "Show HN:
+ * 如何在我的低配置电脑上运行 GLM-5.2", section 已实现的功能, the native MTP
+ * item) pass through tiers[0 .. n_layers - 1] in order, each layer's
+ * forward being colibri_tier_forward's.
+ *   x    device fp32 [n_layers][S][hidden]: layer l's input.  The attention
+ *        and norms between the layers are not part of this library, so the
+ *        caller supplies every layer's input (recorded or synthetic
+ *        activations).
+ *   out  device fp32 [n_layers][S][hidden]: layer l's output, bit-identical
+ *        to colibri_tier_forward's and the resident forward's on x_l.
+ *   lookahead  nonzero: the router look-ahead of the same section (the
+ *        next layer's experts predicted from the current layer's input and
+ *        read while it computes): before layer l runs, layer l + 1's
+ *        router routes x_l on layer l + 1's copy stream and plans a
+ *        prefetch there (colibri_tier_prefetch's policy); its loads are
+ *        queued behind layer l's own misses, and layer l + 1's forward uses
+ *        them as colibri_tier_forward uses any prefetch.  Requires S <= 8.
+ *   union_mask, stats  both null (no statistics), or: union_mask device
+ *        uint32 [n_layers][(n_experts + 31) / 32], per layer the set of
+ *        experts the previous step routed to (zero it before the first
+ *        step; each step replaces it with its own), and stats device int32
+ *        [n_layers][2], per layer the number of distinct routed experts of
+ *        this step (the union its batched forward reads once) and how many
+ *        of them the previous step's set held.
+ *   ws   workspace of colibri_tier_workspace_bytes(tiers[0], S).
+ * Every tier has the same hidden, inter, n_experts, top_k and shared
+ * expert, appears once, and lives on the current device.  Calls are ordered
+ * on `stream` like colibri_tier_forward's and return without waiting for
+ * the device when every layer's misses fit two passes; work enqueued on
+ * `stream` after the call follows every read of x.  x and out are 16-byte
+ * aligned.  Returns COLI_E_INVAL for a null or repeated tier, differing
+ * shapes, null buffers (or one of union_mask and stats null) or another
+ * current device, COLI_E_UNSUPPORTED for misaligned buffers or look-ahead
+ * with S > 8, COLI_E_WORKSPACE for a short workspace; after COLI_E_HIP the
+ * tiers' states are unspecified.
+ */
+int colibri_tier_verify_step(coli_tier* const* tiers, int32_t n_layers, const float* x, int32_t S,
+                             float* out, int32_t lookahead, void* ws, size_t ws_bytes,
+                             uint32_t* union_mask, int32_t* stats, coli_stream_t stream);
+
 /* Statistics of the tier's cache (as colibri_cache_stats); waits for `stream`. */
 int colibri_tier_stats(const coli_tier* t, coli_cache_stats* st, coli_stream_t stream);
 

@@ -24,6 +24,14 @@ extern "C" {
 int colibri_probe_read(const void* buf, size_t bytes, int32_t n_blocks, int32_t blocked, uint32_t* sink,
                        void* stream);
 
+/* The one-token GEMV kernels' weight read pattern without their
+ * arithmetic: wave w reads 16 consecutive rows of 512 * ni bytes (ni = 2 or
+ * 6) starting at buf + 16 w * 512 * ni, in items of two rows by 512 bytes,
+ * chunk-major (chunk_major != 0) or row-major, 2 ni items in flight;
+ * n_waves waves in workgroups of four (buf holds n_waves * 16 rows). */
+int colibri_probe_rows(const void* buf, int32_t ni, int32_t n_waves, int32_t chunk_major, uint32_t* sink,
+                       void* stream);
+
 /* n_blocks workgroups of four waves; each wave issues iters rounds of 8
  * independent v_mfma_i32_16x16x{k}_i8 (k = 32 or 64), i.e. 8 * iters *
  * 16 * 16 * k * 2 integer operations per wave.  sink: n_blocks words. */

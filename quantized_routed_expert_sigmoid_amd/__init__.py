@@ -113,7 +113,9 @@ def _load(path: str):
             ("colibri_tier_pin", ctypes.c_int, [_vp, _vp, _i32, _vp]),
             ("colibri_tier_workspace_bytes", ctypes.c_size_t, [_vp, _i32]),
             ("colibri_tier_forward", ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.c_size_t,
-                                                    _vp])]:
+                                                    _vp]),
+            ("colibri_tier_verify_step", ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _i32, _vp,
+                                                        ctypes.c_size_t, _vp, _vp, _vp])]:
         f = getattr(L, name)
         f.restype = res
         f.argtypes = args
@@ -483,3 +485,19 @@ class TieredLayer:
         usage = (_u64 * E)()
         _check(lib().colibri_tier_state(self._h, slot_of, usage, _stream()), "colibri_tier_state")
         return list(slot_of), list(usage)
+
+
+def tier_verify_step(tiers: Sequence[TieredLayer], x: torch.Tensor, out: torch.Tensor, ws: torch.Tensor,
+                     union_mask: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
+                     lookahead: bool = True):
+    """One verify step through the tiers in order (colibri_tier_verify_step):
+    x [n_layers][S][hidden] per-layer inputs, out [n_layers][S][hidden];
+    union_mask int32 [n_layers][(E + 31) / 32] (zero before the first step)
+    and stats int32 [n_layers][2] (distinct experts of the step, and how many
+    of them the previous step used), both given or both None."""
+    n = len(tiers)
+    arr = (_vp * n)(*[t._h for t in tiers])
+    _check(lib().colibri_tier_verify_step(arr, n, _ptr(x), x.shape[1], _ptr(out), 1 if lookahead else 0,
+                                          _ptr(ws), ws.numel(), _ptr(union_mask), _ptr(stats), _stream()),
+           "colibri_tier_verify_step")
+    return out

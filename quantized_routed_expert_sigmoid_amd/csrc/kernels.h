@@ -307,6 +307,12 @@ hipError_t launch_tier_pin(const int32_t* experts, int32_t n, const TierState& s
 hipError_t launch_tier_fetch(const int4* loads, const int32_t* info, int32_t pass, const TierBanks& b,
                              hipStream_t s);
 
+/* Draft-union statistics of P routed ids (E <= kTierMaxE): stats[0] =
+ * distinct experts, stats[1] = how many of them the bit set mask
+ * [(E + 31) / 32] held; mask <- this set. */
+hipError_t launch_verify_union(const int32_t* ids, int32_t P, int32_t E, uint32_t* mask, int32_t* stats,
+                               hipStream_t s);
+
 hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t st);
 

@@ -55,6 +55,42 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
         sink[blockIdx.x] = acc;
 }
 
+/* The one-token GEMV kernels' read pattern without their arithmetic: wave w
+ * of the grid reads rows [16 w, 16 w + 16) of rowbytes = 512 NI bytes in
+ * items of two rows by 512 bytes (lane l: row 2p + l / 32, bytes
+ * 512 i + 16 (l mod 32)), item (chunk i, pair p) in chunk-major order (all
+ * pairs of chunk 0, then chunk 1, ...) or row-major order (all chunks of
+ * pair 0, then pair 1, ...), 2 NI items in flight. */
+template <int NI, bool CHUNK_MAJOR>
+__global__ __launch_bounds__(256) void probe_rows_kernel(const uint8_t* __restrict__ base, int n_waves,
+                                                         uint32_t* sink)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wave >= n_waves)
+        return;
+    const uint8_t* rows = base + (size_t)wave * 16 * (512 * NI);
+    constexpr int N = 8 * NI, D = 2 * NI;
+    auto addr = [&](int n) {
+        const int i = CHUNK_MAJOR ? n >> 3 : n % NI, p = CHUNK_MAJOR ? n & 7 : n / NI;
+        return reinterpret_cast<const u32x4*>(rows + (size_t)(2 * p + (lane >> 5)) * (512 * NI) + 512 * i +
+                                              16 * (lane & 31));
+    };
+    u32x4 ring[D];
+#pragma unroll
+    for (int n = 0; n < D; ++n)
+        ring[n] = __builtin_nontemporal_load(addr(n));
+    uint32_t acc = 0;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        acc ^= ring[n % D].x ^ ring[n % D].y ^ ring[n % D].z ^ ring[n % D].w;
+        if (n + D < N)
+            ring[n % D] = __builtin_nontemporal_load(addr(n + D));
+    }
+    if (acc == 0x9E3779B9u)
+        sink[blockIdx.x] = acc;
+}
+
 constexpr int kChains = 8; /* independent accumulators per wave (covers the MFMA latency) */
 
 /* iters rounds of kChains independent int8 MFMAs per wave: K = 32 (one
@@ -117,6 +153,28 @@ int colibri_probe_read(const void* buf, size_t bytes, int32_t n_blocks, int32_t 
     else
         hipLaunchKernelGGL(probe_read_kernel<false>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream,
                            static_cast<const u32x4*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int colibri_probe_rows(const void* buf, int32_t ni, int32_t n_waves, int32_t chunk_major, uint32_t* sink,
+                       void* stream)
+{
+    if (!buf || !sink || n_waves <= 0 || (ni != 2 && ni != 6) || ((uintptr_t)buf % 16) != 0)
+        return 1;
+    const dim3 grid((n_waves + 3) / 4), block(256);
+    const hipStream_t st = (hipStream_t)stream;
+    const uint8_t* b = static_cast<const uint8_t*>(buf);
+    if (ni == 6) {
+        if (chunk_major)
+            hipLaunchKernelGGL((probe_rows_kernel<6, true>), grid, block, 0, st, b, n_waves, sink);
+        else
+            hipLaunchKernelGGL((probe_rows_kernel<6, false>), grid, block, 0, st, b, n_waves, sink);
+    } else {
+        if (chunk_major)
+            hipLaunchKernelGGL((probe_rows_kernel<2, true>), grid, block, 0, st, b, n_waves, sink);
+        else
+            hipLaunchKernelGGL((probe_rows_kernel<2, false>), grid, block, 0, st, b, n_waves, sink);
+    }
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -174,6 +174,7 @@ struct coli_tier {
     hipEvent_t ev_issue = nullptr;    /* the caller's stream when a prefetch was issued */
     hipEvent_t ev_pfplan = nullptr;   /* after the last prefetch's plan */
     hipEvent_t ev_prefetch = nullptr; /* after the last prefetch's fetch */
+    hipEvent_t ev_copy_tail = nullptr; /* the copy stream's work so far (verify steps) */
     bool prefetch_pending = false;    /* a prefetch fetch no forward has waited for */
     int32_t* h_buf = nullptr;       /* pinned host staging */
     size_t h_cap = 0;               /* int32 entries */
@@ -198,6 +199,8 @@ struct coli_tier {
             (void)hipEventDestroy(ev_issue);
         if (ev_pfplan)
             (void)hipEventDestroy(ev_pfplan);
+        if (ev_copy_tail)
+            (void)hipEventDestroy(ev_copy_tail);
         if (h_buf)
             (void)hipHostFree(h_buf);
     }
@@ -332,6 +335,39 @@ int check_call(const coli_tier* t, const float* x, int32_t S, const float* out, 
     return COLI_OK;
 }
 
+/* First half of a look-ahead prefetch, on the tier's copy stream after the
+ * work enqueued on s so far (earlier forwards of this tier included) and
+ * after the previous prefetch (same stream): route x with this layer's
+ * router into the tier's own scratch and plan the prefetch on the state.
+ * ev_pfplan marks the end, after which x is no longer read. */
+hipError_t prefetch_plan(coli_tier* t, const float* x, int32_t S, hipStream_t s)
+{
+    hipError_t e = hipEventRecord(t->ev_issue, s);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(t->copy, t->ev_issue, 0);
+    if (e == hipSuccess)
+        e = route_into(t, x, S, t->pf_xq, t->pf_xd, t->pf_logits, t->pf_ids, t->pf_w, t->copy);
+    if (e == hipSuccess)
+        e = launch_tier_plan(t->pf_ids, S * t->L.top_k, t->st, nullptr, t->pf_loads, t->pf_info, nullptr, true,
+                             t->copy);
+    if (e == hipSuccess)
+        e = hipEventRecord(t->ev_pfplan, t->copy);
+    return e;
+}
+
+/* Second half: the planned loads, next on the copy stream; the tier's next
+ * forward waits for them (for the plan only, when its misses fit two
+ * passes: the loaded slots are then late hits, read after the loads). */
+hipError_t prefetch_loads(coli_tier* t)
+{
+    hipError_t e = launch_tier_fetch(t->pf_loads, t->pf_info, 1, t->banks, t->copy);
+    if (e == hipSuccess)
+        e = hipEventRecord(t->ev_prefetch, t->copy);
+    if (e == hipSuccess)
+        t->prefetch_pending = true;
+    return e;
+}
+
 } // namespace
 
 extern "C" {
@@ -422,6 +458,8 @@ int colibri_tier_create(const coli_moe_layer* L, int32_t n_slots, void* slot_mem
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&t->ev_pfplan, hipEventDisableTiming);
     if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&t->ev_copy_tail, hipEventDisableTiming);
+    if (e == hipSuccess)
         e = t->events(2);
     if (e == hipSuccess)
         e = launch_tier_init(t->st, t->copy);
@@ -506,26 +544,9 @@ int colibri_tier_prefetch(coli_tier* t, const float* x, int32_t S, coli_stream_t
     int st = check_current_device(t);
     if (st)
         return st;
-    hipStream_t s = (hipStream_t)stream;
-    /* everything runs on the copy stream, after what the caller has
-     * enqueued so far (earlier forwards of this tier included) and after the
-     * previous prefetch (same stream) */
-    hipError_t e = hipEventRecord(t->ev_issue, s);
+    hipError_t e = prefetch_plan(t, x, S, (hipStream_t)stream);
     if (e == hipSuccess)
-        e = hipStreamWaitEvent(t->copy, t->ev_issue, 0);
-    if (e == hipSuccess)
-        e = route_into(t, x, S, t->pf_xq, t->pf_xd, t->pf_logits, t->pf_ids, t->pf_w, t->copy);
-    if (e == hipSuccess)
-        e = launch_tier_plan(t->pf_ids, S * t->L.top_k, t->st, nullptr, t->pf_loads, t->pf_info, nullptr, true,
-                             t->copy);
-    if (e == hipSuccess)
-        e = hipEventRecord(t->ev_pfplan, t->copy);
-    if (e == hipSuccess)
-        e = launch_tier_fetch(t->pf_loads, t->pf_info, 1, t->banks, t->copy);
-    if (e == hipSuccess)
-        e = hipEventRecord(t->ev_prefetch, t->copy);
-    if (e == hipSuccess)
-        t->prefetch_pending = true;
+        e = prefetch_loads(t);
     return hip_status(e);
 }
 
@@ -643,6 +664,72 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
     if (e == hipSuccess)
         e = launch_combine(at<float>(ws, Lo.l.y), at<int32_t>(ws, Lo.l.inv), ids, w, S, k, H,
                            shared ? 2 * P : -1, out, s);
+    return hip_status(e);
+}
+
+int colibri_tier_verify_step(coli_tier* const* tiers, int32_t n_layers, const float* x, int32_t S, float* out,
+                             int32_t lookahead, void* ws, size_t ws_bytes, uint32_t* union_mask, int32_t* stats,
+                             coli_stream_t stream)
+{
+    if (!tiers || n_layers < 1 || S < 0)
+        return COLI_E_INVAL;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const coli_tier* t = tiers[l];
+        if (!t)
+            return COLI_E_INVAL;
+        const coli_moe_layer &A = tiers[0]->L, &B = t->L;
+        if (B.hidden != A.hidden || B.inter != A.inter || B.n_experts != A.n_experts || B.top_k != A.top_k ||
+            B.has_shared != A.has_shared)
+            return COLI_E_INVAL;
+        for (int32_t j = 0; j < l; ++j)
+            if (tiers[j] == t)
+                return COLI_E_INVAL; /* one tier per layer: a tier's prefetch and forward would interleave */
+    }
+    coli_tier* const t0 = tiers[0];
+    int st = check_call(t0, x, S, out, true, ws, ws_bytes);
+    if (st || S == 0)
+        return st;
+    if (!union_mask != !stats)
+        return COLI_E_INVAL;
+    if (lookahead && S > kSmallS)
+        return COLI_E_UNSUPPORTED;
+    for (int32_t l = 1; l < n_layers; ++l)
+        if ((st = check_current_device(tiers[l])))
+            return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int32_t H = t0->L.hidden, E = t0->L.n_experts, k = t0->L.top_k;
+    const size_t layer_elems = (size_t)S * H;
+    const int32_t* ids = at<int32_t>(ws, tier_layout(&t0->L, S).l.ids);
+    const int32_t nw = (E + 31) / 32;
+    hipError_t e = hipSuccess;
+    for (int32_t l = 0; l < n_layers && e == hipSuccess; ++l) {
+        coli_tier* t = tiers[l];
+        coli_tier* nxt = lookahead && l + 1 < n_layers ? tiers[l + 1] : nullptr;
+        const float* xl = x + (size_t)l * layer_elems;
+        /* the next layer's routing predicted from this layer's input */
+        if (nxt)
+            e = prefetch_plan(nxt, xl, S, s);
+        if (e == hipSuccess) {
+            st = colibri_tier_forward(t, xl, S, out + (size_t)l * layer_elems, ws, ws_bytes, stream);
+            if (st)
+                return st;
+        }
+        if (nxt) {
+            /* the predicted loads go after this layer's own misses */
+            if (e == hipSuccess)
+                e = hipEventRecord(t->ev_copy_tail, t->copy);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(nxt->copy, t->ev_copy_tail, 0);
+            if (e == hipSuccess)
+                e = prefetch_loads(nxt);
+            /* work the caller enqueues later may overwrite x: it follows the
+             * prediction's read */
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(s, nxt->ev_pfplan, 0);
+        }
+        if (e == hipSuccess && stats)
+            e = launch_verify_union(ids, S * k, E, union_mask + (size_t)l * nw, stats + 2 * (size_t)l, s);
+    }
     return hip_status(e);
 }
 

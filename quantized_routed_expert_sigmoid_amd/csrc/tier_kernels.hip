@@ -384,4 +384,57 @@ hipError_t launch_tier_fetch(const int4* loads, const int32_t* info, int32_t pas
     return hipGetLastError();
 }
 
+/* Draft-union statistics of one layer of a verify step ("Show HN:
+ * 如何在我的低配置电脑上运行 GLM-5.2", section 已实现的功能, the MTP item:
+ * every verified draft may route to experts of its own, and the
+ * batched-union item: each distinct expert of the batch is read once).  One
+ * workgroup builds the bit set of the distinct experts among the P routed
+ * ids, counts it and counts how many of them the previous step's set held;
+ * the stored set then becomes this step's.  The counts are sums of
+ * population counts of LDS words, independent of thread timing. */
+constexpr int kUnionThreads = 256;
+
+__global__ __launch_bounds__(kUnionThreads) void verify_union_kernel(const int32_t* __restrict__ ids, int32_t P,
+                                                                     int32_t E, uint32_t* __restrict__ mask,
+                                                                     int32_t* __restrict__ stats)
+{
+    __shared__ uint32_t cur[kTierMaxE / 32];
+    __shared__ int32_t cnt[2];
+    const int32_t nw = (E + 31) / 32;
+    for (int32_t w = threadIdx.x; w < nw; w += kUnionThreads)
+        cur[w] = 0;
+    if (threadIdx.x < 2)
+        cnt[threadIdx.x] = 0;
+    __syncthreads();
+    for (int32_t p = threadIdx.x; p < P; p += kUnionThreads) {
+        const int32_t e = ids[p];
+        if (e >= 0 && e < E)
+            atomicOr(&cur[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    int32_t u = 0, r = 0;
+    for (int32_t w = threadIdx.x; w < nw; w += kUnionThreads) {
+        const uint32_t c = cur[w];
+        u += __popc(c);
+        r += __popc(c & mask[w]);
+        mask[w] = c;
+    }
+    if (u)
+        atomicAdd(&cnt[0], u);
+    if (r)
+        atomicAdd(&cnt[1], r);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        stats[0] = cnt[0];
+        stats[1] = cnt[1];
+    }
+}
+
+hipError_t launch_verify_union(const int32_t* ids, int32_t P, int32_t E, uint32_t* mask, int32_t* stats,
+                               hipStream_t s)
+{
+    hipLaunchKernelGGL(verify_union_kernel, dim3(1), dim3(kUnionThreads), 0, s, ids, P, E, mask, stats);
+    return hipGetLastError();
+}
+
 } // namespace coli

@@ -264,3 +264,101 @@ def test_tier_prefetch_then_forward(qre, n_slots):
             assert tier.stats()["misses"] == before, "a perfect prediction leaves no miss"
     assert tier.stats()["prefetches"] == 7
     tier.close()
+
+
+VERIFY = dict(name="tv4", layer="tv4", bits=4, hidden=512, inter=256, n_experts=32, top_k=4, S=4,
+              has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4)
+
+
+@pytest.mark.parametrize("n_slots", [6, 16])
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_verify_steps_through_a_stack(qre, n_slots, lookahead):
+    """Four verify steps of S = 4 through three tiered layers in one call
+    each (colibri_tier_verify_step), with and without the router look-ahead:
+    every layer's output equals the resident forward's bit for bit and the
+    oracle's layer forward to the output tolerance (after prefetches that
+    the look-ahead planned and loaded), and the draft-union statistics equal
+    the distinct experts of the oracle's routed ids and their overlap with
+    the previous step's.  Layers 0 and 1 share a router and, in steps 0 and
+    2, an input, so that the look-ahead predicts layer 1 exactly there.
+    Six slots: plans of more than two passes (host round trip); sixteen:
+    two passes."""
+    n_layers, S = 3, VERIFY["S"]
+    w0 = synth.scaled(synth.WORKLOADS["tiny"], **VERIFY)
+    Ls = []
+    for l in range(n_layers):
+        L = synth.make_layer(synth.scaled(w0, layer=f"tv4/l{l}"))
+        if l == 1:
+            L.router_w, L.bias = Ls[0].router_w, Ls[0].bias
+        Ls.append(L)
+    devs = [to_device(L) for L in Ls]
+    tiers = [qre.TieredLayer(to_slow_tier(L, d), n_slots) for L, d in zip(Ls, devs)]
+    E, H, k = w0.n_experts, w0.hidden, w0.top_k
+    ws = tiers[0].workspace(S)
+    mask = torch.zeros(n_layers, (E + 31) // 32, dtype=torch.int32, device="cuda")
+    stats = torch.full((n_layers, 2), -1, dtype=torch.int32, device="cuda")
+    out = torch.empty(n_layers, S, H, device="cuda")
+    prev = [set() for _ in range(n_layers)]
+    for step in range(4):
+        xs = []
+        for l in range(n_layers):
+            if l == 1 and step % 2 == 0:
+                xs.append(xs[0].clone())
+            else:
+                x, _ = gapped_activations(w0, Ls[l].router_w, Ls[l].bias, tag=f"vs{step}/{l}")
+                xs.append(x)
+        x = torch.stack(xs).contiguous()
+        say(f"verify stack: slots={n_slots} lookahead={lookahead} step {step}")
+        pf0 = [t.stats()["prefetches"] for t in tiers]
+        miss1 = tiers[1].stats()["misses"]
+        qre.tier_verify_step(tiers, x.cuda(), out, ws, mask, stats, lookahead=lookahead)
+        torch.cuda.synchronize()
+        got = out.cpu()
+        st = stats.cpu().numpy()
+        for l in range(n_layers):
+            ref = qre.moe_layer_forward(devs[l], x[l].cuda())
+            torch.cuda.synchronize()
+            assert bits_equal(out[l], ref), f"step {step} layer {l}: differs from the resident forward"
+            r = oracle.layer_forward(Ls[l], x[l].numpy())
+            assert_close_rms(got[l].numpy(), r["out"], f"step {step} layer {l} vs oracle")
+            union = set(r["ids"].reshape(-1).tolist())
+            assert st[l].tolist() == [len(union), len(union & prev[l])], f"step {step} layer {l} statistics"
+            prev[l] = union
+        pf = [t.stats()["prefetches"] - p for t, p in zip(tiers, pf0)]
+        assert pf == ([0, 1, 1] if lookahead else [0, 0, 0])
+        if lookahead and step % 2 == 0 and n_slots >= E // 2:
+            # layer 1 predicted from its own input, every predicted miss fits
+            # the slots: its plan finds all of them resident
+            assert tiers[1].stats()["misses"] == miss1, f"step {step}: exact prediction left misses"
+    for t in tiers:
+        t.close()
+
+
+def test_verify_step_argument_errors(qre):
+    w0 = synth.scaled(synth.WORKLOADS["tiny"], **VERIFY)
+    L = synth.make_layer(w0)
+    dev = to_device(L)
+    t = qre.TieredLayer(to_slow_tier(L, dev), 8)
+    S, H = w0.S, w0.hidden
+    x = torch.zeros(2, S, H, device="cuda")
+    out = torch.empty_like(x)
+    ws = t.workspace(S)
+    mask = torch.zeros(2, 1, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(2, 2, dtype=torch.int32, device="cuda")
+    with pytest.raises(qre.ColibriError) as e:
+        qre.tier_verify_step([t, t], x, out, ws, mask, stats)  # one tier twice
+    assert e.value.status == qre.COLI_E_INVAL
+    with pytest.raises(qre.ColibriError) as e:
+        qre.tier_verify_step([t], x, out, ws, mask, None)  # statistics need both buffers
+    assert e.value.status == qre.COLI_E_INVAL
+    with pytest.raises(qre.ColibriError) as e:
+        qre.tier_verify_step([t], x, out, ws[:-1].clone())
+    assert e.value.status == qre.COLI_E_WORKSPACE
+    x9 = torch.zeros(1, 9, H, device="cuda")
+    ws9 = t.workspace(9)
+    with pytest.raises(qre.ColibriError) as e:
+        qre.tier_verify_step([t], x9, torch.empty_like(x9), ws9, lookahead=True)
+    assert e.value.status == qre.COLI_E_UNSUPPORTED
+    qre.tier_verify_step([t], x9, torch.empty_like(x9), ws9, lookahead=False)
+    torch.cuda.synchronize()
+    t.close()

@@ -80,7 +80,7 @@ def capi():
 def test_library_exports_every_declared_symbol(capi):
     lib = capi.lib()
     syms = _declared_symbols()
-    assert len(syms) == 27
+    assert len(syms) == 28
     for name in syms:
         assert hasattr(lib, name), name
 
@@ -138,6 +138,12 @@ def test_tier_sizes_and_validation_before_any_hip_call(capi):
     assert lib.colibri_tier_forward(None, 0x10000000, 1, 0x10000000, 0x10000000, 1 << 20,
                                     None) == capi.COLI_E_INVAL
     assert lib.colibri_tier_pin(None, None, 0, None) == capi.COLI_E_INVAL
+    # the verify step: no tier array, no layers, a null tier in the array
+    f = 0x10000000
+    assert lib.colibri_tier_verify_step(None, 2, f, 4, f, 1, f, 1 << 20, f, f, None) == capi.COLI_E_INVAL
+    one = (ctypes.c_void_p * 1)(None)
+    assert lib.colibri_tier_verify_step(one, 0, f, 4, f, 1, f, 1 << 20, f, f, None) == capi.COLI_E_INVAL
+    assert lib.colibri_tier_verify_step(one, 1, f, 4, f, 1, f, 1 << 20, f, f, None) == capi.COLI_E_INVAL
     assert lib.colibri_tier_workspace_bytes(None, 4) == 0
     st = capi.CacheStats()
     assert lib.colibri_tier_stats(None, ctypes.byref(st), None) == capi.COLI_E_INVAL
