@@ -613,6 +613,29 @@ def device_peaks(torch, qre_probes):
         us = e0.elapsed_time(e1) * 1000.0 / reps
         pattern[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / us / 1e3}
         del copies
+    # the matrix-core kernels' weight read pattern alone (64 rows per
+    # workgroup, 128 bytes of each row per step, two steps in flight, a
+    # barrier per step), at the prefill layer's sizes: every expert once
+    wp = synth.WORKLOADS["prefill"]
+    u = wp.n_experts + (1 if wp.has_shared else 0)
+    tile = {}
+    for name, rows, rowbytes in (("gate_up", 2 * wp.inter * u, wp.hidden * wp.bits // 8),
+                                 ("down", wp.hidden * u, wp.inter * wp.bits // 8)):
+        nbytes = rows * rowbytes
+        tb = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+        tsink = torch.zeros(rows // 64, dtype=torch.int32, device="cuda")
+        args = (ctypes.c_void_p(tb.data_ptr()), rowbytes, rows, 128, 0, 0, ctypes.c_void_p(tsink.data_ptr()),
+                ctypes.c_void_p(st))
+        assert qre_probes.colibri_probe_tile(*args) == 0
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            qre_probes.colibri_probe_tile(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        tile[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / us / 1e3}
+        del tb, tsink
     mfma = {}
     for k in (32, 64):
         blocks, iters = 1024, 4096
@@ -626,14 +649,17 @@ def device_peaks(torch, qre_probes):
         mfma[k] = ops / (e0.elapsed_time(e1) / 1000.0) / 1e12
     return {"hbm_read_stream_GBps": read[best], "read_stream_best": f"{best[0]}, {best[1]} workgroups",
             "int8_mfma_k32_TOPS": mfma[32], "int8_mfma_k64_TOPS": mfma[64],
-            "decode_read_pattern": pattern,
+            "decode_read_pattern": pattern, "prefill_read_pattern": tile,
             "spec": {"hbm_GBps": HBM_PEAK_GBS, "int8_mfma_TOPS": INT8_PEAK_TOPS,
                      "valu_lane_ops_per_s": VALU_PEAK_LANE_OPS},
             "how": "read stream: 1 GiB read once per launch with 16-byte nontemporal loads, best of grid-stride and "
                    "blocked layouts over 512..8192 workgroups; matrix cores: 1024 workgroups of 4 waves, 8 "
                    "independent int8 MFMA chains per wave; decode read pattern: the one-token kernels' weight "
                    "loads (items of 2 rows x 512 B, chunk-major, 16 rows per wave) with no arithmetic, at the "
-                   "decode layer's gate+up and down sizes, one launch each, 16 copies rotated"}
+                   "decode layer's gate+up and down sizes, one launch each, 16 copies rotated; prefill read pattern: "
+                   "the matrix-core kernels' weight loads (64 rows per workgroup, 128 bytes of each row per step, "
+                   "two steps in flight, a barrier per step) with no arithmetic, over every expert of the prefill "
+                   "layer's gate+up and down"}
 
 
 def load_probes():
@@ -644,6 +670,7 @@ def load_probes():
     L = ctypes.CDLL(path)
     L.colibri_probe_rows.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_void_p]
+    L.colibri_probe_tile.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
     L.colibri_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_void_p]
     L.colibri_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -796,6 +823,13 @@ def config_summary(w, res, peaks, copies):
         extra["event_pair_overhead_ms"] = 0.5 * (stage_ms.pop("dispatch") + stage_ms.pop("combine"))
         stage_ms["gate_up_with_selection"] = stage_ms.pop("gate_up")
         stage_ms["down_with_combine"] = stage_ms.pop("down")
+    if w.name == "prefill" and peaks.get("prefill_read_pattern"):
+        # the matrix-core weight read pattern over every expert: the floor of
+        # each FFN stage when all 257 experts are touched
+        pat = peaks["prefill_read_pattern"]
+        extra["read_pattern_floor_ms"] = {k: v["us"] / 1000.0 for k, v in pat.items()}
+        extra["stage_frac_of_read_pattern"] = {k: pat[k]["us"] / 1000.0 / stage_ms[k] for k in ("gate_up", "down")}
+    if w.S == 1:
         pat = peaks.get("decode_read_pattern", {})
         if w.name == "decode" and pat:
             # the same weight bytes read in the same pattern by a kernel that

@@ -32,6 +32,17 @@ int colibri_probe_read(const void* buf, size_t bytes, int32_t n_blocks, int32_t 
 int colibri_probe_rows(const void* buf, int32_t ni, int32_t n_waves, int32_t chunk_major, uint32_t* sink,
                        void* stream);
 
+/* The matrix-core kernels' weight read pattern without their arithmetic:
+ * n_rows / 64 workgroups of 256 threads; workgroup g reads rows
+ * [64 g, 64 g + 64) of rowbytes bytes (buf holds n_rows * rowbytes) in steps
+ * of chunk bytes of every row (chunk = 128, 256 or 512; rowbytes a multiple
+ * of 2 chunk), 16 bytes per thread and load, two steps in flight and a
+ * barrier per step, with nontemporal loads or not; lds_bytes (<= 64 KB) of
+ * unused dynamic LDS per workgroup set the occupancy.  sink: n_rows / 64
+ * words. */
+int colibri_probe_tile(const void* buf, int32_t rowbytes, int32_t n_rows, int32_t chunk, int32_t nontemporal,
+                       int32_t lds_bytes, uint32_t* sink, void* stream);
+
 /* n_blocks workgroups of four waves; each wave issues iters rounds of 8
  * independent v_mfma_i32_16x16x{k}_i8 (k = 32 or 64), i.e. 8 * iters *
  * 16 * 16 * k * 2 integer operations per wave.  sink: n_blocks words. */

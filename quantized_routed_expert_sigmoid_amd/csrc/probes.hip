@@ -91,6 +91,49 @@ __global__ __launch_bounds__(256) void probe_rows_kernel(const uint8_t* __restri
         sink[blockIdx.x] = acc;
 }
 
+/* The matrix-core kernels' weight read pattern without their arithmetic:
+ * workgroup g reads rows [64 g, 64 g + 64) of rowbytes bytes in steps of
+ * CHUNK bytes per row (step s: bytes [CHUNK s, CHUNK s + CHUNK) of each of
+ * the 64 rows), thread t taking the 16-byte piece t mod (CHUNK / 16) of rows
+ * t / (CHUNK / 16) + (256 / (CHUNK / 16)) i; two steps in flight and one
+ * barrier per step, as in the matrix-core K loop.  The dynamic LDS size the
+ * caller passes (unused) sets the occupancy. */
+template <int CHUNK, bool NT>
+__global__ __launch_bounds__(256) void probe_tile_kernel(const uint8_t* __restrict__ base, int rowbytes,
+                                                         uint32_t* sink)
+{
+    constexpr int PR = CHUNK / 16; /* pieces per row */
+    constexpr int RPI = 256 / PR;  /* rows per load instruction */
+    constexpr int NL = 64 / RPI;   /* loads per thread and step */
+    const int t = threadIdx.x;
+    const uint8_t* p0 = base + ((size_t)blockIdx.x * 64 + t / PR) * rowbytes + 16 * (t % PR);
+    const int nsteps = rowbytes / CHUNK;
+    u32x4 r[2][NL];
+    auto load = [&](int s, u32x4(&v)[NL]) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const u32x4* q = reinterpret_cast<const u32x4*>(p0 + (size_t)i * RPI * rowbytes + (size_t)s * CHUNK);
+            v[i] = NT ? __builtin_nontemporal_load(q) : *q;
+        }
+    };
+    load(0, r[0]);
+    load(1, r[1]);
+    uint32_t acc = 0;
+    for (int s = 0; s < nsteps; s += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                acc ^= r[h][i].x ^ r[h][i].y ^ r[h][i].z ^ r[h][i].w;
+            if (s + 2 + h < nsteps)
+                load(s + 2 + h, r[h]);
+            __syncthreads();
+        }
+    }
+    if (acc == 0x9E3779B9u)
+        sink[blockIdx.x] = acc;
+}
+
 constexpr int kChains = 8; /* independent accumulators per wave (covers the MFMA latency) */
 
 /* iters rounds of kChains independent int8 MFMAs per wave: K = 32 (one
@@ -175,6 +218,33 @@ int colibri_probe_rows(const void* buf, int32_t ni, int32_t n_waves, int32_t chu
         else
             hipLaunchKernelGGL((probe_rows_kernel<2, false>), grid, block, 0, st, b, n_waves, sink);
     }
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int colibri_probe_tile(const void* buf, int32_t rowbytes, int32_t n_rows, int32_t chunk, int32_t nontemporal,
+                       int32_t lds_bytes, uint32_t* sink, void* stream)
+{
+    if (!buf || !sink || n_rows <= 0 || n_rows % 64 || (chunk != 128 && chunk != 256 && chunk != 512) ||
+        rowbytes <= 0 || rowbytes % (2 * chunk) || lds_bytes < 0 || lds_bytes > 65536 ||
+        ((uintptr_t)buf % 16) != 0)
+        return 1;
+    const dim3 grid(n_rows / 64), block(256);
+    const hipStream_t st = (hipStream_t)stream;
+    const uint8_t* b = static_cast<const uint8_t*>(buf);
+#define COLI_TILE(C)                                                                                    \
+    do {                                                                                                \
+        if (nontemporal)                                                                                \
+            hipLaunchKernelGGL((probe_tile_kernel<C, true>), grid, block, lds_bytes, st, b, rowbytes, sink); \
+        else                                                                                            \
+            hipLaunchKernelGGL((probe_tile_kernel<C, false>), grid, block, lds_bytes, st, b, rowbytes, sink); \
+    } while (0)
+    if (chunk == 128)
+        COLI_TILE(128);
+    else if (chunk == 256)
+        COLI_TILE(256);
+    else
+        COLI_TILE(512);
+#undef COLI_TILE
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
