@@ -422,7 +422,10 @@ size_t colibri_tier_workspace_bytes(const coli_tier* t, int32_t S);
  * their slots; pass 1 waits for that fetch; one combine ends the call.
  * When n_slots minus the pinned experts is at least min(S * top_k,
  * n_experts), every plan has at most these two passes and the call returns
- * without waiting for the device; with every expert pinned, pass 0 alone.  Otherwise a plan may need more passes:
+ * without waiting for the device; with every expert pinned, pass 0 alone,
+ * and for one token the resident one-token kernels themselves, reading the
+ * experts through the slot map (then the plan, all hits, updates the
+ * cache's counters).  Otherwise a plan may need more passes:
  * the call then waits once for the plan to reach the host (pass 0 is
  * already running) and enqueues each later pass after its own fetch.  The
  * output is bit-identical to colibri_moe_layer_forward on the same weights.

@@ -48,6 +48,64 @@ DebugSlice g_debug_slice = {nullptr, 0, 0, 0, 0, 0, 0};
 }
 #endif
 
+namespace coli {
+
+hipError_t one_token_forward(const coli_moe_layer* L, const FfnArgs& a, const float* x, int8_t* xq, float* xd,
+                             float* logits, int32_t* ids, float* w, float* out, const int32_t* slot_of,
+                             void* const* stage_events, hipStream_t s)
+{
+    const int32_t H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k;
+    const bool shared = a.nseg > 1;
+    auto mark = [&](int i, hipError_t prev) -> hipError_t {
+        if (prev != hipSuccess || !stage_events)
+            return prev;
+        return hipEventRecord((hipEvent_t)stage_events[i], s);
+    };
+    hipError_t e = mark(0, hipSuccess);
+    if (e == hipSuccess)
+        e = launch_route_prep_small(x, 1, H, E, L->router_w, logits, xq, xd, s);
+    e = mark(1, e);
+    DecodeArgs dd;
+    dd.f = a;
+    dd.logits = logits;
+    dd.bias = L->router_bias;
+    dd.E = E;
+    dd.k = k;
+    dd.rsf = L->routed_scaling_factor;
+    dd.opt = route_opts(L);
+    dd.ids = ids;
+    dd.w = w;
+    dd.out = out;
+    dd.hs = nullptr;
+    dd.slot_of = slot_of;
+    const bool fused = down_combine_decode_fits(dd);
+    /* With the fused down + combine (which writes no y rows), the shared
+     * expert's gate/up runs as one-wave jobs spread over every CU, its fp32 h
+     * in the y region: the routed jobs then give each CU the same share.
+     * Per-row scales only. */
+    if (fused && shared && a.seg[1].gu_gb == 0 && I % 8 == 0 && I <= 2048 && (int64_t)(k + 1) * H >= I)
+        dd.hs = a.y;
+    e = mark(2, e);
+    if (e == hipSuccess)
+        e = launch_ffn_gate_up_decode(dd, L->gate.qtype, s);
+    e = mark(3, e);
+    if (fused) {
+        /* down and combine in one launch: the combine stage is empty */
+        if (e == hipSuccess)
+            e = launch_ffn_down_combine_decode(dd, L->down.qtype, s);
+        e = mark(4, e);
+    } else {
+        if (e == hipSuccess)
+            e = launch_ffn_down_decode(dd, L->down.qtype, s);
+        e = mark(4, e);
+        if (e == hipSuccess)
+            e = launch_combine(a.y, nullptr, ids, w, 1, k, H, shared ? k : -1, out, s);
+    }
+    return mark(5, e);
+}
+
+} // namespace coli
+
 extern "C" {
 
 const char* colibri_status_string(int status)
@@ -283,6 +341,8 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     /* One token whose shared expert (if any) runs in the routed launches:
      * router logits with quantisation, selection with gate/up, down, combine. */
     const bool one_token = S == 1 && b.nseg == 0;
+    if (one_token)
+        return hip_status(one_token_forward(L, a, x, xq, xd, logits, ids, w, out, nullptr, stage_events, s));
 
     hipError_t e = mark(0, hipSuccess);
     if (e == hipSuccess)
@@ -295,46 +355,6 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
         e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
                                  L->routed_scaling_factor, route_opts(L), ids, w, s);
     e = mark(1, e);
-    if (one_token) {
-        DecodeArgs dd;
-        dd.f = a;
-        dd.logits = logits;
-        dd.bias = L->router_bias;
-        dd.E = E;
-        dd.k = k;
-        dd.rsf = L->routed_scaling_factor;
-        dd.opt = route_opts(L);
-        dd.ids = ids;
-        dd.w = w;
-        dd.out = out;
-        dd.hs = nullptr;
-        const bool fused = down_combine_decode_fits(dd);
-        /* With the fused down + combine (which writes no y rows), the shared
-         * expert's gate/up runs as one-wave jobs spread over every CU, its
-         * fp32 h in the y region: the routed jobs then give each CU the same
-         * share.  Per-row scales only. */
-        if (fused && shared && a.nseg > 1 && a.seg[1].gu_gb == 0 && I % 8 == 0 && I <= 2048 &&
-            (int64_t)(k + 1) * H >= I)
-            dd.hs = y;
-        e = mark(2, e);
-        if (e == hipSuccess)
-            e = launch_ffn_gate_up_decode(dd, L->gate.qtype, s);
-        e = mark(3, e);
-        if (fused) {
-            /* down and combine in one launch: the combine stage is empty */
-            if (e == hipSuccess)
-                e = launch_ffn_down_combine_decode(dd, L->down.qtype, s);
-            e = mark(4, e);
-        } else {
-            if (e == hipSuccess)
-                e = launch_ffn_down_decode(dd, L->down.qtype, s);
-            e = mark(4, e);
-            if (e == hipSuccess)
-                e = launch_combine(y, nullptr, ids, w, 1, k, H, shared ? k : -1, out, s);
-        }
-        e = mark(5, e);
-        return hip_status(e);
-    }
     if (e == hipSuccess)
         e = S <= kSmallS
                 ? launch_select_dispatch_small(logits, L->router_bias, S, E, k, L->routed_scaling_factor,

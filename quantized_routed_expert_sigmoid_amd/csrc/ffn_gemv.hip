@@ -55,6 +55,14 @@ struct JobLoc {
     int seg, unit, rb;
 };
 
+/* Matrix index of routed expert id (0 <= id < E) in seg[0]'s banks: the id
+ * itself, or its slot in a tiered layer's slot bank; clamped to the bank. */
+__device__ __forceinline__ int decode_matrix(const int32_t* slot_of, int id, int E, int n_mat)
+{
+    const int m = slot_of ? slot_of[min(max(id, 0), E - 1)] : id;
+    return min(max(m, 0), n_mat - 1);
+}
+
 /* Field-wise select keeps the segment in scalar registers (every field of
  * FfnSeg is selected; the zero initialisation only guards additions). */
 __device__ __forceinline__ FfnSeg pick(const FfnArgs& a, int s)
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
         const int sel = sel_ids[u];
         if (sel < 0) /* slot dropped by top-p: the whole workgroup leaves */
             return;
-        e = min(sel, sg.n_mat - 1);
+        e = decode_matrix(d.slot_of, sel, d.E, sg.n_mat);
     }
     /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
     const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) +
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     if (routed && d.ids[u] < 0) /* slot dropped by top-p */
         return;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
-    const int e = routed ? min(d.ids[u], sg.n_mat - 1) : 0;
+    const int e = routed ? decode_matrix(d.slot_of, d.ids[u], d.E, sg.n_mat) : 0;
     const int nb = a.I / 32, region = dec_region(), dlen = kChunk * NI;
     float* P = reinterpret_cast<float*>(dec_lds + wv * region);
     uint32_t* xal = reinterpret_cast<uint32_t*>(dec_lds + kJobWaves * region);
@@ -988,7 +996,7 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
      * staged: its address needs the id, and h's loads need nothing) */
     const int u_l = dc_unit(kept, n_kept, d.k, min(lane, U - 1), all_kept);
     const bool rt_l = u_l < d.k;
-    const int e_l = rt_l ? min(max(d.ids[u_l], 0), a.seg[0].n_mat - 1) : 0;
+    const int e_l = rt_l ? decode_matrix(d.slot_of, d.ids[u_l], d.E, a.seg[0].n_mat) : 0;
     const float w_l = rt_l ? d.w[u_l] : 0.0f;
     /* without a shared expert, compacted unit 0's pair is issued before h is staged */
     if (!shared)

@@ -150,6 +150,10 @@ struct DecodeArgs {
      * quantises it while staging (per-row scales, I <= 2048 and the fused
      * launch only). */
     float* hs;
+    /* nullptr: a routed expert's matrices are at its id in seg[0]'s banks.
+     * Otherwise at slot_of[id] (a tiered layer's slot map, [E], every
+     * routed expert resident). */
+    const int32_t* slot_of;
 };
 
 /* Bounds on the unit counts of a routed group with P pairs of S tokens over

@@ -249,6 +249,14 @@ inline hipError_t run_ffn(const FfnArgs& a, int32_t bits_gu, int32_t bits_d, hip
     return e;
 }
 
+/* The one-token forward (S = 1; a: the FFN arguments, the shared expert if
+ * any in its second segment): quantise + router logits, selection with
+ * gate/up, down with the combine.  slot_of: as DecodeArgs::slot_of.
+ * stage_events (may be null): events 0..5 as the staged forward records
+ * them. */
+hipError_t one_token_forward(const coli_moe_layer* L, const FfnArgs& a, const float* x, int8_t* xq, float* xd,
+                             float* logits, int32_t* ids, float* w, float* out, const int32_t* slot_of,
+                             void* const* stage_events, hipStream_t s);
 
 } // namespace coli
 

@@ -578,6 +578,52 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
     if (e != hipSuccess)
         return COLI_E_HIP;
 
+    /* Every expert pinned, one token: the resident one-token kernels, with
+     * the routed experts read through the slot map (the same kernels on the
+     * same weights, so the same bits); the plan, all hits, then keeps the
+     * cache's usage and counters. */
+    const bool shared = L->has_shared != 0;
+    if (all_pinned && S == 1 &&
+        (!shared || (L->sh_gate.qtype == t->slot[0].qtype && L->sh_down.qtype == t->slot[2].qtype))) {
+        if (t->prefetch_pending) {
+            e = hipStreamWaitEvent(s, t->ev_pfplan, 0);
+            t->prefetch_pending = false;
+        }
+        UnitLists ul;
+        ul.units = at<Unit>(ws, Lo.l.units);
+        ul.n_units = at<int32_t>(ws, Lo.l.n_units);
+        ul.max_units = max_gemv_units(P, E);
+        ul.munits = at<Unit>(ws, Lo.l.munits);
+        ul.n_munits = at<int32_t>(ws, Lo.l.n_munits);
+        ul.max_munits = max_mfma_units(P, E, S);
+        FfnArgs a;
+        debug_attach(a);
+        a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], at<int32_t>(ws, Lo.l.sorted), &ul, k, S, P, 0);
+        a.nseg = 1;
+        if (shared) {
+            a.seg[1] = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P);
+            a.nseg = 2;
+        }
+        a.unit_tokens = 1;
+        a.H = H;
+        a.I = L->inter;
+        a.xq = at<int8_t>(ws, Lo.l.xq);
+        a.xd = at<float>(ws, Lo.l.xd);
+        a.hq = at<int8_t>(ws, Lo.l.hq);
+        a.hd = at<float>(ws, Lo.l.hd);
+        a.y = at<float>(ws, Lo.l.y);
+        if (e == hipSuccess)
+            e = one_token_forward(L, a, x, at<int8_t>(ws, Lo.l.xq), at<float>(ws, Lo.l.xd), at<float>(ws, Lo.l.logits),
+                                  ids, w, out, t->st.slot_of, nullptr, s);
+        if (e == hipSuccess)
+            e = launch_tier_plan(ids, P, t->st, codes, loads, info, pass_pairs, false, s);
+        if (e == hipSuccess)
+            e = hipEventRecord(t->ev_plan, s);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(t->copy, t->ev_plan, 0);
+        return hip_status(e);
+    }
+
     /* 1-2. route and plan, the plan after a pending prefetch's plan.  With
      * two passes the misses always fit the free slots, so the slots the
      * prefetch is still filling are late hits, read only in pass 1, which
@@ -611,7 +657,6 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
         e = hipStreamWaitEvent(t->copy, t->ev_plan, 0);
 
     /* 3. pass 0 at once */
-    const bool shared = L->has_shared != 0;
     if (e == hipSuccess)
         e = run_pass(t, Lo, ws, codes, 0, 0, S, shared, s);
     if (e == hipSuccess)

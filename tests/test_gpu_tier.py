@@ -147,6 +147,26 @@ def test_tier_everything_pinned(qre):
     tier.close()
 
 
+@pytest.mark.parametrize("case", ["decode_int4", "grouped_int4", "small_topp_groups", "many_slots_int2"])
+def test_tier_everything_pinned_one_token(qre, case):
+    """All experts pinned, one token: the tier runs the resident one-token
+    kernels through its slot map (pins in reverse order, so slot != expert);
+    outputs equal the resident forward bit for bit and the device planner's
+    state the host planner's."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], **dict(TIER_CASES[case], S=1))
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    E = w.n_experts
+    tier = qre.TieredLayer(to_slow_tier(L, dev), E)
+    host = qre.ExpertCache(E, E)
+    tier.pin(list(range(E))[::-1])
+    host.pin(list(range(E))[::-1])
+    _run_sequence(qre, w, dev, tier, order=[0, 1, 2, 0, 3], S=1, host=host)
+    st = tier.stats()
+    assert st["misses"] == 0 and st["passes"] == st["plans"] == 5 and st["pin_loads"] == E
+    tier.close()
+
+
 def test_tier_device_slow_tier_and_other_width_shared(qre):
     """The slow tier may be device memory; a shared expert at another width
     runs in launches of its own in pass 0."""
@@ -195,16 +215,22 @@ def test_tier_argument_errors(qre):
     tier.close()
 
 
-def test_tier_forward_in_a_graph(qre):
-    """With enough unpinned slots the tiered forward never waits for the
+@pytest.mark.parametrize("all_pinned", [False, True])
+def test_tier_forward_in_a_graph(qre, all_pinned):
+    """With enough unpinned slots (or every expert pinned: the one-token
+    kernels through the slot map) the tiered forward never waits for the
     host, so it can be captured: replays of one captured forward over
     changing inputs equal the resident forward, and the cache state evolves
     as for eager calls."""
     w = synth.scaled(synth.WORKLOADS["tiny"], **TIER_CASES["decode_int4"])
     L = synth.make_layer(w)
     dev = to_device(L)
-    tier = qre.TieredLayer(to_slow_tier(L, dev), 12)
-    host = qre.ExpertCache(w.n_experts, 12)
+    n_slots = w.n_experts if all_pinned else 12
+    tier = qre.TieredLayer(to_slow_tier(L, dev), n_slots)
+    host = qre.ExpertCache(w.n_experts, n_slots)
+    if all_pinned:
+        tier.pin(list(range(w.n_experts))[::-1])
+        host.pin(list(range(w.n_experts))[::-1])
     x_in = torch.zeros(w.S, w.hidden, device="cuda")
     out = torch.zeros_like(x_in)
     ws = tier.workspace(w.S)
