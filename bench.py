@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=0, help="timed steps (0: per-workload default)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode")
-    ap.add_argument("--copies", type=int, default=16, help="layer copies rotated across steps")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="layer copies rotated across steps (0: the workload's default: 16 for tiny and decode, "
+                         "4 for verify, 2 for prefill and skewed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="time only --workload (default: all five configs)")
     ap.add_argument("--tier", action="store_true",
@@ -742,6 +744,7 @@ def main():
         steps, warmup, copies = (args.steps, args.warmup, args.copies) if name == args.workload else \
             DEFAULTS[name]
         steps = steps or DEFAULTS[name][0]
+        copies = copies or DEFAULTS[name][2]
         print(f"bench: {name} S={wc.S} int{wc.bits}: {steps} steps over {copies} layer copies",
               file=sys.stderr, flush=True)
         cpu_n = 0 if args.no_cpu_baseline else CPU_TOKENS[name]
