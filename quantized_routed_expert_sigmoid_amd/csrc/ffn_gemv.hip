@@ -223,32 +223,85 @@ __device__ __forceinline__ float fold_chunk(const float* tile, int k, const floa
     return acc;
 }
 
-/* The same with group-wise weight scales: block b's coefficient is
- * ws[b / gb] * d_b (ws: the row's ng scales; b0: the chunk's first block;
- * blocks past the row read its last scale, their d is 0).  The group index
- * steps with the block instead of being divided out per block. */
+/* The same with group-wise weight scales: block b's coefficient is the fp32
+ * product of the row's group scale and d_b.  wtile holds the chunk's scale
+ * of every (row, block), laid out as the partial tile (ptile), so its quad
+ * reads are conflict-free like the partials'. */
 __device__ __forceinline__ float fold_chunk_grouped(const float* tile, int k, const float* dc, float acc,
-                                                    const float* ws, int gb, int ng, int b0)
+                                                    const float* wtile)
 {
     const float* row = tile + k * kChunk;
+    const float* wrow = wtile + k * kChunk;
     const int sw = (k >> 1) & 7;
-    int g = b0 / gb, rem = b0 - (b0 / gb) * gb;
+    f32x4 s[8], d[8];
+#pragma unroll
+    for (int q = 0; q < kFoldAhead; ++q) {
+        s[q] = *reinterpret_cast<const f32x4*>(row + ((q ^ sw) << 2));
+        d[q] = *reinterpret_cast<const f32x4*>(dc + 4 * q);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const f32x4 s = *reinterpret_cast<const f32x4*>(row + ((q ^ sw) << 2));
-        const f32x4 d = *reinterpret_cast<const f32x4*>(dc + 4 * q);
-        const float sv[4] = {s.x, s.y, s.z, s.w}, dv[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc = __builtin_fmaf(ws[min(g, ng - 1)] * dv[j], sv[j], acc);
-            if (++rem == gb) {
-                rem = 0;
-                ++g;
-            }
+        if (q + kFoldAhead < 8) {
+            s[q + kFoldAhead] = *reinterpret_cast<const f32x4*>(row + (((q + kFoldAhead) ^ sw) << 2));
+            d[q + kFoldAhead] = *reinterpret_cast<const f32x4*>(dc + 4 * (q + kFoldAhead));
         }
+        /* the coefficients of quad q, formed before its chain steps */
+        const f32x4 w = *reinterpret_cast<const f32x4*>(wrow + ((q ^ sw) << 2));
+        const float c0 = w.x * d[q].x, c1 = w.y * d[q].y, c2 = w.z * d[q].z, c3 = w.w * d[q].w;
+        acc = __builtin_fmaf(c0, s[q].x, acc);
+        acc = __builtin_fmaf(c1, s[q].y, acc);
+        acc = __builtin_fmaf(c2, s[q].z, acc);
+        acc = __builtin_fmaf(c3, s[q].w, acc);
         asm volatile("" : "+v"(acc) : : "memory"); /* as in fold_chunk */
     }
     return acc;
+}
+
+/* The group-wise scales of chunk i for a wave's scale tile: lane l takes
+ * row l mod 16 (clamped to the rows that exist; ws: the scales of the
+ * wave's row 0, ng per row) and blocks 8 (l / 16) .. + 7 of the chunk
+ * (block b's scale is the one of group b / gb; blocks past the row take
+ * its last one, their d is 0).  Loaded at the chunk's start, stored into
+ * the tile before its fold. */
+struct ChunkScales {
+    float v[8];
+};
+
+__device__ __forceinline__ void chunk_scales_load(ChunkScales& S, const float* ws, int ng, int gb, int rows_ok,
+                                                  int i, int lane)
+{
+    /* the lane index through an empty asm, so that the address work of each
+     * chunk stays at its chunk instead of being hoisted to the kernel's top
+     * and held in registers for every chunk */
+    if (gb == 0) {
+        /* per-row scales in a grouped launch: coefficient 1 * d_b = d_b */
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            S.v[j] = 1.0f;
+        return;
+    }
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t r = (uint32_t)min(ln & 15, max(rows_ok, 1) - 1);
+    const int b0 = kChunk * i + 8 * (ln >> 4);
+    int g = b0 / gb, rem = b0 - g * gb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        S.v[j] = ws[r * (uint32_t)ng + (uint32_t)min(g, ng - 1)];
+        if (++rem == gb) {
+            rem = 0;
+            ++g;
+        }
+    }
+}
+
+__device__ __forceinline__ void chunk_scales_store(const ChunkScales& S, float* wtile, int lane)
+{
+    const int r = lane & 15, c0 = 8 * (lane >> 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<f32x4*>(wtile + ptile(r, c0 + 4 * h)) =
+            f32x4{S.v[4 * h], S.v[4 * h + 1], S.v[4 * h + 2], S.v[4 * h + 3]};
 }
 
 /* Chunks per row for nb blocks, rounded up to an instantiated count. */
@@ -329,9 +382,16 @@ __host__ __device__ inline int dec_dlen(int nb)
     return kChunk * (n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 6 ? 6 : 8);
 }
 
-__host__ __device__ inline size_t dec_lds_bytes(int nb)
+/* A wave's LDS region; with group-wise scales it also holds the chunk's
+ * weight-scale tile (16 rows x 32 blocks, after the partial tile). */
+__host__ __device__ inline int dec_region_g(bool grouped)
 {
-    return (size_t)(kJobWaves * dec_region() + 9 * dec_dlen(nb) + 64 + 64) * 4;
+    return grouped ? (dec_region() > 2 * kTile ? dec_region() : 2 * kTile) : dec_region();
+}
+
+__host__ __device__ inline size_t dec_lds_bytes(int nb, bool grouped)
+{
+    return (size_t)(kJobWaves * dec_region_g(grouped) + 9 * dec_dlen(nb) + 64 + 64) * 4;
 }
 
 /* Output row, matrix kind and weight rows of a wave's rows 0..7 and 8..15,
@@ -354,8 +414,9 @@ __device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* ro
 {
     constexpr int D = 2 * NI, N = 8 * NI;
     const int lane = threadIdx.x & 63, c = lane & 31, k = lane & 15;
-    const int ng = GROUPED ? nb / gb : 0;
-    const float* ws = GROUPED ? ws0 + (int64_t)min(k, max(rows_ok, 1) - 1) * ng : nullptr;
+    const int ng = GROUPED && gb ? nb / gb : 0;
+    float* W = P + kTile; /* GROUPED: the chunk's scale tile */
+    ChunkScales CS;
     float acc = 0.0f;
     uint32_t xa[8];
 #pragma unroll
@@ -368,6 +429,10 @@ __device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* ro
             xa[0] = u0.x; xa[1] = u0.y; xa[2] = u0.z; xa[3] = u0.w;
             xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
         }
+        if constexpr (GROUPED) {
+            if (p == 4) /* four items before the fold: late enough to hold few registers */
+                chunk_scales_load(CS, ws0, ng, gb, rows_ok, i, lane);
+        }
         const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
         const int row = 2 * p + (lane >> 5);
         P[ptile(row, c)] = kChunk * i + c < nb ? (float)s : 0.0f;
@@ -377,9 +442,11 @@ __device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* ro
         if (n + D < N) /* resolved at compile time */
             item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, rows8);
         if (p == 7) {
+            if constexpr (GROUPED)
+                chunk_scales_store(CS, W, lane);
             wave_lds_sync();
             if constexpr (GROUPED)
-                acc = fold_chunk_grouped(P, k, dl + kChunk * i, acc, ws, gb, ng, kChunk * i);
+                acc = fold_chunk_grouped(P, k, dl + kChunk * i, acc, W);
             else
                 acc = fold_chunk(P, k, dl + kChunk * i, acc);
             wave_lds_sync(); /* the chunk's partials are read before the next chunk's overwrite them */
@@ -431,7 +498,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     const FfnArgs& a = d.f;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int RB = a.I / 32;
-    const int nb = a.H / 32, region = dec_region(), dlen = kChunk * NI;
+    const int nb = a.H / 32, region = dec_region_g(GROUPED), dlen = kChunk * NI;
     float* P = reinterpret_cast<float*>(dec_lds + wv * region);
     uint32_t* xal = reinterpret_cast<uint32_t*>(dec_lds + kJobWaves * region);
     float* dl = reinterpret_cast<float*>(xal + 8 * dlen);
@@ -515,9 +582,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_decode(DecodeArgs d)
     const int kd = wv < 2 ? kDbgGate : kDbgUp, r16 = rb * 32 + 16 * (wv & 1);
     const DbgRows dr = {u, kd, r16, kd, r16 + 8};
     const float v16 =
-        GROUPED && sg.gu_gb
-            ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, ws0, sg.gu_gb, a, dr)
-            : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, nullptr, 0, a, dr);
+        dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, xal, P, dl, ws0, sg.gu_gb, a, dr);
     if (lane < 16)
         rsum[16 * wv + lane] = v16;
     __syncthreads();
@@ -554,7 +619,7 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
         return;
     const FfnSeg sg = pick(a, routed ? 0 : 1);
     const int e = routed ? decode_matrix(d.slot_of, d.ids[u], d.E, sg.n_mat) : 0;
-    const int nb = a.I / 32, region = dec_region(), dlen = kChunk * NI;
+    const int nb = a.I / 32, region = dec_region_g(GROUPED), dlen = kChunk * NI;
     float* P = reinterpret_cast<float*>(dec_lds + wv * region);
     uint32_t* xal = reinterpret_cast<uint32_t*>(dec_lds + kJobWaves * region);
     float* dl = reinterpret_cast<float*>(xal + 8 * dlen);
@@ -568,9 +633,7 @@ __global__ __launch_bounds__(256) void ffn_down_decode(DecodeArgs d)
     __syncthreads();
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(row0, a.H - 1)) * (nb / sg.d_gb) : nullptr;
     const DbgRows dr = {u, kDbgDown, row0, kDbgDown, row0 + 8};
-    const float v = GROUPED && sg.d_gb
-                        ? dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, ws0, sg.d_gb, a, dr)
-                        : dec_k_loop<BITS, NI, false>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, nullptr, 0, a, dr);
+    const float v = dec_k_loop<BITS, NI, GROUPED>(R, rows0, rowbytes, rows_ok, nb, xal, P, dl, ws0, sg.d_gb, a, dr);
     const int n = row0 + lane;
     if (lane < rows_ok)
         a.y[(int64_t)u * a.H + n] = (sg.d_gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n]) * v;
@@ -590,10 +653,13 @@ constexpr int kDcStage = 4;
  * Dynamic LDS, in words: codes [TMAX][nb][8], block scales [TMAX][32 NI]
  * (zero past nb), per wave the partial tiles [TMAX][16][32], and the job's
  * row values [64][TMAX]. */
-__host__ __device__ inline size_t rows_lds_words(int nb, int tmax)
+/* LDS words of the whole-row kernels: codes [tmax][nb][8], scales
+ * [tmax][dlen], per wave tmax partial tiles, the row values [64][tmax], and
+ * with group-wise scales per wave a scale tile. */
+__host__ __device__ inline size_t rows_lds_words(int nb, int tmax, bool grouped)
 {
     return (size_t)tmax * nb * 8 + (size_t)tmax * dec_dlen(nb) + (size_t)kJobWaves * tmax * kTile +
-           64 * (size_t)tmax;
+           64 * (size_t)tmax + (grouped ? (size_t)kJobWaves * kTile : 0);
 }
 
 constexpr size_t kLdsMax = 160 * 1024; /* LDS of one CU (gfx950) */
@@ -606,19 +672,23 @@ template <int BITS, int NI, int TMAX, bool GROUPED>
 __device__ __forceinline__ float rows_k_loop(Ring<BITS, NI>& R, const uint8_t* rows0, uint32_t rowbytes, int rows_ok,
                                              int nb, int ntok, const uint32_t* xal, const float* dls, float* P,
                                              const float* ws0, int gb, const FfnArgs& a, int64_t o0, int kind,
-                                             int wrow0)
+                                             int wrow0, float* W)
 {
     constexpr int D = 2 * NI, N = 8 * NI;
     const int lane = threadIdx.x & 63, c = lane & 31, k = lane & 15;
     const int tf = min(lane >> 4, TMAX - 1); /* token of the lane's chain */
     const int sd = kChunk * NI;
-    const int ng = GROUPED ? nb / gb : 0;
-    const float* ws = GROUPED ? ws0 + (int64_t)min(k, max(rows_ok, 1) - 1) * ng : nullptr;
+    const int ng = GROUPED && gb ? nb / gb : 0;
+    ChunkScales CS;
     float acc = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         const int i = n >> 3, p = n & 7;
         const int b = kChunk * i + c;
+        if constexpr (GROUPED) {
+            if (p == 4) /* four items before the fold: late enough to hold few registers */
+                chunk_scales_load(CS, ws0, ng, gb, rows_ok, i, lane);
+        }
         const int bc = min(b, nb - 1);
         const int w = ptile(2 * p + (lane >> 5), c);
         /* tokens one at a time (a rolled loop keeps one token's operands live) */
@@ -635,10 +705,12 @@ __device__ __forceinline__ float rows_k_loop(Ring<BITS, NI>& R, const uint8_t* r
         if (n + D < N) /* resolved at compile time */
             item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, nullptr);
         if (p == 7) {
+            if constexpr (GROUPED)
+                chunk_scales_store(CS, W, lane);
             wave_lds_sync();
             const float* dc = dls + tf * sd + kChunk * i;
             if constexpr (GROUPED)
-                acc = fold_chunk_grouped(P + tf * kTile, k, dc, acc, ws, gb, ng, kChunk * i);
+                acc = fold_chunk_grouped(P + tf * kTile, k, dc, acc, W);
             else
                 acc = fold_chunk(P + tf * kTile, k, dc, acc);
             wave_lds_sync();
@@ -716,6 +788,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
     float* dls = reinterpret_cast<float*>(xal + (int64_t)TMAX * nb * 8);
     float* P = dls + TMAX * sd + wv * (TMAX * kTile);
     float* vs = dls + TMAX * sd + kJobWaves * TMAX * kTile;
+    float* W = vs + 64 * TMAX + wv * kTile; /* grouped: the wave's scale tile */
     /* waves 0, 1: gate rows rb*32 + 16w ..; waves 2, 3: the same up rows */
     const int rloc = 16 * (wv & 1);
     const uint8_t* rows0 = (wv < 2 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + L.rb * 32 + rloc) * rowbytes;
@@ -737,11 +810,8 @@ __global__ __launch_bounds__(256) void ffn_gate_up_rows(FfnArgs a)
                                 : nullptr;
     const int64_t o0 = sg.out_base + pos0;
     const int kd = wv < 2 ? kDbgGate : kDbgUp, wr0 = L.rb * 32 + rloc;
-    const float v = GROUPED && sg.gu_gb
-                        ? rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P, ws0,
-                                                               sg.gu_gb, a, o0, kd, wr0)
-                        : rows_k_loop<BITS, NI, TMAX, false>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P,
-                                                             nullptr, 0, a, o0, kd, wr0);
+    const float v = rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, kWaveRows, nb, ntok, xal, dls, P, ws0,
+                                                         sg.gu_gb, a, o0, kd, wr0, W);
     /* job row of the wave's row k: gate rows 0..31, up rows 32..63 */
     const int t_l = lane >> 4;
     if (t_l < ntok)
@@ -789,6 +859,7 @@ __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
     uint32_t* xal = reinterpret_cast<uint32_t*>(rw_lds);
     float* dls = reinterpret_cast<float*>(xal + (int64_t)TMAX * nb * 8);
     float* P = dls + TMAX * sd + wv * (TMAX * kTile);
+    float* W = dls + TMAX * sd + kJobWaves * TMAX * kTile + 64 * TMAX + wv * kTile; /* grouped: scale tile */
     const int first = L.rb * kRowsPerJob + kWaveRows * wv;
     const int rows_ok = min(kWaveRows, max(0, a.H - first));
     const uint8_t* rows0 = sg.down_w + ((int64_t)e * a.H + min(first, a.H - 1)) * rowbytes;
@@ -808,11 +879,8 @@ __global__ __launch_bounds__(256) void ffn_down_rows(FfnArgs a)
     const int ng = sg.d_gb ? nb / sg.d_gb : 0;
     const float* ws0 = sg.d_gb ? sg.down_s + ((int64_t)e * a.H + min(first, a.H - 1)) * ng : nullptr;
     const int64_t o0 = sg.out_base + pos0;
-    const float v = GROUPED && sg.d_gb
-                        ? rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P, ws0,
-                                                               sg.d_gb, a, o0, kDbgDown, first)
-                        : rows_k_loop<BITS, NI, TMAX, false>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P,
-                                                             nullptr, 0, a, o0, kDbgDown, first);
+    const float v = rows_k_loop<BITS, NI, TMAX, GROUPED>(R, rows0, rowbytes, rows_ok, nb, ntok, xal, dls, P, ws0,
+                                                         sg.d_gb, a, o0, kDbgDown, first, W);
     const int t_l = lane >> 4;
     if (t_l < ntok && (lane & 15) < rows_ok)
         a.y[(int64_t)(sg.out_base + pos0 + t_l) * a.H + n] = sc * v;
@@ -1190,7 +1258,7 @@ template <int TMAX, bool GROUPED>
 static void launch_rows_g(const FfnArgs& a, int32_t bits, bool gate_up, dim3 grid, hipStream_t st)
 {
     const int nb = gate_up ? a.H / 32 : a.I / 32;
-    const size_t lds = rows_lds_words(nb, TMAX) * 4;
+    const size_t lds = rows_lds_words(nb, TMAX, GROUPED) * 4;
     switch (gemv_ni(nb)) {
     case 1: launch_rows_ni<1, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
     case 2: launch_rows_ni<2, TMAX, GROUPED>(a, bits, gate_up, grid, lds, st); break;
@@ -1294,7 +1362,7 @@ hipError_t launch_ffn_gate_up_decode(const DecodeArgs& d, int32_t bits, hipStrea
     const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 && !d.hs ? 1 : 0)) * (d.f.I / 32) + (d.hs ? d.f.I / 8 : 0);
     const int nb = d.f.H / 32;
     const dim3 grid((uint32_t)jobs);
-    const size_t lds = dec_lds_bytes(nb);
+    const size_t lds = dec_lds_bytes(nb, any_grouped(d.f, true));
     if (any_grouped(d.f, true))
         gate_up_decode_g<true>(d, bits, grid, lds, nb, st);
     else
@@ -1307,7 +1375,7 @@ hipError_t launch_ffn_down_decode(const DecodeArgs& d, int32_t bits, hipStream_t
     const int64_t jobs = (int64_t)(d.k + (d.f.nseg > 1 ? 1 : 0)) * ((d.f.H + kRowsPerJob - 1) / kRowsPerJob);
     const int nb = d.f.I / 32;
     const dim3 grid((uint32_t)jobs);
-    const size_t lds = dec_lds_bytes(nb);
+    const size_t lds = dec_lds_bytes(nb, any_grouped(d.f, false));
     if (any_grouped(d.f, false))
         down_decode_g<true>(d, bits, grid, lds, nb, st);
     else
