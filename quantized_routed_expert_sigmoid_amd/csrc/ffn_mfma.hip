@@ -53,7 +53,7 @@ template <int BITS, bool GROUPED = false>
 struct KLds {
     uint32_t a[2][64 * Cfg<BITS>::kRowStride];              /* weight rows, packed words */
     uint32_t b[2][Cfg<BITS>::kStep][4][kTok][2];           /* operand words 2g, 2g+1 per (block, g, token) */
-    float ds[2][Cfg<BITS>::kStep][kTok];                    /* block scale * 2^-(8-b) */
+    float ds[2][GROUPED ? 1 : Cfg<BITS>::kStep][kTok];      /* block scale * 2^-(8-b) (per-row kernels) */
     float dr[2][Cfg<BITS>::kStep][kTok];                    /* block scale */
     int flag[2];                                            /* step whose scales need the exact-shift fold */
     float ws[2][GROUPED ? 64 * Cfg<BITS>::kStep : 1];       /* [row][block of the step] weight scale */
@@ -103,11 +103,13 @@ __device__ __forceinline__ int lean_d_block()
 
 /* LDS of the aligned K loop: the two N-tiles' operands of a lane side by
  * side, so that one read brings both. */
-template <int BITS>
+template <int BITS, bool GW = false>
 struct __attribute__((aligned(16))) LeanLds {
     __attribute__((aligned(16))) uint32_t a[2][64 * LCfg<BITS>::kStride]; /* weight rows, packed words */
     __attribute__((aligned(16))) uint32_t b[2][Cfg<BITS>::kStep][4][16][2][2]; /* [block][g][token & 15][tile][word] */
     __attribute__((aligned(16))) float ds[2][Cfg<BITS>::kStep][16][2];        /* [block][token & 15][tile] */
+    /* GW: each row's group-wise weight scale of each block of the step */
+    __attribute__((aligned(16))) float ws[2][Cfg<BITS>::kStep][GW ? 64 : 4]; /* [block][row] */
 };
 
 struct EpiLds {
@@ -117,7 +119,7 @@ struct EpiLds {
 template <int BITS, bool GROUPED = false>
 union MfmaShared {
     KLds<BITS, GROUPED> k;
-    LeanLds<BITS> l;
+    LeanLds<BITS, GROUPED> l;
     EpiLds e;
 };
 
@@ -240,7 +242,7 @@ __device__ __forceinline__ void fetch(Stage<BITS, GROUPED>& P, const LoadLane& L
     if constexpr (GROUPED) {
 #pragma unroll
         for (int i = 0; i < C::kBpt; ++i)
-            P.sc[i] = L.gb ? L.wsrow[min(wb0 + i, L.nb - 1) / L.gb] : 0.0f;
+            P.sc[i] = L.gb ? L.wsrow[min(wb0 + i, L.nb - 1) / L.gb] : 1.0f; /* per-row: 1 * d = d */
     }
 #pragma unroll
     for (int i = 0; i < C::kBpt; ++i) {
@@ -310,11 +312,13 @@ __device__ __forceinline__ void commit(const Stage<BITS, GROUPED>& P, KLds<BITS,
             S.b[buf][j][2 * h + gg][t][1] = P.x[2 * gg + 1];
         }
     }
-    const float ds = P.d * (1.0f / (float)(1 << SHIFT));
-    S.ds[buf][j][t] = ds;
     S.dr[buf][j][t] = P.d;
-    if (SHIFT != 0 && P.d != 0.0f && !(ds >= 1.17549435e-38f))
-        S.flag[buf] = st;
+    if constexpr (!GROUPED) {
+        const float ds = P.d * (1.0f / (float)(1 << SHIFT));
+        S.ds[buf][j][t] = ds;
+        if (SHIFT != 0 && P.d != 0.0f && !(ds >= 1.17549435e-38f))
+            S.flag[buf] = st;
+    }
 }
 
 /* A operand of lane group g (elements 8g .. 8g+7 of the block, in the order
@@ -414,31 +418,31 @@ __device__ __forceinline__ void step(const KLds<BITS, GROUPED>& S, int buf, int 
     const int b0 = st * C::kStep, b1 = b0 + C::kStep;
     if (b0 >= nb)
         return;
+    (void)gb;
     if constexpr (GROUPED) {
-        if (gb) {
-            if (b1 <= nb) {
+        /* every segment of a grouped launch: per-row segments carry scale 1 */
+        if (b1 <= nb) {
 #pragma unroll
-                for (int j = 0; j < C::kStep; ++j)
-                    block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
-                return;
-            }
-            for (int j = 0; j < C::kStep && b0 + j < nb; ++j)
+            for (int j = 0; j < C::kStep; ++j)
                 block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
             return;
         }
-    }
-    const bool exact_shift = BITS != 8 && __builtin_amdgcn_readfirstlane(S.flag[buf]) == st;
-    if (b1 <= nb && !exact_shift) {
+        for (int j = 0; j < C::kStep && b0 + j < nb; ++j)
+            block_mfma_grouped<BITS, NT>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
+    } else {
+        const bool exact_shift = BITS != 8 && __builtin_amdgcn_readfirstlane(S.flag[buf]) == st;
+        if (b1 <= nb && !exact_shift) {
 #pragma unroll
-        for (int j = 0; j < C::kStep; ++j)
-            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
-        return;
-    }
-    for (int j = 0; j < C::kStep && b0 + j < nb; ++j) {
-        if (exact_shift)
-            block_mfma<BITS, NT, true>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
-        else
-            block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
+            for (int j = 0; j < C::kStep; ++j)
+                block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
+            return;
+        }
+        for (int j = 0; j < C::kStep && b0 + j < nb; ++j) {
+            if (exact_shift)
+                block_mfma<BITS, NT, true>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
+            else
+                block_mfma<BITS, NT, false>(S, buf, j, arow, r, g, acc, a, m, b0 + j);
+        }
     }
 }
 
@@ -519,14 +523,42 @@ struct LeanLane {
     uint32_t xo[2];       /* thread: element offset of activation load i's chunk of step 0 */
     uint32_t dof;      /* thread: index of its activation block scale of step 0 */
     int nsteps;
+    /* grouped launches: the wave's window of group-wise weight scales, the
+     * thread's row offset in it (row (l / 4) of the workgroup's 64, ng per
+     * row), blocks per scale (0: per-row segment, scale 1) and the divisor
+     * for block -> group (umulhi(b, magic) = b / gb exactly for b < 2^16) */
+    const float* wsb;
+    uint32_t wso, magic;
+    int gb, ng;
 };
 
-template <int BITS, int NT>
-__device__ __forceinline__ void lean_fetch(Stage<BITS, false>& P, const LeanLane& L, int st)
+/* Weight scales per thread and step in a grouped launch: 64 rows x kStep
+ * blocks over 256 threads. */
+template <int BITS>
+constexpr int kLeanWsPerThread = Cfg<BITS>::kStep / 4;
+
+template <int BITS, bool GW>
+struct LeanStage {
+    Stage<BITS, false> p;
+    float wsc[GW ? kLeanWsPerThread<BITS> : 1];
+};
+
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ void lean_fetch(LeanStage<BITS, GW>& Q, const LeanLane& L, int st)
 {
     using C = Cfg<BITS>;
+    Stage<BITS, false>& P = Q.p;
     /* steps past the row reload its last step (never multiplied) */
     const int s = min(st, L.nsteps - 1);
+    if constexpr (GW) {
+        /* thread l: row l / 4, blocks kLeanWsPerThread * (l % 4) + i of the step */
+#pragma unroll
+        for (int i = 0; i < kLeanWsPerThread<BITS>; ++i) {
+            const uint32_t b = (uint32_t)(s * C::kStep + kLeanWsPerThread<BITS> * ((int)threadIdx.x & 3) + i);
+            const uint32_t g = L.gb == 1 ? b : __umulhi(b, L.magic);
+            Q.wsc[i] = L.gb ? L.wsb[L.wso + min(g, (uint32_t)L.ng - 1u)] : 1.0f;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < LCfg<BITS>::kNL; ++i) {
         const u32x4 u = *reinterpret_cast<const u32x4*>(L.wb[i] + (size_t)s * (C::kRowWords * 4) + L.wo[i]);
@@ -567,12 +599,26 @@ __device__ __forceinline__ void prep_half(const uint32_t* x, uint32_t (&xa)[4])
     }
 }
 
-template <int BITS, int NT>
-__device__ __forceinline__ bool lean_commit(const Stage<BITS, false>& P, LeanLds<BITS>& S, int buf)
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ bool lean_commit(const LeanStage<BITS, GW>& Q, LeanLds<BITS, GW>& S, int buf)
 {
     constexpr int SHIFT = 8 - BITS;
     using LC = LCfg<BITS>;
+    const Stage<BITS, false>& P = Q.p;
     const int l = threadIdx.x;
+    bool bad_ws = false;
+    if constexpr (GW) {
+        /* a coefficient ws * d * 2^-(8-b) is the canonical product times an
+         * exact power of two while both factors lie in [2^-62, 2^62]
+         * (or one is zero): the product stays a normal number */
+#pragma unroll
+        for (int i = 0; i < kLeanWsPerThread<BITS>; ++i) {
+            const float v = Q.wsc[i];
+            S.ws[buf][kLeanWsPerThread<BITS> * (l & 3) + i][l >> 2] = v;
+            const float m = __builtin_fabsf(v);
+            bad_ws = bad_ws || (v != 0.0f && !(m >= 0x1p-62f && m <= 0x1p62f));
+        }
+    }
 #pragma unroll
     for (int i = 0; i < LC::kNL; ++i) {
         const int row = i * LC::kRowsPerLoad + l / LC::kCR;
@@ -598,22 +644,33 @@ __device__ __forceinline__ bool lean_commit(const Stage<BITS, false>& P, LeanLds
     const int j = lean_d_block<BITS>();
     const float ds = P.d * (1.0f / (float)(1 << SHIFT));
     S.ds[buf][j][tr][tn] = ds;
+    if constexpr (GW)
+        return bad_ws || (P.d != 0.0f && !(ds >= 0x1p-62f && ds <= 0x1p62f));
     return SHIFT != 0 && P.d != 0.0f && !(ds >= 1.17549435e-38f);
 }
 
 /* One block's LDS operands for a lane: its weight word(s), the B operand of
  * each N-tile and the tiles' block scales. */
-template <int BITS, int NT>
+template <int BITS, int NT, bool GW>
 struct LeanOps {
     uint32_t w[BITS == 8 ? 2 : 1];
     uint32_t b[2 * NT];
     float d[NT];
+    float ws[GW ? 4 : 1]; /* GW: the scales of the lane's rows 4g .. 4g+3 */
 };
 
-template <int BITS, int NT>
-__device__ __forceinline__ void lean_read(const LeanLds<BITS>& S, int buf, int j, const uint32_t* arow, int r,
-                                          int g, LeanOps<BITS, NT>& o)
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ void lean_read(const LeanLds<BITS, GW>& S, int buf, int j, const uint32_t* arow, int r,
+                                          int g, LeanOps<BITS, NT, GW>& o)
 {
+    if constexpr (GW) {
+        const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const float4 v = *reinterpret_cast<const float4*>(&S.ws[buf][j][16 * wv + 4 * g]);
+        o.ws[0] = v.x;
+        o.ws[1] = v.y;
+        o.ws[2] = v.z;
+        o.ws[3] = v.w;
+    }
     if constexpr (BITS == 8) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(arow + j * BITS + 2 * g);
         o.w[0] = v.x;
@@ -637,8 +694,8 @@ __device__ __forceinline__ void lean_read(const LeanLds<BITS>& S, int buf, int j
     }
 }
 
-template <int BITS, int NT>
-__device__ __forceinline__ void lean_mfma(const LeanOps<BITS, NT>& o, int g, i32x4 (&c)[NT])
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ void lean_mfma(const LeanOps<BITS, NT, GW>& o, int g, i32x4 (&c)[NT])
 {
     /* the A operand of a_operand(), from the one word lane group g needs */
     uint32_t lo, hi;
@@ -661,44 +718,50 @@ __device__ __forceinline__ void lean_mfma(const LeanOps<BITS, NT>& o, int g, i32
     }
 }
 
-template <int BITS, int NT>
-__device__ __forceinline__ void lean_fold(const LeanOps<BITS, NT>& o, const i32x4 (&c)[NT], float (&acc)[2][4])
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ void lean_fold(const LeanOps<BITS, NT, GW>& o, const i32x4 (&c)[NT], float (&acc)[2][4])
 {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            acc[n][v] = __builtin_fmaf(o.d[n], (float)c[n][v], acc[n][v]);
+        for (int v = 0; v < 4; ++v) {
+            /* GW: the coefficient is the fp32 product of the row's group scale
+             * and the token's block scale (times 2^-(8-b), exactly) */
+            const float coef = GW ? o.ws[GW ? v : 0] * o.d[n] : o.d[n];
+            acc[n][v] = __builtin_fmaf(coef, (float)c[n][v], acc[n][v]);
+            if constexpr (GW)
+                asm volatile("" : "+v"(acc[n][v])); /* keeps each block's fold in place */
+        }
 }
 
 /* One K step, software-pipelined over its blocks: while block j
  * multiplies, the operands of block j + 1 are read and block j - 1 is
  * folded, so neither an LDS read nor an MFMA result is waited for right
  * before its use. */
-template <int BITS, int NT>
-__device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float (&acc)[2][4], const FfnArgs& a,
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ void lean_step(const LeanLds<BITS, GW>& S, int buf, float (&acc)[2][4], const FfnArgs& a,
                                           const MDbg& m, int st)
 {
     using C = Cfg<BITS>;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const uint32_t* arow = &S.a[buf][(16 * wv + r) * LCfg<BITS>::kStride];
-    LeanOps<BITS, NT> o[3];
+    LeanOps<BITS, NT, GW> o[3];
     i32x4 c[2][NT];
-    lean_read<BITS, NT>(S, buf, 0, arow, r, g, o[0]);
+    lean_read<BITS, NT, GW>(S, buf, 0, arow, r, g, o[0]);
 #pragma unroll
     for (int j = 0; j <= C::kStep; ++j) {
         if (j + 1 < C::kStep)
-            lean_read<BITS, NT>(S, buf, j + 1, arow, r, g, o[(j + 1) % 3]);
+            lean_read<BITS, NT, GW>(S, buf, j + 1, arow, r, g, o[(j + 1) % 3]);
         __builtin_amdgcn_sched_barrier(0);
         if (j < C::kStep) {
-            lean_mfma<BITS, NT>(o[j % 3], g, c[j & 1]);
+            lean_mfma<BITS, NT, GW>(o[j % 3], g, c[j & 1]);
 #pragma unroll
             for (int n = 0; n < NT; ++n)
                 mdbg(a, m, c[j & 1][n], n, st * C::kStep + j, 8 - BITS);
         }
         if (j >= 1)
-            lean_fold<BITS, NT>(o[(j - 1) % 3], c[(j - 1) & 1], acc);
+            lean_fold<BITS, NT, GW>(o[(j - 1) % 3], c[(j - 1) & 1], acc);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -709,8 +772,8 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS>& S, int buf, float
  * registers lowered the occupancy and were slower.)  Returns true
  * (uniformly) when some step's scales were not exact with the 2^-(8-b)
  * factor taken out; acc is then void. */
-template <int BITS, int NT>
-__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, float (&acc)[2][4],
+template <int BITS, int NT, bool GW>
+__device__ __forceinline__ bool k_loop_lean(LeanLds<BITS, GW>& S, const LeanLane& L, float (&acc)[2][4],
                                             const FfnArgs& a, const MDbg& m)
 {
     constexpr int D = 2, U = 2;
@@ -719,34 +782,34 @@ __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS>& S, const LeanLane& L,
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             acc[n][v] = 0.0f;
-    Stage<BITS, false> P[D];
+    LeanStage<BITS, GW> P[D];
 #pragma unroll
     for (int k = 0; k < D; ++k)
-        lean_fetch<BITS, NT>(P[k], L, k);
-    bool bad = lean_commit<BITS, NT>(P[0], S, 0);
-    lean_fetch<BITS, NT>(P[0], L, D);
+        lean_fetch<BITS, NT, GW>(P[k], L, k);
+    bool bad = lean_commit<BITS, NT, GW>(P[0], S, 0);
+    lean_fetch<BITS, NT, GW>(P[0], L, D);
     __syncthreads();
 #pragma unroll 1
     for (int st = 0; st < L.nsteps; st += U) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int s = st + i;
-            lean_step<BITS, NT>(S, i & 1, acc, a, m, s);
-            bad |= lean_commit<BITS, NT>(P[(i + 1) % D], S, (i + 1) & 1);
-            lean_fetch<BITS, NT>(P[(i + 1) % D], L, s + 1 + D);
+            lean_step<BITS, NT, GW>(S, i & 1, acc, a, m, s);
+            bad |= lean_commit<BITS, NT, GW>(P[(i + 1) % D], S, (i + 1) & 1);
+            lean_fetch<BITS, NT, GW>(P[(i + 1) % D], L, s + 1 + D);
             __syncthreads();
         }
     }
     return __syncthreads_or(bad) != 0;
 }
 
-template <int BITS>
-__device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS>& S, const LeanLane& L, int ntiles,
+template <int BITS, bool GW>
+__device__ __forceinline__ bool mfma_k_loop_lean(LeanLds<BITS, GW>& S, const LeanLane& L, int ntiles,
                                                  float (&acc)[2][4], const FfnArgs& a, const MDbg& m)
 {
     if (ntiles > 1)
-        return k_loop_lean<BITS, 2>(S, L, acc, a, m);
-    return k_loop_lean<BITS, 1>(S, L, acc, a, m);
+        return k_loop_lean<BITS, 2, GW>(S, L, acc, a, m);
+    return k_loop_lean<BITS, 1, GW>(S, L, acc, a, m);
 }
 
 } // namespace
@@ -785,11 +848,21 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     const MDbg md = {sg.out_base + pos0, ntok, 32, kDbgGate, kDbgUp, M.rb * 32, M.rb * 32, a.I};
     float acc[2][4];
     bool general = true;
-    if constexpr (!GROUPED) {
+    {
         /* the aligned loop, while every activation offset fits 31 bits */
-        if (lean_shape<BITS>(nb) && (int64_t)sg.S * a.H < (int64_t(1) << 31)) {
+        if (lean_shape<BITS>(nb) && (int64_t)sg.S * a.H < (int64_t(1) << 31) && nb < 65536) {
             using LC = LCfg<BITS>;
             LeanLane LL;
+            LL.gb = GROUPED ? sg.gu_gb : 0;
+            LL.ng = LL.gb ? nb / LL.gb : 1;
+            LL.magic = LL.gb > 1 ? 0xFFFFFFFFu / (uint32_t)LL.gb + 1u : 0u;
+            {
+                /* scale rows: thread l takes row l / 4 (rows 0..31 gate, 32..63 up) */
+                const int rowt = (int)threadIdx.x >> 2;
+                const bool up = __builtin_amdgcn_readfirstlane(rowt) >= 32;
+                LL.wsb = LL.gb ? (up ? sg.up_s : sg.gate_s) + ((int64_t)e * a.I + M.rb * 32) * LL.ng : nullptr;
+                LL.wso = (uint32_t)(rowt & 31) * (uint32_t)LL.ng;
+            }
 #pragma unroll
             for (int i = 0; i < LC::kNL; ++i) {
                 /* rows 0..31 are gate rows, 32..63 the same up rows; a load's rows
@@ -817,7 +890,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
                 LL.dof = (uint32_t)tk * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
             }
             LL.nsteps = nb / Cfg<BITS>::kStep;
-            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc, a, md);
+            general = mfma_k_loop_lean<BITS, GROUPED>(sm.l, LL, ntiles, acc, a, md);
         }
     }
     if (general)
@@ -894,12 +967,21 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
     const MDbg md = {sg.out_base + pos0, ntok, 64, kDbgDown, kDbgDown, M.rb * 64, M.rb * 64, a.H};
     float acc[2][4];
     bool general = true;
-    if constexpr (!GROUPED) {
+    {
         /* the aligned loop, while the weight offsets in one matrix fit 31 bits */
-        if (lean_shape<BITS>(nb) && (int64_t)a.H * rowbytes < (int64_t(1) << 31)) {
+        if (lean_shape<BITS>(nb) && (int64_t)a.H * rowbytes < (int64_t(1) << 31) && nb < 65536) {
             using LC = LCfg<BITS>;
             const int64_t r0 = sg.out_base + pos0;
             LeanLane LL;
+            LL.gb = GROUPED ? sg.d_gb : 0;
+            LL.ng = LL.gb ? nb / LL.gb : 1;
+            LL.magic = LL.gb > 1 ? 0xFFFFFFFFu / (uint32_t)LL.gb + 1u : 0u;
+            {
+                /* scale rows: thread l takes row l / 4 of the workgroup's 64 */
+                const int rw = M.rb * 64 + ((int)threadIdx.x >> 2);
+                LL.wsb = LL.gb ? sg.down_s + (int64_t)e * a.H * LL.ng : nullptr;
+                LL.wso = (uint32_t)(rw < a.H ? rw : a.H - 1) * (uint32_t)LL.ng;
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int rw = M.rb * 64 + (i < LC::kNL ? i : 0) * LC::kRowsPerLoad + (int)threadIdx.x / LC::kCR;
@@ -918,7 +1000,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
                 LL.dof = (uint32_t)(td < ntok ? td : 0) * (uint32_t)nb + (uint32_t)lean_d_block<BITS>();
             }
             LL.nsteps = nb / Cfg<BITS>::kStep;
-            general = mfma_k_loop_lean<BITS>(sm.l, LL, ntiles, acc, a, md);
+            general = mfma_k_loop_lean<BITS, GROUPED>(sm.l, LL, ntiles, acc, a, md);
         }
     }
     if (general)

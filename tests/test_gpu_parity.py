@@ -219,6 +219,8 @@ def test_expert_ffn_bit_exact(qre, bits, H, I, E, S, k, scale):
     (256, 160, 2, 100, 2, 256, 32, 1.0),   # several MFMA units, ragged N tile
     (96, 96, 5, 40, 3, 32, 96, 1.0),       # MFMA with ragged rows and K tails
     (256, 128, 3, 24, 2, 32, 32, 1e-36),   # tiny activations (subnormal products)
+    (512, 512, 2, 40, 2, 32, 32, 1.0),     # aligned matrix-core loop, one scale per block
+    (1536, 512, 2, 40, 2, 96, 64, 1.0),    # aligned loop, three blocks per scale (block -> group divide)
 ])
 def test_expert_ffn_grouped_scales_bit_exact(qre, bits, H, I, E, S, k, g_gu, g_d, scale):
     """Group-wise weight scales on both kernel families, y bit for bit."""
