@@ -397,8 +397,10 @@ __device__ __forceinline__ void block_mfma_grouped(const KLds<BITS, true>& S, in
         mdbg(a, m, c, n, b, SHIFT);
         const float d = S.dr[buf][j][t];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v) {
             acc[n][v] = __builtin_fmaf(wsv[v] * d, (float)(c[v] >> SHIFT), acc[n][v]);
+            asm volatile("" : "+v"(acc[n][v])); /* keeps each block's fold in place */
+        }
     }
 }
 
@@ -656,21 +658,13 @@ struct LeanOps {
     uint32_t w[BITS == 8 ? 2 : 1];
     uint32_t b[2 * NT];
     float d[NT];
-    float ws[GW ? 4 : 1]; /* GW: the scales of the lane's rows 4g .. 4g+3 */
 };
 
 template <int BITS, int NT, bool GW>
 __device__ __forceinline__ void lean_read(const LeanLds<BITS, GW>& S, int buf, int j, const uint32_t* arow, int r,
                                           int g, LeanOps<BITS, NT, GW>& o)
 {
-    if constexpr (GW) {
-        const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const float4 v = *reinterpret_cast<const float4*>(&S.ws[buf][j][16 * wv + 4 * g]);
-        o.ws[0] = v.x;
-        o.ws[1] = v.y;
-        o.ws[2] = v.z;
-        o.ws[3] = v.w;
-    }
+
     if constexpr (BITS == 8) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(arow + j * BITS + 2 * g);
         o.w[0] = v.x;
@@ -719,15 +713,27 @@ __device__ __forceinline__ void lean_mfma(const LeanOps<BITS, NT, GW>& o, int g,
 }
 
 template <int BITS, int NT, bool GW>
-__device__ __forceinline__ void lean_fold(const LeanOps<BITS, NT, GW>& o, const i32x4 (&c)[NT], float (&acc)[2][4])
+__device__ __forceinline__ void lean_fold(const LeanOps<BITS, NT, GW>& o, const i32x4 (&c)[NT], float (&acc)[2][4],
+                                          const LeanLds<BITS, GW>& S, int buf, int j, int g)
 {
+    float ws[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (GW) {
+        /* the group scales of the lane's rows 4g .. 4g+3 for block j, read at
+         * the fold (not carried in the operand ring) */
+        const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const float4 v = *reinterpret_cast<const float4*>(&S.ws[buf][j][16 * wv + 4 * g]);
+        ws[0] = v.x;
+        ws[1] = v.y;
+        ws[2] = v.z;
+        ws[3] = v.w;
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             /* GW: the coefficient is the fp32 product of the row's group scale
              * and the token's block scale (times 2^-(8-b), exactly) */
-            const float coef = GW ? o.ws[GW ? v : 0] * o.d[n] : o.d[n];
+            const float coef = GW ? ws[v] * o.d[n] : o.d[n];
             acc[n][v] = __builtin_fmaf(coef, (float)c[n][v], acc[n][v]);
             if constexpr (GW)
                 asm volatile("" : "+v"(acc[n][v])); /* keeps each block's fold in place */
@@ -761,7 +767,7 @@ __device__ __forceinline__ void lean_step(const LeanLds<BITS, GW>& S, int buf, f
                 mdbg(a, m, c[j & 1][n], n, st * C::kStep + j, 8 - BITS);
         }
         if (j >= 1)
-            lean_fold<BITS, NT, GW>(o[(j - 1) % 3], c[(j - 1) & 1], acc);
+            lean_fold<BITS, NT, GW>(o[(j - 1) % 3], c[(j - 1) & 1], acc, S, buf, j - 1, g);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -831,18 +837,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
         return;
     const int nb = a.H / 32;
     const int64_t rowbytes = (int64_t)a.H * BITS / 8;
-    /* load lanes: row dot l >> 2 (gate rows 0..31, then the same up rows) and
-     * token l & 31 (tokens past the unit load its first token) */
-    const int rd = threadIdx.x >> 2, tl = threadIdx.x & 31;
-    LoadLane L;
-    L.wrow = (rd < 32 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + M.rb * 32 + (rd & 31)) * rowbytes;
-    const int tok = token_of_m(sg, pos0 + (tl < ntok ? tl : 0));
-    L.xrow = a.xq + (int64_t)tok * a.H;
-    L.xdrow = a.xd + (int64_t)tok * nb;
-    L.nb = nb;
-    L.gb = GROUPED ? sg.gu_gb : 0;
-    L.wsrow = L.gb ? (rd < 32 ? sg.gate_s : sg.up_s) + ((int64_t)e * a.I + M.rb * 32 + (rd & 31)) * (nb / L.gb)
-                   : nullptr;
+    const int gbv = GROUPED ? sg.gu_gb : 0;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
     const MDbg md = {sg.out_base + pos0, ntok, 32, kDbgGate, kDbgUp, M.rb * 32, M.rb * 32, a.I};
@@ -893,8 +888,22 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
             general = mfma_k_loop_lean<BITS, GROUPED>(sm.l, LL, ntiles, acc, a, md);
         }
     }
-    if (general)
+    if (general) {
+        /* load lanes: row dot l >> 2 (gate rows 0..31, then the same up rows)
+         * and token l & 31 (tokens past the unit load its first token); set up
+         * here, so that nothing of it is live across the aligned loop */
+        const int rd = threadIdx.x >> 2, tl = threadIdx.x & 31;
+        LoadLane L;
+        L.wrow = (rd < 32 ? sg.gate_w : sg.up_w) + ((int64_t)e * a.I + M.rb * 32 + (rd & 31)) * rowbytes;
+        const int tok = token_of_m(sg, pos0 + (tl < ntok ? tl : 0));
+        L.xrow = a.xq + (int64_t)tok * a.H;
+        L.xdrow = a.xd + (int64_t)tok * nb;
+        L.nb = nb;
+        L.gb = gbv;
+        L.wsrow = L.gb ? (rd < 32 ? sg.gate_s : sg.up_s) + ((int64_t)e * a.I + M.rb * 32 + (rd & 31)) * (nb / L.gb)
+                       : nullptr;
         mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc, a, md);
+    }
 
     /* epilogue: scaled g (row dots 0..31) and u (32..63) through LDS, then
      * h = silu(g) * u and one Q8_0 block of h per token */
@@ -902,7 +911,7 @@ __global__ __launch_bounds__(256) void ffn_gate_up_mfma(FfnArgs a)
     for (int v = 0; v < 4; ++v) {
         const int rdot = 16 * wv + 4 * g + v;
         const float sc =
-            L.gb ? 1.0f : (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
+            gbv ? 1.0f : (rdot < 32 ? sg.gate_s : sg.up_s)[(int64_t)e * a.I + M.rb * 32 + (rdot & 31)];
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
@@ -952,16 +961,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
         return;
     const int nb = a.I / 32;
     const int64_t rowbytes = (int64_t)a.I * BITS / 8;
-    const int rd = threadIdx.x >> 2, tl = threadIdx.x & 31;
-    const int row = M.rb * 64 + rd;
-    LoadLane L;
-    L.wrow = sg.down_w + ((int64_t)e * a.H + (row < a.H ? row : 0)) * rowbytes;
-    const int64_t row_in = sg.out_base + pos0 + (tl < ntok ? tl : 0);
-    L.xrow = a.hq + row_in * a.I;
-    L.xdrow = a.hd + row_in * nb;
-    L.nb = nb;
-    L.gb = GROUPED ? sg.d_gb : 0;
-    L.wsrow = L.gb ? sg.down_s + ((int64_t)e * a.H + (row < a.H ? row : 0)) * (nb / L.gb) : nullptr;
+    const int gbv = GROUPED ? sg.d_gb : 0;
     const int ntiles = (ntok + 15) / 16;
     const int r = lane & 15, g = lane >> 4;
     const MDbg md = {sg.out_base + pos0, ntok, 64, kDbgDown, kDbgDown, M.rb * 64, M.rb * 64, a.H};
@@ -1003,14 +1003,26 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
             general = mfma_k_loop_lean<BITS, GROUPED>(sm.l, LL, ntiles, acc, a, md);
         }
     }
-    if (general)
+    if (general) {
+        /* load lanes (set up here: nothing of it is live across the aligned loop) */
+        const int rd = threadIdx.x >> 2, tl = threadIdx.x & 31;
+        const int row = M.rb * 64 + rd;
+        LoadLane L;
+        L.wrow = sg.down_w + ((int64_t)e * a.H + (row < a.H ? row : 0)) * rowbytes;
+        const int64_t row_in = sg.out_base + pos0 + (tl < ntok ? tl : 0);
+        L.xrow = a.hq + row_in * a.I;
+        L.xdrow = a.hd + row_in * nb;
+        L.nb = nb;
+        L.gb = gbv;
+        L.wsrow = L.gb ? sg.down_s + ((int64_t)e * a.H + (row < a.H ? row : 0)) * (nb / L.gb) : nullptr;
         mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc, a, md);
+    }
 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int rr = 16 * wv + 4 * g + v;
         const int n_out = M.rb * 64 + rr;
-        const float sc = n_out < a.H ? (L.gb ? 1.0f : sg.down_s[(int64_t)e * a.H + n_out]) : 0.0f;
+        const float sc = n_out < a.H ? (gbv ? 1.0f : sg.down_s[(int64_t)e * a.H + n_out]) : 0.0f;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             if (n < ntiles)
