@@ -176,8 +176,10 @@ def stage_kernel(w, stage):
     if w.S == 1:
         return {"gate_up": f"ffn_gate_up_decode<{w.bits}> (top-k selection + gate/up GEMV)",
                 "down": f"ffn_down_combine_decode<{w.bits}> (down GEMV + weighted combine)"}[stage]
-    if w.S < 8:
+    if w.S <= 8:  # small batches stay on the GEMV kernels
         return f"ffn_{stage}_rows<{w.bits}>"
+    if w.S * w.top_k >= 8 * w.n_experts:  # 8 or more pairs per expert: every expert on the matrix cores
+        return f"ffn_{stage}_mfma<{w.bits}>"
     return f"ffn_{stage}_rows<{w.bits}> + ffn_{stage}_mfma<{w.bits}>"
 
 

@@ -237,14 +237,15 @@ int colibri_expert_ffn_q(const coli_qbank* gate, const coli_qbank* up, const col
     UnitLists ul;
     ul.units = at<Unit>(ws, Lo.units);
     ul.n_units = at<int32_t>(ws, Lo.n_units);
-    ul.max_units = max_gemv_units(rows, n_mat);
+    ul.max_units = max_gemv_units(rows, n_mat, kMfmaMinTokens);
     ul.munits = at<Unit>(ws, Lo.munits);
     ul.n_munits = at<int32_t>(ws, Lo.n_munits);
     ul.max_munits = ffn_max_munits(rows, n_mat);
+    ul.mfma_min = kMfmaMinTokens;
     hipError_t e = launch_schedule(expert_offsets, n_mat, ul, s);
     FfnArgs a;
     debug_attach(a);
-    a.seg[0] = make_seg(gate, up, down, sorted_pairs, &ul, k, S, rows, 0);
+    a.seg[0] = make_seg(gate, up, down, sorted_pairs, &ul, k, S, rows, 0, ul.mfma_min);
     a.seg[1] = a.seg[0];
     a.nseg = 1;
     a.unit_tokens = kUnitTokens; /* caller offsets: units may hold several tokens */
@@ -297,13 +298,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     int32_t* inv = at<int32_t>(ws, Lo.inv);
     int32_t* active = at<int32_t>(ws, Lo.active);
     int32_t* n_active = at<int32_t>(ws, Lo.n_active);
-    UnitLists ul;
-    ul.units = at<Unit>(ws, Lo.units);
-    ul.n_units = at<int32_t>(ws, Lo.n_units);
-    ul.max_units = max_gemv_units(P, E);
-    ul.munits = at<Unit>(ws, Lo.munits);
-    ul.n_munits = at<int32_t>(ws, Lo.n_munits);
-    ul.max_munits = max_mfma_units(P, E, S);
+    const UnitLists ul = layer_unit_lists(ws, Lo, P, E, S);
     float* y = at<float>(ws, Lo.y);
 
     auto mark = [&](int i, hipError_t prev) -> hipError_t {
@@ -313,7 +308,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     };
     FfnArgs a;
     debug_attach(a);
-    a.seg[0] = make_seg(&L->gate, &L->up, &L->down, sorted, &ul, k, S, P, 0);
+    a.seg[0] = make_seg(&L->gate, &L->up, &L->down, sorted, &ul, k, S, P, 0, ul.mfma_min);
     a.nseg = 1;
     a.unit_tokens = S == 1 ? 1 : kUnitTokens; /* distinct experts per token */
     a.H = H;
@@ -325,7 +320,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
     a.y = y;
     FfnArgs b = a; /* shared expert, when it cannot share the routed launch */
     if (shared) {
-        FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P);
+        FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P, ul.mfma_min);
         if (L->sh_gate.qtype == L->gate.qtype && L->sh_down.qtype == L->down.qtype) {
             a.seg[1] = sh;
             a.nseg = 2;

@@ -73,16 +73,17 @@ __device__ __forceinline__ void emit_units(Unit* units, int32_t ubase, int32_t e
     }
 }
 
-/* Unit counts of an expert with c positions: (GEMV units, MFMA units). */
-__device__ __forceinline__ void unit_counts(int32_t c, int32_t& nu_g, int32_t& nu_m)
+/* Unit counts of an expert with c positions under matrix-core threshold
+ * mmin: (GEMV units, MFMA units). */
+__device__ __forceinline__ void unit_counts(int32_t c, int32_t mmin, int32_t& nu_g, int32_t& nu_m)
 {
-    const bool big = c >= kMfmaMinTokens;
+    const bool big = c >= mmin;
     nu_g = big ? 0 : (c + kUnitTokens - 1) / kUnitTokens;
     nu_m = big ? (c + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
 }
 
 /* Packed per-expert counts for one workgroup scan: positions (bits 0..20),
- * active flag (21..31), GEMV units (32..43), MFMA units (44..58).  With at
+ * active flag (21..31), GEMV units (32..43), MFMA units (44..63).  With at
  * most 2^20 pairs and 1024 experts no field can carry into the next. */
 __device__ __forceinline__ uint64_t pack_counts(int32_t c, int32_t nu_g, int32_t nu_m)
 {
@@ -152,7 +153,7 @@ __device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t
     const int32_t e = tid;
     const int32_t c = e < E ? cnt[e] : 0;
     int32_t nu_g, nu_m;
-    unit_counts(c, nu_g, nu_m);
+    unit_counts(c, ul ? ul->mfma_min : kMfmaMinTokens, nu_g, nu_m);
     uint64_t tot;
     const uint64_t pre = block_exclusive_scan<uint64_t>(pack_counts(c, nu_g, nu_m), sh.tmp, &tot);
     const int32_t off = (int32_t)(pre & 0x1FFFFF);
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kDispThreads) void schedule_kernel(const int32_t* _
     const int32_t off = e < n_mat ? offsets[e] : 0;
     const int32_t c = e < n_mat ? min(max(0, offsets[e + 1] - off), kPairLimit) : 0;
     int32_t nu_g, nu_m;
-    unit_counts(c, nu_g, nu_m);
+    unit_counts(c, ul.mfma_min, nu_g, nu_m);
     uint64_t tot;
     const uint64_t pre = block_exclusive_scan<uint64_t>(pack_counts(c, nu_g, nu_m), tmp, &tot);
     if (e < n_mat) {

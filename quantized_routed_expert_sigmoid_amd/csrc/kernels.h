@@ -15,9 +15,10 @@ namespace coli {
  * more tokens are split into several units. */
 constexpr int kUnitTokens = 4;
 
-/* Experts holding at least this many tokens of a batch run on the int8
+/* Experts holding at least a threshold of tokens of a batch run on the int8
  * matrix cores (ffn_mfma.hip) in units of up to kMfmaUnitTokens tokens;
- * experts with fewer run on the GEMV kernels (ffn_gemv.hip). */
+ * experts with fewer run on the GEMV kernels (ffn_gemv.hip).  The threshold
+ * is kMfmaMinTokens, except in a layer's routed batch (layer_mfma_min). */
 constexpr int kMfmaMinTokens = 8;
 constexpr int kMfmaUnitTokens = 32;
 
@@ -49,12 +50,13 @@ struct Unit {
 
 /* Device unit lists written by the dispatch (or schedule) kernel. */
 struct UnitLists {
-    Unit* units;       /* GEMV units (experts with < kMfmaMinTokens tokens) */
+    Unit* units;       /* GEMV units (experts with < mfma_min tokens) */
     int32_t* n_units;
     int32_t max_units;
     Unit* munits;      /* MFMA units */
     int32_t* n_munits;
     int32_t max_munits;
+    int32_t mfma_min;  /* fewest tokens of an expert on the matrix cores */
 };
 
 /* One group of experts run by the FFN kernels.  A group with units ==
@@ -156,35 +158,53 @@ struct DecodeArgs {
     const int32_t* slot_of;
 };
 
-/* Bounds on the unit counts of a routed group with P pairs of S tokens over
- * E experts (n_e pairs each, sum P, n_e <= S).  GEMV: experts with n_e <
- * kMfmaMinTokens give ceil(n_e / 4) <= 2 units each.  MFMA: experts with
- * n_e >= kMfmaMinTokens give ceil(n_e / 32) <= n_e / 32 + 1 units each. */
-inline int32_t max_gemv_units(int64_t P, int32_t E)
+/* The matrix-core threshold of a layer's batch of S tokens (P pairs over E
+ * experts).  Small batches (S <= kSmallS) stay on the GEMV kernels, so they
+ * launch no matrix-core kernel at all.  A batch with at least kMfmaMinTokens
+ * pairs per expert on average runs every expert on the matrix cores and
+ * launches no GEMV kernel: its few small experts cost less there than the
+ * GEMV launches' worst-case grids.  In between, kMfmaMinTokens. */
+inline int32_t layer_mfma_min(int64_t P, int32_t E, int32_t S)
 {
+    if (S <= kSmallS)
+        return kSmallS + 1;
+    if (P >= (int64_t)kMfmaMinTokens * E)
+        return 1;
+    return kMfmaMinTokens;
+}
+
+/* Bounds on the unit counts of a routed group with P pairs over E experts
+ * (n_e pairs each, sum P) and threshold mmin.  GEMV: experts with n_e < mmin
+ * give ceil(n_e / kUnitTokens) units each, at most ceil((mmin - 1) /
+ * kUnitTokens).  MFMA: experts with n_e >= mmin give ceil(n_e / 32) <=
+ * n_e / 32 + 1 units each; none when the batch has fewer than mmin tokens
+ * per expert at most (S < mmin, S = the most pairs one expert can hold). */
+inline int32_t max_gemv_units(int64_t P, int32_t E, int32_t mmin)
+{
+    const int64_t per = (mmin - 1 + kUnitTokens - 1) / kUnitTokens;
     const int64_t active = P < E ? P : E;
     const int64_t a = (P + (kUnitTokens - 1) * active) / kUnitTokens;
-    const int64_t b = 2 * active;
+    const int64_t b = per * active;
     return (int32_t)(a < b ? a : b);
 }
 
-inline int32_t max_mfma_units(int64_t P, int32_t E, int32_t S)
+inline int32_t max_mfma_units(int64_t P, int32_t E, int32_t S, int32_t mmin)
 {
-    if (S < kMfmaMinTokens)
+    if (S < mmin)
         return 0;
-    const int64_t big = P / kMfmaMinTokens < E ? P / kMfmaMinTokens : E;
+    const int64_t big = P / mmin < E ? P / mmin : E;
     return (int32_t)(P / kMfmaUnitTokens + big + 1);
 }
 
 /* Units of a one-expert identity group over S tokens. */
-inline int32_t identity_gemv_units(int32_t S)
+inline int32_t identity_gemv_units(int32_t S, int32_t mmin)
 {
-    return S >= kMfmaMinTokens ? 0 : (S + kUnitTokens - 1) / kUnitTokens;
+    return S >= mmin ? 0 : (S + kUnitTokens - 1) / kUnitTokens;
 }
 
-inline int32_t identity_mfma_units(int32_t S)
+inline int32_t identity_mfma_units(int32_t S, int32_t mmin)
 {
-    return S >= kMfmaMinTokens ? (S + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
+    return S >= mmin ? (S + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
 }
 
 /* K slices of the many-token router logits (S > kSmallS): enough 64 x 64

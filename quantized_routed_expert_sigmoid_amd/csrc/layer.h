@@ -129,12 +129,13 @@ inline Layout layer_layout(int32_t H, int32_t I, int32_t E, int32_t k, int32_t S
 {
     const int64_t P = (int64_t)S * k;
     const int64_t rows = P + extra_rows + (shared ? S : 0);
+    const int32_t mmin = layer_mfma_min(P, E, S);
     Bump b;
     Layout L;
     L.logits = b.take((size_t)router_parts(S, E, H) * S * E * 4);
-    L.units = b.take((size_t)max_gemv_units(P, E) * sizeof(Unit));
+    L.units = b.take((size_t)max_gemv_units(P, E, mmin) * sizeof(Unit));
     L.n_units = b.take(16);
-    L.munits = b.take((size_t)max_mfma_units(P, E, S) * sizeof(Unit));
+    L.munits = b.take((size_t)max_mfma_units(P, E, S, mmin) * sizeof(Unit));
     L.n_munits = b.take(16);
     L.hq = b.take((size_t)rows * I);
     L.hd = b.take((size_t)rows * (I / 32) * 4);
@@ -160,7 +161,7 @@ struct FfnLayout {
  * every expert may reach the MFMA threshold: bound with the largest S. */
 inline int32_t ffn_max_munits(int64_t rows, int32_t n_mat)
 {
-    return max_mfma_units(rows, n_mat, kMfmaMinTokens);
+    return max_mfma_units(rows, n_mat, kMfmaMinTokens, kMfmaMinTokens);
 }
 
 inline FfnLayout ffn_layout(int32_t H, int32_t I, int32_t n_mat, int32_t S, int32_t k)
@@ -169,7 +170,7 @@ inline FfnLayout ffn_layout(int32_t H, int32_t I, int32_t n_mat, int32_t S, int3
     const int64_t rows = (int64_t)S * k;
     Bump b;
     FfnLayout L;
-    L.units = b.take((size_t)max_gemv_units(rows, n_mat) * sizeof(Unit));
+    L.units = b.take((size_t)max_gemv_units(rows, n_mat, kMfmaMinTokens) * sizeof(Unit));
     L.n_units = b.take(16);
     L.munits = b.take((size_t)ffn_max_munits(rows, n_mat) * sizeof(Unit));
     L.n_munits = b.take(16);
@@ -183,6 +184,21 @@ template <typename T>
 inline T* at(void* ws, size_t off)
 {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+/* The unit lists of a layer's routed batch (P pairs of S tokens over E
+ * experts) in a workspace laid out by layer_layout. */
+inline UnitLists layer_unit_lists(void* ws, const Layout& Lo, int64_t P, int32_t E, int32_t S)
+{
+    UnitLists ul;
+    ul.units = at<Unit>(ws, Lo.units);
+    ul.n_units = at<int32_t>(ws, Lo.n_units);
+    ul.munits = at<Unit>(ws, Lo.munits);
+    ul.n_munits = at<int32_t>(ws, Lo.n_munits);
+    ul.mfma_min = layer_mfma_min(P, E, S);
+    ul.max_units = max_gemv_units(P, E, ul.mfma_min);
+    ul.max_munits = max_mfma_units(P, E, S, ul.mfma_min);
+    return ul;
 }
 
 #ifdef COLI_DEBUG_PARTIALS
@@ -207,9 +223,10 @@ inline int hip_status(hipError_t e)
 }
 
 /* A routed group (ul != nullptr: unit lists from the dispatch or schedule
- * kernel) or the identity group of the shared expert (ul == nullptr). */
+ * kernel) or the identity group of the shared expert (ul == nullptr), which
+ * runs on the matrix cores when S >= mmin (the routed batch's threshold). */
 inline FfnSeg make_seg(const coli_qbank* g, const coli_qbank* u, const coli_qbank* d, const int32_t* sorted,
-                const UnitLists* ul, int32_t k, int32_t S, int32_t rows, int32_t out_base)
+                const UnitLists* ul, int32_t k, int32_t S, int32_t rows, int32_t out_base, int32_t mmin)
 {
     FfnSeg s;
     s.gate_w = static_cast<const uint8_t*>(g->data);
@@ -223,8 +240,8 @@ inline FfnSeg make_seg(const coli_qbank* g, const coli_qbank* u, const coli_qban
     s.n_units = ul ? ul->n_units : nullptr;
     s.munits = ul ? ul->munits : nullptr;
     s.n_munits = ul ? ul->n_munits : nullptr;
-    s.max_units = ul ? ul->max_units : identity_gemv_units(S);
-    s.max_munits = ul ? ul->max_munits : identity_mfma_units(S);
+    s.max_units = ul ? ul->max_units : identity_gemv_units(S, mmin);
+    s.max_munits = ul ? ul->max_munits : identity_mfma_units(S, mmin);
     s.k = k;
     s.out_base = out_base;
     s.S = S;

@@ -257,20 +257,14 @@ hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const in
     const int32_t H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k;
     const int32_t P = S * k;
     int32_t* sorted = at<int32_t>(ws, Lo.l.sorted);
-    UnitLists ul;
-    ul.units = at<Unit>(ws, Lo.l.units);
-    ul.n_units = at<int32_t>(ws, Lo.l.n_units);
-    ul.max_units = max_gemv_units(P, E);
-    ul.munits = at<Unit>(ws, Lo.l.munits);
-    ul.n_munits = at<int32_t>(ws, Lo.l.n_munits);
-    ul.max_munits = max_mfma_units(P, E, S);
+    const UnitLists ul = layer_unit_lists(ws, Lo.l, P, E, S);
 
     hipError_t e = launch_dispatch_pass(codes, pass, base, S, k, t->n_slots, at<int32_t>(ws, Lo.l.offsets),
                                         sorted, at<int32_t>(ws, Lo.l.inv), at<int32_t>(ws, Lo.l.active),
                                         at<int32_t>(ws, Lo.l.n_active), ul, s);
     FfnArgs a;
     debug_attach(a);
-    a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], sorted, &ul, k, S, P, base);
+    a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], sorted, &ul, k, S, P, base, ul.mfma_min);
     a.nseg = 1;
     a.unit_tokens = S == 1 ? 1 : kUnitTokens;
     a.H = H;
@@ -283,7 +277,7 @@ hipError_t run_pass(const coli_tier* t, const TierLayout& Lo, void* ws, const in
     FfnArgs b = a;
     b.nseg = 0;
     if (with_shared) {
-        const FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, 2 * P);
+        const FfnSeg sh = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, 2 * P, ul.mfma_min);
         if (L->sh_gate.qtype == t->slot[0].qtype && L->sh_down.qtype == t->slot[2].qtype) {
             a.seg[1] = sh;
             a.nseg = 2;
@@ -589,19 +583,13 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
             e = hipStreamWaitEvent(s, t->ev_pfplan, 0);
             t->prefetch_pending = false;
         }
-        UnitLists ul;
-        ul.units = at<Unit>(ws, Lo.l.units);
-        ul.n_units = at<int32_t>(ws, Lo.l.n_units);
-        ul.max_units = max_gemv_units(P, E);
-        ul.munits = at<Unit>(ws, Lo.l.munits);
-        ul.n_munits = at<int32_t>(ws, Lo.l.n_munits);
-        ul.max_munits = max_mfma_units(P, E, S);
+        const UnitLists ul = layer_unit_lists(ws, Lo.l, P, E, S);
         FfnArgs a;
         debug_attach(a);
-        a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], at<int32_t>(ws, Lo.l.sorted), &ul, k, S, P, 0);
+        a.seg[0] = make_seg(&t->slot[0], &t->slot[1], &t->slot[2], at<int32_t>(ws, Lo.l.sorted), &ul, k, S, P, 0, ul.mfma_min);
         a.nseg = 1;
         if (shared) {
-            a.seg[1] = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P);
+            a.seg[1] = make_seg(&L->sh_gate, &L->sh_up, &L->sh_down, nullptr, nullptr, 1, S, S, P, ul.mfma_min);
             a.nseg = 2;
         }
         a.unit_tokens = 1;

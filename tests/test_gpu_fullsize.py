@@ -5,7 +5,8 @@ colibri_moe_layer_forward over the whole batch): routing ids for every
 token, and complete output rows for every token at S <= 4 and, at S = 512
 and S = 2048, for a sample that holds random tokens, the last token of each
 of the 8 most loaded experts (their ragged last matrix-core unit) and tokens
-of experts on the GEMV units (fewer than 8 tokens).
+of experts with fewer than 8 tokens (at these sizes, with 8 or more pairs per
+expert on average, the layer runs them on the matrix cores too).
 
 Unit level, at S = 512 and S = 2048, through the stage calls over the whole
 batch (route, dispatch, expert FFN): the expert outputs y, which are
@@ -31,7 +32,7 @@ pytestmark = pytest.mark.gpu
 
 _LAYERS = {}
 _X = {}
-MFMA_MIN, MFMA_UNIT = 8, 32  # experts with >= 8 tokens run in units of 32 on the matrix cores
+MFMA_MIN, MFMA_UNIT = 8, 32  # stage calls: experts with >= 8 tokens run in units of 32 on the matrix cores
 N_THREADS = 16               # oracle calls release the GIL
 
 
@@ -118,7 +119,7 @@ def test_full_size_layer(qre, name, n_sample):
         # the last token of each of the 8 most loaded experts (ragged last unit)
         for e in _hot_experts(pos):
             tokens.add(int(srt[pos[e][-1]]) // w.top_k)
-        # tokens of experts on the GEMV units
+        # tokens of experts with fewer than 8 tokens (single small matrix-core units)
         small = [e for e in sorted(pos) if len(pos[e]) < MFMA_MIN][:3]
         for e in small:
             tokens.add(int(srt[pos[e][0]]) // w.top_k)

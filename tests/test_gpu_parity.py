@@ -267,7 +267,9 @@ SMALL_LAYERS = {
                      top_k=4, S=24, has_shared=True, rsf=2.5, var_router=1.0 / 1024, var_bias=1e-4),
     "one_expert": dict(name="one", layer="one", n_experts=4, top_k=1, S=5),
     "all_experts": dict(name="all", layer="all", n_experts=8, top_k=8, S=6, has_shared=True),
-    # experts with >= 8 tokens and a shared expert over S >= 8 run on the matrix cores
+    # S > 8: experts with >= 8 tokens and the shared expert run on the matrix
+    # cores, every expert when the batch has 8 or more pairs per expert
+    # (mfma_int4, mfma_int2_long); mfma_int8_mixed mixes both paths
     "mfma_int4": dict(name="mf4", layer="mf4", bits=4, hidden=512, inter=256, n_experts=8, top_k=2,
                       S=64, has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
     "mfma_int8_mixed": dict(name="mf8", layer="mf8", bits=8, hidden=256, inter=128, n_experts=32,
