@@ -122,8 +122,8 @@ struct PassIds {
 template <typename Ids>
 __device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t k, int32_t E,
                                               int32_t* offsets, int32_t* sorted, int32_t* inv,
-                                              int32_t* active, int32_t* n_active, const UnitLists* ul,
-                                              DispatchShared& sh, int32_t inv_base = 0,
+                                              int32_t* active, int32_t* n_active, const UnitLists& ul,
+                                              bool has_ul, DispatchShared& sh, int32_t inv_base = 0,
                                               bool mark_dropped = true)
 {
     int32_t* cnt = sh.cnt;
@@ -141,10 +141,18 @@ __device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t
     /* a negative id is a dropped slot (no pair); ids past E - 1 violate the
      * documented precondition and are clamped so that no access leaves its
      * buffer */
-    for (int32_t p = tid; p < P; p += kDispThreads) {
-        const int32_t id = ids(p);
-        if (id >= 0)
-            atomicAdd(&cnt[min(id, E - 1)], 1);
+    /* eight ids per thread in flight before their counts (clamped loads,
+     * masked after), so the count pass costs one memory round trip per
+     * 8 * kDispThreads pairs */
+    for (int32_t p0 = 0; p0 < P; p0 += 8 * kDispThreads) {
+        int32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            v[q] = ids(min(p0 + q * kDispThreads + tid, P - 1));
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (p0 + q * kDispThreads + tid < P && v[q] >= 0)
+                atomicAdd(&cnt[min(v[q], E - 1)], 1);
     }
     __syncthreads();
 
@@ -153,7 +161,7 @@ __device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t
     const int32_t e = tid;
     const int32_t c = e < E ? cnt[e] : 0;
     int32_t nu_g, nu_m;
-    unit_counts(c, ul ? ul->mfma_min : kMfmaMinTokens, nu_g, nu_m);
+    unit_counts(c, has_ul ? ul.mfma_min : kMfmaMinTokens, nu_g, nu_m);
     uint64_t tot;
     const uint64_t pre = block_exclusive_scan<uint64_t>(pack_counts(c, nu_g, nu_m), sh.tmp, &tot);
     const int32_t off = (int32_t)(pre & 0x1FFFFF);
@@ -165,17 +173,17 @@ __device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t
         offsets[e] = off;
         if (c > 0)
             active[aidx] = e;
-        if (ul) {
-            emit_units(ul->units, gbase, e, off, nu_g ? c : 0, kUnitTokens, ul->max_units);
-            emit_units(ul->munits, mbase, e, off, nu_m ? c : 0, kMfmaUnitTokens, ul->max_munits);
+        if (has_ul) {
+            emit_units(ul.units, gbase, e, off, nu_g ? c : 0, kUnitTokens, ul.max_units);
+            emit_units(ul.munits, mbase, e, off, nu_m ? c : 0, kMfmaUnitTokens, ul.max_munits);
         }
     }
     if (tid == 0) {
         offsets[E] = (int32_t)(tot & 0x1FFFFF); /* pairs kept */
         *n_active = (int32_t)((tot >> 21) & 0x7FF);
-        if (ul) {
-            *ul->n_units = min((int32_t)((tot >> 32) & 0xFFF), ul->max_units);
-            *ul->n_munits = min((int32_t)(tot >> 44), ul->max_munits);
+        if (has_ul) {
+            *ul.n_units = min((int32_t)((tot >> 32) & 0xFFF), ul.max_units);
+            *ul.n_munits = min((int32_t)(tot >> 44), ul.max_munits);
         }
     }
     __syncthreads();
@@ -185,9 +193,13 @@ __device__ __forceinline__ void dispatch_body(const Ids& ids, int32_t S, int32_t
     while ((1 << nbits) < E)
         ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    /* each round's id is loaded during the previous round */
+    int32_t id_next = P > 0 ? ids(min(tid, P - 1)) : -1;
     for (int32_t r0 = 0; r0 < P; r0 += kDispThreads) {
         const int32_t p = r0 + tid;
-        const int32_t id = p < P ? ids(p) : -1;
+        const int32_t id = p < P ? id_next : -1;
+        if (r0 + kDispThreads < P)
+            id_next = ids(min(r0 + kDispThreads + tid, P - 1));
         const bool valid = id >= 0;
         const int32_t ex = valid ? min(id, E - 1) : 0;
         if (p < P && !valid && inv && mark_dropped)
@@ -228,8 +240,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_kernel(
     int32_t* __restrict__ n_active, UnitLists ul, int32_t has_units)
 {
     __shared__ DispatchShared sh;
-    dispatch_body(PlainIds{ids}, S, k, E, offsets, sorted, inv, active, n_active,
-                  has_units ? &ul : nullptr, sh);
+    dispatch_body(PlainIds{ids}, S, k, E, offsets, sorted, inv, active, n_active, ul, has_units != 0, sh);
 }
 
 hipError_t launch_dispatch(const int32_t* ids, int32_t S, int32_t k, int32_t E, int32_t* offsets,
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_pass_kernel(
     UnitLists ul)
 {
     __shared__ DispatchShared sh;
-    dispatch_body(PassIds{codes, pass}, S, k, n_slots, offsets, sorted, inv, active, n_active, &ul, sh,
+    dispatch_body(PassIds{codes, pass}, S, k, n_slots, offsets, sorted, inv, active, n_active, ul, true, sh,
                   inv_base, pass == 0);
 }
 
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
         select_token(logits + (int64_t)wv * E, bias, E, k, rsf, ids + (int64_t)wv * k,
                      weights + (int64_t)wv * k, sel_s[wv], sel_ids + wv * k, 1, 0, opt);
     __syncthreads();
-    dispatch_body(PlainIds{sel_ids}, S, k, E, offsets, sorted, inv, active, n_active, &ul, sh);
+    dispatch_body(PlainIds{sel_ids}, S, k, E, offsets, sorted, inv, active, n_active, ul, true, sh);
 }
 
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,

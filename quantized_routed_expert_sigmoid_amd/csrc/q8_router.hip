@@ -295,8 +295,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
     const int t = blockIdx.x * 4 + wv;
     if (t >= S)
         return;
-    select_token(logits + (int64_t)t * E, bias, E, k, rsf, ids + (int64_t)t * k,
-                 weights + (int64_t)t * k, sel_s[wv], nullptr, n_parts, (int64_t)S * E, opt);
+    select_token<true>(logits + (int64_t)t * E, bias, E, k, rsf, ids + (int64_t)t * k,
+                       weights + (int64_t)t * k, sel_s[wv], nullptr, n_parts, (int64_t)S * E, opt);
 }
 
 hipError_t launch_router_select(const float* logits, int32_t n_parts, const float* bias, int32_t S,

@@ -80,7 +80,7 @@ __device__ __forceinline__ uint32_t argmax_key(const uint32_t (&key)[PL], int E,
  * oracle, up to the first cumulative share >= top_p.  Slots past the cut get
  * id -1 and weight 0; the kept weights are renormalised over the kept slots
  * (denominator in slot order). */
-template <int PL>
+template <int PL, bool SLICED>
 __device__ __forceinline__ void select_token_pl(const float* lt, const float* bias, int32_t E, int32_t k,
                                                 float rsf, int32_t* ids_out, float* w_out, float* sel_s,
                                                 int32_t* ids_lds, int32_t n_parts, int64_t part_stride,
@@ -89,13 +89,36 @@ __device__ __forceinline__ void select_token_pl(const float* lt, const float* bi
     const int lane = threadIdx.x & 63;
     float s[PL];
     uint32_t key[PL]; /* order-preserving bits of the biased score; 0 = unavailable */
+    /* K slices of the logits, added in slice order.  Each round issues the
+     * loads of Q slices for all of the lane's experts before any add
+     * (clamped to the last slice and expert, so every load is in bounds): the
+     * slices cost one memory round trip per Q rather than one each. */
+    float lg[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+        lg[i] = lt[min(lane + 64 * i, E - 1)];
+    if constexpr (SLICED) {
+        constexpr int Q = PL <= 2 ? 16 : 32 / PL;
+        for (int p0 = 1; p0 < n_parts; p0 += Q) {
+            float v[PL][Q];
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int i = 0; i < PL; ++i)
+                    v[i][q] = lt[(int64_t)min(p0 + q, n_parts - 1) * part_stride + min(lane + 64 * i, E - 1)];
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int i = 0; i < PL; ++i)
+                    if (p0 + q < n_parts)
+                        lg[i] = lg[i] + v[i][q];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int e = lane + 64 * i;
         if (e < E) {
-            float l = lt[e];
-            for (int p = 1; p < n_parts; ++p) /* K slices, added in order */
-                l = l + lt[p * part_stride + e];
+            const float l = lg[i];
             const float sg = 1.0f / (1.0f + expf(-l));
             s[i] = sg;
             key[i] = order_bits(sg + bias[e]);
@@ -323,7 +346,10 @@ __device__ __forceinline__ void select_token_pl(const float* lt, const float* bi
 }
 
 /* Dispatches on the experts per lane (a multiple of 64 up to E), so that the
- * per-lane loops run exactly as many times as there are experts. */
+ * per-lane loops run exactly as many times as there are experts.  SLICED:
+ * the logits are n_parts K slices part_stride apart, added in slice order
+ * (the many-token router); otherwise one slice (n_parts is 1). */
+template <bool SLICED = false>
 __device__ __forceinline__ void select_token(const float* lt, const float* bias, int32_t E, int32_t k,
                                              float rsf, int32_t* ids_out, float* w_out, float* sel_s,
                                              int32_t* ids_lds, int32_t n_parts = 1,
@@ -331,16 +357,16 @@ __device__ __forceinline__ void select_token(const float* lt, const float* bias,
 {
     const int per_lane = (E + 63) / 64; /* uniform */
     if (per_lane <= 1)
-        select_token_pl<1>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+        select_token_pl<1, SLICED>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
     else if (per_lane <= 2)
-        select_token_pl<2>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+        select_token_pl<2, SLICED>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
     else if (per_lane <= 4)
-        select_token_pl<4>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+        select_token_pl<4, SLICED>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
     else if (per_lane <= 8)
-        select_token_pl<8>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
+        select_token_pl<8, SLICED>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride, opt);
     else
-        select_token_pl<kMaxPerLane>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts, part_stride,
-                                     opt);
+        select_token_pl<kMaxPerLane, SLICED>(lt, bias, E, k, rsf, ids_out, w_out, sel_s, ids_lds, n_parts,
+                                             part_stride, opt);
 }
 
 } // namespace coli
