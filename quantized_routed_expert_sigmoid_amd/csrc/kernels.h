@@ -207,15 +207,25 @@ inline int32_t identity_mfma_units(int32_t S, int32_t mmin)
     return S >= mmin ? (S + kMfmaUnitTokens - 1) / kMfmaUnitTokens : 0;
 }
 
-/* K slices of the many-token router logits (S > kSmallS): enough 64 x 64
- * tiles times slices for about 512 workgroups, at most 16 slices and one
- * 16-wide k chunk per slice; 1 for small batches.  The logits buffer holds
+/* Tile edge of the many-token router logits (tokens x experts per
+ * workgroup of four waves): 128 (waves of 64 x 64) when the batch has at
+ * least 32 such tiles, else 64 (waves of 32 x 32). */
+inline int32_t router_tile(int32_t S, int32_t E)
+{
+    const int64_t t128 = (int64_t)((S + 127) / 128) * ((E + 127) / 128);
+    return t128 >= 32 ? 128 : 64;
+}
+
+/* K slices of the many-token router logits (S > kSmallS): enough tiles
+ * times slices for about 512 workgroups, at most 16 slices and one 16-wide k
+ * chunk per slice; 1 for small batches.  The logits buffer holds
  * router_parts * S * E floats. */
 inline int32_t router_parts(int32_t S, int32_t E, int32_t H)
 {
     if (S <= kSmallS)
         return 1;
-    const int64_t tiles = (int64_t)((S + 63) / 64) * ((E + 63) / 64);
+    const int32_t T = router_tile(S, E);
+    const int64_t tiles = (int64_t)((S + T - 1) / T) * ((E + T - 1) / T);
     int64_t p = (512 + tiles - 1) / tiles;
     if (p > 16)
         p = 16;

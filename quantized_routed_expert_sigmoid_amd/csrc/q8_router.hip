@@ -174,67 +174,70 @@ static void launch_logits_small(dim3 grid, int32_t S, hipStream_t st, const floa
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 /* Many tokens: fp32 matrix cores (v_mfma_f32_16x16x4f32).  A workgroup
- * computes a 64-token x 64-expert tile of one K slice; the launch splits K
- * into n_parts slices so that it fills the chip, and the selection kernel
- * adds the slices in order.  Wave (wm, wn) owns 32 tokens x 32 experts, 2 x 2
- * MFMA tiles.  Operands come straight from global memory: lane (r, kg) loads
- * four consecutive k of each of its token rows and expert rows, and MFMA i of
- * a 16-k chunk takes element i -- any assignment of k to MFMA slots is exact
- * as long as both operands use the same one.  Rows past S or E load the last
- * row; their results are not stored. */
+ * computes a T-token x T-expert tile of one K slice (T = 32 WT); the launch
+ * splits K into n_parts slices so that it fills the chip, and the selection
+ * kernel adds the slices in order.  Wave (wm, wn) owns 16 WT tokens x 16 WT
+ * experts, WT x WT MFMA tiles.  Operands come straight from global memory:
+ * lane (r, kg) loads four consecutive k of each of its token rows and expert
+ * rows, and MFMA i of a 16-k chunk takes element i -- any assignment of k to
+ * MFMA slots is exact as long as both operands use the same one.  Rows past
+ * S or E load the last row; their results are not stored.  Larger wave tiles
+ * read each operand for more MFMAs (WT = 4: half the L1 traffic of WT = 2). */
+template <int WT>
 __global__ __launch_bounds__(256) void router_logits_mfma(const float* __restrict__ x, int32_t S,
                                                           int32_t H, int32_t E,
                                                           const float* __restrict__ w,
                                                           float* __restrict__ part, int32_t n_parts)
 {
+    constexpr int T = 32 * WT, WH = 16 * WT;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, kg = lane >> 4;
     const int p = blockIdx.x % n_parts;
     const int tile = blockIdx.x / n_parts;
-    const int tiles_e = (E + 63) / 64;
-    const int t0 = (tile / tiles_e) * 64 + (wv >> 1) * 32;
-    const int e0 = (tile % tiles_e) * 64 + (wv & 1) * 32;
-    const float* xr[2];
-    const float* wr[2];
+    const int tiles_e = (E + T - 1) / T;
+    const int t0 = (tile / tiles_e) * T + (wv >> 1) * WH;
+    const int e0 = (tile % tiles_e) * T + (wv & 1) * WH;
+    const float* xr[WT];
+    const float* wr[WT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < WT; ++m) {
         xr[m] = x + (int64_t)min(t0 + 16 * m + r, S - 1) * H + 4 * kg;
         wr[m] = w + (int64_t)min(e0 + 16 * m + r, E - 1) * H + 4 * kg;
     }
     const int nchunk = H / 16;
     const int c0 = (int)((int64_t)p * nchunk / n_parts);
     const int c1 = (int)((int64_t)(p + 1) * nchunk / n_parts);
-    f32x4 acc[2][2];
+    f32x4 acc[WT][WT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < WT; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < WT; ++n)
             acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float4 a[2], b[2];
+    float4 a[WT], b[WT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < WT; ++m) {
         a[m] = *reinterpret_cast<const float4*>(xr[m] + (int64_t)c0 * 16);
         b[m] = *reinterpret_cast<const float4*>(wr[m] + (int64_t)c0 * 16);
     }
     for (int c = c0; c < c1; ++c) {
         const int cn = min(c + 1, c1 - 1);
-        float4 an[2], bn[2];
+        float4 an[WT], bn[WT];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < WT; ++m) {
             an[m] = *reinterpret_cast<const float4*>(xr[m] + (int64_t)cn * 16);
             bn[m] = *reinterpret_cast<const float4*>(wr[m] + (int64_t)cn * 16);
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < WT; ++m)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
+            for (int n = 0; n < WT; ++n) {
                 acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].x, b[n].x, acc[m][n], 0, 0, 0);
                 acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].y, b[n].y, acc[m][n], 0, 0, 0);
                 acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].z, b[n].z, acc[m][n], 0, 0, 0);
                 acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].w, b[n].w, acc[m][n], 0, 0, 0);
             }
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < WT; ++m) {
             a[m] = an[m];
             b[m] = bn[m];
         }
@@ -242,9 +245,9 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const float* __restric
     /* lane holds D[4 kg + v][r]: token t0 + 16m + 4kg + v, expert e0 + 16n + r */
     float* out = part + (int64_t)p * S * E;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < WT; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < WT; ++n)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int t = t0 + 16 * m + 4 * kg + v, e = e0 + 16 * n + r;
@@ -262,9 +265,13 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
         launch_logits_small(dim3(E), S, st, x, H, E, w, logits, (int8_t*)nullptr, (float*)nullptr);
     } else {
         const int32_t parts = router_parts(S, E, H);
-        const int64_t tiles = (int64_t)((S + 63) / 64) * ((E + 63) / 64);
-        hipLaunchKernelGGL(router_logits_mfma, dim3((uint32_t)(tiles * parts)), dim3(256), 0, st, x, S, H,
-                           E, w, logits, parts);
+        const int32_t T = router_tile(S, E);
+        const int64_t tiles = (int64_t)((S + T - 1) / T) * ((E + T - 1) / T);
+        const dim3 grid((uint32_t)(tiles * parts)), block(256);
+        if (T == 128)
+            hipLaunchKernelGGL(router_logits_mfma<4>, grid, block, 0, st, x, S, H, E, w, logits, parts);
+        else
+            hipLaunchKernelGGL(router_logits_mfma<2>, grid, block, 0, st, x, S, H, E, w, logits, parts);
     }
     return hipGetLastError();
 }

@@ -100,11 +100,12 @@ def test_dispatch_skips_dropped_slots_bit_exact(qre):
 
 
 @pytest.mark.parametrize("case", ["tiny", "odd_experts", "decode_router_s1", "decode_router_s8", "wide_k",
-                                  "ragged_tiles", "decode_router", "glm_router_s70"])
+                                  "ragged_tiles", "ragged_tiles_128", "decode_router", "glm_router_s70"])
 def test_route_parity(qre, case):
     """Small batches (full-size router rows at 1 and 8 tokens included) take
     the one-workgroup-per-expert router; larger ones the matrix-core router
-    with K slices (ragged 64 x 64 tiles included)."""
+    with K slices (ragged 64 x 64 tiles, and ragged 128 x 128 tiles over 15
+    uneven slices, included)."""
     if case == "tiny":
         w, L = _small_layer("tiny_r")
     elif case == "odd_experts":
@@ -119,6 +120,10 @@ def test_route_parity(qre, case):
     elif case == "ragged_tiles":
         w, L = _small_layer("ragged_r", layer="ragged_r", hidden=512, n_experts=100, top_k=6, S=300,
                             rsf=2.5, var_router=1.0 / 512)
+    elif case == "ragged_tiles_128":
+        # 12 x 3 tiles of 128 (the 64 x 64-wave router), ragged in both
+        w, L = _small_layer("ragged_r128", layer="ragged_r128", hidden=256, n_experts=300, top_k=6, S=1500,
+                            rsf=2.5, var_router=1.0 / 256)
     elif case == "glm_router_s70":
         base = synth.WORKLOADS["prefill"]
         w = synth.scaled(base, name="router_s70", S=70)
