@@ -336,7 +336,11 @@ hipError_t launch_schedule(const int32_t* offsets, int32_t n_mat, const UnitList
 }
 
 /* ---- combine: out[t] = y_shared[t] + sum_j w[t][j] * y[inv[t*k+j]] --------
- * (dropped slots, inv < 0 or with inv null ids < 0, are skipped) */
+ * (dropped slots, inv < 0 or with inv null ids < 0, are skipped).  Slots go
+ * in rounds of 8: the round's rows and weights, then its row loads, are all
+ * issued before the first fma (a dropped or missing slot loads row 0 and
+ * adds nothing), so a token costs one round trip per 8 slots; the fmas stay
+ * in slot order. */
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ inv,
@@ -345,6 +349,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int32_t k, int32_t H, int32_t shared_row0,
                                                       float* __restrict__ out)
 {
+    constexpr int R = 8;
     const int64_t n4 = H / 4;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= (int64_t)S * n4)
@@ -354,17 +359,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (shared_row0 >= 0)
         acc = reinterpret_cast<const float4*>(y + (int64_t)(shared_row0 + t) * H)[c];
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = t * k + j;
-        const int32_t row = inv ? inv[p] : (ids[p] >= 0 ? p : -1);
-        if (row < 0) /* slot dropped by top-p */
-            continue;
-        const float wj = w[p];
-        const float4 v = reinterpret_cast<const float4*>(y + (int64_t)row * H)[c];
-        acc.x = __builtin_fmaf(wj, v.x, acc.x);
-        acc.y = __builtin_fmaf(wj, v.y, acc.y);
-        acc.z = __builtin_fmaf(wj, v.z, acc.z);
-        acc.w = __builtin_fmaf(wj, v.w, acc.w);
+    for (int j0 = 0; j0 < k; j0 += R) {
+        int32_t row[R];
+        float wj[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int32_t p = t * k + min(j0 + i, k - 1);
+            row[i] = inv ? inv[p] : (ids[p] >= 0 ? p : -1);
+            wj[i] = w[p];
+        }
+        float4 v[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            v[i] = reinterpret_cast<const float4*>(y + (int64_t)max(row[i], 0) * H)[c];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            if (j0 + i < k && row[i] >= 0) {
+                acc.x = __builtin_fmaf(wj[i], v[i].x, acc.x);
+                acc.y = __builtin_fmaf(wj[i], v[i].y, acc.y);
+                acc.z = __builtin_fmaf(wj[i], v[i].z, acc.z);
+                acc.w = __builtin_fmaf(wj[i], v[i].w, acc.w);
+            }
+        }
     }
     reinterpret_cast<float4*>(out + (int64_t)t * H)[c] = acc;
 }
