@@ -806,7 +806,17 @@ __device__ __forceinline__ bool k_loop_lean(LeanLds<BITS, GW>& S, const LeanLane
             __syncthreads();
         }
     }
-    return __syncthreads_or(bad) != 0;
+    /* the workgroup's OR of bad, through four words of the block-scale
+     * buffers (free after the last step's barrier): no LDS of its own, which
+     * keeps the grouped int4 kernels at four workgroups per CU */
+    int* red = reinterpret_cast<int*>(&S.ds[0][0][0][0]);
+    const bool wbad = __ballot(bad) != 0;
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = wbad ? 1 : 0;
+    __syncthreads();
+    const bool any = (red[0] | red[1] | red[2] | red[3]) != 0;
+    __syncthreads();
+    return any;
 }
 
 template <int BITS, bool GW>
