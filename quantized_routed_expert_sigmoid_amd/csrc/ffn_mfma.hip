@@ -554,11 +554,20 @@ __device__ __forceinline__ void lean_fetch(LeanStage<BITS, GW>& Q, const LeanLan
     const int s = min(st, L.nsteps - 1);
     if constexpr (GW) {
         /* thread l: row l / 4, blocks kLeanWsPerThread * (l % 4) + i of the step */
+        const uint32_t b0 = (uint32_t)(s * C::kStep + kLeanWsPerThread<BITS> * ((int)threadIdx.x & 3));
+        if (kLeanWsPerThread<BITS> == 2 && L.gb == 1 && (reinterpret_cast<uintptr_t>(L.wsb) & 7) == 0) {
+            /* one scale per block: the pair of blocks (b0 and the row offset
+             * even: nb is a multiple of 16 here) in one 8-byte load */
+            const float2 v = *reinterpret_cast<const float2*>(L.wsb + L.wso + min(b0, (uint32_t)L.ng - 2u));
+            Q.wsc[0] = v.x;
+            Q.wsc[kLeanWsPerThread<BITS> - 1] = v.y;
+        } else {
 #pragma unroll
-        for (int i = 0; i < kLeanWsPerThread<BITS>; ++i) {
-            const uint32_t b = (uint32_t)(s * C::kStep + kLeanWsPerThread<BITS> * ((int)threadIdx.x & 3) + i);
-            const uint32_t g = L.gb == 1 ? b : __umulhi(b, L.magic);
-            Q.wsc[i] = L.gb ? L.wsb[L.wso + min(g, (uint32_t)L.ng - 1u)] : 1.0f;
+            for (int i = 0; i < kLeanWsPerThread<BITS>; ++i) {
+                const uint32_t b = b0 + (uint32_t)i;
+                const uint32_t g = L.gb == 1 ? b : __umulhi(b, L.magic);
+                Q.wsc[i] = L.gb ? L.wsb[L.wso + min(g, (uint32_t)L.ng - 1u)] : 1.0f;
+            }
         }
     }
 #pragma unroll
