@@ -52,7 +52,7 @@ namespace coli {
 
 hipError_t one_token_forward(const coli_moe_layer* L, const FfnArgs& a, const float* x, int8_t* xq, float* xd,
                              float* logits, int32_t* ids, float* w, float* out, const int32_t* slot_of,
-                             void* const* stage_events, hipStream_t s)
+                             void* const* stage_events, hipStream_t s, const TierState* note_hits, bool* noted)
 {
     const int32_t H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k;
     const bool shared = a.nseg > 1;
@@ -78,7 +78,15 @@ hipError_t one_token_forward(const coli_moe_layer* L, const FfnArgs& a, const fl
     dd.out = out;
     dd.hs = nullptr;
     dd.slot_of = slot_of;
+    dd.note_hits = 0;
+    dd.ts = TierState{};
     const bool fused = down_combine_decode_fits(dd);
+    if (note_hits && fused) {
+        dd.note_hits = 1;
+        dd.ts = *note_hits;
+    }
+    if (noted)
+        *noted = dd.note_hits != 0;
     /* With the fused down + combine (which writes no y rows), the shared
      * expert's gate/up runs as one-wave jobs spread over every CU, its fp32 h
      * in the y region: the routed jobs then give each CU the same share.

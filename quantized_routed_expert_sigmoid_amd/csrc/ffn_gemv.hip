@@ -1066,6 +1066,12 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
     const bool rt_l = u_l < d.k;
     const int e_l = rt_l ? decode_matrix(d.slot_of, d.ids[u_l], d.E, a.seg[0].n_mat) : 0;
     const float w_l = rt_l ? d.w[u_l] : 0.0f;
+    /* a tiered forward with every expert resident: block 0's first wave
+     * leaves the slot cache's state as the plan kernel leaves it after this
+     * all-hit batch (every kept slot a hit in slot e_l), after the block's
+     * rows */
+    const bool note = d.note_hits != 0 && blockIdx.x == 0 && wv == 0;
+    const int32_t id_n = note && lane < n_kept ? d.ids[u_l] : 0;
     /* without a shared expert, compacted unit 0's pair is issued before h is staged */
     if (!shared)
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, 0), __builtin_amdgcn_readlane(e_l, 0), row0,
@@ -1214,6 +1220,32 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
                               outv);
     if (lane < 2)
         d.out[row0 + lane] = outv;
+    if (note) {
+        /* hits are used now (tick), each expert's usage counts its pair, the
+         * plan consumes every in-flight mark; a hit still marked in flight is
+         * a late hit, which makes the plan two passes */
+        TierHdr* hd = d.ts.hdr;
+        const bool kl = lane < n_kept;
+        const uint32_t tick = hd->tick + 1;
+        const unsigned long long plans = hd->plans, pairs = hd->pairs, hits = hd->hits, passes = hd->passes;
+        const unsigned long long use = d.ts.usage[kl ? id_n : 0];
+        const int32_t infl = d.ts.inflight[kl ? e_l : 0];
+        const bool late = __ballot(kl && infl != 0) != 0;
+        __builtin_amdgcn_wave_barrier();
+        if (kl) {
+            d.ts.last_use[e_l] = tick;
+            d.ts.usage[id_n] = use + 1ull;
+        }
+        for (int sl = lane; sl < d.ts.n; sl += 64)
+            d.ts.inflight[sl] = 0;
+        if (lane == 0) {
+            hd->tick = tick;
+            hd->plans = plans + 1;
+            hd->pairs = pairs + (unsigned long long)n_kept;
+            hd->hits = hits + (unsigned long long)n_kept;
+            hd->passes = passes + (late ? 2 : 1);
+        }
+    }
 }
 
 static int64_t total_jobs(const FfnArgs& a, int RB)

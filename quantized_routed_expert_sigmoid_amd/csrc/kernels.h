@@ -133,6 +133,24 @@ __device__ __forceinline__ void dbg_partial(const FfnArgs& a, int kind, int64_t 
 #endif
 }
 
+/* The slot cache's state of a tiered layer (tier_kernels.hip). */
+struct TierHdr {
+    uint32_t tick; /* plans, prefetches and pins so far (the LRU clock) */
+    int32_t pad;
+    unsigned long long plans, pairs, hits, misses, pin_loads, passes, prefetches, prefetch_loads;
+};
+
+struct TierState {
+    TierHdr* hdr;
+    int32_t* slot_of;          /* [E]: slot or -1 */
+    int32_t* expert_in;        /* [n]: expert or -1 */
+    uint32_t* last_use;        /* [n]: tick of the last use */
+    int32_t* pinned;           /* [n] */
+    int32_t* inflight;         /* [n]: loaded by a prefetch that no plan has consumed */
+    unsigned long long* usage; /* [E]: routed pairs */
+    int32_t E, n;
+};
+
 /* One-token batch (decode): selection inside the gate/up kernel.  f.seg[0]
  * is the routed bank (n_mat = E), f.seg[1] the shared expert when
  * f.nseg == 2; hq / hd / y hold one row per unit (slot order, shared last). */
@@ -156,6 +174,11 @@ struct DecodeArgs {
      * Otherwise at slot_of[id] (a tiered layer's slot map, [E], every
      * routed expert resident). */
     const int32_t* slot_of;
+    /* nonzero: a tiered forward with every expert resident; the fused
+     * down + combine also leaves the slot cache's state `ts` as the plan
+     * kernel leaves it after an all-hit batch */
+    int32_t note_hits;
+    TierState ts;
 };
 
 /* The matrix-core threshold of a layer's batch of S tokens (P pairs over E
@@ -288,23 +311,6 @@ hipError_t launch_ffn_down_mfma(const FfnArgs& a, int32_t bits, hipStream_t st);
  * plan kernel follows the policy of the host planner (expert_cache.cpp)
  * step for step. */
 constexpr int kTierMaxE = 1024; /* experts and slots */
-
-struct TierHdr {
-    uint32_t tick; /* plans, prefetches and pins so far (the LRU clock) */
-    int32_t pad;
-    unsigned long long plans, pairs, hits, misses, pin_loads, passes, prefetches, prefetch_loads;
-};
-
-struct TierState {
-    TierHdr* hdr;
-    int32_t* slot_of;          /* [E]: slot or -1 */
-    int32_t* expert_in;        /* [n]: expert or -1 */
-    uint32_t* last_use;        /* [n]: tick of the last use */
-    int32_t* pinned;           /* [n] */
-    int32_t* inflight;         /* [n]: loaded by a prefetch that no plan has consumed */
-    unsigned long long* usage; /* [E]: routed pairs */
-    int32_t E, n;
-};
 
 /* info[] fields written by the plan and pin kernels. */
 enum { kInfoPass = 0, kInfoLoad, kInfoHit, kInfoMiss, kInfoChunk, kInfoRing, kInfoError, kInfoN = 8 };

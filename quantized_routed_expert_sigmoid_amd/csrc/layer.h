@@ -270,10 +270,14 @@ inline hipError_t run_ffn(const FfnArgs& a, int32_t bits_gu, int32_t bits_d, hip
  * any in its second segment): quantise + router logits, selection with
  * gate/up, down with the combine.  slot_of: as DecodeArgs::slot_of.
  * stage_events (may be null): events 0..5 as the staged forward records
- * them. */
+ * them.  note_hits (may be null): the slot cache of a tiered layer whose
+ * experts are all resident; when the launch fuses down and combine it also
+ * keeps that state as the plan kernel would for this all-hit batch, and
+ * *noted says so (the caller launches the plan kernel otherwise). */
 hipError_t one_token_forward(const coli_moe_layer* L, const FfnArgs& a, const float* x, int8_t* xq, float* xd,
                              float* logits, int32_t* ids, float* w, float* out, const int32_t* slot_of,
-                             void* const* stage_events, hipStream_t s);
+                             void* const* stage_events, hipStream_t s, const TierState* note_hits = nullptr,
+                             bool* noted = nullptr);
 
 } // namespace coli
 

@@ -574,8 +574,9 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
 
     /* Every expert pinned, one token: the resident one-token kernels, with
      * the routed experts read through the slot map (the same kernels on the
-     * same weights, so the same bits); the plan, all hits, then keeps the
-     * cache's usage and counters. */
+     * same weights, so the same bits).  The batch is all hits: the fused
+     * down + combine keeps the cache's usage and counters as the plan kernel
+     * would, which then runs only when that launch is not fused. */
     const bool shared = L->has_shared != 0;
     if (all_pinned && S == 1 &&
         (!shared || (L->sh_gate.qtype == t->slot[0].qtype && L->sh_down.qtype == t->slot[2].qtype))) {
@@ -600,10 +601,11 @@ int colibri_tier_forward(coli_tier* t, const float* x, int32_t S, float* out, vo
         a.hq = at<int8_t>(ws, Lo.l.hq);
         a.hd = at<float>(ws, Lo.l.hd);
         a.y = at<float>(ws, Lo.l.y);
+        bool noted = false;
         if (e == hipSuccess)
             e = one_token_forward(L, a, x, at<int8_t>(ws, Lo.l.xq), at<float>(ws, Lo.l.xd), at<float>(ws, Lo.l.logits),
-                                  ids, w, out, t->st.slot_of, nullptr, s);
-        if (e == hipSuccess)
+                                  ids, w, out, t->st.slot_of, nullptr, s, &t->st, &noted);
+        if (e == hipSuccess && !noted)
             e = launch_tier_plan(ids, P, t->st, codes, loads, info, pass_pairs, false, s);
         if (e == hipSuccess)
             e = hipEventRecord(t->ev_plan, s);
