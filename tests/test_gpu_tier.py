@@ -147,6 +147,47 @@ def test_tier_everything_pinned(qre):
     tier.close()
 
 
+# every expert pinned, one token, 33 units of I = 2048: the down + combine
+# launch does not fuse, so the plan kernel keeps the cache's state
+PINNED_UNFUSED = dict(name="tpu", layer="decm", bits=4, hidden=256, inter=2048, n_experts=64, top_k=32, S=1,
+                      has_shared=True, var_router=1.0 / 256)
+
+
+@pytest.mark.parametrize("case", ["decode_int4", "decode_int4_prefetch", "unfused", "unfused_prefetch"])
+def test_tier_pinned_after_prefetch(qre, case):
+    """Every expert pinned after a prefetch whose loads no plan has consumed:
+    the first forward's hits on those slots are late hits (two passes in the
+    counters), whether the fused down + combine or the plan kernel keeps the
+    state; state and counters follow the host planner's after every batch."""
+    kw = PINNED_UNFUSED if case.startswith("unfused") else dict(TIER_CASES["decode_int4"], S=1)
+    w = synth.scaled(synth.WORKLOADS["tiny"], **kw)
+    say(f"tier pinned case={case} E={w.n_experts} k={w.top_k}")
+    L = synth.make_layer(w)
+    dev = to_device(L)
+    E = w.n_experts
+    tier = qre.TieredLayer(to_slow_tier(L, dev), E)
+    host = qre.ExpertCache(E, E)
+    xs = [synth.activations(w, tag=f"tpin{b}").cuda() for b in range(3)]
+    if case.endswith("prefetch"):
+        tier.prefetch(xs[0])
+        ids_p, _ = qre.route(dev, xs[0])
+        host.prefetch(ids_p.cpu().reshape(-1).tolist())
+    tier.pin(list(range(E))[::-1])
+    host.pin(list(range(E))[::-1])
+    for b in [0, 1, 0, 2]:
+        got = tier.forward(xs[b])
+        ref = qre.moe_layer_forward(dev, xs[b])
+        torch.cuda.synchronize()
+        assert bits_equal(got, ref), f"batch {b}"
+        ids, _ = qre.route(dev, xs[b])
+        host.plan(ids.cpu().reshape(-1).tolist())
+        assert tier.state() == host.state() and tier.stats() == host.stats(), f"batch {b}"
+    st = tier.stats()
+    assert st["misses"] == 0 and st["plans"] == 4
+    assert st["passes"] == (5 if case.endswith("prefetch") else 4)
+    tier.close()
+
+
 @pytest.mark.parametrize("case", ["decode_int4", "grouped_int4", "small_topp_groups", "many_slots_int2"])
 def test_tier_everything_pinned_one_token(qre, case):
     """All experts pinned, one token: the tier runs the resident one-token
