@@ -686,7 +686,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer runs on one MI355X and this build has no multi-GPU path).", file=sys.stderr)
+              "(the library runs the layer on one MI355X; it has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import torch
     import quantized_routed_expert_sigmoid_amd as qre
