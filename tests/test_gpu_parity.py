@@ -281,6 +281,18 @@ SMALL_LAYERS = {
                             top_k=4, S=40, has_shared=True),
     "mfma_int2_long": dict(name="mf2", layer="mf2", bits=2, hidden=256, inter=192, n_experts=4,
                            top_k=2, S=150, has_shared=True),
+    # the matrix-core threshold's edges: at S = 8 an expert holding all 8
+    # tokens stays on the GEMV kernels (two 4-token units); at S = 9 experts
+    # with fewer than 8 tokens stay there; with exactly 8 pairs per expert
+    # every expert runs on the matrix cores (one with 7 tokens); one pair
+    # fewer and the layer mixes both families (8 and 15 tokens on the matrix
+    # cores, 6 and 1 on the GEMV kernels)
+    "thr_s8_two_experts": dict(name="ts8", layer="ts8", n_experts=2, top_k=1, S=8, has_shared=True),
+    "thr_s9": dict(name="ts9", layer="ts9", n_experts=16, top_k=2, S=9),
+    "thr_all_mfma": dict(name="tam", layer="tam", bits=4, hidden=512, inter=256, n_experts=4, top_k=2, S=16,
+                         has_shared=True, var_router=1.0 / 512),
+    "thr_mixed": dict(name="tmx", layer="tam", bits=4, hidden=512, inter=256, n_experts=4, top_k=2, S=15,
+                      has_shared=True, var_router=1.0 / 512),
     # one token: selection inside the gate/up kernel, combine inside the down kernel
     "decode_int4": dict(name="dec4", layer="dec4", bits=4, hidden=512, inter=256, n_experts=64, top_k=6,
                         S=1, has_shared=True, rsf=2.5, var_router=1.0 / 512, var_bias=1e-4),
