@@ -293,7 +293,7 @@ def test_tier_forward_in_a_graph(qre, all_pinned):
         assert bits_equal(out, ref), f"replay of batch {b}"
         ids, _ = qre.route(dev, x)
         host.plan(ids.cpu().reshape(-1).tolist())
-        assert tier.state() == host.state()
+        assert tier.state() == host.state() and tier.stats() == host.stats()
     tier.close()
 
 
