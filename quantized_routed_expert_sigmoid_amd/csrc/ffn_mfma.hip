@@ -1,7 +1,9 @@
 /*
  * ffn_mfma.hip -- gated expert FFN on the integer dot path, grouped-GEMM form
- * on the int8 matrix cores, for experts that hold many tokens of the batch
- * (prefill / verify batches: "Show HN: 如何在我的低配置电脑上运行 GLM-5.2",
+ * on the int8 matrix cores, for the experts of a batch of more than 8 tokens
+ * that hold at least the batch's threshold of its tokens (every expert, when
+ * the batch averages 8 or more tokens per expert; layer_mfma_min in
+ * kernels.h) (prefill batches: "Show HN: 如何在我的低配置电脑上运行 GLM-5.2",
  * implemented features, batched-union MoE item; integer dot-product and
  * quantised-kernel items; Metal section: SwiGLU; resource-policy section:
  * gate and up in one dispatch).
