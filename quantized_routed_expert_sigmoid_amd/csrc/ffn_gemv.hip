@@ -1,7 +1,8 @@
 /*
  * ffn_gemv.hip -- gated expert FFN on the integer dot path, GEMV form, for
- * experts that hold few tokens of a batch (one-token decode, small verify
- * batches, the small experts of a prefill).
+ * experts that hold few tokens of a batch: one-token decode, batches of up to
+ * 8 tokens (verify steps), and the experts below the matrix-core threshold
+ * in batches that average fewer than 8 tokens per expert.
  *
  * ("Show HN: 如何在我的低配置电脑上运行 GLM-5.2": implemented-features section,
  * integer dot-product item -- Q8_0-style int8 activations -- and quantised-
