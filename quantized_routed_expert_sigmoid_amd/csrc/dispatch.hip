@@ -274,6 +274,100 @@ hipError_t launch_dispatch_pass(const int32_t* codes, int32_t pass, int32_t inv_
     return hipGetLastError();
 }
 
+/* The dispatch of at most 64 pairs (ids in LDS, 16-byte aligned), with the
+ * result of dispatch_body written out directly: a pair's sorted position is
+ * the number of kept pairs of lower experts plus those of its own expert
+ * before it.  Every thread e <= E writes offsets[e] from the ids read as
+ * 16-byte vectors; wave 0 holds pair p in lane p and finds, with one ballot
+ * per bit of the expert id, the pairs of its expert and those of lower
+ * experts, then writes the positions, the active list and the unit lists
+ * (in expert order, as the scan of dispatch_body places them).  No
+ * histogram, scan or placement rounds, and no barrier. */
+__device__ __forceinline__ void dispatch_few(const int32_t* sel_ids, int32_t P, int32_t E, int32_t* offsets,
+                                             int32_t* sorted, int32_t* inv, int32_t* active, int32_t* n_active,
+                                             const UnitLists& ul)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    int32_t key[64];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int4 v = reinterpret_cast<const int4*>(sel_ids)[i];
+        key[4 * i] = v.x;
+        key[4 * i + 1] = v.y;
+        key[4 * i + 2] = v.z;
+        key[4 * i + 3] = v.w;
+    }
+    /* a kept pair's key is its clamped expert id; past P and dropped: E */
+#pragma unroll
+    for (int q = 0; q < 64; ++q)
+        key[q] = (q < P && key[q] >= 0) ? min(key[q], E - 1) : E;
+    for (int32_t e = tid; e <= E; e += (int32_t)blockDim.x) {
+        int32_t below = 0;
+#pragma unroll
+        for (int q = 0; q < 64; ++q)
+            below += key[q] < e ? 1 : 0;
+        offsets[e] = below;
+    }
+    if (tid >= 64)
+        return;
+    const int32_t raw = lane < P ? sel_ids[lane] : -1;
+    const bool valid = raw >= 0;
+    const int32_t ex = valid ? min(raw, E - 1) : 0;
+    /* bit-sliced compare against every lane, most significant bit first */
+    int nbits = 1;
+    while ((1 << nbits) < E)
+        ++nbits;
+    uint64_t eqm = __ballot(valid), ltm = 0;
+    for (int b = nbits - 1; b >= 0; --b) {
+        const bool bit = (ex >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        if (bit) {
+            ltm |= eqm & ~ones;
+            eqm &= ones;
+        } else {
+            eqm &= ~ones;
+        }
+    }
+    const uint64_t lt_lane = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int32_t below = __popcll(ltm), cnt = __popcll(eqm), before = __popcll(eqm & lt_lane);
+    const int32_t pos = below + before;
+    if (valid) {
+        sorted[pos] = lane;
+        if (inv)
+            inv[lane] = pos;
+    } else if (lane < P && inv) {
+        inv[lane] = -1;
+    }
+    /* the first pair of each expert speaks for it */
+    const bool first = valid && before == 0;
+    const uint64_t fm = __ballot(first);
+    int32_t gq, mq;
+    unit_counts(cnt, ul.mfma_min, gq, mq);
+    /* sums over the first pairs (of lower experts), one ballot per bit of
+     * the unit counts (at most 64 units per expert here) */
+    const uint64_t lower = fm & ltm;
+    const int32_t aidx = __popcll(lower);
+    int32_t gbase = 0, mbase = 0, tot_g = 0, tot_m = 0;
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+        const uint64_t gb = fm & __ballot((gq >> b) & 1), mb = fm & __ballot((mq >> b) & 1);
+        gbase += __popcll(gb & lower) << b;
+        mbase += __popcll(mb & lower) << b;
+        tot_g += __popcll(gb) << b;
+        tot_m += __popcll(mb) << b;
+    }
+    if (first) {
+        active[aidx] = ex;
+        emit_units(ul.units, gbase, ex, below, gq ? cnt : 0, kUnitTokens, ul.max_units);
+        emit_units(ul.munits, mbase, ex, below, mq ? cnt : 0, kMfmaUnitTokens, ul.max_munits);
+    }
+    if (lane == 0) {
+        *n_active = __popcll(fm);
+        *ul.n_units = min(tot_g, ul.max_units);
+        *ul.n_munits = min(tot_m, ul.max_munits);
+    }
+}
+
 /* Small batches (S <= kSmallS): wave t selects token t's experts (select.h),
  * then the whole workgroup dispatches the S*k pairs from LDS. */
 __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
@@ -293,14 +387,35 @@ __global__ __launch_bounds__(kDispThreads) void select_dispatch_small(
     dispatch_body(PlainIds{sel_ids}, S, k, E, offsets, sorted, inv, active, n_active, ul, true, sh);
 }
 
+/* Small batches of at most 64 pairs: one wave per token (S waves), selection
+ * as above, then dispatch_few. */
+__global__ __launch_bounds__(kSmallS * 64) void select_dispatch_few(
+    const float* __restrict__ logits, const float* __restrict__ bias, int32_t S, int32_t E, int32_t k,
+    float rsf, RouteOpts opt, int32_t* __restrict__ ids, float* __restrict__ weights,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, UnitLists ul)
+{
+    __shared__ __attribute__((aligned(16))) float sel_s[kSmallS][kSelScratch];
+    __shared__ __attribute__((aligned(16))) int32_t sel_ids[64];
+    const int wv = threadIdx.x >> 6;
+    select_token(logits + (int64_t)wv * E, bias, E, k, rsf, ids + (int64_t)wv * k, weights + (int64_t)wv * k,
+                 sel_s[wv], sel_ids + wv * k, 1, 0, opt);
+    __syncthreads();
+    dispatch_few(sel_ids, S * k, E, offsets, sorted, inv, active, n_active, ul);
+}
+
 hipError_t launch_select_dispatch_small(const float* logits, const float* bias, int32_t S, int32_t E,
                                         int32_t k, float rsf, const RouteOpts& opt, int32_t* ids,
                                         float* weights, int32_t* offsets, int32_t* sorted, int32_t* inv,
                                         int32_t* active, int32_t* n_active, const UnitLists& ul,
                                         hipStream_t st)
 {
-    hipLaunchKernelGGL(select_dispatch_small, dim3(1), dim3(kDispThreads), 0, st, logits, bias, S, E, k,
-                       rsf, opt, ids, weights, offsets, sorted, inv, active, n_active, ul);
+    if (S > 0 && S * k <= 64)
+        hipLaunchKernelGGL(select_dispatch_few, dim3(1), dim3(64 * S), 0, st, logits, bias, S, E, k, rsf, opt, ids,
+                           weights, offsets, sorted, inv, active, n_active, ul);
+    else
+        hipLaunchKernelGGL(select_dispatch_small, dim3(1), dim3(kDispThreads), 0, st, logits, bias, S, E, k,
+                           rsf, opt, ids, weights, offsets, sorted, inv, active, n_active, ul);
     return hipGetLastError();
 }
 

@@ -271,6 +271,9 @@ SMALL_LAYERS = {
     "mid_int4": dict(name="mid4", layer="mid_int4", bits=4, hidden=1024, inter=512, n_experts=32,
                      top_k=4, S=24, has_shared=True, rsf=2.5, var_router=1.0 / 1024, var_bias=1e-4),
     "one_expert": dict(name="one", layer="one", n_experts=4, top_k=1, S=5),
+    # 3 tokens x 24 slots: more pairs than one wave places, so the small-batch
+    # launch dispatches with the workgroup's counting sort
+    "small_many_pairs": dict(name="smp", layer="smp", n_experts=64, top_k=24, S=3, has_shared=True),
     "all_experts": dict(name="all", layer="all", n_experts=8, top_k=8, S=6, has_shared=True),
     # S > 8: experts with >= 8 tokens and the shared expert run on the matrix
     # cores, every expert when the batch has 8 or more pairs per expert
@@ -352,6 +355,74 @@ def test_layer_parity_small(qre, case):
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ref["ids"])
     assert_close_rms(out.cpu().numpy(), ref["out"], case)
+
+
+def _layer_ws_small(w, ws):
+    """The dispatch fields of a layer workspace for a batch of at most 8
+    tokens, at the offsets the library's workspace layout gives them (fields
+    in order, each rounded up to 256 bytes; one logit slice; no matrix-core
+    units at this size)."""
+    S, E, k, H, I = w.S, w.n_experts, w.top_k, w.hidden, w.inter
+    P = S * k
+    rows = P + (S if w.has_shared else 0)
+    mmin = 9
+    per = (mmin - 1 + 3) // 4
+    act = min(P, E)
+    max_units = min((P + 3 * act) // 4, per * act)
+    sizes = [("logits", S * E * 4), ("units", max_units * 16), ("n_units", 16), ("munits", 0),
+             ("n_munits", 16), ("hq", rows * I), ("hd", rows * (I // 32) * 4), ("xq", S * H),
+             ("xd", S * (H // 32) * 4), ("ids", P * 4), ("w", P * 4), ("offsets", (E + 1) * 4),
+             ("sorted", P * 4), ("inv", P * 4), ("active", E * 4), ("n_active", 16)]
+    raw = ws.cpu().numpy().view(np.uint8)
+    at, f = 0, {}
+    for name, n in sizes:
+        f[name] = raw[at:at + n]
+        at += (n + 255) // 256 * 256
+    i32 = {n: f[n].view(np.int32) for n in ("units", "n_units", "ids", "offsets", "sorted", "inv", "active",
+                                            "n_active")}
+    return i32, max_units
+
+
+@pytest.mark.parametrize("case,kw", [
+    ("tiny_s8_k2", dict(n_experts=16, top_k=2, S=8)),
+    ("s4_k8_e64", dict(n_experts=64, top_k=8, S=4, has_shared=True)),
+    ("s8_k8_all_fit", dict(n_experts=32, top_k=8, S=8)),
+    ("s3_k24_two_waves", dict(n_experts=64, top_k=24, S=3)),
+    ("s6_top_p", dict(n_experts=64, top_k=8, S=6, top_p=0.7)),
+])
+def test_small_batch_dispatch_in_workspace(qre, case, kw):
+    """Batches of at most 8 tokens select and dispatch in one launch: up to 64
+    pairs are placed directly by one wave, more by the workgroup's counting
+    sort.  Either way the dispatch left in the layer workspace is the
+    oracle's dispatch of the ids chosen, and the unit lists cover every
+    active expert's sorted positions in order, at most 4 per unit."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], name="sd_" + case, layer="sd_" + case, **kw)
+    say(f"small dispatch case={case} S={w.S} E={w.n_experts} k={w.top_k}")
+    L = synth.make_layer(w)
+    x, _ = gapped_activations(w, L.router_w, L.bias)
+    dev = to_device(L)
+    ws = dev.workspace(w.S)
+    ws.fill_(0x5A)
+    qre.moe_layer_forward(dev, x.cuda(), ws=ws)
+    torch.cuda.synchronize()
+    f, max_units = _layer_ws_small(w, ws)
+    S, k, E = w.S, w.top_k, w.n_experts
+    ids = f["ids"][:S * k].reshape(S, k)
+    ref_ids = oracle.layer_forward(L, x.numpy())["ids"]
+    assert np.array_equal(ids, ref_ids)
+    ref = oracle.dispatch(ids, E)
+    n_pairs = int(ref["offsets"][E])
+    assert np.array_equal(f["offsets"][:E + 1], ref["offsets"])
+    assert np.array_equal(f["sorted"][:n_pairs], ref["sorted"][:n_pairs])
+    assert np.array_equal(f["inv"][:S * k], ref["inv"])
+    n = int(f["n_active"][0])
+    assert n == ref["n_active"] and np.array_equal(f["active"][:n], ref["active"])
+    want = [(e, int(ref["offsets"][e]) + u, min(4, int(ref["offsets"][e + 1] - ref["offsets"][e]) - u))
+            for e in ref["active"] for u in range(0, int(ref["offsets"][e + 1] - ref["offsets"][e]), 4)]
+    nu = int(f["n_units"][0])
+    assert nu == min(len(want), max_units)
+    got = f["units"][:4 * nu].reshape(nu, 4)[:, :3]
+    assert np.array_equal(got, np.array(want[:nu], dtype=np.int32).reshape(nu, 3))
 
 
 @pytest.mark.parametrize("S", [1, 3, 20])
