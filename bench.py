@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published (TOPS)
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published (TFLOP/s)
 
 
 def parse():
@@ -664,14 +665,21 @@ def device_peaks(torch, qre_probes):
         torch.cuda.synchronize()
         ops = blocks * 4 * iters * 8 * 16 * 16 * k * 2
         mfma[k] = ops / (e0.elapsed_time(e1) / 1000.0) / 1e12
+    blocks, iters = 1024, 4096
+    qre_probes.colibri_probe_mfma_bf16(64, blocks, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st))
+    e0.record()
+    assert qre_probes.colibri_probe_mfma_bf16(iters, blocks, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    bf16_k32 = blocks * 4 * iters * 8 * 16 * 16 * 32 * 2 / (e0.elapsed_time(e1) / 1000.0) / 1e12
     return {"hbm_read_stream_GBps": read[best], "read_stream_best": f"{best[0]}, {best[1]} workgroups",
-            "int8_mfma_k32_TOPS": mfma[32], "int8_mfma_k64_TOPS": mfma[64],
+            "int8_mfma_k32_TOPS": mfma[32], "int8_mfma_k64_TOPS": mfma[64], "bf16_mfma_k32_TFLOPS": bf16_k32,
             "decode_read_pattern": pattern, "prefill_read_pattern": tile,
-            "spec": {"hbm_GBps": HBM_PEAK_GBS, "int8_mfma_TOPS": INT8_PEAK_TOPS,
+            "spec": {"hbm_GBps": HBM_PEAK_GBS, "int8_mfma_TOPS": INT8_PEAK_TOPS, "bf16_mfma_TFLOPS": BF16_PEAK_TFLOPS,
                      "valu_lane_ops_per_s": VALU_PEAK_LANE_OPS},
             "how": "read stream: 1 GiB read once per launch with 16-byte nontemporal loads, best of grid-stride and "
                    "blocked layouts over 512..8192 workgroups; matrix cores: 1024 workgroups of 4 waves, 8 "
-                   "independent int8 MFMA chains per wave; decode read pattern: the one-token kernels' weight "
+                   "independent int8 (K = 32 and 64) or bf16 (16x16x32) MFMA chains per wave; decode read pattern: the one-token kernels' weight "
                    "loads (items of 2 rows x 512 B, chunk-major, 16 rows per wave) with no arithmetic, at the "
                    "decode layer's gate+up and down sizes, one launch each, 16 copies rotated; prefill read pattern: "
                    "the matrix-core kernels' weight loads (64 rows per workgroup, 128 bytes of each row per step, "
@@ -692,6 +700,8 @@ def load_probes():
                                      ctypes.c_void_p, ctypes.c_void_p]
     L.colibri_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]
+    L.colibri_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.colibri_probe_mfma_bf16_block.argtypes = [ctypes.c_void_p] * 5
     return L
 
 

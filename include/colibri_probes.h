@@ -1,7 +1,7 @@
 /*
  * colibri_probes.h -- measurement kernels (libcolibri_probes.so) used by the
  * benchmark to report achievable device rates beside the published MI355X
- * peaks: an HBM read stream and an int8 matrix-core loop.  They compute
+ * peaks: an HBM read stream and the int8 and bf16 matrix-core loops.  They compute
  * nothing of the layer.  Pointers are device memory owned by the caller;
  * work is enqueued on `stream` (a hipStream_t); returns 0, 1 for a bad
  * argument (nothing enqueued), 4 for a launch error.
@@ -47,6 +47,18 @@ int colibri_probe_tile(const void* buf, int32_t rowbytes, int32_t n_rows, int32_
  * independent v_mfma_i32_16x16x{k}_i8 (k = 32 or 64), i.e. 8 * iters *
  * 16 * 16 * k * 2 integer operations per wave.  sink: n_blocks words. */
 int colibri_probe_mfma_i8(int32_t k, int32_t iters, int32_t n_blocks, int32_t* sink, void* stream);
+
+/* As colibri_probe_mfma_i8 for v_mfma_f32_16x16x32_bf16 (K = 32, fp32
+ * accumulation): 8 * iters * 16 * 16 * 32 * 2 floating-point operations per
+ * wave. */
+int colibri_probe_mfma_bf16(int32_t iters, int32_t n_blocks, int32_t* sink, void* stream);
+
+/* One v_mfma_f32_16x16x32_bf16 by one wave: d = c + a b, with a [16][32]
+ * and b [32][16] bfloat16 bit patterns and c, d [16][16] fp32, all
+ * row-major device arrays.  It shows whether the fp32 sums of integer-valued
+ * products come out exact (the exactness a bfloat16 form of the integer
+ * block partials would need). */
+int colibri_probe_mfma_bf16_block(const uint16_t* a, const uint16_t* b, const float* c, float* d, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kReadUnroll = 8;
 
@@ -181,6 +183,59 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, int32_t* sin
         sink[blockIdx.x] = s;
 }
 
+/* iters rounds of kChains independent v_mfma_f32_16x16x32_bf16 per wave
+ * (the bf16 form with the K = 32 of one Q8_0 block). */
+__global__ __launch_bounds__(256) void probe_mfma_bf16_kernel(int iters, int32_t* sink)
+{
+    const int lane = threadIdx.x & 63;
+    f32x4 c[kChains];
+    bf16x8 a[kChains], b[kChains];
+#pragma unroll
+    for (int j = 0; j < kChains; ++j) {
+        c[j] = f32x4{(float)lane, (float)j, 1.0f, 2.0f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[j][i] = (__bf16)(float)((lane + i + j) & 7);
+            b[j][i] = (__bf16)(float)((lane * 3 + i - j) & 15);
+        }
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kChains; ++j)
+            c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j], c[j], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kChains; ++j)
+        s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    if (s == 1.2345e-30f)
+        sink[blockIdx.x] = 1;
+}
+
+/* One v_mfma_f32_16x16x32_bf16 on operands given as whole matrices: lane l
+ * takes A[l % 16][8 (l / 16) .. + 7], B[8 (l / 16) .. + 7][l % 16] and
+ * C, D[4 (l / 16) + i][l % 16], i = 0..3. */
+__global__ __launch_bounds__(64) void probe_mfma_bf16_block_kernel(const uint16_t* __restrict__ a,
+                                                                   const uint16_t* __restrict__ b,
+                                                                   const float* __restrict__ c, float* __restrict__ d)
+{
+    const int l = threadIdx.x, r = l & 15, g = l >> 4;
+    bf16x8 av, bv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        av[i] = __builtin_bit_cast(__bf16, a[r * 32 + 8 * g + i]);
+        bv[i] = __builtin_bit_cast(__bf16, b[(8 * g + i) * 16 + r]);
+    }
+    f32x4 cv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        cv[i] = c[(4 * g + i) * 16 + r];
+    const f32x4 dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, cv, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        d[(4 * g + i) * 16 + r] = dv[i];
+}
+
 } // namespace
 
 extern "C" {
@@ -256,6 +311,22 @@ int colibri_probe_mfma_i8(int32_t k, int32_t iters, int32_t n_blocks, int32_t* s
         hipLaunchKernelGGL(probe_mfma_kernel<32>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
     else
         hipLaunchKernelGGL(probe_mfma_kernel<64>, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int colibri_probe_mfma_bf16(int32_t iters, int32_t n_blocks, int32_t* sink, void* stream)
+{
+    if (!sink || n_blocks <= 0 || iters <= 0)
+        return 1;
+    hipLaunchKernelGGL(probe_mfma_bf16_kernel, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int colibri_probe_mfma_bf16_block(const uint16_t* a, const uint16_t* b, const float* c, float* d, void* stream)
+{
+    if (!a || !b || !c || !d)
+        return 1;
+    hipLaunchKernelGGL(probe_mfma_bf16_block_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, a, b, c, d);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
