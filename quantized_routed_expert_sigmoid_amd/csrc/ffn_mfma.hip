@@ -1039,26 +1039,25 @@ __global__ __launch_bounds__(256) void ffn_down_mfma(FfnArgs a)
         mfma_k_loop<BITS, GROUPED>(sm.k, L, ntiles, acc, a, md);
     }
 
+    const int n0 = M.rb * 64 + 16 * wv + 4 * g;
+    float sc[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int rr = 16 * wv + 4 * g + v;
-        const int n_out = M.rb * 64 + rr;
-        const float sc = n_out < a.H ? (gbv ? 1.0f : sg.down_s[(int64_t)e * a.H + n_out]) : 0.0f;
+    for (int v = 0; v < 4; ++v)
+        sc[v] = n0 + v < a.H ? (gbv ? 1.0f : sg.down_s[(int64_t)e * a.H + n0 + v]) : 0.0f;
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
-            if (n < ntiles)
-                sm.e.v[rr][16 * n + r] = sc * acc[n][v];
-    }
-    __syncthreads();
-    /* thread: token t, rows 8q .. 8q+7 of the block */
-    const int t = threadIdx.x >> 3, q = threadIdx.x & 7;
-    if (t < ntok && M.rb * 64 + 8 * q < a.H) {
-        float* yr = a.y + (int64_t)(sg.out_base + pos0 + t) * a.H + M.rb * 64 + 8 * q;
+    for (int n = 0; n < 2; ++n) {
+        const int t = 16 * n + r;
+        if (n < ntiles && t < ntok) {
+            float* yr = a.y + (int64_t)(sg.out_base + pos0 + t) * a.H + n0;
+            if (n0 + 3 < a.H && (a.H & 3) == 0) {
+                *reinterpret_cast<float4*>(yr) =
+                    make_float4(sc[0] * acc[n][0], sc[1] * acc[n][1], sc[2] * acc[n][2], sc[3] * acc[n][3]);
+            } else {
 #pragma unroll
-        for (int i = 0; i < 8; i += 4) {
-            const float4 o = make_float4(sm.e.v[8 * q + i][t], sm.e.v[8 * q + i + 1][t],
-                                         sm.e.v[8 * q + i + 2][t], sm.e.v[8 * q + i + 3][t]);
-            *reinterpret_cast<float4*>(yr + i) = o;
+                for (int v = 0; v < 4; ++v)
+                    if (n0 + v < a.H)
+                        yr[v] = sc[v] * acc[n][v];
+            }
         }
     }
 }
