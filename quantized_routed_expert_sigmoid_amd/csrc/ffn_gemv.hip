@@ -1203,15 +1203,11 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
             dc_act<NI>(xal, j1, nb, xa);
             pair_partials<BITS, NI>(B, xa, nb, P + 2 * j1 * sp, sp, a, __builtin_amdgcn_readlane(u_l, j1), row0);
         }
-        if (q == 0 && shared) {
-            /* the shared expert (streamed first) is folded while the routed
-             * pairs load */
-            wave_lds_sync();
-            fold_chains(2 * (U - 1), 2 * U);
-        }
     }
+    /* every chain (at most 64: U <= 32) in one pass, one per lane, after the
+     * stream (a fold inside the loop would hold back the next row loads) */
     wave_lds_sync();
-    fold_chains(0, shared ? 2 * (U - 1) : 2 * U);
+    fold_chains(0, 2 * U);
     wave_lds_sync();
     /* compacted order is slot order: the combine's fma order is kept (every
      * lane runs the chain of row lane & 1; lanes 0 and 1 store) */
