@@ -161,6 +161,60 @@ __device__ __forceinline__ void load_block(const uint8_t* p, uint32_t (&w)[BITS]
     }
 }
 
+/* int8 chunks (32 blocks of 32 bytes: 1 KB of a row) are loaded in halves
+ * of blocks: lane c (of the row's 32 lanes) takes half c & 1 of blocks
+ * c >> 1 and 16 + (c >> 1), so that each of its two load instructions reads
+ * 512 contiguous bytes of the row (every cache line once; whole blocks per
+ * lane would request each line from both instructions).  Blocks past the
+ * row's nb read its last block (in bounds; their partials are discarded).
+ * The lane then owns one block of the chunk, own8(c). */
+/* The split layout is used for int8 rows of four chunks or more (a job's
+ * NI): shorter rows have too few blocks per chunk for it to pay (measured
+ * slower on rows of one and two chunks). */
+template <int BITS, int NI>
+constexpr bool kSplit8 = BITS == 8 && NI >= 4;
+
+__device__ __forceinline__ int own8(int c)
+{
+    return (c & 1) ? 16 + (c >> 1) : (c >> 1);
+}
+
+__device__ __forceinline__ void load_chunk8(const uint8_t* row, int chunk0, int c, int nb, uint32_t (&w)[8])
+{
+    const int b0 = min(chunk0 + (c >> 1), nb - 1), b1 = min(chunk0 + 16 + (c >> 1), nb - 1);
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + b0 * 32 + 16 * (c & 1)));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + b1 * 32 + 16 * (c & 1)));
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+/* The activation words matching load_chunk8's pieces: half c & 1 of blocks
+ * chunk0 + (c >> 1) and chunk0 + 16 + (c >> 1) of a staged [block][8] array. */
+__device__ __forceinline__ void act_chunk8(const uint32_t* xb, int chunk0, int c, int nb, uint32_t (&x)[8])
+{
+    const int b0 = min(chunk0 + (c >> 1), nb - 1), b1 = min(chunk0 + 16 + (c >> 1), nb - 1);
+    const uint4 u0 = *reinterpret_cast<const uint4*>(xb + b0 * 8 + 4 * (c & 1));
+    const uint4 u1 = *reinterpret_cast<const uint4*>(xb + b1 * 8 + 4 * (c & 1));
+    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+}
+
+/* The exact int32 partial of the lane's own block (own8(c)): each half's
+ * four byte dots, plus the other half's from the partner lane c ^ 1 (every
+ * lane of the wave takes part). */
+__device__ __forceinline__ int32_t dot_chunk8(const uint32_t (&w)[8], const uint32_t (&x)[8], int c)
+{
+    int32_t s0 = 0, s1 = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        s0 = COLI_SDOT4(w[k], x[k], s0);
+        s1 = COLI_SDOT4(w[4 + k], x[4 + k], s1);
+    }
+    s0 += shfl_xor_i(s0, 1);
+    s1 += shfl_xor_i(s1, 1);
+    return (c & 1) ? s1 : s0;
+}
+
 /* Orders one wave's LDS writes before its following LDS reads by other lanes
  * of the same wave.  A wave's LDS instructions execute in issue order, so only
  * the compiler has to be kept from moving accesses across this point. */
@@ -331,16 +385,20 @@ struct Ring {
  * unconditional: a lane past the rows or the row's blocks reads the last
  * existing row / block instead (in bounds; its partial is never folded), so
  * no load sits under a branch and each use waits only for its own item. */
-template <int BITS>
+template <int BITS, int NI>
 __device__ __forceinline__ void item_load(Item<BITS>& W, const uint8_t* rows0, uint32_t rowbytes, int n,
                                           int rows_ok, int nb, const uint8_t* rows8)
 {
     const int lane = threadIdx.x & 63;
     const bool hi = rows8 && (n & 7) >= 4; /* uniform */
     const int row = min(2 * (n & 7) + (lane >> 5), max(rows_ok, 1) - 1) - (hi ? 8 : 0);
-    const uint32_t off = (uint32_t)row * rowbytes +
-                         (uint32_t)min(kChunk * (n >> 3) + (lane & 31), nb - 1) * (uint32_t)(4 * BITS);
-    load_block<BITS>((hi ? rows8 : rows0) + off, W.w);
+    if constexpr (kSplit8<BITS, NI>) {
+        load_chunk8((hi ? rows8 : rows0) + (uint32_t)row * rowbytes, kChunk * (n >> 3), lane & 31, nb, W.w);
+    } else {
+        const uint32_t off = (uint32_t)row * rowbytes +
+                             (uint32_t)min(kChunk * (n >> 3) + (lane & 31), nb - 1) * (uint32_t)(4 * BITS);
+        load_block<BITS>((hi ? rows8 : rows0) + off, W.w);
+    }
 }
 
 /* Issues the first 2 NI items (before the activations are staged, so the
@@ -351,7 +409,7 @@ __device__ __forceinline__ void ring_start(Ring<BITS, NI>& R, const uint8_t* row
 {
 #pragma unroll
     for (int n = 0; n < 2 * NI; ++n)
-        item_load<BITS>(R.it[n], rows0, rowbytes, n, rows_ok, nb, rows8);
+        item_load<BITS, NI>(R.it[n], rows0, rowbytes, n, rows_ok, nb, rows8);
 }
 
 /* ---- one token ------------------------------------------------------------
@@ -424,24 +482,34 @@ __device__ __forceinline__ float dec_k_loop(Ring<BITS, NI>& R, const uint8_t* ro
     for (int n = 0; n < N; ++n) {
         const int i = n >> 3, p = n & 7;
         if (p == 0) {
-            /* the lane's activation block of this chunk */
-            const uint4* src = reinterpret_cast<const uint4*>(xal + (kChunk * i + c) * 8);
-            const uint4 u0 = src[0], u1 = src[1];
-            xa[0] = u0.x; xa[1] = u0.y; xa[2] = u0.z; xa[3] = u0.w;
-            xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
+            /* the lane's activation block of this chunk (int8: the halves
+             * matching its weight pieces) */
+            if constexpr (kSplit8<BITS, NI>) {
+                act_chunk8(xal, kChunk * i, c, nb, xa);
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(xal + (kChunk * i + c) * 8);
+                const uint4 u0 = src[0], u1 = src[1];
+                xa[0] = u0.x; xa[1] = u0.y; xa[2] = u0.z; xa[3] = u0.w;
+                xa[4] = u1.x; xa[5] = u1.y; xa[6] = u1.z; xa[7] = u1.w;
+            }
         }
         if constexpr (GROUPED) {
             if (p == 4) /* four items before the fold: late enough to hold few registers */
                 chunk_scales_load(CS, ws0, ng, gb, rows_ok, i, lane);
         }
-        const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
+        int32_t s;
+        if constexpr (kSplit8<BITS, NI>)
+            s = dot_chunk8(R.it[n % D].w, xa, c);
+        else
+            s = block_dot<BITS>(R.it[n % D].w, xa);
+        const int cb = kSplit8<BITS, NI> ? own8(c) : c; /* the lane's block of the chunk */
         const int row = 2 * p + (lane >> 5);
-        P[ptile(row, c)] = kChunk * i + c < nb ? (float)s : 0.0f;
-        if (row < rows_ok && kChunk * i + c < nb)
+        P[ptile(row, cb)] = kChunk * i + cb < nb ? (float)s : 0.0f;
+        if (row < rows_ok && kChunk * i + cb < nb)
             dbg_partial(a, row < 8 ? dr.kind0 : dr.kind8, dr.o, row < 8 ? dr.row0 + row : dr.row8 + row - 8,
-                        kChunk * i + c, s);
+                        kChunk * i + cb, s);
         if (n + D < N) /* resolved at compile time */
-            item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, rows8);
+            item_load<BITS, NI>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, rows8);
         if (p == 7) {
             if constexpr (GROUPED)
                 chunk_scales_store(CS, W, lane);
@@ -691,20 +759,29 @@ __device__ __forceinline__ float rows_k_loop(Ring<BITS, NI>& R, const uint8_t* r
                 chunk_scales_load(CS, ws0, ng, gb, rows_ok, i, lane);
         }
         const int bc = min(b, nb - 1);
-        const int w = ptile(2 * p + (lane >> 5), c);
+        const int cb = kSplit8<BITS, NI> ? own8(c) : c; /* the lane's block of the chunk */
+        const int bo = kChunk * i + cb;
+        const int w = ptile(2 * p + (lane >> 5), cb);
         /* tokens one at a time (a rolled loop keeps one token's operands live) */
 #pragma unroll 1
         for (int t = 0; t < ntok; ++t) {
-            const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)t * nb + bc) * 8);
-            const uint4 u0 = src[0], u1 = src[1];
-            const uint32_t xa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-            const int32_t s = block_dot<BITS>(R.it[n % D].w, xa);
-            P[t * kTile + w] = b < nb ? (float)s : 0.0f;
-            if (b < nb && 2 * p + (lane >> 5) < rows_ok)
-                dbg_partial(a, kind, o0 + t, wrow0 + 2 * p + (lane >> 5), b, s);
+            int32_t s;
+            if constexpr (kSplit8<BITS, NI>) {
+                uint32_t xa[8];
+                act_chunk8(xal + (int64_t)t * nb * 8, kChunk * i, c, nb, xa);
+                s = dot_chunk8(R.it[n % D].w, xa, c);
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)t * nb + bc) * 8);
+                const uint4 u0 = src[0], u1 = src[1];
+                const uint32_t xa[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                s = block_dot<BITS>(R.it[n % D].w, xa);
+            }
+            P[t * kTile + w] = bo < nb ? (float)s : 0.0f;
+            if (bo < nb && 2 * p + (lane >> 5) < rows_ok)
+                dbg_partial(a, kind, o0 + t, wrow0 + 2 * p + (lane >> 5), bo, s);
         }
         if (n + D < N) /* resolved at compile time */
-            item_load<BITS>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, nullptr);
+            item_load<BITS, NI>(R.it[n % D], rows0, rowbytes, n + D, rows_ok, nb, nullptr);
         if (p == 7) {
             if constexpr (GROUPED)
                 chunk_scales_store(CS, W, lane);
@@ -933,8 +1010,12 @@ __device__ __forceinline__ void pair_load(PairLoad<BITS, NI>& L, const uint8_t* 
     const int lane = threadIdx.x & 63;
     const uint8_t* rp = rows0 + (int64_t)(lane >> 5) * rowbytes;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-        load_block<BITS>(rp + (int64_t)min((lane & 31) + kChunk * i, nb - 1) * (4 * BITS), L.w[i]);
+    for (int i = 0; i < NI; ++i) {
+        if constexpr (kSplit8<BITS, NI>)
+            load_chunk8(rp, kChunk * i, lane & 31, nb, L.w[i]);
+        else
+            load_block<BITS>(rp + (int64_t)min((lane & 31) + kChunk * i, nb - 1) * (4 * BITS), L.w[i]);
+    }
 }
 
 /* Exact partials of a loaded pair, as fp32, to P[row * sp + b] (o, wrow0:
@@ -947,11 +1028,21 @@ __device__ __forceinline__ void pair_partials(const PairLoad<BITS, NI>& L, const
     const int row = lane >> 5, c = lane & 31;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int b = c + kChunk * i;
-        if (b < nb) {
-            const int32_t s = block_dot<BITS>(L.w[i], xa[i]);
-            P[row * sp + b] = (float)s;
-            dbg_partial(a, kDbgDown, o, wrow0 + row, b, s);
+        if constexpr (kSplit8<BITS, NI>) {
+            /* every lane takes part in the halves' exchange */
+            const int b = own8(c) + kChunk * i;
+            const int32_t s = dot_chunk8(L.w[i], xa[i], c);
+            if (b < nb) {
+                P[row * sp + b] = (float)s;
+                dbg_partial(a, kDbgDown, o, wrow0 + row, b, s);
+            }
+        } else {
+            const int b = c + kChunk * i;
+            if (b < nb) {
+                const int32_t s = block_dot<BITS>(L.w[i], xa[i]);
+                P[row * sp + b] = (float)s;
+                dbg_partial(a, kDbgDown, o, wrow0 + row, b, s);
+            }
         }
     }
 }
@@ -990,10 +1081,16 @@ __device__ __forceinline__ float fold_row_grouped(const float* pr, const float* 
     return acc;
 }
 
-template <int NI>
+template <int BITS, int NI>
 __device__ __forceinline__ void dc_act(const uint32_t* xal, int j, int nb, uint32_t (&xa)[NI][8])
 {
     const int c = threadIdx.x & 31;
+    if constexpr (kSplit8<BITS, NI>) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            act_chunk8(xal + (int64_t)j * nb * 8, kChunk * i, c, nb, xa[i]);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const uint4* src = reinterpret_cast<const uint4*>(xal + ((int64_t)j * nb + min(c + kChunk * i, nb - 1)) * 8);
@@ -1194,13 +1291,13 @@ __global__ __launch_bounds__(64 * DW) void ffn_down_combine_decode(DecodeArgs d)
         pair_load<BITS, NI>(B, dc_rows(d, __builtin_amdgcn_readlane(u_l, j1), __builtin_amdgcn_readlane(e_l, j1), row0,
                                        rowbytes),
                             rowbytes, nb);
-        dc_act<NI>(xal, j0, nb, xa);
+        dc_act<BITS, NI>(xal, j0, nb, xa);
         pair_partials<BITS, NI>(A, xa, nb, P + 2 * j0 * sp, sp, a, __builtin_amdgcn_readlane(u_l, j0), row0);
         pair_load<BITS, NI>(A, dc_rows(d, __builtin_amdgcn_readlane(u_l, j2), __builtin_amdgcn_readlane(e_l, j2), row0,
                                        rowbytes),
                             rowbytes, nb);
         if (q + 1 < U) {
-            dc_act<NI>(xal, j1, nb, xa);
+            dc_act<BITS, NI>(xal, j1, nb, xa);
             pair_partials<BITS, NI>(B, xa, nb, P + 2 * j1 * sp, sp, a, __builtin_amdgcn_readlane(u_l, j1), row0);
         }
     }
