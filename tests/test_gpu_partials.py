@@ -122,6 +122,12 @@ CASES = {
     # the general loop with a ragged row (H = 288: nine blocks)
     "mfma_ragged": (dict(hidden=288, inter=96, n_experts=2, top_k=2, has_shared=False, var_router=1.0 / 288), 24,
                     False),
+    # rows of 100 blocks (four chunks, the last ragged): int8 rows of four
+    # chunks or more are loaded in half blocks by every GEMV kernel
+    "decode_long_rows": (dict(hidden=3200, inter=3200, n_experts=4, top_k=4, has_shared=True,
+                              var_router=1.0 / 3200), 1, True),
+    "small_batch_long_rows": (dict(hidden=3200, inter=3200, n_experts=4, top_k=2, has_shared=True,
+                                   var_router=1.0 / 3200), 5, False),
 }
 WINDOWS = {"gate": (0, 32), "up": (16, 48), "down": (56, 104)}
 
