@@ -173,6 +173,9 @@ static void launch_logits_small(dim3 grid, int32_t S, hipStream_t st, const floa
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+/* 16-wide k chunks of operands in flight per lane (ring slots) */
+constexpr int kRouterDepth = 4;
+
 /* Many tokens: fp32 matrix cores (v_mfma_f32_16x16x4f32).  A workgroup
  * computes a T-token x T-expert tile of one K slice (T = 32 WT); the launch
  * splits K into n_parts slices so that it fills the chip, and the selection
@@ -182,8 +185,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
  * rows, and MFMA i of a 16-k chunk takes element i -- any assignment of k to
  * MFMA slots is exact as long as both operands use the same one.  Rows past
  * S or E load the last row; their results are not stored.  Larger wave tiles
- * read each operand for more MFMAs (WT = 4: half the L1 traffic of WT = 2). */
-template <int WT>
+ * read each operand for more MFMAs (WT = 4: half the L1 traffic of WT = 2).
+ * D chunks of 16 k are in flight per lane (4: the loads of one chunk ahead
+ * left the many-token launches waiting on memory). */
+template <int WT, int D>
 __global__ __launch_bounds__(256) void router_logits_mfma(const float* __restrict__ x, int32_t S,
                                                           int32_t H, int32_t E,
                                                           const float* __restrict__ w,
@@ -213,33 +218,42 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const float* __restric
 #pragma unroll
         for (int n = 0; n < WT; ++n)
             acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float4 a[WT], b[WT];
+    /* a ring of D chunks in flight: slot i holds chunk c + i; a chunk past
+     * the slice reloads the slice's last one (in bounds) and enters with
+     * its token operand zeroed, adding +0 products, so that the loop needs
+     * no branch around its loads */
+    float4 a[D][WT], b[D][WT];
 #pragma unroll
-    for (int m = 0; m < WT; ++m) {
-        a[m] = *reinterpret_cast<const float4*>(xr[m] + (int64_t)c0 * 16);
-        b[m] = *reinterpret_cast<const float4*>(wr[m] + (int64_t)c0 * 16);
-    }
-    for (int c = c0; c < c1; ++c) {
-        const int cn = min(c + 1, c1 - 1);
-        float4 an[WT], bn[WT];
+    for (int i = 0; i < D; ++i)
 #pragma unroll
         for (int m = 0; m < WT; ++m) {
-            an[m] = *reinterpret_cast<const float4*>(xr[m] + (int64_t)cn * 16);
-            bn[m] = *reinterpret_cast<const float4*>(wr[m] + (int64_t)cn * 16);
+            const int64_t ci = min(c0 + i, c1 - 1);
+            a[i][m] = *reinterpret_cast<const float4*>(xr[m] + ci * 16);
+            b[i][m] = *reinterpret_cast<const float4*>(wr[m] + ci * 16);
         }
+    for (int c = c0; c < c1; c += D) {
 #pragma unroll
-        for (int m = 0; m < WT; ++m)
+        for (int i = 0; i < D; ++i) {
+            const float live = c + i < c1 ? 1.0f : 0.0f;
+            float4 am[WT];
 #pragma unroll
-            for (int n = 0; n < WT; ++n) {
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].x, b[n].x, acc[m][n], 0, 0, 0);
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].y, b[n].y, acc[m][n], 0, 0, 0);
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].z, b[n].z, acc[m][n], 0, 0, 0);
-                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].w, b[n].w, acc[m][n], 0, 0, 0);
+            for (int m = 0; m < WT; ++m)
+                am[m] = make_float4(a[i][m].x * live, a[i][m].y * live, a[i][m].z * live, a[i][m].w * live);
+#pragma unroll
+            for (int m = 0; m < WT; ++m)
+#pragma unroll
+                for (int n = 0; n < WT; ++n) {
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[m].x, b[i][n].x, acc[m][n], 0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[m].y, b[i][n].y, acc[m][n], 0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[m].z, b[i][n].z, acc[m][n], 0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[m].w, b[i][n].w, acc[m][n], 0, 0, 0);
+                }
+            const int64_t cn = min(c + i + D, c1 - 1);
+#pragma unroll
+            for (int m = 0; m < WT; ++m) {
+                a[i][m] = *reinterpret_cast<const float4*>(xr[m] + cn * 16);
+                b[i][m] = *reinterpret_cast<const float4*>(wr[m] + cn * 16);
             }
-#pragma unroll
-        for (int m = 0; m < WT; ++m) {
-            a[m] = an[m];
-            b[m] = bn[m];
         }
     }
     /* lane holds D[4 kg + v][r]: token t0 + 16m + 4kg + v, expert e0 + 16n + r */
@@ -269,9 +283,9 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
         const int64_t tiles = (int64_t)((S + T - 1) / T) * ((E + T - 1) / T);
         const dim3 grid((uint32_t)(tiles * parts)), block(256);
         if (T == 128)
-            hipLaunchKernelGGL(router_logits_mfma<4>, grid, block, 0, st, x, S, H, E, w, logits, parts);
+            hipLaunchKernelGGL((router_logits_mfma<4, kRouterDepth>), grid, block, 0, st, x, S, H, E, w, logits, parts);
         else
-            hipLaunchKernelGGL(router_logits_mfma<2>, grid, block, 0, st, x, S, H, E, w, logits, parts);
+            hipLaunchKernelGGL((router_logits_mfma<2, kRouterDepth>), grid, block, 0, st, x, S, H, E, w, logits, parts);
     }
     return hipGetLastError();
 }
