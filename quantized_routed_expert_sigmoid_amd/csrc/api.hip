@@ -349,11 +349,7 @@ int colibri_moe_layer_forward_staged(const coli_moe_layer* L, const float* x, in
 
     hipError_t e = mark(0, hipSuccess);
     if (e == hipSuccess)
-        e = S <= kSmallS
-                ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
-                : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
-    if (e == hipSuccess && S > kSmallS)
-        e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
+        e = launch_route_prep(x, S, H, E, L->router_w, logits, xq, xd, s);
     if (e == hipSuccess && S > kSmallS)
         e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
                                  L->routed_scaling_factor, route_opts(L), ids, w, s);

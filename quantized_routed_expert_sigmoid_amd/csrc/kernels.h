@@ -269,6 +269,11 @@ hipError_t launch_router_select(const float* logits, int32_t n_parts, const floa
                                 int32_t E, int32_t k, float rsf, const RouteOpts& opt, int32_t* ids,
                                 float* weights, hipStream_t st);
 
+/* Router logits (router_parts slices for S > kSmallS) and Q8_0 quantisation
+ * of x in one launch, for any S. */
+hipError_t launch_route_prep(const float* x, int32_t S, int32_t H, int32_t E, const float* w, float* logits,
+                             int8_t* xq, float* xd, hipStream_t st);
+
 /* S <= kSmallS: router logits and Q8_0 quantisation of x in one launch. */
 hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
                                    float* logits, int8_t* xq, float* xd, hipStream_t st);

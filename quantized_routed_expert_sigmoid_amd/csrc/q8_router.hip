@@ -192,14 +192,21 @@ template <int WT, int D>
 __global__ __launch_bounds__(256) void router_logits_mfma(const float* __restrict__ x, int32_t S,
                                                           int32_t H, int32_t E,
                                                           const float* __restrict__ w,
-                                                          float* __restrict__ part, int32_t n_parts)
+                                                          float* __restrict__ part, int32_t n_parts,
+                                                          int8_t* __restrict__ xq, float* __restrict__ xd)
 {
     constexpr int T = 32 * WT, WH = 16 * WT;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, kg = lane >> 4;
+    const int tiles_e = (E + T - 1) / T;
+    const int n_logit_groups = ((S + T - 1) / T) * tiles_e * n_parts;
+    if ((int)blockIdx.x >= n_logit_groups) {
+        /* quantiser workgroups (launched only with xq != nullptr) */
+        quantize_blocks(x, (int64_t)S * (H / 32), xq, xd, (int64_t)(blockIdx.x - n_logit_groups) * 256 + threadIdx.x);
+        return;
+    }
     const int p = blockIdx.x % n_parts;
     const int tile = blockIdx.x / n_parts;
-    const int tiles_e = (E + T - 1) / T;
     const int t0 = (tile / tiles_e) * T + (wv >> 1) * WH;
     const int e0 = (tile % tiles_e) * T + (wv & 1) * WH;
     const float* xr[WT];
@@ -270,6 +277,25 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const float* __restric
             }
 }
 
+/* The many-token router launch; with xq != nullptr the grid carries the
+ * quantiser workgroups of x's Q8_0 after the logit tiles. */
+static hipError_t launch_logits_mfma(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
+                                     float* logits, int8_t* xq, float* xd, hipStream_t st)
+{
+    const int32_t parts = router_parts(S, E, H);
+    const int32_t T = router_tile(S, E);
+    const int64_t tiles = (int64_t)((S + T - 1) / T) * ((E + T - 1) / T);
+    const int64_t qgroups = xq ? ((int64_t)S * (H / 32) * 8 + 255) / 256 : 0;
+    const dim3 grid((uint32_t)(tiles * parts + qgroups)), block(256);
+    if (T == 128)
+        hipLaunchKernelGGL((router_logits_mfma<4, kRouterDepth>), grid, block, 0, st, x, S, H, E, w, logits, parts,
+                           xq, xd);
+    else
+        hipLaunchKernelGGL((router_logits_mfma<2, kRouterDepth>), grid, block, 0, st, x, S, H, E, w, logits, parts,
+                           xq, xd);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E, const float* w,
                                 float* logits, hipStream_t st)
 {
@@ -277,17 +303,17 @@ hipError_t launch_router_logits(const float* x, int32_t S, int32_t H, int32_t E,
         return hipSuccess;
     if (S <= kSmallS) {
         launch_logits_small(dim3(E), S, st, x, H, E, w, logits, (int8_t*)nullptr, (float*)nullptr);
-    } else {
-        const int32_t parts = router_parts(S, E, H);
-        const int32_t T = router_tile(S, E);
-        const int64_t tiles = (int64_t)((S + T - 1) / T) * ((E + T - 1) / T);
-        const dim3 grid((uint32_t)(tiles * parts)), block(256);
-        if (T == 128)
-            hipLaunchKernelGGL((router_logits_mfma<4, kRouterDepth>), grid, block, 0, st, x, S, H, E, w, logits, parts);
-        else
-            hipLaunchKernelGGL((router_logits_mfma<2, kRouterDepth>), grid, block, 0, st, x, S, H, E, w, logits, parts);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    return launch_logits_mfma(x, S, H, E, w, logits, nullptr, nullptr, st);
+}
+
+hipError_t launch_route_prep(const float* x, int32_t S, int32_t H, int32_t E, const float* w, float* logits,
+                             int8_t* xq, float* xd, hipStream_t st)
+{
+    if (S <= kSmallS)
+        return launch_route_prep_small(x, S, H, E, w, logits, xq, xd, st);
+    return launch_logits_mfma(x, S, H, E, w, logits, xq, xd, st);
 }
 
 hipError_t launch_route_prep_small(const float* x, int32_t S, int32_t H, int32_t E, const float* w,

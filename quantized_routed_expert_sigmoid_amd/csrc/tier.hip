@@ -299,10 +299,7 @@ hipError_t route_into(const coli_tier* t, const float* x, int32_t S, int8_t* xq,
 {
     const coli_moe_layer* L = &t->L;
     const int32_t H = L->hidden, E = L->n_experts, k = L->top_k;
-    hipError_t e = S <= kSmallS ? launch_route_prep_small(x, S, H, E, L->router_w, logits, xq, xd, s)
-                                : launch_quantize_q8_0(x, (int64_t)S * (H / 32), xq, xd, s);
-    if (e == hipSuccess && S > kSmallS)
-        e = launch_router_logits(x, S, H, E, L->router_w, logits, s);
+    hipError_t e = launch_route_prep(x, S, H, E, L->router_w, logits, xq, xd, s);
     if (e == hipSuccess)
         e = launch_router_select(logits, router_parts(S, E, H), L->router_bias, S, E, k,
                                  L->routed_scaling_factor, route_opts(L), ids, w, s);
